@@ -1,0 +1,365 @@
+"""fp64 CPU oracle of the POET-X linear layer (plain definitions, numpy).
+
+TEST INFRASTRUCTURE.  Only tests, the smoke check and the benchmark's CPU
+baseline may import this module.  It shares no code with the HIP library and
+never calls it.
+
+Sources (web pages about POET-X and its parent method POET):
+  [ZC]  "在单张 H100 上预训练 13B 模型：POET-X 如何把正交变换的内存开销砍到 1/3"
+        (zhichai.net blog on POET-X); sections 第一斧 .. 第五斧.
+  [WS]  "[Project POET-X] Scaling Orthogonal Equivalence: Training 13B LLMs with
+        LoRA-level Memory Efficiency" (wispaper.ai blog); numbered methodology
+        sections and "Quantized Training (POET-XQ)".
+  [PN]  "Reparameterized LLM Training via Orthogonal Equivalence Transformation"
+        (NeurIPS 2025 paper notes on POET); 方法详解: 整体框架, 关键设计 1-4,
+        训练策略.
+  [GS]  "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
+        Transformation" (gist.science summary); Resumo técnico, 2. Metodologia.
+
+Conventions (where the pages leave the step open, the plainest reading):
+  * W0 is m x n (m inputs, n outputs); tokens are rows, so the layer
+    y = (R W0 P)^T x of [PN] 整体框架 reads Y = X R W0 P for X in R^{T x m}.
+  * A permutation is an index array pi with Psi[i, pi[i]] = 1, so
+    X Psi^T = X[:, pi] and (Z Psi)[:, pi[i]] = Z[:, i].
+  * One block-stochastic factor per side ([PN] 关键设计 1, c = 1):
+    R = Psi_R^T Diag(G_R^0 .. G_R^{nb-1}) Psi_R, nb = ceil(m / b).  A partial
+    last block of r < b rows is its own r x r CNP block.
+  * Each block G is the Cayley-Neumann form with k = 3 ([PN] 关键设计 2, [ZC]
+    第四斧 item 2): G = I + 2(Q + Q^2 + Q^3) + Q^4 of a skew-symmetric Q.
+  * Q is stored as its strict upper triangle in row-major order with the full
+    block stride b ([ZC] 第四斧 item 1): slot p(i, j) = i*b - i(i+1)/2 + (j-i-1)
+    holds Q[i, j] (i < j), and Q[j, i] = -Q[i, j].  Slots with j >= r in a
+    partial block are ignored and receive a zero gradient.
+  * Gradients are the exact gradients of this forward (intermediate H kept),
+    projected onto the packed parameters: dq[p(i,j)] = dQ[i,j] - dQ[j,i].
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+MASK64 = (1 << 64) - 1
+
+# ----------------------------------------------------------------------------
+# dtype decoding (the oracle's own widening of the stored bit patterns)
+# ----------------------------------------------------------------------------
+
+
+def to_f64(a: np.ndarray, dtype: str, scale: Optional[np.ndarray] = None) -> np.ndarray:
+    """Storage -> float64.  bf16 arrives as uint16 bit patterns; int8 codes are
+    multiplied by their per-column scale (dequantisation, [WS] POET-XQ)."""
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        u = np.asarray(a, dtype=np.uint16).astype(np.uint32) << 16
+        return u.view(np.float32).astype(np.float64)
+    if dtype == "i8":
+        out = np.asarray(a, dtype=np.int8).astype(np.float64)
+        if scale is not None:
+            out = out * np.asarray(scale, dtype=np.float32).astype(np.float64)[None, :]
+        return out
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------
+# packed skew-symmetric storage ([ZC] 第四斧 item 1; [WS] CNP "Half-Storage")
+# ----------------------------------------------------------------------------
+
+
+def packed_len(b: int) -> int:
+    return b * (b - 1) // 2
+
+
+def packed_index(i: int, j: int, b: int) -> int:
+    """Slot of Q[i, j], i < j, in the row-major strict upper triangle of a b x b block."""
+    assert 0 <= i < j < b
+    return i * b - i * (i + 1) // 2 + (j - i - 1)
+
+
+def _triu(b: int):
+    # numpy enumerates the strict upper triangle row by row: the same order as packed_index
+    return np.triu_indices(b, 1)
+
+
+def unpack_skew(qk: np.ndarray, r: int, b: int) -> np.ndarray:
+    """r x r skew-symmetric Q of one block from its packed slots (block stride b)."""
+    qk = np.asarray(qk, dtype=np.float64)
+    assert qk.shape == (packed_len(b),)
+    iu, ju = _triu(b)
+    live = ju < r
+    Q = np.zeros((r, r))
+    Q[iu[live], ju[live]] = qk[live]
+    Q[ju[live], iu[live]] = -qk[live]
+    return Q
+
+
+def pack_skew_grad(dQ: np.ndarray, b: int) -> np.ndarray:
+    """Gradient w.r.t. the packed slots: dq = dQ[i,j] - dQ[j,i]; dead slots 0."""
+    r = dQ.shape[0]
+    iu, ju = _triu(b)
+    live = ju < r
+    out = np.zeros(packed_len(b))
+    out[live] = dQ[iu[live], ju[live]] - dQ[ju[live], iu[live]]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Cayley-Neumann parameterisation ([PN] 关键设计 2; [ZC] 第四斧 item 2)
+# ----------------------------------------------------------------------------
+
+
+def cnp(Q: np.ndarray) -> np.ndarray:
+    """G = I + 2(Q + Q^2 + Q^3) + Q^4: the k = 3 Neumann truncation of the Cayley
+    transform, multiplied out."""
+    I = np.eye(Q.shape[0])
+    Q2 = Q @ Q
+    Q3 = Q2 @ Q
+    Q4 = Q3 @ Q
+    return I + 2.0 * (Q + Q2 + Q3) + Q4
+
+
+def cnp_neumann(Q: np.ndarray, k: int) -> np.ndarray:
+    """(I + Q)(I + Q + ... + Q^k): the truncated Cayley form of [PN] 关键设计 2."""
+    I = np.eye(Q.shape[0])
+    S = I.copy()
+    P = I.copy()
+    for _ in range(k):
+        P = P @ Q
+        S = S + P
+    return (I + Q) @ S
+
+
+def cayley(Q: np.ndarray) -> np.ndarray:
+    """Exact Cayley transform (I + Q)(I - Q)^{-1} ([PN] 关键设计 2)."""
+    I = np.eye(Q.shape[0])
+    return (I + Q) @ np.linalg.solve(I - Q, I)
+
+
+def cnp_adjoint(Q: np.ndarray, U: np.ndarray) -> np.ndarray:
+    """Gradient of <U, cnp(Q)> w.r.t. an unconstrained Q, using Q^T = -Q.
+
+    Each term A E B of the differential of G contributes A^T U B^T:
+    dQ = 2U - 2(QU + UQ) + 2(Q^2 U + Q U Q + U Q^2)
+         - (Q^3 U + Q^2 U Q + Q U Q^2 + U Q^3)."""
+    Q2 = Q @ Q
+    Q3 = Q2 @ Q
+    return (
+        2.0 * U
+        - 2.0 * (Q @ U + U @ Q)
+        + 2.0 * (Q2 @ U + Q @ U @ Q + U @ Q2)
+        - (Q3 @ U + Q2 @ U @ Q + Q @ U @ Q2 + U @ Q3)
+    )
+
+
+# ----------------------------------------------------------------------------
+# block-stochastic factors ([PN] 关键设计 1, block stochastic SPO with c = 1)
+# ----------------------------------------------------------------------------
+
+
+def side_blocks(d: int, b: int):
+    """(start, size) of the ceil(d/b) diagonal blocks of one side."""
+    return [(s, min(b, d - s)) for s in range(0, d, b)]
+
+
+def side_Q(q: np.ndarray, d: int, b: int) -> List[np.ndarray]:
+    return [unpack_skew(q[k], r, b) for k, (_, r) in enumerate(side_blocks(d, b))]
+
+
+def side_G(q: np.ndarray, d: int, b: int, exact: bool = False) -> List[np.ndarray]:
+    f = cayley if exact else cnp
+    return [f(Q) for Q in side_Q(q, d, b)]
+
+
+def perm_matrix(perm: np.ndarray) -> np.ndarray:
+    """Psi with Psi[i, perm[i]] = 1."""
+    d = len(perm)
+    Psi = np.zeros((d, d))
+    Psi[np.arange(d), perm] = 1.0
+    return Psi
+
+
+def block_diag(blocks: Sequence[np.ndarray]) -> np.ndarray:
+    d = sum(B.shape[0] for B in blocks)
+    D = np.zeros((d, d))
+    s = 0
+    for B in blocks:
+        r = B.shape[0]
+        D[s : s + r, s : s + r] = B
+        s += r
+    return D
+
+
+def dense_factor(perm: np.ndarray, blocks: Sequence[np.ndarray]) -> np.ndarray:
+    """R = Psi^T Diag(G^0 ..) Psi as a dense matrix (tiny sizes only)."""
+    Psi = perm_matrix(perm)
+    return Psi.T @ block_diag(blocks) @ Psi
+
+
+def apply_blocks(Z: np.ndarray, blocks: Sequence[np.ndarray], transpose: bool = False) -> np.ndarray:
+    """Row form of the block-diagonal product Z Diag(G) (or Z Diag(G)^T), one
+    block of columns at a time ([ZC] 第三斧: the blocks as a batch)."""
+    out = np.empty_like(Z)
+    s = 0
+    for G in blocks:
+        r = G.shape[0]
+        out[:, s : s + r] = Z[:, s : s + r] @ (G.T if transpose else G)
+        s += r
+    return out
+
+
+# ----------------------------------------------------------------------------
+# permutation merge ([ZC] 第二斧; [GS] 2. Metodologia, 4 -> 2 permutations)
+# ----------------------------------------------------------------------------
+
+
+def premerge(W: np.ndarray, perm_R: np.ndarray, perm_P: np.ndarray) -> np.ndarray:
+    """W~ = Psi_R W Psi_P^T = W[perm_R, :][:, perm_P]."""
+    return W[perm_R][:, perm_P]
+
+
+# ----------------------------------------------------------------------------
+# forward / backward ([ZC] 第一斧 input-centric order; [WS] section 1)
+# ----------------------------------------------------------------------------
+
+
+@dataclass
+class Fwd:
+    Y: np.ndarray
+    H: np.ndarray
+    A: np.ndarray
+    Xt: np.ndarray
+    Wt: np.ndarray
+
+
+def forward(X, W, perm_R, perm_P, G_R, G_P) -> Fwd:
+    """Input-centric forward with fp64 W (dequantised if stored int8):
+    Xt = X[:, pi_R]; A = Xt Diag(G_R); H = A W~; Zt = H Diag(G_P); Y[:, pi_P] = Zt."""
+    Xt = X[:, perm_R]
+    A = apply_blocks(Xt, G_R)
+    Wt = premerge(W, perm_R, perm_P)
+    H = A @ Wt
+    Zt = apply_blocks(H, G_P)
+    Y = np.empty_like(Zt)
+    Y[:, perm_P] = Zt
+    return Fwd(Y, H, A, Xt, Wt)
+
+
+def forward_weight_centric(X, W, R, P) -> np.ndarray:
+    """Original (weight-centric) order: build R W P, then apply it ([ZC] 第一斧)."""
+    return X @ (R @ W @ P)
+
+
+@dataclass
+class Bwd:
+    dX: np.ndarray
+    dG_R: List[np.ndarray]
+    dG_P: List[np.ndarray]
+    dq_R: np.ndarray
+    dq_P: np.ndarray
+
+
+def backward(X, dZ, W, perm_R, perm_P, q_R, q_P, b) -> Bwd:
+    """Exact gradients of forward() w.r.t. X and the packed q of both sides."""
+    m, n = W.shape
+    Q_R, Q_P = side_Q(q_R, m, b), side_Q(q_P, n, b)
+    G_R, G_P = [cnp(Q) for Q in Q_R], [cnp(Q) for Q in Q_P]
+    f = forward(X, W, perm_R, perm_P, G_R, G_P)
+    dZt = dZ[:, perm_P]
+    dG_P = [f.H[:, s : s + r].T @ dZt[:, s : s + r] for s, r in side_blocks(n, b)]
+    dH = apply_blocks(dZt, G_P, transpose=True)
+    dA = dH @ f.Wt.T
+    dG_R = [f.Xt[:, s : s + r].T @ dA[:, s : s + r] for s, r in side_blocks(m, b)]
+    dXt = apply_blocks(dA, G_R, transpose=True)
+    dX = np.empty_like(dXt)
+    dX[:, perm_R] = dXt
+    dq_R = np.stack([pack_skew_grad(cnp_adjoint(Q, U), b) for Q, U in zip(Q_R, dG_R)])
+    dq_P = np.stack([pack_skew_grad(cnp_adjoint(Q, U), b) for Q, U in zip(Q_P, dG_P)])
+    return Bwd(dX, dG_R, dG_P, dq_R, dq_P)
+
+
+def cnp_grad_packed(q: np.ndarray, dG: Sequence[np.ndarray], d: int, b: int) -> np.ndarray:
+    """Packed dq of one side from the block gradients dG (CNP chain rule + skew projection)."""
+    return np.stack([pack_skew_grad(cnp_adjoint(Q, U), b) for Q, U in zip(side_Q(q, d, b), dG)])
+
+
+# ----------------------------------------------------------------------------
+# permutation generator: SplitMix64 (Steele, Lea, Flood 2014) + Durstenfeld shuffle
+# ----------------------------------------------------------------------------
+
+
+def splitmix64_stream(seed: int):
+    """Successive SplitMix64 outputs for a 64-bit seed: the state advances by the
+    golden-ratio increment and each state is put through the two xor-shift-multiply
+    rounds of the published finaliser."""
+    state = seed & MASK64
+    while True:
+        state = (state + 0x9E3779B97F4A7C15) & MASK64
+        z = state
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+        yield z ^ (z >> 31)
+
+
+def perm_from_seed(seed: int, d: int) -> np.ndarray:
+    """Durstenfeld's Fisher-Yates shuffle of the identity: for i = d-1 .. 1 draw
+    j = floor(u * (i + 1) / 2^64) from the next 64-bit output u and swap p[i], p[j]."""
+    p = list(range(d))
+    g = splitmix64_stream(seed)
+    for i in range(d - 1, 0, -1):
+        j = (next(g) * (i + 1)) >> 64
+        p[i], p[j] = p[j], p[i]
+    return np.asarray(p, dtype=np.int32)
+
+
+# ----------------------------------------------------------------------------
+# 8-bit weights (POET-XQ, [WS] "Quantized Training"; [GS] 2. Metodologia)
+# ----------------------------------------------------------------------------
+
+
+def quantize_int8_f32(W: np.ndarray):
+    """Symmetric per-output-column absmax quantisation, every decision in fp32:
+    scale_j = fp32(max_i |W_ij|) / 127 (an all-zero column gets scale 1),
+    code = clamp(round_half_even(W / scale_j), -127, 127)."""
+    W = np.asarray(W, dtype=np.float32)
+    amax = np.max(np.abs(W), axis=0)
+    scale = (amax / np.float32(127.0)).astype(np.float32)
+    scale[amax == 0] = np.float32(1.0)
+    code = np.rint(W / scale[None, :])
+    return np.clip(code, -127, 127).astype(np.int8), scale
+
+
+def round_bf16(a64: np.ndarray) -> np.ndarray:
+    """float64 -> float32 -> bfloat16 (each step round to nearest even); uint16 bits."""
+    u = np.ascontiguousarray(a64.astype(np.float32)).view(np.uint32).astype(np.uint64)
+    return ((u + (((u >> 16) & 1) + 0x7FFF)) >> 16).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# merge-then-reinitialise ([PN] 关键设计 3 and 训练策略)
+# ----------------------------------------------------------------------------
+
+
+@dataclass
+class Merge:
+    W_new: np.ndarray  # merged weight R W P in the natural layout (fp64)
+    Wt_new: np.ndarray  # re-permuted for the new permutations (fp64)
+    perm_R: np.ndarray
+    perm_P: np.ndarray
+
+
+def merge_reinit(Wt, perm_R, perm_P, G_R, G_P, seed_R, seed_P) -> Merge:
+    """Fold the current factors into the weight and draw new permutations.
+
+    Wt is the pre-merged weight of the current permutations (fp64).  The merged
+    weight is W' = R W P = Psi_R^T (Diag(G_R) W~ Diag(G_P)) Psi_P; after the merge
+    the factors restart at the identity (q = 0) with permutations drawn from the
+    seeds, so the new pre-merged weight is W'[pi_R'][:, pi_P']."""
+    m, n = Wt.shape
+    M = apply_blocks(apply_blocks(Wt.T, G_R, transpose=True).T, G_P)  # Diag(G_R) W~ Diag(G_P)
+    W_new = np.empty_like(M)
+    W_new[np.ix_(perm_R, perm_P)] = M
+    pR, pP = perm_from_seed(seed_R, m), perm_from_seed(seed_P, n)
+    return Merge(W_new, premerge(W_new, pR, pP), pR, pP)

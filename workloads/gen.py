@@ -1,0 +1,131 @@
+"""Seeded generators for one POET-X linear's inputs.
+
+Every tensor is drawn from numpy's PCG64 seeded by SeedSequence([workload id,
+linear index, tensor id]) with tensor ids 0 = W0, 1 = q_R, 2 = q_P, 3 = X,
+4 = dZ, 5 = perm_R, 6 = perm_P.  Values are drawn in float64 and rounded once
+to the storage type; bf16 tensors are returned as uint16 bit patterns so both
+consumers see identical bits.
+
+W0 follows the normalized-Gaussian initialisation of the POET notes
+("Reparameterized LLM Training via Orthogonal Equivalence Transformation",
+section 4, initialisation schemes): N(0, 1) entries with every output column
+(every neuron) scaled to unit L2 norm.  For int8 storage the codes are a
+clipped, rounded Gaussian and the per-column fp32 scale is chosen so that each
+dequantised column has unit norm; this is an input recipe, not the layer's
+requantisation rule.
+
+Packed skew parameters q are N(0, std^2) for every packed slot, including the
+slots of a partial last block that the layer must ignore: they are left
+non-zero on purpose so that both implementations are checked to ignore them.
+"""
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+from .configs import Workload
+
+TENSOR_W0, TENSOR_QR, TENSOR_QP, TENSOR_X, TENSOR_DZ, TENSOR_PR, TENSOR_PP = range(7)
+
+
+def packed_len(b: int) -> int:
+    """Number of stored values per b x b block (strict upper triangle)."""
+    return b * (b - 1) // 2
+
+
+def _rng(wid: int, lin: int, tensor: int, extra: int = 0) -> np.random.Generator:
+    words = [wid, lin, tensor] + ([extra] if extra else [])
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(words)))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even); uint16 bits."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    bias = ((u >> 16) & 1) + 0x7FFF
+    return ((u + bias) >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _store(a64: np.ndarray, dtype: str) -> np.ndarray:
+    a32 = a64.astype(np.float32)
+    if dtype == "f32":
+        return a32
+    if dtype == "bf16":
+        return f32_to_bf16_bits(a32)
+    raise ValueError(dtype)
+
+
+@dataclass
+class LinearInputs:
+    m: int
+    n: int
+    b: int
+    T: int
+    act: str  # "f32" | "bf16"
+    w: str  # "f32" | "bf16" | "i8"
+    W0: np.ndarray  # [m, n]: float32, uint16 (bf16 bits) or int8 codes
+    w_scale: Optional[np.ndarray]  # [n] float32 when w == "i8"
+    q_R: np.ndarray  # [ceil(m/b), b(b-1)/2] float32
+    q_P: np.ndarray  # [ceil(n/b), b(b-1)/2] float32
+    perm_R: np.ndarray  # [m] int32
+    perm_P: np.ndarray  # [n] int32
+    X: np.ndarray  # [T, m] float32 or uint16
+    dZ: Optional[np.ndarray]  # [T, n] float32 or uint16
+
+
+def normalized_gaussian(rng: np.random.Generator, m: int, n: int) -> np.ndarray:
+    g = rng.standard_normal((m, n))
+    return g / np.linalg.norm(g, axis=0, keepdims=True)
+
+
+def int8_gaussian(rng: np.random.Generator, m: int, n: int):
+    g = rng.standard_normal((m, n))
+    codes = np.clip(np.rint(g * (127.0 / 4.0)), -127, 127)
+    norms = np.linalg.norm(codes, axis=0)
+    norms[norms == 0] = 1.0
+    return codes.astype(np.int8), (1.0 / norms).astype(np.float32)
+
+
+def make_linear_inputs(
+    wl: Workload,
+    lin: int,
+    T: Optional[int] = None,
+    with_dz: bool = True,
+    q_scale: float = 1.0,
+) -> LinearInputs:
+    """Inputs of linear `lin` of workload `wl`.  `T` overrides the token count
+    (parity tests use fewer tokens than the timed workload); `q_scale`
+    multiplies the q standard deviation (0 gives q = 0)."""
+    L = wl.linears[lin]
+    m, n, b = L.m, L.n, wl.b
+    T = wl.T if T is None else T
+    wid = wl.wid
+    if wl.w == "i8":
+        W0, w_scale = int8_gaussian(_rng(wid, lin, TENSOR_W0), m, n)
+    else:
+        W0, w_scale = _store(normalized_gaussian(_rng(wid, lin, TENSOR_W0), m, n), wl.w), None
+    nbR, nbP = -(-m // b), -(-n // b)
+    std = wl.q_std * q_scale
+    q_R = (_rng(wid, lin, TENSOR_QR).standard_normal((nbR, packed_len(b))) * std).astype(np.float32)
+    q_P = (_rng(wid, lin, TENSOR_QP).standard_normal((nbP, packed_len(b))) * std).astype(np.float32)
+    perm_R = _rng(wid, lin, TENSOR_PR).permutation(m).astype(np.int32)
+    perm_P = _rng(wid, lin, TENSOR_PP).permutation(n).astype(np.int32)
+    X = _store(_rng(wid, lin, TENSOR_X, T).standard_normal((T, m)), wl.act)
+    dZ = _store(_rng(wid, lin, TENSOR_DZ, T).standard_normal((T, n)), wl.act) if with_dz else None
+    return LinearInputs(m, n, b, T, wl.act, wl.w, W0, w_scale, q_R, q_P, perm_R, perm_P, X, dZ)
+
+
+def custom_linear_inputs(
+    m: int, n: int, b: int, T: int, act: str, w: str, q_std: float, seed: int
+) -> LinearInputs:
+    """Same recipe at an arbitrary shape (edge-case tests: ragged blocks, tiny sizes)."""
+    from .configs import LinearShape
+
+    wl = Workload("custom", 1000 + seed, (LinearShape("x", m, n),), b, T, act, w, q_std)
+    return make_linear_inputs(wl, 0)
