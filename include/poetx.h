@@ -1,0 +1,209 @@
+/*
+ * libpoetx: the POET-X orthogonal-equivalence linear layer on AMD MI355X (gfx950).
+ *
+ * The layer (POET paper notes, "Reparameterized LLM Training via Orthogonal
+ * Equivalence Transformation", 整体框架) reparameterises a frozen weight W0
+ * (m inputs x n outputs) as R W0 P with orthogonal R (m x m) and P (n x n) and
+ * computes y = (R W0 P)^T x.  With tokens as rows this is Y = X R W0 P.
+ *
+ * Each factor is one block-stochastic primitive (same notes, 关键设计 1):
+ * R = Psi^T Diag(G^0, ..., G^{nb-1}) Psi with nb = ceil(m / b) blocks, a partial
+ * last block of r = m - (nb-1) b rows, and Psi the permutation with
+ * Psi[i][perm[i]] = 1 (so X Psi^T = X[:, perm]).  Every block is the
+ * Cayley-Neumann form of a skew-symmetric Q (关键设计 2 with k = 3, multiplied out
+ * as in the zhichai.net POET-X blog, 第四斧 item 2):
+ *     G = I + 2 (Q + Q^2 + Q^3) + Q^4.
+ * Q is stored only as its strict upper triangle (第四斧 item 1), row by row with
+ * the full block stride b: slot p(i, j) = i*b - i(i+1)/2 + (j - i - 1) holds
+ * Q[i][j] for i < j, and Q[j][i] = -Q[i][j].  A side's parameters are one fp32
+ * array q[nb][b(b-1)/2]; slots of a partial block with j >= r are ignored.
+ *
+ * The forward runs in input-centric order (blog 第一斧): gather the input
+ * columns by perm_R, apply the R blocks as a batch (第三斧), contract with the
+ * pre-merged weight W~ = W0[perm_R, :][:, perm_P] (the two permutations next to
+ * W0 are folded into it, 第二斧), apply the P blocks, and scatter the output
+ * columns by perm_P.
+ *
+ * Conventions for every call
+ *  - All tensors are caller-owned device memory (plain pointers) unless stated.
+ *    Matrices are row-major with the leading dimension stated per argument.
+ *  - Every call validates its arguments, then enqueues its kernels on `stream`
+ *    (a hipStream_t; NULL means the null stream) and returns without waiting.
+ *    On any error nothing is enqueued and nothing is written.
+ *  - The library never allocates device memory: scratch space is the caller's
+ *    `ws` buffer of at least poetx_workspace_size() bytes, 256-byte aligned.
+ *    Calls that share a workspace must not overlap in time.
+ *  - The library keeps no state between calls except a per-thread error string.
+ *  - Formats the library lays out itself (pre-merged weight, G blocks, saved
+ *    activation) are sized by the *_bytes() helpers; their leading dimensions
+ *    are rounded up to a multiple of 64 elements.
+ */
+#ifndef POETX_H
+#define POETX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  POETX_OK = 0,
+  POETX_E_NULL = 1,        /* a required pointer is NULL */
+  POETX_E_SHAPE = 2,       /* m, n, b, d or T out of range */
+  POETX_E_DTYPE = 3,       /* unsupported dtype or dtype combination */
+  POETX_E_WORKSPACE = 4,   /* ws too small or misaligned */
+  POETX_E_PERM = 5,        /* host permutation argument invalid */
+  POETX_E_HIP = 6,         /* a HIP runtime call failed (see poetx_last_error) */
+  POETX_E_UNSUPPORTED = 7  /* valid request this build does not implement */
+} poetx_status;
+
+typedef enum { POETX_F32 = 0, POETX_BF16 = 1, POETX_I8 = 2 } poetx_dtype;
+
+/* Operation selector for poetx_workspace_size. */
+typedef enum { POETX_OP_CNP = 0, POETX_OP_FWD = 1, POETX_OP_BWD = 2, POETX_OP_MERGE = 3 } poetx_op;
+
+/*
+ * One linear layer.  act_dtype is the dtype of X, Y, dZ, dX, the saved
+ * activation and the G blocks; the block products and contractions run on MFMA
+ * in that dtype with fp32 accumulation.  w_dtype is the storage of the
+ * pre-merged weight: POETX_F32 (with act F32), POETX_BF16 or POETX_I8 (with act
+ * BF16).  POETX_I8 stores symmetric codes with one fp32 scale per output column
+ * (POET-XQ, wispaper.ai POET-X blog, "Quantized Training"): W = code * scale[col].
+ * Limits: 1 <= m, n <= 1 << 20; 2 <= b <= 1024.
+ */
+typedef struct {
+  int32_t m;
+  int32_t n;
+  int32_t b;
+  int32_t act_dtype;
+  int32_t w_dtype;
+} poetx_layer_desc;
+
+/* ---------------------------------------------------------------- helpers -- */
+
+/* Library version string (static storage). */
+const char* poetx_version(void);
+
+/* Message of the last failing call on this thread ("" if none; static per thread). */
+const char* poetx_last_error(void);
+
+/* Number of packed values per b x b block: b (b - 1) / 2. */
+int64_t poetx_packed_len(int32_t b);
+
+/* Bytes of a side's G buffer: [2][nb][b][b] elements of `dtype`.  Slice 0 holds
+ * Delta = G - I of every block, slice 1 holds Delta^T (the layout the forward's
+ * block products read).  Entries outside a partial block's r x r corner are 0. */
+size_t poetx_g_bytes(int32_t d, int32_t b, int32_t dtype);
+
+/* Bytes of the pre-merged weight buffer: values [m][ldw] of w_dtype, ldw =
+ * round_up(n, 64), followed (POETX_I8 only, at offset round_up(m*ldw, 256)) by
+ * the fp32 column scales [ldw] in pre-merged column order. */
+size_t poetx_weight_bytes(const poetx_layer_desc* desc);
+
+/* Bytes of the saved activation H = (X R-side product) W~ kept by the forward
+ * for the backward: [T][round_up(n, 64)] elements of act_dtype. */
+size_t poetx_saved_bytes(const poetx_layer_desc* desc, int64_t T);
+
+/* Workspace bytes for `op` (POETX_OP_CNP uses desc->m as the side length d and
+ * ignores T; POETX_OP_MERGE ignores T).  Returns 0 for invalid arguments. */
+size_t poetx_workspace_size(const poetx_layer_desc* desc, int64_t T, int32_t op);
+
+/* Host helper: the permutation drawn from `seed` (used by poetx_merge_reinit).
+ * SplitMix64 (Steele, Lea, Flood 2014) seeded with `seed` drives a Durstenfeld
+ * shuffle of the identity: for i = d-1 down to 1, j = floor(u * (i+1) / 2^64)
+ * for the next 64-bit output u, swap p[i] and p[j].  host_out: [d] host memory.
+ * Errors: POETX_E_NULL, POETX_E_SHAPE (d < 1). */
+poetx_status poetx_perm_from_seed(uint64_t seed, int32_t d, int32_t* host_out);
+
+/* ------------------------------------------------------------- the calls -- */
+
+/*
+ * Build the CNP blocks of one side (zhichai.net blog, 第四斧: Q^2 computed once,
+ * Q^3, Q^4 and G formed from it; POET notes, 关键设计 2, k = 3).
+ *   q      [nb][b(b-1)/2] fp32, packed skew parameters, nb = ceil(d / b)
+ *   d, b   side length (m for R, n for P) and block size
+ *   dtype  POETX_F32 or POETX_BF16: dtype of g (must equal the layer's act_dtype)
+ *   g      out, poetx_g_bytes(d, b, dtype) bytes: Delta = G - I and Delta^T
+ *   ws     >= poetx_workspace_size(desc with m = d, 0, POETX_OP_CNP)
+ */
+poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype, void* g, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/*
+ * Fold the two permutations adjacent to W0 into it (zhichai.net blog, 第二斧;
+ * gist.science summary, 2. Metodologia: four permutations reduced to two):
+ * Wt[i][j] = W0[perm_R[i]][perm_P[j]], and for POETX_I8 scale_t[j] = scale[perm_P[j]].
+ *   W0     [m][ld_w0] of w_dtype (natural layout), ld_w0 >= n
+ *   w0_scale [n] fp32 column scales (POETX_I8 only, else NULL)
+ *   perm_R [m], perm_P [n] int32 device permutations of 0..m-1 / 0..n-1
+ *   Wt     out, poetx_weight_bytes(desc) bytes (pre-merged layout, scales included)
+ * Pure data movement: the result is bit-exact.
+ */
+poetx_status poetx_premerge(const poetx_layer_desc* desc, const void* W0, int64_t ld_w0, const float* w0_scale,
+                            const int32_t* perm_R, const int32_t* perm_P, void* Wt, void* stream);
+
+/*
+ * Forward Y = X R W0 P (input-centric, wispaper.ai POET-X blog, section 1):
+ *   Xt = X[:, perm_R];  A = Xt Diag(G_R);  H = A W~;  Zt = H Diag(G_P);
+ *   Y[:, perm_P] = Zt.
+ *   X      [T][m] act_dtype, leading dimension m
+ *   perm_R [m], perm_P [n] int32 device
+ *   Wt     pre-merged weight (poetx_premerge / poetx_merge_reinit layout)
+ *   g_R, g_P  G buffers from poetx_cnp_build for the two sides
+ *   Y      out [T][n] act_dtype, leading dimension n
+ *   H_save out, poetx_saved_bytes(desc, T) bytes, read by poetx_linear_bwd
+ *   ws     >= poetx_workspace_size(desc, T, POETX_OP_FWD)
+ * T = 0 is a valid no-op.
+ */
+poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const void* X, const int32_t* perm_R,
+                              const int32_t* perm_P, const void* Wt, const void* g_R, const void* g_P, void* Y,
+                              void* H_save, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of the forward above for upstream gradient dZ = dL/dY: the input
+ * gradient dX and the gradients of both sides' packed parameters.  W0 is frozen
+ * (POET notes, 整体框架), so no weight gradient is formed.  Block gradients are
+ * dG_P = H_blk^T dZt_blk and dG_R = Xt_blk^T dA_blk summed over all T tokens in
+ * a fixed order (deterministic), then taken through the CNP chain rule and
+ * projected onto the packed slots: dq[p(i,j)] = dQ[i][j] - dQ[j][i].
+ *   X, dZ  [T][m], [T][n] act_dtype
+ *   q_R, q_P  the packed parameters the G buffers were built from
+ *   H_save the forward's saved activation for the same X
+ *   dX     out [T][m] act_dtype
+ *   dq_R, dq_P out [nb][b(b-1)/2] fp32, overwritten (dead slots of a partial block are 0)
+ *   ws     >= poetx_workspace_size(desc, T, POETX_OP_BWD)
+ */
+poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+                              const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
+                              const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX,
+                              float* dq_R, float* dq_P, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Merge-then-reinitialise (POET notes, 关键设计 3 and 训练策略): fold the current
+ * factors into the weight, W' = R W P = Psi_R^T (Diag(G_R) W~ Diag(G_P)) Psi_P,
+ * reset the factors to the identity (q_R = q_P = 0), draw new permutations from
+ * the seeds (same generator as poetx_perm_from_seed) and store the new
+ * pre-merged weight W'[perm_R'][:, perm_P'].  The products run in fp32 on MFMA.
+ * bf16 storage rounds to nearest even; int8 storage is re-quantised per output
+ * column: scale = max|w| / 127 (1 for an all-zero column), code =
+ * clamp(round_half_even(w / scale), -127, 127), every step in fp32.
+ *   Wt      in/out pre-merged weight
+ *   perm_R, perm_P  in/out int32 device permutations
+ *   g_R, g_P   G buffers built from the current q_R, q_P
+ *   q_R, q_P   out: zeroed
+ * After the call the first round_up(m*round_up(n,64)*4, 256) bytes of ws hold the
+ * merged weight in fp32 before rounding, laid out [m][round_up(n, 64)] in the
+ * new pre-merged order.
+ *   ws      >= poetx_workspace_size(desc, 0, POETX_OP_MERGE)
+ */
+poetx_status poetx_merge_reinit(const poetx_layer_desc* desc, void* Wt, int32_t* perm_R, int32_t* perm_P,
+                                const void* g_R, const void* g_P, float* q_R, float* q_P, uint64_t seed_R,
+                                uint64_t seed_P, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POETX_H */

@@ -363,3 +363,39 @@ def merge_reinit(Wt, perm_R, perm_P, G_R, G_P, seed_R, seed_P) -> Merge:
     W_new[np.ix_(perm_R, perm_P)] = M
     pR, pP = perm_from_seed(seed_R, m), perm_from_seed(seed_P, n)
     return Merge(W_new, premerge(W_new, pR, pP), pR, pP)
+
+
+# ----------------------------------------------------------------------------
+# sampled outputs at full size
+# ----------------------------------------------------------------------------
+
+
+def block_grads(X, dZ, W, perm_R, perm_P, q_R, q_P, b, blocks_R, blocks_P):
+    """Packed dq of selected blocks only, with the sums over all tokens.
+
+    Same definitions as backward(): dG_P^k = H_k^T dZt_k needs only the block's
+    columns of H = A W~, and dG_R^k = Xt_k^T dA_k only the block's columns of
+    dA = dH W~^T, so the cost is a few block-wide products instead of the whole
+    layer.  Returns {("R"|"P", k): dq_k}."""
+    m, n = W.shape
+    Q_R, Q_P = side_Q(q_R, m, b), side_Q(q_P, n, b)
+    G_R, G_P = [cnp(Q) for Q in Q_R], [cnp(Q) for Q in Q_P]
+    Wt = premerge(W, perm_R, perm_P)
+    Xt = X[:, perm_R]
+    dZt = dZ[:, perm_P]
+    out = {}
+    sbP = side_blocks(n, b)
+    if blocks_P:
+        A = apply_blocks(Xt, G_R)
+        for k in blocks_P:
+            s, r = sbP[k]
+            Hk = A @ Wt[:, s : s + r]
+            out[("P", k)] = pack_skew_grad(cnp_adjoint(Q_P[k], Hk.T @ dZt[:, s : s + r]), b)
+    if blocks_R:
+        dH = apply_blocks(dZt, G_P, transpose=True)
+        sbR = side_blocks(m, b)
+        for k in blocks_R:
+            s, r = sbR[k]
+            dAk = dH @ Wt[s : s + r, :].T
+            out[("R", k)] = pack_skew_grad(cnp_adjoint(Q_R[k], Xt[:, s : s + r].T @ dAk), b)
+    return out

@@ -1,0 +1,204 @@
+"""ctypes binding of libpoetx (include/poetx.h).
+
+Argument marshalling only: each function below has the name of the C entry point
+it calls and forwards raw device pointers, sizes and the HIP stream.  Every step
+of the layer runs in the library's HIP kernels; there is no fallback path, and a
+missing or unloadable library raises.
+
+Tensors are torch tensors on the GPU (torch provides device memory and
+streams).  bfloat16 data may be passed as torch.bfloat16 or as 16-bit integer
+tensors holding the bit patterns.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpoetx.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "poetx.h")
+
+POETX_OK, POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_PERM, POETX_E_HIP, POETX_E_UNSUPPORTED = range(8)
+POETX_F32, POETX_BF16, POETX_I8 = 0, 1, 2
+POETX_OP_CNP, POETX_OP_FWD, POETX_OP_BWD, POETX_OP_MERGE = 0, 1, 2, 3
+
+DTYPES = {"f32": POETX_F32, "bf16": POETX_BF16, "i8": POETX_I8}
+
+
+class PoetxError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libpoetx status {status}: {msg}")
+        self.status = status
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [
+        ("m", ctypes.c_int32),
+        ("n", ctypes.c_int32),
+        ("b", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+        ("w_dtype", ctypes.c_int32),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+_P = ctypes.c_void_p
+_SIG = {
+    "poetx_version": (ctypes.c_char_p, []),
+    "poetx_last_error": (ctypes.c_char_p, []),
+    "poetx_packed_len": (ctypes.c_int64, [ctypes.c_int32]),
+    "poetx_g_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "poetx_weight_bytes": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc)]),
+    "poetx_saved_bytes": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.c_int64]),
+    "poetx_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.c_int64, ctypes.c_int32]),
+    "poetx_perm_from_seed": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
+    "poetx_cnp_build": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
+    "poetx_premerge": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P]),
+    "poetx_linear_fwd": (
+        ctypes.c_int,
+        [ctypes.POINTER(LayerDesc), ctypes.c_int64, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P],
+    ),
+    "poetx_linear_bwd": (
+        ctypes.c_int,
+        [ctypes.POINTER(LayerDesc), ctypes.c_int64] + [_P] * 14 + [ctypes.c_size_t, _P],
+    ),
+    "poetx_merge_reinit": (
+        ctypes.c_int,
+        [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, ctypes.c_uint64, _P, ctypes.c_size_t, _P],
+    ),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpoetx.so (after torch, so that both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        try:
+            import torch  # noqa: F401  (loads the HIP runtime the library must share)
+        except ImportError:
+            pass
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run orthogonal_reparameterized_cnp_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def header_symbols() -> list:
+    """Names of the functions include/poetx.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]+?\b(poetx_\w+)\s*\(", text, re.M)))
+
+
+def _check(st: int):
+    if st != POETX_OK:
+        raise PoetxError(st, lib().poetx_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def desc(m: int, n: int, b: int, act: str, w: str) -> LayerDesc:
+    return LayerDesc(m, n, b, DTYPES[act], DTYPES[w])
+
+
+# ---------------------------------------------------------------- helpers ---
+def poetx_version() -> str:
+    return lib().poetx_version().decode()
+
+
+def poetx_last_error() -> str:
+    return lib().poetx_last_error().decode()
+
+
+def poetx_packed_len(b: int) -> int:
+    return lib().poetx_packed_len(b)
+
+
+def poetx_g_bytes(d: int, b: int, dtype: int) -> int:
+    return lib().poetx_g_bytes(d, b, dtype)
+
+
+def poetx_weight_bytes(dsc: LayerDesc) -> int:
+    return lib().poetx_weight_bytes(ctypes.byref(dsc))
+
+
+def poetx_saved_bytes(dsc: LayerDesc, T: int) -> int:
+    return lib().poetx_saved_bytes(ctypes.byref(dsc), T)
+
+
+def poetx_workspace_size(dsc: LayerDesc, T: int, op: int) -> int:
+    return lib().poetx_workspace_size(ctypes.byref(dsc), T, op)
+
+
+def poetx_perm_from_seed(seed: int, d: int):
+    import numpy as np
+
+    out = np.empty(d, dtype=np.int32)
+    _check(lib().poetx_perm_from_seed(seed, d, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return out
+
+
+# ------------------------------------------------------------- the calls ---
+def poetx_cnp_build(q, d: int, b: int, dtype: int, g, ws, ws_bytes: int, stream=None):
+    _check(lib().poetx_cnp_build(_ptr(q), d, b, dtype, _ptr(g), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def poetx_premerge(dsc: LayerDesc, W0, ld_w0: int, w0_scale, perm_R, perm_P, Wt, stream=None):
+    _check(
+        lib().poetx_premerge(
+            ctypes.byref(dsc), _ptr(W0), ld_w0, _ptr(w0_scale), _ptr(perm_R), _ptr(perm_P), _ptr(Wt), _stream(stream)
+        )
+    )
+
+
+def poetx_linear_fwd(dsc: LayerDesc, T: int, X, perm_R, perm_P, Wt, g_R, g_P, Y, H_save, ws, ws_bytes: int, stream=None):
+    _check(
+        lib().poetx_linear_fwd(
+            ctypes.byref(dsc), T, _ptr(X), _ptr(perm_R), _ptr(perm_P), _ptr(Wt), _ptr(g_R), _ptr(g_P), _ptr(Y),
+            _ptr(H_save), _ptr(ws), ws_bytes, _stream(stream),
+        )
+    )
+
+
+def poetx_linear_bwd(dsc: LayerDesc, T: int, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, dq_R, dq_P,
+                     ws, ws_bytes: int, stream=None):
+    _check(
+        lib().poetx_linear_bwd(
+            ctypes.byref(dsc), T, _ptr(X), _ptr(dZ), _ptr(perm_R), _ptr(perm_P), _ptr(Wt), _ptr(g_R), _ptr(g_P),
+            _ptr(q_R), _ptr(q_P), _ptr(H_save), _ptr(dX), _ptr(dq_R), _ptr(dq_P), _ptr(ws), ws_bytes, _stream(stream),
+        )
+    )
+
+
+def poetx_merge_reinit(dsc: LayerDesc, Wt, perm_R, perm_P, g_R, g_P, q_R, q_P, seed_R: int, seed_P: int, ws,
+                       ws_bytes: int, stream=None):
+    _check(
+        lib().poetx_merge_reinit(
+            ctypes.byref(dsc), _ptr(Wt), _ptr(perm_R), _ptr(perm_P), _ptr(g_R), _ptr(g_P), _ptr(q_R), _ptr(q_P),
+            seed_R & ((1 << 64) - 1), seed_P & ((1 << 64) - 1), _ptr(ws), ws_bytes, _stream(stream),
+        )
+    )

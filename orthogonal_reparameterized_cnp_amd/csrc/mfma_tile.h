@@ -1,0 +1,372 @@
+// Workgroup-level MFMA tile loop for gfx950 (CDNA4, wave64).
+//
+// One workgroup computes a BM x BN tile of C = A * B with fp32 accumulation.
+// Both operands are staged in LDS as [rows][BK] with K contiguous, which is the
+// order in which v_mfma_f32_32x32x16_bf16 (bf16 path) and v_mfma_f32_32x32x2f32
+// (fp32 path) consume them: each lane supplies a run of consecutive K values
+// for one row of A and one column of B.  Operand loaders turn whatever layout
+// the source has (K contiguous, or M/N contiguous and transposed on the way
+// into LDS, or generated on the fly) into that LDS tile; the K loop is double
+// buffered in LDS with the next tile's global loads issued before the MFMAs
+// of the current one, so one barrier per K tile suffices.
+#pragma once
+
+#include "common.h"
+
+namespace px {
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = NW * 64;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+  static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
+};
+
+// LDS row pitch: BK plus 16 bytes, so that the 8 lanes served together by a
+// 128-bit LDS read (8 consecutive rows, same K offset) hit 8 distinct 16-byte
+// bank groups.
+template <typename T> struct LdsPad;
+template <> struct LdsPad<bf16_t> { static constexpr int v = 8; };
+template <> struct LdsPad<float> { static constexpr int v = 4; };
+
+template <class C, typename T> struct Lay {
+  static constexpr int LDK = C::BK + LdsPad<T>::v;
+  static constexpr int A_ELEMS = C::BM * LDK;
+  static constexpr int B_ELEMS = C::BN * LDK;
+  static constexpr int STAGE = A_ELEMS + B_ELEMS;
+  static constexpr int BYTES = 2 * STAGE * (int)sizeof(T);
+};
+
+template <class C> struct Acc {
+  f32x16_v v[C::TM][C::TN];
+  PX_DEV void zero() {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) v[i][j][e] = 0.f;
+  }
+};
+
+// Coordinates of accumulator register e of MFMA tile (i, j) within the workgroup
+// tile: a 32x32 fp32 result is spread so that lane l owns column l % 32 and the
+// rows 8*(e/4) + 4*(l/32) + e%4.
+template <class C> struct AccPos {
+  int wm, wn, lane;
+  PX_DEV int row(int i, int e) const { return wm * C::WTM + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3); }
+  PX_DEV int col(int j) const { return wn * C::WTN + j * 32 + (lane & 31); }
+};
+
+template <class C>
+PX_DEV void mma_stage(const bf16_t* As, const bf16_t* Bs, Acc<C>& acc, int wm, int wn, int lane) {
+  constexpr int LDK = Lay<C, bf16_t>::LDK;
+  const int r = lane & 31, kg = (lane >> 5) * 8;
+#pragma unroll
+  for (int kk = 0; kk < C::BK; kk += 16) {
+    bf16x8_v a[C::TM], b[C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8_v*>(As + (wm * C::WTM + i * 32 + r) * LDK + kk + kg);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      b[j] = *reinterpret_cast<const bf16x8_v*>(Bs + (wn * C::WTN + j * 32 + r) * LDK + kk + kg);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
+  }
+}
+
+template <class C>
+PX_DEV void mma_stage(const float* As, const float* Bs, Acc<C>& acc, int wm, int wn, int lane) {
+  constexpr int LDK = Lay<C, float>::LDK;
+  const int r = lane & 31, kg = (lane >> 5) * 4;
+#pragma unroll
+  for (int kk = 0; kk < C::BK; kk += 8) {
+    f32x4_v a[C::TM], b[C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+      a[i] = *reinterpret_cast<const f32x4_v*>(As + (wm * C::WTM + i * 32 + r) * LDK + kk + kg);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      b[j] = *reinterpret_cast<const f32x4_v*>(Bs + (wn * C::WTN + j * 32 + r) * LDK + kk + kg);
+    // element e of the lane's 4 K values feeds the e-th MFMA; the two lane
+    // halves cover K offsets {e, 4 + e}, so the four MFMAs cover all 8.
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc.v[i][j], 0, 0, 0);
+  }
+}
+
+// K loop.  `K` is the contraction length; loaders zero-fill past it.
+template <class C, typename T, class LA, class LB>
+PX_DEV void mainloop(T* lds, LA& la, LB& lb, int K, Acc<C>& acc, int wm, int wn, int lane) {
+  using L = Lay<C, T>;
+  acc.zero();
+  const int KT = (K + C::BK - 1) / C::BK;
+  if (KT <= 0) return;
+  la.fetch(0);
+  lb.fetch(0);
+  la.stash(lds);
+  lb.stash(lds + L::A_ELEMS);
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    T* cur = lds + (kt & 1) * L::STAGE;
+    T* nxt = lds + ((kt + 1) & 1) * L::STAGE;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      la.fetch((kt + 1) * C::BK);
+      lb.fetch((kt + 1) * C::BK);
+    }
+    mma_stage<C>(cur, cur + L::A_ELEMS, acc, wm, wn, lane);
+    if (more) {
+      la.stash(nxt);
+      lb.stash(nxt + L::A_ELEMS);
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 8-element chunks held in registers between the global load and the LDS store
+// ---------------------------------------------------------------------------
+template <typename D> struct Chunk8;
+template <> struct Chunk8<bf16_t> {
+  uint4 w;  // 8 bf16
+  PX_DEV void zero() { w = make_uint4(0, 0, 0, 0); }
+  PX_DEV void set(int e, bf16_t v) {
+    uint32_t* p = reinterpret_cast<uint32_t*>(&w);
+    const int s = (e & 1) * 16;
+    p[e >> 1] = (p[e >> 1] & ~(0xffffu << s)) | ((uint32_t)v << s);
+  }
+  PX_DEV bf16_t get(int e) const {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(&w);
+    return (bf16_t)(p[e >> 1] >> ((e & 1) * 16));
+  }
+};
+template <> struct Chunk8<float> {
+  float4 a, b;
+  PX_DEV void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
+  PX_DEV void set(int e, float v) { (e < 4 ? reinterpret_cast<float*>(&a)[e] : reinterpret_cast<float*>(&b)[e - 4]) = v; }
+  PX_DEV float get(int e) const { return e < 4 ? reinterpret_cast<const float*>(&a)[e] : reinterpret_cast<const float*>(&b)[e - 4]; }
+};
+
+// vector load of 8 consecutive source elements (address aligned to 8 elements)
+template <typename D, typename S> struct Load8;
+template <> struct Load8<bf16_t, bf16_t> {
+  static PX_DEV void go(const bf16_t* p, Chunk8<bf16_t>& c) { c.w = *reinterpret_cast<const uint4*>(p); }
+};
+template <> struct Load8<float, float> {
+  static PX_DEV void go(const float* p, Chunk8<float>& c) {
+    c.a = reinterpret_cast<const float4*>(p)[0];
+    c.b = reinterpret_cast<const float4*>(p)[1];
+  }
+};
+template <> struct Load8<float, bf16_t> {
+  static PX_DEV void go(const bf16_t* p, Chunk8<float>& c) {
+    const uint4 w = *reinterpret_cast<const uint4*>(p);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c.set(e, __uint_as_float((e & 1) ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16)));
+  }
+};
+template <> struct Load8<bf16_t, float> {
+  static PX_DEV void go(const float* p, Chunk8<bf16_t>& c) {
+    const float4 x = reinterpret_cast<const float4*>(p)[0], y = reinterpret_cast<const float4*>(p)[1];
+    c.w.x = (uint32_t)f2bf(x.x) | ((uint32_t)f2bf(x.y) << 16);
+    c.w.y = (uint32_t)f2bf(x.z) | ((uint32_t)f2bf(x.w) << 16);
+    c.w.z = (uint32_t)f2bf(y.x) | ((uint32_t)f2bf(y.y) << 16);
+    c.w.w = (uint32_t)f2bf(y.z) | ((uint32_t)f2bf(y.w) << 16);
+  }
+};
+template <typename D> struct Load8<D, int8_t> {
+  static PX_DEV void go(const int8_t* p, Chunk8<D>& c) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int8_t v = (int8_t)(((e < 4 ? w.x : w.y) >> ((e & 3) * 8)) & 0xff);
+      c.set(e, Cvt<D, int8_t>::f(v));
+    }
+  }
+};
+
+template <typename S> PX_DEV bool aligned8(const S* p, int64_t ld) {
+  return ((reinterpret_cast<uintptr_t>(p) % (8 * sizeof(S))) == 0) && (ld % 8 == 0);
+}
+
+// ---------------------------------------------------------------------------
+// Loader: source rows with K contiguous.  Tile row `r` is source row r, K
+// offset k is column k (relative to `base`).  Rows >= rows or K >= K read as 0.
+// ---------------------------------------------------------------------------
+template <int ROWS, int BK, int NT, typename S, typename D>
+struct LoadK {
+  static constexpr int CPR = BK / 8;
+  static constexpr int TOT = ROWS * CPR;
+  static constexpr int NCH = (TOT + NT - 1) / NT;
+  const S* base;
+  int64_t ld;
+  int rows, K;
+  bool vec;
+  Chunk8<D> c[NCH];
+
+  PX_DEV void init(const S* base_, int64_t ld_, int rows_, int K_) {
+    base = base_;
+    ld = ld_;
+    rows = rows_;
+    K = K_;
+    vec = aligned8(base_, ld_);
+  }
+  PX_DEV void fetch(int k0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = threadIdx.x + i * NT;
+      if (TOT % NT != 0 && ch >= TOT) break;
+      const int r = ch / CPR, k = k0 + (ch % CPR) * 8;
+      const S* p = base + (int64_t)r * ld + k;
+      if (r < rows && k + 8 <= K && vec) {
+        Load8<D, S>::go(p, c[i]);
+      } else {
+        c[i].zero();
+        if (r < rows)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (k + e < K) c[i].set(e, Cvt<D, S>::f(p[e]));
+      }
+    }
+  }
+  PX_DEV void stash(D* lds) const {
+    constexpr int LDK = BK + LdsPad<D>::v;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = threadIdx.x + i * NT;
+      if (TOT % NT != 0 && ch >= TOT) break;
+      const int r = ch / CPR, kc = (ch % CPR) * 8;
+      if constexpr (sizeof(D) == 2) {
+        *reinterpret_cast<uint4*>(lds + r * LDK + kc) = c[i].w;
+      } else {
+        reinterpret_cast<float4*>(lds + r * LDK + kc)[0] = c[i].a;
+        reinterpret_cast<float4*>(lds + r * LDK + kc)[1] = c[i].b;
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Loader: source with the tile's row index contiguous (element (k, r) at
+// base[k * ld + r]); transposed into the [row][K] LDS tile.  Each thread moves
+// units of 4 K values x 8 rows: four 8-wide global loads along the rows, then
+// eight 4-wide LDS stores along K.
+// ---------------------------------------------------------------------------
+template <int ROWS, int BK, int NT, typename S, typename D>
+struct LoadMN {
+  static constexpr int MC = ROWS / 8;
+  static constexpr int KQ = BK / 4;
+  static constexpr int TOT = MC * KQ;
+  static constexpr int NU = (TOT + NT - 1) / NT;
+  const S* base;
+  int64_t ld;
+  int rows, K;
+  bool vec;
+  Chunk8<D> c[NU][4];
+
+  PX_DEV void init(const S* base_, int64_t ld_, int rows_, int K_) {
+    base = base_;
+    ld = ld_;
+    rows = rows_;
+    K = K_;
+    vec = aligned8(base_, ld_);
+  }
+  PX_DEV void fetch(int k0) {
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int unit = threadIdx.x + u * NT;
+      if (TOT % NT != 0 && unit >= TOT) break;
+      const int r0 = (unit % MC) * 8, kq = k0 + (unit / MC) * 4;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = kq + kk;
+        const S* p = base + (int64_t)k * ld + r0;
+        if (k < K && r0 + 8 <= rows && vec) {
+          Load8<D, S>::go(p, c[u][kk]);
+        } else {
+          c[u][kk].zero();
+          if (k < K)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (r0 + e < rows) c[u][kk].set(e, Cvt<D, S>::f(p[e]));
+        }
+      }
+    }
+  }
+  PX_DEV void stash(D* lds) const {
+    constexpr int LDK = BK + LdsPad<D>::v;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int unit = threadIdx.x + u * NT;
+      if (TOT % NT != 0 && unit >= TOT) break;
+      const int r0 = (unit % MC) * 8, kq = (unit / MC) * 4;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        D* p = lds + (r0 + e) * LDK + kq;
+        if constexpr (sizeof(D) == 2) {
+          uint2 v;
+          v.x = (uint32_t)c[u][0].get(e) | ((uint32_t)c[u][1].get(e) << 16);
+          v.y = (uint32_t)c[u][2].get(e) | ((uint32_t)c[u][3].get(e) << 16);
+          *reinterpret_cast<uint2*>(p) = v;
+        } else {
+          *reinterpret_cast<float4*>(p) = make_float4(c[u][0].get(e), c[u][1].get(e), c[u][2].get(e), c[u][3].get(e));
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Loader: tile values generated by a functor f(row, k) -> float (rows and K
+// are absolute indices: row0 + r, k).  Used for skew blocks unpacked from
+// their packed storage and for small combinations of them.
+// ---------------------------------------------------------------------------
+template <int ROWS, int BK, int NT, typename D, class F>
+struct LoadGen {
+  static constexpr int CPR = BK / 8;
+  static constexpr int TOT = ROWS * CPR;
+  static constexpr int NCH = (TOT + NT - 1) / NT;
+  F f;
+  int row0;
+  Chunk8<D> c[NCH];
+  PX_DEV void fetch(int k0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = threadIdx.x + i * NT;
+      if (TOT % NT != 0 && ch >= TOT) break;
+      const int r = ch / CPR, k = k0 + (ch % CPR) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c[i].set(e, from_f32<D>(f(row0 + r, k + e)));
+    }
+  }
+  PX_DEV void stash(D* lds) const {
+    constexpr int LDK = BK + LdsPad<D>::v;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = threadIdx.x + i * NT;
+      if (TOT % NT != 0 && ch >= TOT) break;
+      const int r = ch / CPR, kc = (ch % CPR) * 8;
+      if constexpr (sizeof(D) == 2) {
+        *reinterpret_cast<uint4*>(lds + r * LDK + kc) = c[i].w;
+      } else {
+        reinterpret_cast<float4*>(lds + r * LDK + kc)[0] = c[i].a;
+        reinterpret_cast<float4*>(lds + r * LDK + kc)[1] = c[i].b;
+      }
+    }
+  }
+};
+
+}  // namespace px

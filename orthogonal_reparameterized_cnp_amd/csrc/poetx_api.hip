@@ -1,0 +1,348 @@
+// C ABI of libpoetx: argument validation, workspace planning and the order of
+// kernel launches for each call.  All arithmetic happens in the kernels of
+// poetx_kernels.hip.
+#include <string>
+
+#include "../../include/poetx.h"
+#include "poetx_internal.h"
+
+using namespace pxk;
+
+namespace {
+
+thread_local std::string g_err;
+
+poetx_status fail(poetx_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+#define PX_HIP(expr)                                                                         \
+  do {                                                                                       \
+    hipError_t e_ = (expr);                                                                  \
+    if (e_ != hipSuccess) return fail(POETX_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int64_t kMaxDim = int64_t(1) << 20;
+constexpr int64_t kMaxT = (int64_t(1) << 31) - 1;
+
+poetx_status check_desc(const poetx_layer_desc* d) {
+  if (!d) return fail(POETX_E_NULL, "desc is NULL");
+  if (d->m < 1 || d->n < 1 || d->m > kMaxDim || d->n > kMaxDim)
+    return fail(POETX_E_SHAPE, "m and n must be in [1, 2^20]");
+  if (d->b < 2 || d->b > 1024) return fail(POETX_E_SHAPE, "b must be in [2, 1024]");
+  if (nblocks(d->m, d->b) > 65535 || nblocks(d->n, d->b) > 65535)
+    return fail(POETX_E_SHAPE, "at most 65535 blocks per side");
+  const bool ok = (d->act_dtype == POETX_F32 && d->w_dtype == POETX_F32) ||
+                  (d->act_dtype == POETX_BF16 && (d->w_dtype == POETX_BF16 || d->w_dtype == POETX_I8));
+  if (!ok) return fail(POETX_E_DTYPE, "supported (act, weight) dtypes: (F32, F32), (BF16, BF16), (BF16, I8)");
+  return POETX_OK;
+}
+
+// Bump allocator over the caller's workspace (256-byte aligned regions).
+struct Plan {
+  size_t off = 0;
+  char* base = nullptr;
+  template <typename T> T* take(size_t bytes) {
+    T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return p;
+  }
+};
+
+size_t g_slice(int d, int b, int dt) { return (size_t)nblocks(d, b) * b * b * dt_size(dt); }
+
+size_t weight_scale_offset(const poetx_layer_desc* d) {
+  return (size_t)round_up((int64_t)d->m * lead(d->n) * (int64_t)dt_size(d->w_dtype), 256);
+}
+
+struct FwdWs {
+  void *Xt, *A, *Zt;
+  int32_t* invP;
+};
+template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
+  const size_t es = dt_size(d->act_dtype);
+  FwdWs w;
+  w.Xt = p.template take<char>(T * lead(d->m) * es);
+  w.A = p.template take<char>(T * lead(d->m) * es);
+  w.Zt = p.template take<char>(T * lead(d->n) * es);
+  w.invP = p.template take<int32_t>((size_t)d->n * 4);
+  return w;
+}
+
+struct BwdWs {
+  void *dZt, *dH, *dA, *Xt, *dXt;
+  float *partP, *partR, *cnp;
+  int32_t* invR;
+  int splitsP, splitsR;
+};
+template <class P> BwdWs plan_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
+  const size_t es = dt_size(d->act_dtype);
+  const int64_t b = d->b, nbR = nblocks(d->m, d->b), nbP = nblocks(d->n, d->b);
+  BwdWs w;
+  w.splitsP = dgrad_splits((int)T, d->n, d->b);
+  w.splitsR = dgrad_splits((int)T, d->m, d->b);
+  w.dZt = p.template take<char>(T * lead(d->n) * es);
+  w.dH = p.template take<char>(T * lead(d->n) * es);
+  w.dA = p.template take<char>(T * lead(d->m) * es);
+  w.Xt = p.template take<char>(T * lead(d->m) * es);
+  w.dXt = p.template take<char>(T * lead(d->m) * es);
+  w.partP = p.template take<float>((size_t)w.splitsP * nbP * b * b * 4);
+  w.partR = p.template take<float>((size_t)w.splitsR * nbR * b * b * 4);
+  w.cnp = p.template take<float>((size_t)7 * std::max(nbR, nbP) * b * b * 4);
+  w.invR = p.template take<int32_t>((size_t)d->m * 4);
+  return w;
+}
+
+struct MergeWs {
+  float *Mq, *M;
+  int32_t *newR, *newP, *invR, *invP, *rhoR, *rhoP, *fy;
+  uint32_t* amax;
+};
+template <class P> MergeWs plan_merge(P& p, const poetx_layer_desc* d) {
+  const size_t mat = (size_t)d->m * lead(d->n) * 4;
+  MergeWs w;
+  w.Mq = p.template take<float>(mat);  // first M1 (left product), finally the re-permuted fp32 weight
+  w.M = p.template take<float>(mat);
+  w.newR = p.template take<int32_t>((size_t)d->m * 4);
+  w.newP = p.template take<int32_t>((size_t)d->n * 4);
+  w.invR = p.template take<int32_t>((size_t)d->m * 4);
+  w.invP = p.template take<int32_t>((size_t)d->n * 4);
+  w.rhoR = p.template take<int32_t>((size_t)d->m * 4);
+  w.rhoP = p.template take<int32_t>((size_t)d->n * 4);
+  w.fy = p.template take<int32_t>((size_t)std::max(d->m, d->n) * 4);
+  w.amax = p.template take<uint32_t>((size_t)d->n * 4);
+  return w;
+}
+
+poetx_status check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return POETX_OK;
+  if (!ws) return fail(POETX_E_NULL, "ws is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % 256) return fail(POETX_E_WORKSPACE, "ws must be 256-byte aligned");
+  if (ws_bytes < need)
+    return fail(POETX_E_WORKSPACE, "ws too small: need " + std::to_string(need) + " bytes, got " + std::to_string(ws_bytes));
+  return POETX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* poetx_version(void) { return "libpoetx 0.1 (gfx950)"; }
+
+const char* poetx_last_error(void) { return g_err.c_str(); }
+
+int64_t poetx_packed_len(int32_t b) { return b < 2 ? 0 : packed_len(b); }
+
+size_t poetx_g_bytes(int32_t d, int32_t b, int32_t dtype) {
+  if (d < 1 || b < 2 || (dtype != POETX_F32 && dtype != POETX_BF16)) return 0;
+  return 2 * g_slice(d, b, dtype);
+}
+
+size_t poetx_weight_bytes(const poetx_layer_desc* desc) {
+  if (check_desc(desc) != POETX_OK) return 0;
+  size_t bytes = weight_scale_offset(desc);
+  if (desc->w_dtype == POETX_I8) bytes += (size_t)lead(desc->n) * 4;
+  return bytes;
+}
+
+size_t poetx_saved_bytes(const poetx_layer_desc* desc, int64_t T) {
+  if (check_desc(desc) != POETX_OK || T < 0) return 0;
+  return (size_t)T * lead(desc->n) * dt_size(desc->act_dtype);
+}
+
+size_t poetx_workspace_size(const poetx_layer_desc* desc, int64_t T, int32_t op) {
+  if (!desc || T < 0 || T > kMaxT) return 0;
+  if (op == POETX_OP_CNP) {
+    if (desc->m < 1 || desc->b < 2) return 0;
+    return (size_t)round_up((int64_t)nblocks(desc->m, desc->b) * desc->b * desc->b * 4, 256);
+  }
+  if (check_desc(desc) != POETX_OK) return 0;
+  Plan p;
+  if (op == POETX_OP_FWD) plan_fwd(p, desc, T);
+  else if (op == POETX_OP_BWD) plan_bwd(p, desc, T);
+  else if (op == POETX_OP_MERGE) plan_merge(p, desc);
+  else return 0;
+  return p.off;
+}
+
+poetx_status poetx_perm_from_seed(uint64_t seed, int32_t d, int32_t* out) {
+  if (!out) return fail(POETX_E_NULL, "host_out is NULL");
+  if (d < 1) return fail(POETX_E_SHAPE, "d must be >= 1");
+  for (int32_t i = 0; i < d; ++i) out[i] = i;
+  uint64_t state = seed;
+  for (int32_t i = d - 1; i >= 1; --i) {
+    state += 0x9E3779B97F4A7C15ull;
+    uint64_t z = state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    const int32_t j = (int32_t)(((unsigned __int128)z * (uint64_t)(i + 1)) >> 64);
+    const int32_t t = out[i];
+    out[i] = out[j];
+    out[j] = t;
+  }
+  return POETX_OK;
+}
+
+poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype, void* g, void* ws, size_t ws_bytes,
+                             void* stream) {
+  if (!q || !g) return fail(POETX_E_NULL, "q and g must be non-NULL");
+  if (d < 1 || d > kMaxDim || b < 2 || b > 1024 || nblocks(d, b) > 65535) return fail(POETX_E_SHAPE, "bad d or b");
+  if (dtype != POETX_F32 && dtype != POETX_BF16) return fail(POETX_E_DTYPE, "g dtype must be F32 or BF16");
+  const size_t need = (size_t)round_up((int64_t)nblocks(d, b) * b * b * 4, 256);
+  poetx_status st = check_ws(ws, ws_bytes, need);
+  if (st != POETX_OK) return st;
+  PX_HIP(cnp_build(dtype, q, d, b, g, reinterpret_cast<float*>(ws), reinterpret_cast<hipStream_t>(stream)));
+  return POETX_OK;
+}
+
+poetx_status poetx_premerge(const poetx_layer_desc* desc, const void* W0, int64_t ld_w0, const float* w0_scale,
+                            const int32_t* perm_R, const int32_t* perm_P, void* Wt, void* stream) {
+  poetx_status st = check_desc(desc);
+  if (st != POETX_OK) return st;
+  if (!W0 || !perm_R || !perm_P || !Wt) return fail(POETX_E_NULL, "W0, perm_R, perm_P and Wt must be non-NULL");
+  if (desc->w_dtype == POETX_I8 && !w0_scale) return fail(POETX_E_NULL, "w0_scale is required for I8 weights");
+  if (ld_w0 < desc->n) return fail(POETX_E_SHAPE, "ld_w0 < n");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int m = desc->m, n = desc->n;
+  PX_HIP(permute(desc->w_dtype, W0, ld_w0, perm_R, perm_P, Wt, lead(n), m, n, n, s));
+  if (desc->w_dtype == POETX_I8) {
+    float* scale_t = reinterpret_cast<float*>(reinterpret_cast<char*>(Wt) + weight_scale_offset(desc));
+    PX_HIP(permute(F32, w0_scale, 0, nullptr, perm_P, scale_t, 0, 1, n, n, s));
+  }
+  return POETX_OK;
+}
+
+poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const void* X, const int32_t* perm_R,
+                              const int32_t* perm_P, const void* Wt, const void* g_R, const void* g_P, void* Y,
+                              void* H_save, void* ws, size_t ws_bytes, void* stream) {
+  poetx_status st = check_desc(desc);
+  if (st != POETX_OK) return st;
+  if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
+  if (T == 0) return POETX_OK;
+  if (!X || !perm_R || !perm_P || !Wt || !g_R || !g_P || !Y || !H_save)
+    return fail(POETX_E_NULL, "a required pointer is NULL");
+  Plan p;
+  plan_fwd(p, desc, T);
+  st = check_ws(ws, ws_bytes, p.off);
+  if (st != POETX_OK) return st;
+  Plan q;
+  q.base = reinterpret_cast<char*>(ws);
+  const FwdWs w = plan_fwd(q, desc, T);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, wt = desc->w_dtype;
+  const int rows = (int)T;
+  const int64_t ldm = lead(m), ldn = lead(n);
+  const char* gR1 = reinterpret_cast<const char*>(g_R) + g_slice(m, b, at);  // Delta_R^T
+  const char* gP1 = reinterpret_cast<const char*>(g_P) + g_slice(n, b, at);  // Delta_P^T
+  const float* scale_t =
+      wt == POETX_I8 ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(Wt) + weight_scale_offset(desc))
+                     : nullptr;
+  // Xt = X[:, perm_R]
+  PX_HIP(permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
+  // A = Xt Diag(G_R)
+  PX_HIP(apply(at, at, w.Xt, ldm, rows, m, b, at, gR1, nullptr, at, w.A, ldm, s));
+  // H = A W~ (int8: codes times the column scale)
+  PX_HIP(gemm(at, at, w.A, ldm, wt, Wt, lead(n), true, rows, n, m, scale_t, at, H_save, ldn, s));
+  // Zt = H Diag(G_P)
+  PX_HIP(apply(at, at, H_save, ldn, rows, n, b, at, gP1, nullptr, at, w.Zt, ldn, s));
+  // Y[:, perm_P] = Zt, i.e. Y = Zt[:, perm_P^{-1}]
+  PX_HIP(inverse_perm(perm_P, n, w.invP, s));
+  PX_HIP(permute(at, w.Zt, ldn, nullptr, w.invP, Y, n, rows, n, n, s));
+  return POETX_OK;
+}
+
+poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+                              const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
+                              const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX,
+                              float* dq_R, float* dq_P, void* ws, size_t ws_bytes, void* stream) {
+  poetx_status st = check_desc(desc);
+  if (st != POETX_OK) return st;
+  if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
+  if (!perm_R || !perm_P || !Wt || !g_R || !g_P || !q_R || !q_P || !dq_R || !dq_P)
+    return fail(POETX_E_NULL, "a required pointer is NULL");
+  if (T > 0 && (!X || !dZ || !H_save || !dX)) return fail(POETX_E_NULL, "a required pointer is NULL");
+  Plan p;
+  plan_bwd(p, desc, T);
+  st = check_ws(ws, ws_bytes, p.off);
+  if (st != POETX_OK) return st;
+  Plan pq;
+  pq.base = reinterpret_cast<char*>(ws);
+  const BwdWs w = plan_bwd(pq, desc, T);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, wt = desc->w_dtype;
+  const int rows = (int)T;
+  const int64_t ldm = lead(m), ldn = lead(n);
+  const float* scale_t =
+      wt == POETX_I8 ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(Wt) + weight_scale_offset(desc))
+                     : nullptr;
+  if (rows > 0) {
+    // dZt = dZ[:, perm_P]
+    PX_HIP(permute(at, dZ, n, nullptr, perm_P, w.dZt, ldn, rows, n, n, s));
+    // dH = dZt Diag(G_P)^T (int8: times the column scale, ready for the code contraction)
+    PX_HIP(apply(at, at, w.dZt, ldn, rows, n, b, at, g_P, scale_t, at, w.dH, ldn, s));
+    // dG_P = H^T dZt per block (split over tokens)
+    PX_HIP(dgrad(at, H_save, ldn, w.dZt, ldn, rows, n, b, w.splitsP, w.partP, s));
+    // dA = dH W~^T
+    PX_HIP(gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
+    // Xt = X[:, perm_R];  dG_R = Xt^T dA per block
+    PX_HIP(permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
+    PX_HIP(dgrad(at, w.Xt, ldm, w.dA, ldm, rows, m, b, w.splitsR, w.partR, s));
+    // dXt = dA Diag(G_R)^T;  dX[:, perm_R] = dXt
+    PX_HIP(apply(at, at, w.dA, ldm, rows, m, b, at, g_R, nullptr, at, w.dXt, ldm, s));
+    PX_HIP(inverse_perm(perm_R, m, w.invR, s));
+    PX_HIP(permute(at, w.dXt, ldm, nullptr, w.invR, dX, m, rows, m, m, s));
+  } else {
+    PX_HIP(fill_zero(w.partP, (size_t)w.splitsP * nblocks(n, b) * b * b * 4, s));
+    PX_HIP(fill_zero(w.partR, (size_t)w.splitsR * nblocks(m, b) * b * b * 4, s));
+  }
+  // CNP chain rule and skew projection, one side at a time (shared scratch)
+  PX_HIP(cnp_backward(at, q_P, n, b, w.partP, w.splitsP, w.cnp, dq_P, s));
+  PX_HIP(cnp_backward(at, q_R, m, b, w.partR, w.splitsR, w.cnp, dq_R, s));
+  return POETX_OK;
+}
+
+poetx_status poetx_merge_reinit(const poetx_layer_desc* desc, void* Wt, int32_t* perm_R, int32_t* perm_P,
+                                const void* g_R, const void* g_P, float* q_R, float* q_P, uint64_t seed_R,
+                                uint64_t seed_P, void* ws, size_t ws_bytes, void* stream) {
+  poetx_status st = check_desc(desc);
+  if (st != POETX_OK) return st;
+  if (!Wt || !perm_R || !perm_P || !g_R || !g_P || !q_R || !q_P) return fail(POETX_E_NULL, "a required pointer is NULL");
+  Plan p;
+  plan_merge(p, desc);
+  st = check_ws(ws, ws_bytes, p.off);
+  if (st != POETX_OK) return st;
+  Plan pq;
+  pq.base = reinterpret_cast<char*>(ws);
+  const MergeWs w = plan_merge(pq, desc);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, wt = desc->w_dtype;
+  const int64_t ldw = lead(n);
+  float* scale_t =
+      wt == POETX_I8 ? reinterpret_cast<float*>(reinterpret_cast<char*>(Wt) + weight_scale_offset(desc)) : nullptr;
+  const char* gP1 = reinterpret_cast<const char*>(g_P) + g_slice(n, b, at);
+  // M1 = Diag(G_R) W~ (dequantised), then M = M1 Diag(G_P)
+  PX_HIP(merge_left(at, g_R, wt, Wt, ldw, scale_t, m, n, b, w.Mq, ldw, s));
+  PX_HIP(apply(F32, F32, w.Mq, ldw, m, n, b, at, gP1, nullptr, F32, w.M, ldw, s));
+  // new permutations; rho = old^{-1} o new maps new pre-merged positions to old ones
+  PX_HIP(perm_from_seed_device(seed_R, m, w.newR, w.fy, s));
+  PX_HIP(perm_from_seed_device(seed_P, n, w.newP, w.fy, s));
+  PX_HIP(inverse_perm(perm_R, m, w.invR, s));
+  PX_HIP(inverse_perm(perm_P, n, w.invP, s));
+  PX_HIP(compose_perm(w.invR, w.newR, m, w.rhoR, s));
+  PX_HIP(compose_perm(w.invP, w.newP, n, w.rhoP, s));
+  PX_HIP(permute(F32, w.M, ldw, w.rhoR, w.rhoP, w.Mq, ldw, m, n, n, s));
+  if (wt == POETX_I8) {
+    PX_HIP(fill_zero(w.amax, (size_t)n * 4, s));
+    PX_HIP(col_absmax(w.Mq, ldw, m, n, w.amax, s));
+  }
+  PX_HIP(store_weight(w.Mq, ldw, m, n, wt, Wt, ldw, w.amax, scale_t, s));
+  PX_HIP(hipMemcpyAsync(perm_R, w.newR, (size_t)m * 4, hipMemcpyDeviceToDevice, s));
+  PX_HIP(hipMemcpyAsync(perm_P, w.newP, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
+  PX_HIP(fill_zero(q_R, (size_t)nblocks(m, b) * packed_len(b) * 4, s));
+  PX_HIP(fill_zero(q_P, (size_t)nblocks(n, b) * packed_len(b) * 4, s));
+  return POETX_OK;
+}
+
+}  // extern "C"

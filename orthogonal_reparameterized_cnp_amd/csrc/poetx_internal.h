@@ -1,0 +1,67 @@
+// Internal launchers shared by the C ABI layer (not part of the public API).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pxk {
+
+enum Dt : int { F32 = 0, BF16 = 1, I8 = 2 };
+
+inline size_t dt_size(int dt) { return dt == F32 ? 4 : dt == BF16 ? 2 : 1; }
+inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+inline int64_t packed_len(int64_t b) { return b * (b - 1) / 2; }
+inline int nblocks(int d, int b) { return (d + b - 1) / b; }
+
+// Leading dimension of every [rows x d] buffer the library lays out itself
+// (pre-merged weight, saved activation, workspace matrices): a multiple of 64
+// elements, so rows start 128-byte aligned for bf16 and 256-byte for fp32.
+inline int64_t lead(int d) { return round_up(d, 64); }
+
+// out[t][i] = in[rowmap ? rowmap[t] : t][colmap[i]] for t < rows, i < d_out.
+hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap, const int32_t* colmap, void* out,
+                   int64_t ld_out, int rows, int d_in, int d_out, hipStream_t s);
+// inv[perm[i]] = i
+hipError_t inverse_perm(const int32_t* perm, int d, int32_t* inv, hipStream_t s);
+// out[i] = a[b[i]]
+hipError_t compose_perm(const int32_t* a, const int32_t* b, int d, int32_t* out, hipStream_t s);
+// Durstenfeld shuffle of the identity driven by SplitMix64(seed)
+hipError_t perm_from_seed_device(uint64_t seed, int d, int32_t* out, int32_t* scratch, hipStream_t s);
+
+// Delta = G - I of every block of one side, and its transpose:
+// g = [2][nb][b][b] in dtype dt (F32 or BF16); S_ws = [nb][b][b] fp32 scratch.
+hipError_t cnp_build(int dt, const float* q, int d, int b, void* g, float* S_ws, hipStream_t s);
+
+// Row-form block-diagonal product: out[:, kb+j] = (in[:, kb+j] + sum_k in[:, kb+k] D_blk[k][j]) * scale[kb+j]
+// where the B operand array `dT` holds D_blk^T, i.e. dT[blk][j][k] = D_blk[k][j].
+// Compute dtype cdt; `in`, `dT`, `out` in their own dtypes.
+hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, int d, int b, int dT_dt, const void* dT,
+                 const float* colscale, int out_dt, void* out, int64_t ld_out, hipStream_t s);
+
+// out = A * B (* colscale), A: [M][K] rows (lda); B either [K][N] (b_kn = true) or [N][K] (b_kn = false).
+hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const void* B, int64_t ldb, bool b_kn, int M,
+                int N, int K, const float* colscale, int out_dt, void* out, int64_t ldo, hipStream_t s);
+
+// part[s][blk][i][j] = sum_{t in split s} A[t][kb+i] * B[t][kb+j]  (fp32, all b x b entries written)
+hipError_t dgrad(int cdt, const void* A, int64_t lda, const void* B, int64_t ldb, int rows, int d, int b, int splits,
+                 float* part, hipStream_t s);
+int dgrad_splits(int rows, int d, int b);
+
+// CNP chain rule for one side: dG partials -> packed dq (overwritten).
+// ws6 holds 7 fp32 [nb][b][b] arrays.
+hipError_t cnp_backward(int cdt, const float* q, int d, int b, const float* part, int splits, float* ws7, float* dq,
+                        hipStream_t s);
+
+// Merge helpers (fp32 MFMA).
+// M1[kb+i][c] = (W[kb+i][c] + sum_k DeltaR_blk[i][k] W[kb+k][c]) * wscale[c]
+hipError_t merge_left(int g_dt, const void* gR, int w_dt, const void* W, int64_t ldw, const float* wscale, int m, int n,
+                      int b, float* M1, int64_t ldm, hipStream_t s);
+// column absmax of M [rows][ld] over rows, as float bits (max over non-negative floats)
+hipError_t col_absmax(const float* M, int64_t ld, int rows, int n, uint32_t* amax, hipStream_t s);
+// write the final weight from fp32 values: f32/bf16 round, or int8 requantisation with fresh scales
+hipError_t store_weight(const float* M, int64_t ld, int rows, int n, int w_dt, void* W, int64_t ldw,
+                        const uint32_t* amax, float* wscale, hipStream_t s);
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
+
+}  // namespace pxk

@@ -1,0 +1,708 @@
+// HIP kernels of libpoetx for gfx950 and their typed launchers.
+//
+// Every dense contraction of the layer (CNP block squares, block-diagonal
+// products, the W~ contractions, the block gradients and the CNP chain rule)
+// is an instance of the LDS-staged MFMA tile loop in mfma_tile.h with a
+// suitable pair of operand loaders and an epilogue.  Permutations are index
+// arrays applied by row-staged gathers through LDS.
+#include "mfma_tile.h"
+#include "poetx_internal.h"
+
+using namespace px;
+
+namespace {
+
+// ----------------------------------------------------------------------------
+// tile shapes
+// ----------------------------------------------------------------------------
+using TBig = Tile<256, 128, 64, 2, 2>;  // bf16: W~ contractions and block products over tokens
+using TSq = Tile<128, 128, 64, 2, 2>;   // bf16: block gradients, CNP (b x b outputs)
+using TF = Tile<64, 64, 32, 2, 2>;      // fp32: small layers
+using TFM = Tile<128, 128, 32, 2, 2>;   // fp32: merge products
+
+template <class C> PX_DEV AccPos<C> acc_pos() {
+  const int w = threadIdx.x >> 6;
+  return AccPos<C>{w / C::WN, w % C::WN, (int)(threadIdx.x & 63)};
+}
+
+template <class C, class F> PX_DEV void each_acc(const Acc<C>& acc, F&& f) {
+  const AccPos<C> p = acc_pos<C>();
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int c = p.col(j);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) f(p.row(i, e), c, acc.v[i][j][e]);
+    }
+}
+
+template <typename T> struct DT;
+template <> struct DT<float> { static constexpr int v = pxk::F32; };
+template <> struct DT<bf16_t> { static constexpr int v = pxk::BF16; };
+template <> struct DT<int8_t> { static constexpr int v = pxk::I8; };
+
+// Kernels whose static LDS use exceeds the default 64 KB limit must opt in once.
+template <typename K> hipError_t allow_lds(K kernel, int bytes) {
+  if (bytes <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+// ----------------------------------------------------------------------------
+// skew-block value functors (absolute indices; zero outside the live r x r block)
+// ----------------------------------------------------------------------------
+struct QRow {  // Q[i][k]
+  const float* qk;
+  int r, b;
+  PX_DEV float operator()(int i, int k) const { return skew_at(qk, i, k, r, b); }
+};
+struct QCol {  // (row n, K index k) -> Q[k][n]
+  const float* qk;
+  int r, b;
+  PX_DEV float operator()(int n, int k) const { return skew_at(qk, k, n, r, b); }
+};
+struct NCol {  // (row n, K index k) -> N[k][n] with N = 2Q + S, S = Q^2
+  const float* qk;
+  const float* S;
+  int r, b;
+  PX_DEV float operator()(int n, int k) const {
+    if (n >= r || k >= r) return 0.f;
+    return 2.f * skew_at(qk, k, n, r, b) + S[(int64_t)k * b + n];
+  }
+};
+
+// ============================================================================
+// CNP build: S = Q^2, then Delta = G - I = 2Q + 2S + S (2Q + S)
+// ============================================================================
+template <class C, typename T>
+__global__ __launch_bounds__(C::NT) void k_cnp_square(const float* __restrict__ q, int d, int b, float* __restrict__ S) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+  const int blk = blockIdx.z, r = min(b, d - blk * b);
+  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
+  if (m0 >= r || n0 >= r) return;  // S is only read inside the live corner
+  const float* qk = q + (int64_t)blk * ((int64_t)b * (b - 1) / 2);
+  LoadGen<C::BM, C::BK, C::NT, T, QRow> la{QRow{qk, r, b}, m0};
+  LoadGen<C::BN, C::BK, C::NT, T, QCol> lb{QCol{qk, r, b}, n0};
+  Acc<C> acc;
+  const AccPos<C> p = acc_pos<C>();
+  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
+  float* Sb = S + (int64_t)blk * b * b;
+  each_acc<C>(acc, [&](int i, int j, float v) {
+    i += m0;
+    j += n0;
+    if (i < r && j < r) Sb[(int64_t)i * b + j] = v;
+  });
+}
+
+template <class C, typename T>
+__global__ __launch_bounds__(C::NT) void k_cnp_delta(const float* __restrict__ q, int d, int b, int nb,
+                                                      const float* __restrict__ S, T* __restrict__ g) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+  const int blk = blockIdx.z, r = min(b, d - blk * b);
+  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
+  const float* qk = q + (int64_t)blk * ((int64_t)b * (b - 1) / 2);
+  const float* Sb = S + (int64_t)blk * b * b;
+  LoadK<C::BM, C::BK, C::NT, float, T> la;
+  la.init(Sb + (int64_t)m0 * b, b, r - m0, r);
+  LoadGen<C::BN, C::BK, C::NT, T, NCol> lb{NCol{qk, Sb, r, b}, n0};
+  Acc<C> acc;
+  const AccPos<C> p = acc_pos<C>();
+  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
+  T* g0 = g + (int64_t)blk * b * b;
+  T* g1 = g + ((int64_t)nb + blk) * b * b;
+  each_acc<C>(acc, [&](int i, int j, float v) {
+    i += m0;
+    j += n0;
+    if (i < b && j < b) {
+      float o = 0.f;
+      if (i < r && j < r) o = v + 2.f * skew_at(qk, i, j, r, b) + 2.f * Sb[(int64_t)i * b + j];
+      const T t = from_f32<T>(o);
+      g0[(int64_t)i * b + j] = t;
+      g1[(int64_t)j * b + i] = t;
+    }
+  });
+}
+
+// ============================================================================
+// block-diagonal product over token rows, identity added in fp32:
+//   out[t][kb+j] = (in[t][kb+j] + sum_k in[t][kb+k] dT[blk][j][k]) * scale[kb+j]
+// ============================================================================
+template <class C, typename T, typename IT, typename GT, typename OT>
+__global__ __launch_bounds__(C::NT) void k_apply(const IT* __restrict__ in, int64_t ld_in, int rows, int d, int b,
+                                                  const GT* __restrict__ dT, const float* __restrict__ colscale,
+                                                  OT* __restrict__ out, int64_t ld_out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+  const int blk = blockIdx.z, kb = blk * b, r = min(b, d - kb);
+  const int m0 = blockIdx.x * C::BM, n0 = blockIdx.y * C::BN;
+  if (n0 >= r) return;
+  LoadK<C::BM, C::BK, C::NT, IT, T> la;
+  la.init(in + (int64_t)m0 * ld_in + kb, ld_in, rows - m0, r);
+  LoadK<C::BN, C::BK, C::NT, GT, T> lb;
+  lb.init(dT + ((int64_t)blk * b + n0) * b, b, r - n0, r);
+  Acc<C> acc;
+  const AccPos<C> p = acc_pos<C>();
+  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
+  each_acc<C>(acc, [&](int i, int j, float v) {
+    const int t = m0 + i, c = n0 + j;
+    if (t < rows && c < r) {
+      const int64_t col = kb + c;
+      v += to_f32<IT>(in[(int64_t)t * ld_in + col]);
+      if (colscale) v *= colscale[col];
+      out[(int64_t)t * ld_out + col] = from_f32<OT>(v);
+    }
+  });
+}
+
+// ============================================================================
+// plain contraction out = A * B (* colscale)
+// ============================================================================
+template <class C, typename T, typename AT, typename BT, typename OT, bool BKN>
+__global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_t lda, const BT* __restrict__ B,
+                                                 int64_t ldb, int M, int N, int K, const float* __restrict__ colscale,
+                                                 OT* __restrict__ out, int64_t ldo) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+  const int m0 = blockIdx.x * C::BM, n0 = blockIdx.y * C::BN;
+  LoadK<C::BM, C::BK, C::NT, AT, T> la;
+  la.init(A + (int64_t)m0 * lda, lda, M - m0, K);
+  using LB = typename std::conditional<BKN, LoadMN<C::BN, C::BK, C::NT, BT, T>, LoadK<C::BN, C::BK, C::NT, BT, T>>::type;
+  LB lb;
+  if constexpr (BKN)
+    lb.init(B + n0, ldb, N - n0, K);
+  else
+    lb.init(B + (int64_t)n0 * ldb, ldb, N - n0, K);
+  Acc<C> acc;
+  const AccPos<C> p = acc_pos<C>();
+  mainloop<C, T>(lds, la, lb, K, acc, p.wm, p.wn, p.lane);
+  each_acc<C>(acc, [&](int i, int j, float v) {
+    const int mm = m0 + i, nn = n0 + j;
+    if (mm < M && nn < N) {
+      if (colscale) v *= colscale[nn];
+      out[(int64_t)mm * ldo + nn] = from_f32<OT>(v);
+    }
+  });
+}
+
+// ============================================================================
+// block gradients: part[s][blk][i][j] = sum_{t in split s} A[t][kb+i] B[t][kb+j]
+// ============================================================================
+template <class C, typename T, typename IT>
+__global__ __launch_bounds__(C::NT) void k_dgrad(const IT* __restrict__ A, int64_t lda, const IT* __restrict__ B,
+                                                  int64_t ldb, int rows, int d, int b, int tchunk,
+                                                  float* __restrict__ part) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+  const int tiles_n = (b + C::BN - 1) / C::BN;
+  const int m0 = (blockIdx.x / tiles_n) * C::BM, n0 = (blockIdx.x % tiles_n) * C::BN;
+  const int blk = blockIdx.y, nb = gridDim.y, s = blockIdx.z;
+  const int kb = blk * b, r = min(b, d - kb);
+  const int t0 = s * tchunk, t1 = min(rows, t0 + tchunk);
+  const int K = max(0, t1 - t0);
+  LoadMN<C::BM, C::BK, C::NT, IT, T> la;
+  la.init(A + (int64_t)t0 * lda + kb + m0, lda, r - m0, K);
+  LoadMN<C::BN, C::BK, C::NT, IT, T> lb;
+  lb.init(B + (int64_t)t0 * ldb + kb + n0, ldb, r - n0, K);
+  Acc<C> acc;
+  const AccPos<C> p = acc_pos<C>();
+  mainloop<C, T>(lds, la, lb, K, acc, p.wm, p.wn, p.lane);
+  float* out = part + ((int64_t)s * nb + blk) * b * b;
+  each_acc<C>(acc, [&](int i, int j, float v) {
+    i += m0;
+    j += n0;
+    if (i < b && j < b) out[(int64_t)i * b + j] = v;
+  });
+}
+
+// U[e] = sum_s part[s][e] in split order (deterministic)
+__global__ void k_reduce_splits(const float* __restrict__ part, int splits, int64_t n, float* __restrict__ U) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  float s = 0.f;
+  for (int k = 0; k < splits; ++k) s += part[(int64_t)k * n + e];
+  U[e] = s;
+}
+
+// ============================================================================
+// CNP chain rule.  With U = dL/dG of a block, V1 = U Q, V2 = V1 Q, V3 = V2 Q:
+//   dQ = X0 + Q (X1 + Q (X2 + Q X3)),
+//   X0 = 2U - 2V1 + 2V2 - V3, X1 = -2U + 2V1 - V2, X2 = 2U - V1, X3 = -U,
+// which is the ten-term adjoint of G = I + 2(Q + Q^2 + Q^3) + Q^4 (Q^T = -Q)
+// grouped by powers of Q on the left.  Steps 0..2 form V1..V3, steps 3..5 the
+// nested products Y1 = X2 - Q U, Y2 = X1 + Q Y1, dQ = X0 + Q Y2.
+// ============================================================================
+template <class C, typename T, int STEP>
+__global__ __launch_bounds__(C::NT) void k_cnp_bwd(const float* __restrict__ q, int d, int b,
+                                                    const float* __restrict__ ws, int64_t bb_all,
+                                                    float* __restrict__ out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+  const int blk = blockIdx.z, r = min(b, d - blk * b);
+  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
+  const float* qk = q + (int64_t)blk * ((int64_t)b * (b - 1) / 2);
+  const int64_t off = (int64_t)blk * b * b;
+  // ws arrays: 0 U, 1 V1, 2 V2, 3 V3, 4 Y1, 5 Y2, 6 dQ
+  const float* U = ws + 0 * bb_all + off;
+  const float* V1 = ws + 1 * bb_all + off;
+  const float* V2 = ws + 2 * bb_all + off;
+  const float* V3 = ws + 3 * bb_all + off;
+  const float* Y1 = ws + 4 * bb_all + off;
+  const float* Y2 = ws + 5 * bb_all + off;
+  Acc<C> acc;
+  const AccPos<C> p = acc_pos<C>();
+  if constexpr (STEP <= 2) {
+    const float* src = STEP == 0 ? U : STEP == 1 ? V1 : V2;
+    LoadK<C::BM, C::BK, C::NT, float, T> la;
+    la.init(src + (int64_t)m0 * b, b, r - m0, r);
+    LoadGen<C::BN, C::BK, C::NT, T, QCol> lb{QCol{qk, r, b}, n0};
+    mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
+  } else {
+    const float* src = STEP == 3 ? U : STEP == 4 ? Y1 : Y2;
+    LoadGen<C::BM, C::BK, C::NT, T, QRow> la{QRow{qk, r, b}, m0};
+    LoadMN<C::BN, C::BK, C::NT, float, T> lb;
+    lb.init(src + n0, b, r - n0, r);
+    mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
+  }
+  float* o = out + off;
+  each_acc<C>(acc, [&](int i, int j, float v) {
+    i += m0;
+    j += n0;
+    if (i >= b || j >= b) return;
+    const int64_t e = (int64_t)i * b + j;
+    float res;
+    if constexpr (STEP <= 2) {
+      res = v;
+    } else if constexpr (STEP == 3) {
+      res = 2.f * U[e] - V1[e] - v;
+    } else if constexpr (STEP == 4) {
+      res = -2.f * U[e] + 2.f * V1[e] - V2[e] + v;
+    } else {
+      res = 2.f * U[e] - 2.f * V1[e] + 2.f * V2[e] - V3[e] + v;
+    }
+    o[e] = (i < r && j < r) ? res : 0.f;
+  });
+}
+
+// dq[blk][p(i,j)] = dQ[i][j] - dQ[j][i] for i < j < r, 0 for dead slots
+__global__ void k_pack_dq(const float* __restrict__ dQ, int d, int b, float* __restrict__ dq) {
+  const int blk = blockIdx.y, r = min(b, d - blk * b);
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)b * b) return;
+  const int i = (int)(e / b), j = (int)(e % b);
+  if (i >= j) return;
+  const float* Qb = dQ + (int64_t)blk * b * b;
+  const float v = (j < r) ? Qb[(int64_t)i * b + j] - Qb[(int64_t)j * b + i] : 0.f;
+  dq[(int64_t)blk * ((int64_t)b * (b - 1) / 2) + packed_slot(i, j, b)] = v;
+}
+
+// ============================================================================
+// permutations
+// ============================================================================
+// Row-staged gather: the workgroup copies whole source rows into LDS with
+// coalesced loads, then writes each output row coalesced, reading LDS at the
+// permuted positions.  Indices are clamped into range so that a malformed
+// permutation cannot address outside the staged rows.
+template <typename E>
+__global__ __launch_bounds__(256) void k_permute_lds(const E* __restrict__ in, int64_t ld_in,
+                                                     const int32_t* __restrict__ rowmap,
+                                                     const int32_t* __restrict__ colmap, E* __restrict__ out,
+                                                     int64_t ld_out, int rows, int d_in, int d_out, int rpw) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* buf = reinterpret_cast<E*>(smem);
+  const int t0 = blockIdx.x * rpw;
+  const int nr = min(rpw, rows - t0);
+  for (int rr = 0; rr < nr; ++rr) {
+    int src = t0 + rr;
+    if (rowmap) src = min(max(rowmap[src], 0), rows - 1);
+    const E* row = in + (int64_t)src * ld_in;
+    for (int i = threadIdx.x; i < d_in; i += blockDim.x) buf[rr * d_in + i] = row[i];
+  }
+  __syncthreads();
+  for (int rr = 0; rr < nr; ++rr) {
+    E* o = out + (int64_t)(t0 + rr) * ld_out;
+    for (int i = threadIdx.x; i < d_out; i += blockDim.x) {
+      const int c = min(max(colmap[i], 0), d_in - 1);
+      o[i] = buf[rr * d_in + c];
+    }
+  }
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void k_permute_direct(const E* __restrict__ in, int64_t ld_in,
+                                                        const int32_t* __restrict__ rowmap,
+                                                        const int32_t* __restrict__ colmap, E* __restrict__ out,
+                                                        int64_t ld_out, int rows, int d_in, int d_out) {
+  const int t = blockIdx.x;
+  int src = t;
+  if (rowmap) src = min(max(rowmap[t], 0), rows - 1);
+  for (int i = threadIdx.x; i < d_out; i += blockDim.x) {
+    const int c = min(max(colmap[i], 0), d_in - 1);
+    out[(int64_t)t * ld_out + i] = in[(int64_t)src * ld_in + c];
+  }
+}
+
+__global__ void k_inverse_perm(const int32_t* __restrict__ perm, int d, int32_t* __restrict__ inv) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < d) inv[min(max(perm[i], 0), d - 1)] = i;
+}
+
+__global__ void k_compose_perm(const int32_t* __restrict__ a, const int32_t* __restrict__ bm, int d,
+                               int32_t* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < d) out[i] = a[min(max(bm[i], 0), d - 1)];
+}
+
+// SplitMix64 output number k (0-based) of the stream seeded with `seed`:
+// the state after k + 1 golden-ratio increments, through the finaliser.
+PX_DEV uint64_t splitmix64_at(uint64_t seed, uint64_t k) {
+  uint64_t z = seed + (k + 1) * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// Durstenfeld shuffle.  The swap partners j_i = floor(u * (i + 1) / 2^64),
+// with u the (d-1-i)-th output, are drawn in parallel; the swaps themselves are
+// inherently sequential and are made by one lane in LDS (or in global memory
+// when d does not fit).
+__global__ __launch_bounds__(256) void k_perm_shuffle(uint64_t seed, int d, int32_t* __restrict__ out,
+                                                      int32_t* __restrict__ jglob, int use_lds) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t* p = use_lds ? reinterpret_cast<int32_t*>(smem) : out;
+  int32_t* jb = use_lds ? reinterpret_cast<int32_t*>(smem) + d : jglob;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    p[i] = i;
+    if (i >= 1) jb[i] = (int32_t)__umul64hi(splitmix64_at(seed, (uint64_t)(d - 1 - i)), (uint64_t)(i + 1));
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int i = d - 1; i >= 1; --i) {
+      const int j = jb[i];
+      const int32_t a = p[i], c = p[j];
+      p[i] = c;
+      p[j] = a;
+    }
+  }
+  __syncthreads();
+  if (use_lds)
+    for (int i = threadIdx.x; i < d; i += blockDim.x) out[i] = p[i];
+}
+
+// ============================================================================
+// merge-then-reinitialise
+// ============================================================================
+// M1[kb+i][c] = (W[kb+i][c] + sum_k DeltaR[blk][i][k] W[kb+k][c]) * wscale[c]
+template <class C, typename GT, typename WT>
+__global__ __launch_bounds__(C::NT) void k_merge_left(const GT* __restrict__ gR, const WT* __restrict__ W, int64_t ldw,
+                                                       const float* __restrict__ wscale, int m, int n, int b,
+                                                       float* __restrict__ M1, int64_t ldm) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* lds = reinterpret_cast<float*>(smem);
+  const int blk = blockIdx.z, kb = blk * b, r = min(b, m - kb);
+  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
+  if (m0 >= r) return;
+  LoadK<C::BM, C::BK, C::NT, GT, float> la;
+  la.init(gR + ((int64_t)blk * b + m0) * b, b, r - m0, r);
+  LoadMN<C::BN, C::BK, C::NT, WT, float> lb;
+  lb.init(W + (int64_t)kb * ldw + n0, ldw, n - n0, r);
+  Acc<C> acc;
+  const AccPos<C> p = acc_pos<C>();
+  mainloop<C, float>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
+  each_acc<C>(acc, [&](int i, int j, float v) {
+    const int ii = m0 + i, c = n0 + j;
+    if (ii < r && c < n) {
+      v += to_f32<WT>(W[(int64_t)(kb + ii) * ldw + c]);
+      if (wscale) v *= wscale[c];
+      M1[(int64_t)(kb + ii) * ldm + c] = v;
+    }
+  });
+}
+
+__global__ void k_col_absmax(const float* __restrict__ M, int64_t ld, int rows, int n, int rows_per,
+                             uint32_t* __restrict__ amax) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n) return;
+  const int r0 = blockIdx.y * rows_per, r1 = min(rows, r0 + rows_per);
+  float mx = 0.f;
+  for (int r = r0; r < r1; ++r) mx = fmaxf(mx, fabsf(M[(int64_t)r * ld + c]));
+  // non-negative floats order like their bit patterns, so max is exact and order-free
+  atomicMax(amax + c, __float_as_uint(mx));
+}
+
+PX_DEV float int8_scale(uint32_t amax_bits) {
+  const float a = __uint_as_float(amax_bits);
+  return a == 0.f ? 1.f : a / 127.f;
+}
+
+template <typename WT>
+__global__ void k_store_weight(const float* __restrict__ M, int64_t ld, int rows, int n, WT* __restrict__ W,
+                               int64_t ldw, const uint32_t* __restrict__ amax, float* __restrict__ wscale) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n) return;
+  float s = 1.f;
+  if constexpr (sizeof(WT) == 1) {
+    s = int8_scale(amax[c]);
+    if (blockIdx.y == 0) wscale[c] = s;
+  }
+  for (int r = blockIdx.y; r < rows; r += gridDim.y) {
+    const float v = M[(int64_t)r * ld + c];
+    if constexpr (sizeof(WT) == 1) {
+      float code = rintf(v / s);
+      code = fminf(fmaxf(code, -127.f), 127.f);
+      W[(int64_t)r * ldw + c] = (int8_t)code;
+    } else {
+      W[(int64_t)r * ldw + c] = from_f32<WT>(v);
+    }
+  }
+}
+
+__global__ void k_fill_zero(uint8_t* __restrict__ p, size_t bytes) {
+  const size_t n16 = bytes / 16;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    reinterpret_cast<uint4*>(p)[i] = make_uint4(0, 0, 0, 0);
+  const size_t tail = bytes - n16 * 16;
+  if (blockIdx.x == 0 && threadIdx.x < tail) p[n16 * 16 + threadIdx.x] = 0;
+}
+
+inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
+
+}  // namespace
+
+// ============================================================================
+// launchers
+// ============================================================================
+namespace pxk {
+
+hipError_t fill_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<size_t>(4096, (bytes / 16 + 255) / 256 + 1);
+  k_fill_zero<<<grid, 256, 0, s>>>(reinterpret_cast<uint8_t*>(p), bytes);
+  return hipGetLastError();
+}
+
+hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap, const int32_t* colmap, void* out,
+                   int64_t ld_out, int rows, int d_in, int d_out, hipStream_t s) {
+  if (rows <= 0 || d_out <= 0) return hipSuccess;
+  const size_t es = dt_size(dt);
+  const size_t row_bytes = (size_t)d_in * es;
+  const size_t budget = 64 * 1024;
+  auto go = [&](auto tag) -> hipError_t {
+    using E = decltype(tag);
+    if (row_bytes <= budget) {
+      const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, budget / row_bytes));
+      k_permute_lds<E><<<cdiv(rows, rpw), 256, rpw * row_bytes, s>>>(
+          reinterpret_cast<const E*>(in), ld_in, rowmap, colmap, reinterpret_cast<E*>(out), ld_out, rows, d_in, d_out,
+          rpw);
+    } else {
+      k_permute_direct<E><<<rows, 256, 0, s>>>(reinterpret_cast<const E*>(in), ld_in, rowmap, colmap,
+                                               reinterpret_cast<E*>(out), ld_out, rows, d_in, d_out);
+    }
+    return hipGetLastError();
+  };
+  if (dt == F32) return go(float{});
+  if (dt == BF16) return go(bf16_t{});
+  return go(int8_t{});
+}
+
+hipError_t inverse_perm(const int32_t* perm, int d, int32_t* inv, hipStream_t s) {
+  k_inverse_perm<<<cdiv(d, 256), 256, 0, s>>>(perm, d, inv);
+  return hipGetLastError();
+}
+
+hipError_t compose_perm(const int32_t* a, const int32_t* b, int d, int32_t* out, hipStream_t s) {
+  k_compose_perm<<<cdiv(d, 256), 256, 0, s>>>(a, b, d, out);
+  return hipGetLastError();
+}
+
+hipError_t perm_from_seed_device(uint64_t seed, int d, int32_t* out, int32_t* scratch, hipStream_t s) {
+  const size_t lds = (size_t)d * 8;
+  const int use_lds = lds <= 160 * 1024;
+  if (use_lds) {
+    hipError_t e = allow_lds(k_perm_shuffle, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  k_perm_shuffle<<<1, 256, use_lds ? lds : 0, s>>>(seed, d, out, scratch, use_lds);
+  return hipGetLastError();
+}
+
+template <class C, typename T> static hipError_t cnp_build_t(const float* q, int d, int b, T* g, float* S, hipStream_t s) {
+  const int nb = nblocks(d, b);
+  const int lds = Lay<C, T>::BYTES;
+  hipError_t e = allow_lds(k_cnp_square<C, T>, lds);
+  if (e == hipSuccess) e = allow_lds(k_cnp_delta<C, T>, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), nb);
+  k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(q, d, b, S);
+  k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(q, d, b, nb, S, g);
+  return hipGetLastError();
+}
+
+hipError_t cnp_build(int dt, const float* q, int d, int b, void* g, float* S_ws, hipStream_t s) {
+  if (dt == BF16) return cnp_build_t<TSq, bf16_t>(q, d, b, reinterpret_cast<bf16_t*>(g), S_ws, s);
+  return cnp_build_t<TF, float>(q, d, b, reinterpret_cast<float*>(g), S_ws, s);
+}
+
+template <class C, typename T, typename IT, typename GT, typename OT>
+static hipError_t apply_t(const void* in, int64_t ld_in, int rows, int d, int b, const void* dT, const float* cs,
+                          void* out, int64_t ld_out, hipStream_t s) {
+  const int lds = Lay<C, T>::BYTES;
+  auto k = k_apply<C, T, IT, GT, OT>;
+  hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(cdiv(rows, C::BM), cdiv(b, C::BN), nblocks(d, b));
+  k<<<grid, C::NT, lds, s>>>(reinterpret_cast<const IT*>(in), ld_in, rows, d, b, reinterpret_cast<const GT*>(dT), cs,
+                             reinterpret_cast<OT*>(out), ld_out);
+  return hipGetLastError();
+}
+
+hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, int d, int b, int dT_dt, const void* dT,
+                 const float* colscale, int out_dt, void* out, int64_t ld_out, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (cdt == BF16 && in_dt == BF16 && dT_dt == BF16 && out_dt == BF16)
+    return apply_t<TBig, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+  if (cdt == F32 && in_dt == F32 && dT_dt == F32 && out_dt == F32)
+    return apply_t<TF, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+  // merge products: fp32 rows times the stored blocks
+  if (cdt == F32 && in_dt == F32 && dT_dt == BF16 && out_dt == F32)
+    return apply_t<TFM, float, float, bf16_t, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+  if (cdt == F32 && in_dt == F32 && dT_dt == F32 && out_dt == F32)
+    return apply_t<TFM, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+  return hipErrorInvalidValue;
+}
+
+template <class C, typename T, typename AT, typename BT, typename OT, bool BKN>
+static hipError_t gemm_t(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K, const float* cs,
+                         void* out, int64_t ldo, hipStream_t s) {
+  const int lds = Lay<C, T>::BYTES;
+  auto k = k_gemm<C, T, AT, BT, OT, BKN>;
+  hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(cdiv(M, C::BM), cdiv(N, C::BN));
+  k<<<grid, C::NT, lds, s>>>(reinterpret_cast<const AT*>(A), lda, reinterpret_cast<const BT*>(B), ldb, M, N, K, cs,
+                             reinterpret_cast<OT*>(out), ldo);
+  return hipGetLastError();
+}
+
+hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const void* B, int64_t ldb, bool b_kn, int M,
+                int N, int K, const float* colscale, int out_dt, void* out, int64_t ldo, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (cdt == BF16 && a_dt == BF16 && out_dt == BF16) {
+    if (b_dt == BF16)
+      return b_kn ? gemm_t<TBig, bf16_t, bf16_t, bf16_t, bf16_t, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
+                  : gemm_t<TBig, bf16_t, bf16_t, bf16_t, bf16_t, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
+    if (b_dt == I8)
+      return b_kn ? gemm_t<TBig, bf16_t, bf16_t, int8_t, bf16_t, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
+                  : gemm_t<TBig, bf16_t, bf16_t, int8_t, bf16_t, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
+  }
+  if (cdt == F32 && a_dt == F32 && b_dt == F32 && out_dt == F32)
+    return b_kn ? gemm_t<TF, float, float, float, float, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
+                : gemm_t<TF, float, float, float, float, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
+  return hipErrorInvalidValue;
+}
+
+int dgrad_splits(int rows, int d, int b) {
+  const int nb = nblocks(d, b);
+  const int t = (b + 127) / 128;
+  const int tiles = t * t * nb;
+  int splits = (1024 + tiles - 1) / tiles;
+  splits = std::min(splits, std::max(1, rows / 256));
+  return std::max(1, std::min(splits, 64));
+}
+
+template <class C, typename T>
+static hipError_t dgrad_t(const void* A, int64_t lda, const void* B, int64_t ldb, int rows, int d, int b, int splits,
+                          float* part, hipStream_t s) {
+  const int lds = Lay<C, T>::BYTES;
+  auto k = k_dgrad<C, T, T>;
+  hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+  int tchunk = (rows + splits - 1) / splits;
+  tchunk = (int)round_up(std::max(tchunk, 1), C::BK);
+  dim3 grid(cdiv(b, C::BM) * cdiv(b, C::BN), nblocks(d, b), splits);
+  k<<<grid, C::NT, lds, s>>>(reinterpret_cast<const T*>(A), lda, reinterpret_cast<const T*>(B), ldb, rows, d, b,
+                             tchunk, part);
+  return hipGetLastError();
+}
+
+hipError_t dgrad(int cdt, const void* A, int64_t lda, const void* B, int64_t ldb, int rows, int d, int b, int splits,
+                 float* part, hipStream_t s) {
+  if (cdt == BF16) return dgrad_t<TSq, bf16_t>(A, lda, B, ldb, rows, d, b, splits, part, s);
+  return dgrad_t<TF, float>(A, lda, B, ldb, rows, d, b, splits, part, s);
+}
+
+template <class C, typename T>
+static hipError_t cnp_backward_t(const float* q, int d, int b, const float* part, int splits, float* ws, float* dq,
+                                 hipStream_t s) {
+  const int nb = nblocks(d, b);
+  const int64_t bb_all = (int64_t)nb * b * b;
+  k_reduce_splits<<<cdiv(bb_all, 256), 256, 0, s>>>(part, splits, bb_all, ws);
+  const int lds = Lay<C, T>::BYTES;
+  dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), nb);
+  hipError_t e = hipSuccess;
+#define PX_STEP(K, OUT)                                                          \
+  e = allow_lds(k_cnp_bwd<C, T, K>, lds);                                        \
+  if (e != hipSuccess) return e;                                                 \
+  k_cnp_bwd<C, T, K><<<grid, C::NT, lds, s>>>(q, d, b, ws, bb_all, ws + (OUT) * bb_all);
+  PX_STEP(0, 1)
+  PX_STEP(1, 2)
+  PX_STEP(2, 3)
+  PX_STEP(3, 4)
+  PX_STEP(4, 5)
+  PX_STEP(5, 6)
+#undef PX_STEP
+  dim3 pg(cdiv((int64_t)b * b, 256), nb);
+  k_pack_dq<<<pg, 256, 0, s>>>(ws + 6 * bb_all, d, b, dq);
+  return hipGetLastError();
+}
+
+hipError_t cnp_backward(int cdt, const float* q, int d, int b, const float* part, int splits, float* ws7, float* dq,
+                        hipStream_t s) {
+  if (cdt == BF16) return cnp_backward_t<TSq, bf16_t>(q, d, b, part, splits, ws7, dq, s);
+  return cnp_backward_t<TF, float>(q, d, b, part, splits, ws7, dq, s);
+}
+
+template <typename GT, typename WT>
+static hipError_t merge_left_t(const void* gR, const void* W, int64_t ldw, const float* wscale, int m, int n, int b,
+                               float* M1, int64_t ldm, hipStream_t s) {
+  using C = TFM;
+  const int lds = Lay<C, float>::BYTES;
+  auto k = k_merge_left<C, GT, WT>;
+  hipError_t e = allow_lds(k, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(cdiv(n, C::BN), cdiv(b, C::BM), nblocks(m, b));
+  k<<<grid, C::NT, lds, s>>>(reinterpret_cast<const GT*>(gR), reinterpret_cast<const WT*>(W), ldw, wscale, m, n, b,
+                             M1, ldm);
+  return hipGetLastError();
+}
+
+hipError_t merge_left(int g_dt, const void* gR, int w_dt, const void* W, int64_t ldw, const float* wscale, int m, int n,
+                      int b, float* M1, int64_t ldm, hipStream_t s) {
+  if (g_dt == F32 && w_dt == F32) return merge_left_t<float, float>(gR, W, ldw, wscale, m, n, b, M1, ldm, s);
+  if (g_dt == BF16 && w_dt == BF16) return merge_left_t<bf16_t, bf16_t>(gR, W, ldw, wscale, m, n, b, M1, ldm, s);
+  if (g_dt == BF16 && w_dt == I8) return merge_left_t<bf16_t, int8_t>(gR, W, ldw, wscale, m, n, b, M1, ldm, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t col_absmax(const float* M, int64_t ld, int rows, int n, uint32_t* amax, hipStream_t s) {
+  const int rows_per = 256;
+  dim3 grid(cdiv(n, 256), cdiv(rows, rows_per));
+  k_col_absmax<<<grid, 256, 0, s>>>(M, ld, rows, n, rows_per, amax);
+  return hipGetLastError();
+}
+
+hipError_t store_weight(const float* M, int64_t ld, int rows, int n, int w_dt, void* W, int64_t ldw,
+                        const uint32_t* amax, float* wscale, hipStream_t s) {
+  dim3 grid(cdiv(n, 256), std::min(rows, 4096));
+  if (w_dt == F32)
+    k_store_weight<float><<<grid, 256, 0, s>>>(M, ld, rows, n, reinterpret_cast<float*>(W), ldw, amax, wscale);
+  else if (w_dt == BF16)
+    k_store_weight<bf16_t><<<grid, 256, 0, s>>>(M, ld, rows, n, reinterpret_cast<bf16_t*>(W), ldw, amax, wscale);
+  else
+    k_store_weight<int8_t><<<grid, 256, 0, s>>>(M, ld, rows, n, reinterpret_cast<int8_t*>(W), ldw, amax, wscale);
+  return hipGetLastError();
+}
+
+}  // namespace pxk

@@ -1,0 +1,131 @@
+"""Device buffers of one POET-X linear, allocated with torch, driven through the C ABI.
+
+The class only owns memory and sequences the library calls; all arithmetic is
+done by libpoetx kernels.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "i8": torch.int8}
+
+
+def lead(d: int) -> int:
+    return (d + 63) // 64 * 64
+
+
+class PoetxLinear:
+    def __init__(self, m: int, n: int, b: int, act: str = "bf16", w: str = "bf16", device: str = "cuda"):
+        self.m, self.n, self.b, self.act, self.w = m, n, b, act, w
+        self.device = torch.device(device)
+        self.desc = B.desc(m, n, b, act, w)
+        self.nbR, self.nbP = -(-m // b), -(-n // b)
+        L = b * (b - 1) // 2
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        self.Wt = torch.zeros(B.poetx_weight_bytes(self.desc), **u8)
+        adt = B.DTYPES[act]
+        self.g_R = torch.empty(B.poetx_g_bytes(m, b, adt), **u8)
+        self.g_P = torch.empty(B.poetx_g_bytes(n, b, adt), **u8)
+        self.q_R = torch.zeros(self.nbR, L, dtype=torch.float32, device=self.device)
+        self.q_P = torch.zeros(self.nbP, L, dtype=torch.float32, device=self.device)
+        self.perm_R = torch.arange(m, dtype=torch.int32, device=self.device)
+        self.perm_P = torch.arange(n, dtype=torch.int32, device=self.device)
+        self.ws = torch.empty(0, **u8)
+        self.H_save: Optional[torch.Tensor] = None
+        self.T = 0
+
+    # -- buffers ------------------------------------------------------------
+    def _ws(self, nbytes: int) -> torch.Tensor:
+        if self.ws.numel() < nbytes:
+            self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.ws
+
+    def ws_bytes(self, T: int) -> int:
+        d = self.desc
+        return max(
+            B.poetx_workspace_size(d, T, B.POETX_OP_FWD),
+            B.poetx_workspace_size(d, T, B.POETX_OP_BWD),
+            B.poetx_workspace_size(d, 0, B.POETX_OP_MERGE),
+            B.poetx_workspace_size(B.desc(max(self.m, self.n), 1, self.b, self.act, self.w), 0, B.POETX_OP_CNP),
+        )
+
+    def reserve(self, T: int):
+        self._ws(self.ws_bytes(T))
+        if self.H_save is None or self.H_save.numel() < B.poetx_saved_bytes(self.desc, T):
+            self.H_save = torch.empty(B.poetx_saved_bytes(self.desc, T), dtype=torch.uint8, device=self.device)
+
+    # -- state --------------------------------------------------------------
+    def load(self, W0: torch.Tensor, w_scale: Optional[torch.Tensor], perm_R, perm_P, q_R, q_P, stream=None):
+        """Natural-layout W0 [m][n] (+ int8 column scales) and factor state -> pre-merged layout."""
+        self.perm_R.copy_(perm_R)
+        self.perm_P.copy_(perm_P)
+        self.q_R.copy_(q_R)
+        self.q_P.copy_(q_P)
+        B.poetx_premerge(self.desc, W0, W0.stride(0), w_scale, self.perm_R, self.perm_P, self.Wt, stream)
+
+    def weight_values(self) -> torch.Tensor:
+        """View of the pre-merged weight values [m][lead(n)] (padding columns included)."""
+        ldw = lead(self.n)
+        es = {"f32": 4, "bf16": 2, "i8": 1}[self.w]
+        return self.Wt[: self.m * ldw * es].view(_TORCH_DT[self.w]).view(self.m, ldw)
+
+    def weight_scales(self) -> torch.Tensor:
+        ldw = lead(self.n)
+        off = (self.m * ldw + 255) // 256 * 256
+        return self.Wt[off : off + 4 * ldw].view(torch.float32)
+
+    def g_slices(self, side: str):
+        d, g = (self.m, self.g_R) if side == "R" else (self.n, self.g_P)
+        nb = -(-d // self.b)
+        dt = _TORCH_DT[self.act]
+        return g.view(dt).view(2, nb, self.b, self.b)
+
+    # -- calls --------------------------------------------------------------
+    def build(self, stream=None):
+        adt = B.DTYPES[self.act]
+        for q, d, g in ((self.q_R, self.m, self.g_R), (self.q_P, self.n, self.g_P)):
+            need = B.poetx_workspace_size(B.desc(d, 1, self.b, self.act, self.w), 0, B.POETX_OP_CNP)
+            ws = self._ws(need)
+            B.poetx_cnp_build(q, d, self.b, adt, g, ws, ws.numel(), stream)
+
+    def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        T = X.shape[0]
+        self.reserve(T)
+        if Y is None:
+            Y = torch.empty(T, self.n, dtype=X.dtype, device=self.device)
+        B.poetx_linear_fwd(self.desc, T, X, self.perm_R, self.perm_P, self.Wt, self.g_R, self.g_P, Y, self.H_save,
+                           self.ws, self.ws.numel(), stream)
+        self.T = T
+        return Y
+
+    def backward(self, X: torch.Tensor, dZ: torch.Tensor, dX=None, dq_R=None, dq_P=None, stream=None):
+        T = X.shape[0]
+        self.reserve(T)
+        if dX is None:
+            dX = torch.empty(T, self.m, dtype=X.dtype, device=self.device)
+        if dq_R is None:
+            dq_R = torch.empty_like(self.q_R)
+        if dq_P is None:
+            dq_P = torch.empty_like(self.q_P)
+        B.poetx_linear_bwd(self.desc, T, X, dZ, self.perm_R, self.perm_P, self.Wt, self.g_R, self.g_P, self.q_R,
+                           self.q_P, self.H_save, dX, dq_R, dq_P, self.ws, self.ws.numel(), stream)
+        return dX, dq_R, dq_P
+
+    def merge_reinit(self, seed_R: int, seed_P: int, stream=None):
+        ws = self._ws(B.poetx_workspace_size(self.desc, 0, B.POETX_OP_MERGE))
+        B.poetx_merge_reinit(self.desc, self.Wt, self.perm_R, self.perm_P, self.g_R, self.g_P, self.q_R, self.q_P,
+                             seed_R, seed_P, ws, ws.numel(), stream)
+
+    def merged_f32(self) -> torch.Tensor:
+        """fp32 merged weight before rounding, left at the start of the workspace by merge_reinit."""
+        ldw = lead(self.n)
+        return self.ws[: self.m * ldw * 4].view(torch.float32).view(self.m, ldw)
+
+    def saved_H(self, T: int) -> torch.Tensor:
+        dt = _TORCH_DT[self.act]
+        return self.H_save.view(dt)[: T * lead(self.n)].view(T, lead(self.n))

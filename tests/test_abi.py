@@ -1,0 +1,81 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header
+declares, the host helpers compute what they document, and invalid arguments
+are rejected with the documented status before any device work.  The device
+pointers passed here are never dereferenced: every call returns in validation."""
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle as O
+from orthogonal_reparameterized_cnp_amd import binding as B
+
+
+@pytest.fixture(scope="module")
+def L():
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = B.header_symbols()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_host_helpers(L):
+    assert B.poetx_version().startswith("libpoetx")
+    assert B.poetx_packed_len(512) == 130816 and B.poetx_packed_len(1) == 0
+    # G buffer: [2][nb][b][b]
+    assert B.poetx_g_bytes(1376, 256, B.POETX_BF16) == 2 * 6 * 256 * 256 * 2
+    assert B.poetx_g_bytes(256, 32, B.POETX_F32) == 2 * 8 * 32 * 32 * 4
+    assert B.poetx_g_bytes(256, 32, B.POETX_I8) == 0
+    d = B.desc(1024, 5461, 256, "bf16", "i8")
+    ldw = 5504
+    assert B.poetx_weight_bytes(d) == (1024 * ldw + 255) // 256 * 256 + 4 * ldw
+    assert B.poetx_saved_bytes(d, 10) == 10 * ldw * 2
+    for op in (B.POETX_OP_FWD, B.POETX_OP_BWD, B.POETX_OP_MERGE):
+        assert B.poetx_workspace_size(d, 100, op) > 0
+    assert B.poetx_workspace_size(B.desc(1024, 5461, 1, "bf16", "bf16"), 100, B.POETX_OP_FWD) == 0
+
+
+@pytest.mark.parametrize("seed,d", [(0, 1), (1, 2), (123, 1376), (2**64 - 1, 5461), (42, 14336)])
+def test_perm_from_seed_matches_oracle(seed, d):
+    np.testing.assert_array_equal(B.poetx_perm_from_seed(seed, d), O.perm_from_seed(seed, d))
+
+
+FAKE = 1 << 20  # an aligned non-null address that validation never dereferences
+
+
+def _fwd(L, dsc, T=4, X=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return L.poetx_linear_fwd(ctypes.byref(dsc), T, X, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_validation_statuses(L):
+    good = B.desc(256, 256, 32, "f32", "f32")
+    assert _fwd(L, B.desc(256, 256, 1, "f32", "f32")) == B.POETX_E_SHAPE
+    assert _fwd(L, B.desc(0, 256, 32, "f32", "f32")) == B.POETX_E_SHAPE
+    assert _fwd(L, B.desc(256, 256, 32, "f32", "bf16")) == B.POETX_E_DTYPE
+    assert _fwd(L, B.desc(256, 256, 32, "bf16", "f32")) == B.POETX_E_DTYPE
+    assert _fwd(L, good, T=-1) == B.POETX_E_SHAPE
+    assert _fwd(L, good, X=None) == B.POETX_E_NULL
+    assert "NULL" in B.poetx_last_error()
+    assert _fwd(L, good, ws_bytes=16) == B.POETX_E_WORKSPACE
+    assert _fwd(L, good, ws=FAKE + 8) == B.POETX_E_WORKSPACE
+    assert _fwd(L, good, T=0) == B.POETX_OK  # empty batch: nothing to do
+    assert L.poetx_linear_fwd(None, 4, *([FAKE] * 9), 1 << 40, None) == B.POETX_E_NULL
+    # backward / merge / build / premerge
+    args = [FAKE] * 13
+    assert L.poetx_linear_bwd(ctypes.byref(good), 4, *args[:4], None, *args[5:13], FAKE, 16, None) == B.POETX_E_NULL
+    assert L.poetx_linear_bwd(ctypes.byref(good), 4, *args, FAKE, 16, None) == B.POETX_E_WORKSPACE
+    assert L.poetx_merge_reinit(ctypes.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 2, FAKE, 1 << 40, None) == B.POETX_E_NULL
+    assert L.poetx_cnp_build(FAKE, 256, 32, B.POETX_I8, FAKE, FAKE, 1 << 30, None) == B.POETX_E_DTYPE
+    assert L.poetx_cnp_build(FAKE, 256, 1, B.POETX_F32, FAKE, FAKE, 1 << 30, None) == B.POETX_E_SHAPE
+    assert L.poetx_cnp_build(FAKE, 256, 32, B.POETX_F32, FAKE, FAKE, 8, None) == B.POETX_E_WORKSPACE
+    i8 = B.desc(256, 256, 32, "bf16", "i8")
+    assert L.poetx_premerge(ctypes.byref(i8), FAKE, 256, None, FAKE, FAKE, FAKE, None) == B.POETX_E_NULL
+    assert L.poetx_premerge(ctypes.byref(good), FAKE, 100, None, FAKE, FAKE, FAKE, None) == B.POETX_E_SHAPE
+    out = (ctypes.c_int32 * 4)()
+    assert L.poetx_perm_from_seed(1, 0, out) == B.POETX_E_SHAPE
+    assert L.poetx_perm_from_seed(1, 4, None) == B.POETX_E_NULL

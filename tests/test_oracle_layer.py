@@ -219,3 +219,13 @@ def test_quantize_int8_decisions():
     # dequantised error is at most half a step
     deq = code.astype(np.float64) * scale.astype(np.float64)[None, :]
     assert np.all(np.abs(deq - W) <= 0.5 * scale[None, :] * (1 + 1e-6))
+
+
+def test_block_grads_match_full_backward():
+    m, n, b, T = 13, 10, 4, 6
+    p = _problem(m, n, b, T, 0.2, 31)
+    g = O.backward(p["X"], p["dZ"], p["W"], p["perm_R"], p["perm_P"], p["q_R"], p["q_P"], b)
+    sel = O.block_grads(p["X"], p["dZ"], p["W"], p["perm_R"], p["perm_P"], p["q_R"], p["q_P"], b, [0, 3], [2])
+    np.testing.assert_allclose(sel[("R", 0)], g.dq_R[0], atol=1e-14)
+    np.testing.assert_allclose(sel[("R", 3)], g.dq_R[3], atol=1e-14)
+    np.testing.assert_allclose(sel[("P", 2)], g.dq_P[2], atol=1e-14)
