@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of the POET-X linear layer (fwd + bwd) on one MI355X.
+
+One step is the whole hot path over one batch: the CNP blocks of both sides of
+every linear of a Llama-8B decoder layer (poetx_cnp_build), the forward of the
+seven linears (q, k, v, o, gate, up, down), then their backward with the CNP
+chain rule down to packed dq.  T = 8192 tokens, b = 512, bf16 activations and
+weights with fp32 accumulation.  Inputs are seeded synthetic tensors already
+resident in HBM when timing starts.
+
+Prints one JSON line: tokens/s of the whole step, the roofline figure of the
+dominant kernel class (the W~ contractions) from hipEvents recorded around its
+launches during the timed steps, and the fp64 CPU oracle timed on a bounded
+sample of the same workload as a baseline.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--workload llama8b]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # dense MFMA: 256 CU x 2.4 GHz x 4096 (bf16) / 256 (fp32) flop/clk
+HBM_PEAK_GBS = 8000.0
+METRIC = "POET-X linear fwd+bwd tokens/s at Llama-8B shapes; % MFMA peak (1 GPU)"
+
+
+def side_sums(d, b):
+    nb = -(-d // b)
+    r = d - (nb - 1) * b
+    return (nb - 1) * b * b + r * r, (nb - 1) * b**3 + r**3
+
+
+def step_flops(wl, T):
+    """Algorithmic flops of one fwd+bwd step: W~ contractions, block products, CNP."""
+    gemm = apply = cnp = 0.0
+    for L in wl.linears:
+        gemm += 4.0 * T * L.m * L.n
+        r2R, r3R = side_sums(L.m, wl.b)
+        r2P, r3P = side_sums(L.n, wl.b)
+        apply += 6.0 * T * (r2R + r2P)  # fwd R, P; bwd P apply, P grad, R grad, R apply
+        cnp += 16.0 * (r3R + r3P)  # build (2 products) + chain rule (6 products)
+    return gemm, apply, cnp
+
+
+def describe(wl):
+    shapes = ", ".join(f"{L.name} {L.m}x{L.n}" for L in wl.linears)
+    return f"{wl.description}: linears {shapes}"
+
+
+def cpu_baseline(inp, wl, lin_flops, total_flops):
+    """fp64 oracle, untuned, on one linear of the workload at full T; scaled to
+    the whole layer by algorithmic flops."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+
+    X = O.to_f64(inp.X, inp.act)
+    dZ = O.to_f64(inp.dZ, inp.act)
+    W = O.to_f64(inp.W0, inp.w, inp.w_scale)
+    q_R, q_P = inp.q_R.astype(np.float64), inp.q_P.astype(np.float64)
+    t0 = time.perf_counter()
+    G_R, G_P = O.side_G(q_R, inp.m, inp.b), O.side_G(q_P, inp.n, inp.b)
+    O.forward(X, W, inp.perm_R, inp.perm_P, G_R, G_P)
+    O.backward(X, dZ, W, inp.perm_R, inp.perm_P, q_R, q_P, inp.b)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    layer_seconds = dt * total_flops / lin_flops
+    return {
+        "value": inp.T / layer_seconds,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (
+            f"linear {inp.m}x{inp.n} of the same layer, all {inp.T} tokens, fwd + bwd incl. CNP "
+            f"({dt:.1f} s); scaled to the 7-linear layer by algorithmic flops x{total_flops / lin_flops:.2f}"
+        ),
+        "seconds": dt,
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="per kernel class timings on stderr")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from orthogonal_reparameterized_cnp_amd import binding as B
+    from orthogonal_reparameterized_cnp_amd.layer import PoetxLinear
+    from workloads import WORKLOADS, make_linear_inputs
+
+    B.lib()
+    wl = WORKLOADS[args.workload]
+    T = wl.T
+    dev = torch.device("cuda:0")
+
+    def to_dev(a, kind):
+        if kind == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    t_gen = time.perf_counter()
+    layers, Xs, dZs, inputs0 = [], [], [], None
+    for i in range(len(wl.linears)):
+        inp = make_linear_inputs(wl, i)
+        lay = PoetxLinear(inp.m, inp.n, inp.b, inp.act, inp.w)
+        scale = to_dev(inp.w_scale, "f32") if inp.w == "i8" else None
+        lay.load(to_dev(inp.W0, inp.w), scale, to_dev(inp.perm_R, "i32"), to_dev(inp.perm_P, "i32"),
+                 to_dev(inp.q_R, "f32"), to_dev(inp.q_P, "f32"))
+        lay.reserve(T)
+        layers.append(lay)
+        Xs.append(to_dev(inp.X, inp.act))
+        dZs.append(to_dev(inp.dZ, inp.act))
+        if i == 0:
+            inputs0 = inp
+    Ys = [torch.empty(T, L.n, dtype=Xs[0].dtype, device=dev) for L in wl.linears]
+    dXs = [torch.empty(T, L.m, dtype=Xs[0].dtype, device=dev) for L in wl.linears]
+    dqs = [(torch.empty_like(l.q_R), torch.empty_like(l.q_P)) for l in layers]
+    torch.cuda.synchronize()
+    print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    def step():
+        for lay in layers:
+            lay.build()
+        for lay, X, Y in zip(layers, Xs, Ys):
+            lay.forward(X, Y)
+        for lay, X, dZ, dX, (dqR, dqP) in zip(reversed(layers), reversed(Xs), reversed(dZs), reversed(dXs),
+                                              reversed(dqs)):
+            lay.backward(X, dZ, dX, dqR, dqP)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    gemm_f, apply_f, cnp_f = step_flops(wl, T)
+    total_f = gemm_f + apply_f + cnp_f
+    B.poetx_timer_enable(B.POETX_KC_GEMM)
+    B.poetx_timer_read()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    n_launch, k_ms, k_flops, k_bytes = B.poetx_timer_read()
+    B.poetx_timer_enable(B.POETX_KC_NONE)
+
+    peak = PEAK_TFLOPS[wl.act]
+    achieved = k_flops / (k_ms * 1e-3) / 1e12 if k_ms > 0 else 0.0
+    result = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.act,
+        "data": "synthetic (seeded normalized-Gaussian W0, N(0,1) X and dZ, N(0, std^2) packed q)",
+        "config": {
+            "workload": describe(wl),
+            "tokens": T,
+            "b": wl.b,
+            "weights": wl.w,
+        },
+        "tflops": total_f / (ms * 1e-3) / 1e12,
+        "mfma_peak_frac": total_f / (ms * 1e-3) / 1e12 / peak,
+        "step_tflop": {"w_contractions": gemm_f / 1e12, "block_products": apply_f / 1e12, "cnp": cnp_f / 1e12},
+        "roofline": {
+            "kernel": "W~ contractions (k_gemm, forward NN-with-transpose and backward NT)",
+            "bound": "mfma",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+            "launches": n_launch,
+            "avg_launch_ms": k_ms / max(n_launch, 1),
+            "algorithmic_gb_per_launch": k_bytes / max(n_launch, 1) / 1e9,
+        },
+        "wall_s_timed": wall,
+    }
+
+    if args.breakdown:
+        for name, kc in (("gemm", B.POETX_KC_GEMM), ("apply", B.POETX_KC_APPLY), ("dgrad", B.POETX_KC_DGRAD),
+                         ("cnp", B.POETX_KC_CNP), ("permute", B.POETX_KC_PERMUTE)):
+            B.poetx_timer_enable(kc)
+            B.poetx_timer_read()
+            step()
+            torch.cuda.synchronize()
+            n, kms, kf, kb = B.poetx_timer_read()
+            B.poetx_timer_enable(B.POETX_KC_NONE)
+            rate = kf / (kms * 1e-3) / 1e12 if kms else 0
+            bw = kb / (kms * 1e-3) / 1e9 if kms else 0
+            print(f"[bench] {name:8s} launches={n:3d} ms/step={kms:8.3f} TFLOP/s={rate:7.1f} "
+                  f"alg GB/s={bw:7.1f}", file=sys.stderr, flush=True)
+
+    if not args.no_cpu_baseline:
+        lin_f = 4.0 * T * inputs0.m * inputs0.n
+        r2R, r3R = side_sums(inputs0.m, wl.b)
+        r2P, r3P = side_sums(inputs0.n, wl.b)
+        lin_f += 6.0 * T * (r2R + r2P) + 16.0 * (r3R + r3P)
+        result["cpu_baseline"] = cpu_baseline(inputs0, wl, lin_f, total_f)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,7 +33,8 @@
  *  - The library never allocates device memory: scratch space is the caller's
  *    `ws` buffer of at least poetx_workspace_size() bytes, 256-byte aligned.
  *    Calls that share a workspace must not overlap in time.
- *  - The library keeps no state between calls except a per-thread error string.
+ *  - The library keeps no state between calls except a per-thread error string
+ *    and, while it is enabled, the measurement timer's record.
  *  - Formats the library lays out itself (pre-merged weight, G blocks, saved
  *    activation) are sized by the *_bytes() helpers; their leading dimensions
  *    are rounded up to a multiple of 64 elements.
@@ -116,6 +117,26 @@ size_t poetx_workspace_size(const poetx_layer_desc* desc, int64_t T, int32_t op)
  * for the next 64-bit output u, swap p[i] and p[j].  host_out: [d] host memory.
  * Errors: POETX_E_NULL, POETX_E_SHAPE (d < 1). */
 poetx_status poetx_perm_from_seed(uint64_t seed, int32_t d, int32_t* host_out);
+
+/* Kernel classes for the measurement timer. */
+typedef enum {
+  POETX_KC_NONE = 0,
+  POETX_KC_GEMM = 1,    /* the W~ contractions (forward and backward) */
+  POETX_KC_APPLY = 2,   /* block-diagonal products over token rows */
+  POETX_KC_DGRAD = 3,   /* block gradients summed over tokens */
+  POETX_KC_CNP = 4,     /* CNP build and chain rule */
+  POETX_KC_PERMUTE = 5  /* permutation gathers */
+} poetx_kernel_class;
+
+/* Measurement support (not for use on a hot path).  While a class is enabled,
+ * every launch of that class, on any stream, is bracketed by two hipEvents
+ * recorded on the launch's stream, and its algorithmic flop and byte counts
+ * are noted.  poetx_timer_read waits for the recorded events, returns the
+ * number of launches, their summed duration in milliseconds and the summed
+ * algorithmic flops and bytes, and clears the record.  kernel_class 0
+ * disables.  Errors: POETX_E_SHAPE (unknown class), POETX_E_NULL, POETX_E_HIP. */
+poetx_status poetx_timer_enable(int32_t kernel_class);
+poetx_status poetx_timer_read(int64_t* launches, double* total_ms, double* flops, double* bytes);
 
 /* ------------------------------------------------------------- the calls -- */
 

@@ -24,6 +24,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "poetx.h")
 POETX_OK, POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_PERM, POETX_E_HIP, POETX_E_UNSUPPORTED = range(8)
 POETX_F32, POETX_BF16, POETX_I8 = 0, 1, 2
 POETX_OP_CNP, POETX_OP_FWD, POETX_OP_BWD, POETX_OP_MERGE = 0, 1, 2, 3
+POETX_KC_NONE, POETX_KC_GEMM, POETX_KC_APPLY, POETX_KC_DGRAD, POETX_KC_CNP, POETX_KC_PERMUTE = range(6)
 
 DTYPES = {"f32": POETX_F32, "bf16": POETX_BF16, "i8": POETX_I8}
 
@@ -65,6 +66,12 @@ _SIG = {
     "poetx_linear_bwd": (
         ctypes.c_int,
         [ctypes.POINTER(LayerDesc), ctypes.c_int64] + [_P] * 14 + [ctypes.c_size_t, _P],
+    ),
+    "poetx_timer_enable": (ctypes.c_int, [ctypes.c_int32]),
+    "poetx_timer_read": (
+        ctypes.c_int,
+        [ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+         ctypes.POINTER(ctypes.c_double)],
     ),
     "poetx_merge_reinit": (
         ctypes.c_int,
@@ -160,6 +167,17 @@ def poetx_perm_from_seed(seed: int, d: int):
     out = np.empty(d, dtype=np.int32)
     _check(lib().poetx_perm_from_seed(seed, d, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
     return out
+
+
+def poetx_timer_enable(kernel_class: int):
+    _check(lib().poetx_timer_enable(kernel_class))
+
+
+def poetx_timer_read():
+    """(launches, total_ms, flops, bytes) of the enabled class since the last read."""
+    n, ms, fl, by = ctypes.c_int64(), ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(lib().poetx_timer_read(ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl), ctypes.byref(by)))
+    return n.value, ms.value, fl.value, by.value
 
 
 # ------------------------------------------------------------- the calls ---

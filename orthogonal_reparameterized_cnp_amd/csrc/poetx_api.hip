@@ -1,7 +1,9 @@
 // C ABI of libpoetx: argument validation, workspace planning and the order of
 // kernel launches for each call.  All arithmetic happens in the kernels of
 // poetx_kernels.hip.
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/poetx.h"
 #include "poetx_internal.h"
@@ -12,10 +14,67 @@ namespace {
 
 thread_local std::string g_err;
 
+// ---------------------------------------------------------------------------
+// measurement timer: hipEvents around the launches of one kernel class
+// ---------------------------------------------------------------------------
+struct TimerRec {
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+struct Timer {
+  std::mutex mu;
+  int cls = 0;
+  std::vector<TimerRec> recs;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Timer& timer() {
+  static Timer t;
+  return t;
+}
+
+struct Timed {
+  bool on = false;
+  hipStream_t s;
+  TimerRec rec{};
+  Timed(int cls, hipStream_t s_, double flops, double bytes) : s(s_) {
+    Timer& t = timer();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (t.cls == 0 || t.cls != cls) return;
+    rec.a = t.get();
+    rec.b = t.get();
+    if (!rec.a || !rec.b) return;
+    rec.flops = flops;
+    rec.bytes = bytes;
+    on = hipEventRecord(rec.a, s) == hipSuccess;
+  }
+  ~Timed() {
+    if (!on) return;
+    Timer& t = timer();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (hipEventRecord(rec.b, s) == hipSuccess) t.recs.push_back(rec);
+  }
+};
+
 poetx_status fail(poetx_status st, const std::string& msg) {
   g_err = msg;
   return st;
 }
+
+#define PX_TIMED(cls, flops, bytes, expr)       \
+  do {                                          \
+    Timed t_((cls), s, (double)(flops), (double)(bytes)); \
+    PX_HIP(expr);                               \
+  } while (0)
 
 #define PX_HIP(expr)                                                                         \
   do {                                                                                       \
@@ -51,6 +110,16 @@ struct Plan {
 };
 
 size_t g_slice(int d, int b, int dt) { return (size_t)nblocks(d, b) * b * b * dt_size(dt); }
+
+// sum over a side's blocks of r^2 and r^3 (algorithmic flop counts)
+double sum_r2(int d, int b) {
+  const double r = d - (double)(nblocks(d, b) - 1) * b;
+  return (nblocks(d, b) - 1) * (double)b * b + r * r;
+}
+double sum_r3(int d, int b) {
+  const double r = d - (double)(nblocks(d, b) - 1) * b;
+  return (nblocks(d, b) - 1) * (double)b * b * b + r * r * r;
+}
 
 size_t weight_scale_offset(const poetx_layer_desc* d) {
   return (size_t)round_up((int64_t)d->m * lead(d->n) * (int64_t)dt_size(d->w_dtype), 256);
@@ -185,6 +254,38 @@ poetx_status poetx_perm_from_seed(uint64_t seed, int32_t d, int32_t* out) {
   return POETX_OK;
 }
 
+poetx_status poetx_timer_enable(int32_t kernel_class) {
+  if (kernel_class < POETX_KC_NONE || kernel_class > POETX_KC_PERMUTE) return fail(POETX_E_SHAPE, "unknown kernel class");
+  Timer& t = timer();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.cls = kernel_class;
+  return POETX_OK;
+}
+
+poetx_status poetx_timer_read(int64_t* launches, double* total_ms, double* flops, double* bytes) {
+  if (!launches || !total_ms || !flops || !bytes) return fail(POETX_E_NULL, "output pointers must be non-NULL");
+  Timer& t = timer();
+  std::lock_guard<std::mutex> g(t.mu);
+  double ms = 0, fl = 0, by = 0;
+  poetx_status st = POETX_OK;
+  for (const TimerRec& r : t.recs) {
+    float e = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&e, r.a, r.b) != hipSuccess)
+      st = fail(POETX_E_HIP, "event timing failed");
+    ms += e;
+    fl += r.flops;
+    by += r.bytes;
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  *launches = (int64_t)t.recs.size();
+  *total_ms = ms;
+  *flops = fl;
+  *bytes = by;
+  t.recs.clear();
+  return st;
+}
+
 poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype, void* g, void* ws, size_t ws_bytes,
                              void* stream) {
   if (!q || !g) return fail(POETX_E_NULL, "q and g must be non-NULL");
@@ -193,7 +294,9 @@ poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype
   const size_t need = (size_t)round_up((int64_t)nblocks(d, b) * b * b * 4, 256);
   poetx_status st = check_ws(ws, ws_bytes, need);
   if (st != POETX_OK) return st;
-  PX_HIP(cnp_build(dtype, q, d, b, g, reinterpret_cast<float*>(ws), reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PX_TIMED(POETX_KC_CNP, 4 * sum_r3(d, b), 2 * g_slice(d, b, dtype) + 2.0 * nblocks(d, b) * b * b * 4,
+           cnp_build(dtype, q, d, b, g, reinterpret_cast<float*>(ws), s));
   return POETX_OK;
 }
 
@@ -239,17 +342,21 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
   const float* scale_t =
       wt == POETX_I8 ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(Wt) + weight_scale_offset(desc))
                      : nullptr;
+  const double es = (double)dt_size(at), wes = (double)dt_size(wt);
   // Xt = X[:, perm_R]
-  PX_HIP(permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
   // A = Xt Diag(G_R)
-  PX_HIP(apply(at, at, w.Xt, ldm, rows, m, b, at, gR1, nullptr, at, w.A, ldm, s));
+  PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
+           apply(at, at, w.Xt, ldm, rows, m, b, at, gR1, nullptr, at, w.A, ldm, s));
   // H = A W~ (int8: codes times the column scale)
-  PX_HIP(gemm(at, at, w.A, ldm, wt, Wt, lead(n), true, rows, n, m, scale_t, at, H_save, ldn, s));
+  PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
+           gemm(at, at, w.A, ldm, wt, Wt, lead(n), true, rows, n, m, scale_t, at, H_save, ldn, s));
   // Zt = H Diag(G_P)
-  PX_HIP(apply(at, at, H_save, ldn, rows, n, b, at, gP1, nullptr, at, w.Zt, ldn, s));
+  PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
+           apply(at, at, H_save, ldn, rows, n, b, at, gP1, nullptr, at, w.Zt, ldn, s));
   // Y[:, perm_P] = Zt, i.e. Y = Zt[:, perm_P^{-1}]
   PX_HIP(inverse_perm(perm_P, n, w.invP, s));
-  PX_HIP(permute(at, w.Zt, ldn, nullptr, w.invP, Y, n, rows, n, n, s));
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, permute(at, w.Zt, ldn, nullptr, w.invP, Y, n, rows, n, n, s));
   return POETX_OK;
 }
 
@@ -277,29 +384,38 @@ poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const voi
   const float* scale_t =
       wt == POETX_I8 ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(Wt) + weight_scale_offset(desc))
                      : nullptr;
+  const double es = (double)dt_size(at), wes = (double)dt_size(wt);
+  const int nbR = nblocks(m, b), nbP = nblocks(n, b);
   if (rows > 0) {
     // dZt = dZ[:, perm_P]
-    PX_HIP(permute(at, dZ, n, nullptr, perm_P, w.dZt, ldn, rows, n, n, s));
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, permute(at, dZ, n, nullptr, perm_P, w.dZt, ldn, rows, n, n, s));
     // dH = dZt Diag(G_P)^T (int8: times the column scale, ready for the code contraction)
-    PX_HIP(apply(at, at, w.dZt, ldn, rows, n, b, at, g_P, scale_t, at, w.dH, ldn, s));
+    PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
+             apply(at, at, w.dZt, ldn, rows, n, b, at, g_P, scale_t, at, w.dH, ldn, s));
     // dG_P = H^T dZt per block (split over tokens)
-    PX_HIP(dgrad(at, H_save, ldn, w.dZt, ldn, rows, n, b, w.splitsP, w.partP, s));
+    PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + 4.0 * w.splitsP * nbP * b * b,
+             dgrad(at, H_save, ldn, w.dZt, ldn, rows, n, b, w.splitsP, w.partP, s));
     // dA = dH W~^T
-    PX_HIP(gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
+    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * n + wes * m * n + es * rows * m,
+             gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
     // Xt = X[:, perm_R];  dG_R = Xt^T dA per block
-    PX_HIP(permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
-    PX_HIP(dgrad(at, w.Xt, ldm, w.dA, ldm, rows, m, b, w.splitsR, w.partR, s));
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
+    PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + 4.0 * w.splitsR * nbR * b * b,
+             dgrad(at, w.Xt, ldm, w.dA, ldm, rows, m, b, w.splitsR, w.partR, s));
     // dXt = dA Diag(G_R)^T;  dX[:, perm_R] = dXt
-    PX_HIP(apply(at, at, w.dA, ldm, rows, m, b, at, g_R, nullptr, at, w.dXt, ldm, s));
+    PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
+             apply(at, at, w.dA, ldm, rows, m, b, at, g_R, nullptr, at, w.dXt, ldm, s));
     PX_HIP(inverse_perm(perm_R, m, w.invR, s));
-    PX_HIP(permute(at, w.dXt, ldm, nullptr, w.invR, dX, m, rows, m, m, s));
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, w.dXt, ldm, nullptr, w.invR, dX, m, rows, m, m, s));
   } else {
-    PX_HIP(fill_zero(w.partP, (size_t)w.splitsP * nblocks(n, b) * b * b * 4, s));
-    PX_HIP(fill_zero(w.partR, (size_t)w.splitsR * nblocks(m, b) * b * b * 4, s));
+    PX_HIP(fill_zero(w.partP, (size_t)w.splitsP * nbP * b * b * 4, s));
+    PX_HIP(fill_zero(w.partR, (size_t)w.splitsR * nbR * b * b * 4, s));
   }
   // CNP chain rule and skew projection, one side at a time (shared scratch)
-  PX_HIP(cnp_backward(at, q_P, n, b, w.partP, w.splitsP, w.cnp, dq_P, s));
-  PX_HIP(cnp_backward(at, q_R, m, b, w.partR, w.splitsR, w.cnp, dq_R, s));
+  PX_TIMED(POETX_KC_CNP, 12 * sum_r3(n, b), 4.0 * (w.splitsP + 13) * nbP * b * b,
+           cnp_backward(at, q_P, n, b, w.partP, w.splitsP, w.cnp, dq_P, s));
+  PX_TIMED(POETX_KC_CNP, 12 * sum_r3(m, b), 4.0 * (w.splitsR + 13) * nbR * b * b,
+           cnp_backward(at, q_R, m, b, w.partR, w.splitsR, w.cnp, dq_R, s));
   return POETX_OK;
 }
 

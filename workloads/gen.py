@@ -1,10 +1,12 @@
 """Seeded generators for one POET-X linear's inputs.
 
 Every tensor is drawn from numpy's PCG64 seeded by SeedSequence([workload id,
-linear index, tensor id]) with tensor ids 0 = W0, 1 = q_R, 2 = q_P, 3 = X,
-4 = dZ, 5 = perm_R, 6 = perm_P.  Values are drawn in float64 and rounded once
-to the storage type; bf16 tensors are returned as uint16 bit patterns so both
-consumers see identical bits.
+linear index, tensor id, ...]) with tensor ids 0 = W0, 1 = q_R, 2 = q_P, 3 = X,
+4 = dZ, 5 = perm_R, 6 = perm_P.  Matrices are drawn in fixed chunks of 512 rows,
+chunk c from SeedSequence([..., c]), so the values do not depend on how many
+threads fill them.  Values are drawn in float64 and rounded once to the storage
+type; bf16 tensors are returned as uint16 bit patterns so both consumers see
+identical bits.
 
 W0 follows the normalized-Gaussian initialisation of the POET notes
 ("Reparameterized LLM Training via Orthogonal Equivalence Transformation",
@@ -19,8 +21,10 @@ slots of a partial last block that the layer must ignore: they are left
 non-zero on purpose so that both implementations are checked to ignore them.
 """
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
-from typing import Optional
+from typing import Callable, Optional
 
 import numpy as np
 
@@ -34,17 +38,45 @@ def packed_len(b: int) -> int:
     return b * (b - 1) // 2
 
 
+CHUNK_ROWS = 512
+
+
 def _rng(wid: int, lin: int, tensor: int, extra: int = 0) -> np.random.Generator:
     words = [wid, lin, tensor] + ([extra] if extra else [])
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(words)))
 
 
+def _chunked_normal(words, shape, finish: Callable[[np.ndarray], np.ndarray], out_dtype) -> np.ndarray:
+    """N(0, 1) matrix drawn in 512-row chunks (chunk c seeded by words + [c]) in
+    parallel threads; `finish` maps each float64 chunk to its stored form."""
+    rows, cols = shape
+    out = np.empty(shape, dtype=out_dtype)
+    starts = list(range(0, rows, CHUNK_ROWS))
+
+    def fill(c):
+        r0 = starts[c]
+        r1 = min(rows, r0 + CHUNK_ROWS)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(words) + [c])))
+        out[r0:r1] = finish(g.standard_normal((r1 - r0, cols)))
+
+    if len(starts) == 1:
+        fill(0)
+    else:
+        with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+            list(ex.map(fill, range(len(starts))))
+    return out
+
+
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (round to nearest, ties to even); uint16 bits."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    bias = ((u >> 16) & 1) + 0x7FFF
-    return ((u + bias) >> 16).astype(np.uint16)
+    """Round float32 values to bfloat16 (round to nearest, ties to even); uint16 bits.
+    Exact for every finite input: the largest finite pattern plus the rounding
+    bias stays below 2^32, so 32-bit arithmetic does not wrap."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -79,17 +111,21 @@ class LinearInputs:
     dZ: Optional[np.ndarray]  # [T, n] float32 or uint16
 
 
-def normalized_gaussian(rng: np.random.Generator, m: int, n: int) -> np.ndarray:
-    g = rng.standard_normal((m, n))
-    return g / np.linalg.norm(g, axis=0, keepdims=True)
+def normalized_gaussian(words, m: int, n: int, dtype: str) -> np.ndarray:
+    g = _chunked_normal(words, (m, n), lambda c: c, np.float64)
+    g /= np.linalg.norm(g, axis=0, keepdims=True)
+    return _store(g, dtype)
 
 
-def int8_gaussian(rng: np.random.Generator, m: int, n: int):
-    g = rng.standard_normal((m, n))
-    codes = np.clip(np.rint(g * (127.0 / 4.0)), -127, 127)
-    norms = np.linalg.norm(codes, axis=0)
+def int8_gaussian(words, m: int, n: int):
+    codes = _chunked_normal(words, (m, n), lambda c: np.clip(np.rint(c * (127.0 / 4.0)), -127, 127), np.int8)
+    norms = np.sqrt(np.einsum("ij,ij->j", codes, codes, dtype=np.float64))
     norms[norms == 0] = 1.0
-    return codes.astype(np.int8), (1.0 / norms).astype(np.float32)
+    return codes, (1.0 / norms).astype(np.float32)
+
+
+def _act_matrix(words, T: int, d: int, dtype: str) -> np.ndarray:
+    return _chunked_normal(words, (T, d), lambda c: _store(c, dtype), np.float32 if dtype == "f32" else np.uint16)
 
 
 def make_linear_inputs(
@@ -107,17 +143,17 @@ def make_linear_inputs(
     T = wl.T if T is None else T
     wid = wl.wid
     if wl.w == "i8":
-        W0, w_scale = int8_gaussian(_rng(wid, lin, TENSOR_W0), m, n)
+        W0, w_scale = int8_gaussian([wid, lin, TENSOR_W0], m, n)
     else:
-        W0, w_scale = _store(normalized_gaussian(_rng(wid, lin, TENSOR_W0), m, n), wl.w), None
+        W0, w_scale = normalized_gaussian([wid, lin, TENSOR_W0], m, n, wl.w), None
     nbR, nbP = -(-m // b), -(-n // b)
     std = wl.q_std * q_scale
     q_R = (_rng(wid, lin, TENSOR_QR).standard_normal((nbR, packed_len(b))) * std).astype(np.float32)
     q_P = (_rng(wid, lin, TENSOR_QP).standard_normal((nbP, packed_len(b))) * std).astype(np.float32)
     perm_R = _rng(wid, lin, TENSOR_PR).permutation(m).astype(np.int32)
     perm_P = _rng(wid, lin, TENSOR_PP).permutation(n).astype(np.int32)
-    X = _store(_rng(wid, lin, TENSOR_X, T).standard_normal((T, m)), wl.act)
-    dZ = _store(_rng(wid, lin, TENSOR_DZ, T).standard_normal((T, n)), wl.act) if with_dz else None
+    X = _act_matrix([wid, lin, TENSOR_X, T], T, m, wl.act)
+    dZ = _act_matrix([wid, lin, TENSOR_DZ, T], T, n, wl.act) if with_dz else None
     return LinearInputs(m, n, b, T, wl.act, wl.w, W0, w_scale, q_R, q_P, perm_R, perm_P, X, dZ)
 
 
