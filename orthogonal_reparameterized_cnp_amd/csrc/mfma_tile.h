@@ -15,9 +15,10 @@
 
 namespace px {
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, bool PF2 = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr bool PREFETCH2 = PF2;  // two K tiles of global loads in flight
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
@@ -63,21 +64,32 @@ template <class C> struct AccPos {
 template <class C>
 PX_DEV void mma_stage(const bf16_t* As, const bf16_t* Bs, Acc<C>& acc, int wm, int wn, int lane) {
   constexpr int LDK = Lay<C, bf16_t>::LDK;
+  constexpr int KS = C::BK / 16;
   const int r = lane & 31, kg = (lane >> 5) * 8;
+  const bf16_t* pa = As + (wm * C::WTM + r) * LDK + kg;
+  const bf16_t* pb = Bs + (wn * C::WTN + r) * LDK + kg;
+  // fragments of k-step s + 1 are read while the MFMAs of step s run
+  bf16x8_v a[2][C::TM], b[2][C::TN];
 #pragma unroll
-  for (int kk = 0; kk < C::BK; kk += 16) {
-    bf16x8_v a[C::TM], b[C::TN];
+  for (int i = 0; i < C::TM; ++i) a[0][i] = *reinterpret_cast<const bf16x8_v*>(pa + i * 32 * LDK);
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8_v*>(As + (wm * C::WTM + i * 32 + r) * LDK + kk + kg);
+  for (int j = 0; j < C::TN; ++j) b[0][j] = *reinterpret_cast<const bf16x8_v*>(pb + j * 32 * LDK);
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j)
-      b[j] = *reinterpret_cast<const bf16x8_v*>(Bs + (wn * C::WTN + j * 32 + r) * LDK + kk + kg);
+  for (int ks = 0; ks < KS; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < KS) {
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+        a[cur ^ 1][i] = *reinterpret_cast<const bf16x8_v*>(pa + i * 32 * LDK + (ks + 1) * 16);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        b[cur ^ 1][j] = *reinterpret_cast<const bf16x8_v*>(pb + j * 32 * LDK + (ks + 1) * 16);
+    }
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
-        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
+        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc.v[i][j], 0, 0, 0);
   }
 }
 
@@ -106,15 +118,18 @@ PX_DEV void mma_stage(const float* As, const float* Bs, Acc<C>& acc, int wm, int
   }
 }
 
-// K loop.  `K` is the contraction length; loaders zero-fill past it.
-template <class C, typename T, class LA, class LB>
-PX_DEV void mainloop(T* lds, LA& la, LB& lb, int K, Acc<C>& acc, int wm, int wn, int lane) {
+struct NoHook {
+  template <typename T> PX_DEV void operator()(int, const T*) const {}
+};
+
+// K loop.  `K` is the contraction length; loaders zero-fill past it.  After the
+// MFMAs of K tile kt, hook(kt, A tile in LDS) runs (before the barrier that
+// lets the tile be overwritten).
+template <bool FAST, class C, typename T, class LA, class LB, class H>
+PX_DEV void mainloop_t(T* lds, LA& la, LB& lb, int KT, Acc<C>& acc, int wm, int wn, int lane, const H& hook) {
   using L = Lay<C, T>;
-  acc.zero();
-  const int KT = (K + C::BK - 1) / C::BK;
-  if (KT <= 0) return;
-  la.fetch(0);
-  lb.fetch(0);
+  la.template fetch<FAST>(0);
+  lb.template fetch<FAST>(0);
   la.stash(lds);
   lb.stash(lds + L::A_ELEMS);
   __syncthreads();
@@ -123,15 +138,70 @@ PX_DEV void mainloop(T* lds, LA& la, LB& lb, int K, Acc<C>& acc, int wm, int wn,
     T* nxt = lds + ((kt + 1) & 1) * L::STAGE;
     const bool more = kt + 1 < KT;
     if (more) {
-      la.fetch((kt + 1) * C::BK);
-      lb.fetch((kt + 1) * C::BK);
+      la.template fetch<FAST>((kt + 1) * C::BK);
+      lb.template fetch<FAST>((kt + 1) * C::BK);
     }
     mma_stage<C>(cur, cur + L::A_ELEMS, acc, wm, wn, lane);
+    hook(kt, cur);
     if (more) {
       la.stash(nxt);
       lb.stash(nxt + L::A_ELEMS);
     }
     __syncthreads();
+  }
+}
+
+// Two register sets per operand: the global loads of K tile kt + 2 are issued
+// while tile kt is multiplied, so each load has two tiles of MFMA time to land.
+template <bool FAST, class C, typename T, class LA, class LB, class H>
+PX_DEV void mainloop2_t(T* lds, LA& la0, LB& lb0, int KT, Acc<C>& acc, int wm, int wn, int lane, const H& hook) {
+  using L = Lay<C, T>;
+  LA la1 = la0;
+  LB lb1 = lb0;
+  la0.template fetch<FAST>(0);
+  lb0.template fetch<FAST>(0);
+  la0.stash(lds);
+  lb0.stash(lds + L::A_ELEMS);
+  if (KT > 1) {
+    la0.template fetch<FAST>(C::BK);
+    lb0.template fetch<FAST>(C::BK);
+  }
+  __syncthreads();
+  // step(kt): tile kt + 1 sits in set P, tile kt + 2 goes into set Q
+  auto step = [&](int kt, LA& laP, LB& lbP, LA& laQ, LB& lbQ) {
+    T* cur = lds + (kt & 1) * L::STAGE;
+    T* nxt = lds + ((kt + 1) & 1) * L::STAGE;
+    if (kt + 2 < KT) {
+      laQ.template fetch<FAST>((kt + 2) * C::BK);
+      lbQ.template fetch<FAST>((kt + 2) * C::BK);
+    }
+    mma_stage<C>(cur, cur + L::A_ELEMS, acc, wm, wn, lane);
+    hook(kt, cur);
+    if (kt + 1 < KT) {
+      laP.stash(nxt);
+      lbP.stash(nxt + L::A_ELEMS);
+    }
+    __syncthreads();
+  };
+  for (int kt = 0; kt < KT; kt += 2) {
+    step(kt, la0, lb0, la1, lb1);
+    if (kt + 1 < KT) step(kt + 1, la1, lb1, la0, lb0);
+  }
+}
+
+template <class C, typename T, class LA, class LB, class H = NoHook>
+PX_DEV void mainloop(T* lds, LA& la, LB& lb, int K, Acc<C>& acc, int wm, int wn, int lane, const H& hook = H()) {
+  acc.zero();
+  const int KT = (K + C::BK - 1) / C::BK;
+  if (KT <= 0) return;
+  // tiles entirely inside both operands take the loop without bounds checks
+  if (la.full() && lb.full() && K % C::BK == 0) {
+    if constexpr (C::PREFETCH2)
+      mainloop2_t<true, C>(lds, la, lb, KT, acc, wm, wn, lane, hook);
+    else
+      mainloop_t<true, C>(lds, la, lb, KT, acc, wm, wn, lane, hook);
+  } else {
+    mainloop_t<false, C>(lds, la, lb, KT, acc, wm, wn, lane, hook);
   }
 }
 
@@ -224,7 +294,17 @@ struct LoadK {
     K = K_;
     vec = aligned8(base_, ld_);
   }
-  PX_DEV void fetch(int k0) {
+  PX_DEV bool full() const { return vec && rows >= ROWS; }
+  template <bool FAST> PX_DEV void fetch(int k0) {
+    if constexpr (FAST) {  // whole tile inside: unconditional vector loads
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ch = threadIdx.x + i * NT;
+        if (TOT % NT != 0 && ch >= TOT) break;
+        Load8<D, S>::go(base + (int64_t)(ch / CPR) * ld + k0 + (ch % CPR) * 8, c[i]);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = threadIdx.x + i * NT;
@@ -263,7 +343,9 @@ struct LoadK {
 // Loader: source with the tile's row index contiguous (element (k, r) at
 // base[k * ld + r]); transposed into the [row][K] LDS tile.  Each thread moves
 // units of 4 K values x 8 rows: four 8-wide global loads along the rows, then
-// eight 4-wide LDS stores along K.
+// eight 4-wide LDS stores along K.  Consecutive lanes take consecutive K quads
+// of the same 8 rows, so the 16 lanes served together by a 64-bit LDS store
+// write one contiguous 128-byte row segment (no bank conflicts).
 // ---------------------------------------------------------------------------
 template <int ROWS, int BK, int NT, typename S, typename D>
 struct LoadMN {
@@ -284,12 +366,24 @@ struct LoadMN {
     K = K_;
     vec = aligned8(base_, ld_);
   }
-  PX_DEV void fetch(int k0) {
+  PX_DEV bool full() const { return vec && rows >= ROWS; }
+  template <bool FAST> PX_DEV void fetch(int k0) {
+    if constexpr (FAST) {  // whole tile inside: unconditional vector loads
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int unit = threadIdx.x + u * NT;
+        if (TOT % NT != 0 && unit >= TOT) break;
+        const S* p = base + (int64_t)(k0 + (unit % KQ) * 4) * ld + (unit / KQ) * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) Load8<D, S>::go(p + (int64_t)kk * ld, c[u][kk]);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int unit = threadIdx.x + u * NT;
       if (TOT % NT != 0 && unit >= TOT) break;
-      const int r0 = (unit % MC) * 8, kq = k0 + (unit / MC) * 4;
+      const int r0 = (unit / KQ) * 8, kq = k0 + (unit % KQ) * 4;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int k = kq + kk;
@@ -312,7 +406,7 @@ struct LoadMN {
     for (int u = 0; u < NU; ++u) {
       const int unit = threadIdx.x + u * NT;
       if (TOT % NT != 0 && unit >= TOT) break;
-      const int r0 = (unit % MC) * 8, kq = (unit / MC) * 4;
+      const int r0 = (unit / KQ) * 8, kq = (unit % KQ) * 4;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         D* p = lds + (r0 + e) * LDK + kq;
@@ -324,46 +418,6 @@ struct LoadMN {
         } else {
           *reinterpret_cast<float4*>(p) = make_float4(c[u][0].get(e), c[u][1].get(e), c[u][2].get(e), c[u][3].get(e));
         }
-      }
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Loader: tile values generated by a functor f(row, k) -> float (rows and K
-// are absolute indices: row0 + r, k).  Used for skew blocks unpacked from
-// their packed storage and for small combinations of them.
-// ---------------------------------------------------------------------------
-template <int ROWS, int BK, int NT, typename D, class F>
-struct LoadGen {
-  static constexpr int CPR = BK / 8;
-  static constexpr int TOT = ROWS * CPR;
-  static constexpr int NCH = (TOT + NT - 1) / NT;
-  F f;
-  int row0;
-  Chunk8<D> c[NCH];
-  PX_DEV void fetch(int k0) {
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = threadIdx.x + i * NT;
-      if (TOT % NT != 0 && ch >= TOT) break;
-      const int r = ch / CPR, k = k0 + (ch % CPR) * 8;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c[i].set(e, from_f32<D>(f(row0 + r, k + e)));
-    }
-  }
-  PX_DEV void stash(D* lds) const {
-    constexpr int LDK = BK + LdsPad<D>::v;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int ch = threadIdx.x + i * NT;
-      if (TOT % NT != 0 && ch >= TOT) break;
-      const int r = ch / CPR, kc = (ch % CPR) * 8;
-      if constexpr (sizeof(D) == 2) {
-        *reinterpret_cast<uint4*>(lds + r * LDK + kc) = c[i].w;
-      } else {
-        reinterpret_cast<float4*>(lds + r * LDK + kc)[0] = c[i].a;
-        reinterpret_cast<float4*>(lds + r * LDK + kc)[1] = c[i].b;
       }
     }
   }

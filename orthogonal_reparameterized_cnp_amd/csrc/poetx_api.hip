@@ -158,7 +158,7 @@ template <class P> BwdWs plan_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
   w.dXt = p.template take<char>(T * lead(d->m) * es);
   w.partP = p.template take<float>((size_t)w.splitsP * nbP * b * b * 4);
   w.partR = p.template take<float>((size_t)w.splitsR * nbR * b * b * 4);
-  w.cnp = p.template take<float>((size_t)7 * std::max(nbR, nbP) * b * b * 4);
+  w.cnp = p.template take<float>(cnp_backward_ws_bytes(d->act_dtype, d->m, d->n, d->b));
   w.invR = p.template take<int32_t>((size_t)d->m * 4);
   return w;
 }
@@ -223,8 +223,8 @@ size_t poetx_saved_bytes(const poetx_layer_desc* desc, int64_t T) {
 size_t poetx_workspace_size(const poetx_layer_desc* desc, int64_t T, int32_t op) {
   if (!desc || T < 0 || T > kMaxT) return 0;
   if (op == POETX_OP_CNP) {
-    if (desc->m < 1 || desc->b < 2) return 0;
-    return (size_t)round_up((int64_t)nblocks(desc->m, desc->b) * desc->b * desc->b * 4, 256);
+    if (desc->m < 1 || desc->b < 2 || (desc->act_dtype != POETX_F32 && desc->act_dtype != POETX_BF16)) return 0;
+    return cnp_build_ws_bytes(desc->act_dtype, desc->m, desc->b);
   }
   if (check_desc(desc) != POETX_OK) return 0;
   Plan p;
@@ -291,12 +291,12 @@ poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype
   if (!q || !g) return fail(POETX_E_NULL, "q and g must be non-NULL");
   if (d < 1 || d > kMaxDim || b < 2 || b > 1024 || nblocks(d, b) > 65535) return fail(POETX_E_SHAPE, "bad d or b");
   if (dtype != POETX_F32 && dtype != POETX_BF16) return fail(POETX_E_DTYPE, "g dtype must be F32 or BF16");
-  const size_t need = (size_t)round_up((int64_t)nblocks(d, b) * b * b * 4, 256);
+  const size_t need = cnp_build_ws_bytes(dtype, d, b);
   poetx_status st = check_ws(ws, ws_bytes, need);
   if (st != POETX_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   PX_TIMED(POETX_KC_CNP, 4 * sum_r3(d, b), 2 * g_slice(d, b, dtype) + 2.0 * nblocks(d, b) * b * b * 4,
-           cnp_build(dtype, q, d, b, g, reinterpret_cast<float*>(ws), s));
+           cnp_build(dtype, q, d, b, g, ws, s));
   return POETX_OK;
 }
 
@@ -411,11 +411,11 @@ poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const voi
     PX_HIP(fill_zero(w.partP, (size_t)w.splitsP * nbP * b * b * 4, s));
     PX_HIP(fill_zero(w.partR, (size_t)w.splitsR * nbR * b * b * 4, s));
   }
-  // CNP chain rule and skew projection, one side at a time (shared scratch)
-  PX_TIMED(POETX_KC_CNP, 12 * sum_r3(n, b), 4.0 * (w.splitsP + 13) * nbP * b * b,
-           cnp_backward(at, q_P, n, b, w.partP, w.splitsP, w.cnp, dq_P, s));
-  PX_TIMED(POETX_KC_CNP, 12 * sum_r3(m, b), 4.0 * (w.splitsR + 13) * nbR * b * b,
-           cnp_backward(at, q_R, m, b, w.partR, w.splitsR, w.cnp, dq_R, s));
+  // CNP chain rule and skew projection, both sides in the same launches
+  const CnpSide sides[2] = {{q_R, m, w.partR, w.splitsR, dq_R}, {q_P, n, w.partP, w.splitsP, dq_P}};
+  PX_TIMED(POETX_KC_CNP, 12 * (sum_r3(m, b) + sum_r3(n, b)),
+           4.0 * (w.splitsR * nbR + w.splitsP * nbP) * b * b + cnp_backward_ws_bytes(at, m, n, b),
+           cnp_backward(at, sides, 2, b, w.cnp, s));
   return POETX_OK;
 }
 

@@ -30,8 +30,9 @@ hipError_t compose_perm(const int32_t* a, const int32_t* b, int d, int32_t* out,
 hipError_t perm_from_seed_device(uint64_t seed, int d, int32_t* out, int32_t* scratch, hipStream_t s);
 
 // Delta = G - I of every block of one side, and its transpose:
-// g = [2][nb][b][b] in dtype dt (F32 or BF16); S_ws = [nb][b][b] fp32 scratch.
-hipError_t cnp_build(int dt, const float* q, int d, int b, void* g, float* S_ws, hipStream_t s);
+// g = [2][nb][b][b] in dtype dt (F32 or BF16); ws of cnp_build_ws_bytes bytes.
+hipError_t cnp_build(int dt, const float* q, int d, int b, void* g, void* ws, hipStream_t s);
+size_t cnp_build_ws_bytes(int dt, int d, int b);
 
 // Row-form block-diagonal product: out[:, kb+j] = (in[:, kb+j] + sum_k in[:, kb+k] D_blk[k][j]) * scale[kb+j]
 // where the B operand array `dT` holds D_blk^T, i.e. dT[blk][j][k] = D_blk[k][j].
@@ -48,10 +49,17 @@ hipError_t dgrad(int cdt, const void* A, int64_t lda, const void* B, int64_t ldb
                  float* part, hipStream_t s);
 int dgrad_splits(int rows, int d, int b);
 
-// CNP chain rule for one side: dG partials -> packed dq (overwritten).
-// ws6 holds 7 fp32 [nb][b][b] arrays.
-hipError_t cnp_backward(int cdt, const float* q, int d, int b, const float* part, int splits, float* ws7, float* dq,
-                        hipStream_t s);
+// CNP chain rule for one or two sides of a linear: token-split partials of
+// dG -> packed dq (overwritten).  ws of cnp_backward_ws_bytes bytes.
+struct CnpSide {
+  const float* q;
+  int d;
+  const float* part;  // [splits][nb][b][b] fp32
+  int splits;
+  float* dq;
+};
+hipError_t cnp_backward(int cdt, const CnpSide* sides, int nsides, int b, void* ws, hipStream_t s);
+size_t cnp_backward_ws_bytes(int dt, int d0, int d1, int b);
 
 // Merge helpers (fp32 MFMA).
 // M1[kb+i][c] = (W[kb+i][c] + sum_k DeltaR_blk[i][k] W[kb+k][c]) * wscale[c]

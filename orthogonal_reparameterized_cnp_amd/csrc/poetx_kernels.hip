@@ -5,130 +5,40 @@
 // is an instance of the LDS-staged MFMA tile loop in mfma_tile.h with a
 // suitable pair of operand loaders and an epilogue.  Permutations are index
 // arrays applied by row-staged gathers through LDS.
-#include "mfma_tile.h"
-#include "poetx_internal.h"
+#include "kernel_util.h"
 
 using namespace px;
 
 namespace {
 
-// ----------------------------------------------------------------------------
-// tile shapes
-// ----------------------------------------------------------------------------
-using TBig = Tile<256, 128, 64, 2, 2>;  // bf16: W~ contractions and block products over tokens
-using TSq = Tile<128, 128, 64, 2, 2>;   // bf16: block gradients, CNP (b x b outputs)
-using TF = Tile<64, 64, 32, 2, 2>;      // fp32: small layers
-using TFM = Tile<128, 128, 32, 2, 2>;   // fp32: merge products
-
-template <class C> PX_DEV AccPos<C> acc_pos() {
-  const int w = threadIdx.x >> 6;
-  return AccPos<C>{w / C::WN, w % C::WN, (int)(threadIdx.x & 63)};
-}
-
-template <class C, class F> PX_DEV void each_acc(const Acc<C>& acc, F&& f) {
-  const AccPos<C> p = acc_pos<C>();
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) {
-      const int c = p.col(j);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) f(p.row(i, e), c, acc.v[i][j][e]);
-    }
-}
-
-template <typename T> struct DT;
-template <> struct DT<float> { static constexpr int v = pxk::F32; };
-template <> struct DT<bf16_t> { static constexpr int v = pxk::BF16; };
-template <> struct DT<int8_t> { static constexpr int v = pxk::I8; };
-
-// Kernels whose static LDS use exceeds the default 64 KB limit must opt in once.
-template <typename K> hipError_t allow_lds(K kernel, int bytes) {
-  if (bytes <= 65536) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
-
-// ----------------------------------------------------------------------------
-// skew-block value functors (absolute indices; zero outside the live r x r block)
-// ----------------------------------------------------------------------------
-struct QRow {  // Q[i][k]
-  const float* qk;
-  int r, b;
-  PX_DEV float operator()(int i, int k) const { return skew_at(qk, i, k, r, b); }
-};
-struct QCol {  // (row n, K index k) -> Q[k][n]
-  const float* qk;
-  int r, b;
-  PX_DEV float operator()(int n, int k) const { return skew_at(qk, k, n, r, b); }
-};
-struct NCol {  // (row n, K index k) -> N[k][n] with N = 2Q + S, S = Q^2
-  const float* qk;
-  const float* S;
-  int r, b;
-  PX_DEV float operator()(int n, int k) const {
-    if (n >= r || k >= r) return 0.f;
-    return 2.f * skew_at(qk, k, n, r, b) + S[(int64_t)k * b + n];
-  }
-};
-
-// ============================================================================
-// CNP build: S = Q^2, then Delta = G - I = 2Q + 2S + S (2Q + S)
-// ============================================================================
-template <class C, typename T>
-__global__ __launch_bounds__(C::NT) void k_cnp_square(const float* __restrict__ q, int d, int b, float* __restrict__ S) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* lds = reinterpret_cast<T*>(smem);
-  const int blk = blockIdx.z, r = min(b, d - blk * b);
-  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
-  if (m0 >= r || n0 >= r) return;  // S is only read inside the live corner
-  const float* qk = q + (int64_t)blk * ((int64_t)b * (b - 1) / 2);
-  LoadGen<C::BM, C::BK, C::NT, T, QRow> la{QRow{qk, r, b}, m0};
-  LoadGen<C::BN, C::BK, C::NT, T, QCol> lb{QCol{qk, r, b}, n0};
-  Acc<C> acc;
-  const AccPos<C> p = acc_pos<C>();
-  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
-  float* Sb = S + (int64_t)blk * b * b;
-  each_acc<C>(acc, [&](int i, int j, float v) {
-    i += m0;
-    j += n0;
-    if (i < r && j < r) Sb[(int64_t)i * b + j] = v;
-  });
-}
-
-template <class C, typename T>
-__global__ __launch_bounds__(C::NT) void k_cnp_delta(const float* __restrict__ q, int d, int b, int nb,
-                                                      const float* __restrict__ S, T* __restrict__ g) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* lds = reinterpret_cast<T*>(smem);
-  const int blk = blockIdx.z, r = min(b, d - blk * b);
-  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
-  const float* qk = q + (int64_t)blk * ((int64_t)b * (b - 1) / 2);
-  const float* Sb = S + (int64_t)blk * b * b;
-  LoadK<C::BM, C::BK, C::NT, float, T> la;
-  la.init(Sb + (int64_t)m0 * b, b, r - m0, r);
-  LoadGen<C::BN, C::BK, C::NT, T, NCol> lb{NCol{qk, Sb, r, b}, n0};
-  Acc<C> acc;
-  const AccPos<C> p = acc_pos<C>();
-  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
-  T* g0 = g + (int64_t)blk * b * b;
-  T* g1 = g + ((int64_t)nb + blk) * b * b;
-  each_acc<C>(acc, [&](int i, int j, float v) {
-    i += m0;
-    j += n0;
-    if (i < b && j < b) {
-      float o = 0.f;
-      if (i < r && j < r) o = v + 2.f * skew_at(qk, i, j, r, b) + 2.f * Sb[(int64_t)i * b + j];
-      const T t = from_f32<T>(o);
-      g0[(int64_t)i * b + j] = t;
-      g1[(int64_t)j * b + i] = t;
-    }
-  });
-}
-
 // ============================================================================
 // block-diagonal product over token rows, identity added in fp32:
 //   out[t][kb+j] = (in[t][kb+j] + sum_k in[t][kb+k] dT[blk][j][k]) * scale[kb+j]
 // ============================================================================
+// The identity term is added from the A tile in LDS: the block's output column
+// c equals K index c, so during the K tile that holds columns [k0, k0 + BK)
+// each wave adds A[row][c - k0] to the accumulators of its column groups that
+// fall in that range.
+template <class C, typename T> struct IdentityHook {
+  Acc<C>* acc;
+  int n0;
+  PX_DEV void operator()(int kt, const T* A) const {
+    constexpr int LDK = Lay<C, T>::LDK;
+    const AccPos<C> p = acc_pos<C>();
+    const int k0 = kt * C::BK;
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int g = n0 + p.wn * C::WTN + j * 32;  // first column of this wave's group
+      if (g < k0 || g >= k0 + C::BK) continue;
+      const int kc = n0 + p.col(j) - k0;
+#pragma unroll
+      for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc->v[i][j][e] += to_f32<T>(A[p.row(i, e) * LDK + kc]);
+    }
+  }
+};
+
 template <class C, typename T, typename IT, typename GT, typename OT>
 __global__ __launch_bounds__(C::NT) void k_apply(const IT* __restrict__ in, int64_t ld_in, int rows, int d, int b,
                                                   const GT* __restrict__ dT, const float* __restrict__ colscale,
@@ -144,28 +54,43 @@ __global__ __launch_bounds__(C::NT) void k_apply(const IT* __restrict__ in, int6
   lb.init(dT + ((int64_t)blk * b + n0) * b, b, r - n0, r);
   Acc<C> acc;
   const AccPos<C> p = acc_pos<C>();
-  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
-  each_acc<C>(acc, [&](int i, int j, float v) {
-    const int t = m0 + i, c = n0 + j;
-    if (t < rows && c < r) {
-      const int64_t col = kb + c;
-      v += to_f32<IT>(in[(int64_t)t * ld_in + col]);
-      if (colscale) v *= colscale[col];
-      out[(int64_t)t * ld_out + col] = from_f32<OT>(v);
-    }
-  });
+  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane, IdentityHook<C, T>{&acc, n0});
+  const float* cs = colscale ? colscale + kb + n0 : nullptr;
+  store_tile<C, OT>(acc, smem, out + (int64_t)m0 * ld_out + kb + n0, ld_out, rows - m0, r - n0,
+                    [&](int c) { return cs ? cs[c] : 1.f; });
 }
 
 // ============================================================================
 // plain contraction out = A * B (* colscale)
 // ============================================================================
+// Workgroups are dealt to the 8 XCDs round robin by launch order.  The launch
+// index is remapped so that each XCD receives a contiguous range of tile
+// numbers, and tile numbers run through groups of GM row tiles, so the
+// workgroups sharing one XCD's L2 work on a compact patch of A rows and B
+// columns.
+struct TileMap {
+  int tm, tn;
+  static constexpr int GM = 8;
+  PX_DEV void at(int id, int& bm, int& bn) const {
+    const int total = tm * tn;
+    if (total % 8 == 0) id = (id % 8) * (total / 8) + id / 8;
+    const int group = id / (GM * tn);
+    const int first = group * GM;
+    const int gsize = min(tm - first, GM);
+    bm = first + (id % (GM * tn)) % gsize;
+    bn = (id % (GM * tn)) / gsize;
+  }
+};
+
 template <class C, typename T, typename AT, typename BT, typename OT, bool BKN>
 __global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_t lda, const BT* __restrict__ B,
                                                  int64_t ldb, int M, int N, int K, const float* __restrict__ colscale,
-                                                 OT* __restrict__ out, int64_t ldo) {
+                                                 OT* __restrict__ out, int64_t ldo, TileMap map) {
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
-  const int m0 = blockIdx.x * C::BM, n0 = blockIdx.y * C::BN;
+  int bm, bn;
+  map.at(blockIdx.x, bm, bn);
+  const int m0 = bm * C::BM, n0 = bn * C::BN;
   LoadK<C::BM, C::BK, C::NT, AT, T> la;
   la.init(A + (int64_t)m0 * lda, lda, M - m0, K);
   using LB = typename std::conditional<BKN, LoadMN<C::BN, C::BK, C::NT, BT, T>, LoadK<C::BN, C::BK, C::NT, BT, T>>::type;
@@ -177,13 +102,9 @@ __global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_
   Acc<C> acc;
   const AccPos<C> p = acc_pos<C>();
   mainloop<C, T>(lds, la, lb, K, acc, p.wm, p.wn, p.lane);
-  each_acc<C>(acc, [&](int i, int j, float v) {
-    const int mm = m0 + i, nn = n0 + j;
-    if (mm < M && nn < N) {
-      if (colscale) v *= colscale[nn];
-      out[(int64_t)mm * ldo + nn] = from_f32<OT>(v);
-    }
-  });
+  const float* cs = colscale ? colscale + n0 : nullptr;
+  store_tile<C, OT>(acc, smem, out + (int64_t)m0 * ldo + n0, ldo, M - m0, N - n0,
+                    [&](int c) { return cs ? cs[c] : 1.f; });
 }
 
 // ============================================================================
@@ -209,101 +130,17 @@ __global__ __launch_bounds__(C::NT) void k_dgrad(const IT* __restrict__ A, int64
   const AccPos<C> p = acc_pos<C>();
   mainloop<C, T>(lds, la, lb, K, acc, p.wm, p.wn, p.lane);
   float* out = part + ((int64_t)s * nb + blk) * b * b;
-  each_acc<C>(acc, [&](int i, int j, float v) {
-    i += m0;
-    j += n0;
-    if (i < b && j < b) out[(int64_t)i * b + j] = v;
-  });
-}
-
-// U[e] = sum_s part[s][e] in split order (deterministic)
-__global__ void k_reduce_splits(const float* __restrict__ part, int splits, int64_t n, float* __restrict__ U) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= n) return;
-  float s = 0.f;
-  for (int k = 0; k < splits; ++k) s += part[(int64_t)k * n + e];
-  U[e] = s;
-}
-
-// ============================================================================
-// CNP chain rule.  With U = dL/dG of a block, V1 = U Q, V2 = V1 Q, V3 = V2 Q:
-//   dQ = X0 + Q (X1 + Q (X2 + Q X3)),
-//   X0 = 2U - 2V1 + 2V2 - V3, X1 = -2U + 2V1 - V2, X2 = 2U - V1, X3 = -U,
-// which is the ten-term adjoint of G = I + 2(Q + Q^2 + Q^3) + Q^4 (Q^T = -Q)
-// grouped by powers of Q on the left.  Steps 0..2 form V1..V3, steps 3..5 the
-// nested products Y1 = X2 - Q U, Y2 = X1 + Q Y1, dQ = X0 + Q Y2.
-// ============================================================================
-template <class C, typename T, int STEP>
-__global__ __launch_bounds__(C::NT) void k_cnp_bwd(const float* __restrict__ q, int d, int b,
-                                                    const float* __restrict__ ws, int64_t bb_all,
-                                                    float* __restrict__ out) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* lds = reinterpret_cast<T*>(smem);
-  const int blk = blockIdx.z, r = min(b, d - blk * b);
-  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
-  const float* qk = q + (int64_t)blk * ((int64_t)b * (b - 1) / 2);
-  const int64_t off = (int64_t)blk * b * b;
-  // ws arrays: 0 U, 1 V1, 2 V2, 3 V3, 4 Y1, 5 Y2, 6 dQ
-  const float* U = ws + 0 * bb_all + off;
-  const float* V1 = ws + 1 * bb_all + off;
-  const float* V2 = ws + 2 * bb_all + off;
-  const float* V3 = ws + 3 * bb_all + off;
-  const float* Y1 = ws + 4 * bb_all + off;
-  const float* Y2 = ws + 5 * bb_all + off;
-  Acc<C> acc;
-  const AccPos<C> p = acc_pos<C>();
-  if constexpr (STEP <= 2) {
-    const float* src = STEP == 0 ? U : STEP == 1 ? V1 : V2;
-    LoadK<C::BM, C::BK, C::NT, float, T> la;
-    la.init(src + (int64_t)m0 * b, b, r - m0, r);
-    LoadGen<C::BN, C::BK, C::NT, T, QCol> lb{QCol{qk, r, b}, n0};
-    mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
-  } else {
-    const float* src = STEP == 3 ? U : STEP == 4 ? Y1 : Y2;
-    LoadGen<C::BM, C::BK, C::NT, T, QRow> la{QRow{qk, r, b}, m0};
-    LoadMN<C::BN, C::BK, C::NT, float, T> lb;
-    lb.init(src + n0, b, r - n0, r);
-    mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
-  }
-  float* o = out + off;
-  each_acc<C>(acc, [&](int i, int j, float v) {
-    i += m0;
-    j += n0;
-    if (i >= b || j >= b) return;
-    const int64_t e = (int64_t)i * b + j;
-    float res;
-    if constexpr (STEP <= 2) {
-      res = v;
-    } else if constexpr (STEP == 3) {
-      res = 2.f * U[e] - V1[e] - v;
-    } else if constexpr (STEP == 4) {
-      res = -2.f * U[e] + 2.f * V1[e] - V2[e] + v;
-    } else {
-      res = 2.f * U[e] - 2.f * V1[e] + 2.f * V2[e] - V3[e] + v;
-    }
-    o[e] = (i < r && j < r) ? res : 0.f;
-  });
-}
-
-// dq[blk][p(i,j)] = dQ[i][j] - dQ[j][i] for i < j < r, 0 for dead slots
-__global__ void k_pack_dq(const float* __restrict__ dQ, int d, int b, float* __restrict__ dq) {
-  const int blk = blockIdx.y, r = min(b, d - blk * b);
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (int64_t)b * b) return;
-  const int i = (int)(e / b), j = (int)(e % b);
-  if (i >= j) return;
-  const float* Qb = dQ + (int64_t)blk * b * b;
-  const float v = (j < r) ? Qb[(int64_t)i * b + j] - Qb[(int64_t)j * b + i] : 0.f;
-  dq[(int64_t)blk * ((int64_t)b * (b - 1) / 2) + packed_slot(i, j, b)] = v;
+  store_tile<C, float>(acc, smem, out + (int64_t)m0 * b + n0, b, b - m0, b - n0, Unit());
 }
 
 // ============================================================================
 // permutations
 // ============================================================================
 // Row-staged gather: the workgroup copies whole source rows into LDS with
-// coalesced loads, then writes each output row coalesced, reading LDS at the
-// permuted positions.  Indices are clamped into range so that a malformed
-// permutation cannot address outside the staged rows.
+// 16-byte coalesced loads, then writes each output row with 16-byte stores,
+// every lane gathering its 16 bytes from LDS at the permuted positions.
+// Indices are clamped into range so that a malformed permutation cannot
+// address outside the staged rows.
 template <typename E>
 __global__ __launch_bounds__(256) void k_permute_lds(const E* __restrict__ in, int64_t ld_in,
                                                      const int32_t* __restrict__ rowmap,
@@ -311,20 +148,49 @@ __global__ __launch_bounds__(256) void k_permute_lds(const E* __restrict__ in, i
                                                      int64_t ld_out, int rows, int d_in, int d_out, int rpw) {
   extern __shared__ __align__(16) unsigned char smem[];
   E* buf = reinterpret_cast<E*>(smem);
+  constexpr int V = 16 / sizeof(E);
+  const int pitch = (d_in + V - 1) / V * V;
   const int t0 = blockIdx.x * rpw;
   const int nr = min(rpw, rows - t0);
+  const bool vin = (reinterpret_cast<uintptr_t>(in) % 16 == 0) && (ld_in % V == 0) && (d_in % V == 0);
   for (int rr = 0; rr < nr; ++rr) {
     int src = t0 + rr;
     if (rowmap) src = min(max(rowmap[src], 0), rows - 1);
     const E* row = in + (int64_t)src * ld_in;
-    for (int i = threadIdx.x; i < d_in; i += blockDim.x) buf[rr * d_in + i] = row[i];
+    E* dst = buf + rr * pitch;
+    if (vin) {
+      for (int i = threadIdx.x; i < d_in / V; i += blockDim.x)
+        reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(row)[i];
+    } else {
+      for (int i = threadIdx.x; i < d_in; i += blockDim.x) dst[i] = row[i];
+    }
   }
   __syncthreads();
+  const bool vout = (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (ld_out % V == 0) &&
+                    (reinterpret_cast<uintptr_t>(colmap) % 16 == 0);
+  const int nchunk = (d_out + V - 1) / V;
   for (int rr = 0; rr < nr; ++rr) {
     E* o = out + (int64_t)(t0 + rr) * ld_out;
-    for (int i = threadIdx.x; i < d_out; i += blockDim.x) {
-      const int c = min(max(colmap[i], 0), d_in - 1);
-      o[i] = buf[rr * d_in + c];
+    const E* srow = buf + rr * pitch;
+    for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+      const int i0 = c * V;
+      if (vout && i0 + V <= d_out) {
+        int32_t idx[V];
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q) {
+          const int4 w = reinterpret_cast<const int4*>(colmap + i0)[q];
+          idx[4 * q] = w.x;
+          idx[4 * q + 1] = w.y;
+          idx[4 * q + 2] = w.z;
+          idx[4 * q + 3] = w.w;
+        }
+        E vals[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) vals[e] = srow[min(max(idx[e], 0), d_in - 1)];
+        *reinterpret_cast<uint4*>(o + i0) = *reinterpret_cast<const uint4*>(vals);
+      } else {
+        for (int e = 0; e < V && i0 + e < d_out; ++e) o[i0 + e] = srow[min(max(colmap[i0 + e], 0), d_in - 1)];
+      }
     }
   }
 }
@@ -467,8 +333,6 @@ __global__ void k_fill_zero(uint8_t* __restrict__ p, size_t bytes) {
   if (blockIdx.x == 0 && threadIdx.x < tail) p[n16 * 16 + threadIdx.x] = 0;
 }
 
-inline unsigned cdiv(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
-
 }  // namespace
 
 // ============================================================================
@@ -491,9 +355,10 @@ hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap,
   const size_t budget = 64 * 1024;
   auto go = [&](auto tag) -> hipError_t {
     using E = decltype(tag);
-    if (row_bytes <= budget) {
-      const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, budget / row_bytes));
-      k_permute_lds<E><<<cdiv(rows, rpw), 256, rpw * row_bytes, s>>>(
+    const size_t pitch_bytes = (row_bytes + 15) / 16 * 16;
+    if (pitch_bytes <= budget) {
+      const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, budget / pitch_bytes));
+      k_permute_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch_bytes, s>>>(
           reinterpret_cast<const E*>(in), ld_in, rowmap, colmap, reinterpret_cast<E*>(out), ld_out, rows, d_in, d_out,
           rpw);
     } else {
@@ -528,27 +393,10 @@ hipError_t perm_from_seed_device(uint64_t seed, int d, int32_t* out, int32_t* sc
   return hipGetLastError();
 }
 
-template <class C, typename T> static hipError_t cnp_build_t(const float* q, int d, int b, T* g, float* S, hipStream_t s) {
-  const int nb = nblocks(d, b);
-  const int lds = Lay<C, T>::BYTES;
-  hipError_t e = allow_lds(k_cnp_square<C, T>, lds);
-  if (e == hipSuccess) e = allow_lds(k_cnp_delta<C, T>, lds);
-  if (e != hipSuccess) return e;
-  dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), nb);
-  k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(q, d, b, S);
-  k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(q, d, b, nb, S, g);
-  return hipGetLastError();
-}
-
-hipError_t cnp_build(int dt, const float* q, int d, int b, void* g, float* S_ws, hipStream_t s) {
-  if (dt == BF16) return cnp_build_t<TSq, bf16_t>(q, d, b, reinterpret_cast<bf16_t*>(g), S_ws, s);
-  return cnp_build_t<TF, float>(q, d, b, reinterpret_cast<float*>(g), S_ws, s);
-}
-
 template <class C, typename T, typename IT, typename GT, typename OT>
 static hipError_t apply_t(const void* in, int64_t ld_in, int rows, int d, int b, const void* dT, const float* cs,
                           void* out, int64_t ld_out, hipStream_t s) {
-  const int lds = Lay<C, T>::BYTES;
+  const int lds = smem_bytes<C, T, OT>();
   auto k = k_apply<C, T, IT, GT, OT>;
   hipError_t e = allow_lds(k, lds);
   if (e != hipSuccess) return e;
@@ -562,7 +410,7 @@ hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, in
                  const float* colscale, int out_dt, void* out, int64_t ld_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (cdt == BF16 && in_dt == BF16 && dT_dt == BF16 && out_dt == BF16)
-    return apply_t<TBig, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+    return apply_t<TGemm, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
   if (cdt == F32 && in_dt == F32 && dT_dt == F32 && out_dt == F32)
     return apply_t<TF, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
   // merge products: fp32 rows times the stored blocks
@@ -576,14 +424,24 @@ hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, in
 template <class C, typename T, typename AT, typename BT, typename OT, bool BKN>
 static hipError_t gemm_t(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K, const float* cs,
                          void* out, int64_t ldo, hipStream_t s) {
-  const int lds = Lay<C, T>::BYTES;
+  const int lds = smem_bytes<C, T, OT>();
   auto k = k_gemm<C, T, AT, BT, OT, BKN>;
   hipError_t e = allow_lds(k, lds);
   if (e != hipSuccess) return e;
-  dim3 grid(cdiv(M, C::BM), cdiv(N, C::BN));
-  k<<<grid, C::NT, lds, s>>>(reinterpret_cast<const AT*>(A), lda, reinterpret_cast<const BT*>(B), ldb, M, N, K, cs,
-                             reinterpret_cast<OT*>(out), ldo);
+  const TileMap map{(int)cdiv(M, C::BM), (int)cdiv(N, C::BN)};
+  k<<<map.tm * map.tn, C::NT, lds, s>>>(reinterpret_cast<const AT*>(A), lda, reinterpret_cast<const BT*>(B), ldb, M, N,
+                                        K, cs, reinterpret_cast<OT*>(out), ldo, map);
   return hipGetLastError();
+}
+
+// bf16 contraction: the 256 x 256 tile when it yields at least one workgroup
+// per CU, else the 256 x 128 tile.
+template <typename BT, bool BKN>
+static hipError_t gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K,
+                            const float* cs, void* out, int64_t ldo, hipStream_t s) {
+  if ((int64_t)cdiv(M, 256) * cdiv(N, 256) >= 256)
+    return gemm_t<TGemm, bf16_t, bf16_t, BT, bf16_t, BKN>(A, lda, B, ldb, M, N, K, cs, out, ldo, s);
+  return gemm_t<TBig, bf16_t, bf16_t, BT, bf16_t, BKN>(A, lda, B, ldb, M, N, K, cs, out, ldo, s);
 }
 
 hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const void* B, int64_t ldb, bool b_kn, int M,
@@ -591,11 +449,11 @@ hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const v
   if (M <= 0 || N <= 0) return hipSuccess;
   if (cdt == BF16 && a_dt == BF16 && out_dt == BF16) {
     if (b_dt == BF16)
-      return b_kn ? gemm_t<TBig, bf16_t, bf16_t, bf16_t, bf16_t, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
-                  : gemm_t<TBig, bf16_t, bf16_t, bf16_t, bf16_t, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
+      return b_kn ? gemm_bf16<bf16_t, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
+                  : gemm_bf16<bf16_t, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
     if (b_dt == I8)
-      return b_kn ? gemm_t<TBig, bf16_t, bf16_t, int8_t, bf16_t, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
-                  : gemm_t<TBig, bf16_t, bf16_t, int8_t, bf16_t, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
+      return b_kn ? gemm_bf16<int8_t, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
+                  : gemm_bf16<int8_t, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
   }
   if (cdt == F32 && a_dt == F32 && b_dt == F32 && out_dt == F32)
     return b_kn ? gemm_t<TF, float, float, float, float, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
@@ -615,7 +473,7 @@ int dgrad_splits(int rows, int d, int b) {
 template <class C, typename T>
 static hipError_t dgrad_t(const void* A, int64_t lda, const void* B, int64_t ldb, int rows, int d, int b, int splits,
                           float* part, hipStream_t s) {
-  const int lds = Lay<C, T>::BYTES;
+  const int lds = smem_bytes<C, T, float>();
   auto k = k_dgrad<C, T, T>;
   hipError_t e = allow_lds(k, lds);
   if (e != hipSuccess) return e;
@@ -631,37 +489,6 @@ hipError_t dgrad(int cdt, const void* A, int64_t lda, const void* B, int64_t ldb
                  float* part, hipStream_t s) {
   if (cdt == BF16) return dgrad_t<TSq, bf16_t>(A, lda, B, ldb, rows, d, b, splits, part, s);
   return dgrad_t<TF, float>(A, lda, B, ldb, rows, d, b, splits, part, s);
-}
-
-template <class C, typename T>
-static hipError_t cnp_backward_t(const float* q, int d, int b, const float* part, int splits, float* ws, float* dq,
-                                 hipStream_t s) {
-  const int nb = nblocks(d, b);
-  const int64_t bb_all = (int64_t)nb * b * b;
-  k_reduce_splits<<<cdiv(bb_all, 256), 256, 0, s>>>(part, splits, bb_all, ws);
-  const int lds = Lay<C, T>::BYTES;
-  dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), nb);
-  hipError_t e = hipSuccess;
-#define PX_STEP(K, OUT)                                                          \
-  e = allow_lds(k_cnp_bwd<C, T, K>, lds);                                        \
-  if (e != hipSuccess) return e;                                                 \
-  k_cnp_bwd<C, T, K><<<grid, C::NT, lds, s>>>(q, d, b, ws, bb_all, ws + (OUT) * bb_all);
-  PX_STEP(0, 1)
-  PX_STEP(1, 2)
-  PX_STEP(2, 3)
-  PX_STEP(3, 4)
-  PX_STEP(4, 5)
-  PX_STEP(5, 6)
-#undef PX_STEP
-  dim3 pg(cdiv((int64_t)b * b, 256), nb);
-  k_pack_dq<<<pg, 256, 0, s>>>(ws + 6 * bb_all, d, b, dq);
-  return hipGetLastError();
-}
-
-hipError_t cnp_backward(int cdt, const float* q, int d, int b, const float* part, int splits, float* ws7, float* dq,
-                        hipStream_t s) {
-  if (cdt == BF16) return cnp_backward_t<TSq, bf16_t>(q, d, b, part, splits, ws7, dq, s);
-  return cnp_backward_t<TF, float>(q, d, b, part, splits, ws7, dq, s);
 }
 
 template <typename GT, typename WT>
