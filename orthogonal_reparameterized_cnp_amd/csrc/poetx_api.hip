@@ -140,25 +140,18 @@ template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
 }
 
 struct BwdWs {
-  void *dZt, *dH, *dA, *Xt, *dXt;
-  float *partP, *partR, *cnp;
+  void *dZt, *dH, *dA, *Xt, *dXt, *cnp;
   int32_t* invR;
-  int splitsP, splitsR;
 };
 template <class P> BwdWs plan_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
   const size_t es = dt_size(d->act_dtype);
-  const int64_t b = d->b, nbR = nblocks(d->m, d->b), nbP = nblocks(d->n, d->b);
   BwdWs w;
-  w.splitsP = dgrad_splits((int)T, d->n, d->b);
-  w.splitsR = dgrad_splits((int)T, d->m, d->b);
   w.dZt = p.template take<char>(T * lead(d->n) * es);
   w.dH = p.template take<char>(T * lead(d->n) * es);
   w.dA = p.template take<char>(T * lead(d->m) * es);
   w.Xt = p.template take<char>(T * lead(d->m) * es);
   w.dXt = p.template take<char>(T * lead(d->m) * es);
-  w.partP = p.template take<float>((size_t)w.splitsP * nbP * b * b * 4);
-  w.partR = p.template take<float>((size_t)w.splitsR * nbR * b * b * 4);
-  w.cnp = p.template take<float>(cnp_backward_ws_bytes(d->act_dtype, d->m, d->n, d->b));
+  w.cnp = p.template take<char>(cnp_backward_ws_bytes(d->act_dtype, d->m, d->n, d->b));
   w.invR = p.template take<int32_t>((size_t)d->m * 4);
   return w;
 }
@@ -385,37 +378,31 @@ poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const voi
       wt == POETX_I8 ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(Wt) + weight_scale_offset(desc))
                      : nullptr;
   const double es = (double)dt_size(at), wes = (double)dt_size(wt);
-  const int nbR = nblocks(m, b), nbP = nblocks(n, b);
+  // dZt = dZ[:, perm_P]
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, permute(at, dZ, n, nullptr, perm_P, w.dZt, ldn, rows, n, n, s));
+  // dH = dZt Diag(G_P)^T (int8: times the column scale, ready for the code contraction)
+  PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
+           apply(at, at, w.dZt, ldn, rows, n, b, at, g_P, scale_t, at, w.dH, ldn, s));
+  // dA = dH W~^T
+  PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * n + wes * m * n + es * rows * m,
+           gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
+  // Xt = X[:, perm_R]
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
+  // block gradients of both sides over all tokens: dG_R = Xt^T dA, dG_P = H^T dZt
+  const CnpSide sides[2] = {{q_R, m, w.Xt, ldm, w.dA, ldm, dq_R}, {q_P, n, H_save, ldn, w.dZt, ldn, dq_P}};
+  PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * (sum_r2(m, b) + sum_r2(n, b)),
+           2.0 * rows * (m + n) * es + (4 + 2 * es) * (sum_r2(m, b) + sum_r2(n, b)),
+           block_grads(at, sides, rows, b, w.cnp, s));
+  // dXt = dA Diag(G_R)^T;  dX[:, perm_R] = dXt
+  PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
+           apply(at, at, w.dA, ldm, rows, m, b, at, g_R, nullptr, at, w.dXt, ldm, s));
   if (rows > 0) {
-    // dZt = dZ[:, perm_P]
-    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, permute(at, dZ, n, nullptr, perm_P, w.dZt, ldn, rows, n, n, s));
-    // dH = dZt Diag(G_P)^T (int8: times the column scale, ready for the code contraction)
-    PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
-             apply(at, at, w.dZt, ldn, rows, n, b, at, g_P, scale_t, at, w.dH, ldn, s));
-    // dG_P = H^T dZt per block (split over tokens)
-    PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + 4.0 * w.splitsP * nbP * b * b,
-             dgrad(at, H_save, ldn, w.dZt, ldn, rows, n, b, w.splitsP, w.partP, s));
-    // dA = dH W~^T
-    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * n + wes * m * n + es * rows * m,
-             gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
-    // Xt = X[:, perm_R];  dG_R = Xt^T dA per block
-    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
-    PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + 4.0 * w.splitsR * nbR * b * b,
-             dgrad(at, w.Xt, ldm, w.dA, ldm, rows, m, b, w.splitsR, w.partR, s));
-    // dXt = dA Diag(G_R)^T;  dX[:, perm_R] = dXt
-    PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
-             apply(at, at, w.dA, ldm, rows, m, b, at, g_R, nullptr, at, w.dXt, ldm, s));
     PX_HIP(inverse_perm(perm_R, m, w.invR, s));
     PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, w.dXt, ldm, nullptr, w.invR, dX, m, rows, m, m, s));
-  } else {
-    PX_HIP(fill_zero(w.partP, (size_t)w.splitsP * nbP * b * b * 4, s));
-    PX_HIP(fill_zero(w.partR, (size_t)w.splitsR * nbR * b * b * 4, s));
   }
-  // CNP chain rule and skew projection, both sides in the same launches
-  const CnpSide sides[2] = {{q_R, m, w.partR, w.splitsR, dq_R}, {q_P, n, w.partP, w.splitsP, dq_P}};
-  PX_TIMED(POETX_KC_CNP, 12 * (sum_r3(m, b) + sum_r3(n, b)),
-           4.0 * (w.splitsR * nbR + w.splitsP * nbP) * b * b + cnp_backward_ws_bytes(at, m, n, b),
-           cnp_backward(at, sides, 2, b, w.cnp, s));
+  // CNP chain rule and skew projection of both sides
+  PX_TIMED(POETX_KC_CNP, 12 * (sum_r3(m, b) + sum_r3(n, b)), cnp_backward_ws_bytes(at, m, n, b),
+           cnp_chain(at, sides, b, w.cnp, s));
   return POETX_OK;
 }
 

@@ -4,7 +4,8 @@
 // Build (POET-X blog on zhichai.net, 第四斧: Q^2 once, Q^3 and Q^4 from it):
 //   S = Q^2, N = 2Q + S,  G - I = 2Q + 2S + S N  (= 2Q + 2Q^2 + 2Q^3 + Q^4).
 // Chain rule of G = I + 2(Q + Q^2 + Q^3) + Q^4 with Q^T = -Q, grouped by powers
-// of Q on the left: with U = dL/dG, V1 = U Q, V2 = V1 Q, V3 = V2 Q,
+// of Q on the left: with U = dL/dG (the block gradient, summed over tokens
+// here too), V1 = U Q, V2 = V1 Q, V3 = V2 Q,
 //   dQ = X0 + Q (X1 + Q (X2 + Q X3)),
 //   X0 = 2U - 2V1 + 2V2 - V3, X1 = -2U + 2V1 - V2, X2 = 2U - V1, X3 = -U,
 // then dq[p(i,j)] = dQ[i][j] - dQ[j][i] on the packed slots.
@@ -119,52 +120,25 @@ __global__ __launch_bounds__(C::NT) void k_cnp_delta(Sides sd, int b, int nb_all
   });
 }
 
-// U = sum of the token-split partials (fixed order), as fp32, operand dtype and
-// operand-dtype transpose (64 x 64 tiles transposed through LDS).
-struct Parts {
-  const float* part[2];
-  int splits[2];
-  int nb[2];
+// Block gradients U = dL/dG summed over all tokens, both sides in one launch:
+// side s, block blk: U[i][j] = sum_t A_s[t][kb + i] * B_s[t][kb + j] (R side:
+// A = Xt, B = dA; P side: A = H, B = dZt).  Each workgroup owns one output
+// tile and runs the whole token range, so the sum order is fixed.  Written as
+// fp32, operand dtype and operand-dtype transpose, the forms the chain reads.
+template <typename T> struct GradSides {
+  const T* A[2];
+  const T* B[2];
+  int64_t lda[2], ldb[2];
 };
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_reduce_u(Parts pt, int b, float* __restrict__ U32, T* __restrict__ Ub,
-                                                  T* __restrict__ Utb) {
-  __shared__ float tile[64][65];
-  const int z = blockIdx.y;
-  const int s = z >= pt.nb[0];
-  const int blk = z - s * pt.nb[0];
-  const int tpr = (b + 63) / 64;
-  const int ti = (blockIdx.x / tpr) * 64, tj = (blockIdx.x % tpr) * 64;
-  const int64_t bb = (int64_t)b * b;
-  const float* part = pt.part[s] + (int64_t)blk * bb;
-  const int64_t stride = (int64_t)pt.nb[s] * bb;
-  const int64_t off = (int64_t)z * bb;
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int i = ti + e / 64, j = tj + e % 64;
-    float v = 0.f;
-    if (i < b && j < b) {
-      const int64_t x = (int64_t)i * b + j;
-      for (int k = 0; k < pt.splits[s]; ++k) v += part[k * stride + x];
-      U32[off + x] = v;
-      Ub[off + x] = from_f32<T>(v);
-    }
-    tile[e / 64][e % 64] = v;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
-    const int j = tj + e / 64, i = ti + e % 64;
-    if (i < b && j < b) Utb[off + (int64_t)j * b + i] = from_f32<T>(tile[e % 64][e / 64]);
-  }
-}
 
 template <typename T> struct Chain {
   const T* Qb;
-  const float* U32;
-  const T* Ub;
-  const T* Utb;
+  float* U32;
+  T* Ub;
+  T* Utb;
   float* V1_32;
   T* V1b;
+  float* P2_32;  // Q U
   float* V2_32;
   T* V2b;
   float* V3_32;
@@ -173,25 +147,72 @@ template <typename T> struct Chain {
   float* dQ32;
 };
 
-template <class C, typename T, int STEP>
-__global__ __launch_bounds__(C::NT) void k_cnp_chain(Sides sd, int b, Chain<T> ch) {
+template <class C, typename T>
+__global__ __launch_bounds__(C::NT) void k_block_grads(Sides sd, GradSides<T> gs, int rows, int b, Chain<T> ch) {
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
-  const int z = blockIdx.z;
+  const int z = blockIdx.y;
+  const int s = z >= sd.nb0;
+  const int blk = z - s * sd.nb0;
+  const int kb = blk * b, r = min(b, sd.d[s] - kb);
+  const int tiles_n = (b + C::BN - 1) / C::BN;
+  const int m0 = (blockIdx.x / tiles_n) * C::BM, n0 = (blockIdx.x % tiles_n) * C::BN;
+  if (m0 >= r || n0 >= r) return;  // only the live corner is read later
+  LoadMN<C::BM, C::BK, C::NT, T, T> la;
+  la.init(gs.A[s] + kb + m0, gs.lda[s], r - m0, rows);
+  LoadMN<C::BN, C::BK, C::NT, T, T> lb;
+  lb.init(gs.B[s] + kb + n0, gs.ldb[s], r - n0, rows);
+  Acc<C> acc;
+  const AccPos<C> p = acc_pos<C>();
+  mainloop<C, T>(lds, la, lb, rows, acc, p.wm, p.wn, p.lane);
+  const int64_t off = (int64_t)z * b * b;
+  each_acc4<C>(acc, [&](int i0, int j, const float* v) {
+    i0 += m0;
+    j += n0;
+    if (j >= r || i0 >= r) return;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (i0 + e >= r) continue;
+      const int64_t x = off + (int64_t)(i0 + e) * b + j;
+      ch.U32[x] = v[e];
+      ch.Ub[x] = from_f32<T>(v[e]);
+    }
+    T* dst = ch.Utb + off + (int64_t)j * b + i0;
+    if (i0 + 4 <= r)
+      store4<T>(dst, v);
+    else
+      for (int e = 0; e < 4 && i0 + e < r; ++e) dst[e] = from_f32<T>(v[e]);
+  });
+}
+
+// Chain rule in four launches (see the file header for V1..V3, X0..X3):
+//   step 1: V1 = U Q            and  P2 = Q U          (2 NB blocks of work)
+//   step 2: V2 = V1 Q           with Y1 = 2U - V1 - P2 written transposed
+//   step 3: V3 = V2 Q           and  Y2 = -2U + 2V1 - V2 + Q Y1 (transposed)
+//   step 4: dQ = 2U - 2V1 + 2V2 - V3 + Q Y2
+// Products X Q load Q's rows as the B operand and negate (X Q^T = -X Q).
+template <class C, typename T, int STEP>
+__global__ __launch_bounds__(C::NT) void k_cnp_chain(Sides sd, int b, int NB, Chain<T> ch) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* lds = reinterpret_cast<T*>(smem);
+  const bool second = (STEP == 1 || STEP == 3) && (int)blockIdx.z >= NB;
+  const int z = blockIdx.z - (second ? NB : 0);
   const float* qk;
   int r;
   sd.at(z, b, qk, r);
   const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
   if (m0 >= r || n0 >= r) return;  // later steps and the packing read only the live corner
   const int64_t off = (int64_t)z * b * b;
+  // right-multiplication by Q (first products of steps 1-3) or left-multiplication (the rest)
+  const bool right = (STEP <= 3) && !second;
   LoadK<C::BM, C::BK, C::NT, T, T> la;
   LoadK<C::BN, C::BK, C::NT, T, T> lb;
-  if constexpr (STEP <= 2) {  // V_{k+1} = V_k Q = -(V_k Q^T)
-    const T* src = STEP == 0 ? ch.Ub : STEP == 1 ? ch.V1b : ch.V2b;
+  if (right) {
+    const T* src = STEP == 1 ? ch.Ub : STEP == 2 ? ch.V1b : ch.V2b;
     la.init(src + off + (int64_t)m0 * b, b, r - m0, r);
     lb.init(ch.Qb + off + (int64_t)n0 * b, b, r - n0, r);
-  } else {  // Q Y with Y^T rows as the B operand
-    const T* srcT = STEP == 3 ? ch.Utb : STEP == 4 ? ch.Y1tb : ch.Y2tb;
+  } else {
+    const T* srcT = STEP == 1 ? ch.Utb : STEP == 3 ? ch.Y1tb : ch.Y2tb;
     la.init(ch.Qb + off + (int64_t)m0 * b, b, r - m0, r);
     lb.init(srcT + off + (int64_t)n0 * b, b, r - n0, r);
   }
@@ -201,31 +222,35 @@ __global__ __launch_bounds__(C::NT) void k_cnp_chain(Sides sd, int b, Chain<T> c
   each_acc4<C>(acc, [&](int i0, int j, const float* v) {
     i0 += m0;
     j += n0;
-    if (j >= r) return;
+    if (j >= r || i0 >= r) return;
     float o[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int i = i0 + e;
-      if (i >= r) continue;
-      const int64_t x = off + (int64_t)i * b + j;
-      if constexpr (STEP == 0) {
-        ch.V1_32[x] = -v[e];
-        ch.V1b[x] = from_f32<T>(-v[e]);
-      } else if constexpr (STEP == 1) {
-        ch.V2_32[x] = -v[e];
-        ch.V2b[x] = from_f32<T>(-v[e]);
-      } else if constexpr (STEP == 2) {
-        ch.V3_32[x] = -v[e];
-      } else if constexpr (STEP == 3) {
-        o[e] = 2.f * ch.U32[x] - ch.V1_32[x] - v[e];
-      } else if constexpr (STEP == 4) {
-        o[e] = -2.f * ch.U32[x] + 2.f * ch.V1_32[x] - ch.V2_32[x] + v[e];
+      if (i0 + e >= r) continue;
+      const int64_t x = off + (int64_t)(i0 + e) * b + j;
+      if (right) {
+        const float val = -v[e];
+        if (STEP == 1) {
+          ch.V1_32[x] = val;
+          ch.V1b[x] = from_f32<T>(val);
+        } else if (STEP == 2) {
+          ch.V2_32[x] = val;
+          ch.V2b[x] = from_f32<T>(val);
+          o[e] = 2.f * ch.U32[x] - ch.V1_32[x] - ch.P2_32[x];  // Y1
+        } else {
+          ch.V3_32[x] = val;
+        }
+      } else if (STEP == 1) {
+        ch.P2_32[x] = v[e];
+      } else if (STEP == 3) {
+        o[e] = -2.f * ch.U32[x] + 2.f * ch.V1_32[x] - ch.V2_32[x] + v[e];  // Y2
       } else {
         ch.dQ32[x] = 2.f * ch.U32[x] - 2.f * ch.V1_32[x] + 2.f * ch.V2_32[x] - ch.V3_32[x] + v[e];
       }
     }
-    if constexpr (STEP == 3 || STEP == 4) {
-      T* dst = (STEP == 3 ? ch.Y1tb : ch.Y2tb) + off + (int64_t)j * b + i0;
+    const bool wr = (STEP == 2 && right) || (STEP == 3 && !right);
+    if (wr) {
+      T* dst = (STEP == 2 ? ch.Y1tb : ch.Y2tb) + off + (int64_t)j * b + i0;
       if (i0 + 4 <= r)
         store4<T>(dst, o);
       else
@@ -283,13 +308,7 @@ hipError_t build_t(const float* q, int d, int b, T* g, void* ws, hipStream_t s) 
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t backward_t(const pxk::CnpSide* sides, int nsides, int b, void* ws, hipStream_t s) {
-  using C = typename CnpTile<T>::C;
-  const int nb0 = pxk::nblocks(sides[0].d, b);
-  const int nb1 = nsides > 1 ? pxk::nblocks(sides[1].d, b) : 0;
-  const int NB = nb0 + nb1;
-  const size_t E = (size_t)NB * b * b;
+template <typename T> Chain<T> carve(void* ws, size_t E) {
   char* w = reinterpret_cast<char*>(ws);
   auto takeT = [&]() {
     T* p = reinterpret_cast<T*>(w);
@@ -308,34 +327,57 @@ hipError_t backward_t(const pxk::CnpSide* sides, int nsides, int b, void* ws, hi
   ch.Utb = takeT();
   ch.V1_32 = takeF();
   ch.V1b = takeT();
+  ch.P2_32 = takeF();
   ch.V2_32 = takeF();
   ch.V2b = takeT();
   ch.V3_32 = takeF();
   ch.Y1tb = takeT();
   ch.Y2tb = takeT();
   ch.dQ32 = takeF();
-  Sides sd{{sides[0].q, nsides > 1 ? sides[1].q : sides[0].q}, {sides[0].d, nsides > 1 ? sides[1].d : sides[0].d}, nb0};
-  Parts pt{{sides[0].part, nsides > 1 ? sides[1].part : sides[0].part},
-           {sides[0].splits, nsides > 1 ? sides[1].splits : 0},
-           {nb0, nb1}};
-  DqOut out{{sides[0].dq, nsides > 1 ? sides[1].dq : sides[0].dq}};
+  return ch;
+}
+
+template <typename T>
+hipError_t grads_t(const pxk::CnpSide* sides, int rows, int b, void* ws, hipStream_t s) {
+  using C = typename CnpTile<T>::C;
+  const int nb0 = pxk::nblocks(sides[0].d, b), nb1 = pxk::nblocks(sides[1].d, b);
+  const int NB = nb0 + nb1;
+  Chain<T> ch = carve<T>(ws, (size_t)NB * b * b);
+  Sides sd{{sides[0].q, sides[1].q}, {sides[0].d, sides[1].d}, nb0};
+  GradSides<T> gs;
+  for (int k = 0; k < 2; ++k) {
+    gs.A[k] = reinterpret_cast<const T*>(sides[k].A);
+    gs.B[k] = reinterpret_cast<const T*>(sides[k].B);
+    gs.lda[k] = sides[k].lda;
+    gs.ldb[k] = sides[k].ldb;
+  }
   k_unpack_q<T><<<dim3(cdiv((int64_t)b * b, 256), NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb));
-  const int tpr = (b + 63) / 64;
-  k_reduce_u<T><<<dim3(tpr * tpr, NB), 256, 0, s>>>(pt, b, const_cast<float*>(ch.U32), const_cast<T*>(ch.Ub),
-                                                     const_cast<T*>(ch.Utb));
-  const int lds = Lay<C, T>::BYTES;
-  dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), NB);
+  const int lds = smem_bytes<C, T, T>();
+  hipError_t e = allow_lds(k_block_grads<C, T>, lds);
+  if (e != hipSuccess) return e;
+  dim3 grid(cdiv(b, C::BM) * cdiv(b, C::BN), NB);
+  k_block_grads<C, T><<<grid, C::NT, lds, s>>>(sd, gs, rows, b, ch);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t chain_t(const pxk::CnpSide* sides, int b, void* ws, hipStream_t s) {
+  using C = typename CnpTile<T>::C;
+  const int nb0 = pxk::nblocks(sides[0].d, b), nb1 = pxk::nblocks(sides[1].d, b);
+  const int NB = nb0 + nb1;
+  Chain<T> ch = carve<T>(ws, (size_t)NB * b * b);
+  Sides sd{{sides[0].q, sides[1].q}, {sides[0].d, sides[1].d}, nb0};
+  DqOut out{{sides[0].dq, sides[1].dq}};
+  const int lds = smem_bytes<C, T, T>();
   hipError_t e = hipSuccess;
-#define PX_CHAIN(K)                               \
-  e = allow_lds(k_cnp_chain<C, T, K>, lds);       \
-  if (e != hipSuccess) return e;                  \
-  k_cnp_chain<C, T, K><<<grid, C::NT, lds, s>>>(sd, b, ch);
-  PX_CHAIN(0)
-  PX_CHAIN(1)
-  PX_CHAIN(2)
-  PX_CHAIN(3)
-  PX_CHAIN(4)
-  PX_CHAIN(5)
+#define PX_CHAIN(K, MULT)                                                                  \
+  e = allow_lds(k_cnp_chain<C, T, K>, lds);                                                 \
+  if (e != hipSuccess) return e;                                                            \
+  k_cnp_chain<C, T, K><<<dim3(cdiv(b, C::BN), cdiv(b, C::BM), (MULT) * NB), C::NT, lds, s>>>(sd, b, NB, ch);
+  PX_CHAIN(1, 2)
+  PX_CHAIN(2, 1)
+  PX_CHAIN(3, 2)
+  PX_CHAIN(4, 1)
 #undef PX_CHAIN
   k_pack_dq<<<dim3(cdiv((int64_t)b * b, 256), NB), 256, 0, s>>>(sd, b, ch.dQ32, out);
   return hipGetLastError();
@@ -351,8 +393,8 @@ size_t cnp_build_ws_bytes(int dt, int d, int b) {
 }
 
 size_t cnp_backward_ws_bytes(int dt, int d0, int d1, int b) {
-  const size_t E = (size_t)(nblocks(d0, b) + (d1 > 0 ? nblocks(d1, b) : 0)) * b * b, es = dt_size(dt);
-  return al256(E * es) * 7 + al256(E * 4) * 5;
+  const size_t E = (size_t)(nblocks(d0, b) + nblocks(d1, b)) * b * b, es = dt_size(dt);
+  return al256(E * es) * 7 + al256(E * 4) * 6;
 }
 
 hipError_t cnp_build(int dt, const float* q, int d, int b, void* g, void* ws, hipStream_t s) {
@@ -360,9 +402,14 @@ hipError_t cnp_build(int dt, const float* q, int d, int b, void* g, void* ws, hi
   return build_t<float>(q, d, b, reinterpret_cast<float*>(g), ws, s);
 }
 
-hipError_t cnp_backward(int cdt, const CnpSide* sides, int nsides, int b, void* ws, hipStream_t s) {
-  if (cdt == BF16) return backward_t<bf16_t>(sides, nsides, b, ws, s);
-  return backward_t<float>(sides, nsides, b, ws, s);
+hipError_t block_grads(int cdt, const CnpSide* sides, int rows, int b, void* ws, hipStream_t s) {
+  if (cdt == BF16) return grads_t<bf16_t>(sides, rows, b, ws, s);
+  return grads_t<float>(sides, rows, b, ws, s);
+}
+
+hipError_t cnp_chain(int cdt, const CnpSide* sides, int b, void* ws, hipStream_t s) {
+  if (cdt == BF16) return chain_t<bf16_t>(sides, b, ws, s);
+  return chain_t<float>(sides, b, ws, s);
 }
 
 }  // namespace pxk

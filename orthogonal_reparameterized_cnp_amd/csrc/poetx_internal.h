@@ -44,21 +44,21 @@ hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, in
 hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const void* B, int64_t ldb, bool b_kn, int M,
                 int N, int K, const float* colscale, int out_dt, void* out, int64_t ldo, hipStream_t s);
 
-// part[s][blk][i][j] = sum_{t in split s} A[t][kb+i] * B[t][kb+j]  (fp32, all b x b entries written)
-hipError_t dgrad(int cdt, const void* A, int64_t lda, const void* B, int64_t ldb, int rows, int d, int b, int splits,
-                 float* part, hipStream_t s);
-int dgrad_splits(int rows, int d, int b);
-
-// CNP chain rule for one or two sides of a linear: token-split partials of
-// dG -> packed dq (overwritten).  ws of cnp_backward_ws_bytes bytes.
+// Block gradients and CNP chain rule of both sides of a linear (side 0 = R,
+// side 1 = P), sharing one scratch of cnp_backward_ws_bytes bytes:
+//   block_grads: U_s[blk] = sum over all rows t of A_s[t][blk cols]^T B_s[t][blk cols]
+//   cnp_chain:   U -> dQ through the CNP chain rule -> packed dq (overwritten)
 struct CnpSide {
   const float* q;
   int d;
-  const float* part;  // [splits][nb][b][b] fp32
-  int splits;
+  const void* A;  // [rows][lda]: Xt for R, H for P
+  int64_t lda;
+  const void* B;  // [rows][ldb]: dA for R, dZt for P
+  int64_t ldb;
   float* dq;
 };
-hipError_t cnp_backward(int cdt, const CnpSide* sides, int nsides, int b, void* ws, hipStream_t s);
+hipError_t block_grads(int cdt, const CnpSide* sides, int rows, int b, void* ws, hipStream_t s);
+hipError_t cnp_chain(int cdt, const CnpSide* sides, int b, void* ws, hipStream_t s);
 size_t cnp_backward_ws_bytes(int dt, int d0, int d1, int b);
 
 // Merge helpers (fp32 MFMA).

@@ -108,32 +108,6 @@ __global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_
 }
 
 // ============================================================================
-// block gradients: part[s][blk][i][j] = sum_{t in split s} A[t][kb+i] B[t][kb+j]
-// ============================================================================
-template <class C, typename T, typename IT>
-__global__ __launch_bounds__(C::NT) void k_dgrad(const IT* __restrict__ A, int64_t lda, const IT* __restrict__ B,
-                                                  int64_t ldb, int rows, int d, int b, int tchunk,
-                                                  float* __restrict__ part) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* lds = reinterpret_cast<T*>(smem);
-  const int tiles_n = (b + C::BN - 1) / C::BN;
-  const int m0 = (blockIdx.x / tiles_n) * C::BM, n0 = (blockIdx.x % tiles_n) * C::BN;
-  const int blk = blockIdx.y, nb = gridDim.y, s = blockIdx.z;
-  const int kb = blk * b, r = min(b, d - kb);
-  const int t0 = s * tchunk, t1 = min(rows, t0 + tchunk);
-  const int K = max(0, t1 - t0);
-  LoadMN<C::BM, C::BK, C::NT, IT, T> la;
-  la.init(A + (int64_t)t0 * lda + kb + m0, lda, r - m0, K);
-  LoadMN<C::BN, C::BK, C::NT, IT, T> lb;
-  lb.init(B + (int64_t)t0 * ldb + kb + n0, ldb, r - n0, K);
-  Acc<C> acc;
-  const AccPos<C> p = acc_pos<C>();
-  mainloop<C, T>(lds, la, lb, K, acc, p.wm, p.wn, p.lane);
-  float* out = part + ((int64_t)s * nb + blk) * b * b;
-  store_tile<C, float>(acc, smem, out + (int64_t)m0 * b + n0, b, b - m0, b - n0, Unit());
-}
-
-// ============================================================================
 // permutations
 // ============================================================================
 // Row-staged gather: the workgroup copies whole source rows into LDS with
@@ -459,36 +433,6 @@ hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const v
     return b_kn ? gemm_t<TF, float, float, float, float, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
                 : gemm_t<TF, float, float, float, float, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
   return hipErrorInvalidValue;
-}
-
-int dgrad_splits(int rows, int d, int b) {
-  const int nb = nblocks(d, b);
-  const int t = (b + 127) / 128;
-  const int tiles = t * t * nb;
-  int splits = (1024 + tiles - 1) / tiles;
-  splits = std::min(splits, std::max(1, rows / 256));
-  return std::max(1, std::min(splits, 64));
-}
-
-template <class C, typename T>
-static hipError_t dgrad_t(const void* A, int64_t lda, const void* B, int64_t ldb, int rows, int d, int b, int splits,
-                          float* part, hipStream_t s) {
-  const int lds = smem_bytes<C, T, float>();
-  auto k = k_dgrad<C, T, T>;
-  hipError_t e = allow_lds(k, lds);
-  if (e != hipSuccess) return e;
-  int tchunk = (rows + splits - 1) / splits;
-  tchunk = (int)round_up(std::max(tchunk, 1), C::BK);
-  dim3 grid(cdiv(b, C::BM) * cdiv(b, C::BN), nblocks(d, b), splits);
-  k<<<grid, C::NT, lds, s>>>(reinterpret_cast<const T*>(A), lda, reinterpret_cast<const T*>(B), ldb, rows, d, b,
-                             tchunk, part);
-  return hipGetLastError();
-}
-
-hipError_t dgrad(int cdt, const void* A, int64_t lda, const void* B, int64_t ldb, int rows, int d, int b, int splits,
-                 float* part, hipStream_t s) {
-  if (cdt == BF16) return dgrad_t<TSq, bf16_t>(A, lda, B, ldb, rows, d, b, splits, part, s);
-  return dgrad_t<TF, float>(A, lda, B, ldb, rows, d, b, splits, part, s);
 }
 
 template <typename GT, typename WT>
