@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "mfma_dma.h"
 #include "mfma_tile.h"
 #include "poetx_internal.h"
 
@@ -13,11 +14,16 @@ namespace px {
 using TGemm = Tile<256, 256, 64, 4, 2>;  // bf16: W~ contractions and block products (8 waves of 64 x 128)
 using TBig = Tile<256, 128, 64, 2, 2>;   // bf16: narrow contractions
 using TSq = Tile<128, 128, 64, 2, 2>;   // bf16: block gradients, CNP (b x b outputs)
+// direct-to-LDS configurations (K-contiguous operands, interior tiles)
+using DGemm = DCfg<256, 256, 64, 2, 4, 2, false, false, true>;  // 8 waves, same block size as TGemm
+using DSq = DCfg<128, 128, 64, 2, 2, 3, false, false, true>;    // 4 waves, same block size as TSq
 using TF = Tile<64, 64, 32, 2, 2>;      // fp32: small layers
 using TFM = Tile<128, 128, 32, 2, 2>;   // fp32: merge products
 
+// wave position inside the C::NT threads that share one tile (a workgroup may
+// hold several such groups, each with its own K range)
 template <class C> PX_DEV AccPos<C> acc_pos() {
-  const int w = threadIdx.x >> 6;
+  const int w = (int)(threadIdx.x % C::NT) >> 6;
   return AccPos<C>{w / C::WN, w % C::WN, (int)(threadIdx.x & 63)};
 }
 
@@ -108,11 +114,47 @@ PX_DEV void store_tile(const Acc<C>& acc, void* lds, OT* out, int64_t ldo, int r
   }
 }
 
+template <class A> using cfg_of = typename std::decay_t<A>::Cfg;
+
+// f[i][j][e] = src[(row0 + row) * ld + col0 + col] at the calling lane's
+// accumulator positions, with row0 + row and col0 + col clamped to
+// [0, rmax) x [0, cmax) so that every load is in range and none is predicated:
+// all of them are issued before the first is used.
+template <class C>
+PX_DEV void load_at_acc(float (&f)[C::TM][C::TN][16], const float* src, int64_t ld, int row0, int col0, int rmax,
+                        int cmax) {
+  const AccPos<C> p = acc_pos<C>();
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+      const int c = min(col0 + p.col(j), cmax - 1);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) f[i][j][e] = src[(int64_t)min(row0 + p.row(i, e), rmax - 1) * ld + c];
+    }
+}
+
+// true when a K-contiguous operand tile can be copied with 16-byte DMA:
+// all rows present, base 16-byte aligned, row pitch a multiple of 8 elements
+PX_DEV bool dma_rows_ok(const void* base, int64_t ld, int rows_avail, int rows_tile) {
+  return rows_avail >= rows_tile && (reinterpret_cast<uintptr_t>(base) % 16 == 0) && (ld % 8 == 0);
+}
+
 // dynamic LDS for a kernel: the double-buffered operand tiles, or the
 // epilogue's staging tile if that is larger
 template <class C, typename T, typename OT> constexpr int smem_bytes() {
   constexpr int epi = C::BM * (C::BN + 16 / (int)sizeof(OT)) * (int)sizeof(OT);
   return Lay<C, T>::BYTES > epi ? Lay<C, T>::BYTES : epi;
+}
+
+template <class CD> constexpr int dma_smem_bytes() {
+  if constexpr (std::is_same<CD, void>::value) {
+    return 0;
+  } else {
+    // bf16 staging of the whole tile (either orientation)
+    constexpr int epi = (CD::BM > CD::BN ? CD::BM : CD::BN) * ((CD::BM > CD::BN ? CD::BM : CD::BN) + 8) * 2;
+    return CD::LDS_BYTES > epi ? CD::LDS_BYTES : epi;
+  }
 }
 
 struct Unit {

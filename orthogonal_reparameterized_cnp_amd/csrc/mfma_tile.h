@@ -41,6 +41,7 @@ template <class C, typename T> struct Lay {
 };
 
 template <class C> struct Acc {
+  using Cfg = C;
   f32x16_v v[C::TM][C::TN];
   PX_DEV void zero() {
 #pragma unroll
@@ -299,7 +300,7 @@ struct LoadK {
     if constexpr (FAST) {  // whole tile inside: unconditional vector loads
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const int ch = threadIdx.x + i * NT;
+        const int ch = (int)(threadIdx.x % NT) + i * NT;
         if (TOT % NT != 0 && ch >= TOT) break;
         Load8<D, S>::go(base + (int64_t)(ch / CPR) * ld + k0 + (ch % CPR) * 8, c[i]);
       }
@@ -307,7 +308,7 @@ struct LoadK {
     }
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ch = threadIdx.x + i * NT;
+      const int ch = (int)(threadIdx.x % NT) + i * NT;
       if (TOT % NT != 0 && ch >= TOT) break;
       const int r = ch / CPR, k = k0 + (ch % CPR) * 8;
       const S* p = base + (int64_t)r * ld + k;
@@ -326,7 +327,7 @@ struct LoadK {
     constexpr int LDK = BK + LdsPad<D>::v;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ch = threadIdx.x + i * NT;
+      const int ch = (int)(threadIdx.x % NT) + i * NT;
       if (TOT % NT != 0 && ch >= TOT) break;
       const int r = ch / CPR, kc = (ch % CPR) * 8;
       if constexpr (sizeof(D) == 2) {
@@ -371,7 +372,7 @@ struct LoadMN {
     if constexpr (FAST) {  // whole tile inside: unconditional vector loads
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const int unit = threadIdx.x + u * NT;
+        const int unit = (int)(threadIdx.x % NT) + u * NT;
         if (TOT % NT != 0 && unit >= TOT) break;
         const S* p = base + (int64_t)(k0 + (unit % KQ) * 4) * ld + (unit / KQ) * 8;
 #pragma unroll
@@ -381,7 +382,7 @@ struct LoadMN {
     }
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int unit = threadIdx.x + u * NT;
+      const int unit = (int)(threadIdx.x % NT) + u * NT;
       if (TOT % NT != 0 && unit >= TOT) break;
       const int r0 = (unit / KQ) * 8, kq = k0 + (unit % KQ) * 4;
 #pragma unroll
@@ -404,7 +405,7 @@ struct LoadMN {
     constexpr int LDK = BK + LdsPad<D>::v;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
-      const int unit = threadIdx.x + u * NT;
+      const int unit = (int)(threadIdx.x % NT) + u * NT;
       if (TOT % NT != 0 && unit >= TOT) break;
       const int r0 = (unit / KQ) * 8, kq = (unit % KQ) * 4;
 #pragma unroll

@@ -14,7 +14,9 @@
 // row-major operands.  Products with Q on the right load Q's rows as the B
 // operand, which yields X Q^T = -X Q (the sign is folded into the epilogue);
 // products with a non-symmetric matrix on the right read the transpose that
-// the producing epilogue wrote.
+// the producing epilogue wrote.  The linear combinations X0..X2 are carried
+// in one fp32 array that each step updates in place, so every step reads and
+// writes each element once.
 #include "kernel_util.h"
 
 using namespace px;
@@ -34,25 +36,126 @@ struct Sides {
   }
 };
 
+
+// K loop over two K-contiguous bf16/fp32 operand tiles (row pitch b): the
+// direct-to-LDS loop for interior bf16 tiles, else the checked register loop.
+template <class C, typename T, class Epi>
+PX_DEV void run_kk(unsigned char* smem, const T* a0, int rows_a, const T* b0, int rows_b, int b, int K, Epi&& epi) {
+  if constexpr (std::is_same<T, bf16_t>::value && C::BM == DSq::BM && C::BN == DSq::BN && C::NT == DSq::NT) {
+    if (dma_rows_ok(a0, b, rows_a, DSq::BM) && dma_rows_ok(b0, b, rows_b, DSq::BN) && K % DSq::BK == 0) {
+      Acc<DSq> acc;
+      const AccPos<DSq> p = acc_pos<DSq>();
+      const DmaSrc src{reinterpret_cast<const bf16_t*>(a0), b, reinterpret_cast<const bf16_t*>(b0), b};
+      dma_mainloop<DSq>(reinterpret_cast<char*>(smem), src, K / DSq::BK, acc, p.wm, p.wn, p.lane, NoHook());
+      epi(acc);
+      return;
+    }
+  }
+  LoadK<C::BM, C::BK, C::NT, T, T> la;
+  la.init(a0, b, rows_a, K);
+  LoadK<C::BN, C::BK, C::NT, T, T> lb;
+  lb.init(b0, b, rows_b, K);
+  Acc<C> acc;
+  const AccPos<C> p = acc_pos<C>();
+  mainloop<C, T>(reinterpret_cast<T*>(smem), la, lb, K, acc, p.wm, p.wn, p.lane);
+  epi(acc);
+}
+
+// Two products of the same shape, X0 Y0^T and X1 Y1^T, one after the other in
+// the same workgroup; epi(acc0, acc1).  Both take the same loop.
+template <class C, typename T, class Epi>
+PX_DEV void run_kk2(unsigned char* smem, const T* x0, const T* y0, const T* x1, const T* y1, int rows_x, int rows_y,
+                    int b, int K, Epi&& epi) {
+  if constexpr (std::is_same<T, bf16_t>::value && C::BM == DSq::BM && C::BN == DSq::BN && C::NT == DSq::NT) {
+    if (dma_rows_ok(x0, b, rows_x, DSq::BM) && dma_rows_ok(x1, b, rows_x, DSq::BM) &&
+        dma_rows_ok(y0, b, rows_y, DSq::BN) && dma_rows_ok(y1, b, rows_y, DSq::BN) && K % DSq::BK == 0) {
+      Acc<DSq> a0, a1;
+      const AccPos<DSq> p = acc_pos<DSq>();
+      const DmaSrc s0{reinterpret_cast<const bf16_t*>(x0), b, reinterpret_cast<const bf16_t*>(y0), b};
+      dma_mainloop<DSq>(reinterpret_cast<char*>(smem), s0, K / DSq::BK, a0, p.wm, p.wn, p.lane, NoHook());
+      __syncthreads();
+      const DmaSrc s1{reinterpret_cast<const bf16_t*>(x1), b, reinterpret_cast<const bf16_t*>(y1), b};
+      dma_mainloop<DSq>(reinterpret_cast<char*>(smem), s1, K / DSq::BK, a1, p.wm, p.wn, p.lane, NoHook());
+      epi(a0, a1);
+      return;
+    }
+  }
+  const AccPos<C> p = acc_pos<C>();
+  Acc<C> a0, a1;
+  {
+    LoadK<C::BM, C::BK, C::NT, T, T> la;
+    la.init(x0, b, rows_x, K);
+    LoadK<C::BN, C::BK, C::NT, T, T> lb;
+    lb.init(y0, b, rows_y, K);
+    mainloop<C, T>(reinterpret_cast<T*>(smem), la, lb, K, a0, p.wm, p.wn, p.lane);
+  }
+  __syncthreads();
+  {
+    LoadK<C::BM, C::BK, C::NT, T, T> la;
+    la.init(x1, b, rows_x, K);
+    LoadK<C::BN, C::BK, C::NT, T, T> lb;
+    lb.init(y1, b, rows_y, K);
+    mainloop<C, T>(reinterpret_cast<T*>(smem), la, lb, K, a1, p.wm, p.wn, p.lane);
+  }
+  epi(a0, a1);
+}
+
+// Dense Q from the packed parameters, one 64 x 64 tile per workgroup: entries
+// above the diagonal are read along packed rows; entries below it come from
+// the mirrored tile, staged through LDS so that both reads and writes are
+// row-contiguous.  Writes the operand copy Qb and, if Q32 is set, an fp32 copy.
 template <typename T>
-__global__ void k_unpack_q(Sides sd, int b, T* __restrict__ Qb) {
+__global__ __launch_bounds__(256) void k_unpack_q(Sides sd, int b, T* __restrict__ Qb, float* __restrict__ Q32) {
+  __shared__ float t[64][65];
   const int z = blockIdx.y;
   const float* qk;
   int r;
   sd.at(z, b, qk, r);
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (int64_t)b * b) return;
-  const int i = (int)(e / b), j = (int)(e % b);
-  Qb[(int64_t)z * b * b + e] = from_f32<T>(skew_at(qk, i, j, r, b));
+  const int tiles = (b + 63) / 64;
+  const int i0 = (blockIdx.x / tiles) * 64, j0 = (blockIdx.x % tiles) * 64;
+  const int c = threadIdx.x & 63, rr = threadIdx.x >> 6;
+  // a block of size b has b (b - 1) / 2 slots; with none (b = 1) Q is zero
+  const bool any = b > 1;
+  // every load below reads a valid slot (slot 0 stands in for masked ones)
+  if (i0 >= j0) {
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int j = j0 + rr + 4 * k, i = i0 + c;
+      const bool ok = any && j < i && i < r;
+      v[k] = qk[ok ? packed_slot(j, i, b) : 0];
+      v[k] = ok ? v[k] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) t[rr + 4 * k][c] = v[k];
+  }
+  __syncthreads();
+  float u[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int i = i0 + rr + 4 * k, j = j0 + c;
+    const bool ok = any && i < j && j < r;
+    u[k] = qk[ok ? packed_slot(i, j, b) : 0];
+    u[k] = ok ? u[k] : 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int ii = rr + 4 * k, i = i0 + ii, j = j0 + c;
+    if (i >= b || j >= b) continue;
+    const float v = (j < i && i < r) ? -t[c][ii] : u[k];
+    const int64_t e = (int64_t)z * b * b + (int64_t)i * b + j;
+    Qb[e] = from_f32<T>(v);
+    if (Q32) Q32[e] = v;
+  }
 }
 
-// S = Q Q = -(Q Q^T); writes S (fp32 and operand dtype) and N^T = S - 2Q.
+// S = Q Q = -(Q Q^T).  Writes S and N^T = S - 2Q in the operand dtype, and
+// replaces Q32 in place by the fp32 partial sum 2Q + 2S.
 template <class C, typename T>
 __global__ __launch_bounds__(C::NT) void k_cnp_square(Sides sd, int b, const T* __restrict__ Qb,
-                                                      float* __restrict__ S32, T* __restrict__ Sb,
+                                                      float* __restrict__ Q32, T* __restrict__ Sb,
                                                       T* __restrict__ Ntb) {
   extern __shared__ __align__(16) unsigned char smem[];
-  T* lds = reinterpret_cast<T*>(smem);
   const int z = blockIdx.z;
   const float* qk;
   int r;
@@ -60,63 +163,73 @@ __global__ __launch_bounds__(C::NT) void k_cnp_square(Sides sd, int b, const T* 
   const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
   if (m0 >= r || n0 >= r) return;  // nothing outside the live corner is read later
   const int64_t off = (int64_t)z * b * b;
-  LoadK<C::BM, C::BK, C::NT, T, T> la;
-  la.init(Qb + off + (int64_t)m0 * b, b, r - m0, r);
-  LoadK<C::BN, C::BK, C::NT, T, T> lb;
-  lb.init(Qb + off + (int64_t)n0 * b, b, r - n0, r);
-  Acc<C> acc;
-  const AccPos<C> p = acc_pos<C>();
-  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
-  each_acc<C>(acc, [&](int i, int j, float v) {
-    i += m0;
-    j += n0;
-    if (i < r && j < r) {
-      const int64_t e = off + (int64_t)i * b + j;
-      const float s = -v;
-      S32[e] = s;
-      Sb[e] = from_f32<T>(s);
-      Ntb[e] = from_f32<T>(s - 2.f * skew_at(qk, i, j, r, b));
-    }
+  run_kk<C, T>(smem, Qb + off + (int64_t)m0 * b, r - m0, Qb + off + (int64_t)n0 * b, r - n0, b, r, [&](auto& acc) {
+    using CC = cfg_of<decltype(acc)>;
+    float q[CC::TM][CC::TN][16];
+    load_at_acc<CC>(q, Q32 + off, b, m0, n0, r, r);
+    const AccPos<CC> p = acc_pos<CC>();
+#pragma unroll
+    for (int ti = 0; ti < CC::TM; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < CC::TN; ++tj) {
+        const int j = n0 + p.col(tj);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int i = m0 + p.row(ti, e);
+          if (i < r && j < r) {
+            const int64_t x = off + (int64_t)i * b + j;
+            const float sv = -acc.v[ti][tj][e], qv = q[ti][tj][e];
+            Q32[x] = 2.f * qv + 2.f * sv;
+            Sb[x] = from_f32<T>(sv);
+            Ntb[x] = from_f32<T>(sv - 2.f * qv);
+          }
+        }
+      }
   });
 }
 
-// G - I = 2Q + 2S + S N, written as slice 0 (row-major) and slice 1 (transposed)
+// G - I = (2Q + 2S) + S N, written as slice 0 (row-major) and slice 1
+// (transposed); zero outside the live r x r corner.
 template <class C, typename T>
-__global__ __launch_bounds__(C::NT) void k_cnp_delta(Sides sd, int b, int nb_all, const float* __restrict__ S32,
+__global__ __launch_bounds__(C::NT) void k_cnp_delta(Sides sd, int b, int nb_all, const float* __restrict__ T2,
                                                      const T* __restrict__ Sb, const T* __restrict__ Ntb,
                                                      T* __restrict__ g) {
   extern __shared__ __align__(16) unsigned char smem[];
-  T* lds = reinterpret_cast<T*>(smem);
   const int z = blockIdx.z;
   const float* qk;
   int r;
   sd.at(z, b, qk, r);
   const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
   const int64_t off = (int64_t)z * b * b;
-  LoadK<C::BM, C::BK, C::NT, T, T> la;
-  la.init(Sb + off + (int64_t)m0 * b, b, r - m0, r);
-  LoadK<C::BN, C::BK, C::NT, T, T> lb;
-  lb.init(Ntb + off + (int64_t)n0 * b, b, r - n0, r);
-  Acc<C> acc;
-  const AccPos<C> p = acc_pos<C>();
-  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
   T* g0 = g + off;
   T* g1 = g + (int64_t)nb_all * b * b + off;
-  each_acc4<C>(acc, [&](int i0, int j, const float* v) {
-    i0 += m0;
-    j += n0;
-    if (j >= b || i0 >= b) return;
-    float o[4];
+  run_kk<C, T>(smem, Sb + off + (int64_t)m0 * b, r - m0, Ntb + off + (int64_t)n0 * b, r - n0, b, r, [&](auto& acc) {
+    using CC = cfg_of<decltype(acc)>;
+    float t2[CC::TM][CC::TN][16];
+    load_at_acc<CC>(t2, T2 + off, b, m0, n0, max(r, 1), max(r, 1));
+    const AccPos<CC> p = acc_pos<CC>();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = i0 + e;
-      o[e] = (i < r && j < r) ? v[e] + 2.f * skew_at(qk, i, j, r, b) + 2.f * S32[off + (int64_t)i * b + j] : 0.f;
-      if (i < b) g0[(int64_t)i * b + j] = from_f32<T>(o[e]);
-    }
-    if (i0 + 4 <= b)
-      store4<T>(g1 + (int64_t)j * b + i0, o);
-    else
-      for (int e = 0; e < 4 && i0 + e < b; ++e) g1[(int64_t)j * b + i0 + e] = from_f32<T>(o[e]);
+    for (int ti = 0; ti < CC::TM; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < CC::TN; ++tj) {
+        const int j = n0 + p.col(tj);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int i0 = m0 + p.row(ti, 4 * g);
+          if (j >= b || i0 >= b) continue;
+          float o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = i0 + e;
+            o[e] = (i < r && j < r) ? acc.v[ti][tj][4 * g + e] + t2[ti][tj][4 * g + e] : 0.f;
+            if (i < b) g0[(int64_t)i * b + j] = from_f32<T>(o[e]);
+          }
+          if (i0 + 4 <= b)
+            store4<T>(g1 + (int64_t)j * b + i0, o);
+          else
+            for (int e = 0; e < 4 && i0 + e < b; ++e) g1[(int64_t)j * b + i0 + e] = from_f32<T>(o[e]);
+        }
+      }
   });
 }
 
@@ -133,24 +246,24 @@ template <typename T> struct GradSides {
 
 template <typename T> struct Chain {
   const T* Qb;
-  float* U32;
+  float* F32;  // U, then 2U - 2V1, then (2U - 2V1) + 2V2, then dQ (updated in place)
   T* Ub;
   T* Utb;
-  float* V1_32;
   T* V1b;
-  float* P2_32;  // Q U
-  float* V2_32;
   T* V2b;
-  float* V3_32;
   T* Y1tb;
   T* Y2tb;
-  float* dQ32;
 };
 
-template <class C, typename T>
-__global__ __launch_bounds__(C::NT) void k_block_grads(Sides sd, GradSides<T> gs, int rows, int b, Chain<T> ch) {
+// G groups of C::NT threads split the token range of one output tile; their
+// partial sums are added in group order through LDS, so results do not depend
+// on timing.  The launcher uses G > 1 only when rows is a multiple of G * BK,
+// so that every group runs the same number of K steps (and barriers).
+template <class C, typename T, int G>
+__global__ __launch_bounds__(C::NT * G) void k_block_grads(Sides sd, GradSides<T> gs, int rows, int b, Chain<T> ch) {
   extern __shared__ __align__(16) unsigned char smem[];
-  T* lds = reinterpret_cast<T*>(smem);
+  const int grp = G == 1 ? 0 : (int)(threadIdx.x / C::NT);
+  T* lds = reinterpret_cast<T*>(smem + grp * Lay<C, T>::BYTES);
   const int z = blockIdx.y;
   const int s = z >= sd.nb0;
   const int blk = z - s * sd.nb0;
@@ -158,13 +271,39 @@ __global__ __launch_bounds__(C::NT) void k_block_grads(Sides sd, GradSides<T> gs
   const int tiles_n = (b + C::BN - 1) / C::BN;
   const int m0 = (blockIdx.x / tiles_n) * C::BM, n0 = (blockIdx.x % tiles_n) * C::BN;
   if (m0 >= r || n0 >= r) return;  // only the live corner is read later
+  const int per = rows / G;
+  const int64_t t0 = (int64_t)grp * per;
   LoadMN<C::BM, C::BK, C::NT, T, T> la;
-  la.init(gs.A[s] + kb + m0, gs.lda[s], r - m0, rows);
+  la.init(gs.A[s] + t0 * gs.lda[s] + kb + m0, gs.lda[s], r - m0, per);
   LoadMN<C::BN, C::BK, C::NT, T, T> lb;
-  lb.init(gs.B[s] + kb + n0, gs.ldb[s], r - n0, rows);
+  lb.init(gs.B[s] + t0 * gs.ldb[s] + kb + n0, gs.ldb[s], r - n0, per);
   Acc<C> acc;
   const AccPos<C> p = acc_pos<C>();
-  mainloop<C, T>(lds, la, lb, rows, acc, p.wm, p.wn, p.lane);
+  mainloop<C, T>(lds, la, lb, per, acc, p.wm, p.wn, p.lane);
+  if constexpr (G > 1) {
+    // the loop ended with a barrier: the operand tiles are free for the fold
+    constexpr int PITCH = C::BN + 4;
+    float* red = reinterpret_cast<float*>(smem);
+    for (int g = 1; g < G; ++g) {
+      if (grp == g)
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) red[p.row(i, e) * PITCH + p.col(j)] = acc.v[i][j][e];
+      __syncthreads();
+      if (grp == 0)
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc.v[i][j][e] += red[p.row(i, e) * PITCH + p.col(j)];
+      __syncthreads();
+    }
+    if (grp != 0) return;
+  }
   const int64_t off = (int64_t)z * b * b;
   each_acc4<C>(acc, [&](int i0, int j, const float* v) {
     i0 += m0;
@@ -174,7 +313,7 @@ __global__ __launch_bounds__(C::NT) void k_block_grads(Sides sd, GradSides<T> gs
     for (int e = 0; e < 4; ++e) {
       if (i0 + e >= r) continue;
       const int64_t x = off + (int64_t)(i0 + e) * b + j;
-      ch.U32[x] = v[e];
+      ch.F32[x] = v[e];
       ch.Ub[x] = from_f32<T>(v[e]);
     }
     T* dst = ch.Utb + off + (int64_t)j * b + i0;
@@ -185,77 +324,68 @@ __global__ __launch_bounds__(C::NT) void k_block_grads(Sides sd, GradSides<T> gs
   });
 }
 
-// Chain rule in four launches (see the file header for V1..V3, X0..X3):
-//   step 1: V1 = U Q            and  P2 = Q U          (2 NB blocks of work)
-//   step 2: V2 = V1 Q           with Y1 = 2U - V1 - P2 written transposed
-//   step 3: V3 = V2 Q           and  Y2 = -2U + 2V1 - V2 + Q Y1 (transposed)
-//   step 4: dQ = 2U - 2V1 + 2V2 - V3 + Q Y2
-// Products X Q load Q's rows as the B operand and negate (X Q^T = -X Q).
+// Chain rule in three launches; each workgroup forms one tile of two
+// products, X Q (X = U, V1, V2) and Q Y (Y = U, Y1, Y2):
+//   step 1: V1 = U Q,  P = Q U;   Y1 = 2U - V1 - P,         F = 2U - 2V1
+//   step 2: V2 = V1 Q, Q Y1;      Y2 = -F - V2 + Q Y1,      F = F + 2V2
+//   step 3: V3 = V2 Q, Q Y2;      dQ = F - V3 + Q Y2
+// X Q loads Q's rows as the B operand, which gives X Q^T = -X Q; Q Y loads
+// the rows of Y^T, which the previous step wrote.
 template <class C, typename T, int STEP>
-__global__ __launch_bounds__(C::NT) void k_cnp_chain(Sides sd, int b, int NB, Chain<T> ch) {
+__global__ __launch_bounds__(C::NT) void k_cnp_step(Sides sd, int b, Chain<T> ch) {
   extern __shared__ __align__(16) unsigned char smem[];
-  T* lds = reinterpret_cast<T*>(smem);
-  const bool second = (STEP == 1 || STEP == 3) && (int)blockIdx.z >= NB;
-  const int z = blockIdx.z - (second ? NB : 0);
+  const int z = blockIdx.z;
   const float* qk;
   int r;
   sd.at(z, b, qk, r);
   const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
   if (m0 >= r || n0 >= r) return;  // later steps and the packing read only the live corner
   const int64_t off = (int64_t)z * b * b;
-  // right-multiplication by Q (first products of steps 1-3) or left-multiplication (the rest)
-  const bool right = (STEP <= 3) && !second;
-  LoadK<C::BM, C::BK, C::NT, T, T> la;
-  LoadK<C::BN, C::BK, C::NT, T, T> lb;
-  if (right) {
-    const T* src = STEP == 1 ? ch.Ub : STEP == 2 ? ch.V1b : ch.V2b;
-    la.init(src + off + (int64_t)m0 * b, b, r - m0, r);
-    lb.init(ch.Qb + off + (int64_t)n0 * b, b, r - n0, r);
-  } else {
-    const T* srcT = STEP == 1 ? ch.Utb : STEP == 3 ? ch.Y1tb : ch.Y2tb;
-    la.init(ch.Qb + off + (int64_t)m0 * b, b, r - m0, r);
-    lb.init(srcT + off + (int64_t)n0 * b, b, r - n0, r);
-  }
-  Acc<C> acc;
-  const AccPos<C> p = acc_pos<C>();
-  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane);
-  each_acc4<C>(acc, [&](int i0, int j, const float* v) {
-    i0 += m0;
-    j += n0;
-    if (j >= r || i0 >= r) return;
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
+  const T* X = STEP == 1 ? ch.Ub : STEP == 2 ? ch.V1b : ch.V2b;
+  const T* Yt = STEP == 1 ? ch.Utb : STEP == 2 ? ch.Y1tb : ch.Y2tb;
+  run_kk2<C, T>(smem, X + off + (int64_t)m0 * b, ch.Qb + off + (int64_t)n0 * b, ch.Qb + off + (int64_t)m0 * b,
+                Yt + off + (int64_t)n0 * b, r - m0, r - n0, b, r, [&](auto& xq, auto& qy) {
+    using CC = cfg_of<decltype(xq)>;
+    float f[CC::TM][CC::TN][16];
+    load_at_acc<CC>(f, ch.F32 + off, b, m0, n0, r, r);
+    const AccPos<CC> p = acc_pos<CC>();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (i0 + e >= r) continue;
-      const int64_t x = off + (int64_t)(i0 + e) * b + j;
-      if (right) {
-        const float val = -v[e];
-        if (STEP == 1) {
-          ch.V1_32[x] = val;
-          ch.V1b[x] = from_f32<T>(val);
-        } else if (STEP == 2) {
-          ch.V2_32[x] = val;
-          ch.V2b[x] = from_f32<T>(val);
-          o[e] = 2.f * ch.U32[x] - ch.V1_32[x] - ch.P2_32[x];  // Y1
-        } else {
-          ch.V3_32[x] = val;
+    for (int ti = 0; ti < CC::TM; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < CC::TN; ++tj) {
+        const int j = n0 + p.col(tj);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int i0 = m0 + p.row(ti, 4 * g);
+          if (j >= r || i0 >= r) continue;
+          float y[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (i0 + e >= r) continue;
+            const int k = 4 * g + e;
+            const int64_t x = off + (int64_t)(i0 + e) * b + j;
+            const float fv = f[ti][tj][k], v = -xq.v[ti][tj][k], c = qy.v[ti][tj][k];
+            if (STEP == 1) {
+              ch.V1b[x] = from_f32<T>(v);
+              ch.F32[x] = 2.f * fv - 2.f * v;
+              y[e] = 2.f * fv - v - c;
+            } else if (STEP == 2) {
+              ch.V2b[x] = from_f32<T>(v);
+              ch.F32[x] = fv + 2.f * v;
+              y[e] = -fv - v + c;
+            } else {
+              ch.F32[x] = fv - v + c;
+            }
+          }
+          if (STEP <= 2) {
+            T* dst = (STEP == 1 ? ch.Y1tb : ch.Y2tb) + off + (int64_t)j * b + i0;
+            if (i0 + 4 <= r)
+              store4<T>(dst, y);
+            else
+              for (int e = 0; e < 4 && i0 + e < r; ++e) dst[e] = from_f32<T>(y[e]);
+          }
         }
-      } else if (STEP == 1) {
-        ch.P2_32[x] = v[e];
-      } else if (STEP == 3) {
-        o[e] = -2.f * ch.U32[x] + 2.f * ch.V1_32[x] - ch.V2_32[x] + v[e];  // Y2
-      } else {
-        ch.dQ32[x] = 2.f * ch.U32[x] - 2.f * ch.V1_32[x] + 2.f * ch.V2_32[x] - ch.V3_32[x] + v[e];
       }
-    }
-    const bool wr = (STEP == 2 && right) || (STEP == 3 && !right);
-    if (wr) {
-      T* dst = (STEP == 2 ? ch.Y1tb : ch.Y2tb) + off + (int64_t)j * b + i0;
-      if (i0 + 4 <= r)
-        store4<T>(dst, o);
-      else
-        for (int e = 0; e < 4 && i0 + e < r; ++e) dst[e] = from_f32<T>(o[e]);
-    }
   });
 }
 
@@ -263,18 +393,41 @@ struct DqOut {
   float* dq[2];
 };
 
-__global__ void k_pack_dq(Sides sd, int b, const float* __restrict__ dQ32, DqOut out) {
+// dq[p(i, j)] = dQ[i][j] - dQ[j][i] for i < j (zero where j >= r), one 64 x 64
+// tile on or above the diagonal per workgroup; the mirrored tile is staged
+// through LDS so that reads and writes are row-contiguous.
+__global__ __launch_bounds__(256) void k_pack_dq(Sides sd, int b, const float* __restrict__ dQ32, DqOut out) {
+  __shared__ float t[64][65];
   const int z = blockIdx.y;
   const int s = z >= sd.nb0;
   const int blk = z - s * sd.nb0;
   const int r = min(b, sd.d[s] - blk * b);
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (int64_t)b * b) return;
-  const int i = (int)(e / b), j = (int)(e % b);
-  if (i >= j) return;
-  const float* Qb = dQ32 + (int64_t)z * b * b;
-  const float v = (j < r) ? Qb[(int64_t)i * b + j] - Qb[(int64_t)j * b + i] : 0.f;
-  out.dq[s][(int64_t)blk * ((int64_t)b * (b - 1) / 2) + packed_slot(i, j, b)] = v;
+  const int tiles = (b + 63) / 64;
+  const int i0 = (blockIdx.x / tiles) * 64, j0 = (blockIdx.x % tiles) * 64;
+  if (i0 > j0) return;
+  const float* D = dQ32 + (int64_t)z * b * b;
+  const int c = threadIdx.x & 63, rr = threadIdx.x >> 6;
+  // loads from positions clamped into the live corner, all issued up front
+  float v[16], u[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int j = min(j0 + rr + 4 * k, r - 1), i = min(i0 + c, r - 1);
+    v[k] = D[(int64_t)j * b + i];
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int i = min(i0 + rr + 4 * k, r - 1), j = min(j0 + c, r - 1);
+    u[k] = D[(int64_t)i * b + j];
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) t[rr + 4 * k][c] = v[k];
+  __syncthreads();
+  float* dq = out.dq[s] + (int64_t)blk * ((int64_t)b * (b - 1) / 2);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int ii = rr + 4 * k, i = i0 + ii, j = j0 + c;
+    if (i < j && j < b) dq[packed_slot(i, j, b)] = (j < r) ? u[k] - t[c][ii] : 0.f;
+  }
 }
 
 template <typename T> struct CnpTile;
@@ -291,20 +444,21 @@ hipError_t build_t(const float* q, int d, int b, T* g, void* ws, hipStream_t s) 
   char* w = reinterpret_cast<char*>(ws);
   T* Qb = reinterpret_cast<T*>(w);
   w += al256(E * sizeof(T));
-  float* S32 = reinterpret_cast<float*>(w);
+  float* Q32 = reinterpret_cast<float*>(w);  // Q, then 2Q + 2S
   w += al256(E * 4);
   T* Sb = reinterpret_cast<T*>(w);
   w += al256(E * sizeof(T));
   T* Ntb = reinterpret_cast<T*>(w);
   Sides sd{{q, q}, {d, d}, nb};
-  const int lds = Lay<C, T>::BYTES;
+  const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = allow_lds(k_cnp_square<C, T>, lds);
   if (e == hipSuccess) e = allow_lds(k_cnp_delta<C, T>, lds);
   if (e != hipSuccess) return e;
-  k_unpack_q<T><<<dim3(cdiv((int64_t)b * b, 256), nb), 256, 0, s>>>(sd, b, Qb);
+  const unsigned t64 = cdiv(b, 64);
+  k_unpack_q<T><<<dim3(t64 * t64, nb), 256, 0, s>>>(sd, b, Qb, Q32);
   dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), nb);
-  k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(sd, b, Qb, S32, Sb, Ntb);
-  k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(sd, b, nb, S32, Sb, Ntb, g);
+  k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(sd, b, Qb, Q32, Sb, Ntb);
+  k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(sd, b, nb, Q32, Sb, Ntb, g);
   return hipGetLastError();
 }
 
@@ -315,25 +469,16 @@ template <typename T> Chain<T> carve(void* ws, size_t E) {
     w += al256(E * sizeof(T));
     return p;
   };
-  auto takeF = [&]() {
-    float* p = reinterpret_cast<float*>(w);
-    w += al256(E * 4);
-    return p;
-  };
   Chain<T> ch;
+  ch.F32 = reinterpret_cast<float*>(w);
+  w += al256(E * 4);
   ch.Qb = takeT();
-  ch.U32 = takeF();
   ch.Ub = takeT();
   ch.Utb = takeT();
-  ch.V1_32 = takeF();
   ch.V1b = takeT();
-  ch.P2_32 = takeF();
-  ch.V2_32 = takeF();
   ch.V2b = takeT();
-  ch.V3_32 = takeF();
   ch.Y1tb = takeT();
   ch.Y2tb = takeT();
-  ch.dQ32 = takeF();
   return ch;
 }
 
@@ -351,12 +496,22 @@ hipError_t grads_t(const pxk::CnpSide* sides, int rows, int b, void* ws, hipStre
     gs.lda[k] = sides[k].lda;
     gs.ldb[k] = sides[k].ldb;
   }
-  k_unpack_q<T><<<dim3(cdiv((int64_t)b * b, 256), NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb));
-  const int lds = smem_bytes<C, T, T>();
-  hipError_t e = allow_lds(k_block_grads<C, T>, lds);
-  if (e != hipSuccess) return e;
+  const unsigned t64 = cdiv(b, 64);
+  k_unpack_q<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb), nullptr);
   dim3 grid(cdiv(b, C::BM) * cdiv(b, C::BN), NB);
-  k_block_grads<C, T><<<grid, C::NT, lds, s>>>(sd, gs, rows, b, ch);
+  hipError_t e;
+  if (rows % (2 * C::BK) == 0) {
+    // two groups per tile, each over half of the tokens
+    constexpr int lds = std::max(2 * Lay<C, T>::BYTES, C::BM * (C::BN + 4) * 4);
+    e = allow_lds(k_block_grads<C, T, 2>, lds);
+    if (e != hipSuccess) return e;
+    k_block_grads<C, T, 2><<<grid, 2 * C::NT, lds, s>>>(sd, gs, rows, b, ch);
+  } else {
+    constexpr int lds = Lay<C, T>::BYTES;
+    e = allow_lds(k_block_grads<C, T, 1>, lds);
+    if (e != hipSuccess) return e;
+    k_block_grads<C, T, 1><<<grid, C::NT, lds, s>>>(sd, gs, rows, b, ch);
+  }
   return hipGetLastError();
 }
 
@@ -368,18 +523,19 @@ hipError_t chain_t(const pxk::CnpSide* sides, int b, void* ws, hipStream_t s) {
   Chain<T> ch = carve<T>(ws, (size_t)NB * b * b);
   Sides sd{{sides[0].q, sides[1].q}, {sides[0].d, sides[1].d}, nb0};
   DqOut out{{sides[0].dq, sides[1].dq}};
-  const int lds = smem_bytes<C, T, T>();
+  const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = hipSuccess;
-#define PX_CHAIN(K, MULT)                                                                  \
-  e = allow_lds(k_cnp_chain<C, T, K>, lds);                                                 \
-  if (e != hipSuccess) return e;                                                            \
-  k_cnp_chain<C, T, K><<<dim3(cdiv(b, C::BN), cdiv(b, C::BM), (MULT) * NB), C::NT, lds, s>>>(sd, b, NB, ch);
-  PX_CHAIN(1, 2)
-  PX_CHAIN(2, 1)
-  PX_CHAIN(3, 2)
-  PX_CHAIN(4, 1)
-#undef PX_CHAIN
-  k_pack_dq<<<dim3(cdiv((int64_t)b * b, 256), NB), 256, 0, s>>>(sd, b, ch.dQ32, out);
+  const dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), NB);
+#define PX_STEP(K)                                   \
+  e = allow_lds(k_cnp_step<C, T, K>, lds);            \
+  if (e != hipSuccess) return e;                      \
+  k_cnp_step<C, T, K><<<grid, C::NT, lds, s>>>(sd, b, ch);
+  PX_STEP(1)
+  PX_STEP(2)
+  PX_STEP(3)
+#undef PX_STEP
+  const unsigned t64 = cdiv(b, 64);
+  k_pack_dq<<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, ch.F32, out);
   return hipGetLastError();
 }
 
@@ -394,7 +550,7 @@ size_t cnp_build_ws_bytes(int dt, int d, int b) {
 
 size_t cnp_backward_ws_bytes(int dt, int d0, int d1, int b) {
   const size_t E = (size_t)(nblocks(d0, b) + nblocks(d1, b)) * b * b, es = dt_size(dt);
-  return al256(E * es) * 7 + al256(E * 4) * 6;
+  return al256(E * es) * 7 + al256(E * 4);
 }
 
 hipError_t cnp_build(int dt, const float* q, int d, int b, void* g, void* ws, hipStream_t s) {

@@ -18,12 +18,12 @@ namespace {
 // The identity term is added from the A tile in LDS: the block's output column
 // c equals K index c, so during the K tile that holds columns [k0, k0 + BK)
 // each wave adds A[row][c - k0] to the accumulators of its column groups that
-// fall in that range.
-template <class C, typename T> struct IdentityHook {
+// fall in that range.  `elem` reads element (row, k) of the staged A tile.
+template <class C, class E> struct IdentityHook {
   Acc<C>* acc;
   int n0;
-  PX_DEV void operator()(int kt, const T* A) const {
-    constexpr int LDK = Lay<C, T>::LDK;
+  E elem;
+  template <typename P> PX_DEV void operator()(int kt, const P* A) const {
     const AccPos<C> p = acc_pos<C>();
     const int k0 = kt * C::BK;
 #pragma unroll
@@ -34,30 +34,126 @@ template <class C, typename T> struct IdentityHook {
 #pragma unroll
       for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc->v[i][j][e] += to_f32<T>(A[p.row(i, e) * LDK + kc]);
+        for (int e = 0; e < 16; ++e) acc->v[i][j][e] += elem(A, p.row(i, e), kc);
+    }
+  }
+};
+template <class C, typename T> struct PaddedElem {  // register-path LDS layout
+  PX_DEV float operator()(const T* A, int r, int k) const { return to_f32<T>(A[r * Lay<C, T>::LDK + k]); }
+};
+
+// Identity term of the direct-to-LDS apply, as extra MFMAs.  The loop runs
+// with swapped operands (first operand: rows of D^T, i.e. output columns;
+// second: rows of the input tile), so out^T += I x in^T adds in[row][col] to
+// the accumulator of (col, row) exactly (products with 1 and 0 are exact).
+// The identity fragment is built in registers, and only the two 16-wide
+// k-steps that cover a 32-column group of output columns need it, so a wave
+// adds 2 x TM x TN MFMAs per tile and reads nothing more.
+template <class CD> struct IdentityMfma {
+  int n0;  // first output column of the tile (block-local, equal to its K index)
+  int wm, lane;
+  PX_DEV void operator()(int k, const bf16x8_v* /*a*/, const bf16x8_v* b, Acc<CD>& acc) const {
+#pragma unroll
+    for (int i = 0; i < CD::TM; ++i) {
+      const int c0 = n0 + wm * CD::WTM + i * 32;  // first output column of group i
+      if (k + 16 <= c0 || k >= c0 + 32) continue;
+      // lane holds column c0 + lane % 32 at K indices k + 8 (lane / 32) + e
+      const int c = c0 + (lane & 31), kl = k + 8 * (lane >> 5);
+      typedef short s16x8 __attribute__((ext_vector_type(8)));
+      s16x8 bits;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bits[e] = (short)(kl + e == c ? 0x3F80 : 0);  // bf16 1.0 or 0
+      bf16x8_v id;
+      __builtin_memcpy(&id, &bits, 16);
+#pragma unroll
+      for (int j = 0; j < CD::TN; ++j) acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(id, b[j], acc.v[i][j], 0, 0, 0);
     }
   }
 };
 
-template <class C, typename T, typename IT, typename GT, typename OT>
+// Epilogue of the direct-to-LDS apply, from transposed accumulators (a lane
+// owns 4 consecutive columns of one row): out = acc * scale, staged through
+// LDS as bf16 with one 8-byte write per 4 values, then written with 16-byte
+// row-contiguous stores.  `out` and `cs` point at the tile's first row and
+// column; the whole tile is in range and 16-byte aligned (checked by the
+// caller).  `lds` holds BN x (BM + 8) bf16; the K loop has ended.
+template <class CD>
+PX_DEV void apply_store_t(const Acc<CD>& acc, void* lds, const float* cs, bf16_t* out, int64_t ld_out) {
+  constexpr int PITCH = CD::BM + 8;  // bf16 per staged row (acc column index = tile row)
+  constexpr int CPR = CD::BM / 8;    // 16-byte chunks per row
+  bf16_t* t = reinterpret_cast<bf16_t*>(lds);
+  const AccPos<CD> p = acc_pos<CD>();
+#pragma unroll
+  for (int i = 0; i < CD::TM; ++i)
+#pragma unroll
+    for (int j = 0; j < CD::TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row = p.col(j), col = p.row(i, 4 * g);
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = acc.v[i][j][4 * g + e] * (cs ? cs[col + e] : 1.f);
+        uint2 w;
+        w.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
+        w.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+        *reinterpret_cast<uint2*>(t + row * PITCH + col) = w;
+      }
+  __syncthreads();
+  static_assert(CD::BN * CPR % CD::NT == 0, "chunks must split evenly");
+#pragma unroll
+  for (int q = 0; q < CD::BN * CPR / CD::NT; ++q) {
+    const int ch = threadIdx.x + q * CD::NT, row = ch / CPR, col = (ch % CPR) * 8;
+    *reinterpret_cast<uint4*>(out + (int64_t)row * ld_out + col) = *reinterpret_cast<const uint4*>(t + row * PITCH + col);
+  }
+}
+
+template <class CD, class C, typename T, typename IT, typename GT, typename OT>
 __global__ __launch_bounds__(C::NT) void k_apply(const IT* __restrict__ in, int64_t ld_in, int rows, int d, int b,
                                                   const GT* __restrict__ dT, const float* __restrict__ colscale,
                                                   OT* __restrict__ out, int64_t ld_out) {
   extern __shared__ __align__(16) unsigned char smem[];
   T* lds = reinterpret_cast<T*>(smem);
-  const int blk = blockIdx.z, kb = blk * b, r = min(b, d - kb);
-  const int m0 = blockIdx.x * C::BM, n0 = blockIdx.y * C::BN;
+  // Units run block-major, then row tile, then column tile.  Workgroups are
+  // dealt to the 8 XCDs round robin, so the launch index is remapped to give
+  // each XCD a contiguous range of units: an XCD then fetches only its own
+  // blocks of D^T into its L2, and the column tiles of one row tile, which
+  // share their input rows, run back to back on the same XCD.
+  const int nrt = (rows + C::BM - 1) / C::BM, nct = (b + C::BN - 1) / C::BN;
+  const int units = nrt * nct * ((d + b - 1) / b);
+  int u = blockIdx.x;
+  if (units % 8 == 0) u = (u % 8) * (units / 8) + u / 8;
+  const int blk = u / (nrt * nct), rem = u % (nrt * nct);
+  const int kb = blk * b, r = min(b, d - kb);
+  const int m0 = (rem / nct) * C::BM, n0 = (rem % nct) * C::BN;
   if (n0 >= r) return;
+  const IT* a0 = in + (int64_t)m0 * ld_in + kb;
+  const GT* b0 = dT + ((int64_t)blk * b + n0) * b;
+  const float* cs = colscale ? colscale + kb + n0 : nullptr;
+  auto epi = [&](auto& acc) {
+    store_tile<cfg_of<decltype(acc)>, OT>(acc, smem, out + (int64_t)m0 * ld_out + kb + n0, ld_out, rows - m0, r - n0,
+                                          [&](int c) { return cs ? cs[c] : 1.f; });
+  };
+  if constexpr (!std::is_same<CD, void>::value) {
+    OT* o0 = out + (int64_t)m0 * ld_out + kb + n0;
+    if (dma_rows_ok(a0, ld_in, rows - m0, CD::BM) && dma_rows_ok(b0, b, r - n0, CD::BN) && r % CD::BK == 0 &&
+        reinterpret_cast<uintptr_t>(o0) % 16 == 0 && ld_out % 8 == 0) {
+      Acc<CD> acc;
+      const AccPos<CD> p = acc_pos<CD>();
+      const DmaSrc src{reinterpret_cast<const bf16_t*>(a0), ld_in, reinterpret_cast<const bf16_t*>(b0), b};
+      dma_mainloop<CD, NoHook, true>(reinterpret_cast<char*>(smem), src, r / CD::BK, acc, p.wm, p.wn, p.lane,
+                                     NoHook(), IdentityMfma<CD>{n0, p.wm, p.lane});
+      apply_store_t<CD>(acc, smem, cs, reinterpret_cast<bf16_t*>(o0), ld_out);
+      return;
+    }
+  }
   LoadK<C::BM, C::BK, C::NT, IT, T> la;
-  la.init(in + (int64_t)m0 * ld_in + kb, ld_in, rows - m0, r);
+  la.init(a0, ld_in, rows - m0, r);
   LoadK<C::BN, C::BK, C::NT, GT, T> lb;
-  lb.init(dT + ((int64_t)blk * b + n0) * b, b, r - n0, r);
+  lb.init(b0, b, r - n0, r);
   Acc<C> acc;
   const AccPos<C> p = acc_pos<C>();
-  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane, IdentityHook<C, T>{&acc, n0});
-  const float* cs = colscale ? colscale + kb + n0 : nullptr;
-  store_tile<C, OT>(acc, smem, out + (int64_t)m0 * ld_out + kb + n0, ld_out, rows - m0, r - n0,
-                    [&](int c) { return cs ? cs[c] : 1.f; });
+  mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane, IdentityHook<C, PaddedElem<C, T>>{&acc, n0, {}});
+  epi(acc);
 }
 
 // ============================================================================
@@ -82,7 +178,7 @@ struct TileMap {
   }
 };
 
-template <class C, typename T, typename AT, typename BT, typename OT, bool BKN>
+template <class CD, class C, typename T, typename AT, typename BT, typename OT, bool BKN>
 __global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_t lda, const BT* __restrict__ B,
                                                  int64_t ldb, int M, int N, int K, const float* __restrict__ colscale,
                                                  OT* __restrict__ out, int64_t ldo, TileMap map) {
@@ -91,6 +187,20 @@ __global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_
   int bm, bn;
   map.at(blockIdx.x, bm, bn);
   const int m0 = bm * C::BM, n0 = bn * C::BN;
+  const float* cs = colscale ? colscale + n0 : nullptr;
+  if constexpr (!std::is_same<CD, void>::value) {
+    const AT* a0 = A + (int64_t)m0 * lda;
+    const BT* b0 = B + (int64_t)n0 * ldb;
+    if (dma_rows_ok(a0, lda, M - m0, CD::BM) && dma_rows_ok(b0, ldb, N - n0, CD::BN) && K % CD::BK == 0) {
+      Acc<CD> acc;
+      const AccPos<CD> p = acc_pos<CD>();
+      const DmaSrc src{reinterpret_cast<const bf16_t*>(a0), lda, reinterpret_cast<const bf16_t*>(b0), ldb};
+      dma_mainloop<CD>(reinterpret_cast<char*>(smem), src, K / CD::BK, acc, p.wm, p.wn, p.lane, NoHook());
+      store_tile<CD, OT>(acc, smem, out + (int64_t)m0 * ldo + n0, ldo, M - m0, N - n0,
+                         [&](int c) { return cs ? cs[c] : 1.f; });
+      return;
+    }
+  }
   LoadK<C::BM, C::BK, C::NT, AT, T> la;
   la.init(A + (int64_t)m0 * lda, lda, M - m0, K);
   using LB = typename std::conditional<BKN, LoadMN<C::BN, C::BK, C::NT, BT, T>, LoadK<C::BN, C::BK, C::NT, BT, T>>::type;
@@ -102,7 +212,6 @@ __global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_
   Acc<C> acc;
   const AccPos<C> p = acc_pos<C>();
   mainloop<C, T>(lds, la, lb, K, acc, p.wm, p.wn, p.lane);
-  const float* cs = colscale ? colscale + n0 : nullptr;
   store_tile<C, OT>(acc, smem, out + (int64_t)m0 * ldo + n0, ldo, M - m0, N - n0,
                     [&](int c) { return cs ? cs[c] : 1.f; });
 }
@@ -326,12 +435,15 @@ hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap,
   if (rows <= 0 || d_out <= 0) return hipSuccess;
   const size_t es = dt_size(dt);
   const size_t row_bytes = (size_t)d_in * es;
-  const size_t budget = 64 * 1024;
+  // Small workgroups keep many rows in flight per CU: about 8 KB of rows per
+  // workgroup (one row at d >= 4096 bf16) measured fastest, against 2-3x
+  // slower copies with 64 KB per workgroup.
+  const size_t budget = 64 * 1024, target = 8 * 1024;
   auto go = [&](auto tag) -> hipError_t {
     using E = decltype(tag);
     const size_t pitch_bytes = (row_bytes + 15) / 16 * 16;
     if (pitch_bytes <= budget) {
-      const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, budget / pitch_bytes));
+      const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, target / pitch_bytes));
       k_permute_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch_bytes, s>>>(
           reinterpret_cast<const E*>(in), ld_in, rowmap, colmap, reinterpret_cast<E*>(out), ld_out, rows, d_in, d_out,
           rpw);
@@ -367,16 +479,17 @@ hipError_t perm_from_seed_device(uint64_t seed, int d, int32_t* out, int32_t* sc
   return hipGetLastError();
 }
 
-template <class C, typename T, typename IT, typename GT, typename OT>
+template <class CD, class C, typename T, typename IT, typename GT, typename OT>
 static hipError_t apply_t(const void* in, int64_t ld_in, int rows, int d, int b, const void* dT, const float* cs,
                           void* out, int64_t ld_out, hipStream_t s) {
-  const int lds = smem_bytes<C, T, OT>();
-  auto k = k_apply<C, T, IT, GT, OT>;
+  const int lds = std::max(smem_bytes<C, T, OT>(), dma_smem_bytes<CD>());
+  auto k = k_apply<CD, C, T, IT, GT, OT>;
   hipError_t e = allow_lds(k, lds);
   if (e != hipSuccess) return e;
-  dim3 grid(cdiv(rows, C::BM), cdiv(b, C::BN), nblocks(d, b));
-  k<<<grid, C::NT, lds, s>>>(reinterpret_cast<const IT*>(in), ld_in, rows, d, b, reinterpret_cast<const GT*>(dT), cs,
-                             reinterpret_cast<OT*>(out), ld_out);
+  const int64_t units = (int64_t)cdiv(rows, C::BM) * cdiv(b, C::BN) * nblocks(d, b);
+  if (units > INT32_MAX) return hipErrorInvalidValue;
+  k<<<(unsigned)units, C::NT, lds, s>>>(reinterpret_cast<const IT*>(in), ld_in, rows, d, b,
+                                        reinterpret_cast<const GT*>(dT), cs, reinterpret_cast<OT*>(out), ld_out);
   return hipGetLastError();
 }
 
@@ -384,22 +497,22 @@ hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, in
                  const float* colscale, int out_dt, void* out, int64_t ld_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   if (cdt == BF16 && in_dt == BF16 && dT_dt == BF16 && out_dt == BF16)
-    return apply_t<TGemm, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+    return apply_t<DGemm, TGemm, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
   if (cdt == F32 && in_dt == F32 && dT_dt == F32 && out_dt == F32)
-    return apply_t<TF, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+    return apply_t<void, TF, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
   // merge products: fp32 rows times the stored blocks
   if (cdt == F32 && in_dt == F32 && dT_dt == BF16 && out_dt == F32)
-    return apply_t<TFM, float, float, bf16_t, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+    return apply_t<void, TFM, float, float, bf16_t, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
   if (cdt == F32 && in_dt == F32 && dT_dt == F32 && out_dt == F32)
-    return apply_t<TFM, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+    return apply_t<void, TFM, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
   return hipErrorInvalidValue;
 }
 
-template <class C, typename T, typename AT, typename BT, typename OT, bool BKN>
+template <class CD, class C, typename T, typename AT, typename BT, typename OT, bool BKN>
 static hipError_t gemm_t(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K, const float* cs,
                          void* out, int64_t ldo, hipStream_t s) {
-  const int lds = smem_bytes<C, T, OT>();
-  auto k = k_gemm<C, T, AT, BT, OT, BKN>;
+  const int lds = std::max(smem_bytes<C, T, OT>(), dma_smem_bytes<CD>());
+  auto k = k_gemm<CD, C, T, AT, BT, OT, BKN>;
   hipError_t e = allow_lds(k, lds);
   if (e != hipSuccess) return e;
   const TileMap map{(int)cdiv(M, C::BM), (int)cdiv(N, C::BN)};
@@ -413,9 +526,11 @@ static hipError_t gemm_t(const void* A, int64_t lda, const void* B, int64_t ldb,
 template <typename BT, bool BKN>
 static hipError_t gemm_bf16(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K,
                             const float* cs, void* out, int64_t ldo, hipStream_t s) {
+  // the direct-to-LDS loop serves bf16 operands that are both K-contiguous
+  using CD = typename std::conditional<!BKN && std::is_same<BT, bf16_t>::value, DGemm, void>::type;
   if ((int64_t)cdiv(M, 256) * cdiv(N, 256) >= 256)
-    return gemm_t<TGemm, bf16_t, bf16_t, BT, bf16_t, BKN>(A, lda, B, ldb, M, N, K, cs, out, ldo, s);
-  return gemm_t<TBig, bf16_t, bf16_t, BT, bf16_t, BKN>(A, lda, B, ldb, M, N, K, cs, out, ldo, s);
+    return gemm_t<CD, TGemm, bf16_t, bf16_t, BT, bf16_t, BKN>(A, lda, B, ldb, M, N, K, cs, out, ldo, s);
+  return gemm_t<void, TBig, bf16_t, bf16_t, BT, bf16_t, BKN>(A, lda, B, ldb, M, N, K, cs, out, ldo, s);
 }
 
 hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const void* B, int64_t ldb, bool b_kn, int M,
@@ -430,8 +545,8 @@ hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const v
                   : gemm_bf16<int8_t, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
   }
   if (cdt == F32 && a_dt == F32 && b_dt == F32 && out_dt == F32)
-    return b_kn ? gemm_t<TF, float, float, float, float, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
-                : gemm_t<TF, float, float, float, float, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
+    return b_kn ? gemm_t<void, TF, float, float, float, float, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
+                : gemm_t<void, TF, float, float, float, float, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
   return hipErrorInvalidValue;
 }
 
