@@ -17,6 +17,9 @@ sample of the same workload as a baseline.
 """
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +30,9 @@ import numpy as np
 PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # dense MFMA: 256 CU x 2.4 GHz x 4096 (bf16) / 256 (fp32) flop/clk
 HBM_PEAK_GBS = 8000.0
 METRIC = "POET-X linear fwd+bwd tokens/s at Llama-8B shapes; % MFMA peak (1 GPU)"
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "llama8b_gemm_traffic.md")
+COPY_PROBE_BYTES = 256 << 20  # device-to-device copy of known size, the counters' calibration
 
 
 def side_sums(d, b):
@@ -83,6 +89,99 @@ def cpu_baseline(inp, wl, lin_flops, total_flops):
     }
 
 
+def kernel_source_hash():
+    """sha256 over the HIP sources and headers: counter figures are only valid for the code they measured."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "orthogonal_reparameterized_cnp_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_counter_csv(d):
+    """[(dispatch id, kernel name, KiB)] from a rocprofv3 --pmc output directory."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    out = []
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    return sorted(out)
+
+
+def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
+    """Turn one FETCH_SIZE run and one WRITE_SIZE run of `bench.py --copy-probe` into per-launch HBM
+    bytes of the W~ contractions, each counter scaled by what it reads for the copy probe."""
+    res = {}
+    for key, d in (("fetch", fetch_dir), ("write", write_dir)):
+        rows = read_counter_csv(d)
+        # the probe is the last device copy before the step's first CNP kernel (warm-up 0)
+        first_step = min((i for i, n, _ in rows if "k_unpack_q" in n), default=None)
+        copies = [v for i, n, v in rows if "copyBuffer" in n and first_step is not None and i < first_step]
+        gemm = [v for _, n, v in rows if "k_gemm<" in n]
+        if not copies or not gemm or copies[-1] * 1024 < COPY_PROBE_BYTES / 4:
+            raise SystemExit(f"{d}: copy probe or k_gemm dispatches missing")
+        # the probe reads and writes COPY_PROBE_BYTES once
+        factor = COPY_PROBE_BYTES / (copies[-1] * 1024)
+        res[key] = {"factor": factor, "launches": len(gemm), "bytes_per_launch": sum(gemm) * 1024 * factor / len(gemm)}
+    traffic = res["fetch"]["bytes_per_launch"] + res["write"]["bytes_per_launch"]
+    line = {
+        "kernel_source_hash": kernel_source_hash(),
+        "traffic_bytes_per_launch": traffic,
+        "fetch_bytes_per_launch": res["fetch"]["bytes_per_launch"],
+        "write_bytes_per_launch": res["write"]["bytes_per_launch"],
+        "fetch_scale": res["fetch"]["factor"],
+        "write_scale": res["write"]["factor"],
+        "launches": res["fetch"]["launches"],
+    }
+    txt = f"""# W~ contractions (k_gemm): HBM traffic per launch (rocprofv3 counters)
+
+Workload: one step of bench.py's default (7 POET-X linears of a Llama-8B decoder layer, T = 8192, b = 512,
+bf16), with a {COPY_PROBE_BYTES >> 20} MiB device-to-device copy before the step as calibration.
+
+Commands (from the repository root on one MI355X, one counter per run):
+
+    {cmd_fetch}
+    {cmd_write}
+    python bench.py --summarize-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
+
+Each counter is scaled by the factor that maps its reading for the copy probe to the probe's true
+bytes: FETCH_SIZE x{res['fetch']['factor']:.3f}, WRITE_SIZE x{res['write']['factor']:.3f}.
+
+| | per k_gemm launch (mean of {res['fetch']['launches']}) |
+|---|---|
+| bytes fetched | {res['fetch']['bytes_per_launch'] / 1e9:.4f} GB |
+| bytes written | {res['write']['bytes_per_launch'] / 1e9:.4f} GB |
+| traffic | {traffic / 1e9:.4f} GB |
+
+bench.py reports `roofline.traffic` from the line below while the kernel sources still hash to the same value.
+
+traffic-json: {json.dumps(line)}
+"""
+    with open(TRAFFIC_MD, "w") as fh:
+        fh.write(txt)
+    print(txt)
+
+
+def committed_traffic():
+    """Per-launch HBM bytes of the W~ contractions from the committed counter summary, or None when the
+    summary is missing or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_MD) as fh:
+            for l in fh:
+                if l.startswith("traffic-json: "):
+                    d = json.loads(l[len("traffic-json: "):])
+                    if d.get("kernel_source_hash") == kernel_source_hash():
+                        return d["traffic_bytes_per_launch"]
+    except OSError:
+        pass
+    return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,7 +190,17 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="per kernel class timings on stderr")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help=f"run a {COPY_PROBE_BYTES >> 20} MiB device copy before the steps (counter calibration)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the k_gemm traffic summary from two rocprofv3 --pmc runs and exit (no GPU)")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        base = "rocprofv3 --pmc {c} --output-format csv -d {d} -o llama8b -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-probe"
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
+                          base.format(c="FETCH_SIZE", d=args.summarize_traffic[0]),
+                          base.format(c="WRITE_SIZE", d=args.summarize_traffic[1]))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
@@ -144,6 +253,14 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.copy_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        print(f"[bench] copy probe: {COPY_PROBE_BYTES} bytes device to device", file=sys.stderr, flush=True)
 
     gemm_f, apply_f, cnp_f = step_flops(wl, T)
     total_f = gemm_f + apply_f + cnp_f
@@ -193,7 +310,8 @@ def main():
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": committed_traffic(),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "launches": n_launch,
             "avg_launch_ms": k_ms / max(n_launch, 1),
             "algorithmic_gb_per_launch": k_bytes / max(n_launch, 1) / 1e9,
