@@ -2,9 +2,10 @@
 """Throughput of the POET-X linear layer (fwd + bwd) on one MI355X.
 
 One step is the whole hot path over one batch: the CNP blocks of both sides of
-every linear of a Llama-8B decoder layer (poetx_cnp_build), the forward of the
-seven linears (q, k, v, o, gate, up, down), then their backward with the CNP
-chain rule down to packed dq.  T = 8192 tokens, b = 512, bf16 activations and
+every linear of a Llama-8B decoder layer (one poetx_cnp_build_batch), the
+forward of the seven linears (q, k, v, o, gate, up, down), then their backward
+(poetx_linear_bwd_dx) and the CNP chain rule of all sides down to packed dq
+(one poetx_cnp_backward_batch).  T = 8192 tokens, b = 512, bf16 activations and
 weights with fp32 accumulation.  Inputs are seeded synthetic tensors already
 resident in HBM when timing starts.
 
@@ -208,7 +209,7 @@ def main():
     import torch
 
     from orthogonal_reparameterized_cnp_amd import binding as B
-    from orthogonal_reparameterized_cnp_amd.layer import PoetxLinear
+    from orthogonal_reparameterized_cnp_amd.layer import PoetxGroup, PoetxLinear
     from workloads import WORKLOADS, make_linear_inputs
 
     B.lib()
@@ -241,14 +242,18 @@ def main():
     torch.cuda.synchronize()
     print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
+    # The layer's seven linears share their CNP work: every side's G is built in
+    # one batch, and the chain rule to dq runs once for all sides after the
+    # backward of the last linear (results bit-identical to per-linear calls).
+    group = PoetxGroup(layers)
+
     def step():
-        for lay in layers:
-            lay.build()
+        group.build()
         for lay, X, Y in zip(layers, Xs, Ys):
             lay.forward(X, Y)
-        for lay, X, dZ, dX, (dqR, dqP) in zip(reversed(layers), reversed(Xs), reversed(dZs), reversed(dXs),
-                                              reversed(dqs)):
-            lay.backward(X, dZ, dX, dqR, dqP)
+        for i in reversed(range(len(layers))):
+            group.backward_dx(i, Xs[i], dZs[i], dXs[i])
+        group.backward_q(dqs)
 
     for _ in range(args.warmup):
         step()

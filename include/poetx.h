@@ -223,6 +223,64 @@ poetx_status poetx_merge_reinit(const poetx_layer_desc* desc, void* Wt, int32_t*
                                 const void* g_R, const void* g_P, float* q_R, float* q_P, uint64_t seed_R,
                                 uint64_t seed_P, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- batched CNP (one layer) -- */
+
+/* Most sides one batched CNP call accepts. */
+#define POETX_MAX_SIDES 64
+
+/* Workspace bytes of poetx_cnp_build_batch for `count` sides of lengths d[i]
+ * (host array) and block size b; 0 for invalid arguments. */
+size_t poetx_cnp_batch_workspace_size(int32_t count, const int32_t* d, int32_t b, int32_t dtype);
+
+/*
+ * poetx_cnp_build for `count` sides at once (e.g. both sides of every linear of
+ * a decoder layer, rebuilt after each optimiser step): the blocks of all sides
+ * share each launch.  The result is bit-identical to `count` separate
+ * poetx_cnp_build calls.  q, d and g are HOST arrays of length count holding
+ * the per-side arguments of poetx_cnp_build (device pointers, side lengths).
+ *   count  1 .. POETX_MAX_SIDES
+ *   ws     >= poetx_cnp_batch_workspace_size(count, d, b, dtype)
+ * Errors: POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_HIP.
+ */
+poetx_status poetx_cnp_build_batch(int32_t count, const float* const* q, const int32_t* d, int32_t b, int32_t dtype,
+                                   void* const* g, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of a gradient state holding `blocks` CNP blocks of size b: the summed
+ * block gradients and the chain rule's intermediates.  Opaque layout. */
+size_t poetx_cnp_grad_bytes(int64_t blocks, int32_t b, int32_t dtype);
+
+/*
+ * poetx_linear_bwd split in two, so that the CNP chain rule of many linears can
+ * run as one batch.  This call computes dX exactly as poetx_linear_bwd does and
+ * the block gradients dG_R, dG_P (same definition and summation order), which
+ * it stores in the gradient state `dg` at blocks [dg_first, dg_first + nb_R +
+ * nb_P) (R side first) of a state sized for dg_blocks blocks.
+ *   dg        gradient state of poetx_cnp_grad_bytes(dg_blocks, b, act_dtype) bytes
+ *   ws        >= poetx_workspace_size(desc, T, POETX_OP_BWD)
+ * Other arguments as for poetx_linear_bwd.  Errors as for poetx_linear_bwd, and
+ * POETX_E_SHAPE when the linear's blocks do not fit in [0, dg_blocks).
+ */
+poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+                                 const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
+                                 const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX,
+                                 void* dg, int64_t dg_first, int64_t dg_blocks, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/*
+ * The CNP chain rule and skew projection (as in poetx_linear_bwd) for `count`
+ * sides whose block gradients fill the gradient state `dg` in order: side i
+ * owns the next ceil(d[i] / b) blocks.  q, d and dq are HOST arrays of length
+ * count (device pointers, side lengths); dq[i] [nb_i][b(b-1)/2] fp32 is
+ * overwritten, dead slots of a partial block with 0.  The result is
+ * bit-identical to the chain rule inside poetx_linear_bwd.
+ *   count  1 .. POETX_MAX_SIDES, with the sum of the sides' blocks equal to the
+ *          state's block count
+ *   dg     gradient state written by poetx_linear_bwd_dx; dg_bytes its size
+ * Errors: POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_HIP.
+ */
+poetx_status poetx_cnp_backward_batch(int32_t count, const float* const* q, const int32_t* d, int32_t b, int32_t dtype,
+                                      void* dg, size_t dg_bytes, float* const* dq, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

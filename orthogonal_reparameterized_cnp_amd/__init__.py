@@ -2,7 +2,8 @@
 
 The compute lives in libpoetx.so (hand-written HIP kernels behind a C ABI,
 include/poetx.h); `binding` is its ctypes binding with the same function names
-and `layer.PoetxLinear` owns the device buffers of one linear.
+`layer.PoetxLinear` owns the device buffers of one linear, and `layer.PoetxGroup`
+runs the CNP work of several linears (e.g. one decoder layer) as one batch.
 """
 
 from .binding import (  # noqa: F401
@@ -17,10 +18,15 @@ from .binding import (  # noqa: F401
     PoetxError,
     desc,
     lib,
+    poetx_cnp_backward_batch,
+    poetx_cnp_batch_workspace_size,
     poetx_cnp_build,
+    poetx_cnp_build_batch,
+    poetx_cnp_grad_bytes,
     poetx_g_bytes,
     poetx_last_error,
     poetx_linear_bwd,
+    poetx_linear_bwd_dx,
     poetx_linear_fwd,
     poetx_merge_reinit,
     poetx_packed_len,

@@ -77,6 +77,24 @@ _SIG = {
         ctypes.c_int,
         [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, _P, _P, ctypes.c_uint64, ctypes.c_uint64, _P, ctypes.c_size_t, _P],
     ),
+    "poetx_cnp_batch_workspace_size": (
+        ctypes.c_size_t, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32]
+    ),
+    "poetx_cnp_build_batch": (
+        ctypes.c_int,
+        [ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32,
+         ctypes.POINTER(_P), _P, ctypes.c_size_t, _P],
+    ),
+    "poetx_cnp_grad_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
+    "poetx_linear_bwd_dx": (
+        ctypes.c_int,
+        [ctypes.POINTER(LayerDesc), ctypes.c_int64] + [_P] * 12 + [ctypes.c_int64, ctypes.c_int64, _P, ctypes.c_size_t, _P],
+    ),
+    "poetx_cnp_backward_batch": (
+        ctypes.c_int,
+        [ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, _P,
+         ctypes.c_size_t, ctypes.POINTER(_P), _P],
+    ),
 }
 
 
@@ -220,3 +238,42 @@ def poetx_merge_reinit(dsc: LayerDesc, Wt, perm_R, perm_P, g_R, g_P, q_R, q_P, s
             seed_R & ((1 << 64) - 1), seed_P & ((1 << 64) - 1), _ptr(ws), ws_bytes, _stream(stream),
         )
     )
+
+
+# ------------------------------------------------- batched CNP (one layer) ---
+def _ptr_array(ts):
+    return (_P * len(ts))(*[_ptr(t) for t in ts])
+
+
+def _i32_array(xs):
+    return (ctypes.c_int32 * len(xs))(*xs)
+
+
+def poetx_cnp_batch_workspace_size(d, b: int, dtype: int) -> int:
+    return lib().poetx_cnp_batch_workspace_size(len(d), _i32_array(d), b, dtype)
+
+
+def poetx_cnp_build_batch(q, d, b: int, dtype: int, g, ws, ws_bytes: int, stream=None):
+    """q, d, g: per-side lists (device tensors / ints), marshalled into host arrays."""
+    _check(lib().poetx_cnp_build_batch(len(d), _ptr_array(q), _i32_array(d), b, dtype, _ptr_array(g), _ptr(ws),
+                                       ws_bytes, _stream(stream)))
+
+
+def poetx_cnp_grad_bytes(blocks: int, b: int, dtype: int) -> int:
+    return lib().poetx_cnp_grad_bytes(blocks, b, dtype)
+
+
+def poetx_linear_bwd_dx(dsc: LayerDesc, T: int, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, dg,
+                        dg_first: int, dg_blocks: int, ws, ws_bytes: int, stream=None):
+    _check(
+        lib().poetx_linear_bwd_dx(
+            ctypes.byref(dsc), T, _ptr(X), _ptr(dZ), _ptr(perm_R), _ptr(perm_P), _ptr(Wt), _ptr(g_R), _ptr(g_P),
+            _ptr(q_R), _ptr(q_P), _ptr(H_save), _ptr(dX), _ptr(dg), dg_first, dg_blocks, _ptr(ws), ws_bytes,
+            _stream(stream),
+        )
+    )
+
+
+def poetx_cnp_backward_batch(q, d, b: int, dtype: int, dg, dg_bytes: int, dq, stream=None):
+    _check(lib().poetx_cnp_backward_batch(len(d), _ptr_array(q), _i32_array(d), b, dtype, _ptr(dg), dg_bytes,
+                                          _ptr_array(dq), _stream(stream)))

@@ -141,6 +141,7 @@ template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
 
 struct BwdWs {
   void *dZt, *dH, *dA, *Xt, *dXt, *cnp;
+  float* part;
   int32_t* invR;
 };
 template <class P> BwdWs plan_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
@@ -151,7 +152,9 @@ template <class P> BwdWs plan_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
   w.dA = p.template take<char>(T * lead(d->m) * es);
   w.Xt = p.template take<char>(T * lead(d->m) * es);
   w.dXt = p.template take<char>(T * lead(d->m) * es);
-  w.cnp = p.template take<char>(cnp_backward_ws_bytes(d->act_dtype, d->m, d->n, d->b));
+  w.cnp = p.template take<char>(cnp_grad_bytes(d->act_dtype, (int64_t)nblocks(d->m, d->b) + nblocks(d->n, d->b), d->b));
+  w.part = p.template take<float>(
+      block_grads_part_bytes(d->act_dtype, (int)T, nblocks(d->m, d->b) + nblocks(d->n, d->b), d->b));
   w.invR = p.template take<int32_t>((size_t)d->m * 4);
   return w;
 }
@@ -186,6 +189,25 @@ poetx_status check_ws(void* ws, size_t ws_bytes, size_t need) {
   return POETX_OK;
 }
 
+constexpr int64_t kMaxBlocks = 65535;  // CNP blocks per launch (one grid dimension)
+static_assert(POETX_MAX_SIDES == kMaxSides, "side table size");
+
+// count sides of lengths d[i] with block size b: validity and total block count
+poetx_status check_sides(int32_t count, const int32_t* d, int32_t b, int32_t dtype, int64_t* blocks) {
+  if (count < 1 || count > POETX_MAX_SIDES) return fail(POETX_E_SHAPE, "count must be in [1, POETX_MAX_SIDES]");
+  if (!d) return fail(POETX_E_NULL, "d is NULL");
+  if (b < 2 || b > 1024) return fail(POETX_E_SHAPE, "b must be in [2, 1024]");
+  if (dtype != POETX_F32 && dtype != POETX_BF16) return fail(POETX_E_DTYPE, "dtype must be F32 or BF16");
+  int64_t nb = 0;
+  for (int i = 0; i < count; ++i) {
+    if (d[i] < 1 || d[i] > kMaxDim) return fail(POETX_E_SHAPE, "d[i] must be in [1, 2^20]");
+    nb += nblocks(d[i], b);
+  }
+  if (nb > kMaxBlocks) return fail(POETX_E_SHAPE, "more than 65535 blocks in one batch");
+  *blocks = nb;
+  return POETX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,7 +239,7 @@ size_t poetx_workspace_size(const poetx_layer_desc* desc, int64_t T, int32_t op)
   if (!desc || T < 0 || T > kMaxT) return 0;
   if (op == POETX_OP_CNP) {
     if (desc->m < 1 || desc->b < 2 || (desc->act_dtype != POETX_F32 && desc->act_dtype != POETX_BF16)) return 0;
-    return cnp_build_ws_bytes(desc->act_dtype, desc->m, desc->b);
+    return cnp_build_ws_bytes(desc->act_dtype, nblocks(desc->m, desc->b), desc->b);
   }
   if (check_desc(desc) != POETX_OK) return 0;
   Plan p;
@@ -282,15 +304,37 @@ poetx_status poetx_timer_read(int64_t* launches, double* total_ms, double* flops
 poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype, void* g, void* ws, size_t ws_bytes,
                              void* stream) {
   if (!q || !g) return fail(POETX_E_NULL, "q and g must be non-NULL");
-  if (d < 1 || d > kMaxDim || b < 2 || b > 1024 || nblocks(d, b) > 65535) return fail(POETX_E_SHAPE, "bad d or b");
-  if (dtype != POETX_F32 && dtype != POETX_BF16) return fail(POETX_E_DTYPE, "g dtype must be F32 or BF16");
-  const size_t need = cnp_build_ws_bytes(dtype, d, b);
-  poetx_status st = check_ws(ws, ws_bytes, need);
+  return poetx_cnp_build_batch(1, &q, &d, b, dtype, &g, ws, ws_bytes, stream);
+}
+
+size_t poetx_cnp_batch_workspace_size(int32_t count, const int32_t* d, int32_t b, int32_t dtype) {
+  int64_t blocks = 0;
+  if (check_sides(count, d, b, dtype, &blocks) != POETX_OK) return 0;
+  return cnp_build_ws_bytes(dtype, blocks, b);
+}
+
+poetx_status poetx_cnp_build_batch(int32_t count, const float* const* q, const int32_t* d, int32_t b, int32_t dtype,
+                                   void* const* g, void* ws, size_t ws_bytes, void* stream) {
+  if (!q || !g) return fail(POETX_E_NULL, "q and g must be non-NULL");
+  int64_t blocks = 0;
+  poetx_status st = check_sides(count, d, b, dtype, &blocks);
+  if (st != POETX_OK) return st;
+  double flops = 0, bytes = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!q[i] || !g[i]) return fail(POETX_E_NULL, "q[i] and g[i] must be non-NULL");
+    flops += 4 * sum_r3(d[i], b);
+    bytes += 2.0 * g_slice(d[i], b, dtype) + 2.0 * nblocks(d[i], b) * b * b * 4;
+  }
+  st = check_ws(ws, ws_bytes, cnp_build_ws_bytes(dtype, blocks, b));
   if (st != POETX_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  PX_TIMED(POETX_KC_CNP, 4 * sum_r3(d, b), 2 * g_slice(d, b, dtype) + 2.0 * nblocks(d, b) * b * b * 4,
-           cnp_build(dtype, q, d, b, g, ws, s));
+  PX_TIMED(POETX_KC_CNP, flops, bytes, cnp_build_batch(dtype, count, q, d, b, g, ws, s));
   return POETX_OK;
+}
+
+size_t poetx_cnp_grad_bytes(int64_t blocks, int32_t b, int32_t dtype) {
+  if (blocks < 1 || blocks > kMaxBlocks || b < 2 || b > 1024 || (dtype != POETX_F32 && dtype != POETX_BF16)) return 0;
+  return cnp_grad_bytes(dtype, blocks, b);
 }
 
 poetx_status poetx_premerge(const poetx_layer_desc* desc, const void* W0, int64_t ld_w0, const float* w0_scale,
@@ -353,24 +397,16 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
   return POETX_OK;
 }
 
-poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
-                              const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
-                              const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX,
-                              float* dq_R, float* dq_P, void* ws, size_t ws_bytes, void* stream) {
-  poetx_status st = check_desc(desc);
-  if (st != POETX_OK) return st;
-  if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
-  if (!perm_R || !perm_P || !Wt || !g_R || !g_P || !q_R || !q_P || !dq_R || !dq_P)
-    return fail(POETX_E_NULL, "a required pointer is NULL");
-  if (T > 0 && (!X || !dZ || !H_save || !dX)) return fail(POETX_E_NULL, "a required pointer is NULL");
-  Plan p;
-  plan_bwd(p, desc, T);
-  st = check_ws(ws, ws_bytes, p.off);
-  if (st != POETX_OK) return st;
-  Plan pq;
-  pq.base = reinterpret_cast<char*>(ws);
-  const BwdWs w = plan_bwd(pq, desc, T);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+}  // extern "C"
+
+namespace {
+
+// dX and the block gradients of both sides into blocks [first, first + nb_R + nb_P)
+// of the gradient state dg (total blocks); shared by both backward entry points.
+poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+                         const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
+                         const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX, void* dg,
+                         int64_t first, int64_t total, const BwdWs& w, hipStream_t s) {
   const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, wt = desc->w_dtype;
   const int rows = (int)T;
   const int64_t ldm = lead(m), ldn = lead(n);
@@ -389,10 +425,10 @@ poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const voi
   // Xt = X[:, perm_R]
   PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
   // block gradients of both sides over all tokens: dG_R = Xt^T dA, dG_P = H^T dZt
-  const CnpSide sides[2] = {{q_R, m, w.Xt, ldm, w.dA, ldm, dq_R}, {q_P, n, H_save, ldn, w.dZt, ldn, dq_P}};
+  const CnpSide sides[2] = {{q_R, m, w.Xt, ldm, w.dA, ldm}, {q_P, n, H_save, ldn, w.dZt, ldn}};
   PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * (sum_r2(m, b) + sum_r2(n, b)),
            2.0 * rows * (m + n) * es + (4 + 2 * es) * (sum_r2(m, b) + sum_r2(n, b)),
-           block_grads(at, sides, rows, b, w.cnp, s));
+           block_grads(at, sides, rows, b, dg, first, total, w.part, s));
   // dXt = dA Diag(G_R)^T;  dX[:, perm_R] = dXt
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
            apply(at, at, w.dA, ldm, rows, m, b, at, g_R, nullptr, at, w.dXt, ldm, s));
@@ -400,9 +436,85 @@ poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const voi
     PX_HIP(inverse_perm(perm_R, m, w.invR, s));
     PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, w.dXt, ldm, nullptr, w.invR, dX, m, rows, m, m, s));
   }
+  return POETX_OK;
+}
+
+poetx_status check_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ, const int32_t* perm_R,
+                       const int32_t* perm_P, const void* Wt, const void* g_R, const void* g_P, const float* q_R,
+                       const float* q_P, const void* H_save, void* dX, void* ws, size_t ws_bytes) {
+  poetx_status st = check_desc(desc);
+  if (st != POETX_OK) return st;
+  if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
+  if (!perm_R || !perm_P || !Wt || !g_R || !g_P || !q_R || !q_P) return fail(POETX_E_NULL, "a required pointer is NULL");
+  if (T > 0 && (!X || !dZ || !H_save || !dX)) return fail(POETX_E_NULL, "a required pointer is NULL");
+  Plan p;
+  plan_bwd(p, desc, T);
+  return check_ws(ws, ws_bytes, p.off);
+}
+
+}  // namespace
+
+extern "C" {
+
+poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+                              const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
+                              const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX,
+                              float* dq_R, float* dq_P, void* ws, size_t ws_bytes, void* stream) {
+  poetx_status st = check_bwd(desc, T, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, ws, ws_bytes);
+  if (st != POETX_OK) return st;
+  if (!dq_R || !dq_P) return fail(POETX_E_NULL, "a required pointer is NULL");
+  Plan pq;
+  pq.base = reinterpret_cast<char*>(ws);
+  const BwdWs w = plan_bwd(pq, desc, T);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype;
+  const int64_t blocks = (int64_t)nblocks(m, b) + nblocks(n, b);
+  st = bwd_dx_core(desc, T, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, w.cnp, 0, blocks, w, s);
+  if (st != POETX_OK) return st;
   // CNP chain rule and skew projection of both sides
-  PX_TIMED(POETX_KC_CNP, 12 * (sum_r3(m, b) + sum_r3(n, b)), cnp_backward_ws_bytes(at, m, n, b),
-           cnp_chain(at, sides, b, w.cnp, s));
+  const float* qs[2] = {q_R, q_P};
+  const int ds[2] = {m, n};
+  float* dqs[2] = {dq_R, dq_P};
+  PX_TIMED(POETX_KC_CNP, 12 * (sum_r3(m, b) + sum_r3(n, b)), cnp_grad_bytes(at, blocks, b),
+           cnp_chain_batch(at, 2, qs, ds, b, w.cnp, dqs, s));
+  return POETX_OK;
+}
+
+poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+                                 const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
+                                 const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX,
+                                 void* dg, int64_t dg_first, int64_t dg_blocks, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  poetx_status st = check_bwd(desc, T, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, ws, ws_bytes);
+  if (st != POETX_OK) return st;
+  if (!dg) return fail(POETX_E_NULL, "dg is NULL");
+  if (reinterpret_cast<uintptr_t>(dg) % 256) return fail(POETX_E_WORKSPACE, "dg must be 256-byte aligned");
+  const int64_t blocks = (int64_t)nblocks(desc->m, desc->b) + nblocks(desc->n, desc->b);
+  if (dg_blocks < 1 || dg_blocks > kMaxBlocks || dg_first < 0 || dg_first + blocks > dg_blocks)
+    return fail(POETX_E_SHAPE, "the linear's blocks must fit in [0, dg_blocks) of the gradient state");
+  Plan pq;
+  pq.base = reinterpret_cast<char*>(ws);
+  const BwdWs w = plan_bwd(pq, desc, T);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return bwd_dx_core(desc, T, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, dg, dg_first, dg_blocks, w, s);
+}
+
+poetx_status poetx_cnp_backward_batch(int32_t count, const float* const* q, const int32_t* d, int32_t b, int32_t dtype,
+                                      void* dg, size_t dg_bytes, float* const* dq, void* stream) {
+  if (!q || !dq || !dg) return fail(POETX_E_NULL, "q, dq and dg must be non-NULL");
+  int64_t blocks = 0;
+  poetx_status st = check_sides(count, d, b, dtype, &blocks);
+  if (st != POETX_OK) return st;
+  double flops = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!q[i] || !dq[i]) return fail(POETX_E_NULL, "q[i] and dq[i] must be non-NULL");
+    flops += 12 * sum_r3(d[i], b);
+  }
+  if (dg_bytes < cnp_grad_bytes(dtype, blocks, b))
+    return fail(POETX_E_WORKSPACE, "dg smaller than poetx_cnp_grad_bytes of the sides' block count");
+  if (reinterpret_cast<uintptr_t>(dg) % 256) return fail(POETX_E_WORKSPACE, "dg must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PX_TIMED(POETX_KC_CNP, flops, cnp_grad_bytes(dtype, blocks, b), cnp_chain_batch(dtype, count, q, d, b, dg, dq, s));
   return POETX_OK;
 }
 

@@ -23,19 +23,31 @@ using namespace px;
 
 namespace {
 
-// Up to two sides of one linear share a launch: block z < nb0 belongs to side 0.
-struct Sides {
-  const float* q[2];
-  int d[2];
-  int nb0;
-  PX_DEV void at(int z, int b, const float*& qk, int& r) const {
-    const int s = z >= nb0;
-    const int blk = z - s * nb0;
+// The sides of one launch (the two sides of a linear, or every side of a
+// batch): their blocks are numbered consecutively, side s owning global blocks
+// [first[s], first[s + 1]).  Passed by value as a kernel argument.
+struct SideTable {
+  const float* q[pxk::kMaxSides];
+  int d[pxk::kMaxSides];
+  int first[pxk::kMaxSides + 1];
+  int count;
+  PX_DEV int side_of(int z) const {
+    int s = 0;
+    while (s + 1 < count && z >= first[s + 1]) ++s;
+    return s;
+  }
+  // side s, block blk of that side, its live size r and its packed parameters
+  PX_DEV void at(int z, int b, int& s, int& blk, int& r, const float*& qk) const {
+    s = side_of(z);
+    blk = z - first[s];
     r = min(b, d[s] - blk * b);
     qk = q[s] + (int64_t)blk * ((int64_t)b * (b - 1) / 2);
   }
+  PX_DEV void at(int z, int b, const float*& qk, int& r) const {
+    int s, blk;
+    at(z, b, s, blk, r, qk);
+  }
 };
-
 
 // K loop over two K-contiguous bf16/fp32 operand tiles (row pitch b): the
 // direct-to-LDS loop for interior bf16 tiles, else the checked register loop.
@@ -105,7 +117,7 @@ PX_DEV void run_kk2(unsigned char* smem, const T* x0, const T* y0, const T* x1, 
 // the mirrored tile, staged through LDS so that both reads and writes are
 // row-contiguous.  Writes the operand copy Qb and, if Q32 is set, an fp32 copy.
 template <typename T>
-__global__ __launch_bounds__(256) void k_unpack_q(Sides sd, int b, T* __restrict__ Qb, float* __restrict__ Q32) {
+__global__ __launch_bounds__(256) void k_unpack_q(SideTable sd, int b, T* __restrict__ Qb, float* __restrict__ Q32) {
   __shared__ float t[64][65];
   const int z = blockIdx.y;
   const float* qk;
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(256) void k_unpack_q(Sides sd, int b, T* __restrict
 // S = Q Q = -(Q Q^T).  Writes S and N^T = S - 2Q in the operand dtype, and
 // replaces Q32 in place by the fp32 partial sum 2Q + 2S.
 template <class C, typename T>
-__global__ __launch_bounds__(C::NT) void k_cnp_square(Sides sd, int b, const T* __restrict__ Qb,
+__global__ __launch_bounds__(C::NT) void k_cnp_square(SideTable sd, int b, const T* __restrict__ Qb,
                                                       float* __restrict__ Q32, T* __restrict__ Sb,
                                                       T* __restrict__ Ntb) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -190,19 +202,23 @@ __global__ __launch_bounds__(C::NT) void k_cnp_square(Sides sd, int b, const T* 
 
 // G - I = (2Q + 2S) + S N, written as slice 0 (row-major) and slice 1
 // (transposed); zero outside the live r x r corner.
+struct GOut {
+  void* g[pxk::kMaxSides];  // side s: [2][nb_s][b][b], slice 0 = G - I, slice 1 = its transpose
+};
+
 template <class C, typename T>
-__global__ __launch_bounds__(C::NT) void k_cnp_delta(Sides sd, int b, int nb_all, const float* __restrict__ T2,
-                                                     const T* __restrict__ Sb, const T* __restrict__ Ntb,
-                                                     T* __restrict__ g) {
+__global__ __launch_bounds__(C::NT) void k_cnp_delta(SideTable sd, int b, const float* __restrict__ T2,
+                                                     const T* __restrict__ Sb, const T* __restrict__ Ntb, GOut go) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int z = blockIdx.z;
   const float* qk;
-  int r;
-  sd.at(z, b, qk, r);
+  int side, blk, r;
+  sd.at(z, b, side, blk, r, qk);
   const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
   const int64_t off = (int64_t)z * b * b;
-  T* g0 = g + off;
-  T* g1 = g + (int64_t)nb_all * b * b + off;
+  const int64_t nb_s = sd.first[side + 1] - sd.first[side];
+  T* g0 = reinterpret_cast<T*>(go.g[side]) + (int64_t)blk * b * b;
+  T* g1 = reinterpret_cast<T*>(go.g[side]) + (nb_s + blk) * b * b;
   run_kk<C, T>(smem, Sb + off + (int64_t)m0 * b, r - m0, Ntb + off + (int64_t)n0 * b, r - n0, b, r, [&](auto& acc) {
     using CC = cfg_of<decltype(acc)>;
     float t2[CC::TM][CC::TN][16];
@@ -260,14 +276,16 @@ template <typename T> struct Chain {
 // on timing.  The launcher uses G > 1 only when rows is a multiple of G * BK,
 // so that every group runs the same number of K steps (and barriers).
 template <class C, typename T, int G>
-__global__ __launch_bounds__(C::NT * G) void k_block_grads(Sides sd, GradSides<T> gs, int rows, int b, Chain<T> ch) {
+__global__ __launch_bounds__(C::NT * G) void k_block_grads(SideTable sd, GradSides<T> gs, int rows, int b, Chain<T> ch,
+                                                           int64_t zoff) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int grp = G == 1 ? 0 : (int)(threadIdx.x / C::NT);
   T* lds = reinterpret_cast<T*>(smem + grp * Lay<C, T>::BYTES);
-  const int z = blockIdx.y;
-  const int s = z >= sd.nb0;
-  const int blk = z - s * sd.nb0;
-  const int kb = blk * b, r = min(b, sd.d[s] - kb);
+  const int zl = blockIdx.y;  // block of this linear; zoff + zl is its place in the gradient arrays
+  int s, blk, r;
+  const float* qk;
+  sd.at(zl, b, s, blk, r, qk);
+  const int kb = blk * b;
   const int tiles_n = (b + C::BN - 1) / C::BN;
   const int m0 = (blockIdx.x / tiles_n) * C::BM, n0 = (blockIdx.x % tiles_n) * C::BN;
   if (m0 >= r || n0 >= r) return;  // only the live corner is read later
@@ -304,7 +322,7 @@ __global__ __launch_bounds__(C::NT * G) void k_block_grads(Sides sd, GradSides<T
     }
     if (grp != 0) return;
   }
-  const int64_t off = (int64_t)z * b * b;
+  const int64_t off = (zoff + zl) * b * b;
   each_acc4<C>(acc, [&](int i0, int j, const float* v) {
     i0 += m0;
     j += n0;
@@ -324,6 +342,87 @@ __global__ __launch_bounds__(C::NT * G) void k_block_grads(Sides sd, GradSides<T
   });
 }
 
+// Block gradients of large blocks (b a multiple of 256), split over tokens:
+// workgroup (tile, block, s) sums rows [s * rows / S, (s + 1) * rows / S) of
+// its 256 x 256 tile and writes the fp32 partial to part[s][block].  Big tiles
+// give each K step enough MFMA work to cover its loads, and the token split
+// gives the grid enough workgroups; k_block_grads_reduce then adds the S
+// partials in split order.
+template <class C, typename T>
+__global__ __launch_bounds__(C::NT) void k_block_grads_part(SideTable sd, GradSides<T> gs, int rows, int b, int S,
+                                                            float* __restrict__ part) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int zl = blockIdx.y, sp = blockIdx.z;
+  int s, blk, r;
+  const float* qk;
+  sd.at(zl, b, s, blk, r, qk);
+  const int kb = blk * b;
+  const int tiles_n = (b + C::BN - 1) / C::BN;
+  const int m0 = (blockIdx.x / tiles_n) * C::BM, n0 = (blockIdx.x % tiles_n) * C::BN;
+  if (m0 >= r || n0 >= r) return;  // only the live corner is read later
+  const int per = rows / S;
+  const int64_t t0 = (int64_t)sp * per;
+  LoadMN<C::BM, C::BK, C::NT, T, T> la;
+  la.init(gs.A[s] + t0 * gs.lda[s] + kb + m0, gs.lda[s], r - m0, per);
+  LoadMN<C::BN, C::BK, C::NT, T, T> lb;
+  lb.init(gs.B[s] + t0 * gs.ldb[s] + kb + n0, gs.ldb[s], r - n0, per);
+  Acc<C> acc;
+  const AccPos<C> p = acc_pos<C>();
+  mainloop<C, T>(reinterpret_cast<T*>(smem), la, lb, per, acc, p.wm, p.wn, p.lane);
+  float* P = part + ((int64_t)sp * gridDim.y + zl) * b * b;
+  each_acc<C>(acc, [&](int i, int j, float v) {
+    i += m0;
+    j += n0;
+    if (i < r && j < r) P[(int64_t)i * b + j] = v;
+  });
+}
+
+// U = part[0] + part[1] + ... + part[S-1] (in that order) over the live corner
+// of every block, written as the chain rule reads it: fp32, operand dtype and
+// operand-dtype transpose (through an LDS tile so every access is
+// row-contiguous).  One 64 x 64 tile per workgroup.
+template <typename T>
+__global__ __launch_bounds__(256) void k_block_grads_reduce(SideTable sd, int b, int S, const float* __restrict__ part,
+                                                            Chain<T> ch, int64_t zoff) {
+  __shared__ float t[64][65];
+  const int zl = blockIdx.y;
+  int s, blk, r;
+  const float* qk;
+  sd.at(zl, b, s, blk, r, qk);
+  const int tiles = (b + 63) / 64;
+  const int i0 = (blockIdx.x / tiles) * 64, j0 = (blockIdx.x % tiles) * 64;
+  if (i0 >= r || j0 >= r) return;
+  const int c = threadIdx.x & 63, rr = threadIdx.x >> 6;
+  float u[16];
+  for (int sp = 0; sp < S; ++sp) {
+    const float* P = part + ((int64_t)sp * gridDim.y + zl) * b * b;
+    float v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = min(i0 + rr + 4 * k, r - 1), j = min(j0 + c, r - 1);
+      v[k] = P[(int64_t)i * b + j];
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) u[k] = sp == 0 ? v[k] : u[k] + v[k];
+  }
+  const int64_t off = (zoff + zl) * b * b;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int i = i0 + rr + 4 * k, j = j0 + c;
+    t[rr + 4 * k][c] = u[k];
+    if (i < r && j < r) {
+      ch.F32[off + (int64_t)i * b + j] = u[k];
+      ch.Ub[off + (int64_t)i * b + j] = from_f32<T>(u[k]);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int jj = rr + 4 * k, j = j0 + jj, i = i0 + c;  // Utb[j][i] = U[i][j]
+    if (i < r && j < r) ch.Utb[off + (int64_t)j * b + i] = from_f32<T>(t[c][jj]);
+  }
+}
+
 // Chain rule in three launches; each workgroup forms one tile of two
 // products, X Q (X = U, V1, V2) and Q Y (Y = U, Y1, Y2):
 //   step 1: V1 = U Q,  P = Q U;   Y1 = 2U - V1 - P,         F = 2U - 2V1
@@ -332,7 +431,7 @@ __global__ __launch_bounds__(C::NT * G) void k_block_grads(Sides sd, GradSides<T
 // X Q loads Q's rows as the B operand, which gives X Q^T = -X Q; Q Y loads
 // the rows of Y^T, which the previous step wrote.
 template <class C, typename T, int STEP>
-__global__ __launch_bounds__(C::NT) void k_cnp_step(Sides sd, int b, Chain<T> ch) {
+__global__ __launch_bounds__(C::NT) void k_cnp_step(SideTable sd, int b, Chain<T> ch) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int z = blockIdx.z;
   const float* qk;
@@ -390,18 +489,18 @@ __global__ __launch_bounds__(C::NT) void k_cnp_step(Sides sd, int b, Chain<T> ch
 }
 
 struct DqOut {
-  float* dq[2];
+  float* dq[pxk::kMaxSides];
 };
 
 // dq[p(i, j)] = dQ[i][j] - dQ[j][i] for i < j (zero where j >= r), one 64 x 64
 // tile on or above the diagonal per workgroup; the mirrored tile is staged
 // through LDS so that reads and writes are row-contiguous.
-__global__ __launch_bounds__(256) void k_pack_dq(Sides sd, int b, const float* __restrict__ dQ32, DqOut out) {
+__global__ __launch_bounds__(256) void k_pack_dq(SideTable sd, int b, const float* __restrict__ dQ32, DqOut out) {
   __shared__ float t[64][65];
   const int z = blockIdx.y;
-  const int s = z >= sd.nb0;
-  const int blk = z - s * sd.nb0;
-  const int r = min(b, sd.d[s] - blk * b);
+  int s, blk, r;
+  const float* qk;
+  sd.at(z, b, s, blk, r, qk);
   const int tiles = (b + 63) / 64;
   const int i0 = (blockIdx.x / tiles) * 64, j0 = (blockIdx.x % tiles) * 64;
   if (i0 > j0) return;
@@ -437,9 +536,9 @@ template <> struct CnpTile<float> { using C = TF; };
 inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
 
 template <typename T>
-hipError_t build_t(const float* q, int d, int b, T* g, void* ws, hipStream_t s) {
+hipError_t build_t(const SideTable& sd, int b, const GOut& go, void* ws, hipStream_t s) {
   using C = typename CnpTile<T>::C;
-  const int nb = pxk::nblocks(d, b);
+  const int nb = sd.first[sd.count];
   const size_t E = (size_t)nb * b * b;
   char* w = reinterpret_cast<char*>(ws);
   T* Qb = reinterpret_cast<T*>(w);
@@ -449,7 +548,6 @@ hipError_t build_t(const float* q, int d, int b, T* g, void* ws, hipStream_t s) 
   T* Sb = reinterpret_cast<T*>(w);
   w += al256(E * sizeof(T));
   T* Ntb = reinterpret_cast<T*>(w);
-  Sides sd{{q, q}, {d, d}, nb};
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = allow_lds(k_cnp_square<C, T>, lds);
   if (e == hipSuccess) e = allow_lds(k_cnp_delta<C, T>, lds);
@@ -458,7 +556,7 @@ hipError_t build_t(const float* q, int d, int b, T* g, void* ws, hipStream_t s) 
   k_unpack_q<T><<<dim3(t64 * t64, nb), 256, 0, s>>>(sd, b, Qb, Q32);
   dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), nb);
   k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(sd, b, Qb, Q32, Sb, Ntb);
-  k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(sd, b, nb, Q32, Sb, Ntb, g);
+  k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(sd, b, Q32, Sb, Ntb, go);
   return hipGetLastError();
 }
 
@@ -482,13 +580,27 @@ template <typename T> Chain<T> carve(void* ws, size_t E) {
   return ch;
 }
 
+SideTable make_table(int count, const float* const* q, const int* d, int b) {
+  SideTable t{};
+  t.count = count;
+  t.first[0] = 0;
+  for (int i = 0; i < count; ++i) {
+    t.q[i] = q[i];
+    t.d[i] = d[i];
+    t.first[i + 1] = t.first[i] + pxk::nblocks(d[i], b);
+  }
+  return t;
+}
+
 template <typename T>
-hipError_t grads_t(const pxk::CnpSide* sides, int rows, int b, void* ws, hipStream_t s) {
+hipError_t grads_t(const pxk::CnpSide* sides, int rows, int b, void* dg, int64_t zoff, int64_t total, float* part,
+                   hipStream_t s) {
   using C = typename CnpTile<T>::C;
-  const int nb0 = pxk::nblocks(sides[0].d, b), nb1 = pxk::nblocks(sides[1].d, b);
-  const int NB = nb0 + nb1;
-  Chain<T> ch = carve<T>(ws, (size_t)NB * b * b);
-  Sides sd{{sides[0].q, sides[1].q}, {sides[0].d, sides[1].d}, nb0};
+  const float* q[2] = {sides[0].q, sides[1].q};
+  const int d[2] = {sides[0].d, sides[1].d};
+  const SideTable sd = make_table(2, q, d, b);
+  const int NB = sd.first[2];
+  Chain<T> ch = carve<T>(dg, (size_t)total * b * b);
   GradSides<T> gs;
   for (int k = 0; k < 2; ++k) {
     gs.A[k] = reinterpret_cast<const T*>(sides[k].A);
@@ -496,33 +608,42 @@ hipError_t grads_t(const pxk::CnpSide* sides, int rows, int b, void* ws, hipStre
     gs.lda[k] = sides[k].lda;
     gs.ldb[k] = sides[k].ldb;
   }
-  const unsigned t64 = cdiv(b, 64);
-  k_unpack_q<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb), nullptr);
-  dim3 grid(cdiv(b, C::BM) * cdiv(b, C::BN), NB);
   hipError_t e;
+  const int S = pxk::block_grads_splits(sizeof(T) == 2 ? pxk::BF16 : pxk::F32, rows, NB, b);
+  if (S > 0) {
+    using CB = TGemm;  // 256 x 256, 8 waves
+    constexpr int lds = Lay<CB, T>::BYTES;
+    e = allow_lds(k_block_grads_part<CB, T>, lds);
+    if (e != hipSuccess) return e;
+    k_block_grads_part<CB, T><<<dim3(cdiv(b, CB::BM) * cdiv(b, CB::BN), NB, S), CB::NT, lds, s>>>(sd, gs, rows, b, S,
+                                                                                                 part);
+    const unsigned t64 = cdiv(b, 64);
+    k_block_grads_reduce<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, S, part, ch, zoff);
+    return hipGetLastError();
+  }
+  dim3 grid(cdiv(b, C::BM) * cdiv(b, C::BN), NB);
   if (rows % (2 * C::BK) == 0) {
     // two groups per tile, each over half of the tokens
     constexpr int lds = std::max(2 * Lay<C, T>::BYTES, C::BM * (C::BN + 4) * 4);
     e = allow_lds(k_block_grads<C, T, 2>, lds);
     if (e != hipSuccess) return e;
-    k_block_grads<C, T, 2><<<grid, 2 * C::NT, lds, s>>>(sd, gs, rows, b, ch);
+    k_block_grads<C, T, 2><<<grid, 2 * C::NT, lds, s>>>(sd, gs, rows, b, ch, zoff);
   } else {
     constexpr int lds = Lay<C, T>::BYTES;
     e = allow_lds(k_block_grads<C, T, 1>, lds);
     if (e != hipSuccess) return e;
-    k_block_grads<C, T, 1><<<grid, C::NT, lds, s>>>(sd, gs, rows, b, ch);
+    k_block_grads<C, T, 1><<<grid, C::NT, lds, s>>>(sd, gs, rows, b, ch, zoff);
   }
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t chain_t(const pxk::CnpSide* sides, int b, void* ws, hipStream_t s) {
+hipError_t chain_t(const SideTable& sd, int b, void* dg, const DqOut& out, hipStream_t s) {
   using C = typename CnpTile<T>::C;
-  const int nb0 = pxk::nblocks(sides[0].d, b), nb1 = pxk::nblocks(sides[1].d, b);
-  const int NB = nb0 + nb1;
-  Chain<T> ch = carve<T>(ws, (size_t)NB * b * b);
-  Sides sd{{sides[0].q, sides[1].q}, {sides[0].d, sides[1].d}, nb0};
-  DqOut out{{sides[0].dq, sides[1].dq}};
+  const int NB = sd.first[sd.count];
+  Chain<T> ch = carve<T>(dg, (size_t)NB * b * b);
+  const unsigned t64 = cdiv(b, 64);
+  k_unpack_q<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb), nullptr);
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = hipSuccess;
   const dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), NB);
@@ -534,7 +655,6 @@ hipError_t chain_t(const pxk::CnpSide* sides, int b, void* ws, hipStream_t s) {
   PX_STEP(2)
   PX_STEP(3)
 #undef PX_STEP
-  const unsigned t64 = cdiv(b, 64);
   k_pack_dq<<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, ch.F32, out);
   return hipGetLastError();
 }
@@ -543,29 +663,55 @@ hipError_t chain_t(const pxk::CnpSide* sides, int b, void* ws, hipStream_t s) {
 
 namespace pxk {
 
-size_t cnp_build_ws_bytes(int dt, int d, int b) {
-  const size_t E = (size_t)nblocks(d, b) * b * b, es = dt_size(dt);
+size_t cnp_build_ws_bytes(int dt, int64_t blocks, int b) {
+  const size_t E = (size_t)blocks * b * b, es = dt_size(dt);
   return al256(E * es) * 3 + al256(E * 4);
 }
 
-size_t cnp_backward_ws_bytes(int dt, int d0, int d1, int b) {
-  const size_t E = (size_t)(nblocks(d0, b) + nblocks(d1, b)) * b * b, es = dt_size(dt);
+size_t cnp_grad_bytes(int dt, int64_t blocks, int b) {
+  const size_t E = (size_t)blocks * b * b, es = dt_size(dt);
   return al256(E * es) * 7 + al256(E * 4);
 }
 
-hipError_t cnp_build(int dt, const float* q, int d, int b, void* g, void* ws, hipStream_t s) {
-  if (dt == BF16) return build_t<bf16_t>(q, d, b, reinterpret_cast<bf16_t*>(g), ws, s);
-  return build_t<float>(q, d, b, reinterpret_cast<float*>(g), ws, s);
+hipError_t cnp_build_batch(int dt, int count, const float* const* q, const int* d, int b, void* const* g, void* ws,
+                           hipStream_t s) {
+  if (count < 1 || count > kMaxSides) return hipErrorInvalidValue;
+  const SideTable sd = make_table(count, q, d, b);
+  GOut go{};
+  for (int i = 0; i < count; ++i) go.g[i] = g[i];
+  if (dt == BF16) return build_t<bf16_t>(sd, b, go, ws, s);
+  return build_t<float>(sd, b, go, ws, s);
 }
 
-hipError_t block_grads(int cdt, const CnpSide* sides, int rows, int b, void* ws, hipStream_t s) {
-  if (cdt == BF16) return grads_t<bf16_t>(sides, rows, b, ws, s);
-  return grads_t<float>(sides, rows, b, ws, s);
+int block_grads_splits(int dt, int rows, int blocks, int b) {
+  // bf16 blocks of a multiple of 256: 256 x 256 tiles, token splits (powers of
+  // two up to 8, each a multiple of 64 rows) until the grid has 512 workgroups
+  if (dt != BF16 || b % 256 != 0 || rows <= 0) return 0;
+  const int64_t tiles = (int64_t)(b / 256) * (b / 256) * blocks;
+  int S = 1;
+  while (S < 8 && tiles * S < 512 && rows % (2 * S * 64) == 0) S *= 2;
+  return S;
 }
 
-hipError_t cnp_chain(int cdt, const CnpSide* sides, int b, void* ws, hipStream_t s) {
-  if (cdt == BF16) return chain_t<bf16_t>(sides, b, ws, s);
-  return chain_t<float>(sides, b, ws, s);
+size_t block_grads_part_bytes(int dt, int rows, int blocks, int b) {
+  const int S = block_grads_splits(dt, rows, blocks, b);
+  return (size_t)S * blocks * b * b * 4;
+}
+
+hipError_t block_grads(int cdt, const CnpSide* sides, int rows, int b, void* dg, int64_t zoff, int64_t total,
+                       float* part, hipStream_t s) {
+  if (cdt == BF16) return grads_t<bf16_t>(sides, rows, b, dg, zoff, total, part, s);
+  return grads_t<float>(sides, rows, b, dg, zoff, total, part, s);
+}
+
+hipError_t cnp_chain_batch(int cdt, int count, const float* const* q, const int* d, int b, void* dg, float* const* dq,
+                           hipStream_t s) {
+  if (count < 1 || count > kMaxSides) return hipErrorInvalidValue;
+  const SideTable sd = make_table(count, q, d, b);
+  DqOut out{};
+  for (int i = 0; i < count; ++i) out.dq[i] = dq[i];
+  if (cdt == BF16) return chain_t<bf16_t>(sd, b, dg, out, s);
+  return chain_t<float>(sd, b, dg, out, s);
 }
 
 }  // namespace pxk

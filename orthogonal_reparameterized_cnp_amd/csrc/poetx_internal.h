@@ -29,10 +29,16 @@ hipError_t compose_perm(const int32_t* a, const int32_t* b, int d, int32_t* out,
 // Durstenfeld shuffle of the identity driven by SplitMix64(seed)
 hipError_t perm_from_seed_device(uint64_t seed, int d, int32_t* out, int32_t* scratch, hipStream_t s);
 
-// Delta = G - I of every block of one side, and its transpose:
-// g = [2][nb][b][b] in dtype dt (F32 or BF16); ws of cnp_build_ws_bytes bytes.
-hipError_t cnp_build(int dt, const float* q, int d, int b, void* g, void* ws, hipStream_t s);
-size_t cnp_build_ws_bytes(int dt, int d, int b);
+// Most sides in one batched CNP launch (the size of the kernels' side table).
+constexpr int kMaxSides = 64;
+
+// Delta = G - I of every block of `count` sides, and its transpose: side i
+// writes g[i] = [2][nb_i][b][b] in dtype dt (F32 or BF16).  Sides are
+// independent; the blocks of all of them share each launch.  ws holds
+// cnp_build_ws_bytes(dt, sum of nb_i, b) bytes.
+hipError_t cnp_build_batch(int dt, int count, const float* const* q, const int* d, int b, void* const* g, void* ws,
+                           hipStream_t s);
+size_t cnp_build_ws_bytes(int dt, int64_t blocks, int b);
 
 // Row-form block-diagonal product: out[:, kb+j] = (in[:, kb+j] + sum_k in[:, kb+k] D_blk[k][j]) * scale[kb+j]
 // where the B operand array `dT` holds D_blk^T, i.e. dT[blk][j][k] = D_blk[k][j].
@@ -44,10 +50,14 @@ hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, in
 hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const void* B, int64_t ldb, bool b_kn, int M,
                 int N, int K, const float* colscale, int out_dt, void* out, int64_t ldo, hipStream_t s);
 
-// Block gradients and CNP chain rule of both sides of a linear (side 0 = R,
-// side 1 = P), sharing one scratch of cnp_backward_ws_bytes bytes:
-//   block_grads: U_s[blk] = sum over all rows t of A_s[t][blk cols]^T B_s[t][blk cols]
-//   cnp_chain:   U -> dQ through the CNP chain rule -> packed dq (overwritten)
+// Block gradients and CNP chain rule.  The gradient state `dg` of
+// cnp_grad_bytes(dt, blocks, b) bytes holds, for `blocks` CNP blocks of one
+// batch of sides, the block gradients and the chain rule's intermediates.
+//   block_grads: the two sides of one linear (side 0 = R, side 1 = P),
+//     U_s[blk] = sum over all rows t of A_s[t][blk cols]^T B_s[t][blk cols],
+//     written to blocks [zoff, zoff + nb_R + nb_P) of dg (which has `total` blocks)
+//   cnp_chain_batch: U -> dQ through the CNP chain rule -> packed dq[i]
+//     (overwritten) for `count` sides whose blocks fill dg in order
 struct CnpSide {
   const float* q;
   int d;
@@ -55,11 +65,17 @@ struct CnpSide {
   int64_t lda;
   const void* B;  // [rows][ldb]: dA for R, dZt for P
   int64_t ldb;
-  float* dq;
 };
-hipError_t block_grads(int cdt, const CnpSide* sides, int rows, int b, void* ws, hipStream_t s);
-hipError_t cnp_chain(int cdt, const CnpSide* sides, int b, void* ws, hipStream_t s);
-size_t cnp_backward_ws_bytes(int dt, int d0, int d1, int b);
+//   Large bf16 blocks are summed in token splits whose fp32 partials go to
+//   `part` (block_grads_part_bytes bytes, 0 when no split is used) and are
+//   added in split order.
+hipError_t block_grads(int cdt, const CnpSide* sides, int rows, int b, void* dg, int64_t zoff, int64_t total,
+                       float* part, hipStream_t s);
+int block_grads_splits(int dt, int rows, int blocks, int b);
+size_t block_grads_part_bytes(int dt, int rows, int blocks, int b);
+hipError_t cnp_chain_batch(int cdt, int count, const float* const* q, const int* d, int b, void* dg, float* const* dq,
+                           hipStream_t s);
+size_t cnp_grad_bytes(int dt, int64_t blocks, int b);
 
 // Merge helpers (fp32 MFMA).
 // M1[kb+i][c] = (W[kb+i][c] + sum_k DeltaR_blk[i][k] W[kb+k][c]) * wscale[c]

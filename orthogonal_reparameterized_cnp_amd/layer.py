@@ -129,3 +129,57 @@ class PoetxLinear:
     def saved_H(self, T: int) -> torch.Tensor:
         dt = _TORCH_DT[self.act]
         return self.H_save.view(dt)[: T * lead(self.n)].view(T, lead(self.n))
+
+
+class PoetxGroup:
+    """Several linears whose CNP work runs batched: one build of every side's G
+    (poetx_cnp_build_batch) and one chain rule for every side's dq
+    (poetx_cnp_backward_batch) after each linear's poetx_linear_bwd_dx.
+
+    Results are bit-identical to the per-linear calls; the batch only shares
+    launches between the sides.
+    """
+
+    def __init__(self, layers):
+        if not layers:
+            raise ValueError("empty group")
+        L0 = layers[0]
+        if any(l.b != L0.b or l.act != L0.act or l.device != L0.device for l in layers):
+            raise ValueError("the linears of a group must share b, act dtype and device")
+        self.layers = list(layers)
+        self.b, self.act, self.device = L0.b, L0.act, L0.device
+        self.adt = B.DTYPES[self.act]
+        self.d = [x for l in self.layers for x in (l.m, l.n)]
+        self.first, blocks = [], 0
+        for l in self.layers:
+            self.first.append(blocks)
+            blocks += l.nbR + l.nbP
+        self.blocks = blocks
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        self.dg = torch.empty(B.poetx_cnp_grad_bytes(blocks, self.b, self.adt), **u8)
+        self.ws = torch.empty(B.poetx_cnp_batch_workspace_size(self.d, self.b, self.adt), **u8)
+
+    def build(self, stream=None):
+        q = [x for l in self.layers for x in (l.q_R, l.q_P)]
+        g = [x for l in self.layers for x in (l.g_R, l.g_P)]
+        B.poetx_cnp_build_batch(q, self.d, self.b, self.adt, g, self.ws, self.ws.numel(), stream)
+
+    def backward_dx(self, i: int, X: torch.Tensor, dZ: torch.Tensor, dX=None, stream=None) -> torch.Tensor:
+        """dX of linear i; its block gradients go to the group's gradient state."""
+        lay = self.layers[i]
+        T = X.shape[0]
+        lay.reserve(T)
+        if dX is None:
+            dX = torch.empty(T, lay.m, dtype=X.dtype, device=self.device)
+        B.poetx_linear_bwd_dx(lay.desc, T, X, dZ, lay.perm_R, lay.perm_P, lay.Wt, lay.g_R, lay.g_P, lay.q_R, lay.q_P,
+                              lay.H_save, dX, self.dg, self.first[i], self.blocks, lay.ws, lay.ws.numel(), stream)
+        return dX
+
+    def backward_q(self, dqs=None, stream=None):
+        """dq of every side from the gradient state; dqs: [(dq_R, dq_P)] per linear (allocated if None)."""
+        if dqs is None:
+            dqs = [(torch.empty_like(l.q_R), torch.empty_like(l.q_P)) for l in self.layers]
+        q = [x for l in self.layers for x in (l.q_R, l.q_P)]
+        dq = [x for pair in dqs for x in pair]
+        B.poetx_cnp_backward_batch(q, self.d, self.b, self.adt, self.dg, self.dg.numel(), dq, stream)
+        return dqs

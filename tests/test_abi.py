@@ -79,3 +79,62 @@ def test_validation_statuses(L):
     out = (ctypes.c_int32 * 4)()
     assert L.poetx_perm_from_seed(1, 0, out) == B.POETX_E_SHAPE
     assert L.poetx_perm_from_seed(1, 4, None) == B.POETX_E_NULL
+
+
+def _pp(*ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def _ii(*xs):
+    return (ctypes.c_int32 * len(xs))(*xs)
+
+
+def test_batched_cnp_helpers(L):
+    f32, bf = B.POETX_F32, B.POETX_BF16
+    # one side in a batch needs what the single build needs
+    for d, b, dt in ((1376, 256, bf), (256, 32, f32), (5461, 256, bf)):
+        single = B.poetx_workspace_size(B.desc(d, 1, b, "bf16" if dt == bf else "f32", "bf16" if dt == bf else "f32"),
+                                        0, B.POETX_OP_CNP)
+        assert B.poetx_cnp_batch_workspace_size([d], b, dt) == single > 0
+    assert B.poetx_cnp_batch_workspace_size([4096, 14336], 512, bf) > B.poetx_cnp_batch_workspace_size([4096], 512, bf)
+    assert L.poetx_cnp_batch_workspace_size(0, _ii(256), 32, f32) == 0
+    assert B.poetx_cnp_batch_workspace_size([256], 32, B.POETX_I8) == 0
+    assert B.poetx_cnp_grad_bytes(10, 512, bf) > B.poetx_cnp_grad_bytes(5, 512, bf) > 0
+    assert B.poetx_cnp_grad_bytes(0, 512, bf) == 0
+    assert B.poetx_cnp_grad_bytes(10, 1, bf) == 0
+    assert B.poetx_cnp_grad_bytes(10, 512, B.POETX_I8) == 0
+
+
+def test_batched_cnp_validation(L):
+    f32 = B.POETX_F32
+    big = 1 << 40
+    ok3 = (_pp(FAKE, FAKE, FAKE), _ii(256, 96, 300), 32, f32, _pp(FAKE, FAKE, FAKE))
+    assert L.poetx_cnp_build_batch(0, *ok3, FAKE, big, None) == B.POETX_E_SHAPE
+    assert L.poetx_cnp_build_batch(65, _pp(*[FAKE] * 65), _ii(*[256] * 65), 32, f32, _pp(*[FAKE] * 65), FAKE, big,
+                                   None) == B.POETX_E_SHAPE
+    assert L.poetx_cnp_build_batch(3, _pp(FAKE, None, FAKE), _ii(256, 96, 300), 32, f32, _pp(FAKE, FAKE, FAKE),
+                                   FAKE, big, None) == B.POETX_E_NULL
+    assert L.poetx_cnp_build_batch(3, *ok3[:3], B.POETX_I8, ok3[4], FAKE, big, None) == B.POETX_E_DTYPE
+    assert L.poetx_cnp_build_batch(3, *ok3, FAKE, 64, None) == B.POETX_E_WORKSPACE
+    assert L.poetx_cnp_build_batch(3, ok3[0], _ii(256, 0, 300), 32, f32, ok3[4], FAKE, big, None) == B.POETX_E_SHAPE
+    # more than 65535 blocks in one batch
+    assert L.poetx_cnp_build_batch(2, _pp(FAKE, FAKE), _ii(1 << 20, 1 << 20), 2, f32, _pp(FAKE, FAKE), FAKE, big,
+                                   None) == B.POETX_E_SHAPE
+    # backward_dx: gradient state checks come after the bwd checks
+    good = B.desc(256, 96, 32, "f32", "f32")  # 8 + 3 blocks
+    a = [FAKE] * 11
+    bwd_dx = lambda dg, first, total: L.poetx_linear_bwd_dx(ctypes.byref(good), 4, *a, dg, first, total, FAKE, big,
+                                                            None)
+    assert bwd_dx(None, 0, 11) == B.POETX_E_NULL
+    assert bwd_dx(FAKE + 16, 0, 11) == B.POETX_E_WORKSPACE
+    assert bwd_dx(FAKE, 1, 11) == B.POETX_E_SHAPE
+    assert bwd_dx(FAKE, -1, 20) == B.POETX_E_SHAPE
+    assert L.poetx_linear_bwd_dx(ctypes.byref(good), 4, *a, FAKE, 0, 11, FAKE, 16, None) == B.POETX_E_WORKSPACE
+    # backward_batch
+    need = B.poetx_cnp_grad_bytes(11, 32, f32)
+    bb = lambda dq, dg_bytes: L.poetx_cnp_backward_batch(2, _pp(FAKE, FAKE), _ii(256, 96), 32, f32, FAKE, dg_bytes,
+                                                         dq, None)
+    assert bb(_pp(FAKE, None), need) == B.POETX_E_NULL
+    assert bb(_pp(FAKE, FAKE), need - 1) == B.POETX_E_WORKSPACE
+    assert L.poetx_cnp_backward_batch(2, _pp(FAKE, FAKE), _ii(256, 96), 32, f32, None, need, _pp(FAKE, FAKE),
+                                      None) == B.POETX_E_NULL
