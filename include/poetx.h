@@ -103,8 +103,11 @@ size_t poetx_g_bytes(int32_t d, int32_t b, int32_t dtype);
  * the fp32 column scales [ldw] in pre-merged column order. */
 size_t poetx_weight_bytes(const poetx_layer_desc* desc);
 
-/* Bytes of the saved activation H = (X R-side product) W~ kept by the forward
- * for the backward: [T][round_up(n, 64)] elements of act_dtype. */
+/* Bytes of the state the forward saves for the backward of the same T tokens:
+ * H = Xt Diag(G_R) W~ as [T][round_up(n, 64)] elements of act_dtype, then, at
+ * the next 256-byte boundary, the gathered input Xt = X[:, perm_R] as
+ * [T][round_up(m, 64)].  The backward reads Xt from here instead of gathering X
+ * again, so a caller need not keep X for the backward. */
 size_t poetx_saved_bytes(const poetx_layer_desc* desc, int64_t T);
 
 /* Workspace bytes for `op` (POETX_OP_CNP uses desc->m as the side length d and
@@ -174,7 +177,8 @@ poetx_status poetx_premerge(const poetx_layer_desc* desc, const void* W0, int64_
  *   Wt     pre-merged weight (poetx_premerge / poetx_merge_reinit layout)
  *   g_R, g_P  G buffers from poetx_cnp_build for the two sides
  *   Y      out [T][n] act_dtype, leading dimension n
- *   H_save out, poetx_saved_bytes(desc, T) bytes, read by poetx_linear_bwd
+ *   H_save out, poetx_saved_bytes(desc, T) bytes: the saved state (H, then Xt)
+ *          read by poetx_linear_bwd
  *   ws     >= poetx_workspace_size(desc, T, POETX_OP_FWD)
  * T = 0 is a valid no-op.
  */
@@ -189,9 +193,10 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
  * dG_P = H_blk^T dZt_blk and dG_R = Xt_blk^T dA_blk summed over all T tokens in
  * a fixed order (deterministic), then taken through the CNP chain rule and
  * projected onto the packed slots: dq[p(i,j)] = dQ[i][j] - dQ[j][i].
- *   X, dZ  [T][m], [T][n] act_dtype
+ *   X      not read (the gathered input is in the saved state); may be NULL
+ *   dZ     [T][n] act_dtype
  *   q_R, q_P  the packed parameters the G buffers were built from
- *   H_save the forward's saved activation for the same X
+ *   H_save the forward's saved state for the same T tokens
  *   dX     out [T][m] act_dtype
  *   dq_R, dq_P out [nb][b(b-1)/2] fp32, overwritten (dead slots of a partial block are 0)
  *   ws     >= poetx_workspace_size(desc, T, POETX_OP_BWD)

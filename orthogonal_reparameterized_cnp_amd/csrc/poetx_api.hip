@@ -125,14 +125,19 @@ size_t weight_scale_offset(const poetx_layer_desc* d) {
   return (size_t)round_up((int64_t)d->m * lead(d->n) * (int64_t)dt_size(d->w_dtype), 256);
 }
 
+// The forward's saved state: H [T][lead(n)], then (256-byte aligned) the
+// gathered input Xt [T][lead(m)], both in act_dtype.
+size_t saved_xt_offset(const poetx_layer_desc* d, int64_t T) {
+  return (size_t)round_up(T * lead(d->n) * (int64_t)dt_size(d->act_dtype), 256);
+}
+
 struct FwdWs {
-  void *Xt, *A, *Zt;
+  void *A, *Zt;
   int32_t* invP;
 };
 template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
   const size_t es = dt_size(d->act_dtype);
   FwdWs w;
-  w.Xt = p.template take<char>(T * lead(d->m) * es);
   w.A = p.template take<char>(T * lead(d->m) * es);
   w.Zt = p.template take<char>(T * lead(d->n) * es);
   w.invP = p.template take<int32_t>((size_t)d->n * 4);
@@ -140,7 +145,7 @@ template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
 }
 
 struct BwdWs {
-  void *dZt, *dH, *dA, *Xt, *dXt, *cnp;
+  void *dZt, *dH, *dA, *dXt, *cnp;
   float* part;
   int32_t* invR;
 };
@@ -150,7 +155,6 @@ template <class P> BwdWs plan_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
   w.dZt = p.template take<char>(T * lead(d->n) * es);
   w.dH = p.template take<char>(T * lead(d->n) * es);
   w.dA = p.template take<char>(T * lead(d->m) * es);
-  w.Xt = p.template take<char>(T * lead(d->m) * es);
   w.dXt = p.template take<char>(T * lead(d->m) * es);
   w.cnp = p.template take<char>(cnp_grad_bytes(d->act_dtype, (int64_t)nblocks(d->m, d->b) + nblocks(d->n, d->b), d->b));
   w.part = p.template take<float>(
@@ -232,7 +236,7 @@ size_t poetx_weight_bytes(const poetx_layer_desc* desc) {
 
 size_t poetx_saved_bytes(const poetx_layer_desc* desc, int64_t T) {
   if (check_desc(desc) != POETX_OK || T < 0) return 0;
-  return (size_t)T * lead(desc->n) * dt_size(desc->act_dtype);
+  return saved_xt_offset(desc, T) + (size_t)T * lead(desc->m) * dt_size(desc->act_dtype);
 }
 
 size_t poetx_workspace_size(const poetx_layer_desc* desc, int64_t T, int32_t op) {
@@ -380,11 +384,12 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
       wt == POETX_I8 ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(Wt) + weight_scale_offset(desc))
                      : nullptr;
   const double es = (double)dt_size(at), wes = (double)dt_size(wt);
-  // Xt = X[:, perm_R]
-  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
+  // Xt = X[:, perm_R], kept in the saved state for the backward
+  void* Xt = reinterpret_cast<char*>(H_save) + saved_xt_offset(desc, T);
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, Xt, ldm, rows, m, m, s));
   // A = Xt Diag(G_R)
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
-           apply(at, at, w.Xt, ldm, rows, m, b, at, gR1, nullptr, at, w.A, ldm, s));
+           apply(at, at, Xt, ldm, rows, m, b, at, gR1, nullptr, at, w.A, ldm, s));
   // H = A W~ (int8: codes times the column scale)
   PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
            gemm(at, at, w.A, ldm, wt, Wt, lead(n), true, rows, n, m, scale_t, at, H_save, ldn, s));
@@ -422,10 +427,10 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* X,
   // dA = dH W~^T
   PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * n + wes * m * n + es * rows * m,
            gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
-  // Xt = X[:, perm_R]
-  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, w.Xt, ldm, rows, m, m, s));
-  // block gradients of both sides over all tokens: dG_R = Xt^T dA, dG_P = H^T dZt
-  const CnpSide sides[2] = {{q_R, m, w.Xt, ldm, w.dA, ldm}, {q_P, n, H_save, ldn, w.dZt, ldn}};
+  // block gradients of both sides over all tokens: dG_R = Xt^T dA, dG_P = H^T dZt, with Xt and H
+  // from the forward's saved state
+  const void* Xt = reinterpret_cast<const char*>(H_save) + saved_xt_offset(desc, T);
+  const CnpSide sides[2] = {{q_R, m, Xt, ldm, w.dA, ldm}, {q_P, n, H_save, ldn, w.dZt, ldn}};
   PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * (sum_r2(m, b) + sum_r2(n, b)),
            2.0 * rows * (m + n) * es + (4 + 2 * es) * (sum_r2(m, b) + sum_r2(n, b)),
            block_grads(at, sides, rows, b, dg, first, total, w.part, s));
@@ -446,7 +451,8 @@ poetx_status check_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, c
   if (st != POETX_OK) return st;
   if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
   if (!perm_R || !perm_P || !Wt || !g_R || !g_P || !q_R || !q_P) return fail(POETX_E_NULL, "a required pointer is NULL");
-  if (T > 0 && (!X || !dZ || !H_save || !dX)) return fail(POETX_E_NULL, "a required pointer is NULL");
+  if (T > 0 && (!dZ || !H_save || !dX)) return fail(POETX_E_NULL, "a required pointer is NULL");
+  (void)X;  // the gathered input comes from the saved state
   Plan p;
   plan_bwd(p, desc, T);
   return check_ws(ws, ws_bytes, p.off);

@@ -34,7 +34,8 @@ def test_host_helpers(L):
     d = B.desc(1024, 5461, 256, "bf16", "i8")
     ldw = 5504
     assert B.poetx_weight_bytes(d) == (1024 * ldw + 255) // 256 * 256 + 4 * ldw
-    assert B.poetx_saved_bytes(d, 10) == 10 * ldw * 2
+    # saved state: H [T][lead(n)], then at a 256-byte boundary Xt [T][lead(m)]
+    assert B.poetx_saved_bytes(d, 10) == (10 * ldw * 2 + 255) // 256 * 256 + 10 * 1024 * 2
     for op in (B.POETX_OP_FWD, B.POETX_OP_BWD, B.POETX_OP_MERGE):
         assert B.poetx_workspace_size(d, 100, op) > 0
     assert B.poetx_workspace_size(B.desc(1024, 5461, 1, "bf16", "bf16"), 100, B.POETX_OP_FWD) == 0

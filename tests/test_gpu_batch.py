@@ -88,3 +88,21 @@ def test_group_backward(act, b, shapes, T, oracle):
             assert_close("dX", host(dX_g, act), ref["dX"], act)
             assert_close("dq_R", host(dqR_g, "f32"), ref["dq_R"], act)
             assert_close("dq_P", host(dqP_g, "f32"), ref["dq_P"], act)
+
+
+def test_backward_reads_saved_input_not_x():
+    """The backward takes the gathered input from the forward's saved state: passing no X (or a
+    different X) gives bit-identical results."""
+    print("backward without X", flush=True)
+    inp = custom_linear_inputs(520, 300, 256, 200, "bf16", "bf16", 0.05, seed=21)
+    lay = make_layer(inp)
+    X, dZ = dev(inp.X, "bf16"), dev(inp.dZ, "bf16")
+    lay.forward(X)
+    ref = [t.clone() for t in lay.backward(X, dZ)]
+    T = X.shape[0]
+    dX = torch.empty_like(ref[0])
+    dq_R, dq_P = torch.empty_like(ref[1]), torch.empty_like(ref[2])
+    B.poetx_linear_bwd(lay.desc, T, None, dZ, lay.perm_R, lay.perm_P, lay.Wt, lay.g_R, lay.g_P, lay.q_R, lay.q_P,
+                       lay.H_save, dX, dq_R, dq_P, lay.ws, lay.ws.numel())
+    torch.cuda.synchronize()
+    assert torch.equal(dX, ref[0]) and torch.equal(dq_R, ref[1]) and torch.equal(dq_P, ref[2])
