@@ -183,6 +183,56 @@ def committed_traffic():
     return None
 
 
+def time_merge(key, to_dev, dev):
+    """poetx_merge_reinit of every linear of one decoder layer of workload `key` (merge-then-reinitialise:
+    fold R and P into the weight, requantise int8 per column, draw new permutations, zero q), timed with
+    events around the calls after one untimed merge; amortised over the workload's merge period."""
+    import torch
+
+    from orthogonal_reparameterized_cnp_amd.layer import PoetxLinear
+    from workloads import WORKLOADS, make_linear_inputs
+
+    wl = WORKLOADS[key]
+    layers = []
+    for i in range(len(wl.linears)):
+        inp = make_linear_inputs(wl, i, T=1)
+        lay = PoetxLinear(inp.m, inp.n, inp.b, inp.act, inp.w)
+        scale = to_dev(inp.w_scale, "f32") if inp.w == "i8" else None
+        lay.load(to_dev(inp.W0, inp.w), scale, to_dev(inp.perm_R, "i32"), to_dev(inp.perm_P, "i32"),
+                 to_dev(inp.q_R, "f32"), to_dev(inp.q_P, "f32"))
+        lay.build()
+        lay._ws(lay.ws_bytes(1))
+        layers.append(lay)
+    torch.cuda.synchronize()
+
+    def merge_all(seed):
+        for j, lay in enumerate(layers):
+            lay.merge_reinit(seed + 2 * j, seed + 2 * j + 1)
+
+    merge_all(1)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    merge_all(1001)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end)
+    flops = 0.0
+    for L in wl.linears:
+        flops += 2.0 * (L.n * side_sums(L.m, wl.b)[0] + L.m * side_sums(L.n, wl.b)[0])
+    period = wl.merge_every or 1
+    print(f"[bench] merge {key}: {ms:.3f} ms per layer merge ({flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s fp32 MFMA), "
+          f"every {period} steps: {ms / period:.4f} ms per step", file=sys.stderr, flush=True)
+    return {
+        "workload": describe(wl),
+        "weights": wl.w,
+        "ms_per_layer_merge": ms,
+        "every_steps": period,
+        "amortised_ms_per_step": ms / period,
+        "tflops_fp32": flops / (ms * 1e-3) / 1e12,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -191,6 +241,9 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="per kernel class timings on stderr")
+    ap.add_argument("--merge", metavar="WORKLOAD", nargs="?", const="llama13b_int8", default=None,
+                    help="also time poetx_merge_reinit of every linear of WORKLOAD (default llama13b_int8) and "
+                         "report it amortised over the workload's merge period")
     ap.add_argument("--copy-probe", action="store_true",
                     help=f"run a {COPY_PROBE_BYTES >> 20} MiB device copy before the steps (counter calibration)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -337,6 +390,9 @@ def main():
             bw = kb / (kms * 1e-3) / 1e9 if kms else 0
             print(f"[bench] {name:8s} launches={n:3d} ms/step={kms:8.3f} TFLOP/s={rate:7.1f} "
                   f"alg GB/s={bw:7.1f}", file=sys.stderr, flush=True)
+
+    if args.merge:
+        result["merge"] = time_merge(args.merge, to_dev, dev)
 
     if not args.no_cpu_baseline:
         lin_f = 4.0 * T * inputs0.m * inputs0.n
