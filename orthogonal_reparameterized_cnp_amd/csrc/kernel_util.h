@@ -12,6 +12,7 @@
 namespace px {
 
 using TGemm = Tile<256, 256, 64, 4, 2>;  // bf16: W~ contractions and block products (8 waves of 64 x 128)
+using TGemmI = Tile<256, 256, 64, 4, 2, false, true>;  // the same with the MFMA / LDS interleave hint (bf16 W~)
 using TBig = Tile<256, 128, 64, 2, 2>;   // bf16: narrow contractions
 using TSq = Tile<128, 128, 64, 2, 2>;   // bf16: block gradients, CNP (b x b outputs)
 // direct-to-LDS configurations (K-contiguous operands, interior tiles)

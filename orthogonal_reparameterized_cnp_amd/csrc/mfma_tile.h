@@ -15,10 +15,11 @@
 
 namespace px {
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, bool PF2 = false>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, bool PF2 = false, bool IG = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
   static constexpr bool PREFETCH2 = PF2;  // two K tiles of global loads in flight
+  static constexpr bool INTERLEAVE = IG;  // ask the compiler to interleave MFMAs and LDS reads
   static constexpr int NW = WM * WN, NT = NW * 64;
   static constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   static constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
@@ -62,7 +63,7 @@ template <class C> struct AccPos {
   PX_DEV int col(int j) const { return wn * C::WTN + j * 32 + (lane & 31); }
 };
 
-template <class C>
+template <class C, bool IGLP = false>
 PX_DEV void mma_stage(const bf16_t* As, const bf16_t* Bs, Acc<C>& acc, int wm, int wn, int lane) {
   constexpr int LDK = Lay<C, bf16_t>::LDK;
   constexpr int KS = C::BK / 16;
@@ -91,10 +92,11 @@ PX_DEV void mma_stage(const bf16_t* As, const bf16_t* Bs, Acc<C>& acc, int wm, i
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
         acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc.v[i][j], 0, 0, 0);
+    if constexpr (IGLP) __builtin_amdgcn_iglp_opt(1);
   }
 }
 
-template <class C>
+template <class C, bool IGLP = false>
 PX_DEV void mma_stage(const float* As, const float* Bs, Acc<C>& acc, int wm, int wn, int lane) {
   constexpr int LDK = Lay<C, float>::LDK;
   const int r = lane & 31, kg = (lane >> 5) * 4;
@@ -142,7 +144,9 @@ PX_DEV void mainloop_t(T* lds, LA& la, LB& lb, int KT, Acc<C>& acc, int wm, int 
       la.template fetch<FAST>((kt + 1) * C::BK);
       lb.template fetch<FAST>((kt + 1) * C::BK);
     }
-    mma_stage<C>(cur, cur + L::A_ELEMS, acc, wm, wn, lane);
+    // the interleave hint only in the unchecked loop without a per-tile hook (with either, the
+    // compiler's scheduling of the larger region takes minutes and tens of GB)
+    mma_stage<C, FAST && C::INTERLEAVE && std::is_same<H, NoHook>::value>(cur, cur + L::A_ELEMS, acc, wm, wn, lane);
     hook(kt, cur);
     if (more) {
       la.stash(nxt);
