@@ -611,7 +611,7 @@ hipError_t grads_t(const pxk::CnpSide* sides, int rows, int b, void* dg, int64_t
   hipError_t e;
   const int S = pxk::block_grads_splits(sizeof(T) == 2 ? pxk::BF16 : pxk::F32, rows, NB, b);
   if (S > 0) {
-    using CB = TGemm;  // 256 x 256, 8 waves
+    using CB = TGemmI;  // 256 x 256, 8 waves, MFMA / LDS interleave hint
     constexpr int lds = Lay<CB, T>::BYTES;
     e = allow_lds(k_block_grads_part<CB, T>, lds);
     if (e != hipSuccess) return e;
