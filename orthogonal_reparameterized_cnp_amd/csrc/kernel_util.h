@@ -17,7 +17,7 @@ using TBig = Tile<256, 128, 64, 2, 2>;   // bf16: narrow contractions
 using TSq = Tile<128, 128, 64, 2, 2>;   // bf16: block gradients, CNP (b x b outputs)
 // direct-to-LDS configurations (K-contiguous operands, interior tiles)
 using DGemm = DCfg<256, 256, 64, 2, 4, 2, false, false, true>;  // 8 waves, same block size as TGemm
-using DSq = DCfg<128, 128, 64, 2, 2, 3, false, false, true>;    // 4 waves, same block size as TSq
+using DSq = DCfg<128, 128, 64, 2, 2, 2, false, false, true>;    // 4 waves, same block size as TSq
 using TF = Tile<64, 64, 32, 2, 2>;      // fp32: small layers
 using TFM = Tile<128, 128, 32, 2, 2>;   // fp32: merge products
 
@@ -133,6 +133,19 @@ PX_DEV void load_at_acc(float (&f)[C::TM][C::TN][16], const float* src, int64_t 
 #pragma unroll
       for (int e = 0; e < 16; ++e) f[i][j][e] = src[(int64_t)min(row0 + p.row(i, e), rmax - 1) * ld + c];
     }
+}
+
+// the same for the accumulator row group ti only: f[j][e] for tile (ti, j)
+template <class C>
+PX_DEV void load_at_acc_i(float (&f)[C::TN][16], const float* src, int64_t ld, int row0, int col0, int rmax, int cmax,
+                          int ti) {
+  const AccPos<C> p = acc_pos<C>();
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) {
+    const int c = min(col0 + p.col(j), cmax - 1);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f[j][e] = src[(int64_t)min(row0 + p.row(ti, e), rmax - 1) * ld + c];
+  }
 }
 
 // true when a K-contiguous operand tile can be copied with 16-byte DMA:

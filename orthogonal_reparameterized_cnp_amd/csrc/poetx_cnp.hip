@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void k_unpack_q(SideTable sd, int b, T* __rest
 // S = Q Q = -(Q Q^T).  Writes S and N^T = S - 2Q in the operand dtype, and
 // replaces Q32 in place by the fp32 partial sum 2Q + 2S.
 template <class C, typename T>
-__global__ __launch_bounds__(C::NT) void k_cnp_square(SideTable sd, int b, const T* __restrict__ Qb,
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_square(SideTable sd, int b, const T* __restrict__ Qb,
                                                       float* __restrict__ Q32, T* __restrict__ Sb,
                                                       T* __restrict__ Ntb) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -207,7 +207,7 @@ struct GOut {
 };
 
 template <class C, typename T>
-__global__ __launch_bounds__(C::NT) void k_cnp_delta(SideTable sd, int b, const float* __restrict__ T2,
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_delta(SideTable sd, int b, const float* __restrict__ T2,
                                                      const T* __restrict__ Sb, const T* __restrict__ Ntb, GOut go) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int z = blockIdx.z;
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(256) void k_block_grads_reduce(SideTable sd, int b,
 // X Q loads Q's rows as the B operand, which gives X Q^T = -X Q; Q Y loads
 // the rows of Y^T, which the previous step wrote.
 template <class C, typename T, int STEP>
-__global__ __launch_bounds__(C::NT) void k_cnp_step(SideTable sd, int b, Chain<T> ch) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_step(SideTable sd, int b, Chain<T> ch) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int z = blockIdx.z;
   const float* qk;
@@ -445,11 +445,12 @@ __global__ __launch_bounds__(C::NT) void k_cnp_step(SideTable sd, int b, Chain<T
   run_kk2<C, T>(smem, X + off + (int64_t)m0 * b, ch.Qb + off + (int64_t)n0 * b, ch.Qb + off + (int64_t)m0 * b,
                 Yt + off + (int64_t)n0 * b, r - m0, r - n0, b, r, [&](auto& xq, auto& qy) {
     using CC = cfg_of<decltype(xq)>;
-    float f[CC::TM][CC::TN][16];
-    load_at_acc<CC>(f, ch.F32 + off, b, m0, n0, r, r);
     const AccPos<CC> p = acc_pos<CC>();
 #pragma unroll
-    for (int ti = 0; ti < CC::TM; ++ti)
+    for (int ti = 0; ti < CC::TM; ++ti) {
+      // one row group of F at a time keeps the epilogue's registers down
+      float f[CC::TN][16];
+      load_at_acc_i<CC>(f, ch.F32 + off, b, m0, n0, r, r, ti);
 #pragma unroll
       for (int tj = 0; tj < CC::TN; ++tj) {
         const int j = n0 + p.col(tj);
@@ -463,7 +464,7 @@ __global__ __launch_bounds__(C::NT) void k_cnp_step(SideTable sd, int b, Chain<T
             if (i0 + e >= r) continue;
             const int k = 4 * g + e;
             const int64_t x = off + (int64_t)(i0 + e) * b + j;
-            const float fv = f[ti][tj][k], v = -xq.v[ti][tj][k], c = qy.v[ti][tj][k];
+            const float fv = f[tj][k], v = -xq.v[ti][tj][k], c = qy.v[ti][tj][k];
             if (STEP == 1) {
               ch.V1b[x] = from_f32<T>(v);
               ch.F32[x] = 2.f * fv - 2.f * v;
@@ -485,6 +486,7 @@ __global__ __launch_bounds__(C::NT) void k_cnp_step(SideTable sd, int b, Chain<T
           }
         }
       }
+    }
   });
 }
 
