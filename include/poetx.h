@@ -99,8 +99,12 @@ int64_t poetx_packed_len(int32_t b);
 size_t poetx_g_bytes(int32_t d, int32_t b, int32_t dtype);
 
 /* Bytes of the pre-merged weight buffer: values [m][ldw] of w_dtype, ldw =
- * round_up(n, 64), followed (POETX_I8 only, at offset round_up(m*ldw, 256)) by
- * the fp32 column scales [ldw] in pre-merged column order. */
+ * round_up(n, 64), followed at offset round_up(m*ldw*size(w_dtype), 256) by
+ *  - POETX_I8: the fp32 column scales [ldw] in pre-merged column order;
+ *  - POETX_BF16: the transposed copy [n][round_up(m, 64)] of the values
+ *    (columns m and up zero), which the forward contraction reads so that
+ *    both of its operands are contiguous along the summed index.
+ * poetx_premerge and poetx_merge_reinit write every part. */
 size_t poetx_weight_bytes(const poetx_layer_desc* desc);
 
 /* Bytes of the state the forward saves for the backward of the same T tokens:
@@ -162,7 +166,8 @@ poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype
  *   W0     [m][ld_w0] of w_dtype (natural layout), ld_w0 >= n
  *   w0_scale [n] fp32 column scales (POETX_I8 only, else NULL)
  *   perm_R [m], perm_P [n] int32 device permutations of 0..m-1 / 0..n-1
- *   Wt     out, poetx_weight_bytes(desc) bytes (pre-merged layout, scales included)
+ *   Wt     out, poetx_weight_bytes(desc) bytes (pre-merged layout, scales or
+ *          transposed copy included)
  * Pure data movement: the result is bit-exact.
  */
 poetx_status poetx_premerge(const poetx_layer_desc* desc, const void* W0, int64_t ld_w0, const float* w0_scale,

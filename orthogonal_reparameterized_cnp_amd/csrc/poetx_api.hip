@@ -125,6 +125,11 @@ size_t weight_scale_offset(const poetx_layer_desc* d) {
   return (size_t)round_up((int64_t)d->m * lead(d->n) * (int64_t)dt_size(d->w_dtype), 256);
 }
 
+// bf16 weights also keep W~^T [n][lead(m)] at the same offset (they have no
+// scales): the forward reads it as a K-contiguous operand
+bool has_weight_t(const poetx_layer_desc* d) { return d->w_dtype == POETX_BF16; }
+size_t weight_t_offset(const poetx_layer_desc* d) { return weight_scale_offset(d); }
+
 // The forward's saved state: H [T][lead(n)], then (256-byte aligned) the
 // gathered input Xt [T][lead(m)], both in act_dtype.
 size_t saved_xt_offset(const poetx_layer_desc* d, int64_t T) {
@@ -231,6 +236,7 @@ size_t poetx_weight_bytes(const poetx_layer_desc* desc) {
   if (check_desc(desc) != POETX_OK) return 0;
   size_t bytes = weight_scale_offset(desc);
   if (desc->w_dtype == POETX_I8) bytes += (size_t)lead(desc->n) * 4;
+  if (has_weight_t(desc)) bytes += (size_t)desc->n * lead(desc->m) * dt_size(desc->w_dtype);
   return bytes;
 }
 
@@ -351,6 +357,8 @@ poetx_status poetx_premerge(const poetx_layer_desc* desc, const void* W0, int64_
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int m = desc->m, n = desc->n;
   PX_HIP(permute(desc->w_dtype, W0, ld_w0, perm_R, perm_P, Wt, lead(n), m, n, n, s));
+  if (has_weight_t(desc))
+    PX_HIP(transpose(desc->w_dtype, Wt, lead(n), m, n, reinterpret_cast<char*>(Wt) + weight_t_offset(desc), lead(m), s));
   if (desc->w_dtype == POETX_I8) {
     float* scale_t = reinterpret_cast<float*>(reinterpret_cast<char*>(Wt) + weight_scale_offset(desc));
     PX_HIP(permute(F32, w0_scale, 0, nullptr, perm_P, scale_t, 0, 1, n, n, s));
@@ -390,9 +398,15 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
   // A = Xt Diag(G_R)
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
            apply(at, at, Xt, ldm, rows, m, b, at, gR1, nullptr, at, w.A, ldm, s));
-  // H = A W~ (int8: codes times the column scale)
-  PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
-           gemm(at, at, w.A, ldm, wt, Wt, lead(n), true, rows, n, m, scale_t, at, H_save, ldn, s));
+  // H = A W~ (int8: codes times the column scale); bf16 weights are read from the W~^T copy
+  if (has_weight_t(desc)) {
+    const void* Wtt = reinterpret_cast<const char*>(Wt) + weight_t_offset(desc);
+    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
+             gemm(at, at, w.A, ldm, wt, Wtt, ldm, false, rows, n, m, nullptr, at, H_save, ldn, s));
+  } else {
+    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
+             gemm(at, at, w.A, ldm, wt, Wt, lead(n), true, rows, n, m, scale_t, at, H_save, ldn, s));
+  }
   // Zt = H Diag(G_P)
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
            apply(at, at, H_save, ldn, rows, n, b, at, gP1, nullptr, at, w.Zt, ldn, s));
@@ -559,6 +573,8 @@ poetx_status poetx_merge_reinit(const poetx_layer_desc* desc, void* Wt, int32_t*
     PX_HIP(col_absmax(w.Mq, ldw, m, n, w.amax, s));
   }
   PX_HIP(store_weight(w.Mq, ldw, m, n, wt, Wt, ldw, w.amax, scale_t, s));
+  if (has_weight_t(desc))
+    PX_HIP(transpose(wt, Wt, ldw, m, n, reinterpret_cast<char*>(Wt) + weight_t_offset(desc), lead(m), s));
   PX_HIP(hipMemcpyAsync(perm_R, w.newR, (size_t)m * 4, hipMemcpyDeviceToDevice, s));
   PX_HIP(hipMemcpyAsync(perm_P, w.newP, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
   PX_HIP(fill_zero(q_R, (size_t)nblocks(m, b) * packed_len(b) * 4, s));

@@ -278,6 +278,29 @@ __global__ __launch_bounds__(256) void k_permute_lds(const E* __restrict__ in, i
   }
 }
 
+// dst[c][r] = src[r][c] (bit copy) through a 64 x 64 LDS tile, so that both
+// the reads and the writes run along rows; dst columns r in [rows, ld_dst)
+// are zero-filled.  Workgroup (x, y) covers dst rows [64y, 64y + 64) and dst
+// columns [64x, 64x + 64).
+template <typename U>
+__global__ __launch_bounds__(256) void k_transpose(const U* __restrict__ src, int64_t ld_src, int rows, int cols,
+                                                   U* __restrict__ dst, int64_t ld_dst) {
+  __shared__ uint32_t t[64][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int x = threadIdx.x & 63, y = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + y + 4 * k, c = c0 + x;
+    t[y + 4 * k][x] = (r < rows && c < cols) ? (uint32_t)src[(int64_t)r * ld_src + c] : 0u;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int c = c0 + y + 4 * k, r = r0 + x;
+    if (c < cols && r < ld_dst) dst[(int64_t)c * ld_dst + r] = (U)t[x][y + 4 * k];
+  }
+}
+
 template <typename E>
 __global__ __launch_bounds__(256) void k_permute_direct(const E* __restrict__ in, int64_t ld_in,
                                                         const int32_t* __restrict__ rowmap,
@@ -456,6 +479,23 @@ hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap,
   if (dt == F32) return go(float{});
   if (dt == BF16) return go(bf16_t{});
   return go(int8_t{});
+}
+
+hipError_t transpose(int dt, const void* src, int64_t ld_src, int rows, int cols, void* dst, int64_t ld_dst,
+                     hipStream_t s) {
+  if (rows <= 0 || cols <= 0 || ld_dst < rows) return rows <= 0 || cols <= 0 ? hipSuccess : hipErrorInvalidValue;
+  const dim3 grid(cdiv(ld_dst, 64), cdiv(cols, 64));
+  if (grid.y > 65535) return hipErrorInvalidValue;
+  if (dt == F32)
+    k_transpose<uint32_t><<<grid, 256, 0, s>>>(reinterpret_cast<const uint32_t*>(src), ld_src, rows, cols,
+                                               reinterpret_cast<uint32_t*>(dst), ld_dst);
+  else if (dt == BF16)
+    k_transpose<uint16_t><<<grid, 256, 0, s>>>(reinterpret_cast<const uint16_t*>(src), ld_src, rows, cols,
+                                               reinterpret_cast<uint16_t*>(dst), ld_dst);
+  else
+    k_transpose<uint8_t><<<grid, 256, 0, s>>>(reinterpret_cast<const uint8_t*>(src), ld_src, rows, cols,
+                                              reinterpret_cast<uint8_t*>(dst), ld_dst);
+  return hipGetLastError();
 }
 
 hipError_t inverse_perm(const int32_t* perm, int d, int32_t* inv, hipStream_t s) {

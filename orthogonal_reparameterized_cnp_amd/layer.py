@@ -74,6 +74,13 @@ class PoetxLinear:
         es = {"f32": 4, "bf16": 2, "i8": 1}[self.w]
         return self.Wt[: self.m * ldw * es].view(_TORCH_DT[self.w]).view(self.m, ldw)
 
+    def weight_t(self) -> torch.Tensor:
+        """View of the transposed copy [n][lead(m)] that bf16 weights keep after the values."""
+        if self.w != "bf16":
+            raise ValueError("only bf16 weights keep a transposed copy")
+        off = (self.m * lead(self.n) * 2 + 255) // 256 * 256
+        return self.Wt[off : off + self.n * lead(self.m) * 2].view(torch.bfloat16).view(self.n, lead(self.m))
+
     def weight_scales(self) -> torch.Tensor:
         ldw = lead(self.n)
         off = (self.m * ldw + 255) // 256 * 256

@@ -34,6 +34,9 @@ def test_host_helpers(L):
     d = B.desc(1024, 5461, 256, "bf16", "i8")
     ldw = 5504
     assert B.poetx_weight_bytes(d) == (1024 * ldw + 255) // 256 * 256 + 4 * ldw
+    # bf16: values, then at a 256-byte boundary the transposed copy [n][lead(m)]
+    assert B.poetx_weight_bytes(B.desc(1000, 5461, 256, "bf16", "bf16")) == (1000 * ldw * 2 + 255) // 256 * 256 + 5461 * 1024 * 2
+    assert B.poetx_weight_bytes(B.desc(1000, 100, 32, "f32", "f32")) == 1000 * 128 * 4
     # saved state: H [T][lead(n)], then at a 256-byte boundary Xt [T][lead(m)]
     assert B.poetx_saved_bytes(d, 10) == (10 * ldw * 2 + 255) // 256 * 256 + 10 * 1024 * 2
     for op in (B.POETX_OP_FWD, B.POETX_OP_BWD, B.POETX_OP_MERGE):

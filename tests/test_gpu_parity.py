@@ -58,6 +58,11 @@ def test_premerge_bit_exact(w, act):
     if w == "bf16":
         want = want.view(np.int16)
     np.testing.assert_array_equal(got, want)
+    if w == "bf16":
+        # the transposed copy the forward reads: exact transpose, zero past column m
+        wt = _bits(lay.weight_t())
+        np.testing.assert_array_equal(wt[:, : inp.m], want.T)
+        assert not wt[:, inp.m :].any()
     if w == "i8":
         np.testing.assert_array_equal(_bits(lay.weight_scales())[: inp.n], inp.w_scale[inp.perm_P])
 
@@ -170,6 +175,7 @@ def test_merge_reinit(m, n, b, act, w, std):
         np.testing.assert_array_equal(vals, Wq)
     elif w == "bf16":
         np.testing.assert_array_equal(vals.view(np.uint16), O.round_bf16(Wq.astype(np.float64)))
+        np.testing.assert_array_equal(_bits(lay.weight_t())[:, :m], vals.T)
     else:
         code, scale = O.quantize_int8_f32(Wq)
         np.testing.assert_array_equal(vals, code)
