@@ -343,8 +343,9 @@ __global__ __launch_bounds__(C::NT * G) void k_block_grads(SideTable sd, GradSid
 }
 
 // Block gradients of large blocks (b a multiple of 256), split over tokens:
-// workgroup (tile, block, s) sums rows [s * rows / S, (s + 1) * rows / S) of
-// its 256 x 256 tile and writes the fp32 partial to part[s][block].  Big tiles
+// workgroup (tile, block, s) sums the rows of 64-row K tiles
+// [s * KT / S, (s + 1) * KT / S) (KT = rows / 64; S = 1 takes all rows) of its
+// 256 x 256 tile and writes the fp32 partial to part[s][block].  Big tiles
 // give each K step enough MFMA work to cover its loads, and the token split
 // gives the grid enough workgroups; k_block_grads_reduce then adds the S
 // partials in split order.
@@ -360,8 +361,13 @@ __global__ __launch_bounds__(C::NT) void k_block_grads_part(SideTable sd, GradSi
   const int tiles_n = (b + C::BN - 1) / C::BN;
   const int m0 = (blockIdx.x / tiles_n) * C::BM, n0 = (blockIdx.x % tiles_n) * C::BN;
   if (m0 >= r || n0 >= r) return;  // only the live corner is read later
-  const int per = rows / S;
-  const int64_t t0 = (int64_t)sp * per;
+  int64_t t0 = 0;
+  int per = rows;
+  if (S > 1) {  // rows is a multiple of 64 (checked by the launcher)
+    const int KT = rows / 64, k0 = (int)((int64_t)sp * KT / S), k1 = (int)((int64_t)(sp + 1) * KT / S);
+    t0 = (int64_t)k0 * 64;
+    per = (k1 - k0) * 64;
+  }
   LoadMN<C::BM, C::BK, C::NT, T, T> la;
   la.init(gs.A[s] + t0 * gs.lda[s] + kb + m0, gs.lda[s], r - m0, per);
   LoadMN<C::BN, C::BK, C::NT, T, T> lb;
@@ -686,13 +692,28 @@ hipError_t cnp_build_batch(int dt, int count, const float* const* q, const int* 
 }
 
 int block_grads_splits(int dt, int rows, int blocks, int b) {
-  // bf16 blocks of a multiple of 256: 256 x 256 tiles, token splits (powers of
-  // two up to 8, each a multiple of 64 rows) until the grid has 512 workgroups
+  // bf16 blocks of a multiple of 256: 256 x 256 tiles, one workgroup per CU
+  // at a time.  The token range is cut into S splits of whole 64-row K tiles;
+  // S minimises rounds * K tiles per workgroup (rounds = workgroups / CUs,
+  // rounded up) plus the cost of writing and re-reading the S partials
+  // (about 0.2 K-tile times per 512 x 512 fp32 block and split).
   if (dt != BF16 || b % 256 != 0 || rows <= 0) return 0;
+  if (rows % 64 != 0) return 1;
+  constexpr int kCUs = 256;
   const int64_t tiles = (int64_t)(b / 256) * (b / 256) * blocks;
-  int S = 1;
-  while (S < 8 && tiles * S < 512 && rows % (2 * S * 64) == 0) S *= 2;
-  return S;
+  const int KT = rows / 64;
+  const double per_split = 0.2 * blocks * ((double)b / 512) * ((double)b / 512);
+  int best = 1;
+  double best_cost = 0;
+  for (int S = 1; S <= 16 && S <= KT; ++S) {
+    const int64_t rounds = (tiles * S + kCUs - 1) / kCUs;
+    const double cost = (double)rounds * ((KT + S - 1) / S) + per_split * S;
+    if (S == 1 || cost < best_cost) {
+      best = S;
+      best_cost = cost;
+    }
+  }
+  return best;
 }
 
 size_t block_grads_part_bytes(int dt, int rows, int blocks, int b) {

@@ -51,9 +51,12 @@ CASES = [
     ("f32", 32, [(96, 50), (33, 64)], 70, True),
     ("bf16", 512, [(1024, 1536), (600, 520)], 256, True),
     ("bf16", 512, [(4096, 1024), (4096, 4096), (14336, 4096)], 1024, False),
-    # token-split block gradients: ragged T (one split), T = 3 * 128 (two splits), partial blocks
+    # token-split block gradients: ragged T (one split), T = 6 * 64 (six splits of one K tile),
+    # 11 and 5 K tiles over 6 and 3 splits (uneven), partial blocks
     ("bf16", 256, [(600, 520), (256, 300)], 300, True),
     ("bf16", 256, [(700, 256)], 384, True),
+    ("bf16", 256, [(700, 256)], 704, True),
+    ("bf16", 512, [(1024, 512)], 320, True),
 ]
 
 
