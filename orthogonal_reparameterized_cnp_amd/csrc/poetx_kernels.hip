@@ -536,8 +536,12 @@ static hipError_t apply_t(const void* in, int64_t ld_in, int rows, int d, int b,
 hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, int d, int b, int dT_dt, const void* dT,
                  const float* colscale, int out_dt, void* out, int64_t ld_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (cdt == BF16 && in_dt == BF16 && dT_dt == BF16 && out_dt == BF16)
-    return apply_t<DGemm, TGemm, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+  if (cdt == BF16 && in_dt == BF16 && dT_dt == BF16 && out_dt == BF16) {
+    // 256 x 256 tiles when they give every CU a workgroup, else 128 x 128 tiles (two per CU)
+    if ((int64_t)cdiv(rows, 256) * cdiv(b, 256) * nblocks(d, b) >= 256)
+      return apply_t<DGemm, TGemm, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+    return apply_t<DSq, TSq, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+  }
   if (cdt == F32 && in_dt == F32 && dT_dt == F32 && out_dt == F32)
     return apply_t<void, TF, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
   // merge products: fp32 rows times the stored blocks
