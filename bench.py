@@ -362,7 +362,7 @@ def main():
         "mfma_peak_frac": total_f / (ms * 1e-3) / 1e12 / peak,
         "step_tflop": {"w_contractions": gemm_f / 1e12, "block_products": apply_f / 1e12, "cnp": cnp_f / 1e12},
         "roofline": {
-            "kernel": "W~ contractions (k_gemm, forward NN-with-transpose and backward NT)",
+            "kernel": "W~ contractions (k_gemm: forward against the stored W~^T and backward, both NT)",
             "bound": "mfma",
             "achieved": achieved,
             "peak": peak,
