@@ -33,6 +33,7 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "POET-X linear fwd+bwd tokens/s at Llama-8B shapes; % MFMA peak (1 GPU)"
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "llama8b_gemm_traffic.md")
+CLASSES_MD = os.path.join(ROOT, "profiles", "llama8b_kernel_classes.md")
 COPY_PROBE_BYTES = 256 << 20  # device-to-device copy of known size, the counters' calibration
 
 
@@ -168,6 +169,107 @@ traffic-json: {json.dumps(line)}
     print(txt)
 
 
+KERNEL_CLASSES = (  # kernel-name prefix -> class, as in --breakdown
+    ("k_gemm<", "W~ contractions"),
+    ("k_apply<", "block products"),
+    ("k_block_grads", "block gradients"),
+    ("k_cnp_", "CNP products"),
+    ("k_unpack_q", "CNP pack/unpack"),
+    ("k_pack_dq", "CNP pack/unpack"),
+    ("k_permute", "permutations"),
+    ("k_inverse_perm", "permutations"),
+)
+N_XCC = 8  # GRBM_GUI_ACTIVE is reported once per XCD; the counter CSV holds their sum
+
+
+def kernel_class(name):
+    for prefix, cls in KERNEL_CLASSES:
+        if prefix in name:
+            return cls
+    return None
+
+
+def read_counter_rows(d):
+    """{dispatch id: {"name", "ns", counter: value}} from a rocprofv3 --pmc output directory."""
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    out = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                e = out.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                          "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def summarize_classes(mfma_dir, fetch_dir, write_dir, cmds):
+    """Per kernel class of one bench step: MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over all SIMDs and
+    the XCDs' busy cycles) and copy-calibrated HBM bytes and rates (FETCH_SIZE, WRITE_SIZE)."""
+    n_simd = 256 * 4
+    rows = {k: read_counter_rows(d) for k, d in (("mfma", mfma_dir), ("fetch", fetch_dir), ("write", write_dir))}
+    scale = {}
+    for key in ("fetch", "write"):
+        r = rows[key]
+        first_step = min((i for i, e in r.items() if "k_unpack_q" in e["name"]), default=None)
+        copies = [(i, e) for i, e in sorted(r.items()) if "copyBuffer" in e["name"] and first_step and i < first_step]
+        ctr = "FETCH_SIZE" if key == "fetch" else "WRITE_SIZE"
+        if not copies:
+            raise SystemExit(f"{key}: copy probe missing")
+        scale[key] = COPY_PROBE_BYTES / (copies[-1][1][ctr] * 1024)
+    cls = {}
+    for key, ctr in (("mfma", None), ("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        for i, e in rows[key].items():
+            c = kernel_class(e["name"])
+            if c is None:
+                continue
+            a = cls.setdefault(c, {"n": 0, "ns_mfma": 0, "busy": 0.0, "gui": 0.0, "ns_fetch": 0, "fetch": 0.0,
+                                   "ns_write": 0, "write": 0.0})
+            if key == "mfma":
+                a["n"] += 1
+                a["ns_mfma"] += e["ns"]
+                a["busy"] += e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+                a["gui"] += e.get("GRBM_GUI_ACTIVE", 0.0)
+            else:
+                a["ns_" + key] += e["ns"]
+                a[key] += e[ctr] * 1024 * scale[key]
+    lines = []
+    for c in dict.fromkeys(c for _, c in KERNEL_CLASSES):
+        a = cls.get(c)
+        if not a:
+            continue
+        busy = a["busy"] / (a["gui"] / N_XCC * n_simd) if a["gui"] else 0.0
+        gbs = lambda k: a[k] / (a["ns_" + k] * 1e-9) / 1e9 if a["ns_" + k] else 0.0
+        lines.append(f"| {c} | {a['n']} | {a['ns_mfma'] / 1e6:.3f} | {100 * busy:.1f}% | {a['fetch'] / 1e9:.3f} | "
+                     f"{a['write'] / 1e9:.3f} | {gbs('fetch') + gbs('write'):.0f} |")
+    txt = f"""# One bench step by kernel class: MFMA busy and HBM traffic (rocprofv3 counters)
+
+Workload: one step of bench.py's default (7 POET-X linears of a Llama-8B decoder layer, T = 8192, b = 512,
+bf16), warm-up 0; the FETCH_SIZE and WRITE_SIZE runs add a {COPY_PROBE_BYTES >> 20} MiB device copy as calibration.
+
+Commands (from the repository root on one MI355X, one counter set per run):
+
+    {cmds[0]}
+    {cmds[1]}
+    {cmds[2]}
+    python bench.py --summarize-classes gpurun_out/pmc_mfma gpurun_out/pmc_fetch gpurun_out/pmc_write
+
+- MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES summed over all {n_simd} SIMDs / ({n_simd} x the XCDs' busy cycles, GRBM_GUI_ACTIVE
+  summed over {N_XCC} XCDs / {N_XCC}). It counts cycles with the matrix pipe occupied, at the clock the chip ran.
+- Bytes between the L2s and memory (HBM or the Infinity Cache; the counters do not tell them apart):
+  FETCH_SIZE x{scale['fetch']:.3f} and WRITE_SIZE x{scale['write']:.3f} (the factors that map each counter's
+  reading for the copy probe to its true bytes); rates divide by the same run's kernel durations.
+- Durations are those of the counter run (the profiler serialises dispatches), not the bench timing.
+
+| class | launches | ms | MFMA busy | GB fetched | GB written | GB/s (fetch + write) |
+|---|---|---|---|---|---|---|
+""" + "\n".join(lines) + "\n"
+    with open(CLASSES_MD, "w") as fh:
+        fh.write(txt)
+    print(txt)
+
+
 def committed_traffic():
     """Per-launch HBM bytes of the W~ contractions from the committed counter summary, or None when the
     summary is missing or the kernel sources changed since it was taken."""
@@ -246,6 +348,8 @@ def main():
                          "report it amortised over the workload's merge period")
     ap.add_argument("--copy-probe", action="store_true",
                     help=f"run a {COPY_PROBE_BYTES >> 20} MiB device copy before the steps (counter calibration)")
+    ap.add_argument("--summarize-classes", nargs=3, metavar=("MFMA_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write the per-kernel-class counter summary from three rocprofv3 --pmc runs")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the k_gemm traffic summary from two rocprofv3 --pmc runs and exit (no GPU)")
     args = ap.parse_args()
@@ -254,6 +358,13 @@ def main():
         summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
                           base.format(c="FETCH_SIZE", d=args.summarize_traffic[0]),
                           base.format(c="WRITE_SIZE", d=args.summarize_traffic[1]))
+        return
+    if args.summarize_classes:
+        m, f, w = args.summarize_classes
+        base = "rocprofv3 --pmc {c} --output-format csv -d {d} -o llama8b -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline"
+        summarize_classes(m, f, w, (base.format(c="SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE", d=m),
+                                    base.format(c="FETCH_SIZE", d=f) + " --copy-probe",
+                                    base.format(c="WRITE_SIZE", d=w) + " --copy-probe"))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)

@@ -49,6 +49,17 @@ struct SideTable {
   }
 };
 
+// Workgroups are dealt to the 8 XCDs round robin by launch index, so
+// consecutive indices land on different L2s.  The product kernels remap the
+// launch index to a unit number that gives each XCD a contiguous range of
+// units (the first units % 8 XCDs one more); units run tile-fastest within a
+// block, so the tiles that share a block's operand panels run together on one
+// XCD and fetch those panels into its L2 once.
+PX_DEV int xcd_unit(int id, int units) {
+  const int x = id % 8, k = id / 8, q = units / 8, r = units % 8;
+  return x * q + min(x, r) + k;
+}
+
 // K loop over two K-contiguous bf16/fp32 operand tiles (row pitch b): the
 // direct-to-LDS loop for interior bf16 tiles, else the checked register loop.
 template <class C, typename T, class Epi>
@@ -168,11 +179,12 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
                                                       float* __restrict__ Q32, T* __restrict__ Sb,
                                                       T* __restrict__ Ntb) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int z = blockIdx.z;
+  const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM;
+  const int u = xcd_unit(blockIdx.x, gridDim.x), z = u / (tm * tn);
   const float* qk;
   int r;
   sd.at(z, b, qk, r);
-  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
+  const int m0 = (u % (tm * tn) / tn) * C::BM, n0 = (u % tn) * C::BN;
   if (m0 >= r || n0 >= r) return;  // nothing outside the live corner is read later
   const int64_t off = (int64_t)z * b * b;
   run_kk<C, T>(smem, Qb + off + (int64_t)m0 * b, r - m0, Qb + off + (int64_t)n0 * b, r - n0, b, r, [&](auto& acc) {
@@ -210,11 +222,12 @@ template <class C, typename T>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_delta(SideTable sd, int b, const float* __restrict__ T2,
                                                      const T* __restrict__ Sb, const T* __restrict__ Ntb, GOut go) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int z = blockIdx.z;
+  const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM;
+  const int u = xcd_unit(blockIdx.x, gridDim.x), z = u / (tm * tn);
   const float* qk;
   int side, blk, r;
   sd.at(z, b, side, blk, r, qk);
-  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
+  const int m0 = (u % (tm * tn) / tn) * C::BM, n0 = (u % tn) * C::BN;
   const int64_t off = (int64_t)z * b * b;
   const int64_t nb_s = sd.first[side + 1] - sd.first[side];
   T* g0 = reinterpret_cast<T*>(go.g[side]) + (int64_t)blk * b * b;
@@ -281,13 +294,14 @@ __global__ __launch_bounds__(C::NT * G) void k_block_grads(SideTable sd, GradSid
   extern __shared__ __align__(16) unsigned char smem[];
   const int grp = G == 1 ? 0 : (int)(threadIdx.x / C::NT);
   T* lds = reinterpret_cast<T*>(smem + grp * Lay<C, T>::BYTES);
-  const int zl = blockIdx.y;  // block of this linear; zoff + zl is its place in the gradient arrays
+  const int tiles_n = (b + C::BN - 1) / C::BN, tiles = tiles_n * ((b + C::BM - 1) / C::BM);
+  const int u = xcd_unit(blockIdx.x, gridDim.x);
+  const int zl = u / tiles;  // block of this linear; zoff + zl is its place in the gradient arrays
   int s, blk, r;
   const float* qk;
   sd.at(zl, b, s, blk, r, qk);
   const int kb = blk * b;
-  const int tiles_n = (b + C::BN - 1) / C::BN;
-  const int m0 = (blockIdx.x / tiles_n) * C::BM, n0 = (blockIdx.x % tiles_n) * C::BN;
+  const int m0 = (u % tiles / tiles_n) * C::BM, n0 = (u % tiles_n) * C::BN;
   if (m0 >= r || n0 >= r) return;  // only the live corner is read later
   const int per = rows / G;
   const int64_t t0 = (int64_t)grp * per;
@@ -353,13 +367,15 @@ template <class C, typename T>
 __global__ __launch_bounds__(C::NT) void k_block_grads_part(SideTable sd, GradSides<T> gs, int rows, int b, int S,
                                                             float* __restrict__ part) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int zl = blockIdx.y, sp = blockIdx.z;
+  // units: tile fastest, then split, then block
+  const int tiles_n = (b + C::BN - 1) / C::BN, tiles = tiles_n * ((b + C::BM - 1) / C::BM);
+  const int u = xcd_unit(blockIdx.x, gridDim.x);
+  const int sp = u / tiles % S, zl = u / tiles / S, NB = sd.first[sd.count];
   int s, blk, r;
   const float* qk;
   sd.at(zl, b, s, blk, r, qk);
   const int kb = blk * b;
-  const int tiles_n = (b + C::BN - 1) / C::BN;
-  const int m0 = (blockIdx.x / tiles_n) * C::BM, n0 = (blockIdx.x % tiles_n) * C::BN;
+  const int m0 = (u % tiles / tiles_n) * C::BM, n0 = (u % tiles_n) * C::BN;
   if (m0 >= r || n0 >= r) return;  // only the live corner is read later
   int64_t t0 = 0;
   int per = rows;
@@ -375,7 +391,7 @@ __global__ __launch_bounds__(C::NT) void k_block_grads_part(SideTable sd, GradSi
   Acc<C> acc;
   const AccPos<C> p = acc_pos<C>();
   mainloop<C, T>(reinterpret_cast<T*>(smem), la, lb, per, acc, p.wm, p.wn, p.lane);
-  float* P = part + ((int64_t)sp * gridDim.y + zl) * b * b;
+  float* P = part + ((int64_t)sp * NB + zl) * b * b;
   each_acc<C>(acc, [&](int i, int j, float v) {
     i += m0;
     j += n0;
@@ -439,11 +455,12 @@ __global__ __launch_bounds__(256) void k_block_grads_reduce(SideTable sd, int b,
 template <class C, typename T, int STEP>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_step(SideTable sd, int b, Chain<T> ch) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int z = blockIdx.z;
+  const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM;
+  const int u = xcd_unit(blockIdx.x, gridDim.x), z = u / (tm * tn);
   const float* qk;
   int r;
   sd.at(z, b, qk, r);
-  const int m0 = blockIdx.y * C::BM, n0 = blockIdx.x * C::BN;
+  const int m0 = (u % (tm * tn) / tn) * C::BM, n0 = (u % tn) * C::BN;
   if (m0 >= r || n0 >= r) return;  // later steps and the packing read only the live corner
   const int64_t off = (int64_t)z * b * b;
   const T* X = STEP == 1 ? ch.Ub : STEP == 2 ? ch.V1b : ch.V2b;
@@ -562,7 +579,7 @@ hipError_t build_t(const SideTable& sd, int b, const GOut& go, void* ws, hipStre
   if (e != hipSuccess) return e;
   const unsigned t64 = cdiv(b, 64);
   k_unpack_q<T><<<dim3(t64 * t64, nb), 256, 0, s>>>(sd, b, Qb, Q32);
-  dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), nb);
+  const unsigned grid = cdiv(b, C::BN) * cdiv(b, C::BM) * nb;
   k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(sd, b, Qb, Q32, Sb, Ntb);
   k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(sd, b, Q32, Sb, Ntb, go);
   return hipGetLastError();
@@ -623,13 +640,12 @@ hipError_t grads_t(const pxk::CnpSide* sides, int rows, int b, void* dg, int64_t
     constexpr int lds = Lay<CB, T>::BYTES;
     e = allow_lds(k_block_grads_part<CB, T>, lds);
     if (e != hipSuccess) return e;
-    k_block_grads_part<CB, T><<<dim3(cdiv(b, CB::BM) * cdiv(b, CB::BN), NB, S), CB::NT, lds, s>>>(sd, gs, rows, b, S,
-                                                                                                 part);
+    k_block_grads_part<CB, T><<<cdiv(b, CB::BM) * cdiv(b, CB::BN) * NB * S, CB::NT, lds, s>>>(sd, gs, rows, b, S, part);
     const unsigned t64 = cdiv(b, 64);
     k_block_grads_reduce<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, S, part, ch, zoff);
     return hipGetLastError();
   }
-  dim3 grid(cdiv(b, C::BM) * cdiv(b, C::BN), NB);
+  const unsigned grid = cdiv(b, C::BM) * cdiv(b, C::BN) * NB;
   if (rows % (2 * C::BK) == 0) {
     // two groups per tile, each over half of the tokens
     constexpr int lds = std::max(2 * Lay<C, T>::BYTES, C::BM * (C::BN + 4) * 4);
@@ -654,7 +670,7 @@ hipError_t chain_t(const SideTable& sd, int b, void* dg, const DqOut& out, hipSt
   k_unpack_q<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb), nullptr);
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = hipSuccess;
-  const dim3 grid(cdiv(b, C::BN), cdiv(b, C::BM), NB);
+  const unsigned grid = cdiv(b, C::BN) * cdiv(b, C::BM) * NB;
 #define PX_STEP(K)                                   \
   e = allow_lds(k_cnp_step<C, T, K>, lds);            \
   if (e != hipSuccess) return e;                      \
