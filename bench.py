@@ -343,6 +343,8 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="per kernel class timings on stderr")
+    ap.add_argument("--mode", choices=("xfast", "xmem"), default="xfast",
+                    help="xfast saves H for the backward; xmem saves only the gathered input and recomputes H")
     ap.add_argument("--merge", metavar="WORKLOAD", nargs="?", const="llama13b_int8", default=None,
                     help="also time poetx_merge_reinit of every linear of WORKLOAD (default llama13b_int8) and "
                          "report it amortised over the workload's merge period")
@@ -390,7 +392,7 @@ def main():
     layers, Xs, dZs, inputs0 = [], [], [], None
     for i in range(len(wl.linears)):
         inp = make_linear_inputs(wl, i)
-        lay = PoetxLinear(inp.m, inp.n, inp.b, inp.act, inp.w)
+        lay = PoetxLinear(inp.m, inp.n, inp.b, inp.act, inp.w, mode=args.mode)
         scale = to_dev(inp.w_scale, "f32") if inp.w == "i8" else None
         lay.load(to_dev(inp.W0, inp.w), scale, to_dev(inp.perm_R, "i32"), to_dev(inp.perm_P, "i32"),
                  to_dev(inp.q_R, "f32"), to_dev(inp.q_P, "f32"))
@@ -468,6 +470,7 @@ def main():
             "tokens": T,
             "b": wl.b,
             "weights": wl.w,
+            "mode": args.mode,
         },
         "tflops": total_f / (ms * 1e-3) / 1e12,
         "mfma_peak_frac": total_f / (ms * 1e-3) / 1e12 / peak,

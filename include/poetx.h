@@ -62,6 +62,16 @@ typedef enum {
 
 typedef enum { POETX_F32 = 0, POETX_BF16 = 1, POETX_I8 = 2 } poetx_dtype;
 
+/*
+ * Activation saving (gist.science summary, 4. Resultados: the POET-Xfast and
+ * POET-Xmem variants).  POETX_XFAST saves H = Xt Diag(G_R) W~ and the gathered
+ * input Xt.  POETX_XMEM saves Xt only; the backward recomputes H from it with
+ * the forward's own kernels (one more block product and W~ contraction), so its
+ * results are bit-identical to POETX_XFAST while the saved state shrinks by
+ * T x round_up(n, 64) activations.
+ */
+typedef enum { POETX_XFAST = 0, POETX_XMEM = 1 } poetx_mode;
+
 /* Operation selector for poetx_workspace_size. */
 typedef enum { POETX_OP_CNP = 0, POETX_OP_FWD = 1, POETX_OP_BWD = 2, POETX_OP_MERGE = 3 } poetx_op;
 
@@ -80,6 +90,7 @@ typedef struct {
   int32_t b;
   int32_t act_dtype;
   int32_t w_dtype;
+  int32_t mode; /* poetx_mode: what the forward saves for the backward */
 } poetx_layer_desc;
 
 /* ---------------------------------------------------------------- helpers -- */
@@ -107,11 +118,12 @@ size_t poetx_g_bytes(int32_t d, int32_t b, int32_t dtype);
  * poetx_premerge and poetx_merge_reinit write every part. */
 size_t poetx_weight_bytes(const poetx_layer_desc* desc);
 
-/* Bytes of the state the forward saves for the backward of the same T tokens:
- * H = Xt Diag(G_R) W~ as [T][round_up(n, 64)] elements of act_dtype, then, at
- * the next 256-byte boundary, the gathered input Xt = X[:, perm_R] as
- * [T][round_up(m, 64)].  The backward reads Xt from here instead of gathering X
- * again, so a caller need not keep X for the backward. */
+/* Bytes of the state the forward saves for the backward of the same T tokens.
+ * POETX_XFAST: H = Xt Diag(G_R) W~ as [T][round_up(n, 64)] elements of
+ * act_dtype, then, at the next 256-byte boundary, the gathered input
+ * Xt = X[:, perm_R] as [T][round_up(m, 64)].  POETX_XMEM: Xt only, at offset 0.
+ * The backward reads Xt from here instead of gathering X again, so a caller
+ * need not keep X for the backward. */
 size_t poetx_saved_bytes(const poetx_layer_desc* desc, int64_t T);
 
 /* Workspace bytes for `op` (POETX_OP_CNP uses desc->m as the side length d and
@@ -182,7 +194,8 @@ poetx_status poetx_premerge(const poetx_layer_desc* desc, const void* W0, int64_
  *   Wt     pre-merged weight (poetx_premerge / poetx_merge_reinit layout)
  *   g_R, g_P  G buffers from poetx_cnp_build for the two sides
  *   Y      out [T][n] act_dtype, leading dimension n
- *   H_save out, poetx_saved_bytes(desc, T) bytes: the saved state (H, then Xt)
+ *   H_save out, poetx_saved_bytes(desc, T) bytes: the saved state (H, then Xt;
+ *          Xt only for POETX_XMEM)
  *          read by poetx_linear_bwd
  *   ws     >= poetx_workspace_size(desc, T, POETX_OP_FWD)
  * T = 0 is a valid no-op.

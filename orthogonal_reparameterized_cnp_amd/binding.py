@@ -27,6 +27,8 @@ POETX_OP_CNP, POETX_OP_FWD, POETX_OP_BWD, POETX_OP_MERGE = 0, 1, 2, 3
 POETX_KC_NONE, POETX_KC_GEMM, POETX_KC_APPLY, POETX_KC_DGRAD, POETX_KC_CNP, POETX_KC_PERMUTE = range(6)
 
 DTYPES = {"f32": POETX_F32, "bf16": POETX_BF16, "i8": POETX_I8}
+POETX_XFAST, POETX_XMEM = 0, 1  # what the forward saves: H and Xt, or Xt only (H recomputed)
+MODES = {"xfast": POETX_XFAST, "xmem": POETX_XMEM}
 
 
 class PoetxError(RuntimeError):
@@ -42,6 +44,7 @@ class LayerDesc(ctypes.Structure):
         ("b", ctypes.c_int32),
         ("act_dtype", ctypes.c_int32),
         ("w_dtype", ctypes.c_int32),
+        ("mode", ctypes.c_int32),
     ]
 
 
@@ -146,8 +149,8 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def desc(m: int, n: int, b: int, act: str, w: str) -> LayerDesc:
-    return LayerDesc(m, n, b, DTYPES[act], DTYPES[w])
+def desc(m: int, n: int, b: int, act: str, w: str, mode: str = "xfast") -> LayerDesc:
+    return LayerDesc(m, n, b, DTYPES[act], DTYPES[w], MODES[mode])
 
 
 # ---------------------------------------------------------------- helpers ---

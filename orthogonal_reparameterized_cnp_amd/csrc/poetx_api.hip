@@ -92,6 +92,7 @@ poetx_status check_desc(const poetx_layer_desc* d) {
   if (d->b < 2 || d->b > 1024) return fail(POETX_E_SHAPE, "b must be in [2, 1024]");
   if (nblocks(d->m, d->b) > 65535 || nblocks(d->n, d->b) > 65535)
     return fail(POETX_E_SHAPE, "at most 65535 blocks per side");
+  if (d->mode != POETX_XFAST && d->mode != POETX_XMEM) return fail(POETX_E_SHAPE, "mode must be XFAST or XMEM");
   const bool ok = (d->act_dtype == POETX_F32 && d->w_dtype == POETX_F32) ||
                   (d->act_dtype == POETX_BF16 && (d->w_dtype == POETX_BF16 || d->w_dtype == POETX_I8));
   if (!ok) return fail(POETX_E_DTYPE, "supported (act, weight) dtypes: (F32, F32), (BF16, BF16), (BF16, I8)");
@@ -131,13 +132,14 @@ bool has_weight_t(const poetx_layer_desc* d) { return d->w_dtype == POETX_BF16; 
 size_t weight_t_offset(const poetx_layer_desc* d) { return weight_scale_offset(d); }
 
 // The forward's saved state: H [T][lead(n)], then (256-byte aligned) the
-// gathered input Xt [T][lead(m)], both in act_dtype.
+// gathered input Xt [T][lead(m)], both in act_dtype; Xt alone for Xmem.
 size_t saved_xt_offset(const poetx_layer_desc* d, int64_t T) {
+  if (d->mode == POETX_XMEM) return 0;
   return (size_t)round_up(T * lead(d->n) * (int64_t)dt_size(d->act_dtype), 256);
 }
 
 struct FwdWs {
-  void *A, *Zt;
+  void *A, *Zt, *H;  // H: Xmem only (Xfast writes it to the saved state)
   int32_t* invP;
 };
 template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
@@ -146,6 +148,7 @@ template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
   w.A = p.template take<char>(T * lead(d->m) * es);
   w.Zt = p.template take<char>(T * lead(d->n) * es);
   w.invP = p.template take<int32_t>((size_t)d->n * 4);
+  w.H = d->mode == POETX_XMEM ? p.template take<char>(T * lead(d->n) * es) : nullptr;
   return w;
 }
 
@@ -366,6 +369,42 @@ poetx_status poetx_premerge(const poetx_layer_desc* desc, const void* W0, int64_
   return POETX_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// H = (Xt Diag(G_R)) W~ with A as the intermediate: the forward's first block
+// product and its W~ contraction, also used by the Xmem backward to recompute
+// H (same kernels on the same inputs, so the same bits).
+poetx_status xt_to_h(const poetx_layer_desc* desc, int64_t T, const void* Xt, const void* Wt, const void* g_R, void* A,
+                     void* H, hipStream_t s) {
+  const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, wt = desc->w_dtype;
+  const int rows = (int)T;
+  const int64_t ldm = lead(m), ldn = lead(n);
+  const char* gR1 = reinterpret_cast<const char*>(g_R) + g_slice(m, b, at);  // Delta_R^T
+  const float* scale_t =
+      wt == POETX_I8 ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(Wt) + weight_scale_offset(desc))
+                     : nullptr;
+  const double es = (double)dt_size(at), wes = (double)dt_size(wt);
+  // A = Xt Diag(G_R)
+  PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
+           apply(at, at, Xt, ldm, rows, m, b, at, gR1, nullptr, at, A, ldm, s));
+  // H = A W~ (int8: codes times the column scale); bf16 weights are read from the W~^T copy
+  if (has_weight_t(desc)) {
+    const void* Wtt = reinterpret_cast<const char*>(Wt) + weight_t_offset(desc);
+    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
+             gemm(at, at, A, ldm, wt, Wtt, ldm, false, rows, n, m, nullptr, at, H, ldn, s));
+  } else {
+    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
+             gemm(at, at, A, ldm, wt, Wt, lead(n), true, rows, n, m, scale_t, at, H, ldn, s));
+  }
+  return POETX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const void* X, const int32_t* perm_R,
                               const int32_t* perm_P, const void* Wt, const void* g_R, const void* g_P, void* Y,
                               void* H_save, void* ws, size_t ws_bytes, void* stream) {
@@ -383,33 +422,21 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
   q.base = reinterpret_cast<char*>(ws);
   const FwdWs w = plan_fwd(q, desc, T);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, wt = desc->w_dtype;
+  const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype;
   const int rows = (int)T;
   const int64_t ldm = lead(m), ldn = lead(n);
-  const char* gR1 = reinterpret_cast<const char*>(g_R) + g_slice(m, b, at);  // Delta_R^T
   const char* gP1 = reinterpret_cast<const char*>(g_P) + g_slice(n, b, at);  // Delta_P^T
-  const float* scale_t =
-      wt == POETX_I8 ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(Wt) + weight_scale_offset(desc))
-                     : nullptr;
-  const double es = (double)dt_size(at), wes = (double)dt_size(wt);
+  const double es = (double)dt_size(at);
   // Xt = X[:, perm_R], kept in the saved state for the backward
   void* Xt = reinterpret_cast<char*>(H_save) + saved_xt_offset(desc, T);
   PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, Xt, ldm, rows, m, m, s));
-  // A = Xt Diag(G_R)
-  PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
-           apply(at, at, Xt, ldm, rows, m, b, at, gR1, nullptr, at, w.A, ldm, s));
-  // H = A W~ (int8: codes times the column scale); bf16 weights are read from the W~^T copy
-  if (has_weight_t(desc)) {
-    const void* Wtt = reinterpret_cast<const char*>(Wt) + weight_t_offset(desc);
-    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
-             gemm(at, at, w.A, ldm, wt, Wtt, ldm, false, rows, n, m, nullptr, at, H_save, ldn, s));
-  } else {
-    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
-             gemm(at, at, w.A, ldm, wt, Wt, lead(n), true, rows, n, m, scale_t, at, H_save, ldn, s));
-  }
+  // A = Xt Diag(G_R), H = A W~: H saved (Xfast) or kept in the workspace (Xmem)
+  void* H = desc->mode == POETX_XMEM ? w.H : H_save;
+  st = xt_to_h(desc, T, Xt, Wt, g_R, w.A, H, s);
+  if (st != POETX_OK) return st;
   // Zt = H Diag(G_P)
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
-           apply(at, at, H_save, ldn, rows, n, b, at, gP1, nullptr, at, w.Zt, ldn, s));
+           apply(at, at, H, ldn, rows, n, b, at, gP1, nullptr, at, w.Zt, ldn, s));
   // Y[:, perm_P] = Zt, i.e. Y = Zt[:, perm_P^{-1}]
   PX_HIP(inverse_perm(perm_P, n, w.invP, s));
   PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, permute(at, w.Zt, ldn, nullptr, w.invP, Y, n, rows, n, n, s));
@@ -442,9 +469,16 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* X,
   PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * n + wes * m * n + es * rows * m,
            gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
   // block gradients of both sides over all tokens: dG_R = Xt^T dA, dG_P = H^T dZt, with Xt and H
-  // from the forward's saved state
+  // from the forward's saved state.  Xmem recomputes H from Xt, into the buffers that dH (consumed
+  // by the contraction above) and dXt (written below) occupy.
   const void* Xt = reinterpret_cast<const char*>(H_save) + saved_xt_offset(desc, T);
-  const CnpSide sides[2] = {{q_R, m, Xt, ldm, w.dA, ldm}, {q_P, n, H_save, ldn, w.dZt, ldn}};
+  const void* H = H_save;
+  if (desc->mode == POETX_XMEM) {
+    const poetx_status st = xt_to_h(desc, T, Xt, Wt, g_R, w.dXt, w.dH, s);
+    if (st != POETX_OK) return st;
+    H = w.dH;
+  }
+  const CnpSide sides[2] = {{q_R, m, Xt, ldm, w.dA, ldm}, {q_P, n, H, ldn, w.dZt, ldn}};
   PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * (sum_r2(m, b) + sum_r2(n, b)),
            2.0 * rows * (m + n) * es + (4 + 2 * es) * (sum_r2(m, b) + sum_r2(n, b)),
            block_grads(at, sides, rows, b, dg, first, total, w.part, s));

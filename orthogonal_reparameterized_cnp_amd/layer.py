@@ -20,10 +20,13 @@ def lead(d: int) -> int:
 
 
 class PoetxLinear:
-    def __init__(self, m: int, n: int, b: int, act: str = "bf16", w: str = "bf16", device: str = "cuda"):
-        self.m, self.n, self.b, self.act, self.w = m, n, b, act, w
+    def __init__(self, m: int, n: int, b: int, act: str = "bf16", w: str = "bf16", device: str = "cuda",
+                 mode: str = "xfast"):
+        """mode: "xfast" saves H for the backward, "xmem" saves only the gathered input and the
+        backward recomputes H (bit-identical results, T x n fewer saved activations)."""
+        self.m, self.n, self.b, self.act, self.w, self.mode = m, n, b, act, w, mode
         self.device = torch.device(device)
-        self.desc = B.desc(m, n, b, act, w)
+        self.desc = B.desc(m, n, b, act, w, mode)
         self.nbR, self.nbP = -(-m // b), -(-n // b)
         L = b * (b - 1) // 2
         u8 = dict(dtype=torch.uint8, device=self.device)
@@ -134,6 +137,8 @@ class PoetxLinear:
         return self.ws[: self.m * ldw * 4].view(torch.float32).view(self.m, ldw)
 
     def saved_H(self, T: int) -> torch.Tensor:
+        if self.mode != "xfast":
+            raise ValueError("only the xfast mode saves H")
         dt = _TORCH_DT[self.act]
         return self.H_save.view(dt)[: T * lead(self.n)].view(T, lead(self.n))
 

@@ -60,8 +60,8 @@ def w_natural(inp) -> torch.Tensor:
     return dev(inp.W0, inp.w)
 
 
-def make_layer(inp) -> PoetxLinear:
-    lay = PoetxLinear(inp.m, inp.n, inp.b, inp.act, inp.w)
+def make_layer(inp, mode: str = "xfast") -> PoetxLinear:
+    lay = PoetxLinear(inp.m, inp.n, inp.b, inp.act, inp.w, mode=mode)
     scale = dev(inp.w_scale, "f32") if inp.w == "i8" else None
     lay.load(w_natural(inp), scale, dev(inp.perm_R, "i32"), dev(inp.perm_P, "i32"), dev(inp.q_R, "f32"),
              dev(inp.q_P, "f32"))
@@ -69,8 +69,8 @@ def make_layer(inp) -> PoetxLinear:
     return lay
 
 
-def run_gpu(inp, backward: bool = True):
-    lay = make_layer(inp)
+def run_gpu(inp, backward: bool = True, mode: str = "xfast"):
+    lay = make_layer(inp, mode)
     X = dev(inp.X, inp.act)
     Y = lay.forward(X)
     out = {"layer": lay, "Y": Y}

@@ -42,6 +42,15 @@ def test_host_helpers(L):
     for op in (B.POETX_OP_FWD, B.POETX_OP_BWD, B.POETX_OP_MERGE):
         assert B.poetx_workspace_size(d, 100, op) > 0
     assert B.poetx_workspace_size(B.desc(1024, 5461, 1, "bf16", "bf16"), 100, B.POETX_OP_FWD) == 0
+    # Xmem: the saved state is Xt alone; the forward keeps H in its workspace instead
+    dm = B.desc(1024, 5461, 256, "bf16", "i8", "xmem")
+    assert B.poetx_saved_bytes(dm, 10) == 10 * 1024 * 2
+    assert B.poetx_workspace_size(dm, 10, B.POETX_OP_FWD) == B.poetx_workspace_size(d, 10, B.POETX_OP_FWD) + (
+        (10 * ldw * 2 + 255) // 256 * 256)
+    assert B.poetx_workspace_size(dm, 10, B.POETX_OP_BWD) == B.poetx_workspace_size(d, 10, B.POETX_OP_BWD)
+    bad = B.desc(1024, 5461, 256, "bf16", "i8")
+    bad.mode = 2
+    assert B.poetx_saved_bytes(bad, 10) == 0 and B.poetx_workspace_size(bad, 10, B.POETX_OP_FWD) == 0
 
 
 @pytest.mark.parametrize("seed,d", [(0, 1), (1, 2), (123, 1376), (2**64 - 1, 5461), (42, 14336)])

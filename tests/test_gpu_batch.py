@@ -62,10 +62,21 @@ CASES = [
 
 @pytest.mark.parametrize("act,b,shapes,T,oracle", CASES)
 def test_group_backward(act, b, shapes, T, oracle):
-    print(f"group backward act={act} b={b} shapes={shapes} T={T}", flush=True)
+    _group_case(act, b, shapes, T, oracle, "xfast")
+
+
+@pytest.mark.parametrize("act,b,shapes,T", [("bf16", 512, [(1024, 1536), (600, 520)], 256),
+                                             ("bf16", 256, [(700, 256)], 384)])
+def test_group_backward_xmem(act, b, shapes, T):
+    """Grouped Xmem linears (H recomputed in backward_dx) against per-linear Xfast calls: bit-identical."""
+    _group_case(act, b, shapes, T, False, "xmem")
+
+
+def _group_case(act, b, shapes, T, oracle, mode):
+    print(f"group backward act={act} b={b} shapes={shapes} T={T} mode={mode}", flush=True)
     inps = [custom_linear_inputs(m, n, b, T, act, act, 0.05, seed=11 * m + n) for m, n in shapes]
     single = [make_layer(inp) for inp in inps]  # per-side builds
-    grouped = [make_layer(inp) for inp in inps]
+    grouped = [make_layer(inp, mode) for inp in inps]
     group = PoetxGroup(grouped)
     group.build()  # rebuild every side's G in one batch
     torch.cuda.synchronize()

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle as O
+from orthogonal_reparameterized_cnp_amd.layer import lead
 from tests.poetx_cases import TOL, assert_close, compare_layer, dev, host, make_layer, run_gpu, run_oracle
 from workloads import WORKLOADS, make_linear_inputs
 from workloads.gen import custom_linear_inputs
@@ -117,6 +118,35 @@ def test_layer_ragged(m, n, b, T, act):
 def test_layer_int8(m, n, T):
     inp = custom_linear_inputs(m, n, 512 if m >= 1024 else 128, T, "bf16", "i8", 0.005, seed=m + n)
     compare_layer(inp, run_gpu(inp), run_oracle(inp))
+
+
+# ----------------------------------------------------------------------------
+# Xmem (H recomputed in the backward): bit-identical to Xfast
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize(
+    "m,n,b,T,act,w",
+    [(520, 1030, 256, 260, "bf16", "bf16"), (600, 520, 128, 100, "bf16", "i8"), (200, 131, 64, 77, "f32", "f32"),
+     (1024, 1536, 512, 512, "bf16", "bf16")],
+)
+def test_xmem_matches_xfast(m, n, b, T, act, w):
+    inp = custom_linear_inputs(m, n, b, T, act, w, 0.02, seed=m + n + T)
+    fast = run_gpu(inp, mode="xfast")
+    mem = run_gpu(inp, mode="xmem")
+    for k in ("Y", "dX", "dq_R", "dq_P"):
+        assert torch.equal(_bits_t(fast[k]), _bits_t(mem[k])), f"{k} differs between xfast and xmem"
+    # the xmem saved state is the gathered input alone: X[:, perm_R], bit for bit
+    lay = mem["layer"]
+    Xt = lay.H_save.view(_dt(act))[: T * lead(m)].view(T, lead(m))[:, :m]
+    want = dev(inp.X, act)[:, torch.from_numpy(inp.perm_R.astype(np.int64)).cuda()]
+    assert torch.equal(_bits_t(Xt), _bits_t(want))
+
+
+def _dt(act):
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[act]
+
+
+def _bits_t(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
 def test_empty_batch():
