@@ -49,7 +49,7 @@ struct DCfg {
 // K-contiguous tile [rows][BK]: row r, 16-byte chunk c (8 K values).
 template <int BK> PX_DEV int kmaj_chunk(int r, int c) {
   constexpr int CPR = BK / 8;                // chunks per row
-  constexpr int RPL = CPR >= 8 ? 1 : 8 / CPR;  // rows per 128-byte line
+  constexpr int RPL = 16 / CPR;  // rows per 256 bytes (the 64 four-byte LDS banks)
   return r * CPR + (c ^ ((r / RPL) % CPR));
 }
 // M/N-contiguous tile [BK][R]: K row k, 16-byte chunk c (8 columns).
@@ -71,7 +71,7 @@ PX_DEV void dma_kmaj(const bf16_t* src, int64_t ld, int k0, char* lds_tile, int 
     const int kb = j * NW + wave;
     const int r = kb * RPK + lane / CPR;
     const int phys = lane % CPR;
-    constexpr int RPL = CPR >= 8 ? 1 : 8 / CPR;
+    constexpr int RPL = 16 / CPR;
     const int c = phys ^ ((r / RPL) % CPR);
     const bf16_t* g = src + (int64_t)r * ld + k0 + 8 * c;
     __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(lds_tile + kb * 1024), 16, 0, 0);
