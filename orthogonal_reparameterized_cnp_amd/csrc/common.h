@@ -13,12 +13,22 @@ typedef float f32x4_v __attribute__((ext_vector_type(4)));
 
 PX_DEV float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// float -> bfloat16, round to nearest, ties to even (NaN kept quiet)
+// float -> bfloat16, round to nearest, ties to even: the conversion
+// instruction of gfx950 (v_cvt_pk_bf16_f32), one instruction per pair
 PX_DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+  const __bf16 h = (__bf16)f;
+  bf16_t u;
+  __builtin_memcpy(&u, &h, 2);
+  return u;
+}
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+// (a, b) -> bfloat16 pair, a in the low half
+PX_DEV uint32_t f2bf2(float a, float b) {
+  const bf16x2_v h = __builtin_convertvector((f32x2_v){a, b}, bf16x2_v);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
 }
 
 // element conversions used by the operand loaders

@@ -63,8 +63,8 @@ template <typename T> PX_DEV void store4(T* p, const float v[4]) {
   if constexpr (sizeof(T) == 2) {
     if ((reinterpret_cast<uintptr_t>(p) & 7) == 0) {
       uint2 w;
-      w.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-      w.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+      w.x = f2bf2(v[0], v[1]);
+      w.y = f2bf2(v[2], v[3]);
       *reinterpret_cast<uint2*>(p) = w;
     } else {
       for (int e = 0; e < 4; ++e) p[e] = f2bf(v[e]);

@@ -45,6 +45,25 @@ struct DCfg {
   static_assert((STAGES - 2) * L <= 63, "outstanding loads must fit the vmcnt counter");
 };
 
+// ---- raw buffer access ------------------------------------------------------
+// A resource of 64-bit base, byte size and the gfx9 format
+// word.  Reads past the size return zeros and writes past it are dropped,
+// which bounds a ragged last row tile without per-row checks.
+typedef int i32x4_v __attribute__((ext_vector_type(4)));
+PX_DEV i32x4_v buffer_rsrc(const void* base, int64_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_v r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));  // stride 0
+  r[2] = __builtin_amdgcn_readfirstlane((int)(uint32_t)min(bytes, (int64_t)0x7fffffff));
+  r[3] = 0x00020000;
+  return r;
+}
+__device__ void raw_buffer_load_lds(i32x4_v rsrc, __attribute__((address_space(3))) uint32_t* lds, int size,
+                                    int voffset, int soffset, int offset, int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+__device__ void raw_buffer_store_b128(i32x4_v data, i32x4_v rsrc, int voffset, int soffset,
+                                      int aux) __asm("llvm.amdgcn.raw.buffer.store.v4i32");
+
 // ---- layouts ---------------------------------------------------------------
 // K-contiguous tile [rows][BK]: row r, 16-byte chunk c (8 K values).
 template <int BK> PX_DEV int kmaj_chunk(int r, int c) {

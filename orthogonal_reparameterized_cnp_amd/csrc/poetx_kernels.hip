@@ -94,8 +94,8 @@ PX_DEV void apply_store_t(const Acc<CD>& acc, void* lds, const float* cs, bf16_t
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = acc.v[i][j][4 * g + e] * (cs ? cs[col + e] : 1.f);
         uint2 w;
-        w.x = (uint32_t)f2bf(o[0]) | ((uint32_t)f2bf(o[1]) << 16);
-        w.y = (uint32_t)f2bf(o[2]) | ((uint32_t)f2bf(o[3]) << 16);
+        w.x = f2bf2(o[0], o[1]);
+        w.y = f2bf2(o[2], o[3]);
         *reinterpret_cast<uint2*>(t + row * PITCH + col) = w;
       }
   __syncthreads();
@@ -154,6 +154,249 @@ __global__ __launch_bounds__(C::NT) void k_apply(const IT* __restrict__ in, int6
   const AccPos<C> p = acc_pos<C>();
   mainloop<C, T>(lds, la, lb, r, acc, p.wm, p.wn, p.lane, IdentityHook<C, PaddedElem<C, T>>{&acc, n0, {}});
   epi(acc);
+}
+
+// ============================================================================
+// block-diagonal product, streaming form (bf16, blocks of 256 or 512)
+// ============================================================================
+// A workgroup of 8 waves owns one 256-column group of one block and keeps
+// that group's slice of D^T in VGPRs for as long as it works on the block
+// (wave w: output columns 32 w .. 32 w + 31 of the group, all B K indices, as
+// B / 16 MFMA fragments).  Row tiles of RT tokens x B input columns then
+// stream through a ring of S LDS slots, so S - 1 tiles of input are in flight
+// while one is multiplied; each tile is read from HBM once, however many
+// column groups its block has, because the groups of a block run on one XCD
+// over the same tiles at the same time and share it through L2.
+// Waves 0-3 issue the tile copies and waves 4-7 the output stores, so each
+// wave's vector-memory counter holds one kind of operation and a wait for a
+// tile's copies never waits for stores.  The MFMAs take D^T as their first
+// operand (accumulators hold the transposed tile: a lane owns 4 consecutive
+// output columns of one token row), and the identity term is added by two
+// MFMAs against an identity fragment, which is exact.
+// Work: items (block, row tile) in block-major order, split into contiguous
+// ranges over "pair lanes"; the NH = B / 256 workgroups of a pair lane (one
+// per column group) sit on the same XCD and walk the same range.
+template <int B, int RT, int S> struct StreamCfg {
+  static constexpr int NW = 8, NT = 512, NH = B / 256, NKS = B / 16, NKT = B / 64;
+  static constexpr int SLOT = RT * B * 2;            // bytes of one row tile
+  static constexpr int SUB = RT * 128;               // bytes of one [RT][64] K sub-tile
+  static constexpr int PIECES = SLOT / 1024;          // 1 KB copies per tile
+  static constexpr int PPW = PIECES / 4;              // per loader wave
+  static constexpr int PITCH = 256 + 8;               // staged output row, bf16
+  static constexpr int STAGE = RT * PITCH * 2;
+  static constexpr int LDS = S * SLOT + 2 * STAGE;   // ring + two staged output tiles
+  static constexpr int TMF = RT / 32;                 // 32-row fragments per tile
+  static constexpr int SPL = RT * 32 / 256;           // 16-byte output chunks per store lane
+  static_assert(B == 256 || B == 512, "block of 256 or 512 columns");
+  static_assert(RT % 32 == 0 && PIECES % 4 == 0 && SPL == 4, "row tile of whole fragments and copies");
+  static_assert(S >= 2 && S <= 4 && 2 * PPW <= 63, "outstanding copies must fit the vmcnt counter");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+template <int B, int RT, int S, bool CS>
+__global__ __launch_bounds__(512) void k_apply_stream(const bf16_t* __restrict__ in, int64_t ld_in, int rows,
+                                                      const bf16_t* __restrict__ dT, const float* __restrict__ cs,
+                                                      bf16_t* __restrict__ out, int64_t ld_out, int items,
+                                                      int pair_lanes) {
+  using C = StreamCfg<B, RT, S>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  char* ring = reinterpret_cast<char*>(smem);
+  bf16_t* stage = reinterpret_cast<bf16_t*>(smem + S * C::SLOT);  // two tiles, by item parity
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // launch index -> (XCD, slot on it) -> (pair lane, column group)
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int pl = xcd * (pair_lanes / 8) + slot / C::NH, hc = slot % C::NH;
+  const int i0 = (int)((int64_t)pl * items / pair_lanes), i1 = (int)((int64_t)(pl + 1) * items / pair_lanes);
+  if (i0 >= i1) return;
+  const int rtiles = (rows + RT - 1) / RT;
+  const int c0 = hc * 256 + 32 * wave;  // block-local first output column of this wave
+  const bool loader = wave < 4;
+
+  // Loader lanes: byte offset of each of their 1 KB copy pieces inside a row
+  // tile (piece p = j * 4 + wave: K sub-tile p / (RT / 8), rows 8 (p % (RT / 8))
+  // + lane / 8, the 16-byte chunk chosen by the kmaj swizzle).
+  int voff[C::PPW];
+#pragma unroll
+  for (int j = 0; j < C::PPW; ++j) {
+    const int p = j * 4 + (wave & 3);
+    const int kt = p / (RT / 8), r = (p % (RT / 8)) * 8 + lane / 8;
+    const int c = (lane % 8) ^ ((r / 2) % 8);
+    voff[j] = (int)((int64_t)r * ld_in * 2) + kt * 128 + 16 * c;
+  }
+  // copy of the row tile of item `it` into ring slot `sl` (loader waves only)
+  auto issue = [&](int it, int sl) {
+    const int blk = it / rtiles, m0 = (it % rtiles) * RT;
+    const i32x4_v rs = buffer_rsrc(in + (int64_t)m0 * ld_in + (int64_t)blk * B, (int64_t)(rows - m0) * ld_in * 2);
+    char* dst = ring + sl * C::SLOT;
+#pragma unroll
+    for (int j = 0; j < C::PPW; ++j) {
+      const int p = j * 4 + wave;
+      raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(dst + (p / (RT / 8)) * C::SUB + (p % (RT / 8)) * 1024),
+                          16, voff[j], 0, 0, 0);
+    }
+  };
+  if (loader) {
+#pragma unroll
+    for (int q = 0; q < S - 1; ++q)
+      if (i0 + q < i1) issue(i0 + q, q);
+  }
+
+  // identity fragments for the two k-steps that cover this wave's columns
+  bf16x8_v idf[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    s16x8 bits;
+    const int c = c0 + (lane & 31), kl = c0 + 16 * h + 8 * (lane >> 5);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bits[e] = (short)(kl + e == c ? 0x3F80 : 0);
+    __builtin_memcpy(&idf[h], &bits, 16);
+  }
+  const int s_id = c0 / 16;
+  // store lanes: byte offsets of their 4 staged chunks (row, 8 columns) in LDS and in a row tile of the output
+  const int ts = threadIdx.x & 255;
+  uint32_t st_lds[C::SPL];
+  int st_off[C::SPL];
+#pragma unroll
+  for (int q = 0; q < C::SPL; ++q) {
+    const int ch = ts + 256 * q, row = ch / 32, col = (ch % 32) * 8;
+    st_lds[q] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)(stage + row * C::PITCH + col);  // tile 0
+    st_off[q] = (int)((int64_t)row * ld_out * 2) + col * 2;
+  }
+
+  // store lanes: staged tile `par` (written for item `it`) to the output
+  auto store_tile = [&](int par, int it) {
+    const int blk = it / rtiles, m0 = (it % rtiles) * RT;
+    const uint32_t sb = par * C::STAGE;
+    // read back in assembly, waiting for the four reads inside the block: a
+    // compiler-visible LDS read would wait for every copy in flight first
+    i32x4_v v0, v1, v2, v3;
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
+        : "v"(st_lds[0] + sb), "v"(st_lds[1] + sb), "v"(st_lds[2] + sb), "v"(st_lds[3] + sb)
+        : "memory");
+    const i32x4_v rs = buffer_rsrc(out + (int64_t)m0 * ld_out + (int64_t)blk * B + hc * 256,
+                                   (int64_t)(rows - m0) * ld_out * 2);
+    raw_buffer_store_b128(v0, rs, st_off[0], 0, 0);
+    raw_buffer_store_b128(v1, rs, st_off[1], 0, 0);
+    raw_buffer_store_b128(v2, rs, st_off[2], 0, 0);
+    raw_buffer_store_b128(v3, rs, st_off[3], 0, 0);
+  };
+
+  bf16x8_v dfr[C::NKS];
+  float scl[16];
+  int cur_blk = -1;
+  for (int it = i0; it < i1; ++it) {
+    const int blk = it / rtiles, m0 = (it % rtiles) * RT;
+    if (blk != cur_blk) {
+      cur_blk = blk;
+      const bf16_t* dp = dT + ((int64_t)blk * B + c0 + (lane & 31)) * B + 8 * (lane >> 5);
+#pragma unroll
+      for (int s = 0; s < C::NKS; ++s) dfr[s] = *reinterpret_cast<const bf16x8_v*>(dp + 16 * s);
+      if constexpr (CS) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4_v v = *reinterpret_cast<const f32x4_v*>(cs + (int64_t)blk * B + c0 + 8 * g + 4 * (lane >> 5));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) scl[4 * g + e] = v[e];
+        }
+      }
+      // wait here, once per block: left to the compiler, the wait for these
+      // registers lands before every tile's first MFMA and drains the ring
+      wait_vm<0>();
+    }
+    // tile `it` must have landed: the copies of the tiles after it may stay in flight
+    if (loader) {
+      const int ahead = min(S - 2, i1 - 1 - it);
+      if constexpr (S >= 4) {
+        if (ahead >= 2) wait_vm<2 * C::PPW>();
+        else if (ahead == 1) wait_vm<C::PPW>();
+        else wait_vm<0>();
+      } else if constexpr (S == 3) {
+        if (ahead >= 1) wait_vm<C::PPW>();
+        else wait_vm<0>();
+      } else {
+        wait_vm<0>();
+      }
+    }
+    wait_lgkm0();
+    barrier_raw();
+    if (loader && it + S - 1 < i1) issue(it + S - 1, (it - i0 + S - 1) % S);
+    // the previous item's tile, staged before the barrier, is stored while this one is multiplied
+    if (!loader && it > i0) store_tile((it - 1 - i0) & 1, it - 1);
+    const char* tile = ring + ((it - i0) % S) * C::SLOT;
+    f32x16_v acc[C::TMF];
+#pragma unroll
+    for (int i = 0; i < C::TMF; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][e] = 0.f;
+    // the fragments of a whole 64-wide K sub-tile are read while the previous
+    // sub-tile's MFMAs run
+    bf16x8_v fa[2][4][C::TMF];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < C::TMF; ++i) fa[0][q][i] = frag_kmaj<64>(tile, 32 * i, 16 * q, lane);
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt) {
+      if (kt + 1 < C::NKT) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int i = 0; i < C::TMF; ++i)
+            fa[(kt + 1) & 1][q][i] = frag_kmaj<64>(tile + (kt + 1) * C::SUB, 32 * i, 16 * q, lane);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < C::TMF; ++i)
+          acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dfr[4 * kt + q], fa[kt & 1][q][i], acc[i], 0, 0, 0);
+    }
+    // keep that order: left alone, the scheduler reads each fragment just
+    // before its MFMA and every MFMA waits out an LDS round trip
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * C::TMF, 0);  // LDS reads of sub-tile 0
+#pragma unroll
+    for (int kt = 0; kt < C::NKT; ++kt) {
+      if (kt + 1 < C::NKT) __builtin_amdgcn_sched_group_barrier(0x100, 4 * C::TMF, 0);  // reads of kt + 1
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * C::TMF, 0);                       // MFMAs of kt
+    }
+    // identity term: the input fragments of k-steps s_id and s_id + 1 once more
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int sh = s_id + h;
+#pragma unroll
+      for (int i = 0; i < C::TMF; ++i) {
+        const bf16x8_v a = frag_kmaj<64>(tile + (sh / 4) * C::SUB, 32 * i, (sh % 4) * 16, lane);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(idf[h], a, acc[i], 0, 0, 0);
+      }
+    }
+    // stage the tile (lane: token row 32 i + lane % 32, columns 32 w + 8 g + 4 (lane / 32) + 0..3)
+#pragma unroll
+    for (int i = 0; i < C::TMF; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = CS ? acc[i][4 * g + e] * scl[4 * g + e] : acc[i][4 * g + e];
+        const uint64_t w = (uint64_t)f2bf2(o[0], o[1]) | ((uint64_t)f2bf2(o[2], o[3]) << 32);
+        // written as inline assembly: the compiler cannot tell that the staging
+        // area is disjoint from the ring slots that copies are still filling,
+        // and would otherwise wait for every copy in flight before the write
+        const int row = 32 * i + (lane & 31), col = 32 * wave + 8 * g + 4 * (lane >> 5);
+        const uint32_t a = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)(stage + row * C::PITCH + col) +
+                           ((it - i0) & 1) * C::STAGE;
+        asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(w) : "memory");
+      }
+  }
+  // the last item's tile
+  wait_lgkm0();
+  barrier_raw();
+  if (!loader) store_tile((i1 - 1 - i0) & 1, i1 - 1);
 }
 
 // ============================================================================
@@ -533,15 +776,61 @@ static hipError_t apply_t(const void* in, int64_t ld_in, int rows, int d, int b,
   return hipGetLastError();
 }
 
+// bf16 block products on output tiles: 256 x 256 tiles when they give every
+// CU a workgroup, else 128 x 128 tiles (two per CU)
+static hipError_t apply_bf16_tiled(const void* in, int64_t ld_in, int rows, int d, int b, const void* dT,
+                                   const float* cs, void* out, int64_t ld_out, hipStream_t s) {
+  if ((int64_t)cdiv(rows, 256) * cdiv(b, 256) * nblocks(d, b) >= 256)
+    return apply_t<DGemm, TGemm, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, cs, out, ld_out, s);
+  return apply_t<DSq, TSq, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, cs, out, ld_out, s);
+}
+
+template <int B, int RT, int S>
+static hipError_t apply_stream_t(const void* in, int64_t ld_in, int rows, int nbf, const void* dT, const float* cs,
+                                 void* out, int64_t ld_out, hipStream_t s) {
+  using C = StreamCfg<B, RT, S>;
+  auto k = cs ? k_apply_stream<B, RT, S, true> : k_apply_stream<B, RT, S, false>;
+  hipError_t e = allow_lds(k, C::LDS);
+  if (e != hipSuccess) return e;
+  const int64_t items = (int64_t)nbf * cdiv(rows, RT);
+  // one workgroup per CU; pair lanes come in multiples of 8 (one share per XCD)
+  const int pair_lanes = (int)(std::min<int64_t>(256 / C::NH, items) / 8 * 8);
+  if (pair_lanes < 8 || items > INT32_MAX) return hipErrorInvalidValue;
+  k<<<pair_lanes * C::NH, C::NT, C::LDS, s>>>(reinterpret_cast<const bf16_t*>(in), ld_in, rows,
+                                                reinterpret_cast<const bf16_t*>(dT), cs, reinterpret_cast<bf16_t*>(out),
+                                                ld_out, (int)items, pair_lanes);
+  return hipGetLastError();
+}
+
+static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// bf16 block products: the streaming kernel for the whole blocks of 256 or 512
+// columns when there are enough row tiles to occupy the chip, the tiled kernel
+// for the rest (other block sizes, a partial last block, small inputs)
+static hipError_t apply_bf16(const void* in, int64_t ld_in, int rows, int d, int b, const void* dT, const float* cs,
+                             void* out, int64_t ld_out, hipStream_t s) {
+  const int nbf = d / b;
+  constexpr int RT = 32;
+  // (the kernel addresses a row tile with 32-bit byte offsets)
+  if ((b == 256 || b == 512) && nbf > 0 && (int64_t)nbf * cdiv(rows, RT) >= 64 && ld_in % 8 == 0 &&
+      ld_out % 8 == 0 && ld_in < (1 << 25) && ld_out < (1 << 25) && aligned16(in) && aligned16(out) &&
+      aligned16(dT) && (!cs || aligned16(cs))) {
+    hipError_t e = b == 512 ? apply_stream_t<512, RT, 3>(in, ld_in, rows, nbf, dT, cs, out, ld_out, s)
+                            : apply_stream_t<256, RT, 4>(in, ld_in, rows, nbf, dT, cs, out, ld_out, s);
+    if (e != hipSuccess || nbf * b == d) return e;
+    const int64_t kb = (int64_t)nbf * b;
+    return apply_bf16_tiled(reinterpret_cast<const bf16_t*>(in) + kb, ld_in, rows, d - (int)kb, b,
+                            reinterpret_cast<const bf16_t*>(dT) + kb * b, cs ? cs + kb : nullptr,
+                            reinterpret_cast<bf16_t*>(out) + kb, ld_out, s);
+  }
+  return apply_bf16_tiled(in, ld_in, rows, d, b, dT, cs, out, ld_out, s);
+}
+
 hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, int d, int b, int dT_dt, const void* dT,
                  const float* colscale, int out_dt, void* out, int64_t ld_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (cdt == BF16 && in_dt == BF16 && dT_dt == BF16 && out_dt == BF16) {
-    // 256 x 256 tiles when they give every CU a workgroup, else 128 x 128 tiles (two per CU)
-    if ((int64_t)cdiv(rows, 256) * cdiv(b, 256) * nblocks(d, b) >= 256)
-      return apply_t<DGemm, TGemm, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
-    return apply_t<DSq, TSq, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
-  }
+  if (cdt == BF16 && in_dt == BF16 && dT_dt == BF16 && out_dt == BF16)
+    return apply_bf16(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
   if (cdt == F32 && in_dt == F32 && dT_dt == F32 && out_dt == F32)
     return apply_t<void, TF, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
   // merge products: fp32 rows times the stored blocks

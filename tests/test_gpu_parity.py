@@ -107,14 +107,16 @@ def test_layer_llama1p3b_odd_width(lin):
 @pytest.mark.parametrize(
     "m,n,b,T,act",
     [(200, 131, 64, 77, "bf16"), (200, 131, 64, 77, "f32"), (96, 300, 32, 1, "bf16"), (130, 130, 128, 300, "bf16"),
-     (64, 64, 64, 513, "bf16"), (33, 17, 8, 5, "f32"), (520, 1030, 256, 260, "bf16")],
+     (64, 64, 64, 513, "bf16"), (33, 17, 8, 5, "f32"), (520, 1030, 256, 260, "bf16"),
+     # row-streamed block products (enough row tiles): ragged T and a partial last block of b = 256 / 512
+     (2048, 1300, 256, 1000, "bf16"), (1536, 2600, 512, 700, "bf16")],
 )
 def test_layer_ragged(m, n, b, T, act):
     inp = custom_linear_inputs(m, n, b, T, act, act, 0.05, seed=m * 7 + n)
     compare_layer(inp, run_gpu(inp), run_oracle(inp))
 
 
-@pytest.mark.parametrize("m,n,T", [(1024, 1536, 256), (600, 520, 100)])
+@pytest.mark.parametrize("m,n,T", [(1024, 1536, 256), (600, 520, 100), (2048, 2560, 600)])
 def test_layer_int8(m, n, T):
     inp = custom_linear_inputs(m, n, 512 if m >= 1024 else 128, T, "bf16", "i8", 0.005, seed=m + n)
     compare_layer(inp, run_gpu(inp), run_oracle(inp))
