@@ -172,6 +172,7 @@ traffic-json: {json.dumps(line)}
 KERNEL_CLASSES = (  # kernel-name prefix -> class, as in --breakdown
     ("k_gemm<", "W~ contractions"),
     ("k_apply<", "block products"),
+    ("k_apply_stream<", "block products"),
     ("k_block_grads", "block gradients"),
     ("k_cnp_", "CNP products"),
     ("k_unpack_q", "CNP pack/unpack"),
