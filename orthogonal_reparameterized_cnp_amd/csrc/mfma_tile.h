@@ -428,4 +428,88 @@ struct LoadMN {
   }
 };
 
+
+// ---------------------------------------------------------------------------
+// Transposing loader for bf16 tiles of R rows x 64 K whose source has the row
+// index contiguous (element (k, r) at base[k * ld + r]), into an unpadded LDS
+// tile [R][64] of 128-byte rows whose 16-byte chunks are XOR-swizzled by
+// ((r / 2) ^ (r / 16)) % 8.  A unit is 8 rows x 4 K values: four 16-byte
+// global loads along the rows, then eight 8-byte LDS stores along K.  Units
+// are dealt so that the 8 lanes of each group take 8 consecutive row chunks of
+// one K quad, so every wave instruction reads whole 128-byte lines (LoadMN's
+// order reads 64-byte halves); with the swizzle the 64-bit stores are at most
+// 2-way bank conflicted and the 128-bit fragment reads conflict-free.  The
+// whole tile must lie inside the source (no bounds checks).
+// ---------------------------------------------------------------------------
+PX_DEV int tswz_chunk(int r, int c) { return r * 8 + (c ^ (((r >> 1) ^ (r >> 4)) & 7)); }
+template <int R, int NT> struct LoadT {
+  static constexpr int UNITS = R / 8 * 16;  // (8-row chunk, 4-K quad)
+  static constexpr int NU = UNITS / NT;
+  static_assert(UNITS % NT == 0 && NT % 128 == 0 && R % 64 == 0, "whole units per thread");
+  const bf16_t* base;
+  int64_t ld;
+  uint4 c[NU][4];
+  PX_DEV void init(const bf16_t* b, int64_t l) {
+    base = b;
+    ld = l;
+  }
+  // unit u: row chunk 8 (u / 128) + u % 8 (8 rows each), K quad (u / 8) % 16
+  PX_DEV static void unit(int u, int& cg, int& kq) {
+    cg = 8 * (u / 128) + u % 8;
+    kq = (u / 8) % 16;
+  }
+  PX_DEV void fetch(int k0) {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      int cg, kq;
+      unit((int)(threadIdx.x % NT) + i * NT, cg, kq);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        c[i][kk] = *reinterpret_cast<const uint4*>(base + (int64_t)(k0 + 4 * kq + kk) * ld + 8 * cg);
+    }
+  }
+  PX_DEV void stash(char* tile) const {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      int cg, kq;
+      unit((int)(threadIdx.x % NT) + i * NT, cg, kq);
+      const uint32_t w[4][4] = {{c[i][0].x, c[i][0].y, c[i][0].z, c[i][0].w},
+                                {c[i][1].x, c[i][1].y, c[i][1].z, c[i][1].w},
+                                {c[i][2].x, c[i][2].y, c[i][2].z, c[i][2].w},
+                                {c[i][3].x, c[i][3].y, c[i][3].z, c[i][3].w}};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        auto h = [&](int kk) { return (w[kk][e / 2] >> (16 * (e % 2))) & 0xffffu; };
+        uint2 v;
+        v.x = h(0) | (h(1) << 16);
+        v.y = h(2) | (h(3) << 16);
+        *reinterpret_cast<uint2*>(tile + 16 * tswz_chunk(8 * cg + e, kq / 2) + 8 * (kq % 2)) = v;
+      }
+    }
+  }
+};
+
+// MFMAs of one 64-K step from two LoadT tiles (A rows = output rows, B rows =
+// output columns); the fragments of each 16-K step are read before its MFMAs.
+template <class C>
+PX_DEV void mma_stage_t(const char* As, const char* Bs, Acc<C>& acc, int wm, int wn, int lane) {
+  static_assert(C::BK == 64, "64-K tiles");
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    bf16x8_v a[C::TM], b[C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8_v*>(As + 16 * tswz_chunk(wm * C::WTM + 32 * i + r, 2 * ks + h));
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      b[j] = *reinterpret_cast<const bf16x8_v*>(Bs + 16 * tswz_chunk(wn * C::WTN + 32 * j + r, 2 * ks + h));
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        acc.v[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.v[i][j], 0, 0, 0);
+  }
+}
+
 }  // namespace px

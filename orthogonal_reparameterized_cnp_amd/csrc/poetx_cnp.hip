@@ -384,13 +384,53 @@ __global__ __launch_bounds__(C::NT) void k_block_grads_part(SideTable sd, GradSi
     t0 = (int64_t)k0 * 64;
     per = (k1 - k0) * 64;
   }
-  LoadMN<C::BM, C::BK, C::NT, T, T> la;
-  la.init(gs.A[s] + t0 * gs.lda[s] + kb + m0, gs.lda[s], r - m0, per);
-  LoadMN<C::BN, C::BK, C::NT, T, T> lb;
-  lb.init(gs.B[s] + t0 * gs.ldb[s] + kb + n0, gs.ldb[s], r - n0, per);
   Acc<C> acc;
   const AccPos<C> p = acc_pos<C>();
-  mainloop<C, T>(reinterpret_cast<T*>(smem), la, lb, per, acc, p.wm, p.wn, p.lane);
+  bool done = false;
+  if constexpr (std::is_same<T, bf16_t>::value && C::BK == 64) {
+    // whole tile inside the block and whole 64-row K tiles: the line-wide
+    // transposing loader into the swizzled unpadded tile
+    const T* pa = gs.A[s] + t0 * gs.lda[s] + kb + m0;
+    const T* pb = gs.B[s] + t0 * gs.ldb[s] + kb + n0;
+    if (r - m0 >= C::BM && r - n0 >= C::BN && per % 64 == 0 && aligned8(pa, gs.lda[s]) && aligned8(pb, gs.ldb[s])) {
+      constexpr int TA = C::BM * 128, STG = (C::BM + C::BN) * 128;
+      char* lds = reinterpret_cast<char*>(smem);
+      LoadT<C::BM, C::NT> la;
+      LoadT<C::BN, C::NT> lb;
+      la.init(pa, gs.lda[s]);
+      lb.init(pb, gs.ldb[s]);
+      acc.zero();
+      const int NK = per / 64;
+      la.fetch(0);
+      lb.fetch(0);
+      la.stash(lds);
+      lb.stash(lds + TA);
+      __syncthreads();
+      for (int kt = 0; kt < NK; ++kt) {
+        const char* cur = lds + (kt & 1) * STG;
+        char* nxt = lds + ((kt + 1) & 1) * STG;
+        const bool more = kt + 1 < NK;
+        if (more) {
+          la.fetch((kt + 1) * 64);
+          lb.fetch((kt + 1) * 64);
+        }
+        mma_stage_t<C>(cur, cur + TA, acc, p.wm, p.wn, p.lane);
+        if (more) {
+          la.stash(nxt);
+          lb.stash(nxt + TA);
+        }
+        __syncthreads();
+      }
+      done = true;
+    }
+  }
+  if (!done) {
+    LoadMN<C::BM, C::BK, C::NT, T, T> la;
+    la.init(gs.A[s] + t0 * gs.lda[s] + kb + m0, gs.lda[s], r - m0, per);
+    LoadMN<C::BN, C::BK, C::NT, T, T> lb;
+    lb.init(gs.B[s] + t0 * gs.ldb[s] + kb + n0, gs.ldb[s], r - n0, per);
+    mainloop<C, T>(reinterpret_cast<T*>(smem), la, lb, per, acc, p.wm, p.wn, p.lane);
+  }
   float* P = part + ((int64_t)sp * NB + zl) * b * b;
   each_acc<C>(acc, [&](int i, int j, float v) {
     i += m0;
