@@ -344,8 +344,9 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="per kernel class timings on stderr")
-    ap.add_argument("--mode", choices=("xfast", "xmem"), default="xfast",
-                    help="xfast saves H for the backward; xmem saves only the gathered input and recomputes H")
+    ap.add_argument("--mode", choices=("xfast", "xmem", "xout"), default="xfast",
+                    help="xfast saves H for the backward; xmem saves only the gathered input and recomputes H; "
+                         "xout saves only the gathered input and takes H back from the output")
     ap.add_argument("--merge", metavar="WORKLOAD", nargs="?", const="llama13b_int8", default=None,
                     help="also time poetx_merge_reinit of every linear of WORKLOAD (default llama13b_int8) and "
                          "report it amortised over the workload's merge period")
@@ -419,7 +420,7 @@ def main():
         for lay, X, Y in zip(layers, Xs, Ys):
             lay.forward(X, Y)
         for i in reversed(range(len(layers))):
-            group.backward_dx(i, Xs[i], dZs[i], dXs[i])
+            group.backward_dx(i, Xs[i], dZs[i], dXs[i], Y=Ys[i] if args.mode == "xout" else None)
         group.backward_q(dqs)
 
     for _ in range(args.warmup):

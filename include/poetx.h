@@ -68,9 +68,15 @@ typedef enum { POETX_F32 = 0, POETX_BF16 = 1, POETX_I8 = 2 } poetx_dtype;
  * input Xt.  POETX_XMEM saves Xt only; the backward recomputes H from it with
  * the forward's own kernels (one more block product and W~ contraction), so its
  * results are bit-identical to POETX_XFAST while the saved state shrinks by
- * T x round_up(n, 64) activations.
+ * T x round_up(n, 64) activations.  POETX_XOUT also saves Xt only and takes H
+ * back from the layer's output, H = Y[:, perm_P] Diag(G_P)^T: the checkpoint of
+ * the zhichai.net blog, 第五斧 (b = G_P z, one gather and one block product).
+ * That inverts the P side exactly only for orthogonal blocks; with the CNP
+ * blocks, G G^T = (I - Q^4)^2, so the backward sees H Diag((I - Q_P^4)^2)
+ * instead of H, which changes dq_P (dX and dq_R do not use H).  The caller
+ * passes Y to the backward.
  */
-typedef enum { POETX_XFAST = 0, POETX_XMEM = 1 } poetx_mode;
+typedef enum { POETX_XFAST = 0, POETX_XMEM = 1, POETX_XOUT = 2 } poetx_mode;
 
 /* Operation selector for poetx_workspace_size. */
 typedef enum { POETX_OP_CNP = 0, POETX_OP_FWD = 1, POETX_OP_BWD = 2, POETX_OP_MERGE = 3 } poetx_op;
@@ -121,7 +127,8 @@ size_t poetx_weight_bytes(const poetx_layer_desc* desc);
 /* Bytes of the state the forward saves for the backward of the same T tokens.
  * POETX_XFAST: H = Xt Diag(G_R) W~ as [T][round_up(n, 64)] elements of
  * act_dtype, then, at the next 256-byte boundary, the gathered input
- * Xt = X[:, perm_R] as [T][round_up(m, 64)].  POETX_XMEM: Xt only, at offset 0.
+ * Xt = X[:, perm_R] as [T][round_up(m, 64)].  POETX_XMEM and POETX_XOUT: Xt
+ * only, at offset 0.
  * The backward reads Xt from here instead of gathering X again, so a caller
  * need not keep X for the backward. */
 size_t poetx_saved_bytes(const poetx_layer_desc* desc, int64_t T);
@@ -195,7 +202,7 @@ poetx_status poetx_premerge(const poetx_layer_desc* desc, const void* W0, int64_
  *   g_R, g_P  G buffers from poetx_cnp_build for the two sides
  *   Y      out [T][n] act_dtype, leading dimension n
  *   H_save out, poetx_saved_bytes(desc, T) bytes: the saved state (H, then Xt;
- *          Xt only for POETX_XMEM)
+ *          Xt only for POETX_XMEM and POETX_XOUT)
  *          read by poetx_linear_bwd
  *   ws     >= poetx_workspace_size(desc, T, POETX_OP_FWD)
  * T = 0 is a valid no-op.
@@ -211,7 +218,10 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
  * dG_P = H_blk^T dZt_blk and dG_R = Xt_blk^T dA_blk summed over all T tokens in
  * a fixed order (deterministic), then taken through the CNP chain rule and
  * projected onto the packed slots: dq[p(i,j)] = dQ[i][j] - dQ[j][i].
- *   X      not read (the gathered input is in the saved state); may be NULL
+ *   Y      the forward's output [T][n] act_dtype for the same tokens: read in
+ *          the POETX_XOUT mode (H is taken back from it), not read in the
+ *          others (the gathered input is in the saved state), where it may be
+ *          NULL
  *   dZ     [T][n] act_dtype
  *   q_R, q_P  the packed parameters the G buffers were built from
  *   H_save the forward's saved state for the same T tokens
@@ -219,7 +229,7 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
  *   dq_R, dq_P out [nb][b(b-1)/2] fp32, overwritten (dead slots of a partial block are 0)
  *   ws     >= poetx_workspace_size(desc, T, POETX_OP_BWD)
  */
-poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ,
                               const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
                               const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX,
                               float* dq_R, float* dq_P, void* ws, size_t ws_bytes, void* stream);
@@ -283,7 +293,7 @@ size_t poetx_cnp_grad_bytes(int64_t blocks, int32_t b, int32_t dtype);
  * Other arguments as for poetx_linear_bwd.  Errors as for poetx_linear_bwd, and
  * POETX_E_SHAPE when the linear's blocks do not fit in [0, dg_blocks).
  */
-poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ,
                                  const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
                                  const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX,
                                  void* dg, int64_t dg_first, int64_t dg_blocks, void* ws, size_t ws_bytes,

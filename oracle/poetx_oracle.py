@@ -32,6 +32,10 @@ Conventions (where the pages leave the step open, the plainest reading):
     partial block are ignored and receive a zero gradient.
   * Gradients are the exact gradients of this forward (intermediate H kept),
     projected onto the packed parameters: dq[p(i,j)] = dQ[i,j] - dQ[j,i].
+  * The checkpoint of [ZC] 第五斧 (b = G_P z: the pre-P activation taken back
+    from the output instead of stored) is the opt-in h_from_output below.  In
+    row form it reads H' = Y[:, pi_P] Diag(G_P)^T.  It inverts the P side only
+    for orthogonal blocks; for CNP blocks H' = H Diag((I - Q^4)^2).
 """
 
 from __future__ import annotations
@@ -261,14 +265,23 @@ class Bwd:
     dq_P: np.ndarray
 
 
-def backward(X, dZ, W, perm_R, perm_P, q_R, q_P, b) -> Bwd:
-    """Exact gradients of forward() w.r.t. X and the packed q of both sides."""
+def h_from_output(Y, perm_P, G_P) -> np.ndarray:
+    """[ZC] 第五斧: b = G_P z, the pre-P activation recovered from the layer output
+    (z = G_P^T b in column form).  Row form: H' = Y[:, pi_P] Diag(G_P)^T."""
+    return apply_blocks(Y[:, perm_P], G_P, transpose=True)
+
+
+def backward(X, dZ, W, perm_R, perm_P, q_R, q_P, b, h_output: bool = False) -> Bwd:
+    """Exact gradients of forward() w.r.t. X and the packed q of both sides.
+    h_output: dG_P uses H' = h_from_output(Y, ..) in place of the forward's H
+    (the checkpoint variant; dX and dq_R do not involve H)."""
     m, n = W.shape
     Q_R, Q_P = side_Q(q_R, m, b), side_Q(q_P, n, b)
     G_R, G_P = [cnp(Q) for Q in Q_R], [cnp(Q) for Q in Q_P]
     f = forward(X, W, perm_R, perm_P, G_R, G_P)
     dZt = dZ[:, perm_P]
-    dG_P = [f.H[:, s : s + r].T @ dZt[:, s : s + r] for s, r in side_blocks(n, b)]
+    H = h_from_output(f.Y, perm_P, G_P) if h_output else f.H
+    dG_P = [H[:, s : s + r].T @ dZt[:, s : s + r] for s, r in side_blocks(n, b)]
     dH = apply_blocks(dZt, G_P, transpose=True)
     dA = dH @ f.Wt.T
     dG_R = [f.Xt[:, s : s + r].T @ dA[:, s : s + r] for s, r in side_blocks(m, b)]

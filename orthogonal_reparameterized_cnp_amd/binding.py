@@ -27,8 +27,9 @@ POETX_OP_CNP, POETX_OP_FWD, POETX_OP_BWD, POETX_OP_MERGE = 0, 1, 2, 3
 POETX_KC_NONE, POETX_KC_GEMM, POETX_KC_APPLY, POETX_KC_DGRAD, POETX_KC_CNP, POETX_KC_PERMUTE = range(6)
 
 DTYPES = {"f32": POETX_F32, "bf16": POETX_BF16, "i8": POETX_I8}
-POETX_XFAST, POETX_XMEM = 0, 1  # what the forward saves: H and Xt, or Xt only (H recomputed)
-MODES = {"xfast": POETX_XFAST, "xmem": POETX_XMEM}
+# what the forward saves: H and Xt; Xt only (H recomputed from it); Xt only (H taken back from Y)
+POETX_XFAST, POETX_XMEM, POETX_XOUT = 0, 1, 2
+MODES = {"xfast": POETX_XFAST, "xmem": POETX_XMEM, "xout": POETX_XOUT}
 
 
 class PoetxError(RuntimeError):
@@ -223,11 +224,11 @@ def poetx_linear_fwd(dsc: LayerDesc, T: int, X, perm_R, perm_P, Wt, g_R, g_P, Y,
     )
 
 
-def poetx_linear_bwd(dsc: LayerDesc, T: int, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, dq_R, dq_P,
+def poetx_linear_bwd(dsc: LayerDesc, T: int, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, dq_R, dq_P,
                      ws, ws_bytes: int, stream=None):
     _check(
         lib().poetx_linear_bwd(
-            ctypes.byref(dsc), T, _ptr(X), _ptr(dZ), _ptr(perm_R), _ptr(perm_P), _ptr(Wt), _ptr(g_R), _ptr(g_P),
+            ctypes.byref(dsc), T, _ptr(Y), _ptr(dZ), _ptr(perm_R), _ptr(perm_P), _ptr(Wt), _ptr(g_R), _ptr(g_P),
             _ptr(q_R), _ptr(q_P), _ptr(H_save), _ptr(dX), _ptr(dq_R), _ptr(dq_P), _ptr(ws), ws_bytes, _stream(stream),
         )
     )
@@ -266,11 +267,11 @@ def poetx_cnp_grad_bytes(blocks: int, b: int, dtype: int) -> int:
     return lib().poetx_cnp_grad_bytes(blocks, b, dtype)
 
 
-def poetx_linear_bwd_dx(dsc: LayerDesc, T: int, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, dg,
+def poetx_linear_bwd_dx(dsc: LayerDesc, T: int, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, dg,
                         dg_first: int, dg_blocks: int, ws, ws_bytes: int, stream=None):
     _check(
         lib().poetx_linear_bwd_dx(
-            ctypes.byref(dsc), T, _ptr(X), _ptr(dZ), _ptr(perm_R), _ptr(perm_P), _ptr(Wt), _ptr(g_R), _ptr(g_P),
+            ctypes.byref(dsc), T, _ptr(Y), _ptr(dZ), _ptr(perm_R), _ptr(perm_P), _ptr(Wt), _ptr(g_R), _ptr(g_P),
             _ptr(q_R), _ptr(q_P), _ptr(H_save), _ptr(dX), _ptr(dg), dg_first, dg_blocks, _ptr(ws), ws_bytes,
             _stream(stream),
         )

@@ -92,7 +92,8 @@ poetx_status check_desc(const poetx_layer_desc* d) {
   if (d->b < 2 || d->b > 1024) return fail(POETX_E_SHAPE, "b must be in [2, 1024]");
   if (nblocks(d->m, d->b) > 65535 || nblocks(d->n, d->b) > 65535)
     return fail(POETX_E_SHAPE, "at most 65535 blocks per side");
-  if (d->mode != POETX_XFAST && d->mode != POETX_XMEM) return fail(POETX_E_SHAPE, "mode must be XFAST or XMEM");
+  if (d->mode != POETX_XFAST && d->mode != POETX_XMEM && d->mode != POETX_XOUT)
+    return fail(POETX_E_SHAPE, "mode must be XFAST, XMEM or XOUT");
   const bool ok = (d->act_dtype == POETX_F32 && d->w_dtype == POETX_F32) ||
                   (d->act_dtype == POETX_BF16 && (d->w_dtype == POETX_BF16 || d->w_dtype == POETX_I8));
   if (!ok) return fail(POETX_E_DTYPE, "supported (act, weight) dtypes: (F32, F32), (BF16, BF16), (BF16, I8)");
@@ -132,14 +133,15 @@ bool has_weight_t(const poetx_layer_desc* d) { return d->w_dtype == POETX_BF16; 
 size_t weight_t_offset(const poetx_layer_desc* d) { return weight_scale_offset(d); }
 
 // The forward's saved state: H [T][lead(n)], then (256-byte aligned) the
-// gathered input Xt [T][lead(m)], both in act_dtype; Xt alone for Xmem.
+// gathered input Xt [T][lead(m)], both in act_dtype; Xt alone for Xmem and Xout.
+bool saves_h(const poetx_layer_desc* d) { return d->mode == POETX_XFAST; }
 size_t saved_xt_offset(const poetx_layer_desc* d, int64_t T) {
-  if (d->mode == POETX_XMEM) return 0;
+  if (!saves_h(d)) return 0;
   return (size_t)round_up(T * lead(d->n) * (int64_t)dt_size(d->act_dtype), 256);
 }
 
 struct FwdWs {
-  void *A, *Zt, *H;  // H: Xmem only (Xfast writes it to the saved state)
+  void *A, *Zt, *H;  // H: Xmem and Xout (Xfast writes it to the saved state)
   int32_t* invP;
 };
 template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
@@ -148,12 +150,13 @@ template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
   w.A = p.template take<char>(T * lead(d->m) * es);
   w.Zt = p.template take<char>(T * lead(d->n) * es);
   w.invP = p.template take<int32_t>((size_t)d->n * 4);
-  w.H = d->mode == POETX_XMEM ? p.template take<char>(T * lead(d->n) * es) : nullptr;
+  w.H = saves_h(d) ? nullptr : p.template take<char>(T * lead(d->n) * es);
   return w;
 }
 
 struct BwdWs {
   void *dZt, *dH, *dA, *dXt, *cnp;
+  void* Hr;  // Xout: H taken back from the output
   float* part;
   int32_t* invR;
 };
@@ -168,6 +171,7 @@ template <class P> BwdWs plan_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
   w.part = p.template take<float>(
       block_grads_part_bytes(d->act_dtype, (int)T, nblocks(d->m, d->b) + nblocks(d->n, d->b), d->b));
   w.invR = p.template take<int32_t>((size_t)d->m * 4);
+  w.Hr = d->mode == POETX_XOUT ? p.template take<char>(T * lead(d->n) * es) : nullptr;
   return w;
 }
 
@@ -431,7 +435,7 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
   void* Xt = reinterpret_cast<char*>(H_save) + saved_xt_offset(desc, T);
   PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, Xt, ldm, rows, m, m, s));
   // A = Xt Diag(G_R), H = A W~: H saved (Xfast) or kept in the workspace (Xmem)
-  void* H = desc->mode == POETX_XMEM ? w.H : H_save;
+  void* H = saves_h(desc) ? H_save : w.H;
   st = xt_to_h(desc, T, Xt, Wt, g_R, w.A, H, s);
   if (st != POETX_OK) return st;
   // Zt = H Diag(G_P)
@@ -449,7 +453,7 @@ namespace {
 
 // dX and the block gradients of both sides into blocks [first, first + nb_R + nb_P)
 // of the gradient state dg (total blocks); shared by both backward entry points.
-poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ,
                          const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
                          const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX, void* dg,
                          int64_t first, int64_t total, const BwdWs& w, hipStream_t s) {
@@ -470,13 +474,19 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* X,
            gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
   // block gradients of both sides over all tokens: dG_R = Xt^T dA, dG_P = H^T dZt, with Xt and H
   // from the forward's saved state.  Xmem recomputes H from Xt, into the buffers that dH (consumed
-  // by the contraction above) and dXt (written below) occupy.
+  // by the contraction above) and dXt (written below) occupy.  Xout takes H back from the output:
+  // Zt = Y[:, perm_P] into dH's buffer, then H = Zt Diag(G_P)^T.
   const void* Xt = reinterpret_cast<const char*>(H_save) + saved_xt_offset(desc, T);
   const void* H = H_save;
   if (desc->mode == POETX_XMEM) {
     const poetx_status st = xt_to_h(desc, T, Xt, Wt, g_R, w.dXt, w.dH, s);
     if (st != POETX_OK) return st;
     H = w.dH;
+  } else if (desc->mode == POETX_XOUT) {
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, permute(at, Y, n, nullptr, perm_P, w.dH, ldn, rows, n, n, s));
+    PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
+             apply(at, at, w.dH, ldn, rows, n, b, at, g_P, nullptr, at, w.Hr, ldn, s));
+    H = w.Hr;
   }
   const CnpSide sides[2] = {{q_R, m, Xt, ldm, w.dA, ldm}, {q_P, n, H, ldn, w.dZt, ldn}};
   PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * (sum_r2(m, b) + sum_r2(n, b)),
@@ -492,7 +502,7 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* X,
   return POETX_OK;
 }
 
-poetx_status check_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ, const int32_t* perm_R,
+poetx_status check_bwd(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ, const int32_t* perm_R,
                        const int32_t* perm_P, const void* Wt, const void* g_R, const void* g_P, const float* q_R,
                        const float* q_P, const void* H_save, void* dX, void* ws, size_t ws_bytes) {
   poetx_status st = check_desc(desc);
@@ -500,7 +510,7 @@ poetx_status check_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, c
   if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
   if (!perm_R || !perm_P || !Wt || !g_R || !g_P || !q_R || !q_P) return fail(POETX_E_NULL, "a required pointer is NULL");
   if (T > 0 && (!dZ || !H_save || !dX)) return fail(POETX_E_NULL, "a required pointer is NULL");
-  (void)X;  // the gathered input comes from the saved state
+  if (T > 0 && desc->mode == POETX_XOUT && !Y) return fail(POETX_E_NULL, "Y is NULL (POETX_XOUT reads it)");
   Plan p;
   plan_bwd(p, desc, T);
   return check_ws(ws, ws_bytes, p.off);
@@ -510,11 +520,11 @@ poetx_status check_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, c
 
 extern "C" {
 
-poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ,
                               const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
                               const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX,
                               float* dq_R, float* dq_P, void* ws, size_t ws_bytes, void* stream) {
-  poetx_status st = check_bwd(desc, T, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, ws, ws_bytes);
+  poetx_status st = check_bwd(desc, T, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, ws, ws_bytes);
   if (st != POETX_OK) return st;
   if (!dq_R || !dq_P) return fail(POETX_E_NULL, "a required pointer is NULL");
   Plan pq;
@@ -523,7 +533,7 @@ poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const voi
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype;
   const int64_t blocks = (int64_t)nblocks(m, b) + nblocks(n, b);
-  st = bwd_dx_core(desc, T, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, w.cnp, 0, blocks, w, s);
+  st = bwd_dx_core(desc, T, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, w.cnp, 0, blocks, w, s);
   if (st != POETX_OK) return st;
   // CNP chain rule and skew projection of both sides
   const float* qs[2] = {q_R, q_P};
@@ -534,12 +544,12 @@ poetx_status poetx_linear_bwd(const poetx_layer_desc* desc, int64_t T, const voi
   return POETX_OK;
 }
 
-poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const void* X, const void* dZ,
+poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ,
                                  const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
                                  const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX,
                                  void* dg, int64_t dg_first, int64_t dg_blocks, void* ws, size_t ws_bytes,
                                  void* stream) {
-  poetx_status st = check_bwd(desc, T, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, ws, ws_bytes);
+  poetx_status st = check_bwd(desc, T, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, ws, ws_bytes);
   if (st != POETX_OK) return st;
   if (!dg) return fail(POETX_E_NULL, "dg is NULL");
   if (reinterpret_cast<uintptr_t>(dg) % 256) return fail(POETX_E_WORKSPACE, "dg must be 256-byte aligned");
@@ -550,7 +560,7 @@ poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const 
   pq.base = reinterpret_cast<char*>(ws);
   const BwdWs w = plan_bwd(pq, desc, T);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return bwd_dx_core(desc, T, X, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, dg, dg_first, dg_blocks, w, s);
+  return bwd_dx_core(desc, T, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, dg, dg_first, dg_blocks, w, s);
 }
 
 poetx_status poetx_cnp_backward_batch(int32_t count, const float* const* q, const int32_t* d, int32_t b, int32_t dtype,

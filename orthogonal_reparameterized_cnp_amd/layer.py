@@ -22,8 +22,10 @@ def lead(d: int) -> int:
 class PoetxLinear:
     def __init__(self, m: int, n: int, b: int, act: str = "bf16", w: str = "bf16", device: str = "cuda",
                  mode: str = "xfast"):
-        """mode: "xfast" saves H for the backward, "xmem" saves only the gathered input and the
-        backward recomputes H (bit-identical results, T x n fewer saved activations)."""
+        """mode: "xfast" saves H for the backward; "xmem" saves only the gathered input and the
+        backward recomputes H (bit-identical results, T x n fewer saved activations); "xout" saves
+        only the gathered input and the backward takes H back from the output Y, which it must be
+        given (H Diag((I - Q_P^4)^2) in place of H: dq_P differs, dX and dq_R do not)."""
         self.m, self.n, self.b, self.act, self.w, self.mode = m, n, b, act, w, mode
         self.device = torch.device(device)
         self.desc = B.desc(m, n, b, act, w, mode)
@@ -113,7 +115,13 @@ class PoetxLinear:
         self.T = T
         return Y
 
-    def backward(self, X: torch.Tensor, dZ: torch.Tensor, dX=None, dq_R=None, dq_P=None, stream=None):
+    def _y_arg(self, Y):
+        if self.mode == "xout" and Y is None:
+            raise ValueError("the xout mode takes H back from the forward's output: pass Y")
+        return Y if self.mode == "xout" else None
+
+    def backward(self, X: torch.Tensor, dZ: torch.Tensor, dX=None, dq_R=None, dq_P=None, stream=None, Y=None):
+        """X only gives T (the gathered input is in the saved state); Y: the forward's output (xout)."""
         T = X.shape[0]
         self.reserve(T)
         if dX is None:
@@ -122,8 +130,8 @@ class PoetxLinear:
             dq_R = torch.empty_like(self.q_R)
         if dq_P is None:
             dq_P = torch.empty_like(self.q_P)
-        B.poetx_linear_bwd(self.desc, T, X, dZ, self.perm_R, self.perm_P, self.Wt, self.g_R, self.g_P, self.q_R,
-                           self.q_P, self.H_save, dX, dq_R, dq_P, self.ws, self.ws.numel(), stream)
+        B.poetx_linear_bwd(self.desc, T, self._y_arg(Y), dZ, self.perm_R, self.perm_P, self.Wt, self.g_R, self.g_P,
+                           self.q_R, self.q_P, self.H_save, dX, dq_R, dq_P, self.ws, self.ws.numel(), stream)
         return dX, dq_R, dq_P
 
     def merge_reinit(self, seed_R: int, seed_P: int, stream=None):
@@ -176,15 +184,16 @@ class PoetxGroup:
         g = [x for l in self.layers for x in (l.g_R, l.g_P)]
         B.poetx_cnp_build_batch(q, self.d, self.b, self.adt, g, self.ws, self.ws.numel(), stream)
 
-    def backward_dx(self, i: int, X: torch.Tensor, dZ: torch.Tensor, dX=None, stream=None) -> torch.Tensor:
-        """dX of linear i; its block gradients go to the group's gradient state."""
+    def backward_dx(self, i: int, X: torch.Tensor, dZ: torch.Tensor, dX=None, stream=None, Y=None) -> torch.Tensor:
+        """dX of linear i; its block gradients go to the group's gradient state (Y: as PoetxLinear.backward)."""
         lay = self.layers[i]
         T = X.shape[0]
         lay.reserve(T)
         if dX is None:
             dX = torch.empty(T, lay.m, dtype=X.dtype, device=self.device)
-        B.poetx_linear_bwd_dx(lay.desc, T, X, dZ, lay.perm_R, lay.perm_P, lay.Wt, lay.g_R, lay.g_P, lay.q_R, lay.q_P,
-                              lay.H_save, dX, self.dg, self.first[i], self.blocks, lay.ws, lay.ws.numel(), stream)
+        B.poetx_linear_bwd_dx(lay.desc, T, lay._y_arg(Y), dZ, lay.perm_R, lay.perm_P, lay.Wt, lay.g_R, lay.g_P,
+                              lay.q_R, lay.q_P, lay.H_save, dX, self.dg, self.first[i], self.blocks, lay.ws,
+                              lay.ws.numel(), stream)
         return dX
 
     def backward_q(self, dqs=None, stream=None):

@@ -76,7 +76,7 @@ def run_gpu(inp, backward: bool = True, mode: str = "xfast"):
     out = {"layer": lay, "Y": Y}
     if backward:
         dZ = dev(inp.dZ, inp.act)
-        dX, dq_R, dq_P = lay.backward(X, dZ)
+        dX, dq_R, dq_P = lay.backward(X, dZ, Y=Y if mode == "xout" else None)
         out.update(dX=dX, dq_R=dq_R, dq_P=dq_P)
     torch.cuda.synchronize()
     return out
@@ -86,7 +86,7 @@ def oracle_w(inp) -> np.ndarray:
     return O.to_f64(inp.W0, inp.w, inp.w_scale)
 
 
-def run_oracle(inp, backward: bool = True):
+def run_oracle(inp, backward: bool = True, h_output: bool = False):
     X = O.to_f64(inp.X, inp.act)
     W = oracle_w(inp)
     q_R, q_P = inp.q_R.astype(np.float64), inp.q_P.astype(np.float64)
@@ -94,7 +94,7 @@ def run_oracle(inp, backward: bool = True):
     f = O.forward(X, W, inp.perm_R, inp.perm_P, G_R, G_P)
     out = {"Y": f.Y, "H": f.H, "G_R": G_R, "G_P": G_P}
     if backward:
-        g = O.backward(X, O.to_f64(inp.dZ, inp.act), W, inp.perm_R, inp.perm_P, q_R, q_P, inp.b)
+        g = O.backward(X, O.to_f64(inp.dZ, inp.act), W, inp.perm_R, inp.perm_P, q_R, q_P, inp.b, h_output=h_output)
         out.update(dX=g.dX, dq_R=g.dq_R, dq_P=g.dq_P)
     return out
 

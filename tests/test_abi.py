@@ -48,8 +48,14 @@ def test_host_helpers(L):
     assert B.poetx_workspace_size(dm, 10, B.POETX_OP_FWD) == B.poetx_workspace_size(d, 10, B.POETX_OP_FWD) + (
         (10 * ldw * 2 + 255) // 256 * 256)
     assert B.poetx_workspace_size(dm, 10, B.POETX_OP_BWD) == B.poetx_workspace_size(d, 10, B.POETX_OP_BWD)
+    # Xout: Xt alone as for Xmem; the backward adds one [T][lead(n)] buffer for H taken back from Y
+    do = B.desc(1024, 5461, 256, "bf16", "i8", "xout")
+    assert B.poetx_saved_bytes(do, 10) == B.poetx_saved_bytes(dm, 10)
+    assert B.poetx_workspace_size(do, 10, B.POETX_OP_FWD) == B.poetx_workspace_size(dm, 10, B.POETX_OP_FWD)
+    assert B.poetx_workspace_size(do, 10, B.POETX_OP_BWD) == B.poetx_workspace_size(d, 10, B.POETX_OP_BWD) + (
+        (10 * ldw * 2 + 255) // 256 * 256)
     bad = B.desc(1024, 5461, 256, "bf16", "i8")
-    bad.mode = 2
+    bad.mode = 3
     assert B.poetx_saved_bytes(bad, 10) == 0 and B.poetx_workspace_size(bad, 10, B.POETX_OP_FWD) == 0
 
 
@@ -82,6 +88,11 @@ def test_validation_statuses(L):
     args = [FAKE] * 13
     assert L.poetx_linear_bwd(ctypes.byref(good), 4, *args[:4], None, *args[5:13], FAKE, 16, None) == B.POETX_E_NULL
     assert L.poetx_linear_bwd(ctypes.byref(good), 4, *args, FAKE, 16, None) == B.POETX_E_WORKSPACE
+    # the first tensor slot (the forward's output Y) is read only in the xout mode
+    assert L.poetx_linear_bwd(ctypes.byref(good), 4, None, *args[1:], FAKE, 16, None) == B.POETX_E_WORKSPACE
+    xout = B.desc(256, 256, 32, "f32", "f32", "xout")
+    assert L.poetx_linear_bwd(ctypes.byref(xout), 4, None, *args[1:], FAKE, 1 << 40, None) == B.POETX_E_NULL
+    assert "Y is NULL" in B.poetx_last_error()
     assert L.poetx_merge_reinit(ctypes.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 2, FAKE, 1 << 40, None) == B.POETX_E_NULL
     assert L.poetx_cnp_build(FAKE, 256, 32, B.POETX_I8, FAKE, FAKE, 1 << 30, None) == B.POETX_E_DTYPE
     assert L.poetx_cnp_build(FAKE, 256, 1, B.POETX_F32, FAKE, FAKE, 1 << 30, None) == B.POETX_E_SHAPE

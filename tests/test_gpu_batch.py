@@ -72,10 +72,18 @@ def test_group_backward_xmem(act, b, shapes, T):
     _group_case(act, b, shapes, T, False, "xmem")
 
 
+@pytest.mark.parametrize("act,b,shapes,T", [("bf16", 512, [(1024, 1536), (600, 520)], 256)])
+def test_group_backward_xout(act, b, shapes, T):
+    """Grouped Xout linears (H taken back from Y in backward_dx) against per-linear Xout calls:
+    bit-identical."""
+    _group_case(act, b, shapes, T, False, "xout")
+
+
 def _group_case(act, b, shapes, T, oracle, mode):
     print(f"group backward act={act} b={b} shapes={shapes} T={T} mode={mode}", flush=True)
     inps = [custom_linear_inputs(m, n, b, T, act, act, 0.05, seed=11 * m + n) for m, n in shapes]
-    single = [make_layer(inp) for inp in inps]  # per-side builds
+    # per-side builds; Xmem against Xfast (bit-identical), Xout against Xout (its dq_P differs)
+    single = [make_layer(inp, "xout" if mode == "xout" else "xfast") for inp in inps]
     grouped = [make_layer(inp, mode) for inp in inps]
     group = PoetxGroup(grouped)
     group.build()  # rebuild every side's G in one batch
@@ -85,10 +93,11 @@ def _group_case(act, b, shapes, T, oracle, mode):
     outs = []
     for i, (inp, a, g) in enumerate(zip(inps, single, grouped)):
         X, dZ = dev(inp.X, inp.act), dev(inp.dZ, inp.act)
-        a.forward(X)
-        g.forward(X)
-        dX_a, dqR_a, dqP_a = a.backward(X, dZ)
-        dX_g = group.backward_dx(i, X, dZ)
+        Ya = a.forward(X)
+        Yg = g.forward(X)
+        out_y = mode == "xout"
+        dX_a, dqR_a, dqP_a = a.backward(X, dZ, Y=Ya if out_y else None)
+        dX_g = group.backward_dx(i, X, dZ, Y=Yg if out_y else None)
         outs.append((dX_a, dqR_a, dqP_a, dX_g))
     dqs = group.backward_q()
     torch.cuda.synchronize()

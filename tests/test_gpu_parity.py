@@ -151,6 +151,30 @@ def _bits_t(t: torch.Tensor) -> torch.Tensor:
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
+# ----------------------------------------------------------------------------
+# Xout (H taken back from the output, the checkpoint b = G_P z) against the
+# oracle's h_output backward; dX and dq_R bit-identical to Xfast
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize(
+    "m,n,b,T,act,w",
+    [(520, 1030, 256, 260, "bf16", "bf16"), (2048, 2560, 512, 600, "bf16", "i8"), (200, 131, 64, 77, "f32", "f32"),
+     (1024, 1536, 512, 512, "bf16", "bf16")],
+)
+def test_xout_matches_oracle(m, n, b, T, act, w):
+    print(f"xout m={m} n={n} b={b} T={T} act={act} w={w}", flush=True)
+    inp = custom_linear_inputs(m, n, b, T, act, w, 0.02, seed=m + 3 * n + T)
+    out = run_gpu(inp, mode="xout")
+    ref = run_oracle(inp, h_output=True)
+    kind = inp.act
+    assert_close("Y", host(out["Y"], kind), ref["Y"], kind)
+    assert_close("dX", host(out["dX"], kind), ref["dX"], kind)
+    assert_close("dq_R", host(out["dq_R"], "f32"), ref["dq_R"], kind)
+    assert_close("dq_P", host(out["dq_P"], "f32"), ref["dq_P"], kind)
+    fast = run_gpu(inp, mode="xfast")
+    for k in ("Y", "dX", "dq_R"):
+        assert torch.equal(out[k], fast[k]), k
+
+
 def test_empty_batch():
     inp = custom_linear_inputs(128, 96, 32, 1, "bf16", "bf16", 0.01, seed=5)
     lay = make_layer(inp)

@@ -229,3 +229,50 @@ def test_block_grads_match_full_backward():
     np.testing.assert_allclose(sel[("R", 0)], g.dq_R[0], atol=1e-14)
     np.testing.assert_allclose(sel[("R", 3)], g.dq_R[3], atol=1e-14)
     np.testing.assert_allclose(sel[("P", 2)], g.dq_P[2], atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# the checkpoint of [ZC] 第五斧: H taken back from the output
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", SHAPES)
+def test_h_from_output_closed_form(shape):
+    """H' = Y[:, pi_P] Diag(G_P)^T equals H Diag((I - Q^4)^2) for CNP blocks: the
+    Neumann truncation is the Cayley transform times (I - Q^4), so G G^T = (I - Q^4)^2.
+    The right side is built from Q alone, without G, the output or the permutation."""
+    m, n, b, T = shape
+    p = _problem(m, n, b, T, 0.3, seed=m * 100 + n)
+    G_R, G_P = O.side_G(p["q_R"], m, b), O.side_G(p["q_P"], n, b)
+    f = O.forward(p["X"], p["W"], p["perm_R"], p["perm_P"], G_R, G_P)
+    Hp = O.h_from_output(f.Y, p["perm_P"], G_P)
+    corr = []
+    for Q in O.side_Q(p["q_P"], n, b):
+        E = np.eye(Q.shape[0]) - np.linalg.matrix_power(Q, 4)
+        corr.append(E @ E)
+    expect = f.H @ O.block_diag(corr)
+    assert np.abs(Hp - expect).max() <= 1e-12 * np.abs(expect).max()
+    # and it is not H itself (the q above is large enough to see the difference)
+    assert np.abs(Hp - f.H).max() > 1e-6 * np.abs(f.H).max()
+
+
+@pytest.mark.parametrize("shape", SHAPES[:3])
+def test_h_from_output_exact_for_orthogonal_blocks(shape):
+    m, n, b, T = shape
+    p = _problem(m, n, b, T, 0.3, seed=m + 7 * n)
+    G_R, G_P = O.side_G(p["q_R"], m, b, exact=True), O.side_G(p["q_P"], n, b, exact=True)
+    f = O.forward(p["X"], p["W"], p["perm_R"], p["perm_P"], G_R, G_P)
+    Hp = O.h_from_output(f.Y, p["perm_P"], G_P)
+    assert np.abs(Hp - f.H).max() <= 1e-12 * np.abs(f.H).max()
+
+
+def test_h_output_backward_touches_only_dq_p():
+    """dX and dq_R do not involve H; with q_P = 0 (G_P = I) H' = H and dq_P agrees too."""
+    m, n, b, T = 12, 10, 4, 6
+    p = _problem(m, n, b, T, 0.3, seed=5)
+    args = (p["X"], p["dZ"], p["W"], p["perm_R"], p["perm_P"], p["q_R"], p["q_P"], b)
+    g0, g1 = O.backward(*args), O.backward(*args, h_output=True)
+    np.testing.assert_array_equal(g0.dX, g1.dX)
+    np.testing.assert_array_equal(g0.dq_R, g1.dq_R)
+    assert np.abs(g0.dq_P - g1.dq_P).max() > 0
+    zero = (p["X"], p["dZ"], p["W"], p["perm_R"], p["perm_P"], p["q_R"], np.zeros_like(p["q_P"]), b)
+    h0, h1 = O.backward(*zero), O.backward(*zero, h_output=True)
+    assert np.abs(h0.dq_P - h1.dq_P).max() <= 1e-12 * np.abs(h0.dq_P).max()
