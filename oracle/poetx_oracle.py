@@ -36,10 +36,15 @@ Conventions (where the pages leave the step open, the plainest reading):
     from the output instead of stored) is the opt-in h_from_output below.  In
     row form it reads H' = Y[:, pi_P] Diag(G_P)^T.  It inverts the P side only
     for orthogonal blocks; for CNP blocks H' = H Diag((I - Q^4)^2).
+  * The optimiser that moves the packed q is not named by the pages, which
+    only say that it keeps state for the packed half ([ZC] 第四斧 item 1): it
+    is read as Adam with decoupled weight decay (adam_step).  The training
+    loop (train_steps) restarts q and the moments at every merge.
 """
 
 from __future__ import annotations
 
+import copy
 from dataclasses import dataclass
 from typing import List, Optional, Sequence
 
@@ -412,3 +417,105 @@ def block_grads(X, dZ, W, perm_R, perm_P, q_R, q_P, b, blocks_R, blocks_P):
             dAk = dH @ Wt[s : s + r, :].T
             out[("R", k)] = pack_skew_grad(cnp_adjoint(Q_R[k], Xt[:, s : s + r].T @ dAk), b)
     return out
+
+
+# ----------------------------------------------------------------------------
+# optimiser step on the packed parameters and the training cadence
+# ([ZC] 第四斧 item 1: the optimiser keeps state only for the packed half;
+#  [PN] 训练策略 and 关键设计 3: an inner loop on the small orthogonal
+#  parameters, merged into the weight every T_m steps and then restarted)
+# ----------------------------------------------------------------------------
+
+
+@dataclass
+class AdamHP:
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.0
+
+
+def adam_step(q, g, m1, m2, t: int, hp: AdamHP):
+    """One Adam step (Kingma & Ba 2015: exponential moving averages of the
+    gradient and of its square, each divided by its bias correction 1 - beta^t)
+    with decoupled weight decay (Loshchilov & Hutter 2019: the decay term is
+    added to the normalised step, not to the gradient).  fp64; t is the 1-based
+    number of steps since the moments were zero.  Returns new (q, m1, m2)."""
+    q, g, m1, m2 = (np.asarray(a, dtype=np.float64) for a in (q, g, m1, m2))
+    m1 = hp.beta1 * m1 + (1.0 - hp.beta1) * g
+    m2 = hp.beta2 * m2 + (1.0 - hp.beta2) * g * g
+    m_hat = m1 / (1.0 - hp.beta1**t)
+    v_hat = m2 / (1.0 - hp.beta2**t)
+    q = q - hp.lr * (m_hat / (np.sqrt(v_hat) + hp.eps) + hp.weight_decay * q)
+    return q, m1, m2
+
+
+def store_weight_values(W64: np.ndarray, w: str) -> np.ndarray:
+    """Values of a weight after it is stored in dtype w: fp32 and bf16 round to
+    nearest even, int8 is requantised per column (quantize_int8_f32) and read
+    back as code x scale.  "f64" keeps the values unrounded."""
+    if w == "f64":
+        return np.array(W64, dtype=np.float64)
+    if w == "f32":
+        return W64.astype(np.float32).astype(np.float64)
+    if w == "bf16":
+        return to_f64(round_bf16(W64), "bf16")
+    if w == "i8":
+        code, scale = quantize_int8_f32(W64)
+        return to_f64(code, "i8", scale)
+    raise ValueError(w)
+
+
+@dataclass
+class TrainState:
+    Wt: np.ndarray  # pre-merged weight values W0[pi_R][:, pi_P] (fp64 of the stored dtype)
+    perm_R: np.ndarray
+    perm_P: np.ndarray
+    q_R: np.ndarray
+    q_P: np.ndarray
+    m1_R: np.ndarray
+    m2_R: np.ndarray
+    m1_P: np.ndarray
+    m2_P: np.ndarray
+    t: int  # steps since the moments were last zero
+
+
+def natural_weight(Wt: np.ndarray, perm_R: np.ndarray, perm_P: np.ndarray) -> np.ndarray:
+    """W0 from its pre-merged form: W0[pi_R[i], pi_P[j]] = W~[i, j]."""
+    W = np.empty_like(Wt)
+    W[np.ix_(perm_R, perm_P)] = Wt
+    return W
+
+
+def train_steps(state: TrainState, b: int, w: str, batches, hp: AdamHP, merge_every: int, merge_seeds,
+                first_step: int = 1) -> TrainState:
+    """The inner loop of [PN] 训练策略 on one linear, one step per (X, dZ) batch.
+
+    Step s (counted from first_step): build G from q, take the exact gradient
+    dq of both sides (backward()), and move q by one adam_step with the count
+    of steps since the last restart.  When merge_every > 0 and s is a multiple
+    of it, merge the factors built from the updated q into the weight
+    (merge_reinit with merge_seeds(s) -> (seed_R, seed_P)), store the new
+    pre-merged weight in dtype w, and restart: q = 0, both moments 0, count 0.
+    The moments are cleared because the new permutations give every packed
+    slot a different pair of coordinates (the pages do not say; plainest
+    reading)."""
+    st = copy.deepcopy(state)
+    m, n = st.Wt.shape
+    for s, (X, dZ) in enumerate(batches, start=first_step):
+        W = natural_weight(st.Wt, st.perm_R, st.perm_P)
+        g = backward(X, dZ, W, st.perm_R, st.perm_P, st.q_R, st.q_P, b)
+        st.t += 1
+        st.q_R, st.m1_R, st.m2_R = adam_step(st.q_R, g.dq_R, st.m1_R, st.m2_R, st.t, hp)
+        st.q_P, st.m1_P, st.m2_P = adam_step(st.q_P, g.dq_P, st.m1_P, st.m2_P, st.t, hp)
+        if merge_every > 0 and s % merge_every == 0:
+            seed_R, seed_P = merge_seeds(s)
+            mg = merge_reinit(st.Wt, st.perm_R, st.perm_P, side_G(st.q_R, m, b), side_G(st.q_P, n, b),
+                              seed_R, seed_P)
+            st.Wt = store_weight_values(mg.Wt_new, w)
+            st.perm_R, st.perm_P = mg.perm_R, mg.perm_P
+            for k in ("q_R", "q_P", "m1_R", "m2_R", "m1_P", "m2_P"):
+                setattr(st, k, np.zeros_like(getattr(st, k)))
+            st.t = 0
+    return st

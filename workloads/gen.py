@@ -2,7 +2,7 @@
 
 Every tensor is drawn from numpy's PCG64 seeded by SeedSequence([workload id,
 linear index, tensor id, ...]) with tensor ids 0 = W0, 1 = q_R, 2 = q_P, 3 = X,
-4 = dZ, 5 = perm_R, 6 = perm_P.  Matrices are drawn in fixed chunks of 512 rows,
+4 = dZ, 5 = perm_R, 6 = perm_P (and 7 = dq, 8, 9 = optimiser moments).  Matrices are drawn in fixed chunks of 512 rows,
 chunk c from SeedSequence([..., c]), so the values do not depend on how many
 threads fill them.  Values are drawn in float64 and rounded once to the storage
 type; bf16 tensors are returned as uint16 bit patterns so both consumers see
@@ -30,7 +30,7 @@ import numpy as np
 
 from .configs import Workload
 
-TENSOR_W0, TENSOR_QR, TENSOR_QP, TENSOR_X, TENSOR_DZ, TENSOR_PR, TENSOR_PP = range(7)
+TENSOR_W0, TENSOR_QR, TENSOR_QP, TENSOR_X, TENSOR_DZ, TENSOR_PR, TENSOR_PP, TENSOR_DQ, TENSOR_M1, TENSOR_M2 = range(10)
 
 
 def packed_len(b: int) -> int:
@@ -165,3 +165,28 @@ def custom_linear_inputs(
 
     wl = Workload("custom", 1000 + seed, (LinearShape("x", m, n),), b, T, act, w, q_std)
     return make_linear_inputs(wl, 0)
+
+
+def optimizer_inputs(lens, seed: int, q_std: float = 0.01, g_std: float = 4.0):
+    """Packed parameters, gradients and two moment arrays for sides of lens[i]
+    slots (float32): q ~ N(0, q_std^2), dq ~ N(0, g_std^2), first moment
+    ~ N(0, (g_std/3)^2), second moment g_std^2 (N(0, 1)^2 + 1/4), kept away
+    from zero like a running mean of squares.  Returns [(q, dq, m1, m2)]."""
+    out = []
+    for i, L in enumerate(lens):
+        wid = 3000 + seed
+        q = (_rng(wid, i, TENSOR_QR).standard_normal(L) * q_std).astype(np.float32)
+        dq = (_rng(wid, i, TENSOR_DQ).standard_normal(L) * g_std).astype(np.float32)
+        m1 = (_rng(wid, i, TENSOR_M1).standard_normal(L) * (g_std / 3.0)).astype(np.float32)
+        m2 = ((_rng(wid, i, TENSOR_M2).standard_normal(L) ** 2 + 0.25) * g_std**2).astype(np.float32)
+        out.append((q, dq, m1, m2))
+    return out
+
+
+def loop_batches(m: int, n: int, T: int, act: str, steps: int, seed: int):
+    """(X, dZ) storage arrays for `steps` training steps of one linear."""
+    wid = 4000 + seed
+    return [
+        (_act_matrix([wid, s, TENSOR_X, T], T, m, act), _act_matrix([wid, s, TENSOR_DZ, T], T, n, act))
+        for s in range(steps)
+    ]
