@@ -179,6 +179,7 @@ KERNEL_CLASSES = (  # kernel-name prefix -> class, as in --breakdown
     ("k_pack_dq", "CNP pack/unpack"),
     ("k_permute", "permutations"),
     ("k_inverse_perm", "permutations"),
+    ("k_adam<", "optimiser step"),
 )
 N_XCC = 8  # GRBM_GUI_ACTIVE is reported once per XCD; the counter CSV holds their sum
 
@@ -350,6 +351,8 @@ def main():
     ap.add_argument("--merge", metavar="WORKLOAD", nargs="?", const="llama13b_int8", default=None,
                     help="also time poetx_merge_reinit of every linear of WORKLOAD (default llama13b_int8) and "
                          "report it amortised over the workload's merge period")
+    ap.add_argument("--optimizer", action="store_true",
+                    help="end every step with the Adam step on all packed q (poetx_adam_step_batch)")
     ap.add_argument("--copy-probe", action="store_true",
                     help=f"run a {COPY_PROBE_BYTES >> 20} MiB device copy before the steps (counter calibration)")
     ap.add_argument("--summarize-classes", nargs=3, metavar=("MFMA_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -377,7 +380,7 @@ def main():
     import torch
 
     from orthogonal_reparameterized_cnp_amd import binding as B
-    from orthogonal_reparameterized_cnp_amd.layer import PoetxGroup, PoetxLinear
+    from orthogonal_reparameterized_cnp_amd.layer import PoetxAdam, PoetxGroup, PoetxLinear
     from workloads import WORKLOADS, make_linear_inputs
 
     B.lib()
@@ -414,6 +417,8 @@ def main():
     # one batch, and the chain rule to dq runs once for all sides after the
     # backward of the last linear (results bit-identical to per-linear calls).
     group = PoetxGroup(layers)
+    # Adam on every side's packed q (lr small enough that the timed steps stay near the start)
+    opt = PoetxAdam(layers, lr=1e-5)
 
     def step():
         group.build()
@@ -422,6 +427,8 @@ def main():
         for i in reversed(range(len(layers))):
             group.backward_dx(i, Xs[i], dZs[i], dXs[i], Y=Ys[i] if args.mode == "xout" else None)
         group.backward_q(dqs)
+        if args.optimizer:
+            opt.step(dqs)
 
     for _ in range(args.warmup):
         step()
@@ -473,6 +480,7 @@ def main():
             "b": wl.b,
             "weights": wl.w,
             "mode": args.mode,
+            "optimizer_in_step": "adam" if args.optimizer else None,
         },
         "tflops": total_f / (ms * 1e-3) / 1e12,
         "mfma_peak_frac": total_f / (ms * 1e-3) / 1e12 / peak,
@@ -493,9 +501,27 @@ def main():
         "wall_s_timed": wall,
     }
 
+    # the optimiser step on its own (outside the timed region): HBM-bound, 28 bytes per packed slot
+    B.poetx_timer_enable(B.POETX_KC_OPTIM)
+    B.poetx_timer_read()
+    opt.step(dqs)
+    torch.cuda.synchronize()
+    n_o, o_ms, _, o_bytes = B.poetx_timer_read()
+    B.poetx_timer_enable(B.POETX_KC_NONE)
+    result["optimizer_step"] = {
+        "kernel": "k_adam (Adam with decoupled decay on every side's packed q, one launch)",
+        "launches": n_o,
+        "ms": o_ms,
+        "slots": int(o_bytes / 28),
+        "algorithmic_gb": o_bytes / 1e9,
+        "gb_per_s": o_bytes / (o_ms * 1e-3) / 1e9 if o_ms > 0 else None,
+        "hbm_frac": o_bytes / (o_ms * 1e-3) / 8.0e12 if o_ms > 0 else None,
+    }
+
     if args.breakdown:
         for name, kc in (("gemm", B.POETX_KC_GEMM), ("apply", B.POETX_KC_APPLY), ("dgrad", B.POETX_KC_DGRAD),
-                         ("cnp", B.POETX_KC_CNP), ("permute", B.POETX_KC_PERMUTE)):
+                         ("cnp", B.POETX_KC_CNP), ("permute", B.POETX_KC_PERMUTE),
+                         ("optim", B.POETX_KC_OPTIM)):
             B.poetx_timer_enable(kc)
             B.poetx_timer_read()
             step()

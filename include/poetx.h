@@ -151,7 +151,8 @@ typedef enum {
   POETX_KC_APPLY = 2,   /* block-diagonal products over token rows */
   POETX_KC_DGRAD = 3,   /* block gradients summed over tokens */
   POETX_KC_CNP = 4,     /* CNP build and chain rule */
-  POETX_KC_PERMUTE = 5  /* permutation gathers */
+  POETX_KC_PERMUTE = 5, /* permutation gathers */
+  POETX_KC_OPTIM = 6    /* optimiser steps on the packed parameters */
 } poetx_kernel_class;
 
 /* Measurement support (not for use on a hot path).  While a class is enabled,
@@ -313,6 +314,46 @@ poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const 
  */
 poetx_status poetx_cnp_backward_batch(int32_t count, const float* const* q, const int32_t* d, int32_t b, int32_t dtype,
                                       void* dg, size_t dg_bytes, float* const* dq, void* stream);
+
+/* ------------------------------------------ optimiser step on packed q -- */
+
+/* Hyper-parameters of one Adam step with decoupled weight decay. */
+typedef struct {
+  float lr;           /* step size, finite and >= 0 */
+  float beta1;        /* decay of the first moment, in [0, 1) */
+  float beta2;        /* decay of the second moment, in [0, 1) */
+  float eps;          /* added to the root of the corrected second moment, > 0 */
+  float weight_decay; /* decoupled decay rate, finite (0 disables it) */
+  int64_t t;          /* 1-based number of steps since the moments were zero */
+} poetx_adam_params;
+
+/*
+ * One optimiser step on the packed parameters of `count` sides, in place, in
+ * as few launches as the sides allow (one per 32 sides).  The optimiser keeps
+ * state only for the packed half of each skew Q (zhichai.net POET-X blog,
+ * 第四斧 item 1); the pages do not name it, and the update is Adam (Kingma &
+ * Ba 2015) with decoupled weight decay (Loshchilov & Hutter 2019).  For every
+ * slot, in fp32, with g = dq[i][slot]:
+ *     m1 = beta1 m1 + (1 - beta1) g
+ *     m2 = beta2 m2 + (1 - beta2) g^2
+ *     q  = q - lr ( (m1 / (1 - beta1^t)) / (sqrt(m2 / (1 - beta2^t)) + eps) + weight_decay q )
+ * The bias corrections are formed in double on the host and rounded to fp32.
+ * Slots with g = 0 and zero moments change only by the decay term, so the
+ * dead slots of a partial block (dq = 0 there) stay 0 when q starts 0 there.
+ *   len          HOST array [count]: slots of side i (0 skips the side); for a
+ *                side of length d and block size b, ceil(d/b) * b(b-1)/2
+ *   q, m1, m2    HOST arrays [count] of device pointers to fp32 [len[i]],
+ *                read and overwritten (m1, m2: first and second moments)
+ *   dq           HOST array [count] of device pointers to fp32 [len[i]], read
+ *                only (e.g. written by poetx_linear_bwd)
+ * The four arrays of one side, and the arrays of different sides, must not
+ * overlap.  No workspace; 16-byte aligned pointers take the vector path.
+ *   count  1 .. POETX_MAX_SIDES; len[i] in [0, 2^36]
+ * Errors: POETX_E_NULL, POETX_E_SHAPE (count, len or a hyper-parameter out of
+ * range), POETX_E_HIP.
+ */
+poetx_status poetx_adam_step_batch(int32_t count, const int64_t* len, float* const* q, const float* const* dq,
+                                   float* const* m1, float* const* m2, const poetx_adam_params* hp, void* stream);
 
 #ifdef __cplusplus
 }

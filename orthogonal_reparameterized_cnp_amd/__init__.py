@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     PoetxError,
     desc,
     lib,
+    poetx_adam_step_batch,
     poetx_cnp_backward_batch,
     poetx_cnp_batch_workspace_size,
     poetx_cnp_build,

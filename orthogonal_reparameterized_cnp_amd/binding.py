@@ -24,7 +24,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "poetx.h")
 POETX_OK, POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_PERM, POETX_E_HIP, POETX_E_UNSUPPORTED = range(8)
 POETX_F32, POETX_BF16, POETX_I8 = 0, 1, 2
 POETX_OP_CNP, POETX_OP_FWD, POETX_OP_BWD, POETX_OP_MERGE = 0, 1, 2, 3
-POETX_KC_NONE, POETX_KC_GEMM, POETX_KC_APPLY, POETX_KC_DGRAD, POETX_KC_CNP, POETX_KC_PERMUTE = range(6)
+POETX_KC_NONE, POETX_KC_GEMM, POETX_KC_APPLY, POETX_KC_DGRAD, POETX_KC_CNP, POETX_KC_PERMUTE, POETX_KC_OPTIM = range(7)
 
 DTYPES = {"f32": POETX_F32, "bf16": POETX_BF16, "i8": POETX_I8}
 # what the forward saves: H and Xt; Xt only (H recomputed from it); Xt only (H taken back from Y)
@@ -46,6 +46,17 @@ class LayerDesc(ctypes.Structure):
         ("act_dtype", ctypes.c_int32),
         ("w_dtype", ctypes.c_int32),
         ("mode", ctypes.c_int32),
+    ]
+
+
+class AdamParams(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float),
+        ("beta1", ctypes.c_float),
+        ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("weight_decay", ctypes.c_float),
+        ("t", ctypes.c_int64),
     ]
 
 
@@ -98,6 +109,11 @@ _SIG = {
         ctypes.c_int,
         [ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, _P,
          ctypes.c_size_t, ctypes.POINTER(_P), _P],
+    ),
+    "poetx_adam_step_batch": (
+        ctypes.c_int,
+        [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
+         ctypes.POINTER(_P), ctypes.POINTER(AdamParams), _P],
     ),
 }
 
@@ -281,3 +297,14 @@ def poetx_linear_bwd_dx(dsc: LayerDesc, T: int, Y, dZ, perm_R, perm_P, Wt, g_R, 
 def poetx_cnp_backward_batch(q, d, b: int, dtype: int, dg, dg_bytes: int, dq, stream=None):
     _check(lib().poetx_cnp_backward_batch(len(d), _ptr_array(q), _i32_array(d), b, dtype, _ptr(dg), dg_bytes,
                                           _ptr_array(dq), _stream(stream)))
+
+
+# ------------------------------------------------- optimiser step on packed q ---
+def poetx_adam_step_batch(q, dq, m1, m2, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                          t: int, lens=None, stream=None):
+    """q, dq, m1, m2: per-side lists of fp32 device tensors; lens defaults to each q's numel()."""
+    if lens is None:
+        lens = [x.numel() for x in q]
+    hp = AdamParams(lr, beta1, beta2, eps, weight_decay, t)
+    _check(lib().poetx_adam_step_batch(len(lens), (ctypes.c_int64 * len(lens))(*lens), _ptr_array(q), _ptr_array(dq),
+                                       _ptr_array(m1), _ptr_array(m2), ctypes.byref(hp), _stream(stream)))

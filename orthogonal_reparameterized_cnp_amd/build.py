@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpoetx.so")
-SOURCES = ["poetx_kernels.hip", "poetx_cnp.hip", "poetx_api.hip"]
+SOURCES = ["poetx_kernels.hip", "poetx_cnp.hip", "poetx_optim.hip", "poetx_api.hip"]
 
 # Packed fp32 instructions are kept out of the device code (-packed-fp32-ops);
 # the host pass warns that it does not know the feature, which is harmless.

@@ -1,6 +1,7 @@
 // C ABI of libpoetx: argument validation, workspace planning and the order of
 // kernel launches for each call.  All arithmetic happens in the kernels of
 // poetx_kernels.hip.
+#include <cmath>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -287,7 +288,7 @@ poetx_status poetx_perm_from_seed(uint64_t seed, int32_t d, int32_t* out) {
 }
 
 poetx_status poetx_timer_enable(int32_t kernel_class) {
-  if (kernel_class < POETX_KC_NONE || kernel_class > POETX_KC_PERMUTE) return fail(POETX_E_SHAPE, "unknown kernel class");
+  if (kernel_class < POETX_KC_NONE || kernel_class > POETX_KC_OPTIM) return fail(POETX_E_SHAPE, "unknown kernel class");
   Timer& t = timer();
   std::lock_guard<std::mutex> g(t.mu);
   t.cls = kernel_class;
@@ -623,6 +624,29 @@ poetx_status poetx_merge_reinit(const poetx_layer_desc* desc, void* Wt, int32_t*
   PX_HIP(hipMemcpyAsync(perm_P, w.newP, (size_t)n * 4, hipMemcpyDeviceToDevice, s));
   PX_HIP(fill_zero(q_R, (size_t)nblocks(m, b) * packed_len(b) * 4, s));
   PX_HIP(fill_zero(q_P, (size_t)nblocks(n, b) * packed_len(b) * 4, s));
+  return POETX_OK;
+}
+
+poetx_status poetx_adam_step_batch(int32_t count, const int64_t* len, float* const* q, const float* const* dq,
+                                   float* const* m1, float* const* m2, const poetx_adam_params* hp, void* stream) {
+  if (count < 1 || count > POETX_MAX_SIDES) return fail(POETX_E_SHAPE, "count must be in [1, POETX_MAX_SIDES]");
+  if (!len || !q || !dq || !m1 || !m2 || !hp) return fail(POETX_E_NULL, "len, q, dq, m1, m2 and hp must be non-NULL");
+  if (!(std::isfinite(hp->lr) && hp->lr >= 0.f)) return fail(POETX_E_SHAPE, "lr must be finite and >= 0");
+  if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f && hp->beta2 >= 0.f && hp->beta2 < 1.f))
+    return fail(POETX_E_SHAPE, "beta1 and beta2 must be in [0, 1)");
+  if (!(std::isfinite(hp->eps) && hp->eps > 0.f)) return fail(POETX_E_SHAPE, "eps must be finite and > 0");
+  if (!std::isfinite(hp->weight_decay)) return fail(POETX_E_SHAPE, "weight_decay must be finite");
+  if (hp->t < 1) return fail(POETX_E_SHAPE, "t must be >= 1");
+  double slots = 0;
+  for (int i = 0; i < count; ++i) {
+    if (len[i] < 0 || len[i] > (int64_t(1) << 36)) return fail(POETX_E_SHAPE, "len[i] must be in [0, 2^36]");
+    if (len[i] > 0 && (!q[i] || !dq[i] || !m1[i] || !m2[i]))
+      return fail(POETX_E_NULL, "q[i], dq[i], m1[i] and m2[i] must be non-NULL when len[i] > 0");
+    slots += (double)len[i];
+  }
+  AdamHyper h{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->t};
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PX_TIMED(POETX_KC_OPTIM, 0, 28.0 * slots, adam_batch(count, len, q, dq, m1, m2, h, s));
   return POETX_OK;
 }
 

@@ -91,4 +91,15 @@ hipError_t store_weight(const float* M, int64_t ld, int rows, int n, int w_dt, v
                         const uint32_t* amax, float* wscale, hipStream_t s);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
 
+// Adam step with decoupled weight decay on `count` fp32 arrays in place:
+// side i updates len[i] slots of q[i], m1[i], m2[i] from the gradient g[i].
+// Sides are packed into launches of at most kAdamSidesPerLaunch.
+constexpr int kAdamSidesPerLaunch = 32;
+struct AdamHyper {
+  double lr, beta1, beta2, eps, weight_decay;
+  int64_t t;  // 1-based steps since the moments were zero
+};
+hipError_t adam_batch(int count, const int64_t* len, float* const* q, const float* const* g, float* const* m1,
+                      float* const* m2, const AdamHyper& hp, hipStream_t s);
+
 }  // namespace pxk

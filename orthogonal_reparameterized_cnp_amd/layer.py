@@ -6,6 +6,7 @@ done by libpoetx kernels.
 
 from __future__ import annotations
 
+import contextlib
 from typing import Optional
 
 import torch
@@ -204,3 +205,56 @@ class PoetxGroup:
         dq = [x for pair in dqs for x in pair]
         B.poetx_cnp_backward_batch(q, self.d, self.b, self.adt, self.dg, self.dg.numel(), dq, stream)
         return dqs
+
+
+class PoetxAdam:
+    """Optimiser state for the packed q of several linears, and the training
+    cadence around it: each step() moves every side's q by one Adam step with
+    decoupled weight decay (one poetx_adam_step_batch call for all sides);
+    every `merge_every` steps (0: never) the factors built from the updated q
+    are merged into each linear's weight with new permutations
+    (poetx_cnp_build, poetx_merge_reinit) and q and both moments restart from
+    zero, together with the bias-correction count.
+
+    merge_seeds(step, i) -> (seed_R, seed_P) gives the permutation seeds of
+    linear i at the merge after `step` steps.  The moments are cleared with a
+    torch fill on the given torch stream (None: the current stream).
+    """
+
+    def __init__(self, layers, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8, weight_decay: float = 0.0,
+                 merge_every: int = 0, merge_seeds=None):
+        if not layers:
+            raise ValueError("no linears")
+        self.layers = list(layers)
+        self.lr, self.beta1, self.beta2, self.eps, self.weight_decay = lr, betas[0], betas[1], eps, weight_decay
+        self.merge_every = merge_every
+        self.merge_seeds = merge_seeds or (lambda step, i: ((step << 16) | (2 * i), (step << 16) | (2 * i + 1)))
+        qs = self.params()
+        self.m1 = [torch.zeros_like(q) for q in qs]
+        self.m2 = [torch.zeros_like(q) for q in qs]
+        self.t = 0  # steps since the last restart
+        self.steps = 0  # steps taken
+
+    def params(self):
+        return [x for l in self.layers for x in (l.q_R, l.q_P)]
+
+    def step(self, dqs, stream=None) -> bool:
+        """dqs: [(dq_R, dq_P)] per linear.  Returns True when this step ended with a merge."""
+        dq = [x for pair in dqs for x in pair]
+        if len(dq) != len(self.m1):
+            raise ValueError("one (dq_R, dq_P) pair per linear")
+        self.t += 1
+        self.steps += 1
+        B.poetx_adam_step_batch(self.params(), dq, self.m1, self.m2, self.lr, self.beta1, self.beta2, self.eps,
+                                self.weight_decay, self.t, stream=stream)
+        if not (self.merge_every and self.steps % self.merge_every == 0):
+            return False
+        for i, lay in enumerate(self.layers):
+            lay.build(stream)
+            seed_R, seed_P = self.merge_seeds(self.steps, i)
+            lay.merge_reinit(seed_R, seed_P, stream)
+        with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+            for m in self.m1 + self.m2:
+                m.zero_()
+        self.t = 0
+        return True

@@ -162,3 +162,27 @@ def test_batched_cnp_validation(L):
     assert bb(_pp(FAKE, FAKE), need - 1) == B.POETX_E_WORKSPACE
     assert L.poetx_cnp_backward_batch(2, _pp(FAKE, FAKE), _ii(256, 96), 32, f32, None, need, _pp(FAKE, FAKE),
                                       None) == B.POETX_E_NULL
+
+
+def test_adam_validation(L):
+    """Every rejected call returns before any launch (no GPU needed)."""
+    ll = lambda *xs: (ctypes.c_int64 * len(xs))(*xs)
+    hp = lambda **kw: B.AdamParams(**{**dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, t=1), **kw})
+    four = [_pp(FAKE, FAKE) for _ in range(4)]
+    call = lambda n, lens, arrs, h: L.poetx_adam_step_batch(n, lens, *arrs, ctypes.byref(h) if h else None, None)
+    assert call(0, ll(10, 10), four, hp()) == B.POETX_E_SHAPE
+    assert L.poetx_adam_step_batch(65, ll(*[1] * 65), *[_pp(*[FAKE] * 65)] * 4, ctypes.byref(hp()), None) == \
+        B.POETX_E_SHAPE
+    assert call(2, ll(10, 10), four, None) == B.POETX_E_NULL
+    assert call(2, None, four, hp()) == B.POETX_E_NULL
+    assert call(2, ll(10, 10), [four[0], None, four[2], four[3]], hp()) == B.POETX_E_NULL
+    assert call(2, ll(10, 10), [four[0], _pp(FAKE, None), four[2], four[3]], hp()) == B.POETX_E_NULL
+    assert call(2, ll(10, -1), four, hp()) == B.POETX_E_SHAPE
+    assert call(2, ll(10, (1 << 36) + 1), four, hp()) == B.POETX_E_SHAPE
+    for bad in (dict(t=0), dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0), dict(lr=-1.0), dict(lr=float("nan")),
+                dict(weight_decay=float("inf")), dict(beta1=float("nan"))):
+        assert call(2, ll(10, 10), four, hp(**bad)) == B.POETX_E_SHAPE, bad
+    assert call(2, ll(10, 10), four, hp(t=0)) == B.POETX_E_SHAPE and "t must be" in B.poetx_last_error()
+    assert B.POETX_KC_OPTIM == 6 and L.poetx_timer_enable(B.POETX_KC_OPTIM) == B.POETX_OK
+    assert L.poetx_timer_enable(7) == B.POETX_E_SHAPE
+    assert L.poetx_timer_enable(0) == B.POETX_OK

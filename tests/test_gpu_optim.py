@@ -1,0 +1,165 @@
+"""GPU parity of the optimiser step on packed q (poetx_adam_step_batch) and of
+the training loop around it (steps, merge, restart; layer.PoetxAdam) against
+the fp64 oracle, on seeded inputs.
+
+Bounds:
+  * one Adam step in fp32: each slot goes through about ten roundings of
+    relative size 2^-24, and a moment that cancels (beta m against (1 - beta) g)
+    has an error relative to its terms, not to itself.  Over three chained
+    steps |gpu - ref| <= 2e-6 (|ref| + max |ref|) per array leaves a margin of
+    about three.  The hyper-parameters are rounded to fp32 before the oracle
+    sees them, as the library receives them.
+  * slots that start at zero with a zero gradient and zero moments: bit-exact 0.
+  * the loop: the layer tolerances (max-abs / Frobenius 1e-5 fp32, 2e-2 bf16)
+    for q, both moments and the stored weight; permutations bit-exact.  Adam's
+    normalisation multiplies the relative error of a slot's gradient by about
+    |g| / (|g| + eps), so the loop runs with eps near the gradients' scale
+    (their RMS is about 20 at these shapes); with eps = 1e-8 a slot whose
+    gradient is near zero flips its step by up to 2 lr.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from orthogonal_reparameterized_cnp_amd import binding as B
+from orthogonal_reparameterized_cnp_amd.layer import PoetxAdam
+from tests.poetx_cases import assert_close, dev, host, make_layer
+from workloads.gen import custom_linear_inputs, loop_batches, optimizer_inputs
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+f32 = lambda x: float(np.float32(x))
+
+
+def _hp32(**kw):
+    hp = O.AdamHP(**kw)
+    return O.AdamHP(*(f32(getattr(hp, k)) for k in ("lr", "beta1", "beta2", "eps", "weight_decay")))
+
+
+def _side_buffers(lens, offset: int):
+    """Per-side fp32 device views; offset 1 makes every pointer 4 mod 16 (scalar path)."""
+    bufs = []
+    for L in lens:
+        views = []
+        for _ in range(4):
+            base = torch.empty(L + 8, dtype=torch.float32, device="cuda")
+            views.append(base[offset : offset + L])
+        bufs.append(views)
+    return bufs
+
+
+def _close(name, gpu, ref):
+    d = np.abs(gpu - ref)
+    lim = 2e-6 * (np.abs(ref) + np.abs(ref).max(initial=0.0))
+    worst = float(np.max(d / np.where(lim > 0, lim, 1.0), initial=0.0))
+    print(f"  {name}: worst |d| / bound {worst:.3f}", flush=True)
+    assert np.all(d <= lim), f"{name}: max |d| {d.max():.3e}"
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+@pytest.mark.parametrize("lens", [[3968, 97920, 1, 7, 4093, 0], [130816 * 2 + 5]])
+def test_adam_step_matches_oracle(lens, offset):
+    print(f"adam lens={lens} offset={offset}", flush=True)
+    hp = _hp32(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.05)
+    init = optimizer_inputs(lens, seed=0)
+    bufs = _side_buffers(lens, offset)
+    for (q, _, m1, m2), (bq, _, bm1, bm2) in zip(init, bufs):
+        for src, dst in ((q, bq), (m1, bm1), (m2, bm2)):
+            dst.copy_(torch.from_numpy(src))
+    ref = [[x.astype(np.float64) for x in (q, m1, m2)] for q, _, m1, m2 in init]
+    for t in (1, 2, 3):
+        grads = [g for _, g, _, _ in optimizer_inputs(lens, seed=t)]
+        for g, bb in zip(grads, bufs):
+            bb[1].copy_(torch.from_numpy(g))
+        B.poetx_adam_step_batch([b[0] for b in bufs], [b[1] for b in bufs], [b[2] for b in bufs],
+                                [b[3] for b in bufs], hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, t)
+        ref = [list(O.adam_step(r[0], g.astype(np.float64), r[1], r[2], t, hp)) for r, g in zip(ref, grads)]
+        torch.cuda.synchronize()
+        for i, (bb, r) in enumerate(zip(bufs, ref)):
+            if lens[i] == 0:
+                continue
+            for name, k, j in (("q", 0, 0), ("m1", 2, 1), ("m2", 3, 2)):
+                _close(f"t={t} side {i} {name}", bb[k].cpu().numpy().astype(np.float64), r[j])
+
+
+def test_adam_many_sides_and_dead_slots():
+    """40 sides (two launches of the side table); a partial block whose dead
+    slots start at zero stays exactly zero under decay."""
+    d, b = 100, 32  # 4 blocks, the last of 4 rows
+    L = -(-d // b) * O.packed_len(b)
+    lens = [L] + [37 * (i + 1) for i in range(39)]
+    hp = _hp32(lr=2e-3, beta1=0.8, beta2=0.99, eps=1e-6, weight_decay=0.1)
+    init = optimizer_inputs(lens, seed=7)
+    dead = np.zeros(L, dtype=bool)
+    dead[3 * O.packed_len(b):] = True
+    for i in range(4):
+        for j in range(i + 1, b):
+            if j < 4:
+                dead[3 * O.packed_len(b) + O.packed_index(i, j, b)] = False
+    for a in init[0]:
+        a[dead] = 0.0
+    bufs = [[torch.from_numpy(x).cuda() for x in side] for side in init]
+    B.poetx_adam_step_batch([x[0] for x in bufs], [x[1] for x in bufs], [x[2] for x in bufs], [x[3] for x in bufs],
+                            hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, 1)
+    torch.cuda.synchronize()
+    for i, (side, x) in enumerate(zip(init, bufs)):
+        rq, _, rm2 = O.adam_step(*(a.astype(np.float64) for a in side), 1, hp)
+        _close(f"side {i} q", x[0].cpu().numpy().astype(np.float64), rq)
+        _close(f"side {i} m2", x[3].cpu().numpy().astype(np.float64), rm2)
+    for k in (0, 2, 3):
+        assert not bufs[0][k].cpu().numpy()[dead].any(), "dead slots moved"
+
+
+@pytest.mark.parametrize(
+    "m,n,b,T,act,w,eps",
+    [(60, 40, 16, 48, "f32", "f32", 10.0), (96, 80, 32, 64, "bf16", "bf16", 10.0), (96, 80, 32, 64, "bf16", "i8", 10.0)],
+)
+def test_train_loop_matches_oracle(m, n, b, T, act, w, eps):
+    """Five steps with a merge every second step: q, both moments, the stored
+    weight and the permutations after the loop, against the oracle's loop."""
+    print(f"loop {m}x{n} b={b} T={T} {act}/{w}", flush=True)
+    steps, every = 5, 2
+    inp = custom_linear_inputs(m, n, b, T, act, w, 0.02, seed=21)
+    hp = _hp32(lr=0.01, beta1=0.9, beta2=0.99, eps=eps, weight_decay=0.01)
+    seeds = lambda s, i=0: ((s << 16) | 1, (s << 16) | 2)
+    lay = make_layer(inp)
+    opt = PoetxAdam([lay], lr=hp.lr, betas=(hp.beta1, hp.beta2), eps=hp.eps, weight_decay=hp.weight_decay,
+                    merge_every=every, merge_seeds=seeds)
+    batches = loop_batches(m, n, T, act, steps, seed=3)
+    merged = []
+    for X, dZ in batches:
+        lay.build()
+        Xd = dev(X, act)
+        lay.forward(Xd)
+        _, dq_R, dq_P = lay.backward(Xd, dev(dZ, act))
+        merged.append(opt.step([(dq_R, dq_P)]))
+    torch.cuda.synchronize()
+    assert merged == [False, True, False, True, False] and opt.t == 1
+
+    W = O.to_f64(inp.W0, inp.w, inp.w_scale)
+    st = O.TrainState(O.premerge(W, inp.perm_R, inp.perm_P), inp.perm_R, inp.perm_P,
+                      inp.q_R.astype(np.float64), inp.q_P.astype(np.float64),
+                      *[np.zeros_like(x, dtype=np.float64) for x in (inp.q_R, inp.q_R, inp.q_P, inp.q_P)], 0)
+    ob = [(O.to_f64(X, act), O.to_f64(dZ, act)) for X, dZ in batches]
+    ref = O.train_steps(st, b, w, ob, hp, every, seeds)
+
+    assert np.array_equal(lay.perm_R.cpu().numpy(), ref.perm_R)
+    assert np.array_equal(lay.perm_P.cpu().numpy(), ref.perm_P)
+    kind = "f32" if act == "f32" else "bf16"
+    for name, got, want in (("q_R", lay.q_R, ref.q_R), ("q_P", lay.q_P, ref.q_P), ("m1_R", opt.m1[0], ref.m1_R),
+                            ("m2_R", opt.m2[0], ref.m2_R), ("m1_P", opt.m1[1], ref.m1_P),
+                            ("m2_P", opt.m2[1], ref.m2_P)):
+        assert_close(name, host(got, "f32"), want, kind)
+    Wv = lay.weight_values()[:, :n]
+    if w == "i8":
+        Wg = Wv.cpu().numpy().astype(np.float64) * lay.weight_scales()[:n].cpu().numpy().astype(np.float64)[None, :]
+    else:
+        Wg = host(Wv.contiguous(), w)
+    assert_close("W~", Wg, ref.Wt, kind)
