@@ -21,9 +21,11 @@ Conventions (where the pages leave the step open, the plainest reading):
     y = (R W0 P)^T x of [PN] 整体框架 reads Y = X R W0 P for X in R^{T x m}.
   * A permutation is an index array pi with Psi[i, pi[i]] = 1, so
     X Psi^T = X[:, pi] and (Z Psi)[:, pi[i]] = Z[:, i].
-  * One block-stochastic factor per side ([PN] 关键设计 1, c = 1):
-    R = Psi_R^T Diag(G_R^0 .. G_R^{nb-1}) Psi_R, nb = ceil(m / b).  A partial
-    last block of r < b rows is its own r x r CNP block.
+  * One block-stochastic factor per side ([PN] 关键设计 1, c = 1) in the
+    layer calls: R = Psi_R^T Diag(G_R^0 .. G_R^{nb-1}) Psi_R, nb = ceil(m / b).
+    A partial last block of r < b rows is its own r x r CNP block.  Products
+    of c factors, block-stochastic or fully stochastic (I + D(S)(G - I)D(S)^T
+    for an ordered b-subset S, D(S)[S[j], j] = 1), are spo_* and chain_*.
   * Each block G is the Cayley-Neumann form with k = 3 ([PN] 关键设计 2, [ZC]
     第四斧 item 2): G = I + 2(Q + Q^2 + Q^3) + Q^4 of a skew-symmetric Q.
   * Q is stored as its strict upper triangle in row-major order with the full
@@ -519,3 +521,98 @@ def train_steps(state: TrainState, b: int, w: str, batches, hp: AdamHP, merge_ev
                 setattr(st, k, np.zeros_like(getattr(st, k)))
             st.t = 0
     return st
+
+
+# ----------------------------------------------------------------------------
+# more than one SPO factor per side, and the fully stochastic factor
+# ([PN] 关键设计 1: R is a product of c primitives, each block-stochastic
+#  Psi^T Diag(G^1 .. G^nb) Psi or fully stochastic I + D(S)(G - I)D(S)^T)
+# ----------------------------------------------------------------------------
+
+
+@dataclass
+class SpoFactor:
+    kind: str  # "block": idx is a permutation of all d columns; "full": idx is an ordered b-subset
+    idx: np.ndarray
+    q: np.ndarray  # packed parameters [nb, b(b-1)/2]; nb = 1 for "full"
+    d: int
+    b: int
+
+    def blocks(self) -> List[np.ndarray]:
+        return side_G(self.q, self.d if self.kind == "block" else self.b, self.b)
+
+
+def selection_matrix(S: np.ndarray, d: int) -> np.ndarray:
+    """D(S) in R^{d x b}: column j is the unit vector e_{S[j]}."""
+    D = np.zeros((d, len(S)))
+    D[np.asarray(S), np.arange(len(S))] = 1.0
+    return D
+
+
+def spo_dense(f: SpoFactor) -> np.ndarray:
+    """The factor as an explicit d x d matrix (tiny sizes)."""
+    if f.kind == "block":
+        return dense_factor(f.idx, f.blocks())
+    D = selection_matrix(f.idx, f.d)
+    return np.eye(f.d) + D @ (f.blocks()[0] - np.eye(f.b)) @ D.T
+
+
+def spo_forward(X: np.ndarray, f: SpoFactor):
+    """Row form Y = X F of one factor; also returns the gathered input it keeps.
+    block: Xt = X[:, pi], Y[:, pi] = Xt Diag(G).  full: Xt = X[:, S], Y = X with
+    Y[:, S] = Xt G (the other columns pass through)."""
+    Xt = X[:, f.idx]
+    if f.kind == "block":
+        Y = np.empty_like(X)
+        Y[:, f.idx] = apply_blocks(Xt, f.blocks())
+    else:
+        Y = np.array(X, dtype=np.float64)
+        Y[:, f.idx] = Xt @ f.blocks()[0]
+    return Y, Xt
+
+
+def spo_backward(Xt: np.ndarray, dY: np.ndarray, f: SpoFactor):
+    """Exact gradients of spo_forward: dX = dY F^T and the packed dq of the
+    factor's blocks (dG_k = Xt_k^T dY[:, idx]_k, then the CNP chain rule)."""
+    dA = dY[:, f.idx]
+    G = f.blocks()
+    if f.kind == "block":
+        dG = [Xt[:, s : s + r].T @ dA[:, s : s + r] for s, r in side_blocks(f.d, f.b)]
+        dX = np.empty_like(dY)
+        dX[:, f.idx] = apply_blocks(dA, G, transpose=True)
+        return dX, cnp_grad_packed(f.q, dG, f.d, f.b)
+    dX = np.array(dY, dtype=np.float64)
+    dX[:, f.idx] = dA @ G[0].T
+    return dX, cnp_grad_packed(f.q, [Xt.T @ dA], f.b, f.b)
+
+
+def chain_forward(X, W, R: Sequence[SpoFactor], P: Sequence[SpoFactor]) -> np.ndarray:
+    """Y = X R_1 .. R_c W0 P_1 .. P_c, one factor at a time in row form."""
+    Y = X
+    for f in R:
+        Y = spo_forward(Y, f)[0]
+    Y = Y @ W
+    for f in P:
+        Y = spo_forward(Y, f)[0]
+    return Y
+
+
+def chain_backward(X, dZ, W, R: Sequence[SpoFactor], P: Sequence[SpoFactor]):
+    """Exact dX and the packed dq of every factor (lists in the order of R and P)."""
+    ins_R, Y = [], X
+    for f in R:
+        Y, Xt = spo_forward(Y, f)
+        ins_R.append(Xt)
+    Y = Y @ W
+    ins_P = []
+    for f in P:
+        Y, Xt = spo_forward(Y, f)
+        ins_P.append(Xt)
+    g, dq_P = dZ, [None] * len(P)
+    for k in reversed(range(len(P))):
+        g, dq_P[k] = spo_backward(ins_P[k], g, P[k])
+    g = g @ W.T
+    dq_R = [None] * len(R)
+    for k in reversed(range(len(R))):
+        g, dq_R[k] = spo_backward(ins_R[k], g, R[k])
+    return g, dq_R, dq_P
