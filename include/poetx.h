@@ -315,6 +315,68 @@ poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const 
 poetx_status poetx_cnp_backward_batch(int32_t count, const float* const* q, const int32_t* d, int32_t b, int32_t dtype,
                                       void* dg, size_t dg_bytes, float* const* dq, void* stream);
 
+/* ---------------------------------- one SPO factor (c > 1, fully stochastic) -- */
+
+/*
+ * The layer calls above hold one block-stochastic factor per side.  The POET
+ * notes ("Reparameterized LLM Training via Orthogonal Equivalence
+ * Transformation", 关键设计 1) build R and P as products of c primitives, each
+ * either block-stochastic, Psi^T Diag(G^1, ..., G^nb) Psi, or fully
+ * stochastic, I + D(S) (G - I_b) D(S)^T for an ordered subset S of b of the d
+ * coordinates (D(S)[S[j]][j] = 1).  The calls below apply one such factor to
+ * token rows, Y = X F, and take its backward; a product of c factors is c
+ * calls in order (Y = X R_1 ... R_c W0 P_1 ... P_c with the innermost R_c and
+ * P_1 inside poetx_linear_fwd).
+ */
+typedef enum {
+  POETX_SPO_BLOCK = 0, /* idx: a permutation of the d columns; ceil(d/b) blocks */
+  POETX_SPO_FULL = 1   /* idx: b distinct columns in [0, d), in the order of G's rows; one block */
+} poetx_spo_kind;
+
+typedef struct {
+  int32_t d;         /* columns of the activation, 1 .. 2^20 */
+  int32_t b;         /* block size, 2 .. 1024; FULL: also the subset size, b <= d */
+  int32_t kind;      /* poetx_spo_kind */
+  int32_t act_dtype; /* POETX_F32 or POETX_BF16 (X, Y, dY, dX and G) */
+} poetx_spo_desc;
+
+/* Bytes of the state poetx_spo_fwd saves for the backward: the gathered input
+ * X[:, idx], [T][round_up(d_eff, 64)] with d_eff = d (BLOCK) or b (FULL);
+ * 0 for invalid arguments. */
+size_t poetx_spo_saved_bytes(const poetx_spo_desc* desc, int64_t T);
+/* Workspace bytes of poetx_spo_fwd (op = POETX_OP_FWD) or poetx_spo_bwd
+ * (POETX_OP_BWD); 0 for invalid arguments. */
+size_t poetx_spo_workspace_size(const poetx_spo_desc* desc, int64_t T, int32_t op);
+
+/*
+ * Y = X F for one factor, row form:
+ *   BLOCK: Xt = X[:, idx], Y[:, idx] = Xt Diag(G)
+ *   FULL:  Xt = X[:, idx], Y = X except Y[:, idx] = Xt G
+ *   X, Y   [T][d] contiguous, act_dtype; Y may be X (in place)
+ *   idx    device int32: [d] permutation (BLOCK) or [b] distinct columns (FULL)
+ *   G      the blocks from poetx_cnp_build(q, d_eff, b, act_dtype, G, ...)
+ *   saved  >= poetx_spo_saved_bytes(desc, T); keeps Xt for poetx_spo_bwd
+ *   ws     >= poetx_spo_workspace_size(desc, T, POETX_OP_FWD)
+ * Errors: POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_HIP.
+ */
+poetx_status poetx_spo_fwd(const poetx_spo_desc* desc, int64_t T, const void* X, const int32_t* idx, const void* G,
+                           void* Y, void* saved, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of poetx_spo_fwd: dX = dY F^T, and the packed gradient of the
+ * factor's q (the block gradients Xt_k^T dY[:, idx]_k summed over all T rows,
+ * then the CNP chain rule and skew projection as in poetx_linear_bwd).
+ *   dY, dX  [T][d] contiguous, act_dtype; dX may be dY (in place)
+ *   q       fp32 [nb_eff][b(b-1)/2], the parameters G was built from
+ *   saved   the state written by the forward of the same rows
+ *   dq      fp32 [nb_eff][b(b-1)/2], overwritten (dead slots of a partial block: 0)
+ *   ws      >= poetx_spo_workspace_size(desc, T, POETX_OP_BWD)
+ * Errors: as for poetx_spo_fwd.
+ */
+poetx_status poetx_spo_bwd(const poetx_spo_desc* desc, int64_t T, const void* dY, const int32_t* idx, const void* G,
+                           const float* q, const void* saved, void* dX, float* dq, void* ws, size_t ws_bytes,
+                           void* stream);
+
 /* ------------------------------------------ optimiser step on packed q -- */
 
 /* Hyper-parameters of one Adam step with decoupled weight decay. */

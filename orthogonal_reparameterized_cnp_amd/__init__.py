@@ -34,6 +34,10 @@ from .binding import (  # noqa: F401
     poetx_perm_from_seed,
     poetx_premerge,
     poetx_saved_bytes,
+    poetx_spo_bwd,
+    poetx_spo_fwd,
+    poetx_spo_saved_bytes,
+    poetx_spo_workspace_size,
     poetx_version,
     poetx_weight_bytes,
     poetx_workspace_size,

@@ -49,6 +49,19 @@ class LayerDesc(ctypes.Structure):
     ]
 
 
+POETX_SPO_BLOCK, POETX_SPO_FULL = 0, 1
+SPO_KINDS = {"block": POETX_SPO_BLOCK, "full": POETX_SPO_FULL}
+
+
+class SpoDesc(ctypes.Structure):
+    _fields_ = [
+        ("d", ctypes.c_int32),
+        ("b", ctypes.c_int32),
+        ("kind", ctypes.c_int32),
+        ("act_dtype", ctypes.c_int32),
+    ]
+
+
 class AdamParams(ctypes.Structure):
     _fields_ = [
         ("lr", ctypes.c_float),
@@ -110,6 +123,10 @@ _SIG = {
         [ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, _P,
          ctypes.c_size_t, ctypes.POINTER(_P), _P],
     ),
+    "poetx_spo_saved_bytes": (ctypes.c_size_t, [ctypes.POINTER(SpoDesc), ctypes.c_int64]),
+    "poetx_spo_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(SpoDesc), ctypes.c_int64, ctypes.c_int32]),
+    "poetx_spo_fwd": (ctypes.c_int, [ctypes.POINTER(SpoDesc), ctypes.c_int64] + [_P] * 6 + [ctypes.c_size_t, _P]),
+    "poetx_spo_bwd": (ctypes.c_int, [ctypes.POINTER(SpoDesc), ctypes.c_int64] + [_P] * 8 + [ctypes.c_size_t, _P]),
     "poetx_adam_step_batch": (
         ctypes.c_int,
         [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
@@ -308,3 +325,26 @@ def poetx_adam_step_batch(q, dq, m1, m2, lr: float, beta1: float, beta2: float, 
     hp = AdamParams(lr, beta1, beta2, eps, weight_decay, t)
     _check(lib().poetx_adam_step_batch(len(lens), (ctypes.c_int64 * len(lens))(*lens), _ptr_array(q), _ptr_array(dq),
                                        _ptr_array(m1), _ptr_array(m2), ctypes.byref(hp), _stream(stream)))
+
+
+# ------------------------------------------------------------ one SPO factor ---
+def spo_desc(d: int, b: int, kind: str, act: str) -> SpoDesc:
+    return SpoDesc(d, b, SPO_KINDS[kind], DTYPES[act])
+
+
+def poetx_spo_saved_bytes(dsc: SpoDesc, T: int) -> int:
+    return lib().poetx_spo_saved_bytes(ctypes.byref(dsc), T)
+
+
+def poetx_spo_workspace_size(dsc: SpoDesc, T: int, op: int) -> int:
+    return lib().poetx_spo_workspace_size(ctypes.byref(dsc), T, op)
+
+
+def poetx_spo_fwd(dsc: SpoDesc, T: int, X, idx, G, Y, saved, ws, ws_bytes: int, stream=None):
+    _check(lib().poetx_spo_fwd(ctypes.byref(dsc), T, _ptr(X), _ptr(idx), _ptr(G), _ptr(Y), _ptr(saved), _ptr(ws),
+                               ws_bytes, _stream(stream)))
+
+
+def poetx_spo_bwd(dsc: SpoDesc, T: int, dY, idx, G, q, saved, dX, dq, ws, ws_bytes: int, stream=None):
+    _check(lib().poetx_spo_bwd(ctypes.byref(dsc), T, _ptr(dY), _ptr(idx), _ptr(G), _ptr(q), _ptr(saved), _ptr(dX),
+                               _ptr(dq), _ptr(ws), ws_bytes, _stream(stream)))

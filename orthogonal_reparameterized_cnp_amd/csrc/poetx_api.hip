@@ -627,6 +627,145 @@ poetx_status poetx_merge_reinit(const poetx_layer_desc* desc, void* Wt, int32_t*
   return POETX_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+int spo_d_eff(const poetx_spo_desc* d) { return d->kind == POETX_SPO_BLOCK ? d->d : d->b; }
+
+poetx_status check_spo(const poetx_spo_desc* d, int64_t T) {
+  if (!d) return fail(POETX_E_NULL, "desc is NULL");
+  if (d->d < 1 || d->d > kMaxDim) return fail(POETX_E_SHAPE, "d must be in [1, 2^20]");
+  if (d->b < 2 || d->b > 1024) return fail(POETX_E_SHAPE, "b must be in [2, 1024]");
+  if (d->kind != POETX_SPO_BLOCK && d->kind != POETX_SPO_FULL) return fail(POETX_E_SHAPE, "kind must be BLOCK or FULL");
+  if (d->kind == POETX_SPO_FULL && d->b > d->d) return fail(POETX_E_SHAPE, "a FULL factor needs b <= d");
+  if (nblocks(spo_d_eff(d), d->b) > 65535) return fail(POETX_E_SHAPE, "at most 65535 blocks");
+  if (d->act_dtype != POETX_F32 && d->act_dtype != POETX_BF16) return fail(POETX_E_DTYPE, "act_dtype must be F32 or BF16");
+  if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
+  return POETX_OK;
+}
+
+struct SpoWs {
+  void *A, *B;  // fwd: A = Xt Diag(G); bwd: A = dY[:, idx], B = dXt
+  void* cnp;
+  float* part;
+  int32_t* inv;
+};
+template <class P> SpoWs plan_spo(P& p, const poetx_spo_desc* d, int64_t T, bool bwd) {
+  const int de = spo_d_eff(d), nb = nblocks(de, d->b);
+  const size_t mat = (size_t)T * lead(de) * dt_size(d->act_dtype);
+  SpoWs w{};
+  w.A = p.template take<char>(mat);
+  w.inv = d->kind == POETX_SPO_BLOCK ? p.template take<int32_t>((size_t)d->d * 4) : nullptr;
+  if (bwd) {
+    w.B = p.template take<char>(mat);
+    w.cnp = p.template take<char>(cnp_grad_bytes(d->act_dtype, nb, d->b));
+    w.part = p.template take<float>(block_grads_part_bytes(d->act_dtype, (int)T, nb, d->b));
+  }
+  return w;
+}
+
+// out = in except out[:, idx] = src (FULL), or out = src[:, idx^-1] (BLOCK)
+poetx_status spo_place(const poetx_spo_desc* d, int rows, const void* in, const void* src, const int32_t* idx,
+                       const SpoWs& w, void* out, hipStream_t s) {
+  const int at = d->act_dtype, de = spo_d_eff(d);
+  const double es = (double)dt_size(at);
+  if (rows <= 0) return POETX_OK;
+  if (d->kind == POETX_SPO_BLOCK) {
+    PX_HIP(inverse_perm(idx, d->d, w.inv, s));
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * d->d * es,
+             permute(at, src, lead(de), nullptr, w.inv, out, d->d, rows, d->d, d->d, s));
+    return POETX_OK;
+  }
+  if (out != in) {
+    const size_t row = (size_t)d->d * dt_size(at);
+    PX_HIP(hipMemcpy2DAsync(out, row, in, row, row, (size_t)rows, hipMemcpyDeviceToDevice, s));
+  }
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * de * es,
+           scatter_cols(at, src, lead(de), rows, de, idx, out, d->d, d->d, s));
+  return POETX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t poetx_spo_saved_bytes(const poetx_spo_desc* desc, int64_t T) {
+  if (check_spo(desc, T) != POETX_OK) return 0;
+  return (size_t)T * lead(spo_d_eff(desc)) * dt_size(desc->act_dtype);
+}
+
+size_t poetx_spo_workspace_size(const poetx_spo_desc* desc, int64_t T, int32_t op) {
+  if (check_spo(desc, T) != POETX_OK || (op != POETX_OP_FWD && op != POETX_OP_BWD)) return 0;
+  Plan p;
+  plan_spo(p, desc, T, op == POETX_OP_BWD);
+  return p.off;
+}
+
+poetx_status poetx_spo_fwd(const poetx_spo_desc* desc, int64_t T, const void* X, const int32_t* idx, const void* G,
+                           void* Y, void* saved, void* ws, size_t ws_bytes, void* stream) {
+  poetx_status st = check_spo(desc, T);
+  if (st != POETX_OK) return st;
+  if (T == 0) return POETX_OK;
+  if (!X || !idx || !G || !Y || !saved) return fail(POETX_E_NULL, "a required pointer is NULL");
+  Plan p;
+  plan_spo(p, desc, T, false);
+  st = check_ws(ws, ws_bytes, p.off);
+  if (st != POETX_OK) return st;
+  Plan pq;
+  pq.base = reinterpret_cast<char*>(ws);
+  const SpoWs w = plan_spo(pq, desc, T, false);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int at = desc->act_dtype, de = spo_d_eff(desc), b = desc->b, rows = (int)T;
+  const int64_t ld = lead(de);
+  const double es = (double)dt_size(at);
+  const char* g1 = reinterpret_cast<const char*>(G) + g_slice(de, b, at);  // (G - I)^T
+  // Xt = X[:, idx] (saved), A = Xt Diag(G), then placed back into Y
+  PX_TIMED(POETX_KC_PERMUTE, 0, (double)rows * (desc->d + de) * es,
+           permute(at, X, desc->d, nullptr, idx, saved, ld, rows, desc->d, de, s));
+  PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(de, b), 2.0 * rows * de * es + g_slice(de, b, at),
+           apply(at, at, saved, ld, rows, de, b, at, g1, nullptr, at, w.A, ld, s));
+  return spo_place(desc, rows, X, w.A, idx, w, Y, s);
+}
+
+poetx_status poetx_spo_bwd(const poetx_spo_desc* desc, int64_t T, const void* dY, const int32_t* idx, const void* G,
+                           const float* q, const void* saved, void* dX, float* dq, void* ws, size_t ws_bytes,
+                           void* stream) {
+  poetx_status st = check_spo(desc, T);
+  if (st != POETX_OK) return st;
+  if (!idx || !G || !q || !dq) return fail(POETX_E_NULL, "a required pointer is NULL");
+  if (T > 0 && (!dY || !saved || !dX)) return fail(POETX_E_NULL, "a required pointer is NULL");
+  Plan p;
+  plan_spo(p, desc, T, true);
+  st = check_ws(ws, ws_bytes, p.off);
+  if (st != POETX_OK) return st;
+  Plan pq;
+  pq.base = reinterpret_cast<char*>(ws);
+  const SpoWs w = plan_spo(pq, desc, T, true);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int at = desc->act_dtype, de = spo_d_eff(desc), b = desc->b, rows = (int)T;
+  const int64_t ld = lead(de), nb = nblocks(de, b);
+  const double es = (double)dt_size(at);
+  // dA = dY[:, idx]
+  if (rows > 0)
+    PX_TIMED(POETX_KC_PERMUTE, 0, (double)rows * (desc->d + de) * es,
+             permute(at, dY, desc->d, nullptr, idx, w.A, ld, rows, desc->d, de, s));
+  // dG_k = Xt_k^T dA_k over all rows (the second side of the pair has no blocks)
+  const CnpSide sides[2] = {{q, de, saved, ld, w.A, ld}, {q, 0, nullptr, ld, nullptr, ld}};
+  PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * sum_r2(de, b), 2.0 * rows * de * es + (4 + 2 * es) * sum_r2(de, b),
+           block_grads(at, sides, rows, b, w.cnp, 0, nb, w.part, s));
+  // dXt = dA Diag(G)^T, placed back into dX (FULL: the other columns of dY pass through)
+  PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(de, b), 2.0 * rows * de * es + g_slice(de, b, at),
+           apply(at, at, w.A, ld, rows, de, b, at, G, nullptr, at, w.B, ld, s));
+  st = spo_place(desc, rows, dY, w.B, idx, w, dX, s);
+  if (st != POETX_OK) return st;
+  const float* qs[1] = {q};
+  const int ds[1] = {de};
+  float* dqs[1] = {dq};
+  PX_TIMED(POETX_KC_CNP, 12 * sum_r3(de, b), cnp_grad_bytes(at, nb, b), cnp_chain_batch(at, 1, qs, ds, b, w.cnp, dqs, s));
+  return POETX_OK;
+}
+
 poetx_status poetx_adam_step_batch(int32_t count, const int64_t* len, float* const* q, const float* const* dq,
                                    float* const* m1, float* const* m2, const poetx_adam_params* hp, void* stream) {
   if (count < 1 || count > POETX_MAX_SIDES) return fail(POETX_E_SHAPE, "count must be in [1, POETX_MAX_SIDES]");

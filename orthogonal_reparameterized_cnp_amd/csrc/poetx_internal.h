@@ -25,6 +25,9 @@ hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap,
 // dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < ld_dst
 hipError_t transpose(int dt, const void* src, int64_t ld_src, int rows, int cols, void* dst, int64_t ld_dst,
                      hipStream_t s);
+// dst[t][idx[i]] = src[t][i] for t < rows, i < b (idx values clamped into [0, d))
+hipError_t scatter_cols(int dt, const void* src, int64_t ld_src, int rows, int b, const int32_t* idx, void* dst,
+                        int64_t ld_dst, int d, hipStream_t s);
 // inv[perm[i]] = i
 hipError_t inverse_perm(const int32_t* perm, int d, int32_t* inv, hipStream_t s);
 // out[i] = a[b[i]]

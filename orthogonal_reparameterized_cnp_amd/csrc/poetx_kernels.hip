@@ -563,6 +563,17 @@ __global__ void k_inverse_perm(const int32_t* __restrict__ perm, int d, int32_t*
   if (i < d) inv[min(max(perm[i], 0), d - 1)] = i;
 }
 
+// dst[t][idx[i]] = src[t][i] for i < b (indices clamped into [0, d)); rows in
+// a grid-stride loop over blockIdx.y
+template <typename T>
+__global__ void k_scatter_cols(const T* __restrict__ src, int64_t ld_src, int rows, int b,
+                               const int32_t* __restrict__ idx, T* __restrict__ dst, int64_t ld_dst, int d) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= b) return;
+  const int64_t c = min(max(idx[i], 0), d - 1);
+  for (int t = blockIdx.y; t < rows; t += gridDim.y) dst[(int64_t)t * ld_dst + c] = src[(int64_t)t * ld_src + i];
+}
+
 __global__ void k_compose_perm(const int32_t* __restrict__ a, const int32_t* __restrict__ bm, int d,
                                int32_t* __restrict__ out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -743,6 +754,21 @@ hipError_t transpose(int dt, const void* src, int64_t ld_src, int rows, int cols
 
 hipError_t inverse_perm(const int32_t* perm, int d, int32_t* inv, hipStream_t s) {
   k_inverse_perm<<<cdiv(d, 256), 256, 0, s>>>(perm, d, inv);
+  return hipGetLastError();
+}
+
+hipError_t scatter_cols(int dt, const void* src, int64_t ld_src, int rows, int b, const int32_t* idx, void* dst,
+                        int64_t ld_dst, int d, hipStream_t s) {
+  if (rows <= 0 || b <= 0) return hipSuccess;
+  const dim3 grid(cdiv(b, 256), (unsigned)std::min(rows, 4096));
+  if (dt_size(dt) == 2)
+    k_scatter_cols<uint16_t><<<grid, 256, 0, s>>>(reinterpret_cast<const uint16_t*>(src), ld_src, rows, b, idx,
+                                                  reinterpret_cast<uint16_t*>(dst), ld_dst, d);
+  else if (dt_size(dt) == 4)
+    k_scatter_cols<uint32_t><<<grid, 256, 0, s>>>(reinterpret_cast<const uint32_t*>(src), ld_src, rows, b, idx,
+                                                  reinterpret_cast<uint32_t*>(dst), ld_dst, d);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -258,3 +258,98 @@ class PoetxAdam:
                 m.zero_()
         self.t = 0
         return True
+
+
+class PoetxSpoFactor:
+    """One SPO factor applied to token rows, Y = X F (poetx_spo_fwd / poetx_spo_bwd):
+    kind "block" permutes all d columns and holds ceil(d/b) CNP blocks; kind
+    "full" holds one b x b CNP block on b chosen columns and passes the others
+    through.  Owns q, the column indices, G, the saved state and a workspace."""
+
+    def __init__(self, d: int, b: int, kind: str = "block", act: str = "bf16", device: str = "cuda"):
+        self.d, self.b, self.kind, self.act = d, b, kind, act
+        self.device = torch.device(device)
+        self.desc = B.spo_desc(d, b, kind, act)
+        self.d_eff = d if kind == "block" else b
+        nb = -(-self.d_eff // b)
+        self.adt = B.DTYPES[act]
+        self.q = torch.zeros(nb, b * (b - 1) // 2, dtype=torch.float32, device=self.device)
+        self.idx = torch.arange(self.d_eff, dtype=torch.int32, device=self.device)
+        self.g = torch.empty(B.poetx_g_bytes(self.d_eff, b, self.adt), dtype=torch.uint8, device=self.device)
+        self.saved = torch.empty(0, dtype=torch.uint8, device=self.device)
+        self.ws = torch.empty(0, dtype=torch.uint8, device=self.device)
+
+    def load(self, idx, q):
+        self.idx.copy_(idx)
+        self.q.copy_(q)
+
+    def _ws(self, nbytes: int) -> torch.Tensor:
+        if self.ws.numel() < nbytes:
+            self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.ws
+
+    def reserve(self, T: int):
+        self._ws(max(B.poetx_spo_workspace_size(self.desc, T, B.POETX_OP_FWD),
+                     B.poetx_spo_workspace_size(self.desc, T, B.POETX_OP_BWD)))
+        need = B.poetx_spo_saved_bytes(self.desc, T)
+        if self.saved.numel() < need:
+            self.saved = torch.empty(need, dtype=torch.uint8, device=self.device)
+
+    def build(self, stream=None):
+        ws = self._ws(B.poetx_workspace_size(B.desc(self.d_eff, 1, self.b, self.act, self.act), 0, B.POETX_OP_CNP))
+        B.poetx_cnp_build(self.q, self.d_eff, self.b, self.adt, self.g, ws, ws.numel(), stream)
+
+    def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        T = X.shape[0]
+        self.reserve(T)
+        if Y is None:
+            Y = torch.empty_like(X)
+        B.poetx_spo_fwd(self.desc, T, X, self.idx, self.g, Y, self.saved, self.ws, self.ws.numel(), stream)
+        return Y
+
+    def backward(self, dY: torch.Tensor, dX=None, dq=None, stream=None):
+        T = dY.shape[0]
+        self.reserve(T)
+        if dX is None:
+            dX = torch.empty_like(dY)
+        if dq is None:
+            dq = torch.empty_like(self.q)
+        B.poetx_spo_bwd(self.desc, T, dY, self.idx, self.g, self.q, self.saved, dX, dq, self.ws, self.ws.numel(),
+                        stream)
+        return dX, dq
+
+
+class PoetxChain:
+    """A linear with c factors per side, Y = X R_1 .. R_c W0 P_1 .. P_c: the
+    outer factors R_1 .. R_{c-1} and P_2 .. P_c are PoetxSpoFactor calls around
+    the PoetxLinear, which holds the innermost R_c and P_1 (block-stochastic,
+    folded next to the weight)."""
+
+    def __init__(self, linear: PoetxLinear, outer_R=(), outer_P=()):
+        self.linear, self.outer_R, self.outer_P = linear, list(outer_R), list(outer_P)
+        self.Y_lin = None
+
+    def build(self, stream=None):
+        for f in self.outer_R + self.outer_P:
+            f.build(stream)
+        self.linear.build(stream)
+
+    def forward(self, X: torch.Tensor, stream=None) -> torch.Tensor:
+        for f in self.outer_R:
+            X = f.forward(X, stream=stream)
+        Y = self.linear.forward(X, stream=stream)
+        self.Y_lin, self.X_lin = Y, X
+        for f in self.outer_P:
+            Y = f.forward(Y, stream=stream)
+        return Y
+
+    def backward(self, dZ: torch.Tensor, stream=None):
+        """Returns dX, [dq of outer_R], (dq_R, dq_P) of the linear, [dq of outer_P]."""
+        dq_outer_P = [None] * len(self.outer_P)
+        for k in reversed(range(len(self.outer_P))):
+            dZ, dq_outer_P[k] = self.outer_P[k].backward(dZ, stream=stream)
+        dX, dq_R, dq_P = self.linear.backward(self.X_lin, dZ, stream=stream, Y=self.Y_lin)
+        dq_outer_R = [None] * len(self.outer_R)
+        for k in reversed(range(len(self.outer_R))):
+            dX, dq_outer_R[k] = self.outer_R[k].backward(dX, stream=stream)
+        return dX, dq_outer_R, (dq_R, dq_P), dq_outer_P

@@ -186,3 +186,34 @@ def test_adam_validation(L):
     assert B.POETX_KC_OPTIM == 6 and L.poetx_timer_enable(B.POETX_KC_OPTIM) == B.POETX_OK
     assert L.poetx_timer_enable(7) == B.POETX_E_SHAPE
     assert L.poetx_timer_enable(0) == B.POETX_OK
+
+
+def test_spo_helpers_and_validation(L):
+    """Sizes of the SPO factor calls, and every rejection before any launch."""
+    blk = B.spo_desc(300, 64, "block", "bf16")
+    full = B.spo_desc(1000, 256, "full", "f32")
+    assert B.poetx_spo_saved_bytes(blk, 96) == 96 * 320 * 2
+    assert B.poetx_spo_saved_bytes(full, 10) == 10 * 256 * 4
+    assert B.poetx_spo_workspace_size(blk, 96, B.POETX_OP_BWD) > B.poetx_spo_workspace_size(blk, 96, B.POETX_OP_FWD) > 0
+    assert B.poetx_spo_workspace_size(blk, 96, B.POETX_OP_MERGE) == 0
+    for bad in (B.spo_desc(100, 128, "full", "bf16"), B.spo_desc(0, 64, "block", "bf16"),
+                B.spo_desc(64, 1, "block", "bf16"), B.SpoDesc(64, 32, 2, B.POETX_BF16),
+                B.SpoDesc(64, 32, 0, B.POETX_I8)):
+        assert B.poetx_spo_saved_bytes(bad, 4) == 0
+        assert B.poetx_spo_workspace_size(bad, 4, B.POETX_OP_FWD) == 0
+    big = 1 << 40
+    fwd = lambda dsc, T, X=FAKE, ws=FAKE, wsb=big: L.poetx_spo_fwd(ctypes.byref(dsc), T, X, FAKE, FAKE, FAKE, FAKE,
+                                                                    ws, wsb, None)
+    assert fwd(B.spo_desc(100, 128, "full", "bf16"), 4) == B.POETX_E_SHAPE
+    assert fwd(B.SpoDesc(64, 32, 0, B.POETX_I8), 4) == B.POETX_E_DTYPE
+    assert fwd(blk, -1) == B.POETX_E_SHAPE
+    assert fwd(blk, 4, X=None) == B.POETX_E_NULL
+    assert fwd(blk, 4, wsb=16) == B.POETX_E_WORKSPACE
+    assert fwd(blk, 4, ws=FAKE + 8) == B.POETX_E_WORKSPACE
+    assert fwd(blk, 0, X=None) == B.POETX_OK  # nothing to do
+    bwd = lambda T, q=FAKE, dY=FAKE: L.poetx_spo_bwd(ctypes.byref(blk), T, dY, FAKE, FAKE, q, FAKE, FAKE, FAKE, FAKE,
+                                                     big, None)
+    assert bwd(4, q=None) == B.POETX_E_NULL
+    assert bwd(4, dY=None) == B.POETX_E_NULL
+    assert L.poetx_spo_bwd(ctypes.byref(blk), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == \
+        B.POETX_E_WORKSPACE

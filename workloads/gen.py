@@ -190,3 +190,30 @@ def loop_batches(m: int, n: int, T: int, act: str, steps: int, seed: int):
         (_act_matrix([wid, s, TENSOR_X, T], T, m, act), _act_matrix([wid, s, TENSOR_DZ, T], T, n, act))
         for s in range(steps)
     ]
+
+
+@dataclass
+class SpoInputs:
+    d: int
+    b: int
+    kind: str  # "block" | "full"
+    T: int
+    act: str
+    idx: np.ndarray  # [d] permutation (block) or [b] distinct columns (full), int32
+    q: np.ndarray  # [nb, b(b-1)/2] float32, nb = ceil(d/b) (block) or 1 (full)
+    X: np.ndarray  # [T, d]
+    dY: np.ndarray  # [T, d]
+
+
+def spo_inputs(d: int, b: int, kind: str, T: int, act: str, q_std: float, seed: int) -> SpoInputs:
+    """Inputs of one SPO factor: a numpy-drawn permutation or ordered b-subset
+    of the d columns, N(0, q_std^2) packed parameters (dead slots included),
+    N(0, 1) X and dY."""
+    wid = 5000 + seed
+    perm = _rng(wid, 0, TENSOR_PR).permutation(d).astype(np.int32)
+    idx = perm if kind == "block" else perm[:b].copy()
+    nb = -(-d // b) if kind == "block" else 1
+    q = (_rng(wid, 0, TENSOR_QR).standard_normal((nb, packed_len(b))) * q_std).astype(np.float32)
+    X = _act_matrix([wid, 0, TENSOR_X, T], T, d, act)
+    dY = _act_matrix([wid, 0, TENSOR_DZ, T], T, d, act)
+    return SpoInputs(d, b, kind, T, act, idx, q, X, dY)
