@@ -337,6 +337,44 @@ def time_merge(key, to_dev, dev):
     }
 
 
+def time_spo(T, d, b, act, to_dev):
+    """One extra SPO factor of each kind on token rows at T x d (poetx_spo_fwd + poetx_spo_bwd), timed with
+    events after one untimed call: the cost of each factor a chain of c > 1 factors per side adds."""
+    import torch
+
+    from orthogonal_reparameterized_cnp_amd.layer import PoetxSpoFactor
+    from workloads.gen import spo_inputs
+
+    out = {}
+    for kind in ("block", "full"):
+        inp = spo_inputs(d, b, kind, T, act, 0.005, seed=7)
+        f = PoetxSpoFactor(d, b, kind, act)
+        f.load(to_dev(inp.idx, "i32"), to_dev(inp.q, "f32"))
+        f.build()
+        X, dY = to_dev(inp.X, act), to_dev(inp.dY, act)
+        Y, dX = torch.empty_like(X), torch.empty_like(X)
+        dq = torch.empty_like(f.q)
+        f.forward(X, Y)
+        f.backward(dY, dX, dq)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        f.forward(X, Y)
+        ev[1].record()
+        f.backward(dY, dX, dq)
+        ev[2].record()
+        torch.cuda.synchronize()
+        fwd, bwd = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+        de = f.d_eff
+        r2, r3 = side_sums(de, b)
+        fl_f, fl_b = 2.0 * T * r2, 4.0 * T * r2 + 12.0 * r3
+        out[kind] = {"d": d, "b": b, "T": T, "columns_transformed": de, "fwd_ms": fwd, "bwd_ms": bwd,
+                     "fwd_tflops": fl_f / (fwd * 1e-3) / 1e12, "bwd_tflops": fl_b / (bwd * 1e-3) / 1e12}
+        print(f"[bench] spo {kind} d={d} b={b} T={T}: fwd {fwd:.3f} ms, bwd {bwd:.3f} ms", file=sys.stderr, flush=True)
+        del X, dY, Y, dX, f
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +391,8 @@ def main():
                          "report it amortised over the workload's merge period")
     ap.add_argument("--optimizer", action="store_true",
                     help="end every step with the Adam step on all packed q (poetx_adam_step_batch)")
+    ap.add_argument("--spo", action="store_true",
+                    help="also time one extra SPO factor of each kind (block, full) at the widest side")
     ap.add_argument("--copy-probe", action="store_true",
                     help=f"run a {COPY_PROBE_BYTES >> 20} MiB device copy before the steps (counter calibration)")
     ap.add_argument("--summarize-classes", nargs=3, metavar=("MFMA_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -535,6 +575,8 @@ def main():
 
     if args.merge:
         result["merge"] = time_merge(args.merge, to_dev, dev)
+    if args.spo:
+        result["spo_factor"] = time_spo(T, max(max(L.m, L.n) for L in wl.linears), wl.b, wl.act, to_dev)
 
     if not args.no_cpu_baseline:
         lin_f = 4.0 * T * inputs0.m * inputs0.n

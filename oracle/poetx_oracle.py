@@ -616,3 +616,19 @@ def chain_backward(X, dZ, W, R: Sequence[SpoFactor], P: Sequence[SpoFactor]):
     for k in reversed(range(len(R))):
         g, dq_R[k] = spo_backward(ins_R[k], g, R[k])
     return g, dq_R, dq_P
+
+
+def spo_block_grads(X: np.ndarray, dY: np.ndarray, f: SpoFactor, blocks: Sequence[int]):
+    """Packed dq of selected blocks of one factor, with the sums over all rows:
+    dG_k = X[:, cols_k]^T dY[:, cols_k] for the block's columns cols_k of idx,
+    then the CNP chain rule (the same definitions as spo_backward, restricted
+    to the blocks asked for).  Returns {k: dq_k}."""
+    de = f.d if f.kind == "block" else f.b
+    sb = side_blocks(de, f.b)
+    Q = side_Q(f.q, de, f.b)
+    out = {}
+    for k in blocks:
+        s, r = sb[k]
+        cols = np.asarray(f.idx[s : s + r])
+        out[k] = pack_skew_grad(cnp_adjoint(Q[k], X[:, cols].T @ dY[:, cols]), f.b)
+    return out

@@ -104,3 +104,28 @@ def test_chain_of_two_factors_per_side(act, w, m, n, b, T):
     for name, got, ref in (("dq outer R", dq_oR[0], ref_dq_R[0]), ("dq_R", dq_R, ref_dq_R[1]),
                            ("dq_P", dq_P, ref_dq_P[0]), ("dq outer P", dq_oP[0], ref_dq_P[1])):
         assert_close(name, host(got, "f32"), ref, act)
+
+
+@pytest.mark.parametrize("kind", ["block", "full"])
+def test_spo_factor_full_size_sampled(kind):
+    """The configuration bench.py --spo times (d = 14336, b = 512, T = 8192, bf16,
+    same seed): sampled rows of Y and dX, and sampled blocks of dq with their
+    sums over all 8192 rows, against the oracle."""
+    d, b, T, act = 14336, 512, 8192, "bf16"
+    print(f"spo full size {kind}", flush=True)
+    inp = spo_inputs(d, b, kind, T, act, 0.005, seed=7)
+    f = _factor(inp, act)
+    Y = f.forward(dev(inp.X, act))
+    dX, dq = f.backward(dev(inp.dY, act))
+    torch.cuda.synchronize()
+    of = _oracle_factor(inp)
+    rows = [0, 1, 2047, 4097, 8191]
+    Xs, dYs = O.to_f64(inp.X[rows], act), O.to_f64(inp.dY[rows], act)
+    ref_Y, ref_Xt = O.spo_forward(Xs, of)
+    assert_close("Y rows", host(Y[rows], act), ref_Y, act)
+    assert_close("dX rows", host(dX[rows], act), O.spo_backward(ref_Xt, dYs, of)[0], act)
+    blocks = [0, 13, 27] if kind == "block" else [0]
+    sel = O.spo_block_grads(O.to_f64(inp.X, act), O.to_f64(inp.dY, act), of, blocks)
+    got = host(dq, "f32")
+    for k in blocks:
+        assert_close(f"dq block {k}", got[k], sel[k], act)

@@ -156,3 +156,14 @@ def test_chain_of_one_block_factor_per_side_is_the_layer():
     np.testing.assert_allclose(dX, g.dX, rtol=0, atol=1e-12)
     np.testing.assert_allclose(dq_R[0], g.dq_R, rtol=0, atol=1e-12)
     np.testing.assert_allclose(dq_P[0], g.dq_P, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind,d,b", [("block", 11, 4), ("full", 9, 4)])
+def test_spo_block_grads_is_backward_restricted(kind, d, b):
+    rng = np.random.default_rng(8)
+    f = _factor(rng, kind, d, b, std=0.2)
+    X, dY = rng.standard_normal((7, d)), rng.standard_normal((7, d))
+    _, dq = O.spo_backward(O.spo_forward(X, f)[1], dY, f)
+    sel = O.spo_block_grads(X, dY, f, range(dq.shape[0]))
+    for k, v in sel.items():
+        np.testing.assert_allclose(v, dq[k], rtol=0, atol=1e-12)
