@@ -143,14 +143,12 @@ size_t saved_xt_offset(const poetx_layer_desc* d, int64_t T) {
 
 struct FwdWs {
   void *A, *Zt, *H;  // H: Xmem and Xout (Xfast writes it to the saved state)
-  int32_t* invP;
 };
 template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
   const size_t es = dt_size(d->act_dtype);
   FwdWs w;
   w.A = p.template take<char>(T * lead(d->m) * es);
   w.Zt = p.template take<char>(T * lead(d->n) * es);
-  w.invP = p.template take<int32_t>((size_t)d->n * 4);
   w.H = saves_h(d) ? nullptr : p.template take<char>(T * lead(d->n) * es);
   return w;
 }
@@ -159,7 +157,6 @@ struct BwdWs {
   void *dZt, *dH, *dA, *dXt, *cnp;
   void* Hr;  // Xout: H taken back from the output
   float* part;
-  int32_t* invR;
 };
 template <class P> BwdWs plan_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
   const size_t es = dt_size(d->act_dtype);
@@ -171,7 +168,6 @@ template <class P> BwdWs plan_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
   w.cnp = p.template take<char>(cnp_grad_bytes(d->act_dtype, (int64_t)nblocks(d->m, d->b) + nblocks(d->n, d->b), d->b));
   w.part = p.template take<float>(
       block_grads_part_bytes(d->act_dtype, (int)T, nblocks(d->m, d->b) + nblocks(d->n, d->b), d->b));
-  w.invR = p.template take<int32_t>((size_t)d->m * 4);
   w.Hr = d->mode == POETX_XOUT ? p.template take<char>(T * lead(d->n) * es) : nullptr;
   return w;
 }
@@ -442,9 +438,8 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
   // Zt = H Diag(G_P)
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
            apply(at, at, H, ldn, rows, n, b, at, gP1, nullptr, at, w.Zt, ldn, s));
-  // Y[:, perm_P] = Zt, i.e. Y = Zt[:, perm_P^{-1}]
-  PX_HIP(inverse_perm(perm_P, n, w.invP, s));
-  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, permute(at, w.Zt, ldn, nullptr, w.invP, Y, n, rows, n, n, s));
+  // Y[:, perm_P] = Zt
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, scatter(at, w.Zt, ldn, perm_P, Y, n, rows, n, s));
   return POETX_OK;
 }
 
@@ -496,10 +491,8 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* Y,
   // dXt = dA Diag(G_R)^T;  dX[:, perm_R] = dXt
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
            apply(at, at, w.dA, ldm, rows, m, b, at, g_R, nullptr, at, w.dXt, ldm, s));
-  if (rows > 0) {
-    PX_HIP(inverse_perm(perm_R, m, w.invR, s));
-    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, w.dXt, ldm, nullptr, w.invR, dX, m, rows, m, m, s));
-  }
+  if (rows > 0)
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, scatter(at, w.dXt, ldm, perm_R, dX, m, rows, m, s));
   return POETX_OK;
 }
 
@@ -649,14 +642,12 @@ struct SpoWs {
   void *A, *B;  // fwd: A = Xt Diag(G); bwd: A = dY[:, idx], B = dXt
   void* cnp;
   float* part;
-  int32_t* inv;
 };
 template <class P> SpoWs plan_spo(P& p, const poetx_spo_desc* d, int64_t T, bool bwd) {
   const int de = spo_d_eff(d), nb = nblocks(de, d->b);
   const size_t mat = (size_t)T * lead(de) * dt_size(d->act_dtype);
   SpoWs w{};
   w.A = p.template take<char>(mat);
-  w.inv = d->kind == POETX_SPO_BLOCK ? p.template take<int32_t>((size_t)d->d * 4) : nullptr;
   if (bwd) {
     w.B = p.template take<char>(mat);
     w.cnp = p.template take<char>(cnp_grad_bytes(d->act_dtype, nb, d->b));
@@ -672,9 +663,7 @@ poetx_status spo_place(const poetx_spo_desc* d, int rows, const void* in, const 
   const double es = (double)dt_size(at);
   if (rows <= 0) return POETX_OK;
   if (d->kind == POETX_SPO_BLOCK) {
-    PX_HIP(inverse_perm(idx, d->d, w.inv, s));
-    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * d->d * es,
-             permute(at, src, lead(de), nullptr, w.inv, out, d->d, rows, d->d, d->d, s));
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * d->d * es, scatter(at, src, lead(de), idx, out, d->d, rows, d->d, s));
     return POETX_OK;
   }
   if (out != in) {

@@ -22,6 +22,10 @@ inline int64_t lead(int d) { return round_up(d, 64); }
 // out[t][i] = in[rowmap ? rowmap[t] : t][colmap[i]] for t < rows, i < d_out.
 hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap, const int32_t* colmap, void* out,
                    int64_t ld_out, int rows, int d_in, int d_out, hipStream_t s);
+// out[t][perm[i]] = in[t][i] for t < rows, i < d (the inverse of the gather
+// out[t][i] = in[t][perm[i]]), without forming the inverse permutation
+hipError_t scatter(int dt, const void* in, int64_t ld_in, const int32_t* perm, void* out, int64_t ld_out, int rows,
+                   int d, hipStream_t s);
 // dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < ld_dst
 hipError_t transpose(int dt, const void* src, int64_t ld_src, int rows, int cols, void* dst, int64_t ld_dst,
                      hipStream_t s);

@@ -558,6 +558,70 @@ __global__ __launch_bounds__(256) void k_permute_direct(const E* __restrict__ in
   }
 }
 
+// Row-staged scatter, out[t][perm[i]] = in[t][i]: each source row is read with
+// 16-byte coalesced loads (the permutation as 16-byte index vectors) and
+// written into LDS at the permuted positions; the staged rows then leave with
+// 16-byte stores.  Indices are clamped into [0, d): a malformed permutation
+// leaves some outputs undefined but cannot address outside the staged rows.
+template <typename E>
+__global__ __launch_bounds__(256) void k_scatter_lds(const E* __restrict__ in, int64_t ld_in,
+                                                     const int32_t* __restrict__ perm, E* __restrict__ out,
+                                                     int64_t ld_out, int rows, int d, int rpw) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* buf = reinterpret_cast<E*>(smem);
+  constexpr int V = 16 / sizeof(E);
+  const int pitch = (d + V - 1) / V * V;
+  const int t0 = blockIdx.x * rpw;
+  const int nr = min(rpw, rows - t0);
+  const int dv = d / V;
+  const bool vin = (reinterpret_cast<uintptr_t>(in) % 16 == 0) && (ld_in % V == 0) &&
+                   (reinterpret_cast<uintptr_t>(perm) % 16 == 0);
+  for (int rr = 0; rr < nr; ++rr) {
+    const E* row = in + (int64_t)(t0 + rr) * ld_in;
+    E* dst = buf + rr * pitch;
+    int tail = 0;
+    if (vin) {
+      for (int c = threadIdx.x; c < dv; c += blockDim.x) {
+        const uint4 v = reinterpret_cast<const uint4*>(row)[c];
+        E vals[V];
+        __builtin_memcpy(vals, &v, 16);
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q) {
+          const int4 w = reinterpret_cast<const int4*>(perm + c * V)[q];
+          dst[min(max(w.x, 0), d - 1)] = vals[4 * q];
+          dst[min(max(w.y, 0), d - 1)] = vals[4 * q + 1];
+          dst[min(max(w.z, 0), d - 1)] = vals[4 * q + 2];
+          dst[min(max(w.w, 0), d - 1)] = vals[4 * q + 3];
+        }
+      }
+      tail = dv * V;
+    }
+    for (int i = tail + threadIdx.x; i < d; i += blockDim.x) dst[min(max(perm[i], 0), d - 1)] = row[i];
+  }
+  __syncthreads();
+  const bool vout = (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (ld_out % V == 0);
+  for (int rr = 0; rr < nr; ++rr) {
+    E* o = out + (int64_t)(t0 + rr) * ld_out;
+    const E* srow = buf + rr * pitch;
+    int tail = 0;
+    if (vout) {
+      for (int c = threadIdx.x; c < dv; c += blockDim.x)
+        reinterpret_cast<uint4*>(o)[c] = reinterpret_cast<const uint4*>(srow)[c];
+      tail = dv * V;
+    }
+    for (int i = tail + threadIdx.x; i < d; i += blockDim.x) o[i] = srow[i];
+  }
+}
+
+// The same scatter for rows too long to stage (one row per workgroup).
+template <typename E>
+__global__ __launch_bounds__(256) void k_scatter_direct(const E* __restrict__ in, int64_t ld_in,
+                                                        const int32_t* __restrict__ perm, E* __restrict__ out,
+                                                        int64_t ld_out, int d) {
+  const int64_t t = blockIdx.x;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) out[t * ld_out + min(max(perm[i], 0), d - 1)] = in[t * ld_in + i];
+}
+
 __global__ void k_inverse_perm(const int32_t* __restrict__ perm, int d, int32_t* __restrict__ inv) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < d) inv[min(max(perm[i], 0), d - 1)] = i;
@@ -727,6 +791,29 @@ hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap,
     } else {
       k_permute_direct<E><<<rows, 256, 0, s>>>(reinterpret_cast<const E*>(in), ld_in, rowmap, colmap,
                                                reinterpret_cast<E*>(out), ld_out, rows, d_in, d_out);
+    }
+    return hipGetLastError();
+  };
+  if (dt == F32) return go(float{});
+  if (dt == BF16) return go(bf16_t{});
+  return go(int8_t{});
+}
+
+hipError_t scatter(int dt, const void* in, int64_t ld_in, const int32_t* perm, void* out, int64_t ld_out, int rows,
+                   int d, hipStream_t s) {
+  if (rows <= 0 || d <= 0) return hipSuccess;
+  const size_t es = dt_size(dt);
+  const size_t budget = 64 * 1024, target = 8 * 1024;  // as for permute
+  auto go = [&](auto tag) -> hipError_t {
+    using E = decltype(tag);
+    const size_t pitch_bytes = ((size_t)d * es + 15) / 16 * 16;
+    if (pitch_bytes <= budget) {
+      const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, target / pitch_bytes));
+      k_scatter_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch_bytes, s>>>(
+          reinterpret_cast<const E*>(in), ld_in, perm, reinterpret_cast<E*>(out), ld_out, rows, d, rpw);
+    } else {
+      k_scatter_direct<E><<<rows, 256, 0, s>>>(reinterpret_cast<const E*>(in), ld_in, perm,
+                                               reinterpret_cast<E*>(out), ld_out, d);
     }
     return hipGetLastError();
   };
