@@ -391,6 +391,9 @@ def main():
                          "report it amortised over the workload's merge period")
     ap.add_argument("--optimizer", action="store_true",
                     help="end every step with the Adam step on all packed q (poetx_adam_step_batch)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step into a HIP graph and time its replays (the W~ contraction rate then "
+                         "comes from an eager pass of the same length)")
     ap.add_argument("--spo", action="store_true",
                     help="also time one extra SPO factor of each kind (block, full) at the widest side")
     ap.add_argument("--copy-probe", action="store_true",
@@ -484,20 +487,42 @@ def main():
 
     gemm_f, apply_f, cnp_f = step_flops(wl, T)
     total_f = gemm_f + apply_f + cnp_f
+    graph = None
+    if args.graph:
+        if args.optimizer:
+            raise SystemExit("--graph does not take --optimizer: the Adam step count is a launch argument")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+
+    def timed(fn):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for _ in range(args.steps):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps, time.perf_counter() - t0
+
+    if graph is not None:
+        ms, wall = timed(graph.replay)
     B.poetx_timer_enable(B.POETX_KC_GEMM)
     B.poetx_timer_read()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / args.steps
+    ms_eager, wall_eager = timed(step)
     n_launch, k_ms, k_flops, k_bytes = B.poetx_timer_read()
     B.poetx_timer_enable(B.POETX_KC_NONE)
+    if graph is None:
+        ms, wall = ms_eager, wall_eager
 
     peak = PEAK_TFLOPS[wl.act]
     achieved = k_flops / (k_ms * 1e-3) / 1e12 if k_ms > 0 else 0.0
@@ -521,6 +546,7 @@ def main():
             "weights": wl.w,
             "mode": args.mode,
             "optimizer_in_step": "adam" if args.optimizer else None,
+            "launch": "hip graph replay" if args.graph else "eager",
         },
         "tflops": total_f / (ms * 1e-3) / 1e12,
         "mfma_peak_frac": total_f / (ms * 1e-3) / 1e12 / peak,
@@ -539,6 +565,7 @@ def main():
             "algorithmic_gb_per_launch": k_bytes / max(n_launch, 1) / 1e9,
         },
         "wall_s_timed": wall,
+        "ms_per_step_eager": ms_eager,
     }
 
     # the optimiser step on its own (outside the timed region): HBM-bound, 28 bytes per packed slot
