@@ -179,6 +179,7 @@ KERNEL_CLASSES = (  # kernel-name prefix -> class, as in --breakdown
     ("k_pack_dq", "CNP pack/unpack"),
     ("k_permute", "permutations"),
     ("k_inverse_perm", "permutations"),
+    ("k_scatter", "permutations"),
     ("k_adam<", "optimiser step"),
 )
 N_XCC = 8  # GRBM_GUI_ACTIVE is reported once per XCD; the counter CSV holds their sum
