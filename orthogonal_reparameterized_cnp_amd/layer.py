@@ -253,6 +253,7 @@ class PoetxAdam:
             lay.build(stream)
             seed_R, seed_P = self.merge_seeds(self.steps, i)
             lay.merge_reinit(seed_R, seed_P, stream)
+            lay.build(stream)  # G of the restarted q (the identity), so the layer is usable at once
         with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
             for m in self.m1 + self.m2:
                 m.zero_()

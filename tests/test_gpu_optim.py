@@ -163,3 +163,21 @@ def test_train_loop_matches_oracle(m, n, b, T, act, w, eps):
     else:
         Wg = host(Wv.contiguous(), w)
     assert_close("W~", Wg, ref.Wt, kind)
+
+
+def test_layer_usable_right_after_a_merge():
+    """After the merge step the layer's G is rebuilt from the restarted q, so a
+    forward without an explicit build() equals the forward after one."""
+    inp = custom_linear_inputs(96, 80, 32, 64, "bf16", "bf16", 0.02, seed=23)
+    lay = make_layer(inp)
+    opt = PoetxAdam([lay], lr=0.01, eps=10.0, merge_every=1)
+    X, dZ = loop_batches(96, 80, 64, "bf16", 1, seed=5)[0]
+    Xd = dev(X, "bf16")
+    lay.forward(Xd)
+    _, dq_R, dq_P = lay.backward(Xd, dev(dZ, "bf16"))
+    assert opt.step([(dq_R, dq_P)])
+    Y1 = lay.forward(Xd).clone()
+    lay.build()
+    Y2 = lay.forward(Xd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))

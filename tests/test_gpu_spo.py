@@ -129,3 +129,18 @@ def test_spo_factor_full_size_sampled(kind):
     got = host(dq, "f32")
     for k in blocks:
         assert_close(f"dq block {k}", got[k], sel[k], act)
+
+
+@pytest.mark.parametrize("kind", ["block", "full"])
+def test_spo_empty_batch(kind):
+    """T = 0: the forward writes nothing and the backward's block gradients are
+    empty sums, so dq is exactly zero."""
+    inp = spo_inputs(300, 64, kind, 4, "bf16", 0.02, seed=3)
+    f = _factor(inp, "bf16")
+    X = torch.empty(0, 300, dtype=torch.bfloat16, device="cuda")
+    Y = f.forward(X)
+    dq = torch.full_like(f.q, 7.0)
+    dX, dq = f.backward(torch.empty(0, 300, dtype=torch.bfloat16, device="cuda"), dq=dq)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 300) and dX.shape == (0, 300)
+    assert not dq.any()
