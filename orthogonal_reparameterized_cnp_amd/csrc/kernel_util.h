@@ -18,6 +18,8 @@ using TSq = Tile<128, 128, 64, 2, 2>;   // bf16: block gradients, CNP (b x b out
 // direct-to-LDS configurations (K-contiguous operands, interior tiles)
 using DGemm = DCfg<256, 256, 64, 2, 4, 2, false, false, true>;  // 8 waves, same block size as TGemm
 using DSq = DCfg<128, 128, 64, 2, 2, 2, false, false, true>;    // 4 waves, same block size as TSq
+using TNarrow = Tile<256, 128, 64, 4, 2, false, true>;            // bf16 NT narrow contractions, 8 waves
+using DNarrow = DCfg<256, 128, 64, 4, 2, 2, false, false, true>;  // its direct-to-LDS loop (waves of 64 x 64)
 using TF = Tile<64, 64, 32, 2, 2>;      // fp32: small layers
 using TFM = Tile<128, 128, 32, 2, 2>;   // fp32: merge products
 

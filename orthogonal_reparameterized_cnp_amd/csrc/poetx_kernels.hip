@@ -977,6 +977,8 @@ static hipError_t gemm_bf16(const void* A, int64_t lda, const void* B, int64_t l
   using C = typename std::conditional<std::is_same<BT, bf16_t>::value, TGemmI, TGemm>::type;
   if ((int64_t)cdiv(M, 256) * cdiv(N, 256) >= 256)
     return gemm_t<CD, C, bf16_t, bf16_t, BT, bf16_t, BKN>(A, lda, B, ldb, M, N, K, cs, out, ldo, s);
+  if constexpr (!std::is_same<CD, void>::value)
+    return gemm_t<DNarrow, TNarrow, bf16_t, bf16_t, BT, bf16_t, BKN>(A, lda, B, ldb, M, N, K, cs, out, ldo, s);
   return gemm_t<void, TBig, bf16_t, bf16_t, BT, bf16_t, BKN>(A, lda, B, ldb, M, N, K, cs, out, ldo, s);
 }
 
