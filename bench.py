@@ -569,7 +569,10 @@ def main():
         "ms_per_step_eager": ms_eager,
     }
 
-    # the optimiser step on its own (outside the timed region): HBM-bound, 28 bytes per packed slot
+    # the optimiser step on its own (outside the timed region): HBM-bound, 28 bytes per packed slot;
+    # one untimed call first, so that the kernel's first launch in the process is not timed
+    opt.step(dqs)
+    torch.cuda.synchronize()
     B.poetx_timer_enable(B.POETX_KC_OPTIM)
     B.poetx_timer_read()
     opt.step(dqs)
