@@ -149,7 +149,7 @@ Commands (from the repository root on one MI355X, one counter per run):
 
     {cmd_fetch}
     {cmd_write}
-    python bench.py --summarize-traffic gpurun_out/pmc_fetch gpurun_out/pmc_write
+    python bench.py --summarize-traffic {fetch_dir} {write_dir}
 
 Each counter is scaled by the factor that maps its reading for the copy probe to the probe's true
 bytes: FETCH_SIZE x{res['fetch']['factor']:.3f}, WRITE_SIZE x{res['write']['factor']:.3f}.
@@ -256,7 +256,7 @@ Commands (from the repository root on one MI355X, one counter set per run):
     {cmds[0]}
     {cmds[1]}
     {cmds[2]}
-    python bench.py --summarize-classes gpurun_out/pmc_mfma gpurun_out/pmc_fetch gpurun_out/pmc_write
+    python bench.py --summarize-classes {mfma_dir} {fetch_dir} {write_dir}
 
 - MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES summed over all {n_simd} SIMDs / ({n_simd} x the XCDs' busy cycles, GRBM_GUI_ACTIVE
   summed over {N_XCC} XCDs / {N_XCC}). It counts cycles with the matrix pipe occupied, at the clock the chip ran.
@@ -418,7 +418,7 @@ def main():
                                     base.format(c="WRITE_SIZE", d=w) + " --copy-probe"))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -57,7 +57,7 @@ typedef enum {
   POETX_E_WORKSPACE = 4,   /* ws too small or misaligned */
   POETX_E_PERM = 5,        /* host permutation argument invalid */
   POETX_E_HIP = 6,         /* a HIP runtime call failed (see poetx_last_error) */
-  POETX_E_UNSUPPORTED = 7  /* valid request this build does not implement */
+  POETX_E_UNSUPPORTED = 7  /* valid request the library does not implement */
 } poetx_status;
 
 typedef enum { POETX_F32 = 0, POETX_BF16 = 1, POETX_I8 = 2 } poetx_dtype;
