@@ -666,12 +666,12 @@ poetx_status spo_place(const poetx_spo_desc* d, int rows, const void* in, const 
     PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * d->d * es, scatter(at, src, lead(de), idx, out, d->d, rows, d->d, s));
     return POETX_OK;
   }
-  if (out != in) {
-    const size_t row = (size_t)d->d * dt_size(at);
-    PX_HIP(hipMemcpy2DAsync(out, row, in, row, row, (size_t)rows, hipMemcpyDeviceToDevice, s));
-  }
-  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * de * es,
-           scatter_cols(at, src, lead(de), rows, de, idx, out, d->d, d->d, s));
+  if (out != in)
+    PX_TIMED(POETX_KC_PERMUTE, 0, (2.0 * d->d + de) * rows * es,
+             replace_cols(at, in, d->d, src, lead(de), de, idx, out, d->d, rows, d->d, s));
+  else
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * de * es,
+             scatter_cols(at, src, lead(de), rows, de, idx, out, d->d, d->d, s));
   return POETX_OK;
 }
 

@@ -32,6 +32,9 @@ hipError_t transpose(int dt, const void* src, int64_t ld_src, int rows, int cols
 // dst[t][idx[i]] = src[t][i] for t < rows, i < b (idx values clamped into [0, d))
 hipError_t scatter_cols(int dt, const void* src, int64_t ld_src, int rows, int b, const int32_t* idx, void* dst,
                         int64_t ld_dst, int d, hipStream_t s);
+// out[t] = in[t] with out[t][idx[i]] = src[t][i] for i < b (out != in), in one pass
+hipError_t replace_cols(int dt, const void* in, int64_t ld_in, const void* src, int64_t ld_src, int b,
+                        const int32_t* idx, void* out, int64_t ld_out, int rows, int d, hipStream_t s);
 // inv[perm[i]] = i
 hipError_t inverse_perm(const int32_t* perm, int d, int32_t* inv, hipStream_t s);
 // out[i] = a[b[i]]

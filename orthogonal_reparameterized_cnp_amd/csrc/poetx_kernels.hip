@@ -613,6 +613,55 @@ __global__ __launch_bounds__(256) void k_scatter_lds(const E* __restrict__ in, i
   }
 }
 
+// out[t] = in[t] except out[t][idx[i]] = src[t][i] for i < b: each row of `in`
+// is staged in LDS with 16-byte loads, the b values are written over it at
+// their positions, and the row leaves with 16-byte stores (one pass over the
+// untouched columns instead of a copy followed by a scatter).
+template <typename E>
+__global__ __launch_bounds__(256) void k_replace_cols_lds(const E* __restrict__ in, int64_t ld_in,
+                                                          const E* __restrict__ src, int64_t ld_src, int b,
+                                                          const int32_t* __restrict__ idx, E* __restrict__ out,
+                                                          int64_t ld_out, int rows, int d, int rpw) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* buf = reinterpret_cast<E*>(smem);
+  constexpr int V = 16 / sizeof(E);
+  const int pitch = (d + V - 1) / V * V;
+  const int t0 = blockIdx.x * rpw;
+  const int nr = min(rpw, rows - t0);
+  const int dv = d / V;
+  const bool vin = (reinterpret_cast<uintptr_t>(in) % 16 == 0) && (ld_in % V == 0);
+  for (int rr = 0; rr < nr; ++rr) {
+    const E* row = in + (int64_t)(t0 + rr) * ld_in;
+    E* dst = buf + rr * pitch;
+    int tail = 0;
+    if (vin) {
+      for (int c = threadIdx.x; c < dv; c += blockDim.x)
+        reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(row)[c];
+      tail = dv * V;
+    }
+    for (int i = tail + threadIdx.x; i < d; i += blockDim.x) dst[i] = row[i];
+  }
+  __syncthreads();
+  for (int rr = 0; rr < nr; ++rr) {
+    const E* srow = src + (int64_t)(t0 + rr) * ld_src;
+    E* dst = buf + rr * pitch;
+    for (int i = threadIdx.x; i < b; i += blockDim.x) dst[min(max(idx[i], 0), d - 1)] = srow[i];
+  }
+  __syncthreads();
+  const bool vout = (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (ld_out % V == 0);
+  for (int rr = 0; rr < nr; ++rr) {
+    E* o = out + (int64_t)(t0 + rr) * ld_out;
+    const E* srow = buf + rr * pitch;
+    int tail = 0;
+    if (vout) {
+      for (int c = threadIdx.x; c < dv; c += blockDim.x)
+        reinterpret_cast<uint4*>(o)[c] = reinterpret_cast<const uint4*>(srow)[c];
+      tail = dv * V;
+    }
+    for (int i = tail + threadIdx.x; i < d; i += blockDim.x) o[i] = srow[i];
+  }
+}
+
 // The same scatter for rows too long to stage (one row per workgroup).
 template <typename E>
 __global__ __launch_bounds__(256) void k_scatter_direct(const E* __restrict__ in, int64_t ld_in,
@@ -815,6 +864,31 @@ hipError_t scatter(int dt, const void* in, int64_t ld_in, const int32_t* perm, v
       k_scatter_direct<E><<<rows, 256, 0, s>>>(reinterpret_cast<const E*>(in), ld_in, perm,
                                                reinterpret_cast<E*>(out), ld_out, d);
     }
+    return hipGetLastError();
+  };
+  if (dt == F32) return go(float{});
+  if (dt == BF16) return go(bf16_t{});
+  return go(int8_t{});
+}
+
+hipError_t replace_cols(int dt, const void* in, int64_t ld_in, const void* src, int64_t ld_src, int b,
+                        const int32_t* idx, void* out, int64_t ld_out, int rows, int d, hipStream_t s) {
+  if (rows <= 0 || d <= 0) return hipSuccess;
+  const size_t es = dt_size(dt);
+  const size_t pitch_bytes = ((size_t)d * es + 15) / 16 * 16;
+  const size_t budget = 64 * 1024, target = 8 * 1024;  // as for permute
+  if (pitch_bytes > budget) {  // rows too long to stage: copy, then write the subset
+    const hipError_t e = hipMemcpy2DAsync(out, (size_t)ld_out * es, in, (size_t)ld_in * es, (size_t)d * es,
+                                          (size_t)rows, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return e;
+    return scatter_cols(dt, src, ld_src, rows, b, idx, out, ld_out, d, s);
+  }
+  const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, target / pitch_bytes));
+  auto go = [&](auto tag) -> hipError_t {
+    using E = decltype(tag);
+    k_replace_cols_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch_bytes, s>>>(
+        reinterpret_cast<const E*>(in), ld_in, reinterpret_cast<const E*>(src), ld_src, b, idx,
+        reinterpret_cast<E*>(out), ld_out, rows, d, rpw);
     return hipGetLastError();
   };
   if (dt == F32) return go(float{});
