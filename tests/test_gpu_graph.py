@@ -111,3 +111,49 @@ def test_group_step_replays_in_a_graph():
         for got, want in zip(flat, ref):
             assert torch.equal(got.view(torch.uint8) if got.dtype == torch.bfloat16 else got,
                                want.view(torch.uint8) if want.dtype == torch.bfloat16 else want), f"replay {k}"
+
+
+def test_chain_step_replays_in_a_graph():
+    """Two factors per side (a fully stochastic and a block-stochastic outer
+    factor around the linear): the SPO calls capture like the layer calls."""
+    from orthogonal_reparameterized_cnp_amd.layer import PoetxChain, PoetxSpoFactor
+    from workloads.gen import spo_inputs
+
+    m, n, b, T, act = 320, 200, 64, 96, "bf16"
+    inp = custom_linear_inputs(m, n, b, T, act, "bf16", 0.02, seed=71)
+    lin = make_layer(inp)
+    facs = []
+    for d, kind, seed in ((m, "full", 72), (n, "block", 73)):
+        si = spo_inputs(d, b, kind, T, act, 0.02, seed=seed)
+        f = PoetxSpoFactor(d, b, kind, act)
+        f.load(dev(si.idx, "i32"), dev(si.q, "f32"))
+        facs.append(f)
+    chain = PoetxChain(lin, [facs[0]], [facs[1]])
+    X, dZ = dev(inp.X, act), dev(inp.dZ, act)
+    res = {}
+
+    def step():
+        chain.build()
+        res["Y"] = chain.forward(X)
+        res["dX"], res["dq_oR"], res["dq_lin"], res["dq_oP"] = chain.backward(dZ)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (res["Y"], res["dX"], res["dq_oR"][0], *res["dq_lin"], res["dq_oP"][0])]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    outs = (res["Y"], res["dX"], res["dq_oR"][0], *res["dq_lin"], res["dq_oP"][0])
+    for k in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            assert torch.equal(got.view(torch.uint8) if got.dtype == torch.bfloat16 else got,
+                               want.view(torch.uint8) if want.dtype == torch.bfloat16 else want), f"replay {k}"
