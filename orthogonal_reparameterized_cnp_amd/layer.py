@@ -217,8 +217,10 @@ class PoetxAdam:
     zero, together with the bias-correction count.
 
     merge_seeds(step, i) -> (seed_R, seed_P) gives the permutation seeds of
-    linear i at the merge after `step` steps.  The moments are cleared with a
-    torch fill on the given torch stream (None: the current stream).
+    linear i at the merge after `step` steps.  step() takes a torch.cuda.Stream
+    or None (the current stream); the moments are cleared with a torch fill on
+    that stream.  The bias correction uses the step count as a launch argument,
+    so a captured graph of step() would replay one count.
     """
 
     def __init__(self, layers, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8, weight_decay: float = 0.0,
@@ -240,6 +242,8 @@ class PoetxAdam:
 
     def step(self, dqs, stream=None) -> bool:
         """dqs: [(dq_R, dq_P)] per linear.  Returns True when this step ended with a merge."""
+        if stream is not None and not isinstance(stream, torch.cuda.Stream):
+            raise TypeError("stream must be a torch.cuda.Stream or None")
         dq = [x for pair in dqs for x in pair]
         if len(dq) != len(self.m1):
             raise ValueError("one (dq_R, dq_P) pair per linear")
