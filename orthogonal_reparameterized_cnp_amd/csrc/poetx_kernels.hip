@@ -1018,13 +1018,12 @@ hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, in
   if (rows <= 0) return hipSuccess;
   if (cdt == BF16 && in_dt == BF16 && dT_dt == BF16 && out_dt == BF16)
     return apply_bf16(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
+  // fp32 layers (their merge products included: fp32 weight rows times fp32 blocks)
   if (cdt == F32 && in_dt == F32 && dT_dt == F32 && out_dt == F32)
     return apply_t<void, TF, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
-  // merge products: fp32 rows times the stored blocks
+  // merge products of bf16 layers: fp32 weight rows times the stored bf16 blocks
   if (cdt == F32 && in_dt == F32 && dT_dt == BF16 && out_dt == F32)
     return apply_t<void, TFM, float, float, bf16_t, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
-  if (cdt == F32 && in_dt == F32 && dT_dt == F32 && out_dt == F32)
-    return apply_t<void, TFM, float, float, float, float>(in, ld_in, rows, d, b, dT, colscale, out, ld_out, s);
   return hipErrorInvalidValue;
 }
 

@@ -20,6 +20,30 @@ def lead(d: int) -> int:
     return (d + 63) // 64 * 64
 
 
+def _check(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype):
+    """Reject a tensor the kernels would read or write out of bounds: wrong shape, dtype or
+    layout.  Raises ValueError before any launch."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_device(device: torch.device, **tensors):
+    """Every given tensor must live on `device`, which must be a GPU (the kernels take raw device
+    pointers).  Raises ValueError before any launch."""
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        ok = device.type == "cuda" and t.device.type == "cuda"
+        if not ok or t.device.index != (device.index if device.index is not None else torch.cuda.current_device()):
+            raise ValueError(f"{name} is on {t.device}; the layer's kernels run on {device}, which must be a GPU")
+
+
 class PoetxLinear:
     def __init__(self, m: int, n: int, b: int, act: str = "bf16", w: str = "bf16", device: str = "cuda",
                  mode: str = "xfast"):
@@ -43,7 +67,7 @@ class PoetxLinear:
         self.perm_P = torch.arange(n, dtype=torch.int32, device=self.device)
         self.ws = torch.empty(0, **u8)
         self.H_save: Optional[torch.Tensor] = None
-        self.T = 0
+        self.T = None  # tokens of the last forward (the saved state's)
 
     # -- buffers ------------------------------------------------------------
     def _ws(self, nbytes: int) -> torch.Tensor:
@@ -106,8 +130,17 @@ class PoetxLinear:
             ws = self._ws(need)
             B.poetx_cnp_build(q, d, self.b, adt, g, ws, ws.numel(), stream)
 
+    def _act_dt(self) -> torch.dtype:
+        return _TORCH_DT[self.act]
+
     def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        if not isinstance(X, torch.Tensor) or X.dim() != 2:
+            raise ValueError("X must be a 2-D tensor [T, m]")
         T = X.shape[0]
+        _check(X, "X", (T, self.m), self._act_dt())
+        if Y is not None:
+            _check(Y, "Y", (T, self.n), self._act_dt())
+        _check_device(self.device, X=X, Y=Y)
         self.reserve(T)
         if Y is None:
             Y = torch.empty(T, self.n, dtype=X.dtype, device=self.device)
@@ -121,9 +154,28 @@ class PoetxLinear:
             raise ValueError("the xout mode takes H back from the forward's output: pass Y")
         return Y if self.mode == "xout" else None
 
+    def check_backward(self, T: int, dZ: torch.Tensor, Y=None, dX=None, dq_R=None, dq_P=None):
+        """Arguments of a backward over T tokens: the saved state must come from a forward of the
+        same T tokens, and every tensor must match the layer's shapes, dtype and device."""
+        if self.H_save is None or T != self.T:
+            raise ValueError(f"backward over {T} tokens, but the saved state is from a forward of {self.T}")
+        adt = self._act_dt()
+        _check(dZ, "dZ", (T, self.n), adt)
+        if self.mode == "xout":
+            _check(Y, "Y", (T, self.n), adt)
+        if dX is not None:
+            _check(dX, "dX", (T, self.m), adt)
+        if dq_R is not None:
+            _check(dq_R, "dq_R", tuple(self.q_R.shape), torch.float32)
+        if dq_P is not None:
+            _check(dq_P, "dq_P", tuple(self.q_P.shape), torch.float32)
+        _check_device(self.device, dZ=dZ, Y=Y if self.mode == "xout" else None, dX=dX, dq_R=dq_R, dq_P=dq_P)
+
     def backward(self, X: torch.Tensor, dZ: torch.Tensor, dX=None, dq_R=None, dq_P=None, stream=None, Y=None):
         """X only gives T (the gathered input is in the saved state); Y: the forward's output (xout)."""
         T = X.shape[0]
+        self._y_arg(Y)
+        self.check_backward(T, dZ, Y, dX, dq_R, dq_P)
         self.reserve(T)
         if dX is None:
             dX = torch.empty(T, self.m, dtype=X.dtype, device=self.device)
@@ -189,6 +241,8 @@ class PoetxGroup:
         """dX of linear i; its block gradients go to the group's gradient state (Y: as PoetxLinear.backward)."""
         lay = self.layers[i]
         T = X.shape[0]
+        lay._y_arg(Y)
+        lay.check_backward(T, dZ, Y, dX)
         lay.reserve(T)
         if dX is None:
             dX = torch.empty(T, lay.m, dtype=X.dtype, device=self.device)
@@ -283,6 +337,7 @@ class PoetxSpoFactor:
         self.g = torch.empty(B.poetx_g_bytes(self.d_eff, b, self.adt), dtype=torch.uint8, device=self.device)
         self.saved = torch.empty(0, dtype=torch.uint8, device=self.device)
         self.ws = torch.empty(0, dtype=torch.uint8, device=self.device)
+        self.T = None  # rows of the last forward (the saved state's)
 
     def load(self, idx, q):
         self.idx.copy_(idx)
@@ -305,15 +360,34 @@ class PoetxSpoFactor:
         B.poetx_cnp_build(self.q, self.d_eff, self.b, self.adt, self.g, ws, ws.numel(), stream)
 
     def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        if not isinstance(X, torch.Tensor) or X.dim() != 2:
+            raise ValueError("X must be a 2-D tensor [T, d]")
         T = X.shape[0]
+        adt = _TORCH_DT[self.act]
+        _check(X, "X", (T, self.d), adt)
+        if Y is not None:
+            _check(Y, "Y", (T, self.d), adt)
+        _check_device(self.device, X=X, Y=Y)
         self.reserve(T)
         if Y is None:
             Y = torch.empty_like(X)
         B.poetx_spo_fwd(self.desc, T, X, self.idx, self.g, Y, self.saved, self.ws, self.ws.numel(), stream)
+        self.T = T
         return Y
 
     def backward(self, dY: torch.Tensor, dX=None, dq=None, stream=None):
+        if not isinstance(dY, torch.Tensor) or dY.dim() != 2:
+            raise ValueError("dY must be a 2-D tensor [T, d]")
         T = dY.shape[0]
+        if T != self.T:
+            raise ValueError(f"backward over {T} rows, but the saved state is from a forward of {self.T}")
+        adt = _TORCH_DT[self.act]
+        _check(dY, "dY", (T, self.d), adt)
+        if dX is not None:
+            _check(dX, "dX", (T, self.d), adt)
+        if dq is not None:
+            _check(dq, "dq", tuple(self.q.shape), torch.float32)
+        _check_device(self.device, dY=dY, dX=dX, dq=dq)
         self.reserve(T)
         if dX is None:
             dX = torch.empty_like(dY)

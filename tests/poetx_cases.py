@@ -99,6 +99,23 @@ def run_oracle(inp, backward: bool = True, h_output: bool = False):
     return out
 
 
+def dead_slot_mask(d: int, b: int) -> np.ndarray:
+    """Packed slots of the last block of a side of length d that lie outside its r x r
+    corner (slot (i, j), i < j, with j >= r); empty when the last block is whole."""
+    r = d - (-(-d // b) - 1) * b
+    _, ju = np.triu_indices(b, 1)
+    return ju >= r
+
+
+def assert_dead_slots_zero(name: str, dq: torch.Tensor, d: int, b: int):
+    """dq of the slots a partial last block does not use must be written as +0.0, bit for bit."""
+    mask = dead_slot_mask(d, b)
+    if not mask.any():
+        return
+    bits = dq[-1].detach().cpu().view(torch.int32).numpy()[mask]
+    assert not bits.any(), f"{name}: {np.count_nonzero(bits)} dead slots of the last block are not +0.0"
+
+
 def compare_layer(inp, gpu, ref, backward: bool = True):
     kind = inp.act
     assert_close("Y", host(gpu["Y"], kind), ref["Y"], kind)
@@ -108,3 +125,5 @@ def compare_layer(inp, gpu, ref, backward: bool = True):
         assert_close("dX", host(gpu["dX"], kind), ref["dX"], kind)
         assert_close("dq_R", host(gpu["dq_R"], "f32"), ref["dq_R"], kind)
         assert_close("dq_P", host(gpu["dq_P"], "f32"), ref["dq_P"], kind)
+        assert_dead_slots_zero("dq_R", gpu["dq_R"], inp.m, inp.b)
+        assert_dead_slots_zero("dq_P", gpu["dq_P"], inp.n, inp.b)

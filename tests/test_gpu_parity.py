@@ -243,34 +243,3 @@ def test_merge_reinit(m, n, b, act, w, std):
     ma = np.linalg.norm(Y1 - Y0) / np.linalg.norm(Y0)
     print(f"  fwd after/before merge: rel fro {ma:.3e}")
     assert ma <= lim
-
-
-# ----------------------------------------------------------------------------
-# full-size layers, in the launch configuration the benchmark times:
-# sampled token rows of Y and dX, and sampled blocks of dq (sums over all tokens)
-# ----------------------------------------------------------------------------
-@pytest.mark.parametrize("wl,lin", [("llama8b", 0), ("llama8b", 6), ("llama13b_int8", 4)])
-def test_full_size_sampled(wl, lin):
-    inp = make_linear_inputs(WORKLOADS[wl], lin)
-    out = run_gpu(inp)
-    kind = inp.act
-    rng = np.random.default_rng(lin)
-    rows = np.sort(rng.choice(inp.T, 48, replace=False))
-    X = O.to_f64(inp.X[rows], kind)
-    dZ = O.to_f64(inp.dZ[rows], kind)
-    W = O.to_f64(inp.W0, inp.w, inp.w_scale)
-    q_R, q_P = inp.q_R.astype(np.float64), inp.q_P.astype(np.float64)
-    G_R, G_P = O.side_G(q_R, inp.m, inp.b), O.side_G(q_P, inp.n, inp.b)
-    f = O.forward(X, W, inp.perm_R, inp.perm_P, G_R, G_P)
-    assert_close("Y rows", host(out["Y"], kind)[rows], f.Y, kind)
-    g = O.backward(X, dZ, W, inp.perm_R, inp.perm_P, q_R, q_P, inp.b)
-    assert_close("dX rows", host(out["dX"], kind)[rows], g.dX, kind)
-    nbR, nbP = inp.q_R.shape[0], inp.q_P.shape[0]
-    bR, bP = [0, nbR - 1], [nbP // 2]
-    ref = O.block_grads(O.to_f64(inp.X, kind), O.to_f64(inp.dZ, kind), W, inp.perm_R, inp.perm_P, q_R, q_P, inp.b,
-                        bR, bP)
-    dqR, dqP = host(out["dq_R"], "f32"), host(out["dq_P"], "f32")
-    for k in bR:
-        assert_close(f"dq_R[{k}]", dqR[k], ref[("R", k)], kind)
-    for k in bP:
-        assert_close(f"dq_P[{k}]", dqP[k], ref[("P", k)], kind)
