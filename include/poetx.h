@@ -180,6 +180,26 @@ poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype
                              void* stream);
 
 /*
+ * poetx_cnp_build for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same kernels and the same result, bit for bit, with the workspace taken
+ * from a fixed device array inside the library instead of a caller buffer.
+ *   q, d, b, dtype, g  as for poetx_cnp_build
+ *   stream   must belong to the current device
+ * The array holds POETX_NOALLOC_SCRATCH_BYTES (80 MiB) on each GPU the call
+ * runs on, from the first call on that GPU until the process ends; that is
+ * room for poetx_workspace_size(desc with m = d, 0, POETX_OP_CNP) of any side
+ * up to 32 blocks of 512 in bf16 (d <= 16384 at b = 512) or 20 in fp32.
+ * Every call on one GPU uses the same array: calls that overlap in time on one
+ * GPU (other streams, other threads) race and must be serialised by the caller.
+ * The call allocates nothing (no hipMalloc or torch allocation).
+ * Errors: POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE (the
+ * side's workspace exceeds the array), POETX_E_HIP.
+ */
+#define POETX_NOALLOC_SCRATCH_BYTES (80u << 20)
+poetx_status poetx_cnp_build_noalloc(const float* q, int32_t d, int32_t b, int32_t dtype, void* g, void* stream);
+
+/*
  * Fold the two permutations adjacent to W0 into it (zhichai.net blog, 第二斧;
  * gist.science summary, 2. Metodologia: four permutations reduced to two):
  * Wt[i][j] = W0[perm_R[i]][perm_P[j]], and for POETX_I8 scale_t[j] = scale[perm_P[j]].

@@ -86,6 +86,7 @@ _SIG = {
     "poetx_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.c_int64, ctypes.c_int32]),
     "poetx_perm_from_seed": (ctypes.c_int, [ctypes.c_uint64, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32)]),
     "poetx_cnp_build": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]),
+    "poetx_cnp_build_noalloc": (ctypes.c_int, [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P]),
     "poetx_premerge": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, ctypes.c_int64, _P, _P, _P, _P, _P]),
     "poetx_linear_fwd": (
         ctypes.c_int,
@@ -238,6 +239,10 @@ def poetx_timer_read():
 # ------------------------------------------------------------- the calls ---
 def poetx_cnp_build(q, d: int, b: int, dtype: int, g, ws, ws_bytes: int, stream=None):
     _check(lib().poetx_cnp_build(_ptr(q), d, b, dtype, _ptr(g), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def poetx_cnp_build_noalloc(q, d: int, b: int, dtype: int, g, stream=None):
+    _check(lib().poetx_cnp_build_noalloc(_ptr(q), d, b, dtype, _ptr(g), _stream(stream)))
 
 
 def poetx_premerge(dsc: LayerDesc, W0, ld_w0: int, w0_scale, perm_R, perm_P, Wt, stream=None):

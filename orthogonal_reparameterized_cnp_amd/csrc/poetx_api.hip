@@ -11,6 +11,12 @@
 
 using namespace pxk;
 
+// Workspace of poetx_cnp_build_noalloc: a fixed device array of the library.
+// Each GPU the library runs on holds its own copy for the life of the process.
+// Host code never uses the name as an address (on the host it is a stand-in
+// symbol); the device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[POETX_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_err;
@@ -221,6 +227,33 @@ poetx_status check_sides(int32_t count, const int32_t* d, int32_t b, int32_t dty
   return POETX_OK;
 }
 
+// Device address of `scratch` on the current device, looked up the first time
+// the device is seen and kept per device ordinal.
+struct ScratchTable {
+  std::mutex mu;
+  std::vector<void*> ptr;
+};
+ScratchTable& scratch_table() {
+  static ScratchTable t;
+  return t;
+}
+poetx_status scratch_ptr(void** out) {
+  int dev = -1;
+  PX_HIP(hipGetDevice(&dev));
+  if (dev < 0) return fail(POETX_E_HIP, "no current device");
+  ScratchTable& t = scratch_table();
+  std::lock_guard<std::mutex> g(t.mu);
+  if ((int)t.ptr.size() <= dev) t.ptr.resize(dev + 1, nullptr);
+  if (!t.ptr[dev]) {
+    void* p = nullptr;
+    PX_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(POETX_E_HIP, "hipGetSymbolAddress returned NULL for the scratch array");
+    t.ptr[dev] = p;
+  }
+  *out = t.ptr[dev];
+  return POETX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -319,6 +352,24 @@ poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype
                              void* stream) {
   if (!q || !g) return fail(POETX_E_NULL, "q and g must be non-NULL");
   return poetx_cnp_build_batch(1, &q, &d, b, dtype, &g, ws, ws_bytes, stream);
+}
+
+poetx_status poetx_cnp_build_noalloc(const float* q, int32_t d, int32_t b, int32_t dtype, void* g, void* stream) {
+  if (!q || !g) return fail(POETX_E_NULL, "q and g must be non-NULL");
+  int64_t blocks = 0;
+  poetx_status st = check_sides(1, &d, b, dtype, &blocks);
+  if (st != POETX_OK) return st;
+  const size_t need = cnp_build_ws_bytes(dtype, blocks, b);
+  if (need > (size_t)POETX_NOALLOC_SCRATCH_BYTES)
+    return fail(POETX_E_WORKSPACE, "side needs " + std::to_string(need) + " bytes of scratch; the fixed array holds " +
+                                       std::to_string((size_t)POETX_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  st = scratch_ptr(&ws);
+  if (st != POETX_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const double flops = 4 * sum_r3(d, b), bytes = 2.0 * g_slice(d, b, dtype) + 2.0 * nblocks(d, b) * b * b * 4;
+  PX_TIMED(POETX_KC_CNP, flops, bytes, cnp_build_batch(dtype, 1, &q, &d, b, &g, ws, s));
+  return POETX_OK;
 }
 
 size_t poetx_cnp_batch_workspace_size(int32_t count, const int32_t* d, int32_t b, int32_t dtype) {
