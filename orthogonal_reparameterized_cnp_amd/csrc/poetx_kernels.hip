@@ -134,6 +134,8 @@ __global__ __launch_bounds__(C::NT) void k_apply(const IT* __restrict__ in, int6
                                           [&](int c) { return cs ? cs[c] : 1.f; });
   };
   if constexpr (!std::is_same<CD, void>::value) {
+    // the direct-to-LDS loop deals its copies and fragments over CD::NT threads: it must be the launch size
+    static_assert(CD::NT == C::NT, "direct-to-LDS configuration and tile loop must use the same workgroup size");
     OT* o0 = out + (int64_t)m0 * ld_out + kb + n0;
     if (dma_rows_ok(a0, ld_in, rows - m0, CD::BM) && dma_rows_ok(b0, b, r - n0, CD::BN) && r % CD::BK == 0 &&
         reinterpret_cast<uintptr_t>(o0) % 16 == 0 && ld_out % 8 == 0) {
@@ -432,6 +434,8 @@ __global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_
   const int m0 = bm * C::BM, n0 = bn * C::BN;
   const float* cs = colscale ? colscale + n0 : nullptr;
   if constexpr (!std::is_same<CD, void>::value) {
+    // the direct-to-LDS loop deals its copies and fragments over CD::NT threads: it must be the launch size
+    static_assert(CD::NT == C::NT, "direct-to-LDS configuration and tile loop must use the same workgroup size");
     const AT* a0 = A + (int64_t)m0 * lda;
     const BT* b0 = B + (int64_t)n0 * ldb;
     if (dma_rows_ok(a0, lda, M - m0, CD::BM) && dma_rows_ok(b0, ldb, N - n0, CD::BN) && K % CD::BK == 0) {
