@@ -288,26 +288,29 @@ def committed_traffic():
     return None
 
 
-def time_merge(key, to_dev, dev):
+def time_merge(key, to_dev, dev, layers=None):
     """poetx_merge_reinit of every linear of one decoder layer of workload `key` (merge-then-reinitialise:
     fold R and P into the weight, requantise int8 per column, draw new permutations, zero q), timed with
-    events around the calls after one untimed merge; amortised over the workload's merge period."""
+    events around the calls after one untimed merge; amortised over the workload's merge period.
+    `layers`: the workload's PoetxLinear objects if already built (their weights are merged in place)."""
     import torch
 
     from orthogonal_reparameterized_cnp_amd.layer import PoetxLinear
     from workloads import WORKLOADS, make_linear_inputs
 
     wl = WORKLOADS[key]
-    layers = []
-    for i in range(len(wl.linears)):
-        inp = make_linear_inputs(wl, i, T=1)
-        lay = PoetxLinear(inp.m, inp.n, inp.b, inp.act, inp.w)
-        scale = to_dev(inp.w_scale, "f32") if inp.w == "i8" else None
-        lay.load(to_dev(inp.W0, inp.w), scale, to_dev(inp.perm_R, "i32"), to_dev(inp.perm_P, "i32"),
-                 to_dev(inp.q_R, "f32"), to_dev(inp.q_P, "f32"))
+    if layers is None:
+        layers = []
+        for i in range(len(wl.linears)):
+            inp = make_linear_inputs(wl, i, T=1)
+            lay = PoetxLinear(inp.m, inp.n, inp.b, inp.act, inp.w)
+            scale = to_dev(inp.w_scale, "f32") if inp.w == "i8" else None
+            lay.load(to_dev(inp.W0, inp.w), scale, to_dev(inp.perm_R, "i32"), to_dev(inp.perm_P, "i32"),
+                     to_dev(inp.q_R, "f32"), to_dev(inp.q_P, "f32"))
+            layers.append(lay)
+    for lay in layers:
         lay.build()
         lay._ws(lay.ws_bytes(1))
-        layers.append(lay)
     torch.cuda.synchronize()
 
     def merge_all(seed):
@@ -376,6 +379,152 @@ def time_spo(T, d, b, act, to_dev):
     return out
 
 
+class WorkloadStep:
+    """One decoder layer of a workload on the GPU: seeded inputs resident in HBM, and step(), the
+    whole hot path over one batch (batched CNP build, the forwards, the backwards to dX and the block
+    gradients, the batched CNP chain rule to every side's packed dq, and optionally the Adam step)."""
+
+    def __init__(self, wl, mode, to_dev, dev, optimizer=False):
+        import torch
+
+        from orthogonal_reparameterized_cnp_amd.layer import PoetxAdam, PoetxGroup, PoetxLinear
+        from workloads import make_linear_inputs
+
+        self.wl, self.mode, self.T = wl, mode, wl.T
+        self.layers, self.Xs, self.dZs, self.inputs0 = [], [], [], None
+        for i in range(len(wl.linears)):
+            inp = make_linear_inputs(wl, i)
+            lay = PoetxLinear(inp.m, inp.n, inp.b, inp.act, inp.w, mode=mode)
+            scale = to_dev(inp.w_scale, "f32") if inp.w == "i8" else None
+            lay.load(to_dev(inp.W0, inp.w), scale, to_dev(inp.perm_R, "i32"), to_dev(inp.perm_P, "i32"),
+                     to_dev(inp.q_R, "f32"), to_dev(inp.q_P, "f32"))
+            lay.reserve(self.T)
+            self.layers.append(lay)
+            self.Xs.append(to_dev(inp.X, inp.act))
+            self.dZs.append(to_dev(inp.dZ, inp.act))
+            if i == 0:
+                self.inputs0 = inp
+        dt = self.Xs[0].dtype
+        self.Ys = [torch.empty(self.T, L.n, dtype=dt, device=dev) for L in wl.linears]
+        self.dXs = [torch.empty(self.T, L.m, dtype=dt, device=dev) for L in wl.linears]
+        self.dqs = [(torch.empty_like(l.q_R), torch.empty_like(l.q_P)) for l in self.layers]
+        # The layer's seven linears share their CNP work: every side's G is built in one batch, and the
+        # chain rule to dq runs once for all sides after the backward of the last linear (results
+        # bit-identical to per-linear calls).
+        self.group = PoetxGroup(self.layers)
+        # Adam on every side's packed q (lr small enough that the timed steps stay near the start)
+        self.opt = PoetxAdam(self.layers, lr=1e-5)
+        self.optimizer = optimizer
+        torch.cuda.synchronize()
+
+    def step(self):
+        self.group.build()
+        for lay, X, Y in zip(self.layers, self.Xs, self.Ys):
+            lay.forward(X, Y)
+        for i in reversed(range(len(self.layers))):
+            self.group.backward_dx(i, self.Xs[i], self.dZs[i], self.dXs[i], Y=self.Ys[i] if self.mode == "xout" else None)
+        self.group.backward_q(self.dqs)
+        if self.optimizer:
+            self.opt.step(self.dqs)
+
+
+def timed(fn, steps):
+    """Average ms per call of fn over `steps` calls between two events on the current stream, with a
+    device synchronisation before and after; also the host wall time of the region."""
+    import torch
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, time.perf_counter() - t0
+
+
+def weight_centric_flops(wl, T):
+    """Algorithmic flops of one weight-centric step: the three block products over the weight, the
+    forward contraction, dX and the weight gradient dM, the block gradients from dM, the CNP work."""
+    tot = 0.0
+    for L in wl.linears:
+        r2R, r3R = side_sums(L.m, wl.b)
+        r2P, r3P = side_sums(L.n, wl.b)
+        tot += 2.0 * L.n * r2R + 4.0 * L.m * r2P  # U^T, V, M
+        tot += 6.0 * T * L.m * L.n  # Y, dX, dM
+        tot += 2.0 * L.n * r2R + 2.0 * L.m * r2P  # dG_R, dG_P
+        tot += 16.0 * (r3R + r3P)
+    return tot
+
+
+def time_weight_centric(ws, steps, ic_ms):
+    """The same step computed weight-centric (poetx_wc_fwd / poetx_wc_bwd on the same layers: the factors
+    applied to the weight, dense contractions, the full weight gradient), timed like the headline."""
+    import torch
+
+    from orthogonal_reparameterized_cnp_amd.layer import PoetxWeightCentric
+
+    wcs = [PoetxWeightCentric(l) for l in ws.layers]
+    for wc in wcs:
+        wc.reserve(ws.T)
+
+    def wstep():
+        ws.group.build()
+        for wc, X, Y in zip(wcs, ws.Xs, ws.Ys):
+            wc.forward(X, Y)
+        for i in reversed(range(len(wcs))):
+            wcs[i].backward(ws.dZs[i], ws.dXs[i], *ws.dqs[i])
+
+    for _ in range(2):
+        wstep()
+    ms, _ = timed(wstep, steps)
+    fl = weight_centric_flops(ws.wl, ws.T)
+    print(f"[bench] weight-centric step: {ms:.3f} ms ({ms / ic_ms:.2f}x the input-centric step)",
+          file=sys.stderr, flush=True)
+    del wcs
+    torch.cuda.empty_cache()
+    return {
+        "ms_per_step": ms,
+        "ratio_to_input_centric": ms / ic_ms,
+        "tflop_per_step": fl / 1e12,
+        "tflops": fl / (ms * 1e-3) / 1e12,
+        "what": "poetx_wc_fwd / poetx_wc_bwd on the same layers and inputs: M = Diag(G_R) W~ Diag(G_P) built "
+                "every step, dense contractions with M, the weight gradient dM = Xt^T dZt, block gradients "
+                "from dM; CNP build batched as in the headline, CNP chain rule per linear",
+    }
+
+
+SECONDARY = ("linear256_fp32", "llama60m", "llama1p3b", "llama13b_int8")
+
+
+def time_secondary(key, to_dev, dev):
+    """One step of another workload (same structure as the headline), timed after two warm-up steps; the
+    int8 Llama-13B layer also times its merge-then-reinitialise, amortised over its merge period."""
+    import torch
+
+    from workloads import WORKLOADS
+
+    wl = WORKLOADS[key]
+    ws = WorkloadStep(wl, "xfast", to_dev, dev)
+    for _ in range(2):
+        ws.step()
+    steps = 50 if wl.T * sum(L.m * L.n for L in wl.linears) < 1e10 else 5
+    ms, _ = timed(ws.step, steps)
+    g, a, c = step_flops(wl, wl.T)
+    tf = (g + a + c) / (ms * 1e-3) / 1e12
+    out = {"workload": describe(wl), "weights": wl.w, "tokens": wl.T, "b": wl.b, "steps": steps, "ms_per_step": ms,
+           "tokens_per_s": wl.T / (ms * 1e-3), "tflops": tf, "mfma_peak_frac": tf / PEAK_TFLOPS[wl.act],
+           "peak": f"{wl.act} dense MFMA {PEAK_TFLOPS[wl.act]} TFLOP/s"}
+    print(f"[bench] {key}: {ms:.3f} ms per step, {out['tokens_per_s']:.0f} tokens/s, {tf:.0f} TFLOP/s",
+          file=sys.stderr, flush=True)
+    if wl.merge_every:
+        out["merge"] = time_merge(key, to_dev, dev, layers=ws.layers)
+    del ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -384,6 +533,8 @@ def main():
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="per kernel class timings on stderr")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the weight-centric comparison and the other workloads' lines")
     ap.add_argument("--mode", choices=("xfast", "xmem", "xout"), default="xfast",
                     help="xfast saves H for the backward; xmem saves only the gathered input and recomputes H; "
                          "xout saves only the gathered input and takes H back from the output")
@@ -405,14 +556,14 @@ def main():
                     help="write the k_gemm traffic summary from two rocprofv3 --pmc runs and exit (no GPU)")
     args = ap.parse_args()
     if args.summarize_traffic:
-        base = "rocprofv3 --pmc {c} --output-format csv -d {d} -o llama8b -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-probe"
+        base = "rocprofv3 --pmc {c} --output-format csv -d {d} -o llama8b -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --headline-only --copy-probe"
         summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1],
                           base.format(c="FETCH_SIZE", d=args.summarize_traffic[0]),
                           base.format(c="WRITE_SIZE", d=args.summarize_traffic[1]))
         return
     if args.summarize_classes:
         m, f, w = args.summarize_classes
-        base = "rocprofv3 --pmc {c} --output-format csv -d {d} -o llama8b -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline"
+        base = "rocprofv3 --pmc {c} --output-format csv -d {d} -o llama8b -- python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline --headline-only"
         summarize_classes(m, f, w, (base.format(c="SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE", d=m),
                                     base.format(c="FETCH_SIZE", d=f) + " --copy-probe",
                                     base.format(c="WRITE_SIZE", d=w) + " --copy-probe"))
@@ -424,8 +575,7 @@ def main():
     import torch
 
     from orthogonal_reparameterized_cnp_amd import binding as B
-    from orthogonal_reparameterized_cnp_amd.layer import PoetxAdam, PoetxGroup, PoetxLinear
-    from workloads import WORKLOADS, make_linear_inputs
+    from workloads import WORKLOADS
 
     B.lib()
     wl = WORKLOADS[args.workload]
@@ -438,41 +588,9 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     t_gen = time.perf_counter()
-    layers, Xs, dZs, inputs0 = [], [], [], None
-    for i in range(len(wl.linears)):
-        inp = make_linear_inputs(wl, i)
-        lay = PoetxLinear(inp.m, inp.n, inp.b, inp.act, inp.w, mode=args.mode)
-        scale = to_dev(inp.w_scale, "f32") if inp.w == "i8" else None
-        lay.load(to_dev(inp.W0, inp.w), scale, to_dev(inp.perm_R, "i32"), to_dev(inp.perm_P, "i32"),
-                 to_dev(inp.q_R, "f32"), to_dev(inp.q_P, "f32"))
-        lay.reserve(T)
-        layers.append(lay)
-        Xs.append(to_dev(inp.X, inp.act))
-        dZs.append(to_dev(inp.dZ, inp.act))
-        if i == 0:
-            inputs0 = inp
-    Ys = [torch.empty(T, L.n, dtype=Xs[0].dtype, device=dev) for L in wl.linears]
-    dXs = [torch.empty(T, L.m, dtype=Xs[0].dtype, device=dev) for L in wl.linears]
-    dqs = [(torch.empty_like(l.q_R), torch.empty_like(l.q_P)) for l in layers]
-    torch.cuda.synchronize()
+    ws = WorkloadStep(wl, args.mode, to_dev, dev, optimizer=args.optimizer)
+    layers, inputs0, opt, dqs, step = ws.layers, ws.inputs0, ws.opt, ws.dqs, ws.step
     print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
-
-    # The layer's seven linears share their CNP work: every side's G is built in
-    # one batch, and the chain rule to dq runs once for all sides after the
-    # backward of the last linear (results bit-identical to per-linear calls).
-    group = PoetxGroup(layers)
-    # Adam on every side's packed q (lr small enough that the timed steps stay near the start)
-    opt = PoetxAdam(layers, lr=1e-5)
-
-    def step():
-        group.build()
-        for lay, X, Y in zip(layers, Xs, Ys):
-            lay.forward(X, Y)
-        for i in reversed(range(len(layers))):
-            group.backward_dx(i, Xs[i], dZs[i], dXs[i], Y=Ys[i] if args.mode == "xout" else None)
-        group.backward_q(dqs)
-        if args.optimizer:
-            opt.step(dqs)
 
     for _ in range(args.warmup):
         step()
@@ -504,26 +622,19 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
 
-    def timed(fn):
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record()
-        for _ in range(args.steps):
-            fn()
-        end.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(end) / args.steps, time.perf_counter() - t0
-
+    # the timed steps run with the library's measurement timer off
     if graph is not None:
-        ms, wall = timed(graph.replay)
-    B.poetx_timer_enable(B.POETX_KC_GEMM)
-    B.poetx_timer_read()
-    ms_eager, wall_eager = timed(step)
-    n_launch, k_ms, k_flops, k_bytes = B.poetx_timer_read()
-    B.poetx_timer_enable(B.POETX_KC_NONE)
+        ms, wall = timed(graph.replay, args.steps)
+    ms_eager, wall_eager = timed(step, args.steps)
     if graph is None:
         ms, wall = ms_eager, wall_eager
+    # the W~ contraction rate: a separate pass of the same number of steps with hipEvents recorded
+    # around every k_gemm launch on its stream
+    B.poetx_timer_enable(B.POETX_KC_GEMM)
+    B.poetx_timer_read()
+    timed(step, args.steps)
+    n_launch, k_ms, k_flops, k_bytes = B.poetx_timer_read()
+    B.poetx_timer_enable(B.POETX_KC_NONE)
 
     peak = PEAK_TFLOPS[wl.act]
     achieved = k_flops / (k_ms * 1e-3) / 1e12 if k_ms > 0 else 0.0
@@ -567,6 +678,8 @@ def main():
         },
         "wall_s_timed": wall,
         "ms_per_step_eager": ms_eager,
+        "timing": "step timed with the library's launch timer off; roofline.achieved from a separate pass of "
+                  "the same number of steps with hipEvents around every W~ contraction launch",
     }
 
     # the optimiser step on its own (outside the timed region): HBM-bound, 28 bytes per packed slot;
@@ -604,10 +717,17 @@ def main():
             print(f"[bench] {name:8s} launches={n:3d} ms/step={kms:8.3f} TFLOP/s={rate:7.1f} "
                   f"alg GB/s={bw:7.1f}", file=sys.stderr, flush=True)
 
+    if not args.headline_only:
+        result["weight_centric"] = time_weight_centric(ws, args.steps, ms)
     if args.merge:
         result["merge"] = time_merge(args.merge, to_dev, dev)
     if args.spo:
         result["spo_factor"] = time_spo(T, max(max(L.m, L.n) for L in wl.linears), wl.b, wl.act, to_dev)
+
+    if not args.headline_only and args.workload == "llama8b":
+        del ws, layers, opt, dqs, step
+        torch.cuda.empty_cache()
+        result["other_workloads"] = {k: time_secondary(k, to_dev, dev) for k in SECONDARY}
 
     if not args.no_cpu_baseline:
         lin_f = 4.0 * T * inputs0.m * inputs0.n

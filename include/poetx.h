@@ -437,6 +437,61 @@ typedef struct {
 poetx_status poetx_adam_step_batch(int32_t count, const int64_t* len, float* const* q, const float* const* dq,
                                    float* const* m1, float* const* m2, const poetx_adam_params* hp, void* stream);
 
+/* ----------------------------------- weight-centric baseline (comparison) -- */
+
+/*
+ * The same layer computed in the order original POET uses, for comparison with
+ * the input-centric calls above (zhichai.net POET-X blog, 第一斧; wispaper.ai
+ * POET-X blog, "The 'Weight-Centric' Wall"): the factors are applied to the
+ * weight first, M = Diag(G_R) W~ Diag(G_P) (so that R W0 P = Psi_R^T M Psi_P),
+ * and each direction is then one dense contraction with M.  The backward forms
+ * the full weight gradient dM = Xt^T dZt and takes the block gradients from it:
+ * dG_R = diagonal blocks of dM (W~ Diag(G_P))^T, dG_P = diagonal blocks of
+ * (Diag(G_R) W~)^T dM.  The results are the same function and gradients as
+ * poetx_linear_fwd / poetx_linear_bwd (up to rounding: M, the weight-side
+ * products and dM are stored in act_dtype).
+ * Supported layers: (act, weight) = (F32, F32) or (BF16, BF16); others get
+ * POETX_E_UNSUPPORTED.
+ */
+
+/* Bytes of the state poetx_wc_fwd leaves for poetx_wc_bwd of the same T rows:
+ * M and U = Diag(G_R) W~ as [m][round_up(n, 64)], (W~ Diag(G_P))^T as
+ * [n][round_up(m, 64)], and Xt = X[:, perm_R] as [T][round_up(m, 64)], each at
+ * a 256-byte boundary, in act_dtype; 0 for invalid arguments. */
+size_t poetx_wc_state_bytes(const poetx_layer_desc* desc, int64_t T);
+
+/* Workspace bytes of poetx_wc_fwd (op = POETX_OP_FWD) or poetx_wc_bwd
+ * (POETX_OP_BWD); 0 for invalid arguments. */
+size_t poetx_wc_workspace_size(const poetx_layer_desc* desc, int64_t T, int32_t op);
+
+/*
+ * Weight-centric forward: build M (three block products over the weight and
+ * their transposes), then Y[:, perm_P] = X[:, perm_R] M.
+ *   X, perm_R, perm_P, Wt, g_R, g_P, Y  as for poetx_linear_fwd
+ *   state  out, poetx_wc_state_bytes(desc, T) bytes, 256-byte aligned
+ *   ws     >= poetx_wc_workspace_size(desc, T, POETX_OP_FWD)
+ * T = 0 builds M only.
+ * Errors: POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_UNSUPPORTED,
+ * POETX_E_WORKSPACE, POETX_E_HIP.
+ */
+poetx_status poetx_wc_fwd(const poetx_layer_desc* desc, int64_t T, const void* X, const int32_t* perm_R,
+                          const int32_t* perm_P, const void* Wt, const void* g_R, const void* g_P, void* Y, void* state,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Weight-centric backward for upstream gradient dZ: dX = dZ[:, perm_P] M^T
+ * scattered by perm_R, and dq_R, dq_P through the weight gradient dM (see
+ * above), the CNP chain rule and the skew projection, as in poetx_linear_bwd.
+ *   dZ [T][n], dX out [T][m], q_R, q_P, dq_R, dq_P  as for poetx_linear_bwd
+ *   state  written by poetx_wc_fwd for the same T rows
+ *   ws     >= poetx_wc_workspace_size(desc, T, POETX_OP_BWD)
+ * Errors: as for poetx_wc_fwd.
+ */
+poetx_status poetx_wc_bwd(const poetx_layer_desc* desc, int64_t T, const void* dZ, const int32_t* perm_R,
+                          const int32_t* perm_P, const void* g_R, const void* g_P, const float* q_R, const float* q_P,
+                          const void* state, void* dX, float* dq_R, float* dq_P, void* ws, size_t ws_bytes,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

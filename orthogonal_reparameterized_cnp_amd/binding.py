@@ -128,6 +128,10 @@ _SIG = {
     "poetx_spo_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(SpoDesc), ctypes.c_int64, ctypes.c_int32]),
     "poetx_spo_fwd": (ctypes.c_int, [ctypes.POINTER(SpoDesc), ctypes.c_int64] + [_P] * 6 + [ctypes.c_size_t, _P]),
     "poetx_spo_bwd": (ctypes.c_int, [ctypes.POINTER(SpoDesc), ctypes.c_int64] + [_P] * 8 + [ctypes.c_size_t, _P]),
+    "poetx_wc_state_bytes": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.c_int64]),
+    "poetx_wc_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.c_int64, ctypes.c_int32]),
+    "poetx_wc_fwd": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int64] + [_P] * 9 + [ctypes.c_size_t, _P]),
+    "poetx_wc_bwd": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int64] + [_P] * 12 + [ctypes.c_size_t, _P]),
     "poetx_adam_step_batch": (
         ctypes.c_int,
         [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(_P), ctypes.POINTER(_P), ctypes.POINTER(_P),
@@ -353,3 +357,24 @@ def poetx_spo_fwd(dsc: SpoDesc, T: int, X, idx, G, Y, saved, ws, ws_bytes: int, 
 def poetx_spo_bwd(dsc: SpoDesc, T: int, dY, idx, G, q, saved, dX, dq, ws, ws_bytes: int, stream=None):
     _check(lib().poetx_spo_bwd(ctypes.byref(dsc), T, _ptr(dY), _ptr(idx), _ptr(G), _ptr(q), _ptr(saved), _ptr(dX),
                                _ptr(dq), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+# --------------------------------------------------- weight-centric baseline ---
+def poetx_wc_state_bytes(dsc: LayerDesc, T: int) -> int:
+    return lib().poetx_wc_state_bytes(ctypes.byref(dsc), T)
+
+
+def poetx_wc_workspace_size(dsc: LayerDesc, T: int, op: int) -> int:
+    return lib().poetx_wc_workspace_size(ctypes.byref(dsc), T, op)
+
+
+def poetx_wc_fwd(dsc: LayerDesc, T: int, X, perm_R, perm_P, Wt, g_R, g_P, Y, state, ws, ws_bytes: int, stream=None):
+    _check(lib().poetx_wc_fwd(ctypes.byref(dsc), T, _ptr(X), _ptr(perm_R), _ptr(perm_P), _ptr(Wt), _ptr(g_R), _ptr(g_P),
+                              _ptr(Y), _ptr(state), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def poetx_wc_bwd(dsc: LayerDesc, T: int, dZ, perm_R, perm_P, g_R, g_P, q_R, q_P, state, dX, dq_R, dq_P, ws,
+                 ws_bytes: int, stream=None):
+    _check(lib().poetx_wc_bwd(ctypes.byref(dsc), T, _ptr(dZ), _ptr(perm_R), _ptr(perm_P), _ptr(g_R), _ptr(g_P),
+                              _ptr(q_R), _ptr(q_P), _ptr(state), _ptr(dX), _ptr(dq_R), _ptr(dq_P), _ptr(ws), ws_bytes,
+                              _stream(stream)))

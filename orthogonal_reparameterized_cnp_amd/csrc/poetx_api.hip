@@ -1,6 +1,7 @@
 // C ABI of libpoetx: argument validation, workspace planning and the order of
 // kernel launches for each call.  All arithmetic happens in the kernels of
 // poetx_kernels.hip.
+#include <algorithm>
 #include <cmath>
 #include <mutex>
 #include <string>
@@ -826,6 +827,195 @@ poetx_status poetx_adam_step_batch(int32_t count, const int64_t* len, float* con
   AdamHyper h{hp->lr, hp->beta1, hp->beta2, hp->eps, hp->weight_decay, hp->t};
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   PX_TIMED(POETX_KC_OPTIM, 0, 28.0 * slots, adam_batch(count, len, q, dq, m1, m2, h, s));
+  return POETX_OK;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// weight-centric baseline: the factors applied to the weight, then one dense
+// contraction per direction (the order original POET computes in)
+// ---------------------------------------------------------------------------
+namespace {
+
+// What the forward leaves for the backward: M = Diag(G_R) W~ Diag(G_P) and
+// U = Diag(G_R) W~ as [m][lead(n)], V^T = (W~ Diag(G_P))^T as [n][lead(m)],
+// and Xt = X[:, perm_R] as [T][lead(m)], all in act_dtype.
+struct WcState {
+  void *M, *U, *Vt, *Xt;
+};
+template <class P> WcState plan_wc_state(P& p, const poetx_layer_desc* d, int64_t T) {
+  const size_t es = dt_size(d->act_dtype), mn = (size_t)d->m * lead(d->n), nm = (size_t)d->n * lead(d->m);
+  WcState w;
+  w.M = p.template take<char>(mn * es);
+  w.U = p.template take<char>(mn * es);
+  w.Vt = p.template take<char>(nm * es);
+  w.Xt = p.template take<char>((size_t)T * lead(d->m) * es);
+  return w;
+}
+struct WcFwdWs {
+  void *Wtt, *Ut, *V, *Mt, *Yt;
+};
+template <class P> WcFwdWs plan_wc_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
+  const size_t es = dt_size(d->act_dtype), mn = (size_t)d->m * lead(d->n), nm = (size_t)d->n * lead(d->m);
+  WcFwdWs w;
+  w.Wtt = has_weight_t(d) ? nullptr : p.template take<char>(nm * es);  // fp32 weights keep no transposed copy
+  w.Ut = p.template take<char>(nm * es);
+  w.V = p.template take<char>(mn * es);
+  w.Mt = p.template take<char>(nm * es);
+  w.Yt = p.template take<char>((size_t)T * lead(d->n) * es);
+  return w;
+}
+struct WcBwdWs {
+  void *dZt, *dXt, *Xtt, *dZtt, *dM, *dMt, *cnp;
+  float* part;
+};
+template <class P> WcBwdWs plan_wc_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
+  const int at = d->act_dtype, b = d->b, nbR = nblocks(d->m, b), nbP = nblocks(d->n, b);
+  const size_t es = dt_size(at), mn = (size_t)d->m * lead(d->n), nm = (size_t)d->n * lead(d->m);
+  const int64_t ldT = round_up(T, 64);
+  WcBwdWs w;
+  w.dZt = p.template take<char>((size_t)T * lead(d->n) * es);
+  w.dXt = p.template take<char>((size_t)T * lead(d->m) * es);
+  w.Xtt = p.template take<char>((size_t)d->m * ldT * es);
+  w.dZtt = p.template take<char>((size_t)d->n * ldT * es);
+  w.dM = p.template take<char>(mn * es);
+  w.dMt = p.template take<char>(nm * es);
+  w.cnp = p.template take<char>(cnp_grad_bytes(at, (int64_t)nbR + nbP, b));
+  w.part = p.template take<float>(
+      std::max(block_grads_part_bytes(at, d->n, nbR, b), block_grads_part_bytes(at, d->m, nbP, b)));
+  return w;
+}
+
+poetx_status check_wc(const poetx_layer_desc* desc, int64_t T) {
+  poetx_status st = check_desc(desc);
+  if (st != POETX_OK) return st;
+  if (desc->w_dtype != desc->act_dtype)
+    return fail(POETX_E_UNSUPPORTED, "the weight-centric path takes (F32, F32) or (BF16, BF16) layers");
+  if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
+  return POETX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t poetx_wc_state_bytes(const poetx_layer_desc* desc, int64_t T) {
+  if (check_wc(desc, T) != POETX_OK) return 0;
+  Plan p;
+  plan_wc_state(p, desc, T);
+  return p.off;
+}
+
+size_t poetx_wc_workspace_size(const poetx_layer_desc* desc, int64_t T, int32_t op) {
+  if (check_wc(desc, T) != POETX_OK) return 0;
+  Plan p;
+  if (op == POETX_OP_FWD) plan_wc_fwd(p, desc, T);
+  else if (op == POETX_OP_BWD) plan_wc_bwd(p, desc, T);
+  else return 0;
+  return p.off;
+}
+
+poetx_status poetx_wc_fwd(const poetx_layer_desc* desc, int64_t T, const void* X, const int32_t* perm_R,
+                          const int32_t* perm_P, const void* Wt, const void* g_R, const void* g_P, void* Y, void* state,
+                          void* ws, size_t ws_bytes, void* stream) {
+  poetx_status st = check_wc(desc, T);
+  if (st != POETX_OK) return st;
+  if (!perm_R || !perm_P || !Wt || !g_R || !g_P || !state) return fail(POETX_E_NULL, "a required pointer is NULL");
+  if (T > 0 && (!X || !Y)) return fail(POETX_E_NULL, "X and Y must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(state) % 256) return fail(POETX_E_WORKSPACE, "state must be 256-byte aligned");
+  Plan p;
+  plan_wc_fwd(p, desc, T);
+  st = check_ws(ws, ws_bytes, p.off);
+  if (st != POETX_OK) return st;
+  Plan ps, pw;
+  ps.base = reinterpret_cast<char*>(state);
+  pw.base = reinterpret_cast<char*>(ws);
+  const WcState S = plan_wc_state(ps, desc, T);
+  const WcFwdWs w = plan_wc_fwd(pw, desc, T);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, rows = (int)T;
+  const int64_t ldm = lead(m), ldn = lead(n);
+  const char* gR0 = reinterpret_cast<const char*>(g_R);                       // Delta_R
+  const char* gP1 = reinterpret_cast<const char*>(g_P) + g_slice(n, b, at);  // Delta_P^T
+  const double es = (double)dt_size(at), mn = (double)m * n;
+  const void* Wtt = has_weight_t(desc) ? reinterpret_cast<const char*>(Wt) + weight_t_offset(desc) : w.Wtt;
+  if (!has_weight_t(desc))
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * mn * es, transpose(at, Wt, ldn, m, n, w.Wtt, ldm, s));
+  // U^T = W~^T Diag(G_R)^T, U = Diag(G_R) W~
+  PX_TIMED(POETX_KC_APPLY, 2.0 * n * sum_r2(m, b), 2.0 * mn * es + g_slice(m, b, at),
+           apply(at, at, Wtt, ldm, n, m, b, at, gR0, nullptr, at, w.Ut, ldm, s));
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * mn * es, transpose(at, w.Ut, ldm, n, m, S.U, ldn, s));
+  // V = W~ Diag(G_P), kept transposed for the R-side gradient
+  PX_TIMED(POETX_KC_APPLY, 2.0 * m * sum_r2(n, b), 2.0 * mn * es + g_slice(n, b, at),
+           apply(at, at, Wt, ldn, m, n, b, at, gP1, nullptr, at, w.V, ldn, s));
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * mn * es, transpose(at, w.V, ldn, m, n, S.Vt, ldm, s));
+  // M = U Diag(G_P) = Diag(G_R) W~ Diag(G_P), and M^T for the contraction
+  PX_TIMED(POETX_KC_APPLY, 2.0 * m * sum_r2(n, b), 2.0 * mn * es + g_slice(n, b, at),
+           apply(at, at, S.U, ldn, m, n, b, at, gP1, nullptr, at, S.M, ldn, s));
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * mn * es, transpose(at, S.M, ldn, m, n, w.Mt, ldm, s));
+  if (rows == 0) return POETX_OK;
+  // Xt = X[:, perm_R] (kept for the weight gradient), Yt = Xt M, Y[:, perm_P] = Yt
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, S.Xt, ldm, rows, m, m, s));
+  PX_TIMED(POETX_KC_GEMM, 2.0 * rows * mn, es * (rows * (double)(m + n) + mn),
+           gemm(at, at, S.Xt, ldm, at, w.Mt, ldm, false, rows, n, m, nullptr, at, w.Yt, ldn, s));
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, scatter(at, w.Yt, ldn, perm_P, Y, n, rows, n, s));
+  return POETX_OK;
+}
+
+poetx_status poetx_wc_bwd(const poetx_layer_desc* desc, int64_t T, const void* dZ, const int32_t* perm_R,
+                          const int32_t* perm_P, const void* g_R, const void* g_P, const float* q_R, const float* q_P,
+                          const void* state, void* dX, float* dq_R, float* dq_P, void* ws, size_t ws_bytes,
+                          void* stream) {
+  poetx_status st = check_wc(desc, T);
+  if (st != POETX_OK) return st;
+  if (!perm_R || !perm_P || !g_R || !g_P || !q_R || !q_P || !state || !dq_R || !dq_P)
+    return fail(POETX_E_NULL, "a required pointer is NULL");
+  if (T > 0 && (!dZ || !dX)) return fail(POETX_E_NULL, "dZ and dX must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(state) % 256) return fail(POETX_E_WORKSPACE, "state must be 256-byte aligned");
+  Plan p;
+  plan_wc_bwd(p, desc, T);
+  st = check_ws(ws, ws_bytes, p.off);
+  if (st != POETX_OK) return st;
+  Plan ps, pw;
+  ps.base = reinterpret_cast<char*>(const_cast<void*>(state));
+  pw.base = reinterpret_cast<char*>(ws);
+  const WcState S = plan_wc_state(ps, desc, T);
+  const WcBwdWs w = plan_wc_bwd(pw, desc, T);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, rows = (int)T;
+  const int64_t ldm = lead(m), ldn = lead(n), ldT = round_up(T, 64);
+  const int nbR = nblocks(m, b), nbP = nblocks(n, b);
+  const double es = (double)dt_size(at), mn = (double)m * n;
+  if (rows > 0) {
+    // dZt = dZ[:, perm_P];  dXt = dZt M^T;  dX[:, perm_R] = dXt
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, permute(at, dZ, n, nullptr, perm_P, w.dZt, ldn, rows, n, n, s));
+    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * mn, es * (rows * (double)(m + n) + mn),
+             gemm(at, at, w.dZt, ldn, at, S.M, ldn, false, rows, m, n, nullptr, at, w.dXt, ldm, s));
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, scatter(at, w.dXt, ldm, perm_R, dX, m, rows, m, s));
+    // the weight gradient dM = Xt^T dZt, both operands transposed so that the tokens are contiguous
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, transpose(at, S.Xt, ldm, rows, m, w.Xtt, ldT, s));
+    PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * n * es, transpose(at, w.dZt, ldn, rows, n, w.dZtt, ldT, s));
+    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * mn, es * (rows * (double)(m + n) + mn),
+             gemm(at, at, w.Xtt, ldT, at, w.dZtt, ldT, false, m, n, rows, nullptr, at, w.dM, ldn, s));
+  } else {
+    PX_HIP(fill_zero(w.dM, (size_t)m * ldn * dt_size(at), s));
+  }
+  PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * mn * es, transpose(at, w.dM, ldn, m, n, w.dMt, ldm, s));
+  // block gradients: M = Diag(G_R) V gives dG_R = (dM V^T) on R's diagonal blocks, a sum over the n
+  // columns; M = U Diag(G_P) gives dG_P = (U^T dM) on P's diagonal blocks, a sum over the m rows
+  const CnpSide sR[2] = {{q_R, m, w.dMt, ldm, S.Vt, ldm}, {q_R, 0, nullptr, ldm, nullptr, ldm}};
+  PX_TIMED(POETX_KC_DGRAD, 2.0 * n * sum_r2(m, b), 2.0 * mn * es + (4 + 2 * es) * sum_r2(m, b),
+           block_grads(at, sR, n, b, w.cnp, 0, (int64_t)nbR + nbP, w.part, s));
+  const CnpSide sP[2] = {{q_P, n, S.U, ldn, w.dM, ldn}, {q_P, 0, nullptr, ldn, nullptr, ldn}};
+  PX_TIMED(POETX_KC_DGRAD, 2.0 * m * sum_r2(n, b), 2.0 * mn * es + (4 + 2 * es) * sum_r2(n, b),
+           block_grads(at, sP, m, b, w.cnp, nbR, (int64_t)nbR + nbP, w.part, s));
+  // CNP chain rule and skew projection, as in poetx_linear_bwd
+  const float* qs[2] = {q_R, q_P};
+  const int ds[2] = {m, n};
+  float* dqs[2] = {dq_R, dq_P};
+  PX_TIMED(POETX_KC_CNP, 12 * (sum_r3(m, b) + sum_r3(n, b)), cnp_grad_bytes(at, (int64_t)nbR + nbP, b),
+           cnp_chain_batch(at, 2, qs, ds, b, w.cnp, dqs, s));
   return POETX_OK;
 }
 

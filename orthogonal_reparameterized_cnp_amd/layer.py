@@ -432,3 +432,71 @@ class PoetxChain:
         for k in reversed(range(len(self.outer_R))):
             dX, dq_outer_R[k] = self.outer_R[k].backward(dX, stream=stream)
         return dX, dq_outer_R, (dq_R, dq_P), dq_outer_P
+
+
+class PoetxWeightCentric:
+    """The weight-centric baseline (poetx_wc_fwd / poetx_wc_bwd) on the state of a
+    PoetxLinear: the same pre-merged weight, G blocks, permutations and q, computed
+    by applying the factors to the weight first and then one dense contraction per
+    direction.  Owns the weight-side state and a workspace."""
+
+    def __init__(self, linear: PoetxLinear):
+        if linear.act != linear.w:
+            raise ValueError("the weight-centric path takes layers whose weights have the activation dtype")
+        self.lin = linear
+        u8 = dict(dtype=torch.uint8, device=linear.device)
+        self.state = torch.empty(0, **u8)
+        self.ws = torch.empty(0, **u8)
+        self.T = None
+
+    def reserve(self, T: int):
+        d = self.lin.desc
+        need = B.poetx_wc_state_bytes(d, T)
+        if self.state.numel() < need:
+            self.state = torch.empty(max(need, 256), dtype=torch.uint8, device=self.lin.device)
+        need = max(B.poetx_wc_workspace_size(d, T, B.POETX_OP_FWD), B.poetx_wc_workspace_size(d, T, B.POETX_OP_BWD))
+        if self.ws.numel() < need:
+            self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.lin.device)
+
+    def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        L = self.lin
+        if not isinstance(X, torch.Tensor) or X.dim() != 2:
+            raise ValueError("X must be a 2-D tensor [T, m]")
+        T = X.shape[0]
+        _check(X, "X", (T, L.m), L._act_dt())
+        if Y is not None:
+            _check(Y, "Y", (T, L.n), L._act_dt())
+        _check_device(L.device, X=X, Y=Y)
+        self.reserve(T)
+        if Y is None:
+            Y = torch.empty(T, L.n, dtype=X.dtype, device=L.device)
+        B.poetx_wc_fwd(L.desc, T, X, L.perm_R, L.perm_P, L.Wt, L.g_R, L.g_P, Y, self.state, self.ws, self.ws.numel(),
+                       stream)
+        self.T = T
+        return Y
+
+    def backward(self, dZ: torch.Tensor, dX=None, dq_R=None, dq_P=None, stream=None):
+        L = self.lin
+        if not isinstance(dZ, torch.Tensor) or dZ.dim() != 2:
+            raise ValueError("dZ must be a 2-D tensor [T, n]")
+        T = dZ.shape[0]
+        if T != self.T:
+            raise ValueError(f"backward over {T} tokens, but the saved state is from a forward of {self.T}")
+        adt = L._act_dt()
+        _check(dZ, "dZ", (T, L.n), adt)
+        if dX is not None:
+            _check(dX, "dX", (T, L.m), adt)
+        if dq_R is not None:
+            _check(dq_R, "dq_R", tuple(L.q_R.shape), torch.float32)
+        if dq_P is not None:
+            _check(dq_P, "dq_P", tuple(L.q_P.shape), torch.float32)
+        _check_device(L.device, dZ=dZ, dX=dX, dq_R=dq_R, dq_P=dq_P)
+        if dX is None:
+            dX = torch.empty(T, L.m, dtype=dZ.dtype, device=L.device)
+        if dq_R is None:
+            dq_R = torch.empty_like(L.q_R)
+        if dq_P is None:
+            dq_P = torch.empty_like(L.q_P)
+        B.poetx_wc_bwd(L.desc, T, dZ, L.perm_R, L.perm_P, L.g_R, L.g_P, L.q_R, L.q_P, self.state, dX, dq_R, dq_P,
+                       self.ws, self.ws.numel(), stream)
+        return dX, dq_R, dq_P

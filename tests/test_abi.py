@@ -231,3 +231,42 @@ def test_cnp_build_noalloc_limits(L):
     assert L.poetx_cnp_build_noalloc(None, 512, 512, B.POETX_BF16, FAKE, None) == B.POETX_E_NULL
     assert L.poetx_cnp_build_noalloc(FAKE, 512, 1, B.POETX_BF16, FAKE, None) == B.POETX_E_SHAPE
     assert L.poetx_cnp_build_noalloc(FAKE, 512, 512, B.POETX_I8, FAKE, None) == B.POETX_E_DTYPE
+
+
+def test_weight_centric_sizes_and_statuses(L):
+    d = B.desc(1000, 300, 256, "bf16", "bf16")
+    T = 70
+    # state: M and U [m][lead(n)], V^T [n][lead(m)], Xt [T][lead(m)], each at a 256-byte boundary
+    al = lambda x: (x + 255) // 256 * 256
+    assert B.poetx_wc_state_bytes(d, T) == 2 * al(1000 * 320 * 2) + al(300 * 1024 * 2) + al(T * 1024 * 2)
+    assert B.poetx_wc_workspace_size(d, T, B.POETX_OP_FWD) > 0
+    assert B.poetx_wc_workspace_size(d, T, B.POETX_OP_BWD) > 0
+    assert B.poetx_wc_workspace_size(d, T, B.POETX_OP_MERGE) == 0
+    i8 = B.desc(1000, 300, 256, "bf16", "i8")
+    assert B.poetx_wc_state_bytes(i8, T) == 0
+    args = [FAKE] * 9
+    assert L.poetx_wc_fwd(ctypes.byref(i8), T, *args, 1 << 40, None) == B.POETX_E_UNSUPPORTED
+    assert L.poetx_wc_fwd(ctypes.byref(d), -1, *args, 1 << 40, None) == B.POETX_E_SHAPE
+    assert L.poetx_wc_fwd(ctypes.byref(d), T, *([FAKE] * 8 + [None]), 1 << 40, None) == B.POETX_E_NULL
+    assert L.poetx_wc_fwd(ctypes.byref(d), T, *args, 16, None) == B.POETX_E_WORKSPACE
+    bargs = [FAKE] * 12  # dZ, perm_R, perm_P, g_R, g_P, q_R, q_P, state, dX, dq_R, dq_P, ws
+    assert L.poetx_wc_bwd(ctypes.byref(i8), T, *bargs, 1 << 40, None) == B.POETX_E_UNSUPPORTED
+    assert L.poetx_wc_bwd(ctypes.byref(d), T, *([FAKE] * 10 + [None, FAKE]), 1 << 40, None) == B.POETX_E_NULL
+    assert L.poetx_wc_bwd(ctypes.byref(d), T, *([FAKE] * 11 + [None]), 1 << 40, None) == B.POETX_E_NULL
+    assert L.poetx_wc_bwd(ctypes.byref(d), T, *bargs, 16, None) == B.POETX_E_WORKSPACE
+
+
+def test_binding_signatures_match_header():
+    """Every C entry point the binding types has the header's number of parameters: a missing one
+    would make ctypes pass the trailing arguments (the stream handle) with default conversions."""
+    import re
+
+    text = open(B.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    decls = {}
+    for m in re.finditer(r"\b(poetx_\w+)\s*\(([^;{]*?)\)\s*;", text, re.S):
+        params = m.group(2).strip()
+        decls[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    assert set(B._SIG) <= set(decls), sorted(set(B._SIG) - set(decls))
+    for name, (_, args) in B._SIG.items():
+        assert len(args) == decls[name], f"{name}: binding types {len(args)} arguments, header declares {decls[name]}"
