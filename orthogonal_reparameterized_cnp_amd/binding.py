@@ -18,7 +18,8 @@ import re
 from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libpoetx.so")
+# POETX_LIBRARY names another build of the library (e.g. to compare two builds in one process tree)
+LIB_PATH = os.environ.get("POETX_LIBRARY") or os.path.join(HERE, "libpoetx.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "poetx.h")
 
 POETX_OK, POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_PERM, POETX_E_HIP, POETX_E_UNSUPPORTED = range(8)
