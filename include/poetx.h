@@ -189,7 +189,7 @@ poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype
  * The array holds POETX_NOALLOC_SCRATCH_BYTES (80 MiB) on each GPU the call
  * runs on, from the first call on that GPU until the process ends; that is
  * room for poetx_workspace_size(desc with m = d, 0, POETX_OP_CNP) of any side
- * up to 32 blocks of 512 in bf16 (d <= 16384 at b = 512) or 20 in fp32.
+ * up to 40 blocks of 512 in bf16 (d <= 20480 at b = 512) or 20 in fp32.
  * Every call on one GPU uses the same array: calls that overlap in time on one
  * GPU (other streams, other threads) race and must be serialised by the caller.
  * The call allocates nothing (no hipMalloc or torch allocation).

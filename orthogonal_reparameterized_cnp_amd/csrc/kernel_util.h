@@ -123,8 +123,8 @@ template <class A> using cfg_of = typename std::decay_t<A>::Cfg;
 // accumulator positions, with row0 + row and col0 + col clamped to
 // [0, rmax) x [0, cmax) so that every load is in range and none is predicated:
 // all of them are issued before the first is used.
-template <class C>
-PX_DEV void load_at_acc(float (&f)[C::TM][C::TN][16], const float* src, int64_t ld, int row0, int col0, int rmax,
+template <class C, typename S>
+PX_DEV void load_at_acc(float (&f)[C::TM][C::TN][16], const S* src, int64_t ld, int row0, int col0, int rmax,
                         int cmax) {
   const AccPos<C> p = acc_pos<C>();
 #pragma unroll
@@ -133,7 +133,7 @@ PX_DEV void load_at_acc(float (&f)[C::TM][C::TN][16], const float* src, int64_t 
     for (int j = 0; j < C::TN; ++j) {
       const int c = min(col0 + p.col(j), cmax - 1);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) f[i][j][e] = src[(int64_t)min(row0 + p.row(i, e), rmax - 1) * ld + c];
+      for (int e = 0; e < 16; ++e) f[i][j][e] = to_f32<S>(src[(int64_t)min(row0 + p.row(i, e), rmax - 1) * ld + c]);
     }
 }
 

@@ -126,9 +126,9 @@ PX_DEV void run_kk2(unsigned char* smem, const T* x0, const T* y0, const T* x1, 
 // Dense Q from the packed parameters, one 64 x 64 tile per workgroup: entries
 // above the diagonal are read along packed rows; entries below it come from
 // the mirrored tile, staged through LDS so that both reads and writes are
-// row-contiguous.  Writes the operand copy Qb and, if Q32 is set, an fp32 copy.
+// row-contiguous.  Writes Q in the operand dtype.
 template <typename T>
-__global__ __launch_bounds__(256) void k_unpack_q(SideTable sd, int b, T* __restrict__ Qb, float* __restrict__ Q32) {
+__global__ __launch_bounds__(256) void k_unpack_q(SideTable sd, int b, T* __restrict__ Qb) {
   __shared__ float t[64][65];
   const int z = blockIdx.y;
   const float* qk;
@@ -168,15 +168,14 @@ __global__ __launch_bounds__(256) void k_unpack_q(SideTable sd, int b, T* __rest
     const float v = (j < i && i < r) ? -t[c][ii] : u[k];
     const int64_t e = (int64_t)z * b * b + (int64_t)i * b + j;
     Qb[e] = from_f32<T>(v);
-    if (Q32) Q32[e] = v;
   }
 }
 
-// S = Q Q = -(Q Q^T).  Writes S and N^T = S - 2Q in the operand dtype, and
-// replaces Q32 in place by the fp32 partial sum 2Q + 2S.
+// S = Q Q = -(Q Q^T).  Writes S, N^T = S - 2Q and the partial sum 2Q + 2S in
+// the operand dtype (the epilogue reads Q at its accumulators' positions).
 template <class C, typename T>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_square(SideTable sd, int b, const T* __restrict__ Qb,
-                                                      float* __restrict__ Q32, T* __restrict__ Sb,
+                                                      T* __restrict__ T2, T* __restrict__ Sb,
                                                       T* __restrict__ Ntb) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM;
@@ -190,7 +189,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   run_kk<C, T>(smem, Qb + off + (int64_t)m0 * b, r - m0, Qb + off + (int64_t)n0 * b, r - n0, b, r, [&](auto& acc) {
     using CC = cfg_of<decltype(acc)>;
     float q[CC::TM][CC::TN][16];
-    load_at_acc<CC>(q, Q32 + off, b, m0, n0, r, r);
+    load_at_acc<CC>(q, Qb + off, b, m0, n0, r, r);
     const AccPos<CC> p = acc_pos<CC>();
 #pragma unroll
     for (int ti = 0; ti < CC::TM; ++ti)
@@ -203,7 +202,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
           if (i < r && j < r) {
             const int64_t x = off + (int64_t)i * b + j;
             const float sv = -acc.v[ti][tj][e], qv = q[ti][tj][e];
-            Q32[x] = 2.f * qv + 2.f * sv;
+            T2[x] = from_f32<T>(2.f * qv + 2.f * sv);
             Sb[x] = from_f32<T>(sv);
             Ntb[x] = from_f32<T>(sv - 2.f * qv);
           }
@@ -219,7 +218,7 @@ struct GOut {
 };
 
 template <class C, typename T>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_delta(SideTable sd, int b, const float* __restrict__ T2,
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_delta(SideTable sd, int b, const T* __restrict__ T2,
                                                      const T* __restrict__ Sb, const T* __restrict__ Ntb, GOut go) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM;
@@ -608,8 +607,8 @@ hipError_t build_t(const SideTable& sd, int b, const GOut& go, void* ws, hipStre
   char* w = reinterpret_cast<char*>(ws);
   T* Qb = reinterpret_cast<T*>(w);
   w += al256(E * sizeof(T));
-  float* Q32 = reinterpret_cast<float*>(w);  // Q, then 2Q + 2S
-  w += al256(E * 4);
+  T* T2 = reinterpret_cast<T*>(w);  // 2Q + 2S
+  w += al256(E * sizeof(T));
   T* Sb = reinterpret_cast<T*>(w);
   w += al256(E * sizeof(T));
   T* Ntb = reinterpret_cast<T*>(w);
@@ -618,10 +617,10 @@ hipError_t build_t(const SideTable& sd, int b, const GOut& go, void* ws, hipStre
   if (e == hipSuccess) e = allow_lds(k_cnp_delta<C, T>, lds);
   if (e != hipSuccess) return e;
   const unsigned t64 = cdiv(b, 64);
-  k_unpack_q<T><<<dim3(t64 * t64, nb), 256, 0, s>>>(sd, b, Qb, Q32);
+  k_unpack_q<T><<<dim3(t64 * t64, nb), 256, 0, s>>>(sd, b, Qb);
   const unsigned grid = cdiv(b, C::BN) * cdiv(b, C::BM) * nb;
-  k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(sd, b, Qb, Q32, Sb, Ntb);
-  k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(sd, b, Q32, Sb, Ntb, go);
+  k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(sd, b, Qb, T2, Sb, Ntb);
+  k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(sd, b, T2, Sb, Ntb, go);
   return hipGetLastError();
 }
 
@@ -707,7 +706,7 @@ hipError_t chain_t(const SideTable& sd, int b, void* dg, const DqOut& out, hipSt
   const int NB = sd.first[sd.count];
   Chain<T> ch = carve<T>(dg, (size_t)NB * b * b);
   const unsigned t64 = cdiv(b, 64);
-  k_unpack_q<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb), nullptr);
+  k_unpack_q<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb));
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = hipSuccess;
   const unsigned grid = cdiv(b, C::BN) * cdiv(b, C::BM) * NB;
@@ -729,7 +728,7 @@ namespace pxk {
 
 size_t cnp_build_ws_bytes(int dt, int64_t blocks, int b) {
   const size_t E = (size_t)blocks * b * b, es = dt_size(dt);
-  return al256(E * es) * 3 + al256(E * 4);
+  return al256(E * es) * 4;  // Q, 2Q + 2S, S, N^T
 }
 
 size_t cnp_grad_bytes(int dt, int64_t blocks, int b) {

@@ -221,12 +221,12 @@ def test_spo_helpers_and_validation(L):
 
 def test_cnp_build_noalloc_limits(L):
     """The no-allocation CNP build rejects, before any device call, a side whose workspace
-    exceeds the fixed scratch array (80 MiB): 32 blocks of 512 fit in bf16, 33 do not."""
+    exceeds the fixed scratch array (80 MiB): 40 blocks of 512 fit in bf16, 41 do not."""
     lim = 80 << 20
     cnp_ws = lambda d, act: B.poetx_workspace_size(B.desc(d, 1, 512, act, act), 0, B.POETX_OP_CNP)
-    assert cnp_ws(32 * 512, "bf16") <= lim < cnp_ws(33 * 512, "bf16")
+    assert cnp_ws(40 * 512, "bf16") <= lim < cnp_ws(41 * 512, "bf16")
     assert cnp_ws(20 * 512, "f32") <= lim < cnp_ws(21 * 512, "f32")
-    assert L.poetx_cnp_build_noalloc(FAKE, 33 * 512, 512, B.POETX_BF16, FAKE, None) == B.POETX_E_WORKSPACE
+    assert L.poetx_cnp_build_noalloc(FAKE, 41 * 512, 512, B.POETX_BF16, FAKE, None) == B.POETX_E_WORKSPACE
     assert L.poetx_cnp_build_noalloc(FAKE, 21 * 512, 512, B.POETX_F32, FAKE, None) == B.POETX_E_WORKSPACE
     assert L.poetx_cnp_build_noalloc(None, 512, 512, B.POETX_BF16, FAKE, None) == B.POETX_E_NULL
     assert L.poetx_cnp_build_noalloc(FAKE, 512, 1, B.POETX_BF16, FAKE, None) == B.POETX_E_SHAPE

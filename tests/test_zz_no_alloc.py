@@ -54,9 +54,9 @@ def test_noalloc_matches_cnp_build(cases):
 
 
 def test_noalloc_rejects_oversized_side():
-    # 40 blocks of 512 in bf16 need 105 MB of workspace, more than the fixed array holds
-    d, b = 40 * 512, 512
-    q = torch.zeros(40, b * (b - 1) // 2, dtype=torch.float32, device="cuda")
+    # 48 blocks of 512 in bf16 need 100.7 MB of workspace, more than the fixed array holds
+    d, b = 48 * 512, 512
+    q = torch.zeros(48, b * (b - 1) // 2, dtype=torch.float32, device="cuda")
     g = torch.zeros(B.poetx_g_bytes(d, b, B.POETX_BF16), dtype=torch.uint8, device="cuda")
     with pytest.raises(B.PoetxError) as e:
         B.poetx_cnp_build_noalloc(q, d, b, B.POETX_BF16, g)
