@@ -397,6 +397,45 @@ poetx_status poetx_spo_bwd(const poetx_spo_desc* desc, int64_t T, const void* dY
                            const float* q, const void* saved, void* dX, float* dq, void* ws, size_t ws_bytes,
                            void* stream);
 
+/*
+ * Merging a chain's outer factors into the weight (POET notes, 关键设计 1 and
+ * 3: merge-then-reinitialise of R = R_1 ... R_c and P = P_1 ... P_c).  After
+ * poetx_merge_reinit has folded the linear's own R_c and P_1, its workspace
+ * holds the merged weight in fp32, [m][round_up(n, 64)] in the new pre-merged
+ * order.  Each outer factor F is folded into that matrix W:
+ *   side 1 (F one of P_2 .. P_c, acting on the n output columns):  W <- W F~
+ *   side 0 (F one of R_1 .. R_{c-1}, acting on the m input rows): W <- F~ W
+ * with F~ = Psi F Psi^T the factor in the pre-merged order (Psi the linear's
+ * permutation on that side, Psi[i][perm[i]] = 1): a factor of the same kind
+ * whose index array is perm^-1 o idx.  Fold P_2, ..., P_c in that order and
+ * R_{c-1}, ..., R_1 in that order; then poetx_store_weight writes the result in
+ * the layer's weight format.  The products run in fp32 on MFMA with the
+ * factor's G blocks (its activation dtype), the same blocks its forward uses.
+ *   f      the factor (f->d = n for side 1, m for side 0)
+ *   idx, G the factor's index array and G buffer (poetx_spo_fwd's arguments)
+ *   perm   the linear's permutation on that side after the merge
+ *   W      in/out fp32 [m][ldw], ldw >= n; columns n .. ldw - 1 may be zeroed
+ *   ws     >= poetx_fold_workspace_size(desc, side, f)
+ * Errors: POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_HIP.
+ */
+size_t poetx_fold_workspace_size(const poetx_layer_desc* desc, int32_t side, const poetx_spo_desc* f);
+poetx_status poetx_fold_factor(const poetx_layer_desc* desc, int32_t side, const poetx_spo_desc* f, const int32_t* idx,
+                               const void* G, const int32_t* perm, float* W, int64_t ldw, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/*
+ * Write an fp32 pre-merged weight W [m][ldw] into the layer's weight buffer Wt
+ * (poetx_weight_bytes layout), as poetx_merge_reinit stores its result: fp32
+ * copied, bf16 rounded to nearest even (and the transposed copy written), int8
+ * requantised per output column (scale = max|w| / 127, 1 for an all-zero
+ * column; code = clamp(round_half_even(w / scale), -127, 127), in fp32).
+ *   ws  >= poetx_store_workspace_size(desc)
+ * Errors: POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_HIP.
+ */
+size_t poetx_store_workspace_size(const poetx_layer_desc* desc);
+poetx_status poetx_store_weight(const poetx_layer_desc* desc, const float* W, int64_t ldw, void* Wt, void* ws,
+                                size_t ws_bytes, void* stream);
+
 /* ------------------------------------------ optimiser step on packed q -- */
 
 /* Hyper-parameters of one Adam step with decoupled weight decay. */

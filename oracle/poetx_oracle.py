@@ -618,6 +618,19 @@ def chain_backward(X, dZ, W, R: Sequence[SpoFactor], P: Sequence[SpoFactor]):
     return g, dq_R, dq_P
 
 
+def chain_merge(W, R: Sequence[SpoFactor], P: Sequence[SpoFactor]) -> np.ndarray:
+    """Merge every factor of a chain into the weight ([PN] 关键设计 3 for R and P
+    built as products of c primitives, 关键设计 1): W' = R_1 .. R_c W P_1 .. P_c
+    with the factors as explicit matrices (tiny sizes), so that chain_forward
+    with W' and no factors equals chain_forward with W and the factors."""
+    Wn = np.asarray(W, dtype=np.float64)
+    for f in reversed(list(R)):
+        Wn = spo_dense(f) @ Wn
+    for f in P:
+        Wn = Wn @ spo_dense(f)
+    return Wn
+
+
 def spo_block_grads(X: np.ndarray, dY: np.ndarray, f: SpoFactor, blocks: Sequence[int]):
     """Packed dq of selected blocks of one factor, with the sums over all rows:
     dG_k = X[:, cols_k]^T dY[:, cols_k] for the block's columns cols_k of idx,

@@ -129,6 +129,14 @@ _SIG = {
     "poetx_spo_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(SpoDesc), ctypes.c_int64, ctypes.c_int32]),
     "poetx_spo_fwd": (ctypes.c_int, [ctypes.POINTER(SpoDesc), ctypes.c_int64] + [_P] * 6 + [ctypes.c_size_t, _P]),
     "poetx_spo_bwd": (ctypes.c_int, [ctypes.POINTER(SpoDesc), ctypes.c_int64] + [_P] * 8 + [ctypes.c_size_t, _P]),
+    "poetx_fold_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.c_int32, ctypes.POINTER(SpoDesc)]),
+    "poetx_fold_factor": (
+        ctypes.c_int,
+        [ctypes.POINTER(LayerDesc), ctypes.c_int32, ctypes.POINTER(SpoDesc), _P, _P, _P, _P, ctypes.c_int64, _P,
+         ctypes.c_size_t, _P],
+    ),
+    "poetx_store_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc)]),
+    "poetx_store_weight": (ctypes.c_int, [ctypes.POINTER(LayerDesc), _P, ctypes.c_int64, _P, _P, ctypes.c_size_t, _P]),
     "poetx_wc_state_bytes": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.c_int64]),
     "poetx_wc_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(LayerDesc), ctypes.c_int64, ctypes.c_int32]),
     "poetx_wc_fwd": (ctypes.c_int, [ctypes.POINTER(LayerDesc), ctypes.c_int64] + [_P] * 9 + [ctypes.c_size_t, _P]),
@@ -379,3 +387,22 @@ def poetx_wc_bwd(dsc: LayerDesc, T: int, dZ, perm_R, perm_P, g_R, g_P, q_R, q_P,
     _check(lib().poetx_wc_bwd(ctypes.byref(dsc), T, _ptr(dZ), _ptr(perm_R), _ptr(perm_P), _ptr(g_R), _ptr(g_P),
                               _ptr(q_R), _ptr(q_P), _ptr(state), _ptr(dX), _ptr(dq_R), _ptr(dq_P), _ptr(ws), ws_bytes,
                               _stream(stream)))
+
+
+# ---------------------------------------- merging a chain's outer factors ---
+def poetx_fold_workspace_size(dsc: LayerDesc, side: int, f: SpoDesc) -> int:
+    return lib().poetx_fold_workspace_size(ctypes.byref(dsc), side, ctypes.byref(f))
+
+
+def poetx_fold_factor(dsc: LayerDesc, side: int, f: SpoDesc, idx, G, perm, W, ldw: int, ws, ws_bytes: int,
+                      stream=None):
+    _check(lib().poetx_fold_factor(ctypes.byref(dsc), side, ctypes.byref(f), _ptr(idx), _ptr(G), _ptr(perm), _ptr(W),
+                                   ldw, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def poetx_store_workspace_size(dsc: LayerDesc) -> int:
+    return lib().poetx_store_workspace_size(ctypes.byref(dsc))
+
+
+def poetx_store_weight(dsc: LayerDesc, W, ldw: int, Wt, ws, ws_bytes: int, stream=None):
+    _check(lib().poetx_store_weight(ctypes.byref(dsc), _ptr(W), ldw, _ptr(Wt), _ptr(ws), ws_bytes, _stream(stream)))

@@ -1020,3 +1020,115 @@ poetx_status poetx_wc_bwd(const poetx_layer_desc* desc, int64_t T, const void* d
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// merging the outer factors of a chain into the weight
+// ---------------------------------------------------------------------------
+namespace {
+
+struct FoldWs {
+  int32_t *inv, *sigma;
+  float *Xg, *Ag, *Wtr;
+};
+template <class P> FoldWs plan_fold(P& p, const poetx_layer_desc* d, int32_t side, const poetx_spo_desc* f) {
+  const int de = spo_d_eff(f), dd = f->d, rows = side == 1 ? d->m : d->n;
+  FoldWs w{};
+  w.inv = p.template take<int32_t>((size_t)dd * 4);
+  w.sigma = p.template take<int32_t>((size_t)de * 4);
+  w.Xg = p.template take<float>((size_t)rows * lead(de) * 4);
+  w.Ag = p.template take<float>((size_t)rows * lead(de) * 4);
+  w.Wtr = side == 0 ? p.template take<float>((size_t)d->n * lead(d->m) * 4) : nullptr;
+  return w;
+}
+
+poetx_status check_fold(const poetx_layer_desc* d, int32_t side, const poetx_spo_desc* f) {
+  poetx_status st = check_desc(d);
+  if (st != POETX_OK) return st;
+  st = check_spo(f, 0);
+  if (st != POETX_OK) return st;
+  if (side != 0 && side != 1) return fail(POETX_E_SHAPE, "side must be 0 (R) or 1 (P)");
+  if (f->d != (side == 1 ? d->n : d->m)) return fail(POETX_E_SHAPE, "the factor's d must be n (side 1) or m (side 0)");
+  return POETX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t poetx_fold_workspace_size(const poetx_layer_desc* desc, int32_t side, const poetx_spo_desc* f) {
+  if (check_fold(desc, side, f) != POETX_OK) return 0;
+  Plan p;
+  plan_fold(p, desc, side, f);
+  return p.off;
+}
+
+poetx_status poetx_fold_factor(const poetx_layer_desc* desc, int32_t side, const poetx_spo_desc* f, const int32_t* idx,
+                               const void* G, const int32_t* perm, float* W, int64_t ldw, void* ws, size_t ws_bytes,
+                               void* stream) {
+  poetx_status st = check_fold(desc, side, f);
+  if (st != POETX_OK) return st;
+  if (!idx || !G || !perm || !W) return fail(POETX_E_NULL, "idx, G, perm and W must be non-NULL");
+  if (ldw < desc->n) return fail(POETX_E_SHAPE, "ldw < n");
+  Plan p;
+  plan_fold(p, desc, side, f);
+  st = check_ws(ws, ws_bytes, p.off);
+  if (st != POETX_OK) return st;
+  Plan pq;
+  pq.base = reinterpret_cast<char*>(ws);
+  const FoldWs w = plan_fold(pq, desc, side, f);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int m = desc->m, n = desc->n, d = f->d, de = spo_d_eff(f), b = f->b, gt = f->act_dtype;
+  // the factor in the weight's pre-merged order: index array sigma = perm^-1 o idx
+  PX_HIP(inverse_perm(perm, d, w.inv, s));
+  PX_HIP(compose_idx(w.inv, d, idx, de, w.sigma, s));
+  // rows the factor acts on from the right: W's m rows (P side), or the n rows of W^T (R side, the
+  // factor transposed: W <- F W is W^T <- W^T F^T)
+  float* Rm = W;
+  int64_t ldr = ldw;
+  int rows = m;
+  if (side == 0) {
+    PX_HIP(transpose(F32, W, ldw, m, n, w.Wtr, lead(m), s));
+    Rm = w.Wtr;
+    ldr = lead(m);
+    rows = n;
+  }
+  const char* gsl = reinterpret_cast<const char*>(G) + (side == 1 ? g_slice(de, b, gt) : 0);  // G (P) or G^T (R)
+  PX_HIP(permute(F32, Rm, ldr, nullptr, w.sigma, w.Xg, lead(de), rows, d, de, s));
+  PX_HIP(apply(F32, F32, w.Xg, lead(de), rows, de, b, gt, gsl, nullptr, F32, w.Ag, lead(de), s));
+  if (f->kind == POETX_SPO_BLOCK)
+    PX_HIP(scatter(F32, w.Ag, lead(de), w.sigma, Rm, ldr, rows, d, s));
+  else
+    PX_HIP(scatter_cols(F32, w.Ag, lead(de), rows, de, w.sigma, Rm, ldr, d, s));
+  if (side == 0) PX_HIP(transpose(F32, w.Wtr, lead(m), n, m, W, ldw, s));
+  return POETX_OK;
+}
+
+size_t poetx_store_workspace_size(const poetx_layer_desc* desc) {
+  if (check_desc(desc) != POETX_OK) return 0;
+  return (size_t)round_up((int64_t)desc->n * 4, 256);
+}
+
+poetx_status poetx_store_weight(const poetx_layer_desc* desc, const float* W, int64_t ldw, void* Wt, void* ws,
+                                size_t ws_bytes, void* stream) {
+  poetx_status st = check_desc(desc);
+  if (st != POETX_OK) return st;
+  if (!W || !Wt) return fail(POETX_E_NULL, "W and Wt must be non-NULL");
+  if (ldw < desc->n) return fail(POETX_E_SHAPE, "ldw < n");
+  st = check_ws(ws, ws_bytes, poetx_store_workspace_size(desc));
+  if (st != POETX_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int m = desc->m, n = desc->n, wt = desc->w_dtype;
+  uint32_t* amax = reinterpret_cast<uint32_t*>(ws);
+  float* scale_t =
+      wt == POETX_I8 ? reinterpret_cast<float*>(reinterpret_cast<char*>(Wt) + weight_scale_offset(desc)) : nullptr;
+  if (wt == POETX_I8) {
+    PX_HIP(fill_zero(amax, (size_t)n * 4, s));
+    PX_HIP(col_absmax(W, ldw, m, n, amax, s));
+  }
+  PX_HIP(store_weight(W, ldw, m, n, wt, Wt, lead(n), amax, scale_t, s));
+  if (has_weight_t(desc))
+    PX_HIP(transpose(wt, Wt, lead(n), m, n, reinterpret_cast<char*>(Wt) + weight_t_offset(desc), lead(m), s));
+  return POETX_OK;
+}
+
+}  // extern "C"

@@ -39,6 +39,8 @@ hipError_t replace_cols(int dt, const void* in, int64_t ld_in, const void* src, 
 hipError_t inverse_perm(const int32_t* perm, int d, int32_t* inv, hipStream_t s);
 // out[i] = a[b[i]]
 hipError_t compose_perm(const int32_t* a, const int32_t* b, int d, int32_t* out, hipStream_t s);
+// out[i] = a[b[i]] for i < n, with a of length da (b's values clamped into [0, da))
+hipError_t compose_idx(const int32_t* a, int da, const int32_t* b, int n, int32_t* out, hipStream_t s);
 // Durstenfeld shuffle of the identity driven by SplitMix64(seed)
 hipError_t perm_from_seed_device(uint64_t seed, int d, int32_t* out, int32_t* scratch, hipStream_t s);
 

@@ -691,10 +691,10 @@ __global__ void k_scatter_cols(const T* __restrict__ src, int64_t ld_src, int ro
   for (int t = blockIdx.y; t < rows; t += gridDim.y) dst[(int64_t)t * ld_dst + c] = src[(int64_t)t * ld_src + i];
 }
 
-__global__ void k_compose_perm(const int32_t* __restrict__ a, const int32_t* __restrict__ bm, int d,
+__global__ void k_compose_perm(const int32_t* __restrict__ a, int da, const int32_t* __restrict__ bm, int n,
                                int32_t* __restrict__ out) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < d) out[i] = a[min(max(bm[i], 0), d - 1)];
+  if (i < n) out[i] = a[min(max(bm[i], 0), da - 1)];
 }
 
 // SplitMix64 output number k (0-based) of the stream seeded with `seed`:
@@ -938,7 +938,12 @@ hipError_t scatter_cols(int dt, const void* src, int64_t ld_src, int rows, int b
 }
 
 hipError_t compose_perm(const int32_t* a, const int32_t* b, int d, int32_t* out, hipStream_t s) {
-  k_compose_perm<<<cdiv(d, 256), 256, 0, s>>>(a, b, d, out);
+  return compose_idx(a, d, b, d, out, s);
+}
+
+hipError_t compose_idx(const int32_t* a, int da, const int32_t* b, int n, int32_t* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_compose_perm<<<cdiv(n, 256), 256, 0, s>>>(a, da, b, n, out);
   return hipGetLastError();
 }
 

@@ -422,6 +422,41 @@ class PoetxChain:
             Y = f.forward(Y, stream=stream)
         return Y
 
+    def merge_reinit(self, seed_R: int, seed_P: int, outer_seeds=None, stream=None):
+        """Merge every factor into the weight and restart them all at the identity.
+
+        The linear's own R_c and P_1 are merged first (poetx_merge_reinit, new permutations from
+        seed_R and seed_P); the fp32 merged weight it leaves in its workspace then takes the outer
+        factors, P_2 .. P_c and R_{c-1} .. R_1 in that order (poetx_fold_factor), and is stored in
+        the layer's weight format (poetx_store_weight).  Every G is rebuilt from the current q
+        first.  The outer factors restart with q = 0 and new index arrays drawn from
+        outer_seeds(k, side) (k the position in outer_R / outer_P, side "R" or "P"): a permutation
+        for a block factor, the first b entries of one for a fully stochastic factor."""
+        lin = self.linear
+        ctx = torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+        with ctx:
+            self.build(stream)
+            lin.merge_reinit(seed_R, seed_P, stream)
+            W32 = lin.merged_f32()
+            ldw = W32.shape[1]
+            need = [B.poetx_store_workspace_size(lin.desc)]
+            need += [B.poetx_fold_workspace_size(lin.desc, 1, f.desc) for f in self.outer_P]
+            need += [B.poetx_fold_workspace_size(lin.desc, 0, f.desc) for f in self.outer_R]
+            ws = torch.empty(max(need + [256]), dtype=torch.uint8, device=lin.device)
+            for f in self.outer_P:
+                B.poetx_fold_factor(lin.desc, 1, f.desc, f.idx, f.g, lin.perm_P, W32, ldw, ws, ws.numel(), stream)
+            for f in reversed(self.outer_R):
+                B.poetx_fold_factor(lin.desc, 0, f.desc, f.idx, f.g, lin.perm_R, W32, ldw, ws, ws.numel(), stream)
+            B.poetx_store_weight(lin.desc, W32, ldw, lin.Wt, ws, ws.numel(), stream)
+            if outer_seeds is None:
+                outer_seeds = lambda k, side: ((seed_R if side == "R" else seed_P) + 0x9E3779B97F4A7C15 * (k + 1)) % (1 << 64)
+            for side, facs in (("R", self.outer_R), ("P", self.outer_P)):
+                for k, f in enumerate(facs):
+                    perm = B.poetx_perm_from_seed(outer_seeds(k, side), f.d)[: f.d_eff]
+                    f.idx.copy_(torch.from_numpy(perm.copy()))
+                    f.q.zero_()
+        self.Y_lin = None
+
     def backward(self, dZ: torch.Tensor, stream=None):
         """Returns dX, [dq of outer_R], (dq_R, dq_P) of the linear, [dq of outer_P]."""
         dq_outer_P = [None] * len(self.outer_P)

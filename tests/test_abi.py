@@ -270,3 +270,22 @@ def test_binding_signatures_match_header():
     assert set(B._SIG) <= set(decls), sorted(set(B._SIG) - set(decls))
     for name, (_, args) in B._SIG.items():
         assert len(args) == decls[name], f"{name}: binding types {len(args)} arguments, header declares {decls[name]}"
+
+
+def test_fold_and_store_statuses(L):
+    d = B.desc(320, 200, 64, "bf16", "bf16")
+    fP = B.spo_desc(200, 64, "block", "bf16")
+    fR = B.spo_desc(320, 64, "full", "bf16")
+    assert B.poetx_fold_workspace_size(d, 1, fP) > 0 and B.poetx_fold_workspace_size(d, 0, fR) > 0
+    assert B.poetx_fold_workspace_size(d, 0, fP) == 0  # a P-side factor has d = n, not m
+    assert B.poetx_fold_workspace_size(d, 2, fP) == 0
+    assert B.poetx_store_workspace_size(d) == 256 * ((200 * 4 + 255) // 256)
+    fold = lambda side, f, W=FAKE, ldw=256, ws_bytes=1 << 40: L.poetx_fold_factor(
+        ctypes.byref(d), side, ctypes.byref(f), FAKE, FAKE, FAKE, W, ldw, FAKE, ws_bytes, None)
+    assert fold(0, fP) == B.POETX_E_SHAPE
+    assert fold(1, fP, W=None) == B.POETX_E_NULL
+    assert fold(1, fP, ldw=199) == B.POETX_E_SHAPE
+    assert fold(1, fP, ws_bytes=16) == B.POETX_E_WORKSPACE
+    assert L.poetx_store_weight(ctypes.byref(d), FAKE, 199, FAKE, FAKE, 1 << 40, None) == B.POETX_E_SHAPE
+    assert L.poetx_store_weight(ctypes.byref(d), FAKE, 256, None, FAKE, 1 << 40, None) == B.POETX_E_NULL
+    assert L.poetx_store_weight(ctypes.byref(d), FAKE, 256, FAKE, FAKE, 16, None) == B.POETX_E_WORKSPACE

@@ -144,3 +144,48 @@ def test_spo_empty_batch(kind):
     torch.cuda.synchronize()
     assert Y.shape == (0, 300) and dX.shape == (0, 300)
     assert not dq.any()
+
+
+def _natural(lay, dt):
+    """The stored weight back in the natural order: W[perm_R[i]][perm_P[j]] = W~[i][j]."""
+    Wt = host(lay.weight_values()[:, : lay.n].contiguous(), dt)
+    pR, pP = lay.perm_R.cpu().numpy(), lay.perm_P.cpu().numpy()
+    W = np.empty_like(Wt)
+    W[np.ix_(pR, pP)] = Wt
+    return W
+
+
+@pytest.mark.parametrize("act,m,n,b,T", [("f32", 96, 64, 32, 40), ("bf16", 320, 200, 64, 96)])
+def test_chain_merge_keeps_the_function(act, m, n, b, T):
+    """Merge-then-reinitialise of a chain with two factors per side (R_1 fully stochastic,
+    P_2 block-stochastic outside the linear): the weight afterwards is R_1 R_2 W0 P_1 P_2
+    (the oracle's dense merge), every q restarts at 0, and the chain's forward with the
+    restarted factors equals the oracle's forward with the original ones."""
+    print(f"chain merge {m}x{n} b={b} T={T} {act}", flush=True)
+    inp = custom_linear_inputs(m, n, b, T, act, act, 0.02, seed=51)
+    lin = make_layer(inp)
+    oR = spo_inputs(m, b, "full", T, act, 0.02, seed=52)
+    oP = spo_inputs(n, b, "block", T, act, 0.02, seed=53)
+    fR, fP = _factor(oR, act), _factor(oP, act)
+    chain = PoetxChain(lin, [fR], [fP])
+    chain.build()
+    X = dev(inp.X, act)
+    Y0 = host(chain.forward(X), act)
+    R = [_oracle_factor(oR), O.SpoFactor("block", inp.perm_R, inp.q_R.astype(np.float64), m, b)]
+    P = [O.SpoFactor("block", inp.perm_P, inp.q_P.astype(np.float64), n, b), _oracle_factor(oP)]
+    W = O.to_f64(inp.W0, inp.w)
+    Xo = O.to_f64(inp.X, act)
+    ref = O.chain_forward(Xo, W, R, P)
+    assert_close("Y before the merge", Y0, ref, act)
+    chain.merge_reinit(1000 + m, 2000 + n)
+    torch.cuda.synchronize()
+    for name, q in (("q_R", lin.q_R), ("q_P", lin.q_P), ("outer q_R", fR.q), ("outer q_P", fP.q)):
+        assert not q.any(), f"{name} must restart at 0"
+    np.testing.assert_array_equal(lin.perm_R.cpu().numpy(), O.perm_from_seed(1000 + m, m))
+    np.testing.assert_array_equal(lin.perm_P.cpu().numpy(), O.perm_from_seed(2000 + n, n))
+    assert sorted(fP.idx.cpu().tolist()) == list(range(n))
+    assert len(set(fR.idx.cpu().tolist())) == b
+    assert_close("merged W", _natural(lin, act), O.chain_merge(W, R, P), act)
+    chain.build()
+    Y1 = host(chain.forward(X), act)
+    assert_close("Y after the merge", Y1, ref, act)

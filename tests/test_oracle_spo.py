@@ -167,3 +167,31 @@ def test_spo_block_grads_is_backward_restricted(kind, d, b):
     sel = O.spo_block_grads(X, dY, f, range(dq.shape[0]))
     for k, v in sel.items():
         np.testing.assert_allclose(v, dq[k], rtol=0, atol=1e-12)
+
+
+def test_chain_merge_preserves_the_function():
+    """Merging every factor into the weight leaves the chain's function unchanged: the row-form
+    chain with the factors equals the plain product with the merged weight and no factors."""
+    rng = np.random.default_rng(8)
+    m, n, b = 10, 7, 3
+    R, P, W = _chain(rng, m, n, ["full", "block", "block"], ["block", "full"], b)
+    X = rng.standard_normal((6, m))
+    Wm = O.chain_merge(W, R, P)
+    np.testing.assert_allclose(O.chain_forward(X, Wm, [], []), O.chain_forward(X, W, R, P), rtol=0, atol=1e-12)
+    # the merged weight is not the original one (the factors were not the identity)
+    assert np.abs(Wm - W).max() > 1e-3
+
+
+def test_chain_merge_of_one_factor_per_side_is_the_layer_merge():
+    """c = 1: the dense merge equals merge_reinit's merged weight (blockwise products on the
+    pre-merged weight, scattered back to the natural order)."""
+    rng = np.random.default_rng(9)
+    m, n, b = 11, 9, 4
+    W = rng.standard_normal((m, n))
+    pR, pP = rng.permutation(m).astype(np.int32), rng.permutation(n).astype(np.int32)
+    qR = rng.standard_normal((-(-m // b), O.packed_len(b))) * 0.1
+    qP = rng.standard_normal((-(-n // b), O.packed_len(b))) * 0.1
+    R = [O.SpoFactor("block", pR, qR, m, b)]
+    P = [O.SpoFactor("block", pP, qP, n, b)]
+    ref = O.merge_reinit(O.premerge(W, pR, pP), pR, pP, O.side_G(qR, m, b), O.side_G(qP, n, b), 1, 2)
+    np.testing.assert_allclose(O.chain_merge(W, R, P), ref.W_new, rtol=0, atol=1e-12)
