@@ -237,6 +237,8 @@ def summarize_classes(mfma_dir, fetch_dir, write_dir, cmds):
             else:
                 a["ns_" + key] += e["ns"]
                 a[key] += e[ctr] * 1024 * scale[key]
+    # one k_pack_dq launch ends every step: the timed steps and the separate pass that times the contractions
+    steps = sum(1 for e in rows["mfma"].values() if "k_pack_dq" in e["name"]) or 1
     lines = []
     for c in dict.fromkeys(c for _, c in KERNEL_CLASSES):
         a = cls.get(c)
@@ -244,11 +246,11 @@ def summarize_classes(mfma_dir, fetch_dir, write_dir, cmds):
             continue
         busy = a["busy"] / (a["gui"] / N_XCC * n_simd) if a["gui"] else 0.0
         gbs = lambda k: a[k] / (a["ns_" + k] * 1e-9) / 1e9 if a["ns_" + k] else 0.0
-        lines.append(f"| {c} | {a['n']} | {a['ns_mfma'] / 1e6:.3f} | {100 * busy:.1f}% | {a['fetch'] / 1e9:.3f} | "
-                     f"{a['write'] / 1e9:.3f} | {gbs('fetch') + gbs('write'):.0f} |")
+        lines.append(f"| {c} | {a['n'] / steps:g} | {a['ns_mfma'] / 1e6 / steps:.3f} | {100 * busy:.1f}% | "
+                     f"{a['fetch'] / 1e9 / steps:.3f} | {a['write'] / 1e9 / steps:.3f} | {gbs('fetch') + gbs('write'):.0f} |")
     txt = f"""# One bench step by kernel class: MFMA busy and HBM traffic (rocprofv3 counters)
 
-Workload: one step of bench.py's default (7 POET-X linears of a Llama-8B decoder layer, T = 8192, b = 512,
+Workload: bench.py's default step (7 POET-X linears of a Llama-8B decoder layer, T = 8192, b = 512,
 bf16), warm-up 0; the FETCH_SIZE and WRITE_SIZE runs add a {COPY_PROBE_BYTES >> 20} MiB device copy as calibration.
 
 Commands (from the repository root on one MI355X, one counter set per run):
@@ -264,8 +266,10 @@ Commands (from the repository root on one MI355X, one counter set per run):
   FETCH_SIZE x{scale['fetch']:.3f} and WRITE_SIZE x{scale['write']:.3f} (the factors that map each counter's
   reading for the copy probe to its true bytes); rates divide by the same run's kernel durations.
 - Durations are those of the counter run (the profiler serialises dispatches), not the bench timing.
+- Each run holds {steps} steps (the timed step and the pass that times the W~ contractions); launches, ms and GB
+  are per step. The optimiser step runs after the timed steps, outside them.
 
-| class | launches | ms | MFMA busy | GB fetched | GB written | GB/s (fetch + write) |
+| class | launches / step | ms / step | MFMA busy | GB fetched | GB written | GB/s (fetch + write) |
 |---|---|---|---|---|---|---|
 """ + "\n".join(lines) + "\n"
     with open(CLASSES_MD, "w") as fh:
