@@ -265,4 +265,45 @@ PX_DEV void dma_mainloop(char* lds, const DmaSrc& src, int KT, Acc<C>& acc, int 
   barrier_raw();
 }
 
+// One pipelined K loop over three products of the same shape added in acc:
+// K tile t (0 <= t < 3 KT) comes from source t / KT at K offset
+// (t % KT) * BK, so the copies of the next product are in flight while the
+// last tiles of the current one are multiplied.
+template <class C>
+PX_DEV void dma_mainloop_sum3(char* lds, const DmaSrc& s0, const DmaSrc& s1, const DmaSrc& s2, int KT, Acc<C>& acc,
+                              int wm, int wn, int lane) {
+  const int wave = threadIdx.x >> 6;
+  acc.zero();
+  const int TT = 3 * KT;
+  // source sg as s0 + [sg == 1] (s1 - s0) + [sg == 2] (s2 - s0), in scalar
+  // arithmetic (a select between the three is compiled to a table in scratch)
+  auto addr = [](const bf16_t* p) { return reinterpret_cast<uintptr_t>(p); };
+  const uintptr_t a1 = addr(s1.a) - addr(s0.a), a2 = addr(s2.a) - addr(s0.a);
+  const uintptr_t b1 = addr(s1.b) - addr(s0.b), b2 = addr(s2.b) - addr(s0.b);
+  const int64_t la1 = s1.lda - s0.lda, la2 = s2.lda - s0.lda, lb1 = s1.ldb - s0.ldb, lb2 = s2.ldb - s0.ldb;
+  auto issue = [&](int t, char* stage) {
+    const int sg = t / KT;
+    const uintptr_t e1 = sg == 1, e2 = sg == 2;
+    const DmaSrc s{reinterpret_cast<const bf16_t*>(addr(s0.a) + e1 * a1 + e2 * a2),
+                   s0.lda + (int64_t)e1 * la1 + (int64_t)e2 * la2,
+                   reinterpret_cast<const bf16_t*>(addr(s0.b) + e1 * b1 + e2 * b2),
+                   s0.ldb + (int64_t)e1 * lb1 + (int64_t)e2 * lb2};
+    dma_issue<C>(s, stage, (t - sg * KT) * C::BK, wave, lane);
+  };
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < TT) issue(s, lds + s * C::STAGE_BYTES);
+  for (int kt = 0; kt < TT; ++kt) {
+    wait_ahead<C, C::STAGES - 2>(min(C::STAGES - 2, TT - 1 - kt));
+    wait_lgkm0();
+    barrier_raw();
+    const int nxt = kt + C::STAGES - 1;
+    if (nxt < TT) issue(nxt, lds + (nxt % C::STAGES) * C::STAGE_BYTES);
+    const char* st = lds + (kt % C::STAGES) * C::STAGE_BYTES;
+    dma_mma_stage<C>(st, st + C::A_BYTES, acc, wm, wn, lane);
+  }
+  wait_lgkm0();
+  barrier_raw();
+}
+
 }  // namespace px

@@ -194,9 +194,11 @@ PX_DEV void mainloop2_t(T* lds, LA& la0, LB& lb0, int KT, Acc<C>& acc, int wm, i
   }
 }
 
+// acc = A B^T over K; with zero false, acc += A B^T
 template <class C, typename T, class LA, class LB, class H = NoHook>
-PX_DEV void mainloop(T* lds, LA& la, LB& lb, int K, Acc<C>& acc, int wm, int wn, int lane, const H& hook = H()) {
-  acc.zero();
+PX_DEV void mainloop(T* lds, LA& la, LB& lb, int K, Acc<C>& acc, int wm, int wn, int lane, const H& hook = H(),
+                     bool zero = true) {
+  if (zero) acc.zero();
   const int KT = (K + C::BK - 1) / C::BK;
   if (KT <= 0) return;
   // tiles entirely inside both operands take the loop without bounds checks

@@ -3,20 +3,22 @@
 //
 // Build (POET-X blog on zhichai.net, 第四斧: Q^2 once, Q^3 and Q^4 from it):
 //   S = Q^2, N = 2Q + S,  G - I = 2Q + 2S + S N  (= 2Q + 2Q^2 + 2Q^3 + Q^4).
-// Chain rule of G = I + 2(Q + Q^2 + Q^3) + Q^4 with Q^T = -Q, grouped by powers
-// of Q on the left: with U = dL/dG (the block gradient, summed over tokens
-// here too), V1 = U Q, V2 = V1 Q, V3 = V2 Q,
-//   dQ = X0 + Q (X1 + Q (X2 + Q X3)),
-//   X0 = 2U - 2V1 + 2V2 - V3, X1 = -2U + 2V1 - V2, X2 = 2U - V1, X3 = -U,
-// then dq[p(i,j)] = dQ[i][j] - dQ[j][i] on the packed slots.
+// Chain rule of G = I + 2(Q + Q^2 + Q^3) + Q^4 with Q^T = -Q: with U = dL/dG
+// (the block gradient, summed over tokens here too), the derivative of L with
+// respect to the entries of Q is
+//   D = 2U - 2(UQ + QU) + 2(UQ^2 + QUQ + Q^2U) - (UQ^3 + QUQ^2 + Q^2UQ + Q^3U),
+// the ten terms of dG paired with U.  With V1 = U Q, P = Q U, S = Q^2 and
+// W = 2U - V1 - P the same sum is
+//   D = (2U - 2V1 - 2P) + 2 Q V1 + W S + S W,
+// six b x b products in two launches; then dq[p(i,j)] = D[i][j] - D[j][i] on
+// the packed slots.
 //
 // Q is unpacked once into a dense block buffer; every product reads plain
 // row-major operands.  Products with Q on the right load Q's rows as the B
 // operand, which yields X Q^T = -X Q (the sign is folded into the epilogue);
 // products with a non-symmetric matrix on the right read the transpose that
-// the producing epilogue wrote.  The linear combinations X0..X2 are carried
-// in one fp32 array that each step updates in place, so every step reads and
-// writes each element once.
+// the producing epilogue wrote.  The fp32 part of D is carried in one array
+// that each launch updates in place.
 #include "kernel_util.h"
 
 using namespace px;
@@ -85,7 +87,9 @@ PX_DEV void run_kk(unsigned char* smem, const T* a0, int rows_a, const T* b0, in
 }
 
 // Two products of the same shape, X0 Y0^T and X1 Y1^T, one after the other in
-// the same workgroup; epi(acc0, acc1).  Both take the same loop.
+// the same workgroup; epi(acc0, acc1).  Both take the same loop.  (One
+// pipeline over both, with the accumulator chosen per K tile, needs more than
+// the 256 registers of two waves per SIMD.)
 template <class C, typename T, class Epi>
 PX_DEV void run_kk2(unsigned char* smem, const T* x0, const T* y0, const T* x1, const T* y1, int rows_x, int rows_y,
                     int b, int K, Epi&& epi) {
@@ -96,7 +100,6 @@ PX_DEV void run_kk2(unsigned char* smem, const T* x0, const T* y0, const T* x1, 
       const AccPos<DSq> p = acc_pos<DSq>();
       const DmaSrc s0{reinterpret_cast<const bf16_t*>(x0), b, reinterpret_cast<const bf16_t*>(y0), b};
       dma_mainloop<DSq>(reinterpret_cast<char*>(smem), s0, K / DSq::BK, a0, p.wm, p.wn, p.lane, NoHook());
-      __syncthreads();
       const DmaSrc s1{reinterpret_cast<const bf16_t*>(x1), b, reinterpret_cast<const bf16_t*>(y1), b};
       dma_mainloop<DSq>(reinterpret_cast<char*>(smem), s1, K / DSq::BK, a1, p.wm, p.wn, p.lane, NoHook());
       epi(a0, a1);
@@ -121,6 +124,42 @@ PX_DEV void run_kk2(unsigned char* smem, const T* x0, const T* y0, const T* x1, 
     mainloop<C, T>(reinterpret_cast<T*>(smem), la, lb, K, a1, p.wm, p.wn, p.lane);
   }
   epi(a0, a1);
+}
+
+// Three products of the same shape added in one accumulator,
+// X0 Y0^T + X1 Y1^T + X2 Y2^T; epi(acc).  All three take the same loop.
+template <class C, typename T, class Epi>
+PX_DEV void run_kk_sum3(unsigned char* smem, const T* x0, const T* y0, const T* x1, const T* y1, const T* x2,
+                        const T* y2, int rows_x, int rows_y, int b, int K, Epi&& epi) {
+  if constexpr (std::is_same<T, bf16_t>::value && C::BM == DSq::BM && C::BN == DSq::BN && C::NT == DSq::NT) {
+    if (dma_rows_ok(x0, b, rows_x, DSq::BM) && dma_rows_ok(x1, b, rows_x, DSq::BM) &&
+        dma_rows_ok(x2, b, rows_x, DSq::BM) && dma_rows_ok(y0, b, rows_y, DSq::BN) &&
+        dma_rows_ok(y1, b, rows_y, DSq::BN) && dma_rows_ok(y2, b, rows_y, DSq::BN) && K % DSq::BK == 0) {
+      Acc<DSq> acc;
+      const AccPos<DSq> p = acc_pos<DSq>();
+      const DmaSrc s0{reinterpret_cast<const bf16_t*>(x0), b, reinterpret_cast<const bf16_t*>(y0), b};
+      const DmaSrc s1{reinterpret_cast<const bf16_t*>(x1), b, reinterpret_cast<const bf16_t*>(y1), b};
+      const DmaSrc s2{reinterpret_cast<const bf16_t*>(x2), b, reinterpret_cast<const bf16_t*>(y2), b};
+      dma_mainloop_sum3<DSq>(reinterpret_cast<char*>(smem), s0, s1, s2, K / DSq::BK, acc, p.wm, p.wn, p.lane);
+      epi(acc);
+      return;
+    }
+  }
+  const AccPos<C> p = acc_pos<C>();
+  Acc<C> acc;
+  auto add = [&](const T* x, const T* y, bool first) {
+    LoadK<C::BM, C::BK, C::NT, T, T> la;
+    la.init(x, b, rows_x, K);
+    LoadK<C::BN, C::BK, C::NT, T, T> lb;
+    lb.init(y, b, rows_y, K);
+    mainloop<C, T>(reinterpret_cast<T*>(smem), la, lb, K, acc, p.wm, p.wn, p.lane, NoHook(), first);
+  };
+  add(x0, y0, true);
+  __syncthreads();
+  add(x1, y1, false);
+  __syncthreads();
+  add(x2, y2, false);
+  epi(acc);
 }
 
 // Dense Q from the packed parameters, one 64 x 64 tile per workgroup: entries
@@ -274,13 +313,13 @@ template <typename T> struct GradSides {
 
 template <typename T> struct Chain {
   const T* Qb;
-  float* F32;  // U, then 2U - 2V1, then (2U - 2V1) + 2V2, then dQ (updated in place)
-  T* Ub;
-  T* Utb;
-  T* V1b;
-  T* V2b;
-  T* Y1tb;
-  T* Y2tb;
+  float* F32;  // U, then 2U - 2V1 - 2P, then D (updated in place)
+  T* Ub;       // U
+  T* Utb;      // U^T
+  T* Wb;       // W = 2U - V1 - P
+  T* Wtb;      // W^T
+  T* V1tb;     // (2 V1)^T
+  T* Sb;       // S = Q^2
 };
 
 // G groups of C::NT threads split the token range of one output tile; their
@@ -484,33 +523,47 @@ __global__ __launch_bounds__(256) void k_block_grads_reduce(SideTable sd, int b,
   }
 }
 
-// Chain rule in three launches; each workgroup forms one tile of two
-// products, X Q (X = U, V1, V2) and Q Y (Y = U, Y1, Y2):
-//   step 1: V1 = U Q,  P = Q U;   Y1 = 2U - V1 - P,         F = 2U - 2V1
-//   step 2: V2 = V1 Q, Q Y1;      Y2 = -F - V2 + Q Y1,      F = F + 2V2
-//   step 3: V3 = V2 Q, Q Y2;      dQ = F - V3 + Q Y2
-// X Q loads Q's rows as the B operand, which gives X Q^T = -X Q; Q Y loads
-// the rows of Y^T, which the previous step wrote.
-template <class C, typename T, int STEP>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_step(SideTable sd, int b, Chain<T> ch) {
+// Chain rule, first launch, two workgroups per output tile (both on the XCD
+// of their block).  The first forms U Q^T = -V1 and Q U = P (the rows of U^T
+// as B operand) and writes W = 2U - V1 - P (row-major and transposed),
+// (2 V1)^T and the fp32 part 2U - 2V1 - 2P over U; the second forms
+// Q Q^T = -S and writes S.
+template <class C, typename T>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_grad1(SideTable sd, int b,
+                                                                                            Chain<T> ch) {
   extern __shared__ __align__(16) unsigned char smem[];
-  const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM;
-  const int u = xcd_unit(blockIdx.x, gridDim.x), z = u / (tm * tn);
+  const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM, tiles = tm * tn;
+  // units: tile fastest, then the kind of workgroup, then the block
+  const int u = xcd_unit(blockIdx.x, gridDim.x), z = u / (2 * tiles), kind = u / tiles % 2;
   const float* qk;
   int r;
   sd.at(z, b, qk, r);
-  const int m0 = (u % (tm * tn) / tn) * C::BM, n0 = (u % tn) * C::BN;
-  if (m0 >= r || n0 >= r) return;  // later steps and the packing read only the live corner
+  const int m0 = (u % tiles / tn) * C::BM, n0 = (u % tn) * C::BN;
+  if (m0 >= r || n0 >= r) return;  // the second launch and the packing read only the live corner
   const int64_t off = (int64_t)z * b * b;
-  const T* X = STEP == 1 ? ch.Ub : STEP == 2 ? ch.V1b : ch.V2b;
-  const T* Yt = STEP == 1 ? ch.Utb : STEP == 2 ? ch.Y1tb : ch.Y2tb;
-  run_kk2<C, T>(smem, X + off + (int64_t)m0 * b, ch.Qb + off + (int64_t)n0 * b, ch.Qb + off + (int64_t)m0 * b,
-                Yt + off + (int64_t)n0 * b, r - m0, r - n0, b, r, [&](auto& xq, auto& qy) {
-    using CC = cfg_of<decltype(xq)>;
+  const T* Qm = ch.Qb + off + (int64_t)m0 * b;
+  const T* Qn = ch.Qb + off + (int64_t)n0 * b;
+  if (kind == 1) {
+    run_kk<C, T>(smem, Qm, r - m0, Qn, r - n0, b, r, [&](auto& qq) {
+      using CC = cfg_of<decltype(qq)>;
+      each_acc4<CC>(qq, [&](int i0, int j, const float* v) {
+        i0 += m0;
+        j += n0;
+        if (j >= r || i0 >= r) return;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i0 + e < r) ch.Sb[off + (int64_t)(i0 + e) * b + j] = from_f32<T>(-v[e]);
+      });
+    });
+    return;
+  }
+  run_kk2<C, T>(smem, ch.Ub + off + (int64_t)m0 * b, Qn, Qm, ch.Utb + off + (int64_t)n0 * b, r - m0, r - n0, b, r,
+                [&](auto& uq, auto& qu) {
+    using CC = cfg_of<decltype(uq)>;
     const AccPos<CC> p = acc_pos<CC>();
 #pragma unroll
     for (int ti = 0; ti < CC::TM; ++ti) {
-      // one row group of F at a time keeps the epilogue's registers down
+      // one row group of U at a time keeps the epilogue's registers down
       float f[CC::TN][16];
       load_at_acc_i<CC>(f, ch.F32 + off, b, m0, n0, r, r, ti);
 #pragma unroll
@@ -520,32 +573,66 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         for (int g = 0; g < 4; ++g) {
           const int i0 = m0 + p.row(ti, 4 * g);
           if (j >= r || i0 >= r) continue;
-          float y[4] = {0.f, 0.f, 0.f, 0.f};
+          float w[4] = {0.f, 0.f, 0.f, 0.f}, v2[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if (i0 + e >= r) continue;
             const int k = 4 * g + e;
             const int64_t x = off + (int64_t)(i0 + e) * b + j;
-            const float fv = f[tj][k], v = -xq.v[ti][tj][k], c = qy.v[ti][tj][k];
-            if (STEP == 1) {
-              ch.V1b[x] = from_f32<T>(v);
-              ch.F32[x] = 2.f * fv - 2.f * v;
-              y[e] = 2.f * fv - v - c;
-            } else if (STEP == 2) {
-              ch.V2b[x] = from_f32<T>(v);
-              ch.F32[x] = fv + 2.f * v;
-              y[e] = -fv - v + c;
-            } else {
-              ch.F32[x] = fv - v + c;
+            const float uv = f[tj][k], v1 = -uq.v[ti][tj][k], pv = qu.v[ti][tj][k];
+            w[e] = 2.f * uv - v1 - pv;
+            v2[e] = 2.f * v1;
+            ch.Wb[x] = from_f32<T>(w[e]);
+            ch.F32[x] = 2.f * uv - 2.f * v1 - 2.f * pv;
+          }
+          T* wt = ch.Wtb + off + (int64_t)j * b + i0;
+          T* vt = ch.V1tb + off + (int64_t)j * b + i0;
+          if (i0 + 4 <= r) {
+            store4<T>(wt, w);
+            store4<T>(vt, v2);
+          } else {
+            for (int e = 0; e < 4 && i0 + e < r; ++e) {
+              wt[e] = from_f32<T>(w[e]);
+              vt[e] = from_f32<T>(v2[e]);
             }
           }
-          if (STEP <= 2) {
-            T* dst = (STEP == 1 ? ch.Y1tb : ch.Y2tb) + off + (int64_t)j * b + i0;
-            if (i0 + 4 <= r)
-              store4<T>(dst, y);
-            else
-              for (int e = 0; e < 4 && i0 + e < r; ++e) dst[e] = from_f32<T>(y[e]);
-          }
+        }
+      }
+    }
+  });
+}
+
+// Chain rule, second launch: D = F + Q (2 V1) + W S + S W over F in place,
+// one output tile per workgroup, the three products added in one
+// accumulator (S is symmetric, so its rows serve as the B operand of W S).
+template <class C, typename T>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_grad2(SideTable sd, int b,
+                                                                                            Chain<T> ch) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM;
+  const int u = xcd_unit(blockIdx.x, gridDim.x), z = u / (tm * tn);
+  const float* qk;
+  int r;
+  sd.at(z, b, qk, r);
+  const int m0 = (u % (tm * tn) / tn) * C::BM, n0 = (u % tn) * C::BN;
+  if (m0 >= r || n0 >= r) return;  // the packing reads only the live corner
+  const int64_t off = (int64_t)z * b * b, om = off + (int64_t)m0 * b, on = off + (int64_t)n0 * b;
+  run_kk_sum3<C, T>(smem, ch.Qb + om, ch.V1tb + on, ch.Wb + om, ch.Sb + on, ch.Sb + om, ch.Wtb + on, r - m0, r - n0, b,
+                    r, [&](auto& acc) {
+    using CC = cfg_of<decltype(acc)>;
+    const AccPos<CC> p = acc_pos<CC>();
+#pragma unroll
+    for (int ti = 0; ti < CC::TM; ++ti) {
+      float f[CC::TN][16];
+      load_at_acc_i<CC>(f, ch.F32 + off, b, m0, n0, r, r, ti);
+#pragma unroll
+      for (int tj = 0; tj < CC::TN; ++tj) {
+        const int j = n0 + p.col(tj);
+        if (j >= r) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int i = m0 + p.row(ti, e);
+          if (i < r) ch.F32[off + (int64_t)i * b + j] = f[tj][e] + acc.v[ti][tj][e];
         }
       }
     }
@@ -637,10 +724,10 @@ template <typename T> Chain<T> carve(void* ws, size_t E) {
   ch.Qb = takeT();
   ch.Ub = takeT();
   ch.Utb = takeT();
-  ch.V1b = takeT();
-  ch.V2b = takeT();
-  ch.Y1tb = takeT();
-  ch.Y2tb = takeT();
+  ch.Wb = takeT();
+  ch.Wtb = takeT();
+  ch.V1tb = takeT();
+  ch.Sb = takeT();
   return ch;
 }
 
@@ -710,14 +797,11 @@ hipError_t chain_t(const SideTable& sd, int b, void* dg, const DqOut& out, hipSt
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = hipSuccess;
   const unsigned grid = cdiv(b, C::BN) * cdiv(b, C::BM) * NB;
-#define PX_STEP(K)                                   \
-  e = allow_lds(k_cnp_step<C, T, K>, lds);            \
-  if (e != hipSuccess) return e;                      \
-  k_cnp_step<C, T, K><<<grid, C::NT, lds, s>>>(sd, b, ch);
-  PX_STEP(1)
-  PX_STEP(2)
-  PX_STEP(3)
-#undef PX_STEP
+  e = allow_lds(k_cnp_grad1<C, T>, lds);
+  if (e == hipSuccess) e = allow_lds(k_cnp_grad2<C, T>, lds);
+  if (e != hipSuccess) return e;
+  k_cnp_grad1<C, T><<<2 * grid, C::NT, lds, s>>>(sd, b, ch);
+  k_cnp_grad2<C, T><<<grid, C::NT, lds, s>>>(sd, b, ch);
   k_pack_dq<<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, ch.F32, out);
   return hipGetLastError();
 }

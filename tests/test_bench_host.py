@@ -49,5 +49,5 @@ def test_kernel_classes():
     assert k("k_scatter_lds<unsigned short>") == "permutations"
     assert k("k_permute_lds<unsigned short>") == "permutations"
     assert k("k_adam<4>") == "optimiser step"
-    assert k("k_cnp_step<...>") == "CNP products"
+    assert k("k_cnp_grad1<...>") == "CNP products"
     assert k("at::native::vectorized_elementwise_kernel") is None
