@@ -388,7 +388,7 @@ class WorkloadStep:
     whole hot path over one batch (batched CNP build, the forwards, the backwards to dX and the block
     gradients, the batched CNP chain rule to every side's packed dq, and optionally the Adam step)."""
 
-    def __init__(self, wl, mode, to_dev, dev, optimizer=False):
+    def __init__(self, wl, mode, to_dev, dev, optimizer=False, batch_grads=True):
         import torch
 
         from orthogonal_reparameterized_cnp_amd.layer import PoetxAdam, PoetxGroup, PoetxLinear
@@ -413,9 +413,11 @@ class WorkloadStep:
         self.dXs = [torch.empty(self.T, L.m, dtype=dt, device=dev) for L in wl.linears]
         self.dqs = [(torch.empty_like(l.q_R), torch.empty_like(l.q_P)) for l in self.layers]
         # The layer's seven linears share their CNP work: every side's G is built in one batch, and the
-        # chain rule to dq runs once for all sides after the backward of the last linear (results
+        # block gradients and the chain rule to dq run once for all sides after the backward of the
+        # last linear (batch_grads; without it the block gradients run per linear and the results are
         # bit-identical to per-linear calls).
-        self.group = PoetxGroup(self.layers)
+        self.batch_grads = batch_grads
+        self.group = PoetxGroup(self.layers, batch_grads=batch_grads)
         # Adam on every side's packed q (lr small enough that the timed steps stay near the start)
         self.opt = PoetxAdam(self.layers, lr=1e-5)
         self.optimizer = optimizer
@@ -542,6 +544,9 @@ def main():
     ap.add_argument("--mode", choices=("xfast", "xmem", "xout"), default="xfast",
                     help="xfast saves H for the backward; xmem saves only the gathered input and recomputes H; "
                          "xout saves only the gathered input and takes H back from the output")
+    ap.add_argument("--grads", choices=("batched", "per-linear"), default="batched",
+                    help="block gradients of all sides in shared launches after the last backward (dq equal to "
+                         "the per-linear calls' to fp32 rounding), or inside each linear's backward")
     ap.add_argument("--merge", metavar="WORKLOAD", nargs="?", const="llama13b_int8", default=None,
                     help="also time poetx_merge_reinit of every linear of WORKLOAD (default llama13b_int8) and "
                          "report it amortised over the workload's merge period")
@@ -592,7 +597,7 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     t_gen = time.perf_counter()
-    ws = WorkloadStep(wl, args.mode, to_dev, dev, optimizer=args.optimizer)
+    ws = WorkloadStep(wl, args.mode, to_dev, dev, optimizer=args.optimizer, batch_grads=args.grads == "batched")
     layers, inputs0, opt, dqs, step = ws.layers, ws.inputs0, ws.opt, ws.dqs, ws.step
     print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
@@ -662,6 +667,7 @@ def main():
             "weights": wl.w,
             "mode": args.mode,
             "optimizer_in_step": "adam" if args.optimizer else None,
+            "block_grads": args.grads,
             "launch": "hip graph replay" if args.graph else "eager",
         },
         "tflops": total_f / (ms * 1e-3) / 1e12,

@@ -320,6 +320,54 @@ poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const 
                                  void* dg, int64_t dg_first, int64_t dg_blocks, void* ws, size_t ws_bytes,
                                  void* stream);
 
+/* The operands of one side's block gradients (see poetx_linear_bwd): block k
+ * of the side is dG_k = A[:, kb..kb+r)^T B[:, kb..kb+r) summed over the token
+ * rows, kb = k b, r = min(b, d - kb).  A and B are device [rows][lda] and
+ * [rows][ldb] matrices of the layer's act_dtype: for the R side the gathered
+ * input Xt and dA = dZt Diag(G_P)^T W~^T, for the P side H and dZt. */
+typedef struct poetx_grad_side {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  int32_t d;
+} poetx_grad_side;
+
+/*
+ * poetx_linear_bwd_dx without the block gradients, so that those of many
+ * linears run as one batch (poetx_block_grads_batch).  Computes dX exactly as
+ * poetx_linear_bwd does and writes the operands of the two sides' block
+ * gradients to sides[0] (R) and sides[1] (P) (a HOST array of 2).  They point
+ * into H_save and ws and stay valid until either is written again.
+ * Arguments and errors as for poetx_linear_bwd (q_R, q_P and dq are not taken).
+ */
+poetx_status poetx_linear_bwd_dx_sides(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ,
+                                       const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
+                                       const void* g_P, const void* H_save, void* dX, poetx_grad_side* sides,
+                                       void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of poetx_block_grads_batch (the fp32 partial sums of token
+ * splits; 0 when no split is used or for invalid arguments). */
+size_t poetx_block_grads_workspace_size(int32_t count, const int32_t* d, int64_t rows, int32_t b, int32_t dtype);
+
+/*
+ * The block gradients of `count` sides over the same `rows` token rows, as
+ * poetx_linear_bwd defines them, into the gradient state `dg`: side i owns the
+ * next ceil(d_i / b) blocks, as poetx_cnp_backward_batch then reads them.  The
+ * sides share launches (up to 16 per launch), so the token range is split for
+ * the whole batch: the sums are taken in a fixed order, but in other splits
+ * than per-linear calls, so results match those to fp32 rounding, not bit for
+ * bit.
+ *   sides  HOST array of count operand descriptors (poetx_linear_bwd_dx_sides)
+ *   count  1 .. POETX_MAX_SIDES;  dtype F32 or BF16 (the operands' act_dtype)
+ *   dg     gradient state of at least poetx_cnp_grad_bytes(sum of blocks, b, dtype) bytes
+ *   ws     >= poetx_block_grads_workspace_size(count, d, rows, b, dtype), 256-byte aligned
+ * Errors: POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_HIP.
+ */
+poetx_status poetx_block_grads_batch(int32_t count, const poetx_grad_side* sides, int64_t rows, int32_t b,
+                                     int32_t dtype, void* dg, size_t dg_bytes, void* ws, size_t ws_bytes,
+                                     void* stream);
+
 /*
  * The CNP chain rule and skew projection (as in poetx_linear_bwd) for `count`
  * sides whose block gradients fill the gradient state `dg` in order: side i
@@ -329,7 +377,8 @@ poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const 
  * bit-identical to the chain rule inside poetx_linear_bwd.
  *   count  1 .. POETX_MAX_SIDES, with the sum of the sides' blocks equal to the
  *          state's block count
- *   dg     gradient state written by poetx_linear_bwd_dx; dg_bytes its size
+ *   dg     gradient state written by poetx_linear_bwd_dx or poetx_block_grads_batch;
+ *          dg_bytes its size
  * Errors: POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE, POETX_E_HIP.
  */
 poetx_status poetx_cnp_backward_batch(int32_t count, const float* const* q, const int32_t* d, int32_t b, int32_t dtype,

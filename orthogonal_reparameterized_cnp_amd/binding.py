@@ -30,6 +30,7 @@ POETX_KC_NONE, POETX_KC_GEMM, POETX_KC_APPLY, POETX_KC_DGRAD, POETX_KC_CNP, POET
 DTYPES = {"f32": POETX_F32, "bf16": POETX_BF16, "i8": POETX_I8}
 # what the forward saves: H and Xt; Xt only (H recomputed from it); Xt only (H taken back from Y)
 POETX_XFAST, POETX_XMEM, POETX_XOUT = 0, 1, 2
+POETX_MAX_SIDES = 64  # most sides one batched call accepts
 MODES = {"xfast": POETX_XFAST, "xmem": POETX_XMEM, "xout": POETX_XOUT}
 
 
@@ -60,6 +61,16 @@ class SpoDesc(ctypes.Structure):
         ("b", ctypes.c_int32),
         ("kind", ctypes.c_int32),
         ("act_dtype", ctypes.c_int32),
+    ]
+
+
+class GradSide(ctypes.Structure):
+    _fields_ = [
+        ("A", ctypes.c_void_p),
+        ("lda", ctypes.c_int64),
+        ("B", ctypes.c_void_p),
+        ("ldb", ctypes.c_int64),
+        ("d", ctypes.c_int32),
     ]
 
 
@@ -124,6 +135,18 @@ _SIG = {
         ctypes.c_int,
         [ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, _P,
          ctypes.c_size_t, ctypes.POINTER(_P), _P],
+    ),
+    "poetx_linear_bwd_dx_sides": (
+        ctypes.c_int,
+        [ctypes.POINTER(LayerDesc), ctypes.c_int64] + [_P] * 9 + [ctypes.POINTER(GradSide), _P, ctypes.c_size_t, _P],
+    ),
+    "poetx_block_grads_workspace_size": (
+        ctypes.c_size_t, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    ),
+    "poetx_block_grads_batch": (
+        ctypes.c_int,
+        [ctypes.c_int32, ctypes.POINTER(GradSide), ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_size_t,
+         _P, ctypes.c_size_t, _P],
     ),
     "poetx_spo_saved_bytes": (ctypes.c_size_t, [ctypes.POINTER(SpoDesc), ctypes.c_int64]),
     "poetx_spo_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(SpoDesc), ctypes.c_int64, ctypes.c_int32]),
@@ -327,6 +350,30 @@ def poetx_linear_bwd_dx(dsc: LayerDesc, T: int, Y, dZ, perm_R, perm_P, Wt, g_R, 
             _stream(stream),
         )
     )
+
+
+def poetx_linear_bwd_dx_sides(dsc: LayerDesc, T: int, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, H_save, dX, ws,
+                              ws_bytes: int, stream=None):
+    """dX into `dX`; returns the two sides' block-gradient operands (R, P) as GradSide records."""
+    sides = (GradSide * 2)()
+    _check(
+        lib().poetx_linear_bwd_dx_sides(
+            ctypes.byref(dsc), T, _ptr(Y), _ptr(dZ), _ptr(perm_R), _ptr(perm_P), _ptr(Wt), _ptr(g_R), _ptr(g_P),
+            _ptr(H_save), _ptr(dX), sides, _ptr(ws), ws_bytes, _stream(stream),
+        )
+    )
+    return [sides[0], sides[1]]
+
+
+def poetx_block_grads_workspace_size(d, rows: int, b: int, dtype: int) -> int:
+    return lib().poetx_block_grads_workspace_size(len(d), _i32_array(d), rows, b, dtype)
+
+
+def poetx_block_grads_batch(sides, rows: int, b: int, dtype: int, dg, dg_bytes: int, ws, ws_bytes: int, stream=None):
+    """sides: list of GradSide records (from poetx_linear_bwd_dx_sides), marshalled into a host array."""
+    arr = (GradSide * len(sides))(*sides)
+    _check(lib().poetx_block_grads_batch(len(sides), arr, rows, b, dtype, _ptr(dg), dg_bytes, _ptr(ws), ws_bytes,
+                                         _stream(stream)))
 
 
 def poetx_cnp_backward_batch(q, d, b: int, dtype: int, dg, dg_bytes: int, dq, stream=None):

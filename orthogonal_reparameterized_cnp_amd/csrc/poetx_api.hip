@@ -500,11 +500,13 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
 namespace {
 
 // dX and the block gradients of both sides into blocks [first, first + nb_R + nb_P)
-// of the gradient state dg (total blocks); shared by both backward entry points.
+// of the gradient state dg (total blocks); shared by the backward entry points.
+// With `defer` the block gradients are not formed: defer[0] (R) and defer[1] (P)
+// receive their operands instead.
 poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ,
                          const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
                          const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX, void* dg,
-                         int64_t first, int64_t total, const BwdWs& w, hipStream_t s) {
+                         int64_t first, int64_t total, const BwdWs& w, hipStream_t s, CnpSide* defer = nullptr) {
   const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, wt = desc->w_dtype;
   const int rows = (int)T;
   const int64_t ldm = lead(m), ldn = lead(n);
@@ -537,9 +539,14 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* Y,
     H = w.Hr;
   }
   const CnpSide sides[2] = {{q_R, m, Xt, ldm, w.dA, ldm}, {q_P, n, H, ldn, w.dZt, ldn}};
-  PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * (sum_r2(m, b) + sum_r2(n, b)),
-           2.0 * rows * (m + n) * es + (4 + 2 * es) * (sum_r2(m, b) + sum_r2(n, b)),
-           block_grads(at, sides, rows, b, dg, first, total, w.part, s));
+  if (defer) {
+    defer[0] = sides[0];
+    defer[1] = sides[1];
+  } else {
+    PX_TIMED(POETX_KC_DGRAD, 2.0 * rows * (sum_r2(m, b) + sum_r2(n, b)),
+             2.0 * rows * (m + n) * es + (4 + 2 * es) * (sum_r2(m, b) + sum_r2(n, b)),
+             block_grads(at, sides, rows, b, dg, first, total, w.part, s));
+  }
   // dXt = dA Diag(G_R)^T;  dX[:, perm_R] = dXt
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
            apply(at, at, w.dA, ldm, rows, m, b, at, g_R, nullptr, at, w.dXt, ldm, s));
@@ -548,13 +555,16 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* Y,
   return POETX_OK;
 }
 
+// need_q: the call reads q_R and q_P (not when the block gradients are left to the caller)
 poetx_status check_bwd(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ, const int32_t* perm_R,
                        const int32_t* perm_P, const void* Wt, const void* g_R, const void* g_P, const float* q_R,
-                       const float* q_P, const void* H_save, void* dX, void* ws, size_t ws_bytes) {
+                       const float* q_P, const void* H_save, void* dX, void* ws, size_t ws_bytes,
+                       bool need_q = true) {
   poetx_status st = check_desc(desc);
   if (st != POETX_OK) return st;
   if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
-  if (!perm_R || !perm_P || !Wt || !g_R || !g_P || !q_R || !q_P) return fail(POETX_E_NULL, "a required pointer is NULL");
+  if (!perm_R || !perm_P || !Wt || !g_R || !g_P || (need_q && (!q_R || !q_P)))
+    return fail(POETX_E_NULL, "a required pointer is NULL");
   if (T > 0 && (!dZ || !H_save || !dX)) return fail(POETX_E_NULL, "a required pointer is NULL");
   if (T > 0 && desc->mode == POETX_XOUT && !Y) return fail(POETX_E_NULL, "Y is NULL (POETX_XOUT reads it)");
   Plan p;
@@ -607,6 +617,83 @@ poetx_status poetx_linear_bwd_dx(const poetx_layer_desc* desc, int64_t T, const 
   const BwdWs w = plan_bwd(pq, desc, T);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   return bwd_dx_core(desc, T, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, q_R, q_P, H_save, dX, dg, dg_first, dg_blocks, w, s);
+}
+
+poetx_status poetx_linear_bwd_dx_sides(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ,
+                                       const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
+                                       const void* g_P, const void* H_save, void* dX, poetx_grad_side* sides,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  poetx_status st =
+      check_bwd(desc, T, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, nullptr, nullptr, H_save, dX, ws, ws_bytes, false);
+  if (st != POETX_OK) return st;
+  if (!sides) return fail(POETX_E_NULL, "sides is NULL");
+  Plan pq;
+  pq.base = reinterpret_cast<char*>(ws);
+  const BwdWs w = plan_bwd(pq, desc, T);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  CnpSide cs[2];
+  st = bwd_dx_core(desc, T, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, nullptr, nullptr, H_save, dX, nullptr, 0, 0, w, s,
+                   cs);
+  if (st != POETX_OK) return st;
+  for (int k = 0; k < 2; ++k) sides[k] = poetx_grad_side{cs[k].A, cs[k].lda, cs[k].B, cs[k].ldb, cs[k].d};
+  return POETX_OK;
+}
+
+size_t poetx_block_grads_workspace_size(int32_t count, const int32_t* d, int64_t rows, int32_t b, int32_t dtype) {
+  int64_t blocks = 0;
+  if (rows < 0 || rows > kMaxT || check_sides(count, d, b, dtype, &blocks) != POETX_OK) return 0;
+  // one launch per kGradSides sides, one after the other on the stream: the partials buffer is shared
+  size_t need = 0;
+  for (int c0 = 0; c0 < count; c0 += kGradSides) {
+    int64_t nb = 0;
+    for (int i = c0; i < std::min<int>(count, c0 + kGradSides); ++i) nb += nblocks(d[i], b);
+    need = std::max(need, block_grads_part_bytes(dtype, (int)rows, (int)nb, b));
+  }
+  return need;
+}
+
+poetx_status poetx_block_grads_batch(int32_t count, const poetx_grad_side* sides, int64_t rows, int32_t b,
+                                     int32_t dtype, void* dg, size_t dg_bytes, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (!sides || !dg) return fail(POETX_E_NULL, "sides and dg must be non-NULL");
+  if (count < 1 || count > POETX_MAX_SIDES) return fail(POETX_E_SHAPE, "count must be in [1, POETX_MAX_SIDES]");
+  if (rows < 0 || rows > kMaxT) return fail(POETX_E_SHAPE, "rows must be in [0, 2^31)");
+  int32_t d[POETX_MAX_SIDES];
+  for (int i = 0; i < count; ++i) d[i] = sides[i].d;
+  int64_t blocks = 0;
+  poetx_status st = check_sides(count, d, b, dtype, &blocks);
+  if (st != POETX_OK) return st;
+  const double es = dtype == POETX_BF16 ? 2.0 : 4.0;
+  double flops = 0, bytes = 0;
+  for (int i = 0; i < count; ++i) {
+    if (rows > 0 && (!sides[i].A || !sides[i].B)) return fail(POETX_E_NULL, "sides[i].A and sides[i].B must be non-NULL");
+    if (sides[i].lda < d[i] || sides[i].ldb < d[i]) return fail(POETX_E_SHAPE, "lda and ldb must be >= d");
+    flops += 2.0 * rows * sum_r2(d[i], b);
+    bytes += 2.0 * rows * d[i] * es + (4 + 2 * es) * sum_r2(d[i], b);
+  }
+  if (dg_bytes < cnp_grad_bytes(dtype, blocks, b))
+    return fail(POETX_E_WORKSPACE, "dg smaller than poetx_cnp_grad_bytes of the sides' block count");
+  if (reinterpret_cast<uintptr_t>(dg) % 256) return fail(POETX_E_WORKSPACE, "dg must be 256-byte aligned");
+  const size_t need = poetx_block_grads_workspace_size(count, d, rows, b, dtype);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(POETX_E_WORKSPACE, "ws smaller than poetx_block_grads_workspace_size");
+  if (need > 0 && reinterpret_cast<uintptr_t>(ws) % 256) return fail(POETX_E_WORKSPACE, "ws must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  int64_t zoff = 0;
+  for (int c0 = 0; c0 < count; c0 += kGradSides) {
+    const int nc = std::min<int>(count - c0, kGradSides);
+    CnpSide cs[kGradSides];
+    int64_t nb = 0;
+    for (int k = 0; k < nc; ++k) {
+      const poetx_grad_side& g = sides[c0 + k];
+      cs[k] = CnpSide{nullptr, g.d, g.A, g.lda, g.B, g.ldb};
+      nb += nblocks(g.d, b);
+    }
+    PX_TIMED(POETX_KC_DGRAD, c0 == 0 ? flops : 0.0, c0 == 0 ? bytes : 0.0,
+             block_grads_n(dtype, nc, cs, (int)rows, b, dg, zoff, blocks, reinterpret_cast<float*>(ws), s));
+    zoff += nb;
+  }
+  return POETX_OK;
 }
 
 poetx_status poetx_cnp_backward_batch(int32_t count, const float* const* q, const int32_t* d, int32_t b, int32_t dtype,

@@ -39,11 +39,12 @@ struct SideTable {
     return s;
   }
   // side s, block blk of that side, its live size r and its packed parameters
+  // (null for a table built without them: the block gradients do not read q)
   PX_DEV void at(int z, int b, int& s, int& blk, int& r, const float*& qk) const {
     s = side_of(z);
     blk = z - first[s];
     r = min(b, d[s] - blk * b);
-    qk = q[s] + (int64_t)blk * ((int64_t)b * (b - 1) / 2);
+    qk = q[s] ? q[s] + (int64_t)blk * ((int64_t)b * (b - 1) / 2) : nullptr;
   }
   PX_DEV void at(int z, int b, const float*& qk, int& r) const {
     int s, blk;
@@ -306,9 +307,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 // tile and runs the whole token range, so the sum order is fixed.  Written as
 // fp32, operand dtype and operand-dtype transpose, the forms the chain reads.
 template <typename T> struct GradSides {
-  const T* A[2];
-  const T* B[2];
-  int64_t lda[2], ldb[2];
+  const T* A[pxk::kGradSides];
+  const T* B[pxk::kGradSides];
+  int64_t lda[pxk::kGradSides], ldb[pxk::kGradSides];
 };
 
 template <typename T> struct Chain {
@@ -744,16 +745,21 @@ SideTable make_table(int count, const float* const* q, const int* d, int b) {
 }
 
 template <typename T>
-hipError_t grads_t(const pxk::CnpSide* sides, int rows, int b, void* dg, int64_t zoff, int64_t total, float* part,
-                   hipStream_t s) {
+hipError_t grads_t(int count, const pxk::CnpSide* sides, int rows, int b, void* dg, int64_t zoff, int64_t total,
+                   float* part, hipStream_t s) {
   using C = typename CnpTile<T>::C;
-  const float* q[2] = {sides[0].q, sides[1].q};
-  const int d[2] = {sides[0].d, sides[1].d};
-  const SideTable sd = make_table(2, q, d, b);
-  const int NB = sd.first[2];
+  if (count < 1 || count > pxk::kGradSides) return hipErrorInvalidValue;
+  const float* q[pxk::kGradSides];
+  int d[pxk::kGradSides];
+  for (int k = 0; k < count; ++k) {
+    q[k] = sides[k].q;
+    d[k] = sides[k].d;
+  }
+  const SideTable sd = make_table(count, q, d, b);
+  const int NB = sd.first[count];
   Chain<T> ch = carve<T>(dg, (size_t)total * b * b);
-  GradSides<T> gs;
-  for (int k = 0; k < 2; ++k) {
+  GradSides<T> gs{};
+  for (int k = 0; k < count; ++k) {
     gs.A[k] = reinterpret_cast<const T*>(sides[k].A);
     gs.B[k] = reinterpret_cast<const T*>(sides[k].B);
     gs.lda[k] = sides[k].lda;
@@ -862,8 +868,13 @@ size_t block_grads_part_bytes(int dt, int rows, int blocks, int b) {
 
 hipError_t block_grads(int cdt, const CnpSide* sides, int rows, int b, void* dg, int64_t zoff, int64_t total,
                        float* part, hipStream_t s) {
-  if (cdt == BF16) return grads_t<bf16_t>(sides, rows, b, dg, zoff, total, part, s);
-  return grads_t<float>(sides, rows, b, dg, zoff, total, part, s);
+  return block_grads_n(cdt, 2, sides, rows, b, dg, zoff, total, part, s);
+}
+
+hipError_t block_grads_n(int cdt, int count, const CnpSide* sides, int rows, int b, void* dg, int64_t zoff,
+                         int64_t total, float* part, hipStream_t s) {
+  if (cdt == BF16) return grads_t<bf16_t>(count, sides, rows, b, dg, zoff, total, part, s);
+  return grads_t<float>(count, sides, rows, b, dg, zoff, total, part, s);
 }
 
 hipError_t cnp_chain_batch(int cdt, int count, const float* const* q, const int* d, int b, void* dg, float* const* dq,

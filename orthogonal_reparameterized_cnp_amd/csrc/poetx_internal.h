@@ -46,6 +46,7 @@ hipError_t perm_from_seed_device(uint64_t seed, int d, int32_t* out, int32_t* sc
 
 // Most sides in one batched CNP launch (the size of the kernels' side table).
 constexpr int kMaxSides = 64;
+constexpr int kGradSides = 16;  // sides of one block-gradient launch
 
 // Delta = G - I of every block of `count` sides, and its transpose: side i
 // writes g[i] = [2][nb_i][b][b] in dtype dt (F32 or BF16).  Sides are
@@ -86,6 +87,10 @@ struct CnpSide {
 //   added in split order.
 hipError_t block_grads(int cdt, const CnpSide* sides, int rows, int b, void* dg, int64_t zoff, int64_t total,
                        float* part, hipStream_t s);
+//   block_grads_n: the same for `count` (1 .. kGradSides) sides in one launch,
+//     their blocks numbered consecutively in side order from zoff; q may be null
+hipError_t block_grads_n(int cdt, int count, const CnpSide* sides, int rows, int b, void* dg, int64_t zoff,
+                         int64_t total, float* part, hipStream_t s);
 int block_grads_splits(int dt, int rows, int blocks, int b);
 size_t block_grads_part_bytes(int dt, int rows, int blocks, int b);
 hipError_t cnp_chain_batch(int cdt, int count, const float* const* q, const int* d, int b, void* dg, float* const* dq,

@@ -211,9 +211,18 @@ class PoetxGroup:
 
     Results are bit-identical to the per-linear calls; the batch only shares
     launches between the sides.
+
+    batch_grads=True also batches the block gradients: backward_dx computes
+    only dX (poetx_linear_bwd_dx_sides) and backward_q forms every side's block
+    gradients in shared launches (poetx_block_grads_batch) before the chain
+    rule.  Their token-split sums then differ from the per-linear calls', so
+    dq matches those to fp32 rounding, not bit for bit.  Every linear's
+    backward_dx must come before backward_q, with the same T and no other use
+    of those linears in between (the operands live in their workspaces and
+    saved state).
     """
 
-    def __init__(self, layers):
+    def __init__(self, layers, batch_grads: bool = False):
         if not layers:
             raise ValueError("empty group")
         L0 = layers[0]
@@ -231,6 +240,10 @@ class PoetxGroup:
         u8 = dict(dtype=torch.uint8, device=self.device)
         self.dg = torch.empty(B.poetx_cnp_grad_bytes(blocks, self.b, self.adt), **u8)
         self.ws = torch.empty(B.poetx_cnp_batch_workspace_size(self.d, self.b, self.adt), **u8)
+        self.batch_grads = batch_grads
+        self.sides = [None] * len(self.layers)  # batch_grads: block-gradient operands from backward_dx
+        self.rows = None
+        self.gws = torch.empty(0, **u8)
 
     def build(self, stream=None):
         q = [x for l in self.layers for x in (l.q_R, l.q_P)]
@@ -246,6 +259,13 @@ class PoetxGroup:
         lay.reserve(T)
         if dX is None:
             dX = torch.empty(T, lay.m, dtype=X.dtype, device=self.device)
+        if self.batch_grads:
+            if self.rows is not None and self.rows != T:
+                raise ValueError(f"batch_grads: every linear's backward_dx needs the same T ({self.rows}), got {T}")
+            self.sides[i] = B.poetx_linear_bwd_dx_sides(lay.desc, T, lay._y_arg(Y), dZ, lay.perm_R, lay.perm_P, lay.Wt,
+                                                        lay.g_R, lay.g_P, lay.H_save, dX, lay.ws, lay.ws.numel(), stream)
+            self.rows = T
+            return dX
         B.poetx_linear_bwd_dx(lay.desc, T, lay._y_arg(Y), dZ, lay.perm_R, lay.perm_P, lay.Wt, lay.g_R, lay.g_P,
                               lay.q_R, lay.q_P, lay.H_save, dX, self.dg, self.first[i], self.blocks, lay.ws,
                               lay.ws.numel(), stream)
@@ -253,6 +273,17 @@ class PoetxGroup:
 
     def backward_q(self, dqs=None, stream=None):
         """dq of every side from the gradient state; dqs: [(dq_R, dq_P)] per linear (allocated if None)."""
+        if self.batch_grads:
+            if any(sd is None for sd in self.sides):
+                raise ValueError("batch_grads: backward_dx of every linear must come before backward_q")
+            need = B.poetx_block_grads_workspace_size(self.d, self.rows, self.b, self.adt)
+            if self.gws.numel() < need:
+                self.gws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            sides = [x for pair in self.sides for x in pair]
+            B.poetx_block_grads_batch(sides, self.rows, self.b, self.adt, self.dg, self.dg.numel(), self.gws,
+                                      self.gws.numel(), stream)
+            self.sides = [None] * len(self.layers)
+            self.rows = None
         if dqs is None:
             dqs = [(torch.empty_like(l.q_R), torch.empty_like(l.q_P)) for l in self.layers]
         q = [x for l in self.layers for x in (l.q_R, l.q_P)]

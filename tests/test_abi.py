@@ -289,3 +289,57 @@ def test_fold_and_store_statuses(L):
     assert L.poetx_store_weight(ctypes.byref(d), FAKE, 199, FAKE, FAKE, 1 << 40, None) == B.POETX_E_SHAPE
     assert L.poetx_store_weight(ctypes.byref(d), FAKE, 256, None, FAKE, 1 << 40, None) == B.POETX_E_NULL
     assert L.poetx_store_weight(ctypes.byref(d), FAKE, 256, FAKE, FAKE, 16, None) == B.POETX_E_WORKSPACE
+
+
+def test_block_grads_batch_statuses(L):
+    """Argument checks of the batched block gradients (each returns before any launch)."""
+    d = [4096, 4096, 4096, 1024, 14336, 4096]
+    b, bf = 512, B.DTYPES["bf16"]
+    blocks = sum((x + b - 1) // b for x in d)
+    # the token range is split for the whole batch; fp32 partials of S splits of every block
+    need = B.poetx_block_grads_workspace_size(d, 8192, b, bf)
+    assert need > 0 and need % (blocks * b * b * 4) == 0
+    assert B.poetx_block_grads_workspace_size(d, 8192, b, B.DTYPES["f32"]) == 0  # fp32: no token splits
+    assert B.poetx_block_grads_workspace_size(d, -1, b, bf) == 0
+    assert B.poetx_block_grads_workspace_size([], 8192, b, bf) == 0
+    dg_bytes = B.poetx_cnp_grad_bytes(blocks, b, bf)
+    sides = [B.GradSide(FAKE, x, FAKE, x, x) for x in d]
+
+    def call(sides=sides, rows=8192, dtype=bf, dg=FAKE, dg_bytes=dg_bytes, ws=FAKE, ws_bytes=need, count=None):
+        arr = (B.GradSide * len(sides))(*sides) if sides else None
+        n = len(sides) if count is None else count
+        return L.poetx_block_grads_batch(n, arr, rows, b, dtype, dg, dg_bytes, ws, ws_bytes, None)
+
+    assert call(sides=[]) == B.POETX_E_NULL
+    assert call(count=0) == B.POETX_E_SHAPE
+    assert call(count=B.POETX_MAX_SIDES + 1) == B.POETX_E_SHAPE
+    assert call(rows=-1) == B.POETX_E_SHAPE
+    assert call(dtype=B.DTYPES["i8"]) == B.POETX_E_DTYPE
+    assert call(dg=None) == B.POETX_E_NULL
+    assert call(dg_bytes=dg_bytes - 1) == B.POETX_E_WORKSPACE
+    assert call(dg=FAKE + 16) == B.POETX_E_WORKSPACE  # not 256-byte aligned
+    assert call(ws_bytes=need - 1) == B.POETX_E_WORKSPACE
+    assert call(ws=None) == B.POETX_E_WORKSPACE
+    bad = list(sides)
+    bad[2] = B.GradSide(FAKE, 4095, FAKE, 4096, 4096)  # lda < d
+    assert call(sides=bad) == B.POETX_E_SHAPE
+    bad[2] = B.GradSide(None, 4096, FAKE, 4096, 4096)
+    assert call(sides=bad) == B.POETX_E_NULL
+    bad[2] = B.GradSide(FAKE, 4096, FAKE, 4096, 0)  # d < 1
+    assert call(sides=bad) == B.POETX_E_SHAPE
+
+
+def test_bwd_dx_sides_statuses(L):
+    d = B.desc(320, 200, 64, "bf16", "bf16")
+    T = 64
+    ws = B.poetx_workspace_size(d, T, B.POETX_OP_BWD)
+    sides = (B.GradSide * 2)()
+
+    def call(sides=sides, ws_bytes=ws, H=FAKE, perm=FAKE):
+        return L.poetx_linear_bwd_dx_sides(ctypes.byref(d), T, None, FAKE, perm, FAKE, FAKE, FAKE, FAKE, H, FAKE,
+                                           sides, FAKE, ws_bytes, None)
+
+    assert call(sides=None) == B.POETX_E_NULL
+    assert call(ws_bytes=ws - 1) == B.POETX_E_WORKSPACE
+    assert call(H=None) == B.POETX_E_NULL
+    assert call(perm=None) == B.POETX_E_NULL

@@ -3,7 +3,10 @@ poetx_cnp_backward_batch): bit-identical to the per-side / per-linear calls,
 and the batched backward checked against the fp64 oracle.
 
 Sides of different lengths (partial last blocks, r = 2 .. b) share each batch,
-so the block-to-side lookup of the kernels is exercised at its boundaries."""
+so the block-to-side lookup of the kernels is exercised at its boundaries.
+The batched block gradients (poetx_linear_bwd_dx_sides + poetx_block_grads_batch)
+split the token range for the whole batch, so their dq is compared with the
+per-linear calls to fp32 rounding and with the oracle."""
 
 import numpy as np
 import pytest
@@ -11,7 +14,7 @@ import torch
 
 from orthogonal_reparameterized_cnp_amd import binding as B
 from orthogonal_reparameterized_cnp_amd.layer import PoetxGroup
-from tests.poetx_cases import assert_close, dev, host, make_layer, run_oracle
+from tests.poetx_cases import assert_close, assert_dead_slots_zero, dev, host, make_layer, run_oracle
 from workloads.gen import custom_linear_inputs
 
 pytestmark = [
@@ -129,3 +132,63 @@ def test_backward_reads_saved_input_not_x():
                        lay.H_save, dX, dq_R, dq_P, lay.ws, lay.ws.numel())
     torch.cuda.synchronize()
     assert torch.equal(dX, ref[0]) and torch.equal(dq_R, ref[1]) and torch.equal(dq_P, ref[2])
+
+
+BATCH_GRAD_CASES = [
+    # full blocks over several linears (one shared token split), ragged T, partial blocks, fp32
+    ("bf16", 512, [(4096, 1024), (4096, 4096), (14336, 4096)], 1024, False),
+    ("bf16", 512, [(1024, 1536), (600, 520)], 256, True),
+    ("bf16", 256, [(600, 520), (256, 300)], 300, True),
+    ("bf16", 256, [(700, 256)], 704, True),
+    ("f32", 32, [(96, 50), (33, 64)], 70, True),
+]
+
+
+@pytest.mark.parametrize("act,b,shapes,T,oracle", BATCH_GRAD_CASES)
+def test_group_batch_grads(act, b, shapes, T, oracle):
+    """Block gradients of every side in shared launches (poetx_block_grads_batch): dX bit-identical to the
+    per-linear calls, dq close to theirs, and within the usual bounds of the oracle.  The two differ only
+    in the fp32 order of the token-split sums of U; in bf16 the chain rule reads U rounded to bf16, where
+    such a difference can move an element by one unit (2^-8 relative), hence the bf16 bound."""
+    print(f"group batch_grads act={act} b={b} shapes={shapes} T={T}", flush=True)
+    inps = [custom_linear_inputs(m, n, b, T, act, act, 0.05, seed=7 * m + n) for m, n in shapes]
+    single = [make_layer(inp) for inp in inps]
+    grouped = [make_layer(inp) for inp in inps]
+    group = PoetxGroup(grouped, batch_grads=True)
+    group.build()
+    outs = []
+    for i, (inp, a, g) in enumerate(zip(inps, single, grouped)):
+        X, dZ = dev(inp.X, inp.act), dev(inp.dZ, inp.act)
+        a.forward(X)
+        g.forward(X)
+        dX_a, dqR_a, dqP_a = a.backward(X, dZ)
+        dX_g = group.backward_dx(i, X, dZ)
+        outs.append((dX_a, dqR_a, dqP_a, dX_g))
+    dqs = group.backward_q()
+    torch.cuda.synchronize()
+    for (dX_a, dqR_a, dqP_a, dX_g), (dqR_g, dqP_g) in zip(outs, dqs):
+        assert torch.equal(dX_a, dX_g)
+        for name, x, y in (("dq_R", dqR_g, dqR_a), ("dq_P", dqP_g, dqP_a)):
+            x, y = x.double().cpu(), y.double().cpu()
+            rel = ((x - y).norm() / max(y.norm().item(), 1e-30)).item()
+            print(f"  {name}: relative difference to the per-linear call {rel:.2e}", flush=True)
+            assert rel <= (2e-3 if act == "bf16" else 1e-5), f"{name}: {rel:.2e}"
+    for inp, (dqR_g, dqP_g) in zip(inps, dqs):
+        assert_dead_slots_zero("dq_R", dqR_g, inp.m, inp.b)
+        assert_dead_slots_zero("dq_P", dqP_g, inp.n, inp.b)
+    if oracle:
+        for inp, (_, _, _, dX_g), (dqR_g, dqP_g) in zip(inps, outs, dqs):
+            ref = run_oracle(inp)
+            assert_close("dX", host(dX_g, act), ref["dX"], act)
+            assert_close("dq_R", host(dqR_g, "f32"), ref["dq_R"], act)
+            assert_close("dq_P", host(dqP_g, "f32"), ref["dq_P"], act)
+
+
+def test_group_batch_grads_needs_every_linear():
+    inps = [custom_linear_inputs(m, n, 64, 64, "bf16", "bf16", 0.05, seed=m) for m, n in [(128, 64), (64, 128)]]
+    group = PoetxGroup([make_layer(inp) for inp in inps], batch_grads=True)
+    X, dZ = dev(inps[0].X, "bf16"), dev(inps[0].dZ, "bf16")
+    group.layers[0].forward(X)
+    group.backward_dx(0, X, dZ)
+    with pytest.raises(ValueError):
+        group.backward_q()
