@@ -163,6 +163,35 @@ PX_DEV void run_kk_sum3(unsigned char* smem, const T* x0, const T* y0, const T* 
   epi(acc);
 }
 
+// A tile stored transposed through LDS: the epilogue puts tile rows i0 .. i0 + 3
+// of tile column j (tile-local) with put(); after a barrier, flush() writes the
+// tile transposed, dst[(col0 + j) * ld + row0 + i] for j < ncols, i < nrows,
+// in row-contiguous pieces of 4 elements, instead of one 4-element piece per
+// lane in 64 different rows.  The LDS must be free (after a K loop's final
+// barrier) and hold BYTES per stage.
+template <class CC, typename T> struct TStage {
+  static constexpr int PITCH = CC::BM + 4;  // elements per staged row (one tile column); 8 / 16-byte aligned
+  static constexpr int BYTES = CC::BN * PITCH * (int)sizeof(T);
+  T* t;
+  PX_DEV explicit TStage(void* lds) : t(reinterpret_cast<T*>(lds)) {}
+  PX_DEV void put(int i0, int j, const float v[4]) const { store4<T>(t + j * PITCH + i0, v); }
+  PX_DEV void flush(T* dst, int64_t ld, int row0, int col0, int nrows, int ncols) const {
+    constexpr int Q = CC::BM / 4;  // 4-element pieces per staged row
+    using V = typename std::conditional<sizeof(T) == 2, uint2, uint4>::type;
+    const bool vec = reinterpret_cast<uintptr_t>(dst) % sizeof(V) == 0 && ld % 4 == 0 && row0 % 4 == 0;
+    for (int c = threadIdx.x; c < CC::BN * Q; c += blockDim.x) {
+      const int j = c / Q, i = (c % Q) * 4;
+      if (j >= ncols || i >= nrows) continue;
+      const T* s = t + j * PITCH + i;
+      T* d = dst + (int64_t)(col0 + j) * ld + row0 + i;
+      if (vec && i + 4 <= nrows)
+        *reinterpret_cast<V*>(d) = *reinterpret_cast<const V*>(s);
+      else
+        for (int e = 0; e < 4 && i + e < nrows; ++e) d[e] = s[e];
+    }
+  }
+};
+
 // Dense Q from the packed parameters, one 64 x 64 tile per workgroup: entries
 // above the diagonal are read along packed rows; entries below it come from
 // the mirrored tile, staged through LDS so that both reads and writes are
@@ -276,6 +305,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     float t2[CC::TM][CC::TN][16];
     load_at_acc<CC>(t2, T2 + off, b, m0, n0, max(r, 1), max(r, 1));
     const AccPos<CC> p = acc_pos<CC>();
+    const TStage<CC, T> st(smem);  // slice 1 (the transpose) leaves through LDS
 #pragma unroll
     for (int ti = 0; ti < CC::TM; ++ti)
 #pragma unroll
@@ -292,12 +322,11 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
             o[e] = (i < r && j < r) ? acc.v[ti][tj][4 * g + e] + t2[ti][tj][4 * g + e] : 0.f;
             if (i < b) g0[(int64_t)i * b + j] = from_f32<T>(o[e]);
           }
-          if (i0 + 4 <= b)
-            store4<T>(g1 + (int64_t)j * b + i0, o);
-          else
-            for (int e = 0; e < 4 && i0 + e < b; ++e) g1[(int64_t)j * b + i0 + e] = from_f32<T>(o[e]);
+          st.put(i0 - m0, j - n0, o);
         }
       }
+    __syncthreads();
+    st.flush(g1, b, m0, n0, min(CC::BM, b - m0), min(CC::BN, b - n0));
   });
 }
 
@@ -562,6 +591,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
                 [&](auto& uq, auto& qu) {
     using CC = cfg_of<decltype(uq)>;
     const AccPos<CC> p = acc_pos<CC>();
+    // W^T and (2 V1)^T leave through LDS
+    const TStage<CC, T> sw(smem), sv(smem + TStage<CC, T>::BYTES);
 #pragma unroll
     for (int ti = 0; ti < CC::TM; ++ti) {
       // one row group of U at a time keeps the epilogue's registers down
@@ -586,20 +617,15 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
             ch.Wb[x] = from_f32<T>(w[e]);
             ch.F32[x] = 2.f * uv - 2.f * v1 - 2.f * pv;
           }
-          T* wt = ch.Wtb + off + (int64_t)j * b + i0;
-          T* vt = ch.V1tb + off + (int64_t)j * b + i0;
-          if (i0 + 4 <= r) {
-            store4<T>(wt, w);
-            store4<T>(vt, v2);
-          } else {
-            for (int e = 0; e < 4 && i0 + e < r; ++e) {
-              wt[e] = from_f32<T>(w[e]);
-              vt[e] = from_f32<T>(v2[e]);
-            }
-          }
+          sw.put(i0 - m0, j - n0, w);
+          sv.put(i0 - m0, j - n0, v2);
         }
       }
     }
+    __syncthreads();
+    const int nr = min(CC::BM, r - m0), nc = min(CC::BN, r - n0);
+    sw.flush(ch.Wtb + off, b, m0, n0, nr, nc);
+    sv.flush(ch.V1tb + off, b, m0, n0, nr, nc);
   });
 }
 
@@ -703,6 +729,8 @@ hipError_t build_t(const SideTable& sd, int b, const GOut& go, void* ws, hipStre
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = allow_lds(k_cnp_square<C, T>, lds);
   if (e == hipSuccess) e = allow_lds(k_cnp_delta<C, T>, lds);
+  static_assert(TStage<C, T>::BYTES <= std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0),
+                "the transposed stage of k_cnp_delta fits the K loop's LDS");
   if (e != hipSuccess) return e;
   const unsigned t64 = cdiv(b, 64);
   k_unpack_q<T><<<dim3(t64 * t64, nb), 256, 0, s>>>(sd, b, Qb);
@@ -803,10 +831,12 @@ hipError_t chain_t(const SideTable& sd, int b, void* dg, const DqOut& out, hipSt
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = hipSuccess;
   const unsigned grid = cdiv(b, C::BN) * cdiv(b, C::BM) * NB;
-  e = allow_lds(k_cnp_grad1<C, T>, lds);
+  // the first launch's epilogue stages two transposed tiles
+  const int lds1 = std::max(lds, 2 * TStage<C, T>::BYTES);
+  e = allow_lds(k_cnp_grad1<C, T>, lds1);
   if (e == hipSuccess) e = allow_lds(k_cnp_grad2<C, T>, lds);
   if (e != hipSuccess) return e;
-  k_cnp_grad1<C, T><<<2 * grid, C::NT, lds, s>>>(sd, b, ch);
+  k_cnp_grad1<C, T><<<2 * grid, C::NT, lds1, s>>>(sd, b, ch);
   k_cnp_grad2<C, T><<<grid, C::NT, lds, s>>>(sd, b, ch);
   k_pack_dq<<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, ch.F32, out);
   return hipGetLastError();
