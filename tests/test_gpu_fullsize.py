@@ -117,3 +117,49 @@ def test_merge_full_size_int8(lin):
     code, scale = O.quantize_int8_f32(Wq)
     np.testing.assert_array_equal(lay.weight_values()[:, :n].cpu().numpy(), code)
     np.testing.assert_array_equal(lay.weight_scales()[:n].cpu().numpy(), scale)
+
+
+@pytest.mark.parametrize("wl", ["llama8b", "llama1p3b"])
+def test_layer_batched_grads_full_size(wl):
+    """The decoder layer as the benchmark runs it: the block gradients of all 14 sides in shared launches
+    (one token split for the whole batch) after the seven backwards.  dX is bit-identical to the
+    per-linear calls and dq matches theirs to the bf16 rounding of U (the per-linear results are
+    checked against the oracle above); one dq block per side of the widest linear is also checked
+    against the oracle directly."""
+    from orthogonal_reparameterized_cnp_amd.layer import PoetxGroup
+
+    W_ = WORKLOADS[wl]
+    print(f"batched block gradients {wl}, T={W_.T}", flush=True)
+    inps = [make_linear_inputs(W_, i) for i in range(len(W_.linears))]
+    lays = [make_layer(inp) for inp in inps]
+    group = PoetxGroup(lays, batch_grads=True)
+    group.build()
+    Xs = [dev(inp.X, inp.act) for inp in inps]
+    dZs = [dev(inp.dZ, inp.act) for inp in inps]
+    for lay, X in zip(lays, Xs):
+        lay.forward(X)
+    dXs = [None] * len(lays)
+    for i in reversed(range(len(lays))):
+        dXs[i] = group.backward_dx(i, Xs[i], dZs[i])
+    dqs = group.backward_q()
+    torch.cuda.synchronize()
+    for i, (inp, lay) in enumerate(zip(inps, lays)):
+        dX_a, dqR_a, dqP_a = lay.backward(Xs[i], dZs[i])
+        assert torch.equal(dX_a, dXs[i]), f"linear {i}: dX differs from the per-linear call"
+        for name, x, y in (("dq_R", dqs[i][0], dqR_a), ("dq_P", dqs[i][1], dqP_a)):
+            x, y = x.double().cpu(), y.double().cpu()
+            rel = ((x - y).norm() / max(y.norm().item(), 1e-30)).item()
+            print(f"  linear {i} {name}: relative difference to the per-linear call {rel:.2e}", flush=True)
+            assert rel <= 2e-3, f"linear {i} {name}: {rel:.2e}"
+        assert_dead_slots_zero("dq_R", dqs[i][0], inp.m, inp.b)
+        assert_dead_slots_zero("dq_P", dqs[i][1], inp.n, inp.b)
+    # the oracle on the widest linear (gate): the last block of each side
+    gi = max(range(len(inps)), key=lambda i: inps[i].m * inps[i].n)
+    inp = inps[gi]
+    W = O.to_f64(inp.W0, inp.w, inp.w_scale)
+    q_R, q_P = inp.q_R.astype(np.float64), inp.q_P.astype(np.float64)
+    bR, bP = [inp.q_R.shape[0] - 1], [inp.q_P.shape[0] - 1]
+    ref = O.block_grads(O.to_f64(inp.X, inp.act), O.to_f64(inp.dZ, inp.act), W, inp.perm_R, inp.perm_P, q_R, q_P,
+                        inp.b, bR, bP)
+    assert_close(f"dq_R[{bR[0]}]", host(dqs[gi][0], "f32")[bR[0]], ref[("R", bR[0])], inp.act)
+    assert_close(f"dq_P[{bP[0]}]", host(dqs[gi][1], "f32")[bP[0]], ref[("P", bP[0])], inp.act)
