@@ -384,6 +384,21 @@ poetx_status poetx_block_grads_batch(int32_t count, const poetx_grad_side* sides
 poetx_status poetx_cnp_backward_batch(int32_t count, const float* const* q, const int32_t* d, int32_t b, int32_t dtype,
                                       void* dg, size_t dg_bytes, float* const* dq, void* stream);
 
+/*
+ * poetx_cnp_backward_batch reading the dense Q and S = Q^2 that the
+ * poetx_cnp_build_batch call which built these sides' G left in its workspace
+ * `build_ws`, instead of forming them again (one unpacking and one of the six
+ * b x b products fewer).  The same sides in the same order, and build_ws not
+ * written since that build; the chain rule is then taken at the q the G were
+ * built from.  The result is bit-identical to poetx_cnp_backward_batch with
+ * those q.
+ *   build_ws  the build's workspace, build_ws_bytes >= poetx_cnp_batch_workspace_size
+ * Other arguments and errors as for poetx_cnp_backward_batch.
+ */
+poetx_status poetx_cnp_backward_batch_reuse(int32_t count, const float* const* q, const int32_t* d, int32_t b,
+                                            int32_t dtype, const void* build_ws, size_t build_ws_bytes, void* dg,
+                                            size_t dg_bytes, float* const* dq, void* stream);
+
 /* ---------------------------------- one SPO factor (c > 1, fully stochastic) -- */
 
 /*

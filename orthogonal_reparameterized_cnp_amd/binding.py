@@ -136,6 +136,11 @@ _SIG = {
         [ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, _P,
          ctypes.c_size_t, ctypes.POINTER(_P), _P],
     ),
+    "poetx_cnp_backward_batch_reuse": (
+        ctypes.c_int,
+        [ctypes.c_int32, ctypes.POINTER(_P), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, _P,
+         ctypes.c_size_t, _P, ctypes.c_size_t, ctypes.POINTER(_P), _P],
+    ),
     "poetx_linear_bwd_dx_sides": (
         ctypes.c_int,
         [ctypes.POINTER(LayerDesc), ctypes.c_int64] + [_P] * 9 + [ctypes.POINTER(GradSide), _P, ctypes.c_size_t, _P],
@@ -350,6 +355,12 @@ def poetx_linear_bwd_dx(dsc: LayerDesc, T: int, Y, dZ, perm_R, perm_P, Wt, g_R, 
             _stream(stream),
         )
     )
+
+
+def poetx_cnp_backward_batch_reuse(q, d, b: int, dtype: int, build_ws, build_ws_bytes: int, dg, dg_bytes: int, dq,
+                                   stream=None):
+    _check(lib().poetx_cnp_backward_batch_reuse(len(d), _ptr_array(q), _i32_array(d), b, dtype, _ptr(build_ws),
+                                                build_ws_bytes, _ptr(dg), dg_bytes, _ptr_array(dq), _stream(stream)))
 
 
 def poetx_linear_bwd_dx_sides(dsc: LayerDesc, T: int, Y, dZ, perm_R, perm_P, Wt, g_R, g_P, H_save, dX, ws,

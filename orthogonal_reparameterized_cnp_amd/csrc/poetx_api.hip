@@ -715,6 +715,30 @@ poetx_status poetx_cnp_backward_batch(int32_t count, const float* const* q, cons
   return POETX_OK;
 }
 
+poetx_status poetx_cnp_backward_batch_reuse(int32_t count, const float* const* q, const int32_t* d, int32_t b,
+                                            int32_t dtype, const void* build_ws, size_t build_ws_bytes, void* dg,
+                                            size_t dg_bytes, float* const* dq, void* stream) {
+  if (!q || !dq || !dg || !build_ws) return fail(POETX_E_NULL, "q, dq, dg and build_ws must be non-NULL");
+  int64_t blocks = 0;
+  poetx_status st = check_sides(count, d, b, dtype, &blocks);
+  if (st != POETX_OK) return st;
+  double flops = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!q[i] || !dq[i]) return fail(POETX_E_NULL, "q[i] and dq[i] must be non-NULL");
+    flops += 12 * sum_r3(d[i], b);
+  }
+  if (dg_bytes < cnp_grad_bytes(dtype, blocks, b))
+    return fail(POETX_E_WORKSPACE, "dg smaller than poetx_cnp_grad_bytes of the sides' block count");
+  if (reinterpret_cast<uintptr_t>(dg) % 256) return fail(POETX_E_WORKSPACE, "dg must be 256-byte aligned");
+  if (build_ws_bytes < cnp_build_ws_bytes(dtype, blocks, b))
+    return fail(POETX_E_WORKSPACE, "build_ws smaller than poetx_cnp_batch_workspace_size of the sides");
+  if (reinterpret_cast<uintptr_t>(build_ws) % 256) return fail(POETX_E_WORKSPACE, "build_ws must be 256-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  PX_TIMED(POETX_KC_CNP, flops, cnp_grad_bytes(dtype, blocks, b),
+           cnp_chain_batch(dtype, count, q, d, b, dg, dq, s, build_ws));
+  return POETX_OK;
+}
+
 poetx_status poetx_merge_reinit(const poetx_layer_desc* desc, void* Wt, int32_t* perm_R, int32_t* perm_P,
                                 const void* g_R, const void* g_P, float* q_R, float* q_P, uint64_t seed_R,
                                 uint64_t seed_P, void* ws, size_t ws_bytes, void* stream) {

@@ -560,11 +560,11 @@ __global__ __launch_bounds__(256) void k_block_grads_reduce(SideTable sd, int b,
 // Q Q^T = -S and writes S.
 template <class C, typename T>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_grad1(SideTable sd, int b,
-                                                                                            Chain<T> ch) {
+                                                                                            Chain<T> ch, int kinds) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM, tiles = tm * tn;
-  // units: tile fastest, then the kind of workgroup, then the block
-  const int u = xcd_unit(blockIdx.x, gridDim.x), z = u / (2 * tiles), kind = u / tiles % 2;
+  // units: tile fastest, then the kind of workgroup (kinds = 1: S is given, only the first kind), then the block
+  const int u = xcd_unit(blockIdx.x, gridDim.x), z = u / (kinds * tiles), kind = kinds == 2 ? u / tiles % 2 : 0;
   const float* qk;
   int r;
   sd.at(z, b, qk, r);
@@ -822,12 +822,21 @@ hipError_t grads_t(int count, const pxk::CnpSide* sides, int rows, int b, void* 
 }
 
 template <typename T>
-hipError_t chain_t(const SideTable& sd, int b, void* dg, const DqOut& out, hipStream_t s) {
+hipError_t chain_t(const SideTable& sd, int b, void* dg, const DqOut& out, const void* build, hipStream_t s) {
   using C = typename CnpTile<T>::C;
   const int NB = sd.first[sd.count];
-  Chain<T> ch = carve<T>(dg, (size_t)NB * b * b);
+  const size_t E = (size_t)NB * b * b;
+  Chain<T> ch = carve<T>(dg, E);
   const unsigned t64 = cdiv(b, 64);
-  k_unpack_q<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb));
+  if (build) {
+    // the dense Q and S = Q Q that the build left in its workspace (the same kernels on the same
+    // operands form them here otherwise: the results are bit-identical)
+    const char* w = reinterpret_cast<const char*>(build);
+    ch.Qb = reinterpret_cast<const T*>(w);
+    ch.Sb = const_cast<T*>(reinterpret_cast<const T*>(w + 2 * al256(E * sizeof(T))));
+  } else {
+    k_unpack_q<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb));
+  }
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = hipSuccess;
   const unsigned grid = cdiv(b, C::BN) * cdiv(b, C::BM) * NB;
@@ -836,7 +845,8 @@ hipError_t chain_t(const SideTable& sd, int b, void* dg, const DqOut& out, hipSt
   e = allow_lds(k_cnp_grad1<C, T>, lds1);
   if (e == hipSuccess) e = allow_lds(k_cnp_grad2<C, T>, lds);
   if (e != hipSuccess) return e;
-  k_cnp_grad1<C, T><<<2 * grid, C::NT, lds1, s>>>(sd, b, ch);
+  const int kinds = build ? 1 : 2;
+  k_cnp_grad1<C, T><<<kinds * grid, C::NT, lds1, s>>>(sd, b, ch, kinds);
   k_cnp_grad2<C, T><<<grid, C::NT, lds, s>>>(sd, b, ch);
   k_pack_dq<<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, ch.F32, out);
   return hipGetLastError();
@@ -908,13 +918,13 @@ hipError_t block_grads_n(int cdt, int count, const CnpSide* sides, int rows, int
 }
 
 hipError_t cnp_chain_batch(int cdt, int count, const float* const* q, const int* d, int b, void* dg, float* const* dq,
-                           hipStream_t s) {
+                           hipStream_t s, const void* build) {
   if (count < 1 || count > kMaxSides) return hipErrorInvalidValue;
   const SideTable sd = make_table(count, q, d, b);
   DqOut out{};
   for (int i = 0; i < count; ++i) out.dq[i] = dq[i];
-  if (cdt == BF16) return chain_t<bf16_t>(sd, b, dg, out, s);
-  return chain_t<float>(sd, b, dg, out, s);
+  if (cdt == BF16) return chain_t<bf16_t>(sd, b, dg, out, build, s);
+  return chain_t<float>(sd, b, dg, out, build, s);
 }
 
 }  // namespace pxk

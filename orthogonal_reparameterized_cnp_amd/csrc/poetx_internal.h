@@ -93,8 +93,10 @@ hipError_t block_grads_n(int cdt, int count, const CnpSide* sides, int rows, int
                          int64_t total, float* part, hipStream_t s);
 int block_grads_splits(int dt, int rows, int blocks, int b);
 size_t block_grads_part_bytes(int dt, int rows, int blocks, int b);
+//   build: null, or the workspace of the cnp_build_batch call for the same sides (its dense Q and
+//     S = Q Q are read instead of formed again)
 hipError_t cnp_chain_batch(int cdt, int count, const float* const* q, const int* d, int b, void* dg, float* const* dq,
-                           hipStream_t s);
+                           hipStream_t s, const void* build = nullptr);
 size_t cnp_grad_bytes(int dt, int64_t blocks, int b);
 
 // Merge helpers (fp32 MFMA).

@@ -343,3 +343,23 @@ def test_bwd_dx_sides_statuses(L):
     assert call(ws_bytes=ws - 1) == B.POETX_E_WORKSPACE
     assert call(H=None) == B.POETX_E_NULL
     assert call(perm=None) == B.POETX_E_NULL
+
+
+def test_cnp_backward_reuse_statuses(L):
+    d, b, bf = [320, 200], 64, B.DTYPES["bf16"]
+    blocks = sum((x + b - 1) // b for x in d)
+    dg_bytes = B.poetx_cnp_grad_bytes(blocks, b, bf)
+    ws_bytes = B.poetx_cnp_batch_workspace_size(d, b, bf)
+    q = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    dq = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    dd = (ctypes.c_int32 * 2)(*d)
+
+    def call(build=FAKE, build_bytes=ws_bytes, dg=FAKE, dgb=dg_bytes):
+        return L.poetx_cnp_backward_batch_reuse(2, q, dd, b, bf, build, build_bytes, dg, dgb, dq, None)
+
+    assert call(build=None) == B.POETX_E_NULL
+    assert call(build_bytes=ws_bytes - 1) == B.POETX_E_WORKSPACE
+    assert call(build=FAKE + 16) == B.POETX_E_WORKSPACE
+    assert call(dgb=dg_bytes - 1) == B.POETX_E_WORKSPACE
+    assert L.poetx_cnp_backward_batch_reuse(0, q, dd, b, bf, FAKE, ws_bytes, FAKE, dg_bytes, dq, None) == \
+        B.POETX_E_SHAPE

@@ -1,6 +1,8 @@
 """Batched CNP entry points (poetx_cnp_build_batch, poetx_linear_bwd_dx +
-poetx_cnp_backward_batch): bit-identical to the per-side / per-linear calls,
-and the batched backward checked against the fp64 oracle.
+poetx_cnp_backward_batch, and its form poetx_cnp_backward_batch_reuse that
+reads the build's dense Q and S, which the group uses after its build):
+bit-identical to the per-side / per-linear calls, and the batched backward
+checked against the fp64 oracle.
 
 Sides of different lengths (partial last blocks, r = 2 .. b) share each batch,
 so the block-to-side lookup of the kernels is exercised at its boundaries.
