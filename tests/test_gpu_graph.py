@@ -68,8 +68,11 @@ def test_layer_step_replays_in_a_graph(m, n, b, T, act, w, mode):
                 f"replay {k}: {name} differs from the eager result"
 
 
-def test_group_step_replays_in_a_graph():
-    """Several linears with the batched CNP calls (the benchmark's step shape, small)."""
+@pytest.mark.parametrize("batch_grads", [False, True])
+def test_group_step_replays_in_a_graph(batch_grads):
+    """Several linears with the batched CNP calls (the benchmark's step shape, small), with the block
+    gradients per linear or in one batch after the backwards (the eager step before the capture sizes
+    the batch's workspace, so the capture allocates nothing)."""
     shapes = [(256, 256), (256, 128), (512, 256)]
     b, T, act = 128, 128, "bf16"
     lays, Xs, dZs = [], [], []
@@ -78,7 +81,7 @@ def test_group_step_replays_in_a_graph():
         lays.append(make_layer(inp))
         Xs.append(dev(inp.X, act))
         dZs.append(dev(inp.dZ, act))
-    group = PoetxGroup(lays)
+    group = PoetxGroup(lays, batch_grads=batch_grads)
     Ys = [torch.empty(T, l.n, dtype=torch.bfloat16, device="cuda") for l in lays]
     dXs = [torch.empty(T, l.m, dtype=torch.bfloat16, device="cuda") for l in lays]
     dqs = [(torch.empty_like(l.q_R), torch.empty_like(l.q_P)) for l in lays]
