@@ -241,21 +241,23 @@ class PoetxGroup:
         self.dg = torch.empty(B.poetx_cnp_grad_bytes(blocks, self.b, self.adt), **u8)
         self.ws = torch.empty(B.poetx_cnp_batch_workspace_size(self.d, self.b, self.adt), **u8)
         self.batch_grads = batch_grads
-        self.built = False  # the build workspace holds the dense Q and S of every side (build())
+        self.built = False  # build() ran since the last backward_q: its workspace holds every side's dense Q and S
         self.sides = [None] * len(self.layers)  # batch_grads: block-gradient operands from backward_dx
         self.rows = None
         self.gws = torch.empty(0, **u8)
 
     def build(self, stream=None):
-        """Every side's G in one batch; backward_q then reuses the dense Q and S it leaves in the
-        group's workspace (the sides' q must not change in between)."""
+        """Every side's G in one batch.  The next backward_q reuses the dense Q and S this leaves in the
+        group's workspace: the chain rule is then taken at the q these G were built from, as the forward
+        used them.  A backward_q without a group build before it forms Q and S from the current q."""
         q = [x for l in self.layers for x in (l.q_R, l.q_P)]
         g = [x for l in self.layers for x in (l.g_R, l.g_P)]
         B.poetx_cnp_build_batch(q, self.d, self.b, self.adt, g, self.ws, self.ws.numel(), stream)
         self.built = True
 
     def backward_dx(self, i: int, X: torch.Tensor, dZ: torch.Tensor, dX=None, stream=None, Y=None) -> torch.Tensor:
-        """dX of linear i; its block gradients go to the group's gradient state (Y: as PoetxLinear.backward)."""
+        """dX of linear i; its block gradients go to the group's gradient state, or with batch_grads wait
+        for backward_q (Y: as PoetxLinear.backward)."""
         lay = self.layers[i]
         T = X.shape[0]
         lay._y_arg(Y)
@@ -296,6 +298,7 @@ class PoetxGroup:
             # the chain rule at the q the forward's G were built from, reading the build's dense Q and S
             B.poetx_cnp_backward_batch_reuse(q, self.d, self.b, self.adt, self.ws, self.ws.numel(), self.dg,
                                              self.dg.numel(), dq, stream)
+            self.built = False
         else:
             B.poetx_cnp_backward_batch(q, self.d, self.b, self.adt, self.dg, self.dg.numel(), dq, stream)
         return dqs

@@ -194,3 +194,35 @@ def test_group_batch_grads_needs_every_linear():
     group.backward_dx(0, X, dZ)
     with pytest.raises(ValueError):
         group.backward_q()
+
+
+def test_group_chain_rule_with_and_without_the_group_build():
+    """backward_q reads the dense Q and S of the group build that came before it, once; without a group
+    build (the G built per linear) it forms them itself.  Both give the per-linear dq bit for bit."""
+    shapes, b, T = [(600, 520), (256, 300)], 256, 300
+    inps = [custom_linear_inputs(m, n, b, T, "bf16", "bf16", 0.05, seed=5 * m + n) for m, n in shapes]
+    single = [make_layer(inp) for inp in inps]
+    grouped = [make_layer(inp) for inp in inps]  # each built per linear
+    group = PoetxGroup(grouped)
+    refs = []
+    for inp, a in zip(inps, single):
+        X, dZ = dev(inp.X, "bf16"), dev(inp.dZ, "bf16")
+        a.forward(X)
+        refs.append(a.backward(X, dZ)[1:])
+
+    def step():
+        for i, (inp, g) in enumerate(zip(inps, grouped)):
+            X, dZ = dev(inp.X, "bf16"), dev(inp.dZ, "bf16")
+            g.forward(X)
+            group.backward_dx(i, X, dZ)
+        return group.backward_q()
+
+    for use_group_build in (False, True, False):
+        if use_group_build:
+            group.build()
+        assert group.built == use_group_build
+        dqs = step()
+        torch.cuda.synchronize()
+        assert not group.built  # a group build serves one backward_q
+        for (dqR, dqP), (rR, rP) in zip(dqs, refs):
+            assert torch.equal(dqR, rR) and torch.equal(dqP, rP), f"group build {use_group_build}"
