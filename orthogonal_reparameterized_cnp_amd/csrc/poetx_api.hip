@@ -150,6 +150,7 @@ size_t saved_xt_offset(const poetx_layer_desc* d, int64_t T) {
 
 struct FwdWs {
   void *A, *Zt, *H;  // H: Xmem and Xout (Xfast writes it to the saved state)
+  void* Wb;          // int8 weights: W~^T widened to bf16
 };
 template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
   const size_t es = dt_size(d->act_dtype);
@@ -157,11 +158,13 @@ template <class P> FwdWs plan_fwd(P& p, const poetx_layer_desc* d, int64_t T) {
   w.A = p.template take<char>(T * lead(d->m) * es);
   w.Zt = p.template take<char>(T * lead(d->n) * es);
   w.H = saves_h(d) ? nullptr : p.template take<char>(T * lead(d->n) * es);
+  // int8 weights: the transposed codes widened to bf16 for the W~ contraction
+  w.Wb = d->w_dtype == POETX_I8 ? p.template take<char>((size_t)d->n * lead(d->m) * 2) : nullptr;
   return w;
 }
 
 struct BwdWs {
-  void *dZt, *dH, *dA, *dXt, *cnp;
+  void *dZt, *dH, *dA, *dXt, *cnp, *Wb;
   void* Hr;  // Xout: H taken back from the output
   float* part;
 };
@@ -176,6 +179,10 @@ template <class P> BwdWs plan_bwd(P& p, const poetx_layer_desc* d, int64_t T) {
   w.part = p.template take<float>(
       block_grads_part_bytes(d->act_dtype, (int)T, nblocks(d->m, d->b) + nblocks(d->n, d->b), d->b));
   w.Hr = d->mode == POETX_XOUT ? p.template take<char>(T * lead(d->n) * es) : nullptr;
+  // int8 weights: the codes widened to bf16 for the W~^T contraction (and transposed for the Xmem recompute)
+  w.Wb = d->w_dtype == POETX_I8
+             ? p.template take<char>(std::max((size_t)d->m * lead(d->n), (size_t)d->n * lead(d->m)) * 2)
+             : nullptr;
   return w;
 }
 
@@ -430,7 +437,7 @@ namespace {
 // product and its W~ contraction, also used by the Xmem backward to recompute
 // H (same kernels on the same inputs, so the same bits).
 poetx_status xt_to_h(const poetx_layer_desc* desc, int64_t T, const void* Xt, const void* Wt, const void* g_R, void* A,
-                     void* H, hipStream_t s) {
+                     void* H, void* Wb, hipStream_t s) {
   const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, wt = desc->w_dtype;
   const int rows = (int)T;
   const int64_t ldm = lead(m), ldn = lead(n);
@@ -442,11 +449,17 @@ poetx_status xt_to_h(const poetx_layer_desc* desc, int64_t T, const void* Xt, co
   // A = Xt Diag(G_R)
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
            apply(at, at, Xt, ldm, rows, m, b, at, gR1, nullptr, at, A, ldm, s));
-  // H = A W~ (int8: codes times the column scale); bf16 weights are read from the W~^T copy
+  // H = A W~ (int8: codes times the column scale); bf16 weights are read from the W~^T copy, int8 codes
+  // from their transpose widened to bf16 in the workspace (exact), so both take the same loop
   if (has_weight_t(desc)) {
     const void* Wtt = reinterpret_cast<const char*>(Wt) + weight_t_offset(desc);
     PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
              gemm(at, at, A, ldm, wt, Wtt, ldm, false, rows, n, m, nullptr, at, H, ldn, s));
+  } else if (wt == POETX_I8 && at == POETX_BF16 && Wb) {
+    PX_TIMED(POETX_KC_GEMM, 0, 3.0 * m * n,
+             widen_i8(reinterpret_cast<const int8_t*>(Wt), lead(n), m, n, true, reinterpret_cast<uint16_t*>(Wb), ldm, s));
+    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + 2.0 * m * n + es * rows * n,
+             gemm(at, at, A, ldm, POETX_BF16, Wb, ldm, false, rows, n, m, scale_t, at, H, ldn, s));
   } else {
     PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
              gemm(at, at, A, ldm, wt, Wt, lead(n), true, rows, n, m, scale_t, at, H, ldn, s));
@@ -485,7 +498,7 @@ poetx_status poetx_linear_fwd(const poetx_layer_desc* desc, int64_t T, const voi
   PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, permute(at, X, m, nullptr, perm_R, Xt, ldm, rows, m, m, s));
   // A = Xt Diag(G_R), H = A W~: H saved (Xfast) or kept in the workspace (Xmem)
   void* H = saves_h(desc) ? H_save : w.H;
-  st = xt_to_h(desc, T, Xt, Wt, g_R, w.A, H, s);
+  st = xt_to_h(desc, T, Xt, Wt, g_R, w.A, H, w.Wb, s);
   if (st != POETX_OK) return st;
   // Zt = H Diag(G_P)
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
@@ -519,9 +532,17 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* Y,
   // dH = dZt Diag(G_P)^T (int8: times the column scale, ready for the code contraction)
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
            apply(at, at, w.dZt, ldn, rows, n, b, at, g_P, scale_t, at, w.dH, ldn, s));
-  // dA = dH W~^T
-  PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * n + wes * m * n + es * rows * m,
-           gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
+  // dA = dH W~^T (int8: the codes widened to bf16 in the workspace first, exact)
+  if (wt == POETX_I8 && at == POETX_BF16 && w.Wb) {
+    PX_TIMED(POETX_KC_GEMM, 0, 3.0 * m * n,
+             widen_i8(reinterpret_cast<const int8_t*>(Wt), lead(n), m, n, false, reinterpret_cast<uint16_t*>(w.Wb), ldn,
+                      s));
+    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * n + 2.0 * m * n + es * rows * m,
+             gemm(at, at, w.dH, ldn, POETX_BF16, w.Wb, ldn, false, rows, m, n, nullptr, at, w.dA, ldm, s));
+  } else {
+    PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * n + wes * m * n + es * rows * m,
+             gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
+  }
   // block gradients of both sides over all tokens: dG_R = Xt^T dA, dG_P = H^T dZt, with Xt and H
   // from the forward's saved state.  Xmem recomputes H from Xt, into the buffers that dH (consumed
   // by the contraction above) and dXt (written below) occupy.  Xout takes H back from the output:
@@ -529,7 +550,7 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* Y,
   const void* Xt = reinterpret_cast<const char*>(H_save) + saved_xt_offset(desc, T);
   const void* H = H_save;
   if (desc->mode == POETX_XMEM) {
-    const poetx_status st = xt_to_h(desc, T, Xt, Wt, g_R, w.dXt, w.dH, s);
+    const poetx_status st = xt_to_h(desc, T, Xt, Wt, g_R, w.dXt, w.dH, w.Wb, s);
     if (st != POETX_OK) return st;
     H = w.dH;
   } else if (desc->mode == POETX_XOUT) {

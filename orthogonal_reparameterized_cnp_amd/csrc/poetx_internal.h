@@ -27,6 +27,10 @@ hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap,
 hipError_t scatter(int dt, const void* in, int64_t ld_in, const int32_t* perm, void* out, int64_t ld_out, int rows,
                    int d, hipStream_t s);
 // dst[c][r] = src[r][c] for r < rows, c < cols; dst[c][r] = 0 for rows <= r < ld_dst
+// int8 codes [rows][cols] (pitch ld_src) widened to bf16: dst[r][c], or with
+// trans dst[c][r] (dst columns [rows, ld_dst) zero); exact.
+hipError_t widen_i8(const int8_t* src, int64_t ld_src, int rows, int cols, bool trans, uint16_t* dst, int64_t ld_dst,
+                    hipStream_t s);
 hipError_t transpose(int dt, const void* src, int64_t ld_src, int rows, int cols, void* dst, int64_t ld_dst,
                      hipStream_t s);
 // dst[t][idx[i]] = src[t][i] for t < rows, i < b (idx values clamped into [0, d))

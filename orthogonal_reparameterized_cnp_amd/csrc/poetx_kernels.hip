@@ -548,6 +548,52 @@ __global__ __launch_bounds__(256) void k_transpose(const U* __restrict__ src, in
   }
 }
 
+// int8 codes widened to bf16 (exact: |code| <= 128 needs 8 significant bits),
+// so that the int8 contractions take the bf16 direct-to-LDS loop.  Plain:
+// dst[r][c] = src[r][c], 16 codes per thread and step; transposed: dst[c][r] =
+// src[r][c] through a 64 x 64 LDS tile (as k_transpose), dst columns r in
+// [rows, ld_dst) zero-filled.
+__global__ __launch_bounds__(256) void k_widen_i8(const int8_t* __restrict__ src, int64_t ld_src, int rows, int cols,
+                                                  bf16_t* __restrict__ dst, int64_t ld_dst) {
+  const int per_row = (cols + 15) / 16;
+  const int64_t total = (int64_t)rows * per_row;
+  for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < total; u += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(u / per_row), c0 = (int)(u % per_row) * 16;
+    const int8_t* a = src + (int64_t)r * ld_src + c0;
+    bf16_t* o = dst + (int64_t)r * ld_dst + c0;
+    if (c0 + 16 <= cols && reinterpret_cast<uintptr_t>(a) % 16 == 0 && reinterpret_cast<uintptr_t>(o) % 16 == 0) {
+      const int4 v = *reinterpret_cast<const int4*>(a);
+      const int8_t* b8 = reinterpret_cast<const int8_t*>(&v);
+      uint4 w[2];
+      uint32_t* wp = reinterpret_cast<uint32_t*>(w);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) wp[k] = f2bf2((float)b8[2 * k], (float)b8[2 * k + 1]);
+      reinterpret_cast<uint4*>(o)[0] = w[0];
+      reinterpret_cast<uint4*>(o)[1] = w[1];
+    } else {
+      for (int e = 0; e < 16 && c0 + e < cols; ++e) o[e] = f2bf((float)a[e]);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_widen_i8_t(const int8_t* __restrict__ src, int64_t ld_src, int rows, int cols,
+                                                    bf16_t* __restrict__ dst, int64_t ld_dst) {
+  __shared__ float t[64][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int x = threadIdx.x & 63, y = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int r = r0 + y + 4 * k, c = c0 + x;
+    t[y + 4 * k][x] = (r < rows && c < cols) ? (float)src[(int64_t)r * ld_src + c] : 0.f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int c = c0 + y + 4 * k, r = r0 + x;
+    if (c < cols && r < ld_dst) dst[(int64_t)c * ld_dst + r] = f2bf(t[x][y + 4 * k]);
+  }
+}
+
 template <typename E>
 __global__ __launch_bounds__(256) void k_permute_direct(const E* __restrict__ in, int64_t ld_in,
                                                         const int32_t* __restrict__ rowmap,
@@ -898,6 +944,22 @@ hipError_t replace_cols(int dt, const void* in, int64_t ld_in, const void* src, 
   if (dt == F32) return go(float{});
   if (dt == BF16) return go(bf16_t{});
   return go(int8_t{});
+}
+
+hipError_t widen_i8(const int8_t* src, int64_t ld_src, int rows, int cols, bool trans, bf16_t* dst, int64_t ld_dst,
+                    hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  if (trans) {
+    if (ld_dst < rows) return hipErrorInvalidValue;
+    const dim3 grid(cdiv(ld_dst, 64), cdiv(cols, 64));
+    if (grid.y > 65535) return hipErrorInvalidValue;
+    k_widen_i8_t<<<grid, 256, 0, s>>>(src, ld_src, rows, cols, dst, ld_dst);
+  } else {
+    if (ld_dst < cols) return hipErrorInvalidValue;
+    const int64_t units = (int64_t)rows * cdiv(cols, 16);
+    k_widen_i8<<<(unsigned)std::min<int64_t>(cdiv(units, 256), 8192), 256, 0, s>>>(src, ld_src, rows, cols, dst, ld_dst);
+  }
+  return hipGetLastError();
 }
 
 hipError_t transpose(int dt, const void* src, int64_t ld_src, int rows, int cols, void* dst, int64_t ld_dst,
