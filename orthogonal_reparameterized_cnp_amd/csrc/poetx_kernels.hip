@@ -466,34 +466,93 @@ __global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_
 // ============================================================================
 // permutations
 // ============================================================================
+// Rows of a caller's tensor need not start on a 16-byte boundary (a bf16 row
+// of odd width puts every other row 2 bytes off).  A staged row therefore
+// goes in three parts: the elements before the row's first 16-byte boundary,
+// a 16-byte body, and the rest.  Its LDS copy is shifted by lds_shift() so
+// that the body lands on 16-byte LDS addresses as well; a row pitch of
+// stage_pitch(d) elements leaves room for any shift.
+
+// Elements of p before its first 16-byte boundary, capped at d (all d when p
+// is not even aligned to its element).
+template <typename E>
+__device__ inline int lead16(const E* p, int d) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  if (a % sizeof(E)) return d;
+  return min((int)((16 - a % 16) % 16 / sizeof(E)), d);
+}
+
+// Shift of a staged row whose global row leads with h elements: the LDS
+// element h then sits on a 16-byte boundary.
+template <typename E>
+__device__ inline int lds_shift(int h) {
+  constexpr int V = 16 / sizeof(E);
+  return (V - h % V) % V;
+}
+
+// Staged row pitch in elements: d plus room for the largest shift, rounded up
+// to 16 bytes.
+inline int64_t stage_pitch(int64_t d, size_t es) {
+  const int64_t v = 16 / (int64_t)es;
+  return (d + 2 * v - 2) / v * v;
+}
+
+// dst[0, d) = row[0, d) by the whole workgroup; h = lead16(row, d), and
+// dst + h is 16-byte aligned.
+template <typename E>
+__device__ inline void row_to_lds(const E* __restrict__ row, E* dst, int d, int h) {
+  constexpr int V = 16 / sizeof(E);
+  const int nb = (d - h) / V, t0 = h + nb * V;
+  const uint4* s = reinterpret_cast<const uint4*>(row + h);
+  uint4* o = reinterpret_cast<uint4*>(dst + h);
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) o[i] = s[i];
+  for (int i = threadIdx.x; i < h + d - t0; i += blockDim.x) {
+    const int e = i < h ? i : t0 + i - h;
+    dst[e] = row[e];
+  }
+}
+
+// row[0, d) = src[0, d) by the whole workgroup; h = lead16(row, d), and
+// src + h is 16-byte aligned.
+template <typename E>
+__device__ inline void lds_to_row(const E* src, E* __restrict__ row, int d, int h) {
+  constexpr int V = 16 / sizeof(E);
+  const int nb = (d - h) / V, t0 = h + nb * V;
+  const uint4* s = reinterpret_cast<const uint4*>(src + h);
+  uint4* o = reinterpret_cast<uint4*>(row + h);
+  for (int i = threadIdx.x; i < nb; i += blockDim.x) o[i] = s[i];
+  for (int i = threadIdx.x; i < h + d - t0; i += blockDim.x) {
+    const int e = i < h ? i : t0 + i - h;
+    row[e] = src[e];
+  }
+}
+
 // Row-staged gather: the workgroup copies whole source rows into LDS with
-// 16-byte coalesced loads, then writes each output row with 16-byte stores,
-// every lane gathering its 16 bytes from LDS at the permuted positions.
-// Indices are clamped into range so that a malformed permutation cannot
-// address outside the staged rows.
+// 16-byte coalesced loads (any row alignment, see row_to_lds), then writes
+// each output row with 16-byte stores, every lane gathering its 16 bytes from
+// LDS at the permuted positions.  Indices are clamped into range so that a
+// malformed permutation cannot address outside the staged rows.  pitch =
+// stage_pitch(d_in).
 template <typename E>
 __global__ __launch_bounds__(256) void k_permute_lds(const E* __restrict__ in, int64_t ld_in,
                                                      const int32_t* __restrict__ rowmap,
                                                      const int32_t* __restrict__ colmap, E* __restrict__ out,
-                                                     int64_t ld_out, int rows, int d_in, int d_out, int rpw) {
+                                                     int64_t ld_out, int rows, int d_in, int d_out, int rpw,
+                                                     int pitch) {
   extern __shared__ __align__(16) unsigned char smem[];
   E* buf = reinterpret_cast<E*>(smem);
   constexpr int V = 16 / sizeof(E);
-  const int pitch = (d_in + V - 1) / V * V;
   const int t0 = blockIdx.x * rpw;
   const int nr = min(rpw, rows - t0);
-  const bool vin = (reinterpret_cast<uintptr_t>(in) % 16 == 0) && (ld_in % V == 0) && (d_in % V == 0);
-  for (int rr = 0; rr < nr; ++rr) {
+  auto src_row = [&](int rr) {
     int src = t0 + rr;
     if (rowmap) src = min(max(rowmap[src], 0), rows - 1);
-    const E* row = in + (int64_t)src * ld_in;
-    E* dst = buf + rr * pitch;
-    if (vin) {
-      for (int i = threadIdx.x; i < d_in / V; i += blockDim.x)
-        reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(row)[i];
-    } else {
-      for (int i = threadIdx.x; i < d_in; i += blockDim.x) dst[i] = row[i];
-    }
+    return in + (int64_t)src * ld_in;
+  };
+  for (int rr = 0; rr < nr; ++rr) {
+    const E* row = src_row(rr);
+    const int h = lead16(row, d_in);
+    row_to_lds(row, buf + rr * pitch + lds_shift<E>(h), d_in, h);
   }
   __syncthreads();
   const bool vout = (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (ld_out % V == 0) &&
@@ -501,7 +560,7 @@ __global__ __launch_bounds__(256) void k_permute_lds(const E* __restrict__ in, i
   const int nchunk = (d_out + V - 1) / V;
   for (int rr = 0; rr < nr; ++rr) {
     E* o = out + (int64_t)(t0 + rr) * ld_out;
-    const E* srow = buf + rr * pitch;
+    const E* srow = buf + rr * pitch + lds_shift<E>(lead16(src_row(rr), d_in));
     for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
       const int i0 = c * V;
       if (vout && i0 + V <= d_out) {
@@ -611,16 +670,16 @@ __global__ __launch_bounds__(256) void k_permute_direct(const E* __restrict__ in
 // Row-staged scatter, out[t][perm[i]] = in[t][i]: each source row is read with
 // 16-byte coalesced loads (the permutation as 16-byte index vectors) and
 // written into LDS at the permuted positions; the staged rows then leave with
-// 16-byte stores.  Indices are clamped into [0, d): a malformed permutation
-// leaves some outputs undefined but cannot address outside the staged rows.
+// 16-byte stores (any output row alignment, see lds_to_row).  Indices are
+// clamped into [0, d): a malformed permutation leaves some outputs undefined
+// but cannot address outside the staged rows.  pitch = stage_pitch(d).
 template <typename E>
 __global__ __launch_bounds__(256) void k_scatter_lds(const E* __restrict__ in, int64_t ld_in,
                                                      const int32_t* __restrict__ perm, E* __restrict__ out,
-                                                     int64_t ld_out, int rows, int d, int rpw) {
+                                                     int64_t ld_out, int rows, int d, int rpw, int pitch) {
   extern __shared__ __align__(16) unsigned char smem[];
   E* buf = reinterpret_cast<E*>(smem);
   constexpr int V = 16 / sizeof(E);
-  const int pitch = (d + V - 1) / V * V;
   const int t0 = blockIdx.x * rpw;
   const int nr = min(rpw, rows - t0);
   const int dv = d / V;
@@ -628,7 +687,7 @@ __global__ __launch_bounds__(256) void k_scatter_lds(const E* __restrict__ in, i
                    (reinterpret_cast<uintptr_t>(perm) % 16 == 0);
   for (int rr = 0; rr < nr; ++rr) {
     const E* row = in + (int64_t)(t0 + rr) * ld_in;
-    E* dst = buf + rr * pitch;
+    E* dst = buf + rr * pitch + lds_shift<E>(lead16(out + (int64_t)(t0 + rr) * ld_out, d));
     int tail = 0;
     if (vin) {
       for (int c = threadIdx.x; c < dv; c += blockDim.x) {
@@ -649,17 +708,10 @@ __global__ __launch_bounds__(256) void k_scatter_lds(const E* __restrict__ in, i
     for (int i = tail + threadIdx.x; i < d; i += blockDim.x) dst[min(max(perm[i], 0), d - 1)] = row[i];
   }
   __syncthreads();
-  const bool vout = (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (ld_out % V == 0);
   for (int rr = 0; rr < nr; ++rr) {
     E* o = out + (int64_t)(t0 + rr) * ld_out;
-    const E* srow = buf + rr * pitch;
-    int tail = 0;
-    if (vout) {
-      for (int c = threadIdx.x; c < dv; c += blockDim.x)
-        reinterpret_cast<uint4*>(o)[c] = reinterpret_cast<const uint4*>(srow)[c];
-      tail = dv * V;
-    }
-    for (int i = tail + threadIdx.x; i < d; i += blockDim.x) o[i] = srow[i];
+    const int h = lead16(o, d);
+    lds_to_row(buf + rr * pitch + lds_shift<E>(h), o, d, h);
   }
 }
 
@@ -667,48 +719,40 @@ __global__ __launch_bounds__(256) void k_scatter_lds(const E* __restrict__ in, i
 // is staged in LDS with 16-byte loads, the b values are written over it at
 // their positions, and the row leaves with 16-byte stores (one pass over the
 // untouched columns instead of a copy followed by a scatter).
+// A row is staged at the shift of its input row; it leaves with 16-byte
+// stores when its output row has the same shift, element by element
+// otherwise.  pitch = stage_pitch(d).
 template <typename E>
 __global__ __launch_bounds__(256) void k_replace_cols_lds(const E* __restrict__ in, int64_t ld_in,
                                                           const E* __restrict__ src, int64_t ld_src, int b,
                                                           const int32_t* __restrict__ idx, E* __restrict__ out,
-                                                          int64_t ld_out, int rows, int d, int rpw) {
+                                                          int64_t ld_out, int rows, int d, int rpw, int pitch) {
   extern __shared__ __align__(16) unsigned char smem[];
   E* buf = reinterpret_cast<E*>(smem);
-  constexpr int V = 16 / sizeof(E);
-  const int pitch = (d + V - 1) / V * V;
   const int t0 = blockIdx.x * rpw;
   const int nr = min(rpw, rows - t0);
-  const int dv = d / V;
-  const bool vin = (reinterpret_cast<uintptr_t>(in) % 16 == 0) && (ld_in % V == 0);
   for (int rr = 0; rr < nr; ++rr) {
     const E* row = in + (int64_t)(t0 + rr) * ld_in;
-    E* dst = buf + rr * pitch;
-    int tail = 0;
-    if (vin) {
-      for (int c = threadIdx.x; c < dv; c += blockDim.x)
-        reinterpret_cast<uint4*>(dst)[c] = reinterpret_cast<const uint4*>(row)[c];
-      tail = dv * V;
-    }
-    for (int i = tail + threadIdx.x; i < d; i += blockDim.x) dst[i] = row[i];
+    const int h = lead16(row, d);
+    row_to_lds(row, buf + rr * pitch + lds_shift<E>(h), d, h);
   }
   __syncthreads();
   for (int rr = 0; rr < nr; ++rr) {
     const E* srow = src + (int64_t)(t0 + rr) * ld_src;
-    E* dst = buf + rr * pitch;
+    E* dst = buf + rr * pitch + lds_shift<E>(lead16(in + (int64_t)(t0 + rr) * ld_in, d));
     for (int i = threadIdx.x; i < b; i += blockDim.x) dst[min(max(idx[i], 0), d - 1)] = srow[i];
   }
   __syncthreads();
-  const bool vout = (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (ld_out % V == 0);
   for (int rr = 0; rr < nr; ++rr) {
     E* o = out + (int64_t)(t0 + rr) * ld_out;
-    const E* srow = buf + rr * pitch;
-    int tail = 0;
-    if (vout) {
-      for (int c = threadIdx.x; c < dv; c += blockDim.x)
-        reinterpret_cast<uint4*>(o)[c] = reinterpret_cast<const uint4*>(srow)[c];
-      tail = dv * V;
+    const int h = lead16(o, d);
+    const int sh_in = lds_shift<E>(lead16(in + (int64_t)(t0 + rr) * ld_in, d));
+    const E* srow = buf + rr * pitch + sh_in;
+    if (lds_shift<E>(h) == sh_in) {
+      lds_to_row(srow, o, d, h);
+    } else {
+      for (int i = threadIdx.x; i < d; i += blockDim.x) o[i] = srow[i];
     }
-    for (int i = tail + threadIdx.x; i < d; i += blockDim.x) o[i] = srow[i];
   }
 }
 
@@ -882,11 +926,12 @@ hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap,
   auto go = [&](auto tag) -> hipError_t {
     using E = decltype(tag);
     const size_t pitch_bytes = (row_bytes + 15) / 16 * 16;
-    if (pitch_bytes <= budget) {
+    const int64_t pitch = stage_pitch(d_in, es);
+    if ((size_t)pitch * es <= budget) {
       const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, target / pitch_bytes));
-      k_permute_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch_bytes, s>>>(
+      k_permute_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch * es, s>>>(
           reinterpret_cast<const E*>(in), ld_in, rowmap, colmap, reinterpret_cast<E*>(out), ld_out, rows, d_in, d_out,
-          rpw);
+          rpw, (int)pitch);
     } else {
       k_permute_direct<E><<<rows, 256, 0, s>>>(reinterpret_cast<const E*>(in), ld_in, rowmap, colmap,
                                                reinterpret_cast<E*>(out), ld_out, rows, d_in, d_out);
@@ -906,10 +951,11 @@ hipError_t scatter(int dt, const void* in, int64_t ld_in, const int32_t* perm, v
   auto go = [&](auto tag) -> hipError_t {
     using E = decltype(tag);
     const size_t pitch_bytes = ((size_t)d * es + 15) / 16 * 16;
-    if (pitch_bytes <= budget) {
+    const int64_t pitch = stage_pitch(d, es);
+    if ((size_t)pitch * es <= budget) {
       const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, target / pitch_bytes));
-      k_scatter_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch_bytes, s>>>(
-          reinterpret_cast<const E*>(in), ld_in, perm, reinterpret_cast<E*>(out), ld_out, rows, d, rpw);
+      k_scatter_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch * es, s>>>(
+          reinterpret_cast<const E*>(in), ld_in, perm, reinterpret_cast<E*>(out), ld_out, rows, d, rpw, (int)pitch);
     } else {
       k_scatter_direct<E><<<rows, 256, 0, s>>>(reinterpret_cast<const E*>(in), ld_in, perm,
                                                reinterpret_cast<E*>(out), ld_out, d);
@@ -926,8 +972,9 @@ hipError_t replace_cols(int dt, const void* in, int64_t ld_in, const void* src, 
   if (rows <= 0 || d <= 0) return hipSuccess;
   const size_t es = dt_size(dt);
   const size_t pitch_bytes = ((size_t)d * es + 15) / 16 * 16;
+  const int64_t pitch = stage_pitch(d, es);
   const size_t budget = 64 * 1024, target = 8 * 1024;  // as for permute
-  if (pitch_bytes > budget) {  // rows too long to stage: copy, then write the subset
+  if ((size_t)pitch * es > budget) {  // rows too long to stage: copy, then write the subset
     const hipError_t e = hipMemcpy2DAsync(out, (size_t)ld_out * es, in, (size_t)ld_in * es, (size_t)d * es,
                                           (size_t)rows, hipMemcpyDeviceToDevice, s);
     if (e != hipSuccess) return e;
@@ -936,9 +983,9 @@ hipError_t replace_cols(int dt, const void* in, int64_t ld_in, const void* src, 
   const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, target / pitch_bytes));
   auto go = [&](auto tag) -> hipError_t {
     using E = decltype(tag);
-    k_replace_cols_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch_bytes, s>>>(
+    k_replace_cols_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch * es, s>>>(
         reinterpret_cast<const E*>(in), ld_in, reinterpret_cast<const E*>(src), ld_src, b, idx,
-        reinterpret_cast<E*>(out), ld_out, rows, d, rpw);
+        reinterpret_cast<E*>(out), ld_out, rows, d, rpw, (int)pitch);
     return hipGetLastError();
   };
   if (dt == F32) return go(float{});
