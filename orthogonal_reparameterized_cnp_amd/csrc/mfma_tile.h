@@ -435,57 +435,52 @@ struct LoadMN {
 // Transposing loader for bf16 tiles of R rows x 64 K whose source has the row
 // index contiguous (element (k, r) at base[k * ld + r]), into an unpadded LDS
 // tile [R][64] of 128-byte rows whose 16-byte chunks are XOR-swizzled by
-// ((r / 2) ^ (r / 16)) % 8.  A unit is 8 rows x 4 K values: four 16-byte
-// global loads along the rows, then eight 8-byte LDS stores along K.  Units
-// are dealt so that the 8 lanes of each group take 8 consecutive row chunks of
-// one K quad, so every wave instruction reads whole 128-byte lines (LoadMN's
-// order reads 64-byte halves); with the swizzle the 64-bit stores are at most
-// 2-way bank conflicted and the 128-bit fragment reads conflict-free.  The
-// whole tile must lie inside the source (no bounds checks).
+// ((r / 2) ^ (r / 16)) % 8.  A unit is 8 rows x 8 K values: eight 16-byte
+// global loads along the rows, an 8 x 8 transpose of 16-bit values in
+// registers (v_perm), then eight 16-byte LDS stores along K, one chunk each.
+// Units are dealt so that lanes 0-31 and 32-63 of a wave each read 256
+// consecutive rows of one K (whole 128-byte lines).  NT2 threads load one
+// tile: a contiguous range of thread indices starting at a multiple of NT2.
+// The whole tile must lie inside the source (no bounds checks).
 // ---------------------------------------------------------------------------
 PX_DEV int tswz_chunk(int r, int c) { return r * 8 + (c ^ (((r >> 1) ^ (r >> 4)) & 7)); }
-template <int R, int NT> struct LoadT {
-  static constexpr int UNITS = R / 8 * 16;  // (8-row chunk, 4-K quad)
-  static constexpr int NU = UNITS / NT;
-  static_assert(UNITS % NT == 0 && NT % 128 == 0 && R % 64 == 0, "whole units per thread");
+template <int R, int NT2> struct LoadT {
+  static constexpr int CG = R / 8;        // 8-row chunks
+  static constexpr int UNITS = CG * 8;    // (row chunk, K octet)
+  static constexpr int NU = UNITS / NT2;
+  static_assert(UNITS % NT2 == 0 && NU >= 1 && CG % 32 == 0, "whole units per thread, 32 row chunks per half wave");
   const bf16_t* base;
   int64_t ld;
-  uint4 c[NU][4];
+  uint4 c[NU][8];
   PX_DEV void init(const bf16_t* b, int64_t l) {
     base = b;
     ld = l;
   }
-  // unit u: row chunk 8 (u / 128) + u % 8 (8 rows each), K quad (u / 8) % 16
-  PX_DEV static void unit(int u, int& cg, int& kq) {
-    cg = 8 * (u / 128) + u % 8;
-    kq = (u / 8) % 16;
-  }
+  // unit u: row chunk u % CG (rows 8 (u % CG) .. + 7), K octet u / CG
   PX_DEV void fetch(int k0) {
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
-      int cg, kq;
-      unit((int)(threadIdx.x % NT) + i * NT, cg, kq);
+      const int u = (int)(threadIdx.x % NT2) + i * NT2, cg = u % CG, ko = u / CG;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        c[i][kk] = *reinterpret_cast<const uint4*>(base + (int64_t)(k0 + 4 * kq + kk) * ld + 8 * cg);
+      for (int kk = 0; kk < 8; ++kk)
+        c[i][kk] = *reinterpret_cast<const uint4*>(base + (int64_t)(k0 + 8 * ko + kk) * ld + 8 * cg);
     }
   }
+  PX_DEV static uint32_t word(const uint4& v, int w) { return w == 0 ? v.x : w == 1 ? v.y : w == 2 ? v.z : v.w; }
   PX_DEV void stash(char* tile) const {
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
-      int cg, kq;
-      unit((int)(threadIdx.x % NT) + i * NT, cg, kq);
-      const uint32_t w[4][4] = {{c[i][0].x, c[i][0].y, c[i][0].z, c[i][0].w},
-                                {c[i][1].x, c[i][1].y, c[i][1].z, c[i][1].w},
-                                {c[i][2].x, c[i][2].y, c[i][2].z, c[i][2].w},
-                                {c[i][3].x, c[i][3].y, c[i][3].z, c[i][3].w}};
+      const int u = (int)(threadIdx.x % NT2) + i * NT2, cg = u % CG, ko = u / CG;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        auto h = [&](int kk) { return (w[kk][e / 2] >> (16 * (e % 2))) & 0xffffu; };
-        uint2 v;
-        v.x = h(0) | (h(1) << 16);
-        v.y = h(2) | (h(3) << 16);
-        *reinterpret_cast<uint2*>(tile + 16 * tswz_chunk(8 * cg + e, kq / 2) + 8 * (kq % 2)) = v;
+        // row 8 cg + e: the 16-bit element e of the eight loads, in K order (low halves for even e)
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        uint4 v;
+        v.x = __builtin_amdgcn_perm(word(c[i][1], e / 2), word(c[i][0], e / 2), sel);
+        v.y = __builtin_amdgcn_perm(word(c[i][3], e / 2), word(c[i][2], e / 2), sel);
+        v.z = __builtin_amdgcn_perm(word(c[i][5], e / 2), word(c[i][4], e / 2), sel);
+        v.w = __builtin_amdgcn_perm(word(c[i][7], e / 2), word(c[i][6], e / 2), sel);
+        *reinterpret_cast<uint4*>(tile + 16 * tswz_chunk(8 * cg + e, ko)) = v;
       }
     }
   }

@@ -463,30 +463,24 @@ __global__ __launch_bounds__(C::NT) void k_block_grads_part(SideTable sd, GradSi
     if (r - m0 >= C::BM && r - n0 >= C::BN && per % 64 == 0 && aligned8(pa, gs.lda[s]) && aligned8(pb, gs.ldb[s])) {
       constexpr int TA = C::BM * 128, STG = (C::BM + C::BN) * 128;
       char* lds = reinterpret_cast<char*>(smem);
-      LoadT<C::BM, C::NT> la;
-      LoadT<C::BN, C::NT> lb;
-      la.init(pa, gs.lda[s]);
-      lb.init(pb, gs.ldb[s]);
+      // the first half of the workgroup loads the A tile, the second half the B tile
+      static_assert(C::BM == C::BN, "one loader shape for both operands");
+      const bool is_b = threadIdx.x >= C::NT / 2;
+      LoadT<C::BM, C::NT / 2> ld;
+      ld.init(is_b ? pb : pa, is_b ? gs.ldb[s] : gs.lda[s]);
+      const int mine = is_b ? TA : 0;
       acc.zero();
       const int NK = per / 64;
-      la.fetch(0);
-      lb.fetch(0);
-      la.stash(lds);
-      lb.stash(lds + TA);
+      ld.fetch(0);
+      ld.stash(lds + mine);
       __syncthreads();
       for (int kt = 0; kt < NK; ++kt) {
         const char* cur = lds + (kt & 1) * STG;
         char* nxt = lds + ((kt + 1) & 1) * STG;
         const bool more = kt + 1 < NK;
-        if (more) {
-          la.fetch((kt + 1) * 64);
-          lb.fetch((kt + 1) * 64);
-        }
+        if (more) ld.fetch((kt + 1) * 64);
         mma_stage_t<C>(cur, cur + TA, acc, p.wm, p.wn, p.lane);
-        if (more) {
-          la.stash(nxt);
-          lb.stash(nxt + TA);
-        }
+        if (more) ld.stash(nxt + mine);
         __syncthreads();
       }
       done = true;
