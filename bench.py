@@ -124,7 +124,7 @@ def summarize_traffic(fetch_dir, write_dir, cmd_fetch, cmd_write):
         # the probe is the last device copy before the step's first CNP kernel (warm-up 0)
         first_step = min((i for i, n, _ in rows if "k_unpack_q" in n), default=None)
         copies = [v for i, n, v in rows if "copyBuffer" in n and first_step is not None and i < first_step]
-        gemm = [v for _, n, v in rows if "k_gemm<" in n]
+        gemm = [v for _, n, v in rows if "k_gemm<" in n or "k_gemm_group<" in n]
         if not copies or not gemm or copies[-1] * 1024 < COPY_PROBE_BYTES / 4:
             raise SystemExit(f"{d}: copy probe or k_gemm dispatches missing")
         # the probe reads and writes COPY_PROBE_BYTES once
@@ -171,6 +171,7 @@ traffic-json: {json.dumps(line)}
 
 KERNEL_CLASSES = (  # kernel-name prefix -> class, as in --breakdown
     ("k_gemm<", "W~ contractions"),
+    ("k_gemm_group<", "W~ contractions"),
     ("k_apply<", "block products"),
     ("k_apply_stream<", "block products"),
     ("k_block_grads", "block gradients"),
@@ -388,7 +389,7 @@ class WorkloadStep:
     whole hot path over one batch (batched CNP build, the forwards, the backwards to dX and the block
     gradients, the batched CNP chain rule to every side's packed dq, and optionally the Adam step)."""
 
-    def __init__(self, wl, mode, to_dev, dev, optimizer=False, batch_grads=True):
+    def __init__(self, wl, mode, to_dev, dev, optimizer=False, batch_grads=True, grouped=True):
         import torch
 
         from orthogonal_reparameterized_cnp_amd.layer import PoetxAdam, PoetxGroup, PoetxLinear
@@ -404,7 +405,9 @@ class WorkloadStep:
                      to_dev(inp.q_R, "f32"), to_dev(inp.q_P, "f32"))
             lay.reserve(self.T)
             self.layers.append(lay)
-            self.Xs.append(to_dev(inp.X, inp.act))
+            # linears that read one input (q, k, v; gate, up) share the tensor of the first of them
+            first = next(g[0] for g in wl.input_groups if i in g)
+            self.Xs.append(self.Xs[first] if first != i else to_dev(inp.X, inp.act))
             self.dZs.append(to_dev(inp.dZ, inp.act))
             if i == 0:
                 self.inputs0 = inp
@@ -418,6 +421,10 @@ class WorkloadStep:
         # bit-identical to per-linear calls).
         self.batch_grads = batch_grads
         self.group = PoetxGroup(self.layers, batch_grads=batch_grads)
+        # grouped: the linears that share an input run as one group call (their block products in shared
+        # launches, their W~ contractions in one launch where that fills the GPU); bit-identical outputs
+        self.grouped = grouped and batch_grads
+        self.calls = wl.input_groups if self.grouped else tuple((i,) for i in range(len(wl.linears)))
         # Adam on every side's packed q (lr small enough that the timed steps stay near the start)
         self.opt = PoetxAdam(self.layers, lr=1e-5)
         self.optimizer = optimizer
@@ -425,10 +432,18 @@ class WorkloadStep:
 
     def step(self):
         self.group.build()
-        for lay, X, Y in zip(self.layers, self.Xs, self.Ys):
-            lay.forward(X, Y)
-        for i in reversed(range(len(self.layers))):
-            self.group.backward_dx(i, self.Xs[i], self.dZs[i], self.dXs[i], Y=self.Ys[i] if self.mode == "xout" else None)
+        if not self.grouped:
+            for lay, X, Y in zip(self.layers, self.Xs, self.Ys):
+                lay.forward(X, Y)
+            for i in reversed(range(len(self.layers))):
+                self.group.backward_dx(i, self.Xs[i], self.dZs[i], self.dXs[i],
+                                       Y=self.Ys[i] if self.mode == "xout" else None)
+        else:
+            for g in self.calls:
+                self.group.forward(g, [self.Xs[i] for i in g], [self.Ys[i] for i in g])
+            for g in reversed(self.calls):
+                self.group.backward_dx_many(g, [self.dZs[i] for i in g], [self.dXs[i] for i in g],
+                                            Ys=[self.Ys[i] for i in g] if self.mode == "xout" else None)
         self.group.backward_q(self.dqs)
         if self.optimizer:
             self.opt.step(self.dqs)
@@ -547,6 +562,9 @@ def main():
     ap.add_argument("--grads", choices=("batched", "per-linear"), default="batched",
                     help="block gradients of all sides in shared launches after the last backward (dq equal to "
                          "the per-linear calls' to fp32 rounding), or inside each linear's backward")
+    ap.add_argument("--calls", choices=("grouped", "per-linear"), default="grouped",
+                    help="the linears that read one input (q, k, v; gate, up) as one group call (bit-identical "
+                         "outputs, shared launches), or one call per linear; grouped needs --grads batched")
     ap.add_argument("--merge", metavar="WORKLOAD", nargs="?", const="llama13b_int8", default=None,
                     help="also time poetx_merge_reinit of every linear of WORKLOAD (default llama13b_int8) and "
                          "report it amortised over the workload's merge period")
@@ -597,7 +615,8 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     t_gen = time.perf_counter()
-    ws = WorkloadStep(wl, args.mode, to_dev, dev, optimizer=args.optimizer, batch_grads=args.grads == "batched")
+    ws = WorkloadStep(wl, args.mode, to_dev, dev, optimizer=args.optimizer, batch_grads=args.grads == "batched",
+                      grouped=args.calls == "grouped")
     layers, inputs0, opt, dqs, step = ws.layers, ws.inputs0, ws.opt, ws.dqs, ws.step
     print(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
 
@@ -668,6 +687,7 @@ def main():
             "mode": args.mode,
             "optimizer_in_step": "adam" if args.optimizer else None,
             "block_grads": args.grads,
+            "calls": " | ".join(",".join(wl.linears[i].name for i in g) for g in ws.calls),
             "launch": "hip graph replay" if args.graph else "eager",
         },
         "tflops": total_f / (ms * 1e-3) / 1e12,

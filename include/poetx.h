@@ -346,6 +346,74 @@ poetx_status poetx_linear_bwd_dx_sides(const poetx_layer_desc* desc, int64_t T, 
                                        const void* g_P, const void* H_save, void* dX, poetx_grad_side* sides,
                                        void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Group calls: the forwards, or the backwards to dX, of up to POETX_MAX_GROUP
+ * linears over the same T token rows (for instance q, k and v of an attention
+ * layer, or gate and up of an MLP), with the block products of all of them in
+ * shared launches, and those W~ contractions of equal K that are too small to
+ * fill the GPU alone in one launch where together they do (k and v of a
+ * grouped-query attention layer).  Each linear's outputs are bit-identical to
+ * its own poetx_linear_fwd / poetx_linear_bwd_dx_sides call (the same kernels
+ * take the same operands in the same order; the launches only share
+ * workgroups).  The linears must
+ * share b; their inputs may be the same tensor, and every other buffer (ws,
+ * H_save, outputs) must be their own.  Layers with act_dtype F32 run one call
+ * per linear.
+ */
+#define POETX_MAX_GROUP 8
+
+/* One linear of poetx_linear_fwd_group: the arguments of poetx_linear_fwd. */
+typedef struct poetx_fwd_call {
+  const poetx_layer_desc* desc;
+  const void* X;
+  const int32_t* perm_R;
+  const int32_t* perm_P;
+  const void* Wt;
+  const void* g_R;
+  const void* g_P;
+  void* Y;
+  void* H_save;
+  void* ws;
+  size_t ws_bytes;
+} poetx_fwd_call;
+
+/*
+ * poetx_linear_fwd of calls[0 .. count) (a HOST array), T rows each.
+ * Errors: POETX_E_NULL (calls, or a pointer poetx_linear_fwd requires),
+ * POETX_E_SHAPE (count outside [1, POETX_MAX_GROUP], T outside [0, 2^31), b
+ * not shared), and each call's errors as for poetx_linear_fwd; arguments are
+ * all checked before the first launch.
+ */
+poetx_status poetx_linear_fwd_group(int32_t count, const poetx_fwd_call* calls, int64_t T, void* stream);
+
+/* One linear of poetx_linear_bwd_dx_group: the arguments of
+ * poetx_linear_bwd_dx_sides. */
+typedef struct poetx_bwd_call {
+  const poetx_layer_desc* desc;
+  const void* Y;
+  const void* dZ;
+  const int32_t* perm_R;
+  const int32_t* perm_P;
+  const void* Wt;
+  const void* g_R;
+  const void* g_P;
+  const void* H_save;
+  void* dX;
+  void* ws;
+  size_t ws_bytes;
+} poetx_bwd_call;
+
+/*
+ * poetx_linear_bwd_dx_sides of calls[0 .. count) (a HOST array), T rows each:
+ * dX of every linear, and the operands of its block gradients in
+ * sides[2 i] (R) and sides[2 i + 1] (P) (a HOST array of 2 count), valid
+ * until that linear's H_save or ws is written again.  Errors as for
+ * poetx_linear_fwd_group, with each call's errors as for
+ * poetx_linear_bwd_dx_sides.
+ */
+poetx_status poetx_linear_bwd_dx_group(int32_t count, const poetx_bwd_call* calls, int64_t T, poetx_grad_side* sides,
+                                       void* stream);
+
 /* Workspace bytes of poetx_block_grads_batch (the fp32 partial sums of token
  * splits; 0 when no split is used or for invalid arguments). */
 size_t poetx_block_grads_workspace_size(int32_t count, const int32_t* d, int64_t rows, int32_t b, int32_t dtype);

@@ -31,6 +31,7 @@ DTYPES = {"f32": POETX_F32, "bf16": POETX_BF16, "i8": POETX_I8}
 # what the forward saves: H and Xt; Xt only (H recomputed from it); Xt only (H taken back from Y)
 POETX_XFAST, POETX_XMEM, POETX_XOUT = 0, 1, 2
 POETX_MAX_SIDES = 64  # most sides one batched call accepts
+POETX_MAX_GROUP = 8  # most linears one group call accepts
 MODES = {"xfast": POETX_XFAST, "xmem": POETX_XMEM, "xout": POETX_XOUT}
 
 
@@ -71,6 +72,39 @@ class GradSide(ctypes.Structure):
         ("B", ctypes.c_void_p),
         ("ldb", ctypes.c_int64),
         ("d", ctypes.c_int32),
+    ]
+
+
+class FwdCall(ctypes.Structure):
+    _fields_ = [
+        ("desc", ctypes.POINTER(LayerDesc)),
+        ("X", ctypes.c_void_p),
+        ("perm_R", ctypes.c_void_p),
+        ("perm_P", ctypes.c_void_p),
+        ("Wt", ctypes.c_void_p),
+        ("g_R", ctypes.c_void_p),
+        ("g_P", ctypes.c_void_p),
+        ("Y", ctypes.c_void_p),
+        ("H_save", ctypes.c_void_p),
+        ("ws", ctypes.c_void_p),
+        ("ws_bytes", ctypes.c_size_t),
+    ]
+
+
+class BwdCall(ctypes.Structure):
+    _fields_ = [
+        ("desc", ctypes.POINTER(LayerDesc)),
+        ("Y", ctypes.c_void_p),
+        ("dZ", ctypes.c_void_p),
+        ("perm_R", ctypes.c_void_p),
+        ("perm_P", ctypes.c_void_p),
+        ("Wt", ctypes.c_void_p),
+        ("g_R", ctypes.c_void_p),
+        ("g_P", ctypes.c_void_p),
+        ("H_save", ctypes.c_void_p),
+        ("dX", ctypes.c_void_p),
+        ("ws", ctypes.c_void_p),
+        ("ws_bytes", ctypes.c_size_t),
     ]
 
 
@@ -144,6 +178,10 @@ _SIG = {
     "poetx_linear_bwd_dx_sides": (
         ctypes.c_int,
         [ctypes.POINTER(LayerDesc), ctypes.c_int64] + [_P] * 9 + [ctypes.POINTER(GradSide), _P, ctypes.c_size_t, _P],
+    ),
+    "poetx_linear_fwd_group": (ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(FwdCall), ctypes.c_int64, _P]),
+    "poetx_linear_bwd_dx_group": (
+        ctypes.c_int, [ctypes.c_int32, ctypes.POINTER(BwdCall), ctypes.c_int64, ctypes.POINTER(GradSide), _P]
     ),
     "poetx_block_grads_workspace_size": (
         ctypes.c_size_t, [ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
@@ -374,6 +412,33 @@ def poetx_linear_bwd_dx_sides(dsc: LayerDesc, T: int, Y, dZ, perm_R, perm_P, Wt,
         )
     )
     return [sides[0], sides[1]]
+
+
+def poetx_linear_fwd_group(calls, T: int, stream=None):
+    """calls: list of dicts with the keyword arguments of poetx_linear_fwd (dsc, X, perm_R, perm_P, Wt, g_R, g_P,
+    Y, H_save, ws, ws_bytes), marshalled into a host array of FwdCall records."""
+    descs = [c["dsc"] for c in calls]  # kept alive through the call
+    arr = (FwdCall * len(calls))(*[
+        FwdCall(ctypes.pointer(dsc), _ptr(c["X"]), _ptr(c["perm_R"]), _ptr(c["perm_P"]), _ptr(c["Wt"]), _ptr(c["g_R"]),
+                _ptr(c["g_P"]), _ptr(c["Y"]), _ptr(c["H_save"]), _ptr(c["ws"]), c["ws_bytes"])
+        for c, dsc in zip(calls, descs)
+    ])
+    _check(lib().poetx_linear_fwd_group(len(calls), arr, T, _stream(stream)))
+
+
+def poetx_linear_bwd_dx_group(calls, T: int, stream=None):
+    """calls: list of dicts with the keyword arguments of poetx_linear_bwd_dx_sides (dsc, Y, dZ, perm_R, perm_P, Wt,
+    g_R, g_P, H_save, dX, ws, ws_bytes); returns the block-gradient operands of every linear as pairs (R, P) of
+    GradSide records."""
+    descs = [c["dsc"] for c in calls]
+    arr = (BwdCall * len(calls))(*[
+        BwdCall(ctypes.pointer(dsc), _ptr(c["Y"]), _ptr(c["dZ"]), _ptr(c["perm_R"]), _ptr(c["perm_P"]), _ptr(c["Wt"]),
+                _ptr(c["g_R"]), _ptr(c["g_P"]), _ptr(c["H_save"]), _ptr(c["dX"]), _ptr(c["ws"]), c["ws_bytes"])
+        for c, dsc in zip(calls, descs)
+    ])
+    sides = (GradSide * (2 * len(calls)))()
+    _check(lib().poetx_linear_bwd_dx_group(len(calls), arr, T, sides, _stream(stream)))
+    return [[sides[2 * i], sides[2 * i + 1]] for i in range(len(calls))]
 
 
 def poetx_block_grads_workspace_size(d, rows: int, b: int, dtype: int) -> int:

@@ -660,6 +660,254 @@ poetx_status poetx_linear_bwd_dx_sides(const poetx_layer_desc* desc, int64_t T, 
   return POETX_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// gemm_batch, one launch at a time, so that the contraction timer sees every kernel launch
+poetx_status gemm_batch_timed(int count, const GemmProblem* gp, const double* flops, const double* bytes,
+                              hipStream_t s) {
+  int launch_of[kGemmProblems];
+  const int n = gemm_launches(count, gp, launch_of);
+  for (int l = 0; l < n; ++l) {
+    GemmProblem part[kGemmProblems];
+    int np = 0;
+    double fl = 0, by = 0;
+    for (int i = 0; i < count; ++i)
+      if (launch_of[i] == l) {
+        part[np++] = gp[i];
+        fl += flops[i];
+        by += bytes[i];
+      }
+    PX_TIMED(POETX_KC_GEMM, fl, by, gemm_batch(np, part, s));
+  }
+  return POETX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+poetx_status poetx_linear_fwd_group(int32_t count, const poetx_fwd_call* calls, int64_t T, void* stream) {
+  if (!calls) return fail(POETX_E_NULL, "calls is NULL");
+  if (count < 1 || count > POETX_MAX_GROUP) return fail(POETX_E_SHAPE, "count must be in [1, POETX_MAX_GROUP]");
+  if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
+  bool bf16 = true;
+  for (int i = 0; i < count; ++i) {
+    const poetx_fwd_call& c = calls[i];
+    poetx_status st = check_desc(c.desc);
+    if (st != POETX_OK) return st;
+    if (c.desc->b != calls[0].desc->b) return fail(POETX_E_SHAPE, "the linears of a group must share b");
+    if (T > 0 && (!c.X || !c.perm_R || !c.perm_P || !c.Wt || !c.g_R || !c.g_P || !c.Y || !c.H_save))
+      return fail(POETX_E_NULL, "a required pointer is NULL");
+    Plan p;
+    plan_fwd(p, c.desc, T);
+    st = check_ws(c.ws, c.ws_bytes, p.off);
+    if (st != POETX_OK) return st;
+    bf16 = bf16 && c.desc->act_dtype == POETX_BF16;
+  }
+  if (T == 0) return POETX_OK;
+  if (!bf16) {
+    // fp32 layers: one forward per linear
+    for (int i = 0; i < count; ++i) {
+      const poetx_fwd_call& c = calls[i];
+      const poetx_status st = poetx_linear_fwd(c.desc, T, c.X, c.perm_R, c.perm_P, c.Wt, c.g_R, c.g_P, c.Y, c.H_save,
+                                               c.ws, c.ws_bytes, stream);
+      if (st != POETX_OK) return st;
+    }
+    return POETX_OK;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int rows = (int)T, b = calls[0].desc->b;
+  FwdWs w[POETX_MAX_GROUP];
+  void *Xt[POETX_MAX_GROUP], *H[POETX_MAX_GROUP];
+  ApplySide sr[POETX_MAX_GROUP], sp[POETX_MAX_GROUP];
+  GemmProblem gp[POETX_MAX_GROUP];
+  double fl_g[POETX_MAX_GROUP], by_g[POETX_MAX_GROUP];
+  double fl_r = 0, by_r = 0, fl_p = 0, by_p = 0;
+  for (int i = 0; i < count; ++i) {
+    const poetx_fwd_call& c = calls[i];
+    const poetx_layer_desc* d = c.desc;
+    const int m = d->m, n = d->n;
+    const int64_t ldm = lead(m), ldn = lead(n);
+    Plan q;
+    q.base = reinterpret_cast<char*>(c.ws);
+    w[i] = plan_fwd(q, d, T);
+    Xt[i] = reinterpret_cast<char*>(c.H_save) + saved_xt_offset(d, T);
+    H[i] = saves_h(d) ? c.H_save : w[i].H;
+    const char* gR1 = reinterpret_cast<const char*>(c.g_R) + g_slice(m, b, BF16);  // Delta_R^T
+    const char* gP1 = reinterpret_cast<const char*>(c.g_P) + g_slice(n, b, BF16);  // Delta_P^T
+    sr[i] = ApplySide{Xt[i], ldm, m, gR1, nullptr, w[i].A, ldm};
+    sp[i] = ApplySide{H[i], ldn, n, gP1, nullptr, w[i].Zt, ldn};
+    fl_r += 2.0 * rows * sum_r2(m, b);
+    by_r += 4.0 * rows * m + g_slice(m, b, BF16);
+    fl_p += 2.0 * rows * sum_r2(n, b);
+    by_p += 4.0 * rows * n + g_slice(n, b, BF16);
+    // H = A W~: bf16 weights from the stored W~^T, int8 codes from their transpose widened to bf16 (exact)
+    const float* scale_t = nullptr;
+    const void* Bw = nullptr;
+    if (has_weight_t(d)) {
+      Bw = reinterpret_cast<const char*>(c.Wt) + weight_t_offset(d);
+    } else {
+      scale_t = reinterpret_cast<const float*>(reinterpret_cast<const char*>(c.Wt) + weight_scale_offset(d));
+      Bw = w[i].Wb;
+    }
+    gp[i] = GemmProblem{w[i].A, ldm, Bw, ldm, rows, n, m, scale_t, H[i], ldn};
+    fl_g[i] = 2.0 * rows * m * n;
+    by_g[i] = 2.0 * rows * m + 2.0 * m * n + 2.0 * rows * n;
+  }
+  // Xt = X[:, perm_R], kept in the saved state for the backward; the linears that read one input
+  // tensor gather from it in one pass (each row of X read once)
+  bool gathered[POETX_MAX_GROUP] = {};
+  for (int i = 0; i < count; ++i) {
+    if (gathered[i]) continue;
+    const int m = calls[i].desc->m;
+    const int32_t* cm[POETX_MAX_GROUP];
+    void* xo[POETX_MAX_GROUP];
+    int64_t ld[POETX_MAX_GROUP];
+    int dd[POETX_MAX_GROUP], nm = 0;
+    for (int j = i; j < count; ++j) {
+      if (gathered[j] || calls[j].X != calls[i].X || calls[j].desc->m != m) continue;
+      gathered[j] = true;
+      cm[nm] = calls[j].perm_R;
+      xo[nm] = Xt[j];
+      ld[nm] = lead(m);
+      dd[nm++] = m;
+    }
+    if (nm == 1)
+      PX_TIMED(POETX_KC_PERMUTE, 0, 4.0 * rows * m,
+               permute(BF16, calls[i].X, m, nullptr, cm[0], xo[0], ld[0], rows, m, m, s));
+    else
+      PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * (1 + nm),
+               permute_multi(BF16, calls[i].X, m, nm, cm, xo, ld, dd, rows, m, s));
+  }
+  // A = Xt Diag(G_R) for every linear
+  PX_TIMED(POETX_KC_APPLY, fl_r, by_r, apply_batch(count, sr, rows, b, s));
+  for (int i = 0; i < count; ++i) {
+    const poetx_layer_desc* d = calls[i].desc;
+    if (d->w_dtype == POETX_I8)
+      PX_TIMED(POETX_KC_GEMM, 0, 3.0 * d->m * d->n,
+               widen_i8(reinterpret_cast<const int8_t*>(calls[i].Wt), lead(d->n), d->m, d->n, true,
+                        reinterpret_cast<uint16_t*>(w[i].Wb), lead(d->m), s));
+  }
+  poetx_status st = gemm_batch_timed(count, gp, fl_g, by_g, s);
+  if (st != POETX_OK) return st;
+  // Zt = H Diag(G_P), then Y[:, perm_P] = Zt
+  PX_TIMED(POETX_KC_APPLY, fl_p, by_p, apply_batch(count, sp, rows, b, s));
+  for (int i = 0; i < count; ++i) {
+    const int n = calls[i].desc->n;
+    PX_TIMED(POETX_KC_PERMUTE, 0, 4.0 * rows * n,
+             scatter(BF16, w[i].Zt, lead(n), calls[i].perm_P, calls[i].Y, n, rows, n, s));
+  }
+  return POETX_OK;
+}
+
+poetx_status poetx_linear_bwd_dx_group(int32_t count, const poetx_bwd_call* calls, int64_t T, poetx_grad_side* sides,
+                                       void* stream) {
+  if (!calls || !sides) return fail(POETX_E_NULL, "calls and sides must be non-NULL");
+  if (count < 1 || count > POETX_MAX_GROUP) return fail(POETX_E_SHAPE, "count must be in [1, POETX_MAX_GROUP]");
+  if (T < 0 || T > kMaxT) return fail(POETX_E_SHAPE, "T must be in [0, 2^31)");
+  bool bf16 = true;
+  for (int i = 0; i < count; ++i) {
+    const poetx_bwd_call& c = calls[i];
+    const poetx_status st = check_bwd(c.desc, T, c.Y, c.dZ, c.perm_R, c.perm_P, c.Wt, c.g_R, c.g_P, nullptr, nullptr,
+                                      c.H_save, c.dX, c.ws, c.ws_bytes, false);
+    if (st != POETX_OK) return st;
+    if (c.desc->b != calls[0].desc->b) return fail(POETX_E_SHAPE, "the linears of a group must share b");
+    bf16 = bf16 && c.desc->act_dtype == POETX_BF16;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  BwdWs w[POETX_MAX_GROUP];
+  for (int i = 0; i < count; ++i) {
+    Plan q;
+    q.base = reinterpret_cast<char*>(calls[i].ws);
+    w[i] = plan_bwd(q, calls[i].desc, T);
+  }
+  if (!bf16 || T == 0) {
+    // fp32 layers (and no tokens): one backward per linear
+    for (int i = 0; i < count; ++i) {
+      const poetx_bwd_call& c = calls[i];
+      CnpSide cs[2];
+      const poetx_status st = bwd_dx_core(c.desc, T, c.Y, c.dZ, c.perm_R, c.perm_P, c.Wt, c.g_R, c.g_P, nullptr,
+                                          nullptr, c.H_save, c.dX, nullptr, 0, 0, w[i], s, cs);
+      if (st != POETX_OK) return st;
+      for (int k = 0; k < 2; ++k)
+        sides[2 * i + k] = poetx_grad_side{cs[k].A, cs[k].lda, cs[k].B, cs[k].ldb, cs[k].d};
+    }
+    return POETX_OK;
+  }
+  const int rows = (int)T, b = calls[0].desc->b;
+  ApplySide sp[POETX_MAX_GROUP], sr[POETX_MAX_GROUP];
+  GemmProblem gp[POETX_MAX_GROUP];
+  double fl_g[POETX_MAX_GROUP], by_g[POETX_MAX_GROUP];
+  double fl_r = 0, by_r = 0, fl_p = 0, by_p = 0;
+  for (int i = 0; i < count; ++i) {
+    const poetx_bwd_call& c = calls[i];
+    const poetx_layer_desc* d = c.desc;
+    const int m = d->m, n = d->n;
+    const int64_t ldm = lead(m), ldn = lead(n);
+    const float* scale_t =
+        d->w_dtype == POETX_I8
+            ? reinterpret_cast<const float*>(reinterpret_cast<const char*>(c.Wt) + weight_scale_offset(d))
+            : nullptr;
+    // dZt = dZ[:, perm_P]
+    PX_TIMED(POETX_KC_PERMUTE, 0, 4.0 * rows * n,
+             permute(BF16, c.dZ, n, nullptr, c.perm_P, w[i].dZt, ldn, rows, n, n, s));
+    // dH = dZt Diag(G_P)^T (int8: times the column scale); dA = dH W~^T (int8: the codes widened to bf16)
+    sp[i] = ApplySide{w[i].dZt, ldn, n, c.g_P, scale_t, w[i].dH, ldn};
+    const void* Bw = d->w_dtype == POETX_I8 ? w[i].Wb : c.Wt;
+    gp[i] = GemmProblem{w[i].dH, ldn, Bw, d->w_dtype == POETX_I8 ? ldn : lead(n), rows, m, n, nullptr, w[i].dA, ldm};
+    // dXt = dA Diag(G_R)^T
+    sr[i] = ApplySide{w[i].dA, ldm, m, c.g_R, nullptr, w[i].dXt, ldm};
+    fl_p += 2.0 * rows * sum_r2(n, b);
+    by_p += 4.0 * rows * n + g_slice(n, b, BF16);
+    fl_r += 2.0 * rows * sum_r2(m, b);
+    by_r += 4.0 * rows * m + g_slice(m, b, BF16);
+    fl_g[i] = 2.0 * rows * m * n;
+    by_g[i] = 2.0 * rows * n + (d->w_dtype == POETX_I8 ? 2.0 : (double)dt_size(d->w_dtype)) * m * n + 2.0 * rows * m;
+  }
+  PX_TIMED(POETX_KC_APPLY, fl_p, by_p, apply_batch(count, sp, rows, b, s));
+  for (int i = 0; i < count; ++i) {
+    const poetx_layer_desc* d = calls[i].desc;
+    if (d->w_dtype == POETX_I8)
+      PX_TIMED(POETX_KC_GEMM, 0, 3.0 * d->m * d->n,
+               widen_i8(reinterpret_cast<const int8_t*>(calls[i].Wt), lead(d->n), d->m, d->n, false,
+                        reinterpret_cast<uint16_t*>(w[i].Wb), lead(d->n), s));
+  }
+  poetx_status st = gemm_batch_timed(count, gp, fl_g, by_g, s);
+  if (st != POETX_OK) return st;
+  // H for the P side's block gradients, as in poetx_linear_bwd_dx_sides: saved (Xfast), recomputed from Xt
+  // into the buffers of dH and dXt (Xmem), or taken back from the output (Xout)
+  for (int i = 0; i < count; ++i) {
+    const poetx_bwd_call& c = calls[i];
+    const poetx_layer_desc* d = c.desc;
+    const int m = d->m, n = d->n;
+    const int64_t ldm = lead(m), ldn = lead(n);
+    const void* Xt = reinterpret_cast<const char*>(c.H_save) + saved_xt_offset(d, T);
+    const void* H = c.H_save;
+    if (d->mode == POETX_XMEM) {
+      const poetx_status st = xt_to_h(d, T, Xt, c.Wt, c.g_R, w[i].dXt, w[i].dH, w[i].Wb, s);
+      if (st != POETX_OK) return st;
+      H = w[i].dH;
+    } else if (d->mode == POETX_XOUT) {
+      PX_TIMED(POETX_KC_PERMUTE, 0, 4.0 * rows * n,
+               permute(BF16, c.Y, n, nullptr, c.perm_P, w[i].dH, ldn, rows, n, n, s));
+      PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 4.0 * rows * n + g_slice(n, b, BF16),
+               apply(BF16, BF16, w[i].dH, ldn, rows, n, b, BF16, c.g_P, nullptr, BF16, w[i].Hr, ldn, s));
+      H = w[i].Hr;
+    }
+    sides[2 * i] = poetx_grad_side{Xt, ldm, w[i].dA, ldm, m};
+    sides[2 * i + 1] = poetx_grad_side{H, ldn, w[i].dZt, ldn, n};
+  }
+  PX_TIMED(POETX_KC_APPLY, fl_r, by_r, apply_batch(count, sr, rows, b, s));
+  for (int i = 0; i < count; ++i) {
+    const int m = calls[i].desc->m;
+    PX_TIMED(POETX_KC_PERMUTE, 0, 4.0 * rows * m,
+             scatter(BF16, w[i].dXt, lead(m), calls[i].perm_R, calls[i].dX, m, rows, m, s));
+  }
+  return POETX_OK;
+}
+
 size_t poetx_block_grads_workspace_size(int32_t count, const int32_t* d, int64_t rows, int32_t b, int32_t dtype) {
   int64_t blocks = 0;
   if (rows < 0 || rows > kMaxT || check_sides(count, d, b, dtype, &blocks) != POETX_OK) return 0;

@@ -39,6 +39,11 @@ hipError_t scatter_cols(int dt, const void* src, int64_t ld_src, int rows, int b
 // out[t] = in[t] with out[t][idx[i]] = src[t][i] for i < b (out != in), in one pass
 hipError_t replace_cols(int dt, const void* in, int64_t ld_in, const void* src, int64_t ld_src, int b,
                         const int32_t* idx, void* out, int64_t ld_out, int rows, int d, hipStream_t s);
+// permute without a row map for `count` outputs from one input: out[k][:, i] =
+// in[:, colmap[k][i]] for i < d_out[k], each input row read once
+constexpr int kGatherOuts = 8;
+hipError_t permute_multi(int dt, const void* in, int64_t ld_in, int count, const int32_t* const* colmap,
+                         void* const* out, const int64_t* ld_out, const int* d_out, int rows, int d_in, hipStream_t s);
 // inv[perm[i]] = i
 hipError_t inverse_perm(const int32_t* perm, int d, int32_t* inv, hipStream_t s);
 // out[i] = a[b[i]]
@@ -66,9 +71,43 @@ size_t cnp_build_ws_bytes(int dt, int64_t blocks, int b);
 hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, int d, int b, int dT_dt, const void* dT,
                  const float* colscale, int out_dt, void* out, int64_t ld_out, hipStream_t s);
 
+// `count` bf16 block products of the same rows and b as apply() computes them,
+// the streamed whole blocks of all of them in shared launches (the results are
+// those of one apply() per side).
+constexpr int kApplySides = 8;
+struct ApplySide {
+  const void* in;
+  int64_t ld_in;
+  int d;
+  const void* dT;
+  const float* colscale;
+  void* out;
+  int64_t ld_out;
+};
+hipError_t apply_batch(int count, const ApplySide* sides, int rows, int b, hipStream_t s);
+
 // out = A * B (* colscale), A: [M][K] rows (lda); B either [K][N] (b_kn = true) or [N][K] (b_kn = false).
 hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const void* B, int64_t ldb, bool b_kn, int M,
                 int N, int K, const float* colscale, int out_dt, void* out, int64_t ldo, hipStream_t s);
+
+// `count` bf16 contractions out_q = A_q B_q^T (* colscale_q) (B_q: [N][K] rows):
+// those too small to give every CU a 256 x 256 tile on their own, with equal
+// K, in one launch of 256 x 256 tiles when together they do, the others one
+// gemm() each; the results are those of one gemm() per problem.
+constexpr int kGemmProblems = 8;
+struct GemmProblem {
+  const void* A;
+  int64_t lda;
+  const void* B;
+  int64_t ldb;
+  int M, N, K;
+  const float* colscale;
+  void* out;
+  int64_t ldo;
+};
+hipError_t gemm_batch(int count, const GemmProblem* p, hipStream_t s);
+// the launches gemm_batch makes: launch_of[i] (0 .. n - 1) for each problem, n returned
+int gemm_launches(int count, const GemmProblem* p, int* launch_of);
 
 // Block gradients and CNP chain rule.  The gradient state `dg` of
 // cnp_grad_bytes(dt, blocks, b) bytes holds, for `blocks` CNP blocks of one

@@ -195,11 +195,26 @@ template <int B, int RT, int S> struct StreamCfg {
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-template <int B, int RT, int S, bool CS>
-__global__ __launch_bounds__(512) void k_apply_stream(const bf16_t* __restrict__ in, int64_t ld_in, int rows,
-                                                      const bf16_t* __restrict__ dT, const float* __restrict__ cs,
-                                                      bf16_t* __restrict__ out, int64_t ld_out, int items,
-                                                      int pair_lanes) {
+// The sides of one launch: side s has blocks [first[s], first[s + 1]) of the
+// launch's block numbering, all with the same rows; cs[s] may be null (scale
+// 1) in a CS launch.  Passed by value as a kernel argument.
+struct StreamSides {
+  const bf16_t* in[pxk::kApplySides];
+  const bf16_t* dT[pxk::kApplySides];
+  const float* cs[pxk::kApplySides];
+  bf16_t* out[pxk::kApplySides];
+  int64_t ld_in[pxk::kApplySides], ld_out[pxk::kApplySides];
+  int first[pxk::kApplySides + 1];
+  int count;
+  PX_DEV int side_of(int gb) const {
+    int q = 0;
+    while (q + 1 < count && gb >= first[q + 1]) ++q;
+    return q;
+  }
+};
+
+template <int B, int RT, int S, bool CS, bool MULTI>
+__global__ __launch_bounds__(512) void k_apply_stream(const StreamSides tb, int rows, int items, int pair_lanes) {
   using C = StreamCfg<B, RT, S>;
   extern __shared__ __align__(16) unsigned char smem[];
   char* ring = reinterpret_cast<char*>(smem);
@@ -217,24 +232,35 @@ __global__ __launch_bounds__(512) void k_apply_stream(const bf16_t* __restrict__
   // Loader lanes: byte offset of each of their 1 KB copy pieces inside a row
   // tile (piece p = j * 4 + wave: K sub-tile p / (RT / 8), rows 8 (p % (RT / 8))
   // + lane / 8, the 16-byte chunk chosen by the kmaj swizzle).
-  int voff[C::PPW];
-#pragma unroll
-  for (int j = 0; j < C::PPW; ++j) {
+  auto piece_off = [&](int j, int64_t ld) {
     const int p = j * 4 + (wave & 3);
     const int kt = p / (RT / 8), r = (p % (RT / 8)) * 8 + lane / 8;
     const int c = (lane % 8) ^ ((r / 2) % 8);
-    voff[j] = (int)((int64_t)r * ld_in * 2) + kt * 128 + 16 * c;
+    return (int)((int64_t)r * ld * 2) + kt * 128 + 16 * c;
+  };
+  int voff[C::PPW];
+  if constexpr (!MULTI) {
+#pragma unroll
+    for (int j = 0; j < C::PPW; ++j) voff[j] = piece_off(j, tb.ld_in[0]);
   }
+  // launch block gb -> its side and the side's block
+  auto locate = [&](int gb, int& sd, int& blk) {
+    sd = MULTI ? tb.side_of(gb) : 0;
+    blk = gb - (MULTI ? tb.first[sd] : 0);
+  };
   // copy of the row tile of item `it` into ring slot `sl` (loader waves only)
   auto issue = [&](int it, int sl) {
-    const int blk = it / rtiles, m0 = (it % rtiles) * RT;
-    const i32x4_v rs = buffer_rsrc(in + (int64_t)m0 * ld_in + (int64_t)blk * B, (int64_t)(rows - m0) * ld_in * 2);
+    int sd, blk;
+    locate(it / rtiles, sd, blk);
+    const int m0 = (it % rtiles) * RT;
+    const int64_t ld_in = tb.ld_in[sd];
+    const i32x4_v rs = buffer_rsrc(tb.in[sd] + (int64_t)m0 * ld_in + (int64_t)blk * B, (int64_t)(rows - m0) * ld_in * 2);
     char* dst = ring + sl * C::SLOT;
 #pragma unroll
     for (int j = 0; j < C::PPW; ++j) {
       const int p = j * 4 + wave;
       raw_buffer_load_lds(rs, (__attribute__((address_space(3))) uint32_t*)(dst + (p / (RT / 8)) * C::SUB + (p % (RT / 8)) * 1024),
-                          16, voff[j], 0, 0, 0);
+                          16, MULTI ? piece_off(j, ld_in) : voff[j], 0, 0, 0);
     }
   };
   if (loader) {
@@ -259,16 +285,23 @@ __global__ __launch_bounds__(512) void k_apply_stream(const bf16_t* __restrict__
   const int ts = threadIdx.x & 255;
   uint32_t st_lds[C::SPL];
   int st_off[C::SPL];
+  auto store_off = [&](int q, int64_t ld) {
+    const int ch = ts + 256 * q, row = ch / 32, col = (ch % 32) * 8;
+    return (int)((int64_t)row * ld * 2) + col * 2;
+  };
 #pragma unroll
   for (int q = 0; q < C::SPL; ++q) {
     const int ch = ts + 256 * q, row = ch / 32, col = (ch % 32) * 8;
     st_lds[q] = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) bf16_t*)(stage + row * C::PITCH + col);  // tile 0
-    st_off[q] = (int)((int64_t)row * ld_out * 2) + col * 2;
+    st_off[q] = store_off(q, tb.ld_out[0]);
   }
 
   // store lanes: staged tile `par` (written for item `it`) to the output
   auto store_tile = [&](int par, int it) {
-    const int blk = it / rtiles, m0 = (it % rtiles) * RT;
+    int sd, blk;
+    locate(it / rtiles, sd, blk);
+    const int m0 = (it % rtiles) * RT;
+    const int64_t ld_out = tb.ld_out[sd];
     const uint32_t sb = par * C::STAGE;
     // read back in assembly, waiting for the four reads inside the block: a
     // compiler-visible LDS read would wait for every copy in flight first
@@ -282,28 +315,32 @@ __global__ __launch_bounds__(512) void k_apply_stream(const bf16_t* __restrict__
         : "=&v"(v0), "=&v"(v1), "=&v"(v2), "=&v"(v3)
         : "v"(st_lds[0] + sb), "v"(st_lds[1] + sb), "v"(st_lds[2] + sb), "v"(st_lds[3] + sb)
         : "memory");
-    const i32x4_v rs = buffer_rsrc(out + (int64_t)m0 * ld_out + (int64_t)blk * B + hc * 256,
+    const i32x4_v rs = buffer_rsrc(tb.out[sd] + (int64_t)m0 * ld_out + (int64_t)blk * B + hc * 256,
                                    (int64_t)(rows - m0) * ld_out * 2);
-    raw_buffer_store_b128(v0, rs, st_off[0], 0, 0);
-    raw_buffer_store_b128(v1, rs, st_off[1], 0, 0);
-    raw_buffer_store_b128(v2, rs, st_off[2], 0, 0);
-    raw_buffer_store_b128(v3, rs, st_off[3], 0, 0);
+    raw_buffer_store_b128(v0, rs, MULTI ? store_off(0, ld_out) : st_off[0], 0, 0);
+    raw_buffer_store_b128(v1, rs, MULTI ? store_off(1, ld_out) : st_off[1], 0, 0);
+    raw_buffer_store_b128(v2, rs, MULTI ? store_off(2, ld_out) : st_off[2], 0, 0);
+    raw_buffer_store_b128(v3, rs, MULTI ? store_off(3, ld_out) : st_off[3], 0, 0);
   };
 
   bf16x8_v dfr[C::NKS];
   float scl[16];
   int cur_blk = -1;
   for (int it = i0; it < i1; ++it) {
-    const int blk = it / rtiles, m0 = (it % rtiles) * RT;
-    if (blk != cur_blk) {
-      cur_blk = blk;
-      const bf16_t* dp = dT + ((int64_t)blk * B + c0 + (lane & 31)) * B + 8 * (lane >> 5);
+    const int gb = it / rtiles;
+    if (gb != cur_blk) {
+      cur_blk = gb;
+      int sd, blk;
+      locate(gb, sd, blk);
+      const float* cs = tb.cs[sd];
+      const bf16_t* dp = tb.dT[sd] + ((int64_t)blk * B + c0 + (lane & 31)) * B + 8 * (lane >> 5);
 #pragma unroll
       for (int s = 0; s < C::NKS; ++s) dfr[s] = *reinterpret_cast<const bf16x8_v*>(dp + 16 * s);
       if constexpr (CS) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4_v v = *reinterpret_cast<const f32x4_v*>(cs + (int64_t)blk * B + c0 + 8 * g + 4 * (lane >> 5));
+          const f32x4_v v = cs ? *reinterpret_cast<const f32x4_v*>(cs + (int64_t)blk * B + c0 + 8 * g + 4 * (lane >> 5))
+                               : f32x4_v{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
           for (int e = 0; e < 4; ++e) scl[4 * g + e] = v[e];
         }
@@ -415,6 +452,10 @@ struct TileMap {
   PX_DEV void at(int id, int& bm, int& bn) const {
     const int total = tm * tn;
     if (total % 8 == 0) id = (id % 8) * (total / 8) + id / 8;
+    at_local(id, bm, bn);
+  }
+  // tile number id (after the XCD remap) -> (row tile, column tile)
+  PX_DEV void at_local(int id, int& bm, int& bn) const {
     const int group = id / (GM * tn);
     const int first = group * GM;
     const int gsize = min(tm - first, GM);
@@ -423,14 +464,13 @@ struct TileMap {
   }
 };
 
+// One output tile (bm, bn) of out = A * B (* colscale): the direct-to-LDS
+// loop when both operand panels and K allow it, else the register loop.
 template <class CD, class C, typename T, typename AT, typename BT, typename OT, bool BKN>
-__global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_t lda, const BT* __restrict__ B,
-                                                 int64_t ldb, int M, int N, int K, const float* __restrict__ colscale,
-                                                 OT* __restrict__ out, int64_t ldo, TileMap map) {
-  extern __shared__ __align__(16) unsigned char smem[];
+PX_DEV void gemm_tile(unsigned char* smem, const AT* __restrict__ A, int64_t lda, const BT* __restrict__ B, int64_t ldb,
+                      int M, int N, int K, const float* __restrict__ colscale, OT* __restrict__ out, int64_t ldo,
+                      int bm, int bn) {
   T* lds = reinterpret_cast<T*>(smem);
-  int bm, bn;
-  map.at(blockIdx.x, bm, bn);
   const int m0 = bm * C::BM, n0 = bn * C::BN;
   const float* cs = colscale ? colscale + n0 : nullptr;
   if constexpr (!std::is_same<CD, void>::value) {
@@ -461,6 +501,46 @@ __global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_
   mainloop<C, T>(lds, la, lb, K, acc, p.wm, p.wn, p.lane);
   store_tile<C, OT>(acc, smem, out + (int64_t)m0 * ldo + n0, ldo, M - m0, N - n0,
                     [&](int c) { return cs ? cs[c] : 1.f; });
+}
+
+template <class CD, class C, typename T, typename AT, typename BT, typename OT, bool BKN>
+__global__ __launch_bounds__(C::NT) void k_gemm(const AT* __restrict__ A, int64_t lda, const BT* __restrict__ B,
+                                                 int64_t ldb, int M, int N, int K, const float* __restrict__ colscale,
+                                                 OT* __restrict__ out, int64_t ldo, TileMap map) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int bm, bn;
+  map.at(blockIdx.x, bm, bn);
+  gemm_tile<CD, C, T, AT, BT, OT, BKN>(smem, A, lda, B, ldb, M, N, K, colscale, out, ldo, bm, bn);
+}
+
+// Several contractions of one tile configuration in one launch: problem q
+// owns tiles [first[q], first[q + 1]) of the launch.  Launch indices are
+// remapped as in TileMap so that each XCD receives a contiguous range of tile
+// numbers; inside a problem, tile numbers run through groups of GM row tiles.
+struct GemmTable {
+  const bf16_t* A[pxk::kGemmProblems];
+  const bf16_t* B[pxk::kGemmProblems];
+  const float* cs[pxk::kGemmProblems];
+  bf16_t* out[pxk::kGemmProblems];
+  int64_t lda[pxk::kGemmProblems], ldb[pxk::kGemmProblems], ldo[pxk::kGemmProblems];
+  int M[pxk::kGemmProblems], N[pxk::kGemmProblems], K[pxk::kGemmProblems];
+  int first[pxk::kGemmProblems + 1];
+  int count;
+};
+
+template <class CD, class C>
+__global__ __launch_bounds__(C::NT) void k_gemm_group(const GemmTable tb) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int total = tb.first[tb.count];
+  int id = blockIdx.x;
+  if (total % 8 == 0) id = (id % 8) * (total / 8) + id / 8;
+  int q = 0;
+  while (q + 1 < tb.count && id >= tb.first[q + 1]) ++q;
+  int bm, bn;
+  const TileMap map{(tb.M[q] + C::BM - 1) / C::BM, (tb.N[q] + C::BN - 1) / C::BN};
+  map.at_local(id - tb.first[q], bm, bn);
+  gemm_tile<CD, C, bf16_t, bf16_t, bf16_t, bf16_t, false>(smem, tb.A[q], tb.lda[q], tb.B[q], tb.ldb[q], tb.M[q], tb.N[q],
+                                                          tb.K[q], tb.cs[q], tb.out[q], tb.ldo[q], bm, bn);
 }
 
 // ============================================================================
@@ -527,40 +607,20 @@ __device__ inline void lds_to_row(const E* src, E* __restrict__ row, int d, int 
   }
 }
 
-// Row-staged gather: the workgroup copies whole source rows into LDS with
-// 16-byte coalesced loads (any row alignment, see row_to_lds), then writes
-// each output row with 16-byte stores, every lane gathering its 16 bytes from
-// LDS at the permuted positions.  Indices are clamped into range so that a
-// malformed permutation cannot address outside the staged rows.  pitch =
-// stage_pitch(d_in).
-template <typename E>
-__global__ __launch_bounds__(256) void k_permute_lds(const E* __restrict__ in, int64_t ld_in,
-                                                     const int32_t* __restrict__ rowmap,
-                                                     const int32_t* __restrict__ colmap, E* __restrict__ out,
-                                                     int64_t ld_out, int rows, int d_in, int d_out, int rpw,
-                                                     int pitch) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  E* buf = reinterpret_cast<E*>(smem);
+// Rows t0 .. t0 + nr - 1 of out[:, i] = staged row[colmap[i]] for i < d_out,
+// by the whole workgroup: each lane gathers 16 bytes from LDS at the permuted
+// positions and writes them with one store.  staged(rr): the LDS copy of the
+// rr-th staged row.
+template <typename E, class Staged>
+PX_DEV void gather_staged(const Staged& staged, int nr, int t0, const int32_t* __restrict__ colmap,
+                          E* __restrict__ out, int64_t ld_out, int d_in, int d_out) {
   constexpr int V = 16 / sizeof(E);
-  const int t0 = blockIdx.x * rpw;
-  const int nr = min(rpw, rows - t0);
-  auto src_row = [&](int rr) {
-    int src = t0 + rr;
-    if (rowmap) src = min(max(rowmap[src], 0), rows - 1);
-    return in + (int64_t)src * ld_in;
-  };
-  for (int rr = 0; rr < nr; ++rr) {
-    const E* row = src_row(rr);
-    const int h = lead16(row, d_in);
-    row_to_lds(row, buf + rr * pitch + lds_shift<E>(h), d_in, h);
-  }
-  __syncthreads();
   const bool vout = (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (ld_out % V == 0) &&
                     (reinterpret_cast<uintptr_t>(colmap) % 16 == 0);
   const int nchunk = (d_out + V - 1) / V;
   for (int rr = 0; rr < nr; ++rr) {
     E* o = out + (int64_t)(t0 + rr) * ld_out;
-    const E* srow = buf + rr * pitch + lds_shift<E>(lead16(src_row(rr), d_in));
+    const E* srow = staged(rr);
     for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
       const int i0 = c * V;
       if (vout && i0 + V <= d_out) {
@@ -582,6 +642,66 @@ __global__ __launch_bounds__(256) void k_permute_lds(const E* __restrict__ in, i
       }
     }
   }
+}
+
+// Row-staged gather: the workgroup copies whole source rows into LDS with
+// 16-byte coalesced loads (any row alignment, see row_to_lds), then writes
+// each output row with 16-byte stores (gather_staged).  Indices are clamped
+// into range so that a malformed permutation cannot address outside the
+// staged rows.  pitch = stage_pitch(d_in).
+template <typename E>
+__global__ __launch_bounds__(256) void k_permute_lds(const E* __restrict__ in, int64_t ld_in,
+                                                     const int32_t* __restrict__ rowmap,
+                                                     const int32_t* __restrict__ colmap, E* __restrict__ out,
+                                                     int64_t ld_out, int rows, int d_in, int d_out, int rpw,
+                                                     int pitch) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* buf = reinterpret_cast<E*>(smem);
+  const int t0 = blockIdx.x * rpw;
+  const int nr = min(rpw, rows - t0);
+  auto src_row = [&](int rr) {
+    int src = t0 + rr;
+    if (rowmap) src = min(max(rowmap[src], 0), rows - 1);
+    return in + (int64_t)src * ld_in;
+  };
+  for (int rr = 0; rr < nr; ++rr) {
+    const E* row = src_row(rr);
+    const int h = lead16(row, d_in);
+    row_to_lds(row, buf + rr * pitch + lds_shift<E>(h), d_in, h);
+  }
+  __syncthreads();
+  gather_staged<E>([&](int rr) -> const E* { return buf + rr * pitch + lds_shift<E>(lead16(src_row(rr), d_in)); },
+                   nr, t0, colmap, out, ld_out, d_in, d_out);
+}
+
+// The outputs of one multi-output gather: out[k][:, i] = in[:, colmap[k][i]].
+struct GatherOuts {
+  const int32_t* colmap[pxk::kGatherOuts];
+  void* out[pxk::kGatherOuts];
+  int64_t ld_out[pxk::kGatherOuts];
+  int d_out[pxk::kGatherOuts];
+  int count;
+};
+
+// k_permute_lds for several outputs from one input: each staged row is read
+// from HBM once and gathered into every output.
+template <typename E>
+__global__ __launch_bounds__(256) void k_permute_lds_multi(const E* __restrict__ in, int64_t ld_in, const GatherOuts go,
+                                                           int rows, int d_in, int rpw, int pitch) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* buf = reinterpret_cast<E*>(smem);
+  const int t0 = blockIdx.x * rpw;
+  const int nr = min(rpw, rows - t0);
+  auto src_row = [&](int rr) { return in + (int64_t)(t0 + rr) * ld_in; };
+  for (int rr = 0; rr < nr; ++rr) {
+    const E* row = src_row(rr);
+    const int h = lead16(row, d_in);
+    row_to_lds(row, buf + rr * pitch + lds_shift<E>(h), d_in, h);
+  }
+  __syncthreads();
+  for (int k = 0; k < go.count; ++k)
+    gather_staged<E>([&](int rr) -> const E* { return buf + rr * pitch + lds_shift<E>(lead16(src_row(rr), d_in)); },
+                     nr, t0, go.colmap[k], reinterpret_cast<E*>(go.out[k]), go.ld_out[k], d_in, go.d_out[k]);
 }
 
 // dst[c][r] = src[r][c] (bit copy) through a 64 x 64 LDS tile, so that both
@@ -943,6 +1063,43 @@ hipError_t permute(int dt, const void* in, int64_t ld_in, const int32_t* rowmap,
   return go(int8_t{});
 }
 
+hipError_t permute_multi(int dt, const void* in, int64_t ld_in, int count, const int32_t* const* colmap,
+                         void* const* out, const int64_t* ld_out, const int* d_out, int rows, int d_in, hipStream_t s) {
+  if (rows <= 0 || count <= 0) return hipSuccess;
+  if (count > kGatherOuts) return hipErrorInvalidValue;
+  const size_t es = dt_size(dt);
+  const size_t pitch_bytes = ((size_t)d_in * es + 15) / 16 * 16;
+  const int64_t pitch = stage_pitch(d_in, es);
+  const size_t budget = 64 * 1024, target = 8 * 1024;  // as for permute
+  if ((size_t)pitch * es > budget) {  // rows too long to stage: one gather per output
+    for (int k = 0; k < count; ++k) {
+      const hipError_t e = permute(dt, in, ld_in, nullptr, colmap[k], out[k], ld_out[k], rows, d_in, d_out[k], s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  GatherOuts go{};
+  for (int k = 0; k < count; ++k) {
+    if (d_out[k] <= 0) continue;
+    const int q = go.count++;
+    go.colmap[q] = colmap[k];
+    go.out[q] = out[k];
+    go.ld_out[q] = ld_out[k];
+    go.d_out[q] = d_out[k];
+  }
+  if (go.count == 0) return hipSuccess;
+  const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, target / pitch_bytes));
+  auto go_t = [&](auto tag) -> hipError_t {
+    using E = decltype(tag);
+    k_permute_lds_multi<E><<<cdiv(rows, rpw), 256, rpw * pitch * es, s>>>(reinterpret_cast<const E*>(in), ld_in, go,
+                                                                           rows, d_in, rpw, (int)pitch);
+    return hipGetLastError();
+  };
+  if (dt == F32) return go_t(float{});
+  if (dt == BF16) return go_t(bf16_t{});
+  return go_t(int8_t{});
+}
+
 hipError_t scatter(int dt, const void* in, int64_t ld_in, const int32_t* perm, void* out, int64_t ld_out, int rows,
                    int d, hipStream_t s) {
   if (rows <= 0 || d <= 0) return hipSuccess;
@@ -1090,21 +1247,36 @@ static hipError_t apply_bf16_tiled(const void* in, int64_t ld_in, int rows, int 
   return apply_t<DSq, TSq, bf16_t, bf16_t, bf16_t, bf16_t>(in, ld_in, rows, d, b, dT, cs, out, ld_out, s);
 }
 
+// the streamed whole blocks of the sides in `tb` (tb.first[count] blocks in all)
 template <int B, int RT, int S>
-static hipError_t apply_stream_t(const void* in, int64_t ld_in, int rows, int nbf, const void* dT, const float* cs,
-                                 void* out, int64_t ld_out, hipStream_t s) {
+static hipError_t apply_stream_t(const StreamSides& tb, int rows, bool cs, hipStream_t s) {
   using C = StreamCfg<B, RT, S>;
-  auto k = cs ? k_apply_stream<B, RT, S, true> : k_apply_stream<B, RT, S, false>;
+  const bool multi = tb.count > 1;
+  auto k = multi ? (cs ? k_apply_stream<B, RT, S, true, true> : k_apply_stream<B, RT, S, false, true>)
+                 : (cs ? k_apply_stream<B, RT, S, true, false> : k_apply_stream<B, RT, S, false, false>);
   hipError_t e = allow_lds(k, C::LDS);
   if (e != hipSuccess) return e;
-  const int64_t items = (int64_t)nbf * cdiv(rows, RT);
+  const int64_t items = (int64_t)tb.first[tb.count] * cdiv(rows, RT);
   // one workgroup per CU; pair lanes come in multiples of 8 (one share per XCD)
   const int pair_lanes = (int)(std::min<int64_t>(256 / C::NH, items) / 8 * 8);
   if (pair_lanes < 8 || items > INT32_MAX) return hipErrorInvalidValue;
-  k<<<pair_lanes * C::NH, C::NT, C::LDS, s>>>(reinterpret_cast<const bf16_t*>(in), ld_in, rows,
-                                                reinterpret_cast<const bf16_t*>(dT), cs, reinterpret_cast<bf16_t*>(out),
-                                                ld_out, (int)items, pair_lanes);
+  k<<<pair_lanes * C::NH, C::NT, C::LDS, s>>>(tb, rows, (int)items, pair_lanes);
   return hipGetLastError();
+}
+
+static StreamSides one_side(const void* in, int64_t ld_in, int nbf, const void* dT, const float* cs, void* out,
+                            int64_t ld_out) {
+  StreamSides tb{};
+  tb.in[0] = reinterpret_cast<const bf16_t*>(in);
+  tb.dT[0] = reinterpret_cast<const bf16_t*>(dT);
+  tb.cs[0] = cs;
+  tb.out[0] = reinterpret_cast<bf16_t*>(out);
+  tb.ld_in[0] = ld_in;
+  tb.ld_out[0] = ld_out;
+  tb.first[0] = 0;
+  tb.first[1] = nbf;
+  tb.count = 1;
+  return tb;
 }
 
 static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
@@ -1112,16 +1284,26 @@ static bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 1
 // bf16 block products: the streaming kernel for the whole blocks of 256 or 512
 // columns when there are enough row tiles to occupy the chip, the tiled kernel
 // for the rest (other block sizes, a partial last block, small inputs)
+constexpr int kStreamRT = 32;
+
+// whole blocks of this side can be streamed (the kernel addresses a row tile
+// with 32-bit byte offsets)
+static bool streamable(const void* in, int64_t ld_in, int d, int b, const void* dT, const float* cs, const void* out,
+                       int64_t ld_out) {
+  return (b == 256 || b == 512) && d / b > 0 && ld_in % 8 == 0 && ld_out % 8 == 0 && ld_in < (1 << 25) &&
+         ld_out < (1 << 25) && aligned16(in) && aligned16(out) && aligned16(dT) && (!cs || aligned16(cs));
+}
+
+static hipError_t apply_stream_sides(const StreamSides& tb, int rows, int b, bool cs, hipStream_t s) {
+  return b == 512 ? apply_stream_t<512, kStreamRT, 3>(tb, rows, cs, s) : apply_stream_t<256, kStreamRT, 4>(tb, rows, cs, s);
+}
+
 static hipError_t apply_bf16(const void* in, int64_t ld_in, int rows, int d, int b, const void* dT, const float* cs,
                              void* out, int64_t ld_out, hipStream_t s) {
   const int nbf = d / b;
-  constexpr int RT = 32;
-  // (the kernel addresses a row tile with 32-bit byte offsets)
-  if ((b == 256 || b == 512) && nbf > 0 && (int64_t)nbf * cdiv(rows, RT) >= 64 && ld_in % 8 == 0 &&
-      ld_out % 8 == 0 && ld_in < (1 << 25) && ld_out < (1 << 25) && aligned16(in) && aligned16(out) &&
-      aligned16(dT) && (!cs || aligned16(cs))) {
-    hipError_t e = b == 512 ? apply_stream_t<512, RT, 3>(in, ld_in, rows, nbf, dT, cs, out, ld_out, s)
-                            : apply_stream_t<256, RT, 4>(in, ld_in, rows, nbf, dT, cs, out, ld_out, s);
+  constexpr int RT = kStreamRT;
+  if (streamable(in, ld_in, d, b, dT, cs, out, ld_out) && (int64_t)nbf * cdiv(rows, RT) >= 64) {
+    hipError_t e = apply_stream_sides(one_side(in, ld_in, nbf, dT, cs, out, ld_out), rows, b, cs != nullptr, s);
     if (e != hipSuccess || nbf * b == d) return e;
     const int64_t kb = (int64_t)nbf * b;
     return apply_bf16_tiled(reinterpret_cast<const bf16_t*>(in) + kb, ld_in, rows, d - (int)kb, b,
@@ -1129,6 +1311,55 @@ static hipError_t apply_bf16(const void* in, int64_t ld_in, int rows, int d, int
                             reinterpret_cast<bf16_t*>(out) + kb, ld_out, s);
   }
   return apply_bf16_tiled(in, ld_in, rows, d, b, dT, cs, out, ld_out, s);
+}
+
+hipError_t apply_batch(int count, const ApplySide* sides, int rows, int b, hipStream_t s) {
+  if (rows <= 0 || count <= 0) return hipSuccess;
+  if (count > kApplySides) return hipErrorInvalidValue;
+  // the streamed whole blocks of the sides that apply() would stream share one launch (so every
+  // output is computed as apply() computes it); a side's partial last block, and every other side,
+  // take apply_bf16's other paths
+  auto in_stream = [&](const ApplySide& a) {
+    return streamable(a.in, a.ld_in, a.d, b, a.dT, a.colscale, a.out, a.ld_out) &&
+           (int64_t)(a.d / b) * cdiv(rows, kStreamRT) >= 64;
+  };
+  StreamSides tb{};
+  bool cs = false;
+  int64_t blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    const ApplySide& a = sides[i];
+    if (!in_stream(a)) continue;
+    const int q = tb.count++;
+    tb.in[q] = reinterpret_cast<const bf16_t*>(a.in);
+    tb.dT[q] = reinterpret_cast<const bf16_t*>(a.dT);
+    tb.cs[q] = a.colscale;
+    tb.out[q] = reinterpret_cast<bf16_t*>(a.out);
+    tb.ld_in[q] = a.ld_in;
+    tb.ld_out[q] = a.ld_out;
+    tb.first[q] = (int)blocks;
+    blocks += a.d / b;
+    cs = cs || a.colscale;
+  }
+  tb.first[tb.count] = (int)blocks;
+  if (tb.count > 0) {
+    const hipError_t e = apply_stream_sides(tb, rows, b, cs, s);
+    if (e != hipSuccess) return e;
+  }
+  for (int i = 0; i < count; ++i) {
+    const ApplySide& a = sides[i];
+    hipError_t e = hipSuccess;
+    if (in_stream(a)) {
+      const int64_t kb = (int64_t)(a.d / b) * b;
+      if (kb < a.d)
+        e = apply_bf16_tiled(reinterpret_cast<const bf16_t*>(a.in) + kb, a.ld_in, rows, a.d - (int)kb, b,
+                             reinterpret_cast<const bf16_t*>(a.dT) + kb * b, a.colscale ? a.colscale + kb : nullptr,
+                             reinterpret_cast<bf16_t*>(a.out) + kb, a.ld_out, s);
+    } else {
+      e = apply_bf16(a.in, a.ld_in, rows, a.d, b, a.dT, a.colscale, a.out, a.ld_out, s);
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t apply(int cdt, int in_dt, const void* in, int64_t ld_in, int rows, int d, int b, int dT_dt, const void* dT,
@@ -1188,6 +1419,83 @@ hipError_t gemm(int cdt, int a_dt, const void* A, int64_t lda, int b_dt, const v
     return b_kn ? gemm_t<void, TF, float, float, float, float, true>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s)
                 : gemm_t<void, TF, float, float, float, float, false>(A, lda, B, ldb, M, N, K, colscale, out, ldo, s);
   return hipErrorInvalidValue;
+}
+
+int gemm_launches(int count, const GemmProblem* p, int* launch_of) {
+  auto tiles_of = [](const GemmProblem& x) { return (int64_t)cdiv(x.M, 256) * cdiv(x.N, 256); };
+  // A problem that gives every CU a 256 x 256 tile runs alone, as gemm() runs it: next to another in
+  // one launch it would share the Infinity Cache with it, and the XCDs' contiguous shares of the
+  // launch would end at different times.  Smaller problems of equal K (equal work per tile) share a
+  // launch of 256 x 256 tiles when together they give every CU a tile; the rest run alone.
+  auto small = [&](const GemmProblem& x) { return x.M > 0 && x.N > 0 && tiles_of(x) < 256; };
+  for (int i = 0; i < count; ++i) launch_of[i] = -1;
+  int n = 0;
+  for (int i = 0; i < count; ++i) {
+    if (launch_of[i] >= 0 || !small(p[i])) continue;
+    int64_t tiles = 0;
+    int members = 0;
+    for (int j = i; j < count; ++j)
+      if (launch_of[j] < 0 && small(p[j]) && p[j].K == p[i].K) {
+        tiles += tiles_of(p[j]);
+        ++members;
+      }
+    if (members < 2 || tiles < 256) continue;
+    for (int j = i; j < count; ++j)
+      if (launch_of[j] < 0 && small(p[j]) && p[j].K == p[i].K) launch_of[j] = n;
+    ++n;
+  }
+  for (int i = 0; i < count; ++i)
+    if (launch_of[i] < 0) launch_of[i] = n++;
+  return n;
+}
+
+hipError_t gemm_batch(int count, const GemmProblem* p, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  if (count > kGemmProblems) return hipErrorInvalidValue;
+  int launch_of[kGemmProblems];
+  const int n = gemm_launches(count, p, launch_of);
+  for (int l = 0; l < n; ++l) {
+    GemmTable tb{};
+    int64_t tiles = 0;
+    int last = -1;
+    for (int i = 0; i < count; ++i) {
+      if (launch_of[i] != l) continue;
+      const GemmProblem& x = p[i];
+      last = i;
+      if (x.M <= 0 || x.N <= 0) continue;
+      const int q = tb.count++;
+      tb.A[q] = reinterpret_cast<const bf16_t*>(x.A);
+      tb.B[q] = reinterpret_cast<const bf16_t*>(x.B);
+      tb.cs[q] = x.colscale;
+      tb.out[q] = reinterpret_cast<bf16_t*>(x.out);
+      tb.lda[q] = x.lda;
+      tb.ldb[q] = x.ldb;
+      tb.ldo[q] = x.ldo;
+      tb.M[q] = x.M;
+      tb.N[q] = x.N;
+      tb.K[q] = x.K;
+      tb.first[q] = (int)tiles;
+      tiles += (int64_t)cdiv(x.M, 256) * cdiv(x.N, 256);
+    }
+    tb.first[tb.count] = (int)tiles;
+    hipError_t e = hipSuccess;
+    if (tb.count < 2) {
+      const GemmProblem& x = p[last];
+      e = gemm(BF16, BF16, x.A, x.lda, BF16, x.B, x.ldb, false, x.M, x.N, x.K, x.colscale, BF16, x.out, x.ldo, s);
+    } else {
+      using CD = DGemm;
+      using C = TGemmI;
+      const int lds = std::max(smem_bytes<C, bf16_t, bf16_t>(), dma_smem_bytes<CD>());
+      auto k = k_gemm_group<CD, C>;
+      e = allow_lds(k, lds);
+      if (e == hipSuccess) {
+        k<<<(unsigned)tiles, C::NT, lds, s>>>(tb);
+        e = hipGetLastError();
+      }
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename GT, typename WT>

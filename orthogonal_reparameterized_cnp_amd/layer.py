@@ -133,7 +133,8 @@ class PoetxLinear:
     def _act_dt(self) -> torch.dtype:
         return _TORCH_DT[self.act]
 
-    def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    def _fwd_args(self, X: torch.Tensor, Y: Optional[torch.Tensor]):
+        """Checked forward arguments: T, and Y (allocated if None); the workspace is sized for T."""
         if not isinstance(X, torch.Tensor) or X.dim() != 2:
             raise ValueError("X must be a 2-D tensor [T, m]")
         T = X.shape[0]
@@ -144,6 +145,10 @@ class PoetxLinear:
         self.reserve(T)
         if Y is None:
             Y = torch.empty(T, self.n, dtype=X.dtype, device=self.device)
+        return T, Y
+
+    def forward(self, X: torch.Tensor, Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        T, Y = self._fwd_args(X, Y)
         B.poetx_linear_fwd(self.desc, T, X, self.perm_R, self.perm_P, self.Wt, self.g_R, self.g_P, Y, self.H_save,
                            self.ws, self.ws.numel(), stream)
         self.T = T
@@ -276,6 +281,72 @@ class PoetxGroup:
                               lay.q_R, lay.q_P, lay.H_save, dX, self.dg, self.first[i], self.blocks, lay.ws,
                               lay.ws.numel(), stream)
         return dX
+
+    def _group_idx(self, idx):
+        idx = list(idx)
+        if not idx or len(idx) > B.POETX_MAX_GROUP:
+            raise ValueError(f"a group call takes 1 .. {B.POETX_MAX_GROUP} linears, got {len(idx)}")
+        if len(set(idx)) != len(idx) or any(not 0 <= i < len(self.layers) for i in idx):
+            raise ValueError(f"linear indices must be distinct and in [0, {len(self.layers)})")
+        return idx
+
+    def forward(self, idx, Xs, Ys=None, stream=None):
+        """Forwards of the linears `idx` (indices into the group) in shared launches
+        (poetx_linear_fwd_group), each output bit-identical to that linear's own forward.  Xs: one input
+        per linear, all with the same T (one tensor may serve several linears, as q, k and v share theirs);
+        Ys: outputs, or None to allocate them.  Returns the outputs."""
+        idx = self._group_idx(idx)
+        Ys = [None] * len(idx) if Ys is None else list(Ys)
+        if len(Xs) != len(idx) or len(Ys) != len(idx):
+            raise ValueError("one input and one output per linear")
+        calls, outs, T = [], [], None
+        for i, X, Y in zip(idx, Xs, Ys):
+            lay = self.layers[i]
+            t, Y = lay._fwd_args(X, Y)
+            if T is not None and t != T:
+                raise ValueError(f"every linear of a group call needs the same T ({T}), got {t}")
+            T = t
+            calls.append(dict(dsc=lay.desc, X=X, perm_R=lay.perm_R, perm_P=lay.perm_P, Wt=lay.Wt, g_R=lay.g_R,
+                              g_P=lay.g_P, Y=Y, H_save=lay.H_save, ws=lay.ws, ws_bytes=lay.ws.numel()))
+            outs.append(Y)
+        B.poetx_linear_fwd_group(calls, T, stream)
+        for i in idx:
+            self.layers[i].T = T
+        return outs
+
+    def backward_dx_many(self, idx, dZs, dXs=None, stream=None, Ys=None):
+        """backward_dx of the linears `idx` in shared launches (poetx_linear_bwd_dx_group; with batch_grads,
+        else one backward_dx each): dX of each, bit-identical to its own backward_dx.  dZs: one output
+        gradient per linear; dXs: outputs or None; Ys: the forwards' outputs (xout).  Returns the dX."""
+        idx = self._group_idx(idx)
+        n = len(idx)
+        dXs = [None] * n if dXs is None else list(dXs)
+        Ys = [None] * n if Ys is None else list(Ys)
+        if len(dZs) != n or len(dXs) != n or len(Ys) != n:
+            raise ValueError("one dZ, dX and Y entry per linear")
+        if not self.batch_grads:
+            return [self.backward_dx(i, dZ, dZ, dX, stream, Y) for i, dZ, dX, Y in zip(idx, dZs, dXs, Ys)]
+        T = dZs[0].shape[0] if isinstance(dZs[0], torch.Tensor) and dZs[0].dim() == 2 else None
+        if T is None:
+            raise ValueError("dZ must be a 2-D tensor [T, n]")
+        if self.rows is not None and self.rows != T:
+            raise ValueError(f"batch_grads: every linear's backward_dx needs the same T ({self.rows}), got {T}")
+        calls, outs = [], []
+        for i, dZ, dX, Y in zip(idx, dZs, dXs, Ys):
+            lay = self.layers[i]
+            lay._y_arg(Y)
+            lay.check_backward(T, dZ, Y, dX)
+            lay.reserve(T)
+            if dX is None:
+                dX = torch.empty(T, lay.m, dtype=dZ.dtype, device=self.device)
+            calls.append(dict(dsc=lay.desc, Y=lay._y_arg(Y), dZ=dZ, perm_R=lay.perm_R, perm_P=lay.perm_P, Wt=lay.Wt,
+                              g_R=lay.g_R, g_P=lay.g_P, H_save=lay.H_save, dX=dX, ws=lay.ws, ws_bytes=lay.ws.numel()))
+            outs.append(dX)
+        sides = B.poetx_linear_bwd_dx_group(calls, T, stream)
+        for i, sd in zip(idx, sides):
+            self.sides[i] = sd
+        self.rows = T
+        return outs
 
     def backward_q(self, dqs=None, stream=None):
         """dq of every side from the gradient state; dqs: [(dq_R, dq_P)] per linear (allocated if None)."""

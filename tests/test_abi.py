@@ -345,6 +345,40 @@ def test_bwd_dx_sides_statuses(L):
     assert call(perm=None) == B.POETX_E_NULL
 
 
+def test_group_call_statuses(L):
+    d = B.desc(320, 200, 64, "bf16", "bf16")
+    d32 = B.desc(320, 200, 32, "bf16", "bf16")
+    T = 64
+    wf = B.poetx_workspace_size(d, T, B.POETX_OP_FWD)
+    wb = B.poetx_workspace_size(d, T, B.POETX_OP_BWD)
+
+    def fwd(desc=d, X=FAKE, ws_bytes=wf):
+        return B.FwdCall(ctypes.pointer(desc), X, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes)
+
+    def bwd(desc=d, dZ=FAKE, ws_bytes=wb):
+        return B.BwdCall(ctypes.pointer(desc), None, dZ, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes)
+
+    def run_f(*calls, count=None):
+        arr = (B.FwdCall * max(len(calls), 1))(*calls)
+        return L.poetx_linear_fwd_group(len(calls) if count is None else count, arr, T, None)
+
+    def run_b(*calls, sides=True):
+        arr = (B.BwdCall * len(calls))(*calls)
+        sd = (B.GradSide * (2 * len(calls)))() if sides else None
+        return L.poetx_linear_bwd_dx_group(len(calls), arr, T, sd, None)
+
+    assert L.poetx_linear_fwd_group(1, None, T, None) == B.POETX_E_NULL
+    assert run_f(fwd(), count=0) == B.POETX_E_SHAPE
+    assert run_f(*[fwd()] * (B.POETX_MAX_GROUP + 1)) == B.POETX_E_SHAPE
+    assert run_f(fwd(), fwd(ws_bytes=wf - 1)) == B.POETX_E_WORKSPACE
+    assert run_f(fwd(), fwd(X=None)) == B.POETX_E_NULL
+    assert run_f(fwd(), fwd(desc=d32, ws_bytes=B.poetx_workspace_size(d32, T, B.POETX_OP_FWD))) == B.POETX_E_SHAPE
+    assert run_b(bwd(), sides=False) == B.POETX_E_NULL
+    assert run_b(bwd(), bwd(ws_bytes=wb - 1)) == B.POETX_E_WORKSPACE
+    assert run_b(bwd(), bwd(dZ=None)) == B.POETX_E_NULL
+    assert run_b(bwd(), bwd(desc=d32, ws_bytes=B.poetx_workspace_size(d32, T, B.POETX_OP_BWD))) == B.POETX_E_SHAPE
+
+
 def test_cnp_backward_reuse_statuses(L):
     d, b, bf = [320, 200], 64, B.DTYPES["bf16"]
     blocks = sum((x + b - 1) // b for x in d)

@@ -45,6 +45,7 @@ def test_llama8b_step_flops():
 def test_kernel_classes():
     k = bench.kernel_class
     assert k("void (anonymous namespace)::k_gemm<px::DCfg<256, 256, 64>>(...)") == "W~ contractions"
+    assert k("void (anonymous namespace)::k_gemm_group<px::DCfg<256, 256, 64>>(GemmTable)") == "W~ contractions"
     assert k("k_apply_stream<512, 32, 3, false>") == "block products"
     assert k("k_scatter_lds<unsigned short>") == "permutations"
     assert k("k_permute_lds<unsigned short>") == "permutations"

@@ -32,6 +32,22 @@ class Workload:
     meta: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
+    def input_groups(self) -> Tuple[Tuple[int, ...], ...]:
+        """The linears in layer order, grouped by the input they read: q, k and v share the attention
+        input and gate and up the MLP input; every other linear reads its own."""
+        shared = ({"q", "k", "v"}, {"gate", "up"})
+        groups, i = [], 0
+        while i < len(self.linears):
+            g = [i]
+            for s in shared:
+                if self.linears[i].name in s:
+                    while i + len(g) < len(self.linears) and self.linears[i + len(g)].name in s:
+                        g.append(i + len(g))
+            groups.append(tuple(g))
+            i += len(g)
+        return tuple(groups)
+
+    @property
     def flop_per_token_gemm(self) -> float:
         # fwd H = A W + bwd dA = dH W^T: 2 contractions of 2*m*n each
         return float(sum(4 * L.m * L.n for L in self.linears))
