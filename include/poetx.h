@@ -116,12 +116,14 @@ int64_t poetx_packed_len(int32_t b);
 size_t poetx_g_bytes(int32_t d, int32_t b, int32_t dtype);
 
 /* Bytes of the pre-merged weight buffer: values [m][ldw] of w_dtype, ldw =
- * round_up(n, 64), followed at offset round_up(m*ldw*size(w_dtype), 256) by
+ * round_up(n, 64) (columns n and up zero), followed at offset
+ * round_up(m*ldw*size(w_dtype), 256) by
  *  - POETX_I8: the fp32 column scales [ldw] in pre-merged column order;
  *  - POETX_BF16: the transposed copy [n][round_up(m, 64)] of the values
  *    (columns m and up zero), which the forward contraction reads so that
  *    both of its operands are contiguous along the summed index.
- * poetx_premerge and poetx_merge_reinit write every part. */
+ * poetx_premerge, poetx_merge_reinit and poetx_store_weight write every part;
+ * the contractions sum over the zero padding as well. */
 size_t poetx_weight_bytes(const poetx_layer_desc* desc);
 
 /* Bytes of the state the forward saves for the backward of the same T tokens.

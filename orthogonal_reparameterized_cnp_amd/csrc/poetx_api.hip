@@ -121,6 +121,19 @@ struct Plan {
 
 size_t g_slice(int d, int b, int dt) { return (size_t)nblocks(d, b) * b * b * dt_size(dt); }
 
+// The K of a bf16 W~ contraction: lead(K), a multiple of 64, so that the
+// direct-to-LDS loop serves ragged K too.  Both operands hold zeros in their
+// pitch padding [K, lead(K)) (the library writes them: the weight formats
+// and zero_pad below), so the extra products are exact zeros.
+int k_padded(int K, int act_dtype) { return act_dtype == POETX_BF16 ? (int)lead(K) : K; }
+
+// zeros in the pitch padding [d, lead(d)) of a [rows][lead(d)] activation operand that a W~
+// contraction reads over k_padded(d)
+hipError_t zero_pad(int act_dtype, void* p, int rows, int d, hipStream_t s) {
+  if (act_dtype != POETX_BF16 || lead(d) == d) return hipSuccess;
+  return zero_cols(act_dtype, p, lead(d), rows, d, (int)lead(d), s);
+}
+
 // sum over a side's blocks of r^2 and r^3 (algorithmic flop counts)
 double sum_r2(int d, int b) {
   const double r = d - (double)(nblocks(d, b) - 1) * b;
@@ -420,6 +433,7 @@ poetx_status poetx_premerge(const poetx_layer_desc* desc, const void* W0, int64_
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int m = desc->m, n = desc->n;
   PX_HIP(permute(desc->w_dtype, W0, ld_w0, perm_R, perm_P, Wt, lead(n), m, n, n, s));
+  PX_HIP(zero_cols(desc->w_dtype, Wt, lead(n), m, n, (int)lead(n), s));  // the pitch padding of the format
   if (has_weight_t(desc))
     PX_HIP(transpose(desc->w_dtype, Wt, lead(n), m, n, reinterpret_cast<char*>(Wt) + weight_t_offset(desc), lead(m), s));
   if (desc->w_dtype == POETX_I8) {
@@ -449,17 +463,18 @@ poetx_status xt_to_h(const poetx_layer_desc* desc, int64_t T, const void* Xt, co
   // A = Xt Diag(G_R)
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
            apply(at, at, Xt, ldm, rows, m, b, at, gR1, nullptr, at, A, ldm, s));
+  PX_HIP(zero_pad(at, A, rows, m, s));
   // H = A W~ (int8: codes times the column scale); bf16 weights are read from the W~^T copy, int8 codes
   // from their transpose widened to bf16 in the workspace (exact), so both take the same loop
   if (has_weight_t(desc)) {
     const void* Wtt = reinterpret_cast<const char*>(Wt) + weight_t_offset(desc);
     PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
-             gemm(at, at, A, ldm, wt, Wtt, ldm, false, rows, n, m, nullptr, at, H, ldn, s));
+             gemm(at, at, A, ldm, wt, Wtt, ldm, false, rows, n, k_padded(m, at), nullptr, at, H, ldn, s));
   } else if (wt == POETX_I8 && at == POETX_BF16 && Wb) {
     PX_TIMED(POETX_KC_GEMM, 0, 3.0 * m * n,
              widen_i8(reinterpret_cast<const int8_t*>(Wt), lead(n), m, n, true, reinterpret_cast<uint16_t*>(Wb), ldm, s));
     PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + 2.0 * m * n + es * rows * n,
-             gemm(at, at, A, ldm, POETX_BF16, Wb, ldm, false, rows, n, m, scale_t, at, H, ldn, s));
+             gemm(at, at, A, ldm, POETX_BF16, Wb, ldm, false, rows, n, k_padded(m, at), scale_t, at, H, ldn, s));
   } else {
     PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * m + wes * m * n + es * rows * n,
              gemm(at, at, A, ldm, wt, Wt, lead(n), true, rows, n, m, scale_t, at, H, ldn, s));
@@ -532,16 +547,17 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* Y,
   // dH = dZt Diag(G_P)^T (int8: times the column scale, ready for the code contraction)
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(n, b), 2.0 * rows * n * es + g_slice(n, b, at),
            apply(at, at, w.dZt, ldn, rows, n, b, at, g_P, scale_t, at, w.dH, ldn, s));
+  PX_HIP(zero_pad(at, w.dH, rows, n, s));
   // dA = dH W~^T (int8: the codes widened to bf16 in the workspace first, exact)
   if (wt == POETX_I8 && at == POETX_BF16 && w.Wb) {
     PX_TIMED(POETX_KC_GEMM, 0, 3.0 * m * n,
              widen_i8(reinterpret_cast<const int8_t*>(Wt), lead(n), m, n, false, reinterpret_cast<uint16_t*>(w.Wb), ldn,
                       s));
     PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * n + 2.0 * m * n + es * rows * m,
-             gemm(at, at, w.dH, ldn, POETX_BF16, w.Wb, ldn, false, rows, m, n, nullptr, at, w.dA, ldm, s));
+             gemm(at, at, w.dH, ldn, POETX_BF16, w.Wb, ldn, false, rows, m, k_padded(n, at), nullptr, at, w.dA, ldm, s));
   } else {
     PX_TIMED(POETX_KC_GEMM, 2.0 * rows * m * n, es * rows * n + wes * m * n + es * rows * m,
-             gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, n, nullptr, at, w.dA, ldm, s));
+             gemm(at, at, w.dH, ldn, wt, Wt, lead(n), false, rows, m, k_padded(n, at), nullptr, at, w.dA, ldm, s));
   }
   // block gradients of both sides over all tokens: dG_R = Xt^T dA, dG_P = H^T dZt, with Xt and H
   // from the forward's saved state.  Xmem recomputes H from Xt, into the buffers that dH (consumed
@@ -752,7 +768,7 @@ poetx_status poetx_linear_fwd_group(int32_t count, const poetx_fwd_call* calls, 
       scale_t = reinterpret_cast<const float*>(reinterpret_cast<const char*>(c.Wt) + weight_scale_offset(d));
       Bw = w[i].Wb;
     }
-    gp[i] = GemmProblem{w[i].A, ldm, Bw, ldm, rows, n, m, scale_t, H[i], ldn};
+    gp[i] = GemmProblem{w[i].A, ldm, Bw, ldm, rows, n, k_padded(m, BF16), scale_t, H[i], ldn};
     fl_g[i] = 2.0 * rows * m * n;
     by_g[i] = 2.0 * rows * m + 2.0 * m * n + 2.0 * rows * n;
   }
@@ -783,6 +799,7 @@ poetx_status poetx_linear_fwd_group(int32_t count, const poetx_fwd_call* calls, 
   }
   // A = Xt Diag(G_R) for every linear
   PX_TIMED(POETX_KC_APPLY, fl_r, by_r, apply_batch(count, sr, rows, b, s));
+  for (int i = 0; i < count; ++i) PX_HIP(zero_pad(BF16, w[i].A, rows, calls[i].desc->m, s));
   for (int i = 0; i < count; ++i) {
     const poetx_layer_desc* d = calls[i].desc;
     if (d->w_dtype == POETX_I8)
@@ -856,7 +873,8 @@ poetx_status poetx_linear_bwd_dx_group(int32_t count, const poetx_bwd_call* call
     // dH = dZt Diag(G_P)^T (int8: times the column scale); dA = dH W~^T (int8: the codes widened to bf16)
     sp[i] = ApplySide{w[i].dZt, ldn, n, c.g_P, scale_t, w[i].dH, ldn};
     const void* Bw = d->w_dtype == POETX_I8 ? w[i].Wb : c.Wt;
-    gp[i] = GemmProblem{w[i].dH, ldn, Bw, d->w_dtype == POETX_I8 ? ldn : lead(n), rows, m, n, nullptr, w[i].dA, ldm};
+    gp[i] = GemmProblem{w[i].dH, ldn, Bw, d->w_dtype == POETX_I8 ? ldn : lead(n), rows, m, k_padded(n, BF16), nullptr,
+                        w[i].dA, ldm};
     // dXt = dA Diag(G_R)^T
     sr[i] = ApplySide{w[i].dA, ldm, m, c.g_R, nullptr, w[i].dXt, ldm};
     fl_p += 2.0 * rows * sum_r2(n, b);
@@ -867,6 +885,7 @@ poetx_status poetx_linear_bwd_dx_group(int32_t count, const poetx_bwd_call* call
     by_g[i] = 2.0 * rows * n + (d->w_dtype == POETX_I8 ? 2.0 : (double)dt_size(d->w_dtype)) * m * n + 2.0 * rows * m;
   }
   PX_TIMED(POETX_KC_APPLY, fl_p, by_p, apply_batch(count, sp, rows, b, s));
+  for (int i = 0; i < count; ++i) PX_HIP(zero_pad(BF16, w[i].dH, rows, calls[i].desc->n, s));
   for (int i = 0; i < count; ++i) {
     const poetx_layer_desc* d = calls[i].desc;
     if (d->w_dtype == POETX_I8)
@@ -1043,6 +1062,7 @@ poetx_status poetx_merge_reinit(const poetx_layer_desc* desc, void* Wt, int32_t*
     PX_HIP(col_absmax(w.Mq, ldw, m, n, w.amax, s));
   }
   PX_HIP(store_weight(w.Mq, ldw, m, n, wt, Wt, ldw, w.amax, scale_t, s));
+  PX_HIP(zero_cols(wt, Wt, ldw, m, n, (int)ldw, s));
   if (has_weight_t(desc))
     PX_HIP(transpose(wt, Wt, ldw, m, n, reinterpret_cast<char*>(Wt) + weight_t_offset(desc), lead(m), s));
   PX_HIP(hipMemcpyAsync(perm_R, w.newR, (size_t)m * 4, hipMemcpyDeviceToDevice, s));
@@ -1506,6 +1526,7 @@ poetx_status poetx_store_weight(const poetx_layer_desc* desc, const float* W, in
     PX_HIP(col_absmax(W, ldw, m, n, amax, s));
   }
   PX_HIP(store_weight(W, ldw, m, n, wt, Wt, lead(n), amax, scale_t, s));
+  PX_HIP(zero_cols(wt, Wt, lead(n), m, n, (int)lead(n), s));
   if (has_weight_t(desc))
     PX_HIP(transpose(wt, Wt, lead(n), m, n, reinterpret_cast<char*>(Wt) + weight_t_offset(desc), lead(m), s));
   return POETX_OK;

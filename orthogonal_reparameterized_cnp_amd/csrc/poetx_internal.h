@@ -152,6 +152,8 @@ hipError_t col_absmax(const float* M, int64_t ld, int rows, int n, uint32_t* ama
 hipError_t store_weight(const float* M, int64_t ld, int rows, int n, int w_dt, void* W, int64_t ldw,
                         const uint32_t* amax, float* wscale, hipStream_t s);
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s);
+// p[r][c0 .. c1) = 0 for r < rows of a [rows][ld] matrix of dtype dt
+hipError_t zero_cols(int dt, void* p, int64_t ld, int rows, int c0, int c1, hipStream_t s);
 
 // Adam step with decoupled weight decay on `count` fp32 arrays in place:
 // side i updates len[i] slots of q[i], m1[i], m2[i] from the gradient g[i].

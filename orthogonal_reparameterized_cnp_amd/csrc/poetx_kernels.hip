@@ -1011,6 +1011,14 @@ __global__ void k_store_weight(const float* __restrict__ M, int64_t ld, int rows
   }
 }
 
+// p[r][c0 .. c0 + w) = 0 for r < rows (row pitch ld elements)
+template <typename E>
+__global__ void k_zero_cols(E* __restrict__ p, int64_t ld, int rows, int c0, int w) {
+  const int64_t total = (int64_t)rows * w;
+  for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < total; u += (int64_t)gridDim.x * blockDim.x)
+    p[(u / w) * ld + c0 + u % w] = E(0);
+}
+
 __global__ void k_fill_zero(uint8_t* __restrict__ p, size_t bytes) {
   const size_t n16 = bytes / 16;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -1026,6 +1034,20 @@ __global__ void k_fill_zero(uint8_t* __restrict__ p, size_t bytes) {
 // launchers
 // ============================================================================
 namespace pxk {
+
+hipError_t zero_cols(int dt, void* p, int64_t ld, int rows, int c0, int c1, hipStream_t s) {
+  if (rows <= 0 || c1 <= c0) return hipSuccess;
+  if (c0 < 0 || c1 > ld) return hipErrorInvalidValue;
+  const int w = c1 - c0;
+  const unsigned grid = (unsigned)std::min<int64_t>(cdiv((int64_t)rows * w, 256), 4096);
+  if (dt == F32)
+    k_zero_cols<float><<<grid, 256, 0, s>>>(reinterpret_cast<float*>(p), ld, rows, c0, w);
+  else if (dt == BF16)
+    k_zero_cols<bf16_t><<<grid, 256, 0, s>>>(reinterpret_cast<bf16_t*>(p), ld, rows, c0, w);
+  else
+    k_zero_cols<int8_t><<<grid, 256, 0, s>>>(reinterpret_cast<int8_t*>(p), ld, rows, c0, w);
+  return hipGetLastError();
+}
 
 hipError_t fill_zero(void* p, size_t bytes, hipStream_t s) {
   if (bytes == 0) return hipSuccess;
@@ -1162,6 +1184,10 @@ hipError_t widen_i8(const int8_t* src, int64_t ld_src, int rows, int cols, bool 
     if (ld_dst < cols) return hipErrorInvalidValue;
     const int64_t units = (int64_t)rows * cdiv(cols, 16);
     k_widen_i8<<<(unsigned)std::min<int64_t>(cdiv(units, 256), 8192), 256, 0, s>>>(src, ld_src, rows, cols, dst, ld_dst);
+    // columns [cols, ld_dst) zero as well, as in the transposed form
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return zero_cols(BF16, dst, ld_dst, rows, cols, (int)ld_dst, s);
   }
   return hipGetLastError();
 }
