@@ -8,8 +8,9 @@ The cases reach: one contraction alone next to two grouped ones, forward and bac
 8192 tokens, widths 2048 / 1024 / 1024 under 1024 inputs; the backward groups k and v and leaves q, of
 another K, alone), one input shared by every linear of a call, int8 weights (widened codes, column
 scales in the grouped launch, once next to a bf16 linear without scales), a group of contractions too
-small to launch together, sides too short to stream (ragged T, partial blocks), the Xmem and Xout
-backwards, and fp32 layers (one call per linear)."""
+small to launch together, streamed sides with a partial last block and a ragged K (1300 = 5 x 256 + 20,
+contracted over its zero padding to 1344), sides too short to stream (ragged T, partial blocks), the
+Xmem and Xout backwards, and fp32 layers (one call per linear)."""
 
 import pytest
 import torch
@@ -29,6 +30,7 @@ CASES = [
     ("bf16", "xfast", 512, [(1024, 1024, "i8"), (1024, 1024, "i8")], 8192, True),
     ("bf16", "xfast", 512, [(1024, 1024, "i8"), (1024, 1024, "bf16")], 8192, False),
     ("bf16", "xfast", 512, [(4096, 1024, "bf16"), (1024, 4096, "bf16")], 2048, False),
+    ("bf16", "xfast", 256, [(1300, 600, "bf16"), (1300, 1100, "bf16")], 2048, True),
     ("bf16", "xmem", 256, [(600, 520, "bf16"), (256, 300, "bf16")], 300, False),
     ("bf16", "xout", 512, [(1024, 1536, "bf16"), (600, 520, "bf16")], 256, False),
     ("f32", "xfast", 32, [(96, 50, "f32"), (33, 64, "f32")], 70, False),
