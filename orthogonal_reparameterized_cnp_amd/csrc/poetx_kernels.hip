@@ -755,21 +755,44 @@ __global__ __launch_bounds__(256) void k_widen_i8(const int8_t* __restrict__ src
   }
 }
 
+// Transposed: a 64 x 64 tile of codes per workgroup.  Each thread reads 16
+// codes of one source row (one 16-byte load where the row piece is whole and
+// aligned), writes them widened into the LDS tile t[c][r] (bf16 bits, rows of
+// 64 + 8 elements), and then stores two 16-byte pieces of destination rows:
+// 8 consecutive r of one c each.
 __global__ __launch_bounds__(256) void k_widen_i8_t(const int8_t* __restrict__ src, int64_t ld_src, int rows, int cols,
                                                     bf16_t* __restrict__ dst, int64_t ld_dst) {
-  __shared__ float t[64][65];
+  constexpr int P = 64 + 8;
+  __shared__ __align__(16) uint16_t t[64 * P];
   const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  const int x = threadIdx.x & 63, y = threadIdx.x >> 6;
+  {
+    const int r = threadIdx.x >> 2, cq = (threadIdx.x & 3) * 16;  // source row r0 + r, columns c0 + cq .. + 15
+    const int8_t* a = src + (int64_t)(r0 + r) * ld_src + c0 + cq;
+    int8_t v[16];
+    if (r0 + r < rows && c0 + cq + 16 <= cols && reinterpret_cast<uintptr_t>(a) % 16 == 0) {
+      const int4 w = *reinterpret_cast<const int4*>(a);
+      __builtin_memcpy(v, &w, 16);
+    } else {
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int r = r0 + y + 4 * k, c = c0 + x;
-    t[y + 4 * k][x] = (r < rows && c < cols) ? (float)src[(int64_t)r * ld_src + c] : 0.f;
+      for (int e = 0; e < 16; ++e) v[e] = (r0 + r < rows && c0 + cq + e < cols) ? a[e] : (int8_t)0;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[(cq + e) * P + r] = f2bf((float)v[e]);
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int c = c0 + y + 4 * k, r = r0 + x;
-    if (c < cols && r < ld_dst) dst[(int64_t)c * ld_dst + r] = f2bf(t[x][y + 4 * k]);
+  for (int h = 0; h < 2; ++h) {
+    const int u = threadIdx.x + 256 * h, c = u >> 3, rq = (u & 7) * 8;  // destination row c0 + c, columns r0 + rq .. + 7
+    if (c0 + c >= cols) continue;
+    bf16_t* o = dst + (int64_t)(c0 + c) * ld_dst + r0 + rq;
+    const uint4 w = *reinterpret_cast<const uint4*>(&t[c * P + rq]);
+    if (r0 + rq + 8 <= ld_dst && reinterpret_cast<uintptr_t>(o) % 16 == 0) {
+      *reinterpret_cast<uint4*>(o) = w;
+    } else {
+      uint16_t e8[8];
+      __builtin_memcpy(e8, &w, 16);
+      for (int e = 0; e < 8 && r0 + rq + e < ld_dst; ++e) reinterpret_cast<uint16_t*>(o)[e] = e8[e];
+    }
   }
 }
 
