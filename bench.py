@@ -425,6 +425,11 @@ class WorkloadStep:
         # launches, their W~ contractions in one launch where that fills the GPU); bit-identical outputs
         self.grouped = grouped and batch_grads
         self.calls = wl.input_groups if self.grouped else tuple((i,) for i in range(len(wl.linears)))
+        if self.grouped:
+            # the linears of a call read one input: they share its gradient, the sum of theirs
+            for g in self.calls:
+                for i in g[1:]:
+                    self.dXs[i] = self.dXs[g[0]]
         # Adam on every side's packed q (lr small enough that the timed steps stay near the start)
         self.opt = PoetxAdam(self.layers, lr=1e-5)
         self.optimizer = optimizer
@@ -687,7 +692,8 @@ def main():
             "mode": args.mode,
             "optimizer_in_step": "adam" if args.optimizer else None,
             "block_grads": args.grads,
-            "calls": " | ".join(",".join(wl.linears[i].name for i in g) for g in ws.calls),
+            "calls": " | ".join(",".join(wl.linears[i].name for i in g) for g in ws.calls)
+                     + (" (one input per call, its gradient the sum over the call's linears)" if ws.grouped else ""),
             "launch": "hip graph replay" if args.graph else "eager",
         },
         "tflops": total_f / (ms * 1e-3) / 1e12,

@@ -409,7 +409,10 @@ typedef struct poetx_bwd_call {
  * poetx_linear_bwd_dx_sides of calls[0 .. count) (a HOST array), T rows each:
  * dX of every linear, and the operands of its block gradients in
  * sides[2 i] (R) and sides[2 i + 1] (P) (a HOST array of 2 count), valid
- * until that linear's H_save or ws is written again.  Errors as for
+ * until that linear's H_save or ws is written again.  Calls that pass the same
+ * dX (linears that read one input) receive the sum of their input gradients,
+ * accumulated in fp32 in call order and rounded once to act_dtype; they must
+ * share m (at most 16384) and act_dtype.  Errors as for
  * poetx_linear_fwd_group, with each call's errors as for
  * poetx_linear_bwd_dx_sides.
  */

@@ -534,7 +534,8 @@ namespace {
 poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* Y, const void* dZ,
                          const int32_t* perm_R, const int32_t* perm_P, const void* Wt, const void* g_R,
                          const void* g_P, const float* q_R, const float* q_P, const void* H_save, void* dX, void* dg,
-                         int64_t first, int64_t total, const BwdWs& w, hipStream_t s, CnpSide* defer = nullptr) {
+                         int64_t first, int64_t total, const BwdWs& w, hipStream_t s, CnpSide* defer = nullptr,
+                         bool scatter_dx = true) {
   const int m = desc->m, n = desc->n, b = desc->b, at = desc->act_dtype, wt = desc->w_dtype;
   const int rows = (int)T;
   const int64_t ldm = lead(m), ldn = lead(n);
@@ -587,8 +588,32 @@ poetx_status bwd_dx_core(const poetx_layer_desc* desc, int64_t T, const void* Y,
   // dXt = dA Diag(G_R)^T;  dX[:, perm_R] = dXt
   PX_TIMED(POETX_KC_APPLY, 2.0 * rows * sum_r2(m, b), 2.0 * rows * m * es + g_slice(m, b, at),
            apply(at, at, w.dA, ldm, rows, m, b, at, g_R, nullptr, at, w.dXt, ldm, s));
-  if (rows > 0)
+  if (rows > 0 && scatter_dx)
     PX_TIMED(POETX_KC_PERMUTE, 0, 2.0 * rows * m * es, scatter(at, w.dXt, ldm, perm_R, dX, m, rows, m, s));
+  return POETX_OK;
+}
+
+// dX[:, perm_R] = dXt of every call of a backward group; the calls that pass one dX tensor (they
+// read one input) write the sum of their input gradients, accumulated in fp32 and rounded once
+poetx_status scatter_group_dx(int count, const poetx_bwd_call* calls, const BwdWs* w, int rows, hipStream_t s) {
+  bool done[POETX_MAX_GROUP] = {};
+  for (int i = 0; i < count; ++i) {
+    if (done[i]) continue;
+    const int m = calls[i].desc->m, at = calls[i].desc->act_dtype;
+    const void* in[POETX_MAX_GROUP];
+    int64_t ld[POETX_MAX_GROUP];
+    const int32_t* pm[POETX_MAX_GROUP];
+    int nm = 0;
+    for (int j = i; j < count; ++j) {
+      if (done[j] || calls[j].dX != calls[i].dX) continue;
+      done[j] = true;
+      in[nm] = w[j].dXt;
+      ld[nm] = lead(m);
+      pm[nm++] = calls[j].perm_R;
+    }
+    PX_TIMED(POETX_KC_PERMUTE, 0, (double)dt_size(at) * rows * m * (nm + 1),
+             scatter_sum(at, nm, in, ld, pm, calls[i].dX, m, rows, m, s));
+  }
   return POETX_OK;
 }
 
@@ -831,6 +856,10 @@ poetx_status poetx_linear_bwd_dx_group(int32_t count, const poetx_bwd_call* call
                                       c.H_save, c.dX, c.ws, c.ws_bytes, false);
     if (st != POETX_OK) return st;
     if (c.desc->b != calls[0].desc->b) return fail(POETX_E_SHAPE, "the linears of a group must share b");
+    for (int j = 0; j < i; ++j)
+      if (T > 0 && calls[j].dX == c.dX &&
+          (calls[j].desc->m != c.desc->m || calls[j].desc->act_dtype != c.desc->act_dtype || c.desc->m > 16384))
+        return fail(POETX_E_SHAPE, "calls that share dX must share m (at most 16384) and act_dtype");
     bf16 = bf16 && c.desc->act_dtype == POETX_BF16;
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -841,17 +870,17 @@ poetx_status poetx_linear_bwd_dx_group(int32_t count, const poetx_bwd_call* call
     w[i] = plan_bwd(q, calls[i].desc, T);
   }
   if (!bf16 || T == 0) {
-    // fp32 layers (and no tokens): one backward per linear
+    // fp32 layers (and no tokens): one backward per linear, the scatters to dX as for the group
     for (int i = 0; i < count; ++i) {
       const poetx_bwd_call& c = calls[i];
       CnpSide cs[2];
       const poetx_status st = bwd_dx_core(c.desc, T, c.Y, c.dZ, c.perm_R, c.perm_P, c.Wt, c.g_R, c.g_P, nullptr,
-                                          nullptr, c.H_save, c.dX, nullptr, 0, 0, w[i], s, cs);
+                                          nullptr, c.H_save, c.dX, nullptr, 0, 0, w[i], s, cs, false);
       if (st != POETX_OK) return st;
       for (int k = 0; k < 2; ++k)
         sides[2 * i + k] = poetx_grad_side{cs[k].A, cs[k].lda, cs[k].B, cs[k].ldb, cs[k].d};
     }
-    return POETX_OK;
+    return T > 0 ? scatter_group_dx(count, calls, w, (int)T, s) : POETX_OK;
   }
   const int rows = (int)T, b = calls[0].desc->b;
   ApplySide sp[POETX_MAX_GROUP], sr[POETX_MAX_GROUP];
@@ -919,12 +948,7 @@ poetx_status poetx_linear_bwd_dx_group(int32_t count, const poetx_bwd_call* call
     sides[2 * i + 1] = poetx_grad_side{H, ldn, w[i].dZt, ldn, n};
   }
   PX_TIMED(POETX_KC_APPLY, fl_r, by_r, apply_batch(count, sr, rows, b, s));
-  for (int i = 0; i < count; ++i) {
-    const int m = calls[i].desc->m;
-    PX_TIMED(POETX_KC_PERMUTE, 0, 4.0 * rows * m,
-             scatter(BF16, w[i].dXt, lead(m), calls[i].perm_R, calls[i].dX, m, rows, m, s));
-  }
-  return POETX_OK;
+  return scatter_group_dx(count, calls, w, rows, s);
 }
 
 size_t poetx_block_grads_workspace_size(int32_t count, const int32_t* d, int64_t rows, int32_t b, int32_t dtype) {

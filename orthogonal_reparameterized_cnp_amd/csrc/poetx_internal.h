@@ -44,6 +44,10 @@ hipError_t replace_cols(int dt, const void* in, int64_t ld_in, const void* src, 
 constexpr int kGatherOuts = 8;
 hipError_t permute_multi(int dt, const void* in, int64_t ld_in, int count, const int32_t* const* colmap,
                          void* const* out, const int64_t* ld_out, const int* d_out, int rows, int d_in, hipStream_t s);
+// out[:, perm[k][i]] = sum over k < count of in[k][:, i] (in order, fp32, rounded once to dt; count
+// 1 .. kGatherOuts; rows of up to 16 K fp32 values)
+hipError_t scatter_sum(int dt, int count, const void* const* in, const int64_t* ld_in, const int32_t* const* perm,
+                       void* out, int64_t ld_out, int rows, int d, hipStream_t s);
 // inv[perm[i]] = i
 hipError_t inverse_perm(const int32_t* perm, int d, int32_t* inv, hipStream_t s);
 // out[i] = a[b[i]]

@@ -858,6 +858,71 @@ __global__ __launch_bounds__(256) void k_scatter_lds(const E* __restrict__ in, i
   }
 }
 
+// The inputs of one summed scatter: out[:, perm[k][i]] += in[k][:, i].
+struct ScatterIns {
+  const void* in[pxk::kGatherOuts];
+  int64_t ld_in[pxk::kGatherOuts];
+  const int32_t* perm[pxk::kGatherOuts];
+  int count;
+};
+
+// Summed row scatter, out[t][perm_k[i]] = sum over k of in_k[t][i] (k in
+// order, in fp32, rounded once): each output row is accumulated in an fp32
+// LDS row, every input adding its row at its permuted positions (a
+// permutation touches every position once, so the adds of one input never
+// collide), and leaves with 16-byte stores.  Indices are clamped into [0, d).
+template <typename E>
+__global__ __launch_bounds__(256) void k_scatter_sum_lds(const ScatterIns si, E* __restrict__ out, int64_t ld_out,
+                                                         int rows, int d, int rpw, int pitch) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* acc = reinterpret_cast<float*>(smem);
+  constexpr int V = 16 / sizeof(E);
+  const int t0 = blockIdx.x * rpw;
+  const int nr = min(rpw, rows - t0);
+  for (int i = threadIdx.x; i < nr * pitch; i += blockDim.x) acc[i] = 0.f;
+  __syncthreads();
+  for (int k = 0; k < si.count; ++k) {
+    const E* in = reinterpret_cast<const E*>(si.in[k]);
+    const int32_t* perm = si.perm[k];
+    const bool vin = (reinterpret_cast<uintptr_t>(in) % 16 == 0) && (si.ld_in[k] % V == 0) &&
+                     (reinterpret_cast<uintptr_t>(perm) % 16 == 0);
+    const int dv = vin ? d / V : 0;
+    for (int rr = 0; rr < nr; ++rr) {
+      const E* row = in + (int64_t)(t0 + rr) * si.ld_in[k];
+      float* a = acc + rr * pitch;
+      for (int c = threadIdx.x; c < dv; c += blockDim.x) {
+        const uint4 v = reinterpret_cast<const uint4*>(row)[c];
+        E vals[V];
+        __builtin_memcpy(vals, &v, 16);
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q) {
+          const int4 w = reinterpret_cast<const int4*>(perm + c * V)[q];
+          a[min(max(w.x, 0), d - 1)] += to_f32(vals[4 * q]);
+          a[min(max(w.y, 0), d - 1)] += to_f32(vals[4 * q + 1]);
+          a[min(max(w.z, 0), d - 1)] += to_f32(vals[4 * q + 2]);
+          a[min(max(w.w, 0), d - 1)] += to_f32(vals[4 * q + 3]);
+        }
+      }
+      for (int i = dv * V + threadIdx.x; i < d; i += blockDim.x) a[min(max(perm[i], 0), d - 1)] += to_f32(row[i]);
+    }
+    __syncthreads();
+  }
+  for (int rr = 0; rr < nr; ++rr) {
+    E* o = out + (int64_t)(t0 + rr) * ld_out;
+    const float* a = acc + rr * pitch;
+    const int h = lead16(o, d);
+    for (int i = threadIdx.x; i < h; i += blockDim.x) o[i] = from_f32<E>(a[i]);
+    const int nb = (d - h) / V, tail = h + nb * V;
+    for (int c = threadIdx.x; c < nb; c += blockDim.x) {
+      E vals[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) vals[e] = from_f32<E>(a[h + c * V + e]);
+      *reinterpret_cast<uint4*>(o + h + c * V) = *reinterpret_cast<const uint4*>(vals);
+    }
+    for (int i = tail + threadIdx.x; i < d; i += blockDim.x) o[i] = from_f32<E>(a[i]);
+  }
+}
+
 // out[t] = in[t] except out[t][idx[i]] = src[t][i] for i < b: each row of `in`
 // is staged in LDS with 16-byte loads, the b values are written over it at
 // their positions, and the row leaves with 16-byte stores (one pass over the
@@ -1143,6 +1208,33 @@ hipError_t permute_multi(int dt, const void* in, int64_t ld_in, int count, const
   if (dt == F32) return go_t(float{});
   if (dt == BF16) return go_t(bf16_t{});
   return go_t(int8_t{});
+}
+
+hipError_t scatter_sum(int dt, int count, const void* const* in, const int64_t* ld_in, const int32_t* const* perm,
+                       void* out, int64_t ld_out, int rows, int d, hipStream_t s) {
+  if (rows <= 0 || d <= 0) return hipSuccess;
+  if (count < 1 || count > kGatherOuts) return hipErrorInvalidValue;
+  if (count == 1) return scatter(dt, in[0], ld_in[0], perm[0], out, ld_out, rows, d, s);
+  const size_t pitch = ((size_t)d + 3) / 4 * 4;  // fp32 row, 16-byte aligned
+  const size_t budget = 64 * 1024, target = 16 * 1024;
+  if (pitch * 4 > budget) return hipErrorInvalidValue;
+  ScatterIns si{};
+  for (int k = 0; k < count; ++k) {
+    si.in[k] = in[k];
+    si.ld_in[k] = ld_in[k];
+    si.perm[k] = perm[k];
+  }
+  si.count = count;
+  const int rpw = (int)std::max<size_t>(1, std::min<size_t>(16, target / (pitch * 4)));
+  auto go = [&](auto tag) -> hipError_t {
+    using E = decltype(tag);
+    k_scatter_sum_lds<E><<<cdiv(rows, rpw), 256, rpw * pitch * 4, s>>>(si, reinterpret_cast<E*>(out), ld_out, rows, d,
+                                                                        rpw, (int)pitch);
+    return hipGetLastError();
+  };
+  if (dt == F32) return go(float{});
+  if (dt == BF16) return go(bf16_t{});
+  return hipErrorInvalidValue;
 }
 
 hipError_t scatter(int dt, const void* in, int64_t ld_in, const int32_t* perm, void* out, int64_t ld_out, int rows,

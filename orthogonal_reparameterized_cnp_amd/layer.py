@@ -317,7 +317,9 @@ class PoetxGroup:
     def backward_dx_many(self, idx, dZs, dXs=None, stream=None, Ys=None):
         """backward_dx of the linears `idx` in shared launches (poetx_linear_bwd_dx_group; with batch_grads,
         else one backward_dx each): dX of each, bit-identical to its own backward_dx.  dZs: one output
-        gradient per linear; dXs: outputs or None; Ys: the forwards' outputs (xout).  Returns the dX."""
+        gradient per linear; dXs: outputs or None; Ys: the forwards' outputs (xout).  Linears given the
+        same dX tensor (they read one input) receive the sum of their input gradients, accumulated in
+        fp32 and rounded once (with batch_grads).  Returns the dX."""
         idx = self._group_idx(idx)
         n = len(idx)
         dXs = [None] * n if dXs is None else list(dXs)
@@ -325,6 +327,8 @@ class PoetxGroup:
         if len(dZs) != n or len(dXs) != n or len(Ys) != n:
             raise ValueError("one dZ, dX and Y entry per linear")
         if not self.batch_grads:
+            if any(dX is not None and sum(dX is d for d in dXs) > 1 for dX in dXs):
+                raise ValueError("a dX shared by several linears (their summed input gradient) needs batch_grads")
             return [self.backward_dx(i, dZ, dZ, dX, stream, Y) for i, dZ, dX, Y in zip(idx, dZs, dXs, Ys)]
         T = dZs[0].shape[0] if isinstance(dZs[0], torch.Tensor) and dZs[0].dim() == 2 else None
         if T is None:

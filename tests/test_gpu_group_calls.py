@@ -83,3 +83,44 @@ def test_group_call_arguments():
     group.backward_q()
     torch.cuda.synchronize()
     assert dX0.shape == (64, 128) and dX1.shape == (64, 64)
+
+
+@pytest.mark.parametrize(
+    "act,b,shapes,T",
+    [("bf16", 512, [(1024, 2048), (1024, 1024), (1024, 1024)], 1024), ("bf16", 256, [(600, 520), (600, 300)], 300),
+     ("f32", 32, [(96, 50), (96, 64)], 70)],
+)
+def test_group_shared_dx_is_the_sum(act, b, shapes, T):
+    """Linears that read one input and pass one dX tensor receive the sum of their input gradients: within
+    the rounding of the separate bf16 results (each off by at most half a unit of its own value, the sum
+    rounded once), and within 1e-6 in fp32; the block gradients, and so dq, do not change."""
+    print(f"group shared dX act={act} b={b} shapes={shapes} T={T}", flush=True)
+    inps = [custom_linear_inputs(m, n, b, T, act, act, 0.05, seed=29 * m + n + i) for i, (m, n) in enumerate(shapes)]
+    single, grouped = [make_layer(inp) for inp in inps], [make_layer(inp) for inp in inps]
+    ga, gb = PoetxGroup(single, batch_grads=True), PoetxGroup(grouped, batch_grads=True)
+    ga.build()
+    gb.build()
+    X = dev(inps[0].X, act)
+    dZs = [dev(inp.dZ, act) for inp in inps]
+    idx = list(range(len(inps)))
+    for lay in single:
+        lay.forward(X)
+    gb.forward(idx, [X] * len(idx))
+    dXa = [ga.backward_dx(i, X, dZ) for i, dZ in zip(idx, dZs)]
+    D = torch.empty_like(dXa[0])
+    out = gb.backward_dx_many(idx, dZs, dXs=[D] * len(idx))
+    assert all(o is D for o in out)
+    dqa, dqb = ga.backward_q(), gb.backward_q()
+    torch.cuda.synchronize()
+    parts = torch.stack([x.double() for x in dXa])
+    want, got = parts.sum(0), D.double()
+    if act == "bf16":
+        bound = 2.0 ** -8 * (parts.abs().sum(0) + got.abs()) + 1e-30
+    else:
+        bound = 1e-6 * (parts.abs().sum(0) + got.abs()) + 1e-30
+    worst = ((got - want).abs() / bound).max().item()
+    print(f"  summed dX: worst error / bound {worst:.3f}", flush=True)
+    assert worst <= 1.0
+    for i in idx:
+        for k in range(2):
+            assert torch.equal(dqa[i][k], dqb[i][k])
