@@ -192,10 +192,13 @@ template <class CC, typename T> struct TStage {
   }
 };
 
-// Dense Q from the packed parameters, one 64 x 64 tile per workgroup: entries
-// above the diagonal are read along packed rows; entries below it come from
-// the mirrored tile, staged through LDS so that both reads and writes are
-// row-contiguous.  Writes Q in the operand dtype.
+// Dense Q from the packed parameters.  A workgroup takes one tile (ti, tj),
+// ti <= tj, of 64 x 64: it reads the packed slots of the tile's entries above
+// the diagonal along packed rows into LDS, then writes the tile (for a
+// diagonal tile also its entries below the diagonal, negated from the
+// mirrored ones) and, off the diagonal, the mirrored tile (tj, ti) = -(its
+// transpose), in 16-byte pieces of rows.  Entries outside the live r x r
+// corner, and the diagonal, are zero.  Writes Q in the operand dtype.
 template <typename T>
 __global__ __launch_bounds__(256) void k_unpack_q(SideTable sd, int b, T* __restrict__ Qb) {
   __shared__ float t[64][65];
@@ -204,39 +207,52 @@ __global__ __launch_bounds__(256) void k_unpack_q(SideTable sd, int b, T* __rest
   int r;
   sd.at(z, b, qk, r);
   const int tiles = (b + 63) / 64;
-  const int i0 = (blockIdx.x / tiles) * 64, j0 = (blockIdx.x % tiles) * 64;
-  const int c = threadIdx.x & 63, rr = threadIdx.x >> 6;
-  // a block of size b has b (b - 1) / 2 slots; with none (b = 1) Q is zero
-  const bool any = b > 1;
-  // every load below reads a valid slot (slot 0 stands in for masked ones)
-  if (i0 >= j0) {
-    float v[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int j = j0 + rr + 4 * k, i = i0 + c;
-      const bool ok = any && j < i && i < r;
-      v[k] = qk[ok ? packed_slot(j, i, b) : 0];
-      v[k] = ok ? v[k] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) t[rr + 4 * k][c] = v[k];
+  int u = blockIdx.x, ti = 0;
+  while (u >= tiles - ti) {
+    u -= tiles - ti;
+    ++ti;
   }
-  __syncthreads();
-  float u[16];
+  const int tj = ti + u, i0 = ti * 64, j0 = tj * 64;
+  const int c = threadIdx.x & 63, rr = threadIdx.x >> 6;
+  // every load reads a valid slot (slot 0 stands in for masked ones); a block
+  // of size b has b (b - 1) / 2 slots, none for b = 1 (Q is zero)
+  const bool any = b > 1;
+  float v[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int i = i0 + rr + 4 * k, j = j0 + c;
     const bool ok = any && i < j && j < r;
-    u[k] = qk[ok ? packed_slot(i, j, b) : 0];
-    u[k] = ok ? u[k] : 0.f;
+    v[k] = qk[ok ? packed_slot(i, j, b) : 0];
+    v[k] = ok ? v[k] : 0.f;
   }
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    const int ii = rr + 4 * k, i = i0 + ii, j = j0 + c;
-    if (i >= b || j >= b) continue;
-    const float v = (j < i && i < r) ? -t[c][ii] : u[k];
-    const int64_t e = (int64_t)z * b * b + (int64_t)i * b + j;
-    Qb[e] = from_f32<T>(v);
+  for (int k = 0; k < 16; ++k) t[rr + 4 * k][c] = v[k];
+  __syncthreads();
+  T* Q = Qb + (int64_t)z * b * b;
+  constexpr int V = 16 / sizeof(T);
+  const bool vec = b % V == 0;
+  // one 64 x 64 output tile at (row0, col0): value(row, col) from LDS
+  auto put = [&](int row0, int col0, auto value) {
+    for (int w = threadIdx.x; w < 64 * 64 / V; w += blockDim.x) {
+      const int row = w / (64 / V), col = (w % (64 / V)) * V;
+      if (row0 + row >= b || col0 + col >= b) continue;
+      T* o = Q + (int64_t)(row0 + row) * b + col0 + col;
+      if (vec) {
+        T vals[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) vals[e] = from_f32<T>(value(row, col + e));
+        *reinterpret_cast<uint4*>(o) = *reinterpret_cast<const uint4*>(vals);
+      } else {
+        for (int e = 0; e < V && col0 + col + e < b; ++e) o[e] = from_f32<T>(value(row, col + e));
+      }
+    }
+  };
+  if (ti == tj) {
+    // diagonal tile: above the diagonal as read, below it the negated mirror
+    put(i0, j0, [&](int i, int j) { return i < j ? t[i][j] : i > j ? -t[j][i] : 0.f; });
+  } else {
+    put(i0, j0, [&](int i, int j) { return t[i][j]; });
+    put(j0, i0, [&](int j, int i) { return -t[i][j]; });
   }
 }
 
@@ -727,7 +743,7 @@ hipError_t build_t(const SideTable& sd, int b, const GOut& go, void* ws, hipStre
                 "the transposed stage of k_cnp_delta fits the K loop's LDS");
   if (e != hipSuccess) return e;
   const unsigned t64 = cdiv(b, 64);
-  k_unpack_q<T><<<dim3(t64 * t64, nb), 256, 0, s>>>(sd, b, Qb);
+  k_unpack_q<T><<<dim3(t64 * (t64 + 1) / 2, nb), 256, 0, s>>>(sd, b, Qb);
   const unsigned grid = cdiv(b, C::BN) * cdiv(b, C::BM) * nb;
   k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(sd, b, Qb, T2, Sb, Ntb);
   k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(sd, b, T2, Sb, Ntb, go);
@@ -829,7 +845,7 @@ hipError_t chain_t(const SideTable& sd, int b, void* dg, const DqOut& out, const
     ch.Qb = reinterpret_cast<const T*>(w);
     ch.Sb = const_cast<T*>(reinterpret_cast<const T*>(w + 2 * al256(E * sizeof(T))));
   } else {
-    k_unpack_q<T><<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb));
+    k_unpack_q<T><<<dim3(t64 * (t64 + 1) / 2, NB), 256, 0, s>>>(sd, b, const_cast<T*>(ch.Qb));
   }
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = hipSuccess;
