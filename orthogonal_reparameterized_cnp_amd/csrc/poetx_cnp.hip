@@ -689,9 +689,14 @@ __global__ __launch_bounds__(256) void k_pack_dq(SideTable sd, int b, const floa
   int s, blk, r;
   const float* qk;
   sd.at(z, b, s, blk, r, qk);
+  // one workgroup per tile on or above the diagonal (ti <= tj)
   const int tiles = (b + 63) / 64;
-  const int i0 = (blockIdx.x / tiles) * 64, j0 = (blockIdx.x % tiles) * 64;
-  if (i0 > j0) return;
+  int w = blockIdx.x, ti = 0;
+  while (w >= tiles - ti) {
+    w -= tiles - ti;
+    ++ti;
+  }
+  const int i0 = ti * 64, j0 = (ti + w) * 64;
   const float* D = dQ32 + (int64_t)z * b * b;
   const int c = threadIdx.x & 63, rr = threadIdx.x >> 6;
   // loads from positions clamped into the live corner, all issued up front
@@ -858,7 +863,7 @@ hipError_t chain_t(const SideTable& sd, int b, void* dg, const DqOut& out, const
   const int kinds = build ? 1 : 2;
   k_cnp_grad1<C, T><<<kinds * grid, C::NT, lds1, s>>>(sd, b, ch, kinds);
   k_cnp_grad2<C, T><<<grid, C::NT, lds, s>>>(sd, b, ch);
-  k_pack_dq<<<dim3(t64 * t64, NB), 256, 0, s>>>(sd, b, ch.F32, out);
+  k_pack_dq<<<dim3(t64 * (t64 + 1) / 2, NB), 256, 0, s>>>(sd, b, ch.F32, out);
   return hipGetLastError();
 }
 
