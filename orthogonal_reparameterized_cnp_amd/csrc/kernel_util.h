@@ -117,6 +117,42 @@ PX_DEV void store_tile(const Acc<C>& acc, void* lds, OT* out, int64_t ldo, int r
   }
 }
 
+// store_tile for any value per accumulator element: f(i, j, e) is the value
+// of the calling lane's element (i, j, e) (tile row p.row(i, e), column
+// p.col(j)).  Staged in the LDS rows [0, BM) x (BN + 16 B), then written out in
+// 16-byte chunks; rows >= rows and columns >= cols are not written.
+template <class C, typename OT, class F>
+PX_DEV void store_tile_fn(void* lds, OT* out, int64_t ldo, int rows, int cols, const F& f) {
+  constexpr int V = 16 / (int)sizeof(OT);
+  constexpr int PITCH = C::BN + V;
+  OT* t = reinterpret_cast<OT*>(lds);
+  const AccPos<C> p = acc_pos<C>();
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) {
+    const int c = p.col(j);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t[p.row(i, e) * PITCH + c] = from_f32<OT>(f(i, j, e));
+  }
+  __syncthreads();
+  constexpr int CPR = C::BN / V;
+  const bool vec = (reinterpret_cast<uintptr_t>(out) % 16 == 0) && (ldo % V == 0);
+  const bool whole = vec && rows >= C::BM && cols >= C::BN;
+  for (int ch = threadIdx.x; ch < C::BM * CPR; ch += C::NT) {
+    const int r = ch / CPR, cc = (ch % CPR) * V;
+    const OT* src = t + r * PITCH + cc;
+    OT* dst = out + (int64_t)r * ldo + cc;
+    if (whole || (vec && r < rows && cc + V <= cols)) {
+      *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+    } else if (r < rows) {
+      for (int e = 0; e < V; ++e)
+        if (cc + e < cols) dst[e] = src[e];
+    }
+  }
+}
+
 template <class A> using cfg_of = typename std::decay_t<A>::Cfg;
 
 // f[i][j][e] = src[(row0 + row) * ld + col0 + col] at the calling lane's

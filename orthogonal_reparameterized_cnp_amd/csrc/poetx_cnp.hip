@@ -190,6 +190,27 @@ template <class CC, typename T> struct TStage {
         for (int e = 0; e < 4 && i + e < nrows; ++e) d[e] = s[e];
     }
   }
+  // the staged tile itself, untransposed: dst[(row0 + i) * ld + col0 + j] = value put at (i, j), in
+  // 16-byte pieces of 16 / sizeof(T) consecutive j read down the staged rows
+  PX_DEV void flush_rows(T* dst, int64_t ld, int row0, int col0, int nrows, int ncols) const {
+    constexpr int V = 16 / (int)sizeof(T), Q = CC::BN / V;  // pieces per output row
+    const bool vec = reinterpret_cast<uintptr_t>(dst) % 16 == 0 && ld % V == 0 && col0 % V == 0;
+    for (int c = threadIdx.x; c < CC::BM * Q; c += blockDim.x) {
+      const int i = c / Q, j = (c % Q) * V;
+      if (i >= nrows || j >= ncols) continue;
+      T* d = dst + (int64_t)(row0 + i) * ld + col0 + j;
+      T vals[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) vals[e] = t[(j + e) * PITCH + i];
+      if (vec && j + V <= ncols) {
+        *reinterpret_cast<uint4*>(d) = *reinterpret_cast<const uint4*>(vals);
+      } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e)
+          if (j + e < ncols) d[e] = vals[e];
+      }
+    }
+  }
 };
 
 // Dense Q from the packed parameters.  A workgroup takes one tile (ti, tj),
@@ -275,24 +296,14 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     using CC = cfg_of<decltype(acc)>;
     float q[CC::TM][CC::TN][16];
     load_at_acc<CC>(q, Qb + off, b, m0, n0, r, r);
-    const AccPos<CC> p = acc_pos<CC>();
-#pragma unroll
-    for (int ti = 0; ti < CC::TM; ++ti)
-#pragma unroll
-      for (int tj = 0; tj < CC::TN; ++tj) {
-        const int j = n0 + p.col(tj);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int i = m0 + p.row(ti, e);
-          if (i < r && j < r) {
-            const int64_t x = off + (int64_t)i * b + j;
-            const float sv = -acc.v[ti][tj][e], qv = q[ti][tj][e];
-            T2[x] = from_f32<T>(2.f * qv + 2.f * sv);
-            Sb[x] = from_f32<T>(sv);
-            Ntb[x] = from_f32<T>(sv - 2.f * qv);
-          }
-        }
-      }
+    // the three outputs over the live corner, each staged in LDS and written in 16-byte row pieces
+    const int rows = min(CC::BM, r - m0), cols = min(CC::BN, r - n0);
+    const int64_t at = off + (int64_t)m0 * b + n0;
+    store_tile_fn<CC, T>(smem, T2 + at, b, rows, cols,
+                         [&](int i, int j, int e) { return 2.f * q[i][j][e] + 2.f * -acc.v[i][j][e]; });
+    store_tile_fn<CC, T>(smem, Sb + at, b, rows, cols, [&](int i, int j, int e) { return -acc.v[i][j][e]; });
+    store_tile_fn<CC, T>(smem, Ntb + at, b, rows, cols,
+                         [&](int i, int j, int e) { return -acc.v[i][j][e] - 2.f * q[i][j][e]; });
   });
 }
 
@@ -321,7 +332,17 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     float t2[CC::TM][CC::TN][16];
     load_at_acc<CC>(t2, T2 + off, b, m0, n0, max(r, 1), max(r, 1));
     const AccPos<CC> p = acc_pos<CC>();
-    const TStage<CC, T> st(smem);  // slice 1 (the transpose) leaves through LDS
+    // G - I over the whole b x b block (zero outside the live corner)
+    auto value = [&](int ti, int tj, int e) {
+      const int i = m0 + p.row(ti, e), j = n0 + p.col(tj);
+      return (i < r && j < r) ? acc.v[ti][tj][e] + t2[ti][tj][e] : 0.f;
+    };
+    // slice 0 (row-major) staged in LDS and written in 16-byte row pieces; slice 1 (the transpose)
+    // through a second LDS area past the first
+    const int rows = min(CC::BM, b - m0), cols = min(CC::BN, b - n0);
+    store_tile_fn<CC, T>(smem, g0 + (int64_t)m0 * b + n0, b, rows, cols, value);
+    constexpr int EPI = (CC::BM * (CC::BN + 16 / (int)sizeof(T)) * (int)sizeof(T) + 15) / 16 * 16;
+    const TStage<CC, T> st(smem + EPI);
 #pragma unroll
     for (int ti = 0; ti < CC::TM; ++ti)
 #pragma unroll
@@ -333,16 +354,12 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
           if (j >= b || i0 >= b) continue;
           float o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = i0 + e;
-            o[e] = (i < r && j < r) ? acc.v[ti][tj][4 * g + e] + t2[ti][tj][4 * g + e] : 0.f;
-            if (i < b) g0[(int64_t)i * b + j] = from_f32<T>(o[e]);
-          }
+          for (int e = 0; e < 4; ++e) o[e] = value(ti, tj, 4 * g + e);
           st.put(i0 - m0, j - n0, o);
         }
       }
     __syncthreads();
-    st.flush(g1, b, m0, n0, min(CC::BM, b - m0), min(CC::BN, b - n0));
+    st.flush(g1, b, m0, n0, rows, cols);
   });
 }
 
@@ -624,7 +641,6 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
             const float uv = f[tj][k], v1 = -uq.v[ti][tj][k], pv = qu.v[ti][tj][k];
             w[e] = 2.f * uv - v1 - pv;
             v2[e] = 2.f * v1;
-            ch.Wb[x] = from_f32<T>(w[e]);
             ch.F32[x] = 2.f * uv - 2.f * v1 - 2.f * pv;
           }
           sw.put(i0 - m0, j - n0, w);
@@ -636,6 +652,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     const int nr = min(CC::BM, r - m0), nc = min(CC::BN, r - n0);
     sw.flush(ch.Wtb + off, b, m0, n0, nr, nc);
     sv.flush(ch.V1tb + off, b, m0, n0, nr, nc);
+    sw.flush_rows(ch.Wb + off, b, m0, n0, nr, nc);  // W itself, from the same stage
   });
 }
 
@@ -744,8 +761,9 @@ hipError_t build_t(const SideTable& sd, int b, const GOut& go, void* ws, hipStre
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = allow_lds(k_cnp_square<C, T>, lds);
   if (e == hipSuccess) e = allow_lds(k_cnp_delta<C, T>, lds);
-  static_assert(TStage<C, T>::BYTES <= std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0),
-                "the transposed stage of k_cnp_delta fits the K loop's LDS");
+  static_assert((C::BM * (C::BN + 16 / (int)sizeof(T)) * (int)sizeof(T) + 15) / 16 * 16 + TStage<C, T>::BYTES <=
+                    std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0),
+                "the two output stages of k_cnp_delta fit the K loop's LDS");
   if (e != hipSuccess) return e;
   const unsigned t64 = cdiv(b, 64);
   k_unpack_q<T><<<dim3(t64 * (t64 + 1) / 2, nb), 256, 0, s>>>(sd, b, Qb);
