@@ -188,7 +188,7 @@ poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype
  * from a fixed device array inside the library instead of a caller buffer.
  *   q, d, b, dtype, g  as for poetx_cnp_build
  *   stream   must belong to the current device
- * The array holds POETX_NOALLOC_SCRATCH_BYTES (80 MiB) on each GPU the call
+ * The array holds POETX_NOALLOC_SCRATCH_BYTES (60 MiB) on each GPU the call
  * runs on, from the first call on that GPU until the process ends; that is
  * room for poetx_workspace_size(desc with m = d, 0, POETX_OP_CNP) of any side
  * up to 40 blocks of 512 in bf16 (d <= 20480 at b = 512) or 20 in fp32.
@@ -198,7 +198,7 @@ poetx_status poetx_cnp_build(const float* q, int32_t d, int32_t b, int32_t dtype
  * Errors: POETX_E_NULL, POETX_E_SHAPE, POETX_E_DTYPE, POETX_E_WORKSPACE (the
  * side's workspace exceeds the array), POETX_E_HIP.
  */
-#define POETX_NOALLOC_SCRATCH_BYTES (80u << 20)
+#define POETX_NOALLOC_SCRATCH_BYTES (60u << 20)
 poetx_status poetx_cnp_build_noalloc(const float* q, int32_t d, int32_t b, int32_t dtype, void* g, void* stream);
 
 /*

@@ -174,15 +174,15 @@ PX_DEV void load_at_acc(float (&f)[C::TM][C::TN][16], const S* src, int64_t ld, 
 }
 
 // the same for the accumulator row group ti only: f[j][e] for tile (ti, j)
-template <class C>
-PX_DEV void load_at_acc_i(float (&f)[C::TN][16], const float* src, int64_t ld, int row0, int col0, int rmax, int cmax,
+template <class C, typename S>
+PX_DEV void load_at_acc_i(float (&f)[C::TN][16], const S* src, int64_t ld, int row0, int col0, int rmax, int cmax,
                           int ti) {
   const AccPos<C> p = acc_pos<C>();
 #pragma unroll
   for (int j = 0; j < C::TN; ++j) {
     const int c = min(col0 + p.col(j), cmax - 1);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) f[j][e] = src[(int64_t)min(row0 + p.row(ti, e), rmax - 1) * ld + c];
+    for (int e = 0; e < 16; ++e) f[j][e] = to_f32<S>(src[(int64_t)min(row0 + p.row(ti, e), rmax - 1) * ld + c]);
   }
 }
 

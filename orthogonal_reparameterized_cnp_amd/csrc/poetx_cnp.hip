@@ -2,7 +2,7 @@
 // chain rule from block gradients dG back to the packed parameters.
 //
 // Build (POET-X blog on zhichai.net, 第四斧: Q^2 once, Q^3 and Q^4 from it):
-//   S = Q^2, N = 2Q + S,  G - I = 2Q + 2S + S N  (= 2Q + 2Q^2 + 2Q^3 + Q^4).
+//   S = Q^2, N = 2Q + S,  G - I = (N + S) + N S  (= 2Q + 2Q^2 + 2Q^3 + Q^4).
 // Chain rule of G = I + 2(Q + Q^2 + Q^3) + Q^4 with Q^T = -Q: with U = dL/dG
 // (the block gradient, summed over tokens here too), the derivative of L with
 // respect to the entries of Q is
@@ -277,12 +277,11 @@ __global__ __launch_bounds__(256) void k_unpack_q(SideTable sd, int b, T* __rest
   }
 }
 
-// S = Q Q = -(Q Q^T).  Writes S, N^T = S - 2Q and the partial sum 2Q + 2S in
-// the operand dtype (the epilogue reads Q at its accumulators' positions).
+// S = Q Q = -(Q Q^T).  Writes S and N = 2Q + S in the operand dtype (the
+// epilogue reads Q at its accumulators' positions).
 template <class C, typename T>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_square(SideTable sd, int b, const T* __restrict__ Qb,
-                                                      T* __restrict__ T2, T* __restrict__ Sb,
-                                                      T* __restrict__ Ntb) {
+                                                      T* __restrict__ Nb, T* __restrict__ Sb) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM;
   const int u = xcd_unit(blockIdx.x, gridDim.x), z = u / (tm * tn);
@@ -296,26 +295,25 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     using CC = cfg_of<decltype(acc)>;
     float q[CC::TM][CC::TN][16];
     load_at_acc<CC>(q, Qb + off, b, m0, n0, r, r);
-    // the three outputs over the live corner, each staged in LDS and written in 16-byte row pieces
+    // the two outputs over the live corner, each staged in LDS and written in 16-byte row pieces
     const int rows = min(CC::BM, r - m0), cols = min(CC::BN, r - n0);
     const int64_t at = off + (int64_t)m0 * b + n0;
-    store_tile_fn<CC, T>(smem, T2 + at, b, rows, cols,
-                         [&](int i, int j, int e) { return 2.f * q[i][j][e] + 2.f * -acc.v[i][j][e]; });
     store_tile_fn<CC, T>(smem, Sb + at, b, rows, cols, [&](int i, int j, int e) { return -acc.v[i][j][e]; });
-    store_tile_fn<CC, T>(smem, Ntb + at, b, rows, cols,
-                         [&](int i, int j, int e) { return -acc.v[i][j][e] - 2.f * q[i][j][e]; });
+    store_tile_fn<CC, T>(smem, Nb + at, b, rows, cols,
+                         [&](int i, int j, int e) { return 2.f * q[i][j][e] - acc.v[i][j][e]; });
   });
 }
 
-// G - I = (2Q + 2S) + S N, written as slice 0 (row-major) and slice 1
-// (transposed); zero outside the live r x r corner.
+// G - I = (N + S) + N S (N S = S N: both are polynomials in Q, and N + S = 2Q + 2S),
+// written as slice 0 (row-major) and slice 1 (transposed); zero outside the live
+// r x r corner.  S is symmetric, so its rows serve as the B operand.
 struct GOut {
   void* g[pxk::kMaxSides];  // side s: [2][nb_s][b][b], slice 0 = G - I, slice 1 = its transpose
 };
 
 template <class C, typename T>
-__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_delta(SideTable sd, int b, const T* __restrict__ T2,
-                                                     const T* __restrict__ Sb, const T* __restrict__ Ntb, GOut go) {
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void k_cnp_delta(SideTable sd, int b, const T* __restrict__ Nb,
+                                                     const T* __restrict__ Sb, GOut go) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tn = (b + C::BN - 1) / C::BN, tm = (b + C::BM - 1) / C::BM;
   const int u = xcd_unit(blockIdx.x, gridDim.x), z = u / (tm * tn);
@@ -327,10 +325,20 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(2))) void
   const int64_t nb_s = sd.first[side + 1] - sd.first[side];
   T* g0 = reinterpret_cast<T*>(go.g[side]) + (int64_t)blk * b * b;
   T* g1 = reinterpret_cast<T*>(go.g[side]) + (nb_s + blk) * b * b;
-  run_kk<C, T>(smem, Sb + off + (int64_t)m0 * b, r - m0, Ntb + off + (int64_t)n0 * b, r - n0, b, r, [&](auto& acc) {
+  run_kk<C, T>(smem, Nb + off + (int64_t)m0 * b, r - m0, Sb + off + (int64_t)n0 * b, r - n0, b, r, [&](auto& acc) {
     using CC = cfg_of<decltype(acc)>;
+    // t2 = N + S = 2Q + 2S at the accumulators' positions (S added one row group at a time)
     float t2[CC::TM][CC::TN][16];
-    load_at_acc<CC>(t2, T2 + off, b, m0, n0, max(r, 1), max(r, 1));
+    load_at_acc<CC>(t2, Nb + off, b, m0, n0, max(r, 1), max(r, 1));
+#pragma unroll
+    for (int ti = 0; ti < CC::TM; ++ti) {
+      float sv[CC::TN][16];
+      load_at_acc_i<CC>(sv, Sb + off, b, m0, n0, max(r, 1), max(r, 1), ti);
+#pragma unroll
+      for (int tj = 0; tj < CC::TN; ++tj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) t2[ti][tj][e] += sv[tj][e];
+    }
     const AccPos<CC> p = acc_pos<CC>();
     // G - I over the whole b x b block (zero outside the live corner)
     auto value = [&](int ti, int tj, int e) {
@@ -753,11 +761,9 @@ hipError_t build_t(const SideTable& sd, int b, const GOut& go, void* ws, hipStre
   char* w = reinterpret_cast<char*>(ws);
   T* Qb = reinterpret_cast<T*>(w);
   w += al256(E * sizeof(T));
-  T* T2 = reinterpret_cast<T*>(w);  // 2Q + 2S
+  T* Nb = reinterpret_cast<T*>(w);  // 2Q + S
   w += al256(E * sizeof(T));
-  T* Sb = reinterpret_cast<T*>(w);
-  w += al256(E * sizeof(T));
-  T* Ntb = reinterpret_cast<T*>(w);
+  T* Sb = reinterpret_cast<T*>(w);  // third: the chain rule's reuse of a build reads S here
   const int lds = std::max(Lay<C, T>::BYTES, std::is_same<T, bf16_t>::value ? DSq::LDS_BYTES : 0);
   hipError_t e = allow_lds(k_cnp_square<C, T>, lds);
   if (e == hipSuccess) e = allow_lds(k_cnp_delta<C, T>, lds);
@@ -768,8 +774,8 @@ hipError_t build_t(const SideTable& sd, int b, const GOut& go, void* ws, hipStre
   const unsigned t64 = cdiv(b, 64);
   k_unpack_q<T><<<dim3(t64 * (t64 + 1) / 2, nb), 256, 0, s>>>(sd, b, Qb);
   const unsigned grid = cdiv(b, C::BN) * cdiv(b, C::BM) * nb;
-  k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(sd, b, Qb, T2, Sb, Ntb);
-  k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(sd, b, T2, Sb, Ntb, go);
+  k_cnp_square<C, T><<<grid, C::NT, lds, s>>>(sd, b, Qb, Nb, Sb);
+  k_cnp_delta<C, T><<<grid, C::NT, lds, s>>>(sd, b, Nb, Sb, go);
   return hipGetLastError();
 }
 
@@ -891,7 +897,7 @@ namespace pxk {
 
 size_t cnp_build_ws_bytes(int dt, int64_t blocks, int b) {
   const size_t E = (size_t)blocks * b * b, es = dt_size(dt);
-  return al256(E * es) * 4;  // Q, 2Q + 2S, S, N^T
+  return al256(E * es) * 3;  // Q, N = 2Q + S, S
 }
 
 size_t cnp_grad_bytes(int dt, int64_t blocks, int b) {

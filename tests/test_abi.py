@@ -221,8 +221,8 @@ def test_spo_helpers_and_validation(L):
 
 def test_cnp_build_noalloc_limits(L):
     """The no-allocation CNP build rejects, before any device call, a side whose workspace
-    exceeds the fixed scratch array (80 MiB): 40 blocks of 512 fit in bf16, 41 do not."""
-    lim = 80 << 20
+    exceeds the fixed scratch array (60 MiB): 40 blocks of 512 fit in bf16, 41 do not."""
+    lim = 60 << 20
     cnp_ws = lambda d, act: B.poetx_workspace_size(B.desc(d, 1, 512, act, act), 0, B.POETX_OP_CNP)
     assert cnp_ws(40 * 512, "bf16") <= lim < cnp_ws(41 * 512, "bf16")
     assert cnp_ws(20 * 512, "f32") <= lim < cnp_ws(21 * 512, "f32")

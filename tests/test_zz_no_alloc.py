@@ -54,7 +54,7 @@ def test_noalloc_matches_cnp_build(cases):
 
 
 def test_noalloc_rejects_oversized_side():
-    # 48 blocks of 512 in bf16 need 100.7 MB of workspace, more than the fixed array holds
+    # 48 blocks of 512 in bf16 need 72 MiB of workspace, more than the fixed array's 60 MiB
     d, b = 48 * 512, 512
     q = torch.zeros(48, b * (b - 1) // 2, dtype=torch.float32, device="cuda")
     g = torch.zeros(B.poetx_g_bytes(d, b, B.POETX_BF16), dtype=torch.uint8, device="cuda")
