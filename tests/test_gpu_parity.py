@@ -108,6 +108,9 @@ def test_layer_llama1p3b_odd_width(lin):
     "m,n,b,T,act",
     [(200, 131, 64, 77, "bf16"), (200, 131, 64, 77, "f32"), (96, 300, 32, 1, "bf16"), (130, 130, 128, 300, "bf16"),
      (64, 64, 64, 513, "bf16"), (33, 17, 8, 5, "f32"), (520, 1030, 256, 260, "bf16"),
+     # block sizes that are not a multiple of 8: every b x b row pitch is odd, so the 16-byte epilogue
+     # stores fall back to element stores (and a partial last block of 1 column on the P side)
+     (111, 75, 37, 50, "bf16"), (45, 79, 13, 9, "f32"),
      # row-streamed block products (enough row tiles): ragged T and a partial last block of b = 256 / 512
      (2048, 1300, 256, 1000, "bf16"), (1536, 2600, 512, 700, "bf16")],
 )
